@@ -1,0 +1,289 @@
+"""Pins of the CPU oracle against what the pages and the mathematics fix (no GPU).
+
+Sources: reproduction notes of arXiv 2610.13674 (daiwk.github.io), section "核心公式"
+(group scores, kernel kappa = eps + s-bar^T L L^T s-bar > 0, prefix states H0/H1/H2,
+readout); its section "本地结果与边界" (dense kernel and HD recursion checked equal);
+and the arXiv abstract page (the method starts from a second-order Taylor approximation
+of softmax). Each test names the plausible oracle mistake it would catch.
+"""
+import os
+import shutil
+import subprocess
+import ctypes
+
+import numpy as np
+import pytest
+
+import oracle
+from oal_synth import HeadParams, random_params, small, draw_L
+
+
+def _case(seed, B=1, Hq=2, Hkv=1, T=12, d=8, dv=5, g_hi=3, scale=1.0):
+    rng = np.random.default_rng(seed)
+    q = rng.standard_normal((B, Hq, T, d)) * scale
+    k = rng.standard_normal((B, Hkv, T, d)) * scale
+    v = rng.standard_normal((B, Hkv, T, dv))
+    p = random_params(rng, Hq, d, g_hi=g_hi)
+    return q, k, v, p
+
+
+# --------------------------------------------------------------------------------------
+# 1. A worked example done by hand (d=4 so 1/sqrt(d) = 1/2; dv=2; G=2; T=3).
+#
+#   groups: dims {0,1} -> config g0 (s-bar index 1); dims {2,3} -> g1 (s-bar index 2)
+#   L = [[1,0,0],[0.5,1,0],[0,1,2]], eps = 0.25
+#   z_m = sum_{g>=m} L[g][m] s-bar_g ; kappa = eps + z0^2 + z1^2 + z2^2
+#   i=0,j=0: s-bar=[1,1,1]  -> z=[1.5,2,2]  -> kappa = 0.25+2.25+4+4 = 10.5
+#   i=1,j=0: s-bar=[1,1,1]  -> kappa = 10.5
+#   i=1,j=1: s-bar=[1,0,0]  -> z=[1,0,0]    -> kappa = 1.25
+#   i=2,j=0: s-bar=[1,0,1]  -> z=[1,1,2]    -> kappa = 6.25
+#   i=2,j=1: s-bar=[1,1,-1] -> z=[1.5,0,-2] -> kappa = 6.5
+#   i=2,j=2: s-bar=[1,0,1]  -> kappa = 6.25
+#   y0 = v0 = [1,0]; y1 = (10.5 v0 + 1.25 v1)/11.75 = [42/47, 5/47];
+#   y2 = (6.25 v0 + 6.5 v1 + 6.25 v2)/19 = [0, 1].
+# Catches: L used untransposed (L s-bar gives 12.5 at (0,0)), a missing 1/sqrt(d), a wrong
+# group offset into s-bar, exclusive causality, a dropped eps.
+
+WQ = np.array([[[[2, 0, 0, 2], [0, 2, 2, 0], [1, -1, 1, 1]]]], float)
+WK = np.array([[[[1, 1, 1, 1], [2, 0, 0, -2], [1, 1, -1, 3]]]], float)
+WV = np.array([[[[1, 0], [0, 1], [-1, 2]]]], float)
+WP = HeadParams(np.array([2], np.int32), np.array([[0, 0, 1, 1]], np.uint8),
+                np.array([[[1, 0, 0], [0.5, 1, 0], [0, 1, 2]]], np.float32),
+                np.array([0.25], np.float32))
+
+
+def test_worked_example_by_hand():
+    kap = oracle.kappa_matrix(WQ, WK, WP, 0, 0)
+    want = np.array([[10.5, 0, 0], [10.5, 1.25, 0], [6.25, 6.5, 6.25]])
+    np.testing.assert_allclose(kap, want, rtol=0, atol=1e-13)
+    y, den = oracle.dense(WQ, WK, WV, WP, return_den=True)
+    np.testing.assert_allclose(y[0, 0], [[1, 0], [42 / 47, 5 / 47], [0, 1]], rtol=0, atol=1e-14)
+    np.testing.assert_allclose(den[0, 0], [10.5, 11.75, 19.0], rtol=0, atol=1e-13)
+
+
+def test_worked_example_state_by_hand():
+    # H0 = sum [v;1] = [0,3,3]; H1_0 = 1*[1,0,1] + 2*[0,1,1] + 1*[-1,2,1] = [0,4,4];
+    # H2_(3,3) = 1*[1,0,1] + 4*[0,1,1] + 9*[-1,2,1] = [-8,22,14];
+    # H2_(0,3) = 1*[1,0,1] - 4*[0,1,1] + 3*[-1,2,1] = [-2,2,0].
+    H = oracle.state(WK, WV)[0, 0]
+    d = 4
+    idx = lambda r, t: 1 + d + r * d - r * (r - 1) // 2 + (t - r)
+    np.testing.assert_allclose(H[0], [0, 3, 3])
+    np.testing.assert_allclose(H[1], [0, 4, 4])
+    np.testing.assert_allclose(H[idx(3, 3)], [-8, 22, 14])
+    np.testing.assert_allclose(H[idx(0, 3)], [-2, 2, 0])
+    assert H.shape[0] == 1 + d + d * (d + 1) // 2
+
+
+# --------------------------------------------------------------------------------------
+# 2. Dense kernel sum == the pages' H0/H1/H2 recurrence (their own equivalence check).
+# Catches a wrong (eps, L) -> (a, b, C) expansion, a wrong 1/d vs 1/sqrt(d), wrong GQA map.
+
+@pytest.mark.parametrize("d,g_hi,seed", [(4, 1, 1), (4, 4, 2), (8, 2, 3), (8, 4, 4),
+                                         (64, 4, 5), (64, 6, 6)])
+def test_dense_equals_recurrence(d, g_hi, seed):
+    T = 16 if d == 64 else 24
+    q, k, v, p = _case(seed, B=2, Hq=4, Hkv=2, T=T, d=d, dv=3, g_hi=g_hi)
+    y = oracle.dense(q, k, v, p)
+    yr, H = oracle.recurrence(q, k, v, p, return_state=True)
+    assert np.abs(y - yr).max() <= 1e-12 * max(1.0, np.abs(y).max())
+    # the upper-triangle state equals the recurrence's full H2 folded onto r <= t
+    Hu = oracle.state(k, v)
+    nf = 1 + d
+    np.testing.assert_allclose(Hu[:, :, :nf], H[:, :, :nf], rtol=1e-12, atol=1e-12)
+    f = nf
+    for r in range(d):
+        for t in range(r, d):
+            np.testing.assert_allclose(Hu[:, :, f], H[:, :, nf + r * d + t], rtol=1e-12, atol=1e-10)
+            f += 1
+
+
+# --------------------------------------------------------------------------------------
+# 3. kappa > 0: kappa >= eps for every pair (PSD parameterisation). Includes an L with zero
+# and negative diagonal entries and huge scores. Catches a sign error in the square.
+
+def test_kappa_at_least_eps():
+    for seed in range(4):
+        q, k, v, p = _case(10 + seed, Hq=3, T=20, d=16, g_hi=5, scale=4.0)
+        p.L[0, 1, 1] = 0.0
+        p.L[1] *= -1.0
+        for h in range(3):
+            kap = oracle.kappa_matrix(q, k, p, 0, h)
+            low = np.tril(np.ones_like(kap, dtype=bool))
+            assert (kap[low] >= p.eps[h]).all()
+
+
+# --------------------------------------------------------------------------------------
+# 4. Readout is a positive-weighted average: each y_i lies in the coordinate-wise hull of
+# v_{<=i}. Catches a sign slip that makes a weight negative, or a non-causal key.
+
+def test_convex_hull():
+    q, k, v, p = _case(20, B=2, Hq=4, Hkv=2, T=40, d=16, dv=6, g_hi=4, scale=2.0)
+    y = oracle.dense(q, k, v, p)
+    n_rep = 2
+    for b in range(2):
+        for h in range(4):
+            vv = v[b, h // n_rep]
+            lo = np.minimum.accumulate(vv, axis=0)
+            hi = np.maximum.accumulate(vv, axis=0)
+            assert (y[b, h] >= lo - 1e-12).all() and (y[b, h] <= hi + 1e-12).all()
+
+
+# --------------------------------------------------------------------------------------
+# 5. G=1: all dims in one group, with L chosen so that kappa = 1 + s + s^2/2 (s = q.k/sqrt d),
+# the second-order Taylor expansion of exp(s) named on the abstract page. Compared with a
+# separately written textbook Taylor-kernel attention. Catches a wrong constant slot in L.
+
+@pytest.mark.parametrize("eps", [1e-3, 0.1, 0.0])
+def test_g1_is_second_order_taylor(eps):
+    rng = np.random.default_rng(30)
+    B, H, T, d, dv = 1, 2, 33, 16, 4
+    q = rng.standard_normal((B, H, T, d))
+    k = rng.standard_normal((B, H, T, d))
+    v = rng.standard_normal((B, H, T, dv))
+    c = np.sqrt(1 - eps)
+    L1 = np.array([[c, 0.0], [1 / (2 * c), np.sqrt((1 - 2 * eps) / (4 * (1 - eps)))]], np.float64)
+    p = HeadParams(np.ones(H, np.int32), np.zeros((H, d), np.uint8),
+                   np.stack([L1, L1]).astype(np.float64), np.full(H, eps))
+    y = oracle.dense(q, k, v, p)
+    for h in range(H):
+        s = (q[0, h] @ k[0, h].T) / np.sqrt(d)
+        w = np.tril(1.0 + s + 0.5 * s * s)
+        ref = (w @ v[0, h]) / w.sum(axis=1, keepdims=True)
+        np.testing.assert_allclose(y[0, h], ref, rtol=1e-11, atol=1e-12)
+
+
+# --------------------------------------------------------------------------------------
+# 6. L = 0 and eps > 0: kappa is constant, so y_i is the prefix mean of v (H0 path alone).
+
+def test_l_zero_gives_prefix_mean():
+    q, k, v, p = _case(40, Hq=2, T=25, d=8, dv=3)
+    p.L[:] = 0.0
+    y = oracle.dense(q, k, v, p)
+    mean = np.cumsum(v[0, 0], axis=0) / np.arange(1, 26)[:, None]
+    np.testing.assert_allclose(y[0, 0], mean, rtol=1e-13, atol=1e-14)
+    np.testing.assert_allclose(y[0, 1], mean, rtol=1e-13, atol=1e-14)
+
+
+# --------------------------------------------------------------------------------------
+# 7. Trivial cases: T = 1 returns v_0; constant v returns v everywhere.
+
+def test_t1_and_constant_v():
+    q, k, v, p = _case(50, Hq=2, T=1, d=8, dv=4)
+    y = oracle.dense(q, k, v, p)
+    np.testing.assert_allclose(y[0, 0, 0], v[0, 0, 0], rtol=1e-15)
+    q, k, v, p = _case(51, Hq=2, T=17, d=8, dv=4)
+    v[:] = np.array([0.5, -2.0, 3.0, 7.0])
+    y = oracle.dense(q, k, v, p)
+    np.testing.assert_allclose(y, np.broadcast_to(np.array([0.5, -2.0, 3.0, 7.0]), y.shape),
+                               rtol=1e-13)
+
+
+# --------------------------------------------------------------------------------------
+# 8. Normalisation: (L, eps) -> (alpha L, alpha^2 eps) leaves y unchanged.
+
+def test_scale_invariance():
+    q, k, v, p = _case(60, Hq=2, T=20, d=8, g_hi=3)
+    y = oracle.dense(q, k, v, p)
+    p2 = HeadParams(p.n_groups, p.group_of_dim, p.L.astype(np.float64) * 3.0,
+                    p.eps.astype(np.float64) * 9.0)
+    np.testing.assert_allclose(oracle.dense(q, k, v, p2), y, rtol=1e-12, atol=1e-13)
+
+
+# --------------------------------------------------------------------------------------
+# 9. Group split: splitting the last group in two and giving the new group a copy of the
+# old L row (zero column appended, zero diagonal) leaves kappa and y unchanged, because
+# s_old = s_a + s_b enters L^T s-bar linearly. Catches any per-group scale or a wrong
+# group index. Permuting dims consistently in q, k and the group map leaves y unchanged.
+
+def test_group_split_invariance():
+    rng = np.random.default_rng(70)
+    d, Hq, T = 16, 1, 20
+    q = rng.standard_normal((1, Hq, T, d)) * 2
+    k = rng.standard_normal((1, Hq, T, d)) * 2
+    v = rng.standard_normal((1, Hq, T, 3))
+    G = 3
+    gam = np.array([[0] * 8 + [1] * 4 + [2] * 4], np.uint8)
+    L = draw_L(rng, G, G).astype(np.float64)
+    p = HeadParams(np.array([G], np.int32), gam, L[None], np.array([1e-3]))
+    y = oracle.dense(q, k, v, p)
+    gam2 = gam.copy()
+    gam2[0, 14:16] = 3                     # last group {12..15} -> {12,13} and {14,15}
+    L2 = np.zeros((G + 2, G + 2))
+    L2[:G + 1, :G + 1] = L
+    L2[G + 1, :G + 1] = L[G]               # copy of the split group's row
+    p2 = HeadParams(np.array([G + 1], np.int32), gam2, L2[None], np.array([1e-3]))
+    np.testing.assert_allclose(oracle.dense(q, k, v, p2), y, rtol=1e-12, atol=1e-13)
+
+
+def test_dim_permutation_invariance():
+    q, k, v, p = _case(80, B=1, Hq=2, Hkv=1, T=18, d=16, g_hi=4)
+    y = oracle.dense(q, k, v, p)
+    perm = np.random.default_rng(81).permutation(16)
+    p2 = HeadParams(p.n_groups, p.group_of_dim[:, perm], p.L, p.eps)
+    np.testing.assert_allclose(oracle.dense(q[..., perm], k[..., perm], v, p2), y,
+                               rtol=1e-12, atol=1e-13)
+
+
+def test_dense_rows_match_dense():
+    inp = small(90, B=2, Hq=4, Hkv=2, T=30)
+    y = oracle.dense(inp.q, inp.k, inp.v, inp.params)
+    rows = [(0, 0, 0), (1, 3, 29), (0, 2, 17), (1, 1, 5)]
+    yr = oracle.dense_rows(inp.q, inp.k, inp.v, inp.params, rows)
+    for n, (b, h, i) in enumerate(rows):
+        np.testing.assert_array_equal(yr[n], y[b, h, i])
+
+
+def test_causality():
+    q, k, v, p = _case(95, Hq=2, T=20, d=8)
+    y = oracle.dense(q, k, v, p)
+    k2, v2 = k.copy(), v.copy()
+    k2[0, 0, 12] += 1.0
+    v2[0, 0, 12] -= 3.0
+    y2 = oracle.dense(q, k2, v2, p)
+    np.testing.assert_array_equal(y2[:, :, :12], y[:, :, :12])
+    assert np.abs(y2[:, :, 12:] - y[:, :, 12:]).max() > 1e-6
+
+
+# --------------------------------------------------------------------------------------
+# 10. Mutation check: plausible mistakes planted in a private copy of the oracle (compiled
+# on the CPU into a temporary directory) must each fail one of the pins above.
+
+MUTATIONS = {
+    "L_untransposed": ("z += L[g * (g_max + 1) + m] * sbar[g];",
+                       "z += L[m * (g_max + 1) + g] * sbar[g];"),
+    "no_inv_sqrt_d": ("sbar[g] *= inv_sqrt_d;", "sbar[g] *= 1.0;"),
+    "group_offset": ("sbar[1 + group_of_dim[r]] += q[r] * k[r];",
+                     "sbar[group_of_dim[r]] += q[r] * k[r];"),
+    "exclusive_causal": ("for (int j = 0; j <= i; ++j) {", "for (int j = 0; j < i || j == 0; ++j) {"),
+    "dropped_eps": ("double kap = eps;", "double kap = 0.0;"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTATIONS))
+def test_pins_catch_planted_mistakes(name, tmp_path):
+    if shutil.which("gcc") is None:
+        pytest.skip("gcc not available")
+    src = open(oracle._SRC).read()
+    old, new = MUTATIONS[name]
+    assert src.count(old) == 1, f"mutation anchor for {name} not found"
+    mfile = tmp_path / "mut.c"
+    mfile.write_text(src.replace(old, new))
+    so = tmp_path / "libmut.so"
+    subprocess.check_call(["gcc", "-O1", "-fPIC", "-shared", "-o", str(so), str(mfile), "-lm"])
+    lib = ctypes.CDLL(str(so))
+    saved = oracle._lib
+    try:
+        oracle._lib = None
+        real = oracle._load()
+        for fn in ("oal_oracle_dense", "oal_oracle_kappa_matrix"):
+            getattr(lib, fn).argtypes = getattr(real, fn).argtypes
+        oracle._lib = lib
+        lib.oal_oracle_kappa.restype = ctypes.c_double
+        kap = oracle.kappa_matrix(WQ, WK, WP, 0, 0)
+        y = oracle.dense(WQ, WK, WV, WP)
+        ok = (np.allclose(kap, [[10.5, 0, 0], [10.5, 1.25, 0], [6.25, 6.5, 6.25]]) and
+              np.allclose(y[0, 0], [[1, 0], [42 / 47, 5 / 47], [0, 1]]))
+        assert not ok, f"planted mistake {name} passed the worked-example pin"
+    finally:
+        oracle._lib = saved
