@@ -1,0 +1,190 @@
+#!/usr/bin/env python3
+"""Benchmark of the OAL causal-attention hot path on one MI355X.
+
+Prefill (headline): the Qwen2.5-0.5B-shaped layer, B=1, T=4096, 14 query heads over 2 KV
+heads, d=64, bf16 inputs (synthetic, seeded). A step is one oal_prefill call over the
+batch: chunk-state scan + readout. Successive steps continue the state (each step is
+another 4096 tokens of the same sequences), so no extra work enters the timed region.
+
+Decode: 64 sequences whose prefix states were built by oal_prefill from 4096 synthetic
+tokens each; then --decode-steps oal_decode_step calls (one token per sequence).
+
+Prints one JSON line. `value` is prefill tokens/s; `roofline` is the readout kernel
+(the dominant one) against the bf16 MFMA peak; `decode` holds decode tokens/s and the
+decode kernel against HBM peak; `cpu_baseline` is the fp64 CPU oracle on the full prefill
+batch, timed on this host.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+METRIC = "OAL attention tokens/s at T=4096 (prefill) + decode tok/s; % MFMA/HBM peak"
+D, V1, NFEAT = 64, 65, 2145
+FLOP_PER_TOKEN_HEAD = 2 * NFEAT * V1          # 278,850: one feature-space contraction
+PEAK_BF16_TFLOPS = 2500.0                     # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0                         # MI355X HBM3E
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--chunk", type=int, default=128)
+    ap.add_argument("--batch", type=int, default=1)
+    ap.add_argument("--seq", type=int, default=4096)
+    ap.add_argument("--decode-seqs", type=int, default=64)
+    ap.add_argument("--decode-steps", type=int, default=256)
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--traffic-json", default=os.path.join(os.path.dirname(os.path.abspath(__file__)),
+                                                          "profiles", "traffic.json"))
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(json.dumps({"error": "this build runs on one GPU: the OAL hot path here is a "
+                                   "single-device kernel library; multi-GPU runs are not supported "
+                                   f"(asked for --gpus {args.gpus}, WORLD_SIZE {world})"}))
+        sys.exit(2)
+
+    import torch
+    import grouped_positive_quadratic_amd as gpq
+    from oal_synth import qwen_like, cfg5_prefix, cfg5_steps
+
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream()
+
+    # ---------------- prefill ----------------
+    B, T, C = args.batch, args.seq, args.chunk
+    inp = qwen_like(B, T, 2, name="prefill") if B > 1 or T != 4096 else qwen_like(1, 4096, 2, name="cfg2")
+    Bq, Hq, Hkv, _, _, _ = inp.dims
+    dims = gpq.make_dims(B, Hq, Hkv, "bf16")
+    hp = gpq.HeadParamsC.from_params(inp.params)
+    params, state, ws, _ = gpq.alloc_buffers(dims, T, C)
+    gpq.oal_state_init(dims, hp, params, state)
+    q = torch.from_numpy(inp.q).to(torch.bfloat16).to(dev).contiguous()
+    k = torch.from_numpy(inp.k).to(torch.bfloat16).to(dev).contiguous()
+    v = torch.from_numpy(inp.v).to(torch.bfloat16).to(dev).contiguous()
+    y = torch.empty((B, Hq, T, D), dtype=torch.float32, device=dev)
+    marks = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    for mk in marks:
+        for m in mk:
+            m.record(stream)          # create the underlying events
+    for _ in range(args.warmup):
+        gpq.oal_prefill(dims, T, C, q, k, v, params, state, ws, y)
+    torch.cuda.synchronize()
+    t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t_start.record(stream)
+    for i in range(args.steps):
+        gpq.oal_prefill_timed(dims, T, C, q, k, v, params, state, ws, y, marks[i])
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    ms_total = t_start.elapsed_time(t_end)
+    ms_step = ms_total / args.steps
+    scan_ms = float(np.mean([mk[0].elapsed_time(mk[1]) for mk in marks]))
+    read_ms = float(np.mean([mk[1].elapsed_time(mk[2]) for mk in marks]))
+    tokens = B * T
+    readout_flops = FLOP_PER_TOKEN_HEAD * tokens * Hq
+    scan_flops = FLOP_PER_TOKEN_HEAD * tokens * Hkv
+    achieved = readout_flops / (read_ms * 1e-3) / 1e12
+    traffic = None
+    if os.path.exists(args.traffic_json):
+        try:
+            tj = json.load(open(args.traffic_json))
+            key = f"readout_B{B}_T{T}_C{C}"
+            if key in tj:
+                traffic = tj[key]["bytes_per_launch"]
+        except Exception:
+            traffic = None
+    out = {
+        "metric": METRIC,
+        "value": tokens / (ms_step * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"prefill B={B} T={T} Hq={Hq} Hkv={Hkv} d=64 (Qwen2.5-0.5B-shaped layer)",
+                   "global_batch": B, "seq_len": T, "chunk": C, "parallelism": "none (1 GPU)"},
+        "roofline": {"bound": "mfma", "kernel": "oal_readout", "achieved": achieved,
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
+                     "traffic": traffic, "avg_ms": read_ms,
+                     "algorithmic_flops_per_launch": readout_flops},
+        "phases_ms": {"scan": scan_ms, "readout": read_ms},
+        "prefill_algorithmic_tflops": (readout_flops + scan_flops) / (ms_step * 1e-3) / 1e12,
+    }
+    del q, k, v, y, ws, state, params
+    torch.cuda.empty_cache()
+
+    # ---------------- decode ----------------
+    if not args.no_decode:
+        nseq, nsteps = args.decode_seqs, args.decode_steps
+        pre = cfg5_prefix(n_seq=nseq)
+        toks = cfg5_steps(n_seq=nseq, steps=nsteps)
+        ddims = gpq.make_dims(nseq, 14, 2, "bf16")
+        dhp = gpq.HeadParamsC.from_params(pre.params)
+        dparams, dstate, dws_pre, dws = gpq.alloc_buffers(ddims, 4096, 128)
+        gpq.oal_state_init(ddims, dhp, dparams, dstate)
+        pq = torch.zeros((nseq, 14, 4096, D), dtype=torch.bfloat16, device=dev)
+        pk = torch.from_numpy(pre.k).to(torch.bfloat16).to(dev).contiguous()
+        pv = torch.from_numpy(pre.v).to(torch.bfloat16).to(dev).contiguous()
+        py = torch.empty((nseq, 14, 4096, D), dtype=torch.float32, device=dev)
+        gpq.oal_prefill(ddims, 4096, 128, pq, pk, pv, dparams, dstate, dws_pre, py)
+        torch.cuda.synchronize()
+        del pq, pk, pv, py, dws_pre
+        torch.cuda.empty_cache()
+        tq = torch.from_numpy(toks.q).to(torch.bfloat16).to(dev).permute(2, 0, 1, 3).contiguous()
+        tk = torch.from_numpy(toks.k).to(torch.bfloat16).to(dev).permute(2, 0, 1, 3).contiguous()
+        tv = torch.from_numpy(toks.v).to(torch.bfloat16).to(dev).permute(2, 0, 1, 3).contiguous()
+        dy = torch.empty((nsteps, nseq, 14, D), dtype=torch.float32, device=dev)
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        ev[0].record(stream)
+        for i in range(nsteps):
+            gpq.oal_decode_step(ddims, tq[i], tk[i], tv[i], dparams, dstate, dws, dy[i])
+        ev[1].record(stream)
+        torch.cuda.synchronize()
+        dms = ev[0].elapsed_time(ev[1]) / nsteps
+        state_bytes = 2 * nseq * 2 * NFEAT * V1 * 4                   # state read + write
+        io_bytes = nseq * (14 * D * 2 + 2 * 2 * D * 2 + 14 * D * 4)   # q, k, v in; y out
+        alg = state_bytes + io_bytes
+        dach = alg / (dms * 1e-3) / 1e9
+        out["decode"] = {"value": nseq / (dms * 1e-3), "unit": "tokens/s", "ms_per_step": dms,
+                         "steps": nsteps, "config": {"workload": f"decode {nseq} seqs, 4096-token prefix states, 14q/2kv"},
+                         "roofline": {"bound": "hbm", "kernel": "oal_decode_kernel", "achieved": dach,
+                                      "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": dach / PEAK_HBM_GBS,
+                                      "traffic": None, "algorithmic_bytes_per_launch": alg}}
+
+    # ---------------- CPU oracle baseline ----------------
+    if not args.no_cpu_baseline:
+        import oracle
+        from oal_synth import cfg2
+        ref = cfg2()
+        oracle.dense(ref.q[:, :, :64], ref.k[:, :, :64], ref.v[:, :, :64], ref.params)   # load
+        t0 = time.perf_counter()
+        oracle.dense(ref.q, ref.k, ref.v, ref.params)
+        wall = time.perf_counter() - t0
+        out["cpu_baseline"] = {"value": 4096 / wall, "unit": "tokens/s", "cores": oracle.num_threads(),
+                               "kind": "oracle",
+                               "sample": "full prefill batch (B=1, T=4096, 14 q heads), dense O(T^2) fp64, 1 pass",
+                               "wall_s": wall}
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,193 @@
+"""Python binding of liboal (OAL causal attention on MI355X): argument marshalling only.
+
+Every entry point has the name of the C function in ``include/oal.h`` that it calls. Device
+buffers are torch tensors on the GPU (torch provides memory and streams, nothing else);
+all computation happens in the library's HIP kernels. Importing this module fails loudly
+when the library has not been built (``python -m grouped_positive_quadratic_amd.build``).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "liboal.so")
+
+OAL_F32, OAL_BF16 = 0, 1
+NFEAT, V1, D = 2145, 65, 64
+STATUS = {0: "OAL_OK", 1: "OAL_E_ARG", 2: "OAL_E_SHAPE", 3: "OAL_E_DTYPE", 4: "OAL_E_ALIGN",
+          5: "OAL_E_UNSUPPORTED", 6: "OAL_E_HIP"}
+EXPORTED = ("oal_params_bytes", "oal_state_bytes", "oal_prefill_workspace_bytes",
+            "oal_decode_workspace_bytes", "oal_params_pack", "oal_state_init", "oal_prefill",
+            "oal_prefill_timed", "oal_decode_step", "oal_status_string")
+
+
+class OALError(RuntimeError):
+    def __init__(self, fn: str, code: int):
+        self.code = code
+        super().__init__(f"{fn} failed: {STATUS.get(code, code)} ({status_string(code)})")
+
+
+class oal_dims(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("n_q_heads", ctypes.c_int32),
+                ("n_kv_heads", ctypes.c_int32), ("d_h", ctypes.c_int32),
+                ("d_v", ctypes.c_int32), ("dtype", ctypes.c_int32)]
+
+
+class oal_head_params(ctypes.Structure):
+    _fields_ = [("g_max", ctypes.c_int32), ("n_groups", ctypes.c_void_p),
+                ("group_of_dim", ctypes.c_void_p), ("L", ctypes.c_void_p),
+                ("eps", ctypes.c_void_p)]
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it with "
+                          "`python -m grouped_positive_quadratic_amd.build` (hipcc, gfx950)")
+    lib = ctypes.CDLL(LIB_PATH)
+    P, I, S = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
+    dp = ctypes.POINTER(oal_dims)
+    hp = ctypes.POINTER(oal_head_params)
+    lib.oal_params_bytes.argtypes, lib.oal_params_bytes.restype = [dp], S
+    lib.oal_state_bytes.argtypes, lib.oal_state_bytes.restype = [dp], S
+    lib.oal_prefill_workspace_bytes.argtypes, lib.oal_prefill_workspace_bytes.restype = [dp, I, I], S
+    lib.oal_decode_workspace_bytes.argtypes, lib.oal_decode_workspace_bytes.restype = [dp], S
+    lib.oal_params_pack.argtypes, lib.oal_params_pack.restype = [dp, hp, P, S], ctypes.c_int
+    lib.oal_state_init.argtypes, lib.oal_state_init.restype = [dp, hp, P, P, P], ctypes.c_int
+    lib.oal_prefill.argtypes = [dp, I, I, P, P, P, P, P, P, P, P]
+    lib.oal_prefill.restype = ctypes.c_int
+    lib.oal_prefill_timed.argtypes = [dp, I, I, P, P, P, P, P, P, P, P, ctypes.POINTER(P)]
+    lib.oal_prefill_timed.restype = ctypes.c_int
+    lib.oal_decode_step.argtypes = [dp, P, P, P, P, P, P, P, P]
+    lib.oal_decode_step.restype = ctypes.c_int
+    lib.oal_status_string.argtypes, lib.oal_status_string.restype = [ctypes.c_int], ctypes.c_char_p
+    return lib
+
+
+_lib = _load()
+
+
+def status_string(code: int) -> str:
+    return _lib.oal_status_string(int(code)).decode()
+
+
+def make_dims(batch: int, n_q_heads: int, n_kv_heads: int, dtype: str = "bf16",
+              d_h: int = 64, d_v: int = 64) -> oal_dims:
+    dt = {"bf16": OAL_BF16, "f32": OAL_F32}.get(dtype, dtype)
+    return oal_dims(int(batch), int(n_q_heads), int(n_kv_heads), int(d_h), int(d_v), int(dt))
+
+
+class HeadParamsC:
+    """Host arrays of the per-head parameters, kept alive for the duration of a call."""
+
+    def __init__(self, n_groups, group_of_dim, L, eps):
+        self.n_groups = np.ascontiguousarray(n_groups, dtype=np.int32)
+        self.group_of_dim = np.ascontiguousarray(group_of_dim, dtype=np.uint8)
+        self.L = np.ascontiguousarray(L, dtype=np.float32)
+        self.eps = np.ascontiguousarray(eps, dtype=np.float32)
+        self.c = oal_head_params(int(self.L.shape[1]) - 1,
+                                 self.n_groups.ctypes.data, self.group_of_dim.ctypes.data,
+                                 self.L.ctypes.data, self.eps.ctypes.data)
+
+    @classmethod
+    def from_params(cls, p) -> "HeadParamsC":
+        return cls(p.n_groups, p.group_of_dim, p.L, p.eps)
+
+
+def _ptr(t) -> int | None:
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    if not t.is_cuda:
+        raise ValueError("device buffers must be GPU tensors")
+    if not t.is_contiguous():
+        raise ValueError("device buffers must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(stream):
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _check(fn: str, code: int):
+    if code != 0:
+        raise OALError(fn, code)
+
+
+# ---- sizes -----------------------------------------------------------------------------
+
+def oal_params_bytes(dims: oal_dims) -> int:
+    return int(_lib.oal_params_bytes(ctypes.byref(dims)))
+
+
+def oal_state_bytes(dims: oal_dims) -> int:
+    return int(_lib.oal_state_bytes(ctypes.byref(dims)))
+
+
+def oal_prefill_workspace_bytes(dims: oal_dims, T: int, chunk: int) -> int:
+    return int(_lib.oal_prefill_workspace_bytes(ctypes.byref(dims), int(T), int(chunk)))
+
+
+def oal_decode_workspace_bytes(dims: oal_dims) -> int:
+    return int(_lib.oal_decode_workspace_bytes(ctypes.byref(dims)))
+
+
+# ---- calls -----------------------------------------------------------------------------
+
+def oal_params_pack(dims: oal_dims, params: HeadParamsC) -> np.ndarray:
+    """Host-side parameter blob (uint8 array) exactly as oal_state_init uploads it."""
+    n = oal_params_bytes(dims)
+    blob = np.zeros(max(n, 1), dtype=np.uint8)
+    _check("oal_params_pack", _lib.oal_params_pack(ctypes.byref(dims), ctypes.byref(params.c),
+                                                   blob.ctypes.data, n))
+    return blob[:n]
+
+
+def oal_state_init(dims: oal_dims, params: HeadParamsC, params_dev, state_dev=None, stream=None):
+    _check("oal_state_init", _lib.oal_state_init(ctypes.byref(dims), ctypes.byref(params.c),
+                                                 _ptr(params_dev), _ptr(state_dev), _stream(stream)))
+
+
+def oal_prefill(dims: oal_dims, T: int, chunk: int, q, k, v, params_dev, state_dev, workspace, y,
+                stream=None):
+    _check("oal_prefill", _lib.oal_prefill(ctypes.byref(dims), int(T), int(chunk), _ptr(q), _ptr(k),
+                                           _ptr(v), _ptr(params_dev), _ptr(state_dev),
+                                           _ptr(workspace), _ptr(y), _stream(stream)))
+
+
+def oal_prefill_timed(dims: oal_dims, T: int, chunk: int, q, k, v, params_dev, state_dev, workspace,
+                      y, marks, stream=None):
+    """oal_prefill plus three caller-owned events (torch.cuda.Event, already created) recorded
+    before the scan, between scan and readout, and after the readout."""
+    handles = (ctypes.c_void_p * 3)(*[int(m.cuda_event) for m in marks])
+    _check("oal_prefill_timed", _lib.oal_prefill_timed(
+        ctypes.byref(dims), int(T), int(chunk), _ptr(q), _ptr(k), _ptr(v), _ptr(params_dev),
+        _ptr(state_dev), _ptr(workspace), _ptr(y), _stream(stream), handles))
+
+
+def oal_decode_step(dims: oal_dims, q, k, v, params_dev, state_dev, workspace, y, stream=None):
+    _check("oal_decode_step", _lib.oal_decode_step(ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v),
+                                                   _ptr(params_dev), _ptr(state_dev),
+                                                   _ptr(workspace), _ptr(y), _stream(stream)))
+
+
+# ---- buffer helper (torch allocations sized by the library) ------------------------------
+
+def alloc_buffers(dims: oal_dims, T: int = 0, chunk: int = 128, device: str = "cuda"):
+    """Allocate params, state, prefill workspace and a zeroed decode workspace (uint8/fp32 tensors)."""
+    import torch
+    nb = lambda n: max(int(n), 16)
+    params = torch.empty(nb(oal_params_bytes(dims)), dtype=torch.uint8, device=device)
+    state = torch.empty(nb(oal_state_bytes(dims)) // 4, dtype=torch.float32, device=device)
+    ws = torch.empty(nb(oal_prefill_workspace_bytes(dims, T, chunk)) if T else 16,
+                     dtype=torch.uint8, device=device)
+    dws = torch.zeros(nb(oal_decode_workspace_bytes(dims)), dtype=torch.uint8, device=device)
+    return params, state, ws, dws

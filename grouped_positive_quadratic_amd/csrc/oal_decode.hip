@@ -1,0 +1,192 @@
+// oal_decode.hip -- one decode step: stream each (sequence, KV head) state once.
+//
+// For the new token (reproduction notes of arXiv 2610.13674, section "核心公式"):
+//   H <- H + psi(k) [v;1]^T           (prefix-state recurrence, H_i = H_{i-1} + term_i)
+//   u~_h = phi_h(q_h) . H   for every query head h of the KV head (readout display)
+//   y_h = u~_h[0:64] / u~_h[64]
+// with psi(k) = [1, k_r, k_r k_t (r <= t)] and phi_h(q) = wdec_h o [1, q_r, q_r q_t].
+//
+// The state row f of a KV head holds 65 floats. Workgroup (split, bkv) owns rows
+// [256 split, 256 split + 256): wave w walks 64 of them with lane c on column c (one
+// coalesced 256-byte row read and write per step), then column 64 of the same rows with
+// lane = row. Every byte of the state is read once and written once. Readout partial sums
+// per split go to the workspace; the last workgroup of a (sequence, KV head) to arrive sums
+// the splits in a fixed order, divides and writes y, then resets the arrival counter.
+#include <hip/hip_runtime.h>
+
+#include "oal.h"
+#include "oal_device.h"
+#include "oal_internal.h"
+
+namespace {
+
+constexpr int kRows = 256;          // state rows per workgroup
+constexpr int kThreads = 256;
+constexpr int kSplits = (OAL_NFEAT + kRows - 1) / kRows;
+
+__device__ inline void row_dims(int f, int &r, int &t) {
+    if (f == 0) { r = -1; t = -1; return; }
+    if (f <= OAL_D) { r = f - 1; t = -1; return; }
+    int i = f - 1 - OAL_D, rr = 0;
+    while (i >= OAL_D - rr) { i -= OAL_D - rr; ++rr; }
+    r = rr;
+    t = rr + i;
+}
+
+template <typename T, int MAXH>
+__global__ __launch_bounds__(kThreads) void oal_decode_kernel(
+    int n_q_heads, int n_kv_heads, const T *__restrict__ q, const T *__restrict__ k,
+    const T *__restrict__ v, const unsigned char *__restrict__ params, float *__restrict__ state,
+    float *__restrict__ partial, unsigned int *__restrict__ counters, float *__restrict__ y) {
+    const int split = blockIdx.x;
+    const int bkv = blockIdx.y;
+    const int b = bkv / n_kv_heads, kv = bkv % n_kv_heads;
+    const int n_rep = n_q_heads / n_kv_heads;
+    const int h0 = kv * n_rep;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int f0 = split * kRows;
+    const int nrows = min(kRows, OAL_NFEAT - f0);
+
+    __shared__ float s_k[OAL_D];
+    __shared__ float s_q[MAXH][OAL_D];
+    __shared__ float s_psi[kRows];
+    __shared__ __align__(16) float s_phi[kRows][MAXH];
+    __shared__ float s_red[4][MAXH][OAL_V1];
+    __shared__ int s_last;
+
+    if (tid < OAL_D) s_k[tid] = oal_ld(k + (size_t)bkv * OAL_D + tid);
+    for (int idx = tid; idx < n_rep * OAL_D; idx += kThreads)
+        s_q[idx / OAL_D][idx % OAL_D] = oal_ld(q + ((size_t)b * n_q_heads + h0) * OAL_D + idx);
+    __syncthreads();
+
+    // features of this workgroup's rows: psi (key) and phi_h (query, with coefficient)
+    for (int rr = tid; rr < kRows; rr += kThreads) {
+        int f = f0 + rr;
+        float psi = 0.0f;
+        if (rr < nrows) {
+            int r, t;
+            row_dims(f, r, t);
+            psi = (r < 0) ? 1.0f : (t < 0 ? s_k[r] : s_k[r] * s_k[t]);
+#pragma unroll
+            for (int h = 0; h < MAXH; ++h) {
+                float ph = 0.0f;
+                if (h < n_rep) {
+                    const OalHeadDev *hd = reinterpret_cast<const OalHeadDev *>(
+                        params + sizeof(OalParamsHeader) + (size_t)(h0 + h) * OAL_HEAD_BYTES);
+                    float mono = (r < 0) ? 1.0f : (t < 0 ? s_q[h][r] : s_q[h][r] * s_q[h][t]);
+                    ph = hd->wdec[f] * mono;
+                }
+                s_phi[rr][h] = ph;
+            }
+        } else {
+#pragma unroll
+            for (int h = 0; h < MAXH; ++h) s_phi[rr][h] = 0.0f;
+        }
+        s_psi[rr] = psi;
+    }
+    __syncthreads();
+
+    float *S = state + (size_t)bkv * OAL_NFEAT * OAL_V1;
+    const float vv = oal_ld(v + (size_t)bkv * OAL_D + lane);
+    float acc[MAXH], accd[MAXH];
+#pragma unroll
+    for (int h = 0; h < MAXH; ++h) { acc[h] = 0.0f; accd[h] = 0.0f; }
+
+    const int rbeg = wave * 64, rend = min(nrows, rbeg + 64);
+    for (int rr = rbeg; rr < rend; rr += 8) {
+        float s[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+            s[u] = (rr + u < rend) ? S[(size_t)(f0 + rr + u) * OAL_V1 + lane] : 0.0f;
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            if (rr + u < rend) {
+                s[u] += s_psi[rr + u] * vv;
+                S[(size_t)(f0 + rr + u) * OAL_V1 + lane] = s[u];
+#pragma unroll
+                for (int h = 0; h < MAXH; ++h) acc[h] += s_phi[rr + u][h] * s[u];
+            }
+        }
+    }
+    // column 64 ("1" of [v;1]) of the same rows, lane = row
+    {
+        int rr = rbeg + lane;
+        if (rr < rend) {
+            float *p = S + (size_t)(f0 + rr) * OAL_V1 + OAL_D;
+            float s = *p + s_psi[rr];
+            *p = s;
+#pragma unroll
+            for (int h = 0; h < MAXH; ++h) accd[h] += s_phi[rr][h] * s;
+        }
+    }
+#pragma unroll
+    for (int h = 0; h < MAXH; ++h) {
+        float x = accd[h];
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off);
+        s_red[wave][h][lane] = acc[h];
+        if (lane == 0) s_red[wave][h][OAL_D] = x;
+    }
+    __syncthreads();
+    float *mypart = partial + ((size_t)bkv * kSplits + split) * MAXH * OAL_V1;
+    for (int idx = tid; idx < n_rep * OAL_V1; idx += kThreads) {
+        int h = idx / OAL_V1, c = idx % OAL_V1;
+        mypart[idx] = s_red[0][h][c] + s_red[1][h][c] + s_red[2][h][c] + s_red[3][h][c];
+    }
+    __threadfence();
+    __syncthreads();
+    if (tid == 0) {
+        unsigned int old = atomicAdd(counters + bkv, 1u);
+        s_last = (old == (unsigned int)(kSplits - 1));
+    }
+    __syncthreads();
+    if (!s_last) return;
+    __threadfence();
+    const float *allpart = partial + (size_t)bkv * kSplits * MAXH * OAL_V1;
+    for (int idx = tid; idx < n_rep * OAL_D; idx += kThreads) {
+        int h = idx / OAL_D, c = idx % OAL_D;
+        float num = 0.0f, den = 0.0f;
+        for (int sp = 0; sp < kSplits; ++sp) {
+            const volatile float *pp = allpart + (size_t)sp * MAXH * OAL_V1 + h * OAL_V1;
+            num += pp[c];
+            den += pp[OAL_D];
+        }
+        y[((size_t)b * n_q_heads + h0 + h) * OAL_D + c] = num / den;
+    }
+    if (tid == 0) atomicExch(counters + bkv, 0u);
+}
+
+template <typename T, int MAXH>
+hipError_t launch(const oal_dims &d, const void *q, const void *k, const void *v,
+                  const void *params, float *state, void *ws, float *y, hipStream_t stream) {
+    int bkv = d.batch * d.n_kv_heads;
+    unsigned int *counters = reinterpret_cast<unsigned int *>(ws);
+    size_t cbytes = ((size_t)bkv * sizeof(unsigned int) + 255) / 256 * 256;
+    float *partial = reinterpret_cast<float *>(reinterpret_cast<char *>(ws) + cbytes);
+    dim3 grid(kSplits, bkv);
+    hipLaunchKernelGGL((oal_decode_kernel<T, MAXH>), grid, dim3(kThreads), 0, stream, d.n_q_heads,
+                       d.n_kv_heads, reinterpret_cast<const T *>(q), reinterpret_cast<const T *>(k),
+                       reinterpret_cast<const T *>(v),
+                       reinterpret_cast<const unsigned char *>(params), state, partial, counters, y);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+size_t oal_decode_ws_bytes_impl(const oal_dims &d) {
+    size_t bkv = (size_t)d.batch * d.n_kv_heads;
+    size_t cbytes = (bkv * sizeof(unsigned int) + 255) / 256 * 256;
+    return cbytes + bkv * kSplits * 16 * OAL_V1 * sizeof(float);
+}
+
+hipError_t oal_launch_decode(const oal_dims &d, const void *q, const void *k, const void *v,
+                             const void *params, float *state, void *ws, float *y,
+                             hipStream_t stream) {
+    int n_rep = d.n_q_heads / d.n_kv_heads;
+    if (d.dtype == OAL_BF16) {
+        if (n_rep <= 8) return launch<__bf16, 8>(d, q, k, v, params, state, ws, y, stream);
+        return launch<__bf16, 16>(d, q, k, v, params, state, ws, y, stream);
+    }
+    if (n_rep <= 8) return launch<float, 8>(d, q, k, v, params, state, ws, y, stream);
+    return launch<float, 16>(d, q, k, v, params, state, ws, y, stream);
+}

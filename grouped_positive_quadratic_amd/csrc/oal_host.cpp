@@ -1,0 +1,253 @@
+// oal_host.cpp -- C ABI: argument validation, coefficient tables, kernel launches.
+//
+// Coefficients (reproduction notes of arXiv 2610.13674, section "核心公式"): the kernel
+// kappa = eps + s-bar^T M s-bar with M = L L^T expands, with s_g = sum_{r in g} q_r k_r / 8,
+// into the readout's a H0 + (1/8) sum_r b_r q_r H1_r + (1/64) sum_rt C_rt q_r q_t H2_rt with
+//   a = eps + M_00,  b_r = 2 M_{0,g(r)},  C_rt = M_{g(r),g(t)}   (g(r): s-bar index of dim r)
+// All of it is computed here in fp64 and rounded once to fp32.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstring>
+#include <vector>
+
+#include "oal.h"
+#include "oal_internal.h"
+
+hipError_t oal_launch_decode(const oal_dims &d, const void *q, const void *k, const void *v,
+                             const void *params, float *state, void *ws, float *y, hipStream_t stream);
+hipError_t oal_launch_prefill(const oal_dims &d, int T_len, int C, const void *q, const void *k,
+                              const void *v, const void *params, float *state, void *ws, float *y,
+                              hipStream_t stream, hipEvent_t *marks);
+size_t oal_decode_ws_bytes_impl(const oal_dims &d);
+size_t oal_prefill_ws_bytes_impl(const oal_dims &d, int T_len, int C);
+
+namespace {
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+oal_status check_dims(const oal_dims *d) {
+    if (!d) return OAL_E_ARG;
+    if (d->dtype != OAL_F32 && d->dtype != OAL_BF16) return OAL_E_DTYPE;
+    if (d->batch < 0 || d->n_q_heads < 1 || d->n_kv_heads < 1 || d->d_h < 1 || d->d_v < 1)
+        return OAL_E_SHAPE;
+    if (d->n_q_heads % d->n_kv_heads) return OAL_E_SHAPE;
+    if (d->d_h != OAL_D || d->d_v != OAL_D) return OAL_E_UNSUPPORTED;
+    if ((long long)d->batch * d->n_kv_heads > 65535) return OAL_E_UNSUPPORTED;
+    return OAL_OK;
+}
+
+oal_status check_params(const oal_dims *d, const oal_head_params *hp) {
+    if (!hp || !hp->n_groups || !hp->group_of_dim || !hp->L || !hp->eps) return OAL_E_ARG;
+    if (hp->g_max < 1 || hp->g_max > OAL_MAX_G) return OAL_E_ARG;
+    const int gm1 = hp->g_max + 1;
+    for (int h = 0; h < d->n_q_heads; ++h) {
+        int G = hp->n_groups[h];
+        if (G < 1 || G > d->d_h || G > hp->g_max) return OAL_E_ARG;
+        for (int r = 0; r < d->d_h; ++r)
+            if (hp->group_of_dim[(size_t)h * d->d_h + r] >= G) return OAL_E_ARG;
+        float e = hp->eps[h];
+        if (!(e >= 0.0f) || !std::isfinite(e)) return OAL_E_ARG;
+        const float *Lh = hp->L + (size_t)h * gm1 * gm1;
+        for (int a = 0; a <= G; ++a)
+            for (int b = 0; b <= a; ++b)
+                if (!std::isfinite(Lh[a * gm1 + b])) return OAL_E_ARG;
+    }
+    return OAL_OK;
+}
+
+void pack_head(const oal_head_params *hp, int h, OalHeadDev *out) {
+    const int gm1 = hp->g_max + 1;
+    const int G = hp->n_groups[h];
+    const float *Lh = hp->L + (size_t)h * gm1 * gm1;
+    const uint8_t *gam = hp->group_of_dim + (size_t)h * OAL_D;
+    // lower triangle of L (rows/cols 0..G), fp64
+    std::vector<double> L((G + 1) * (G + 1), 0.0), M((G + 1) * (G + 1), 0.0);
+    for (int a = 0; a <= G; ++a)
+        for (int b = 0; b <= a; ++b) L[a * (G + 1) + b] = Lh[a * gm1 + b];
+    for (int a = 0; a <= G; ++a)
+        for (int b = 0; b <= G; ++b) {
+            double s = 0.0;
+            for (int m = 0; m <= G; ++m) s += L[a * (G + 1) + m] * L[b * (G + 1) + m];
+            M[a * (G + 1) + b] = s;
+        }
+    auto Mq = [&](int a, int b) { return M[(a + 1) * (G + 1) + (b + 1)]; };  // config ids
+    // bulk group: most dims (lowest id on ties)
+    int count[OAL_MAX_G] = {0};
+    for (int r = 0; r < OAL_D; ++r) count[gam[r]]++;
+    int bulk = 0;
+    for (int g = 1; g < G; ++g)
+        if (count[g] > count[bulk]) bulk = g;
+    // rank-1 factor through the bulk column of the group block of M
+    std::vector<double> w0(G, 0.0);
+    double mbb = Mq(bulk, bulk);
+    if (mbb > 0.0) {
+        double sq = std::sqrt(mbb);
+        for (int a = 0; a < G; ++a) w0[a] = Mq(a, bulk) / sq;
+    }
+    std::memset(out, 0, sizeof(OalHeadDev));
+    out->G = G;
+    out->bulk = bulk;
+    out->eps = hp->eps[h];
+    out->a = (float)((double)hp->eps[h] + M[0]);
+    out->L00 = (float)L[0];
+    for (int r = 0; r < OAL_D; ++r) {
+        out->gamma[r] = gam[r];
+        out->lin[r] = (float)(2.0 * M[0 * (G + 1) + 1 + gam[r]]);
+        out->w0[r] = (float)w0[gam[r]];
+    }
+    for (int a = 0; a < G; ++a)
+        for (int b = 0; b < G; ++b)
+            out->Dg[a * OAL_D + b] = (a == bulk || b == bulk) ? 0.0f : (float)(Mq(a, b) - w0[a] * w0[b]);
+    for (int m = 0; m <= G; ++m)
+        for (int r = 0; r < OAL_D; ++r) {
+            int gr = 1 + gam[r];
+            out->Lz[m * OAL_D + r] = gr >= m ? (float)(L[gr * (G + 1) + m] / 8.0) : 0.0f;
+        }
+    // decode coefficients per state row
+    out->wdec[0] = out->a;
+    for (int r = 0; r < OAL_D; ++r) out->wdec[1 + r] = (float)(2.0 * M[1 + gam[r]] / 8.0);
+    for (int r = 0; r < OAL_D; ++r)
+        for (int t = r; t < OAL_D; ++t)
+            out->wdec[oal_quad_row(r, t)] = (float)((r < t ? 2.0 : 1.0) * Mq(gam[r], gam[t]) / 64.0);
+    // K-steps of the prefill slot order that hold a non-bulk x non-bulk pair
+    for (int tb = 0; tb < 8; ++tb)
+        for (int rq = 0; rq <= 2 * tb + 1; ++rq)
+            for (int g = 0; g < 4; ++g)
+                for (int e = 0; e < 8; ++e) {
+                    int ra, rb;
+                    if (oal_slot_kind(tb, rq, g, e, &ra, &rb) != OAL_SLOT_QUAD) continue;
+                    if (out->Dg[gam[ra] * OAL_D + gam[rb]] != 0.0f) {
+                        int s = oal_kstep(tb, rq);
+                        out->corr[s >> 5] |= 1u << (s & 31);
+                    }
+                }
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *oal_status_string(oal_status s) {
+    switch (s) {
+    case OAL_OK: return "ok";
+    case OAL_E_ARG: return "invalid argument";
+    case OAL_E_SHAPE: return "inconsistent shape";
+    case OAL_E_DTYPE: return "unsupported dtype";
+    case OAL_E_ALIGN: return "device pointer not 16-byte aligned";
+    case OAL_E_UNSUPPORTED: return "unsupported configuration";
+    case OAL_E_HIP: return "HIP runtime error";
+    }
+    return "unknown status";
+}
+
+size_t oal_params_bytes(const oal_dims *d) {
+    if (check_dims(d) != OAL_OK) return 0;
+    return sizeof(OalParamsHeader) + (size_t)d->n_q_heads * OAL_HEAD_BYTES;
+}
+
+size_t oal_state_bytes(const oal_dims *d) {
+    if (check_dims(d) != OAL_OK) return 0;
+    return (size_t)d->batch * d->n_kv_heads * OAL_NFEAT * OAL_V1 * sizeof(float);
+}
+
+size_t oal_prefill_workspace_bytes(const oal_dims *d, int32_t T, int32_t chunk) {
+    if (check_dims(d) != OAL_OK || T < 0) return 0;
+    if (chunk != 64 && chunk != 128 && chunk != 256) return 0;
+    if (T == 0 || d->batch == 0) return 0;
+    return oal_prefill_ws_bytes_impl(*d, T, chunk);
+}
+
+size_t oal_decode_workspace_bytes(const oal_dims *d) {
+    if (check_dims(d) != OAL_OK) return 0;
+    if (d->n_q_heads / d->n_kv_heads > 16) return 0;
+    return oal_decode_ws_bytes_impl(*d);
+}
+
+oal_status oal_params_pack(const oal_dims *d, const oal_head_params *hp, void *blob, size_t bytes) {
+    oal_status st = check_dims(d);
+    if (st != OAL_OK) return st;
+    if (!blob) return OAL_E_ARG;
+    if ((st = check_params(d, hp)) != OAL_OK) return st;
+    if (bytes < oal_params_bytes(d)) return OAL_E_ARG;
+    unsigned char *p = static_cast<unsigned char *>(blob);
+    std::memset(p, 0, oal_params_bytes(d));
+    OalParamsHeader *hdr = reinterpret_cast<OalParamsHeader *>(p);
+    hdr->magic = OAL_PARAMS_MAGIC;
+    hdr->n_q_heads = d->n_q_heads;
+    hdr->d_h = d->d_h;
+    hdr->d_v = d->d_v;
+    hdr->head_bytes = OAL_HEAD_BYTES;
+    for (int h = 0; h < d->n_q_heads; ++h)
+        pack_head(hp, h, reinterpret_cast<OalHeadDev *>(p + sizeof(OalParamsHeader) + (size_t)h * OAL_HEAD_BYTES));
+    return OAL_OK;
+}
+
+oal_status oal_state_init(const oal_dims *d, const oal_head_params *hp, void *params_dev,
+                          float *state_dev, hipStream_t stream) {
+    oal_status st = check_dims(d);
+    if (st != OAL_OK) return st;
+    if (!params_dev) return OAL_E_ARG;
+    if (!aligned16(params_dev) || (state_dev && !aligned16(state_dev))) return OAL_E_ALIGN;
+    if ((st = check_params(d, hp)) != OAL_OK) return st;
+    size_t bytes = oal_params_bytes(d);
+    std::vector<unsigned char> blob(bytes);
+    if ((st = oal_params_pack(d, hp, blob.data(), bytes)) != OAL_OK) return st;
+    if (hipMemcpyAsync(params_dev, blob.data(), bytes, hipMemcpyHostToDevice, stream) != hipSuccess)
+        return OAL_E_HIP;
+    if (state_dev && oal_state_bytes(d) > 0 &&
+        hipMemsetAsync(state_dev, 0, oal_state_bytes(d), stream) != hipSuccess)
+        return OAL_E_HIP;
+    if (hipStreamSynchronize(stream) != hipSuccess) return OAL_E_HIP;
+    return OAL_OK;
+}
+
+static oal_status prefill_impl(const oal_dims *d, int32_t T, int32_t chunk, const void *q,
+                               const void *k, const void *v, const void *params_dev,
+                               float *state_dev, void *workspace, float *y, hipStream_t stream,
+                               hipEvent_t *marks) {
+    oal_status st = check_dims(d);
+    if (st != OAL_OK) return st;
+    if (T < 0) return OAL_E_SHAPE;
+    if (chunk != 64 && chunk != 128 && chunk != 256) return OAL_E_UNSUPPORTED;
+    if (T == 0 || d->batch == 0) return OAL_OK;
+    if (!q || !k || !v || !params_dev || !state_dev || !workspace || !y) return OAL_E_ARG;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(params_dev) ||
+        !aligned16(state_dev) || !aligned16(workspace) || !aligned16(y))
+        return OAL_E_ALIGN;
+    if ((T + chunk - 1) / chunk > 65535) return OAL_E_UNSUPPORTED;
+    hipError_t e = oal_launch_prefill(*d, T, chunk, q, k, v, params_dev, state_dev, workspace, y,
+                                      stream, marks);
+    return e == hipSuccess ? OAL_OK : OAL_E_HIP;
+}
+
+oal_status oal_prefill(const oal_dims *d, int32_t T, int32_t chunk, const void *q, const void *k,
+                       const void *v, const void *params_dev, float *state_dev, void *workspace,
+                       float *y, hipStream_t stream) {
+    return prefill_impl(d, T, chunk, q, k, v, params_dev, state_dev, workspace, y, stream, nullptr);
+}
+
+oal_status oal_prefill_timed(const oal_dims *d, int32_t T, int32_t chunk, const void *q,
+                             const void *k, const void *v, const void *params_dev,
+                             float *state_dev, void *workspace, float *y, hipStream_t stream,
+                             hipEvent_t marks[3]) {
+    if (!marks || !marks[0] || !marks[1] || !marks[2]) return OAL_E_ARG;
+    return prefill_impl(d, T, chunk, q, k, v, params_dev, state_dev, workspace, y, stream, marks);
+}
+
+oal_status oal_decode_step(const oal_dims *d, const void *q, const void *k, const void *v,
+                           const void *params_dev, float *state_dev, void *workspace, float *y,
+                           hipStream_t stream) {
+    oal_status st = check_dims(d);
+    if (st != OAL_OK) return st;
+    if (d->n_q_heads / d->n_kv_heads > 16) return OAL_E_UNSUPPORTED;
+    if (d->batch == 0) return OAL_OK;
+    if (!q || !k || !v || !params_dev || !state_dev || !workspace || !y) return OAL_E_ARG;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(params_dev) ||
+        !aligned16(state_dev) || !aligned16(workspace) || !aligned16(y))
+        return OAL_E_ALIGN;
+    hipError_t e = oal_launch_decode(*d, q, k, v, params_dev, state_dev, workspace, y, stream);
+    return e == hipSuccess ? OAL_OK : OAL_E_HIP;
+}
+
+}  // extern "C"

@@ -1,0 +1,156 @@
+/*
+ * oal.h -- C ABI of the OAL causal-attention library for AMD Instinct MI355X (gfx950).
+ *
+ * What it computes (reproduction notes of arXiv 2610.13674 on daiwk.github.io, section
+ * "核心公式"; arXiv abstract page of 2610.13674v1):
+ *
+ *   per query head h with KV head kv = h / (n_q_heads / n_kv_heads) (contiguous GQA map):
+ *     s_g    = sum_{r in group g} q_r k_r / sqrt(d_h),   s-bar = [1, s_1, ..., s_G]
+ *     kappa  = eps_h + s-bar^T L_h L_h^T s-bar            (> 0 by the PSD parameterisation)
+ *     y_i    = sum_{j<=i} kappa(q_i,k_j) v_j / sum_{j<=i} kappa(q_i,k_j)
+ *   evaluated in linear time through the prefix states of the KV head
+ *     H0 = sum_{j<=i} [v_j;1],  H1_r = sum k_{j,r} [v_j;1],  H2_rt = sum k_{j,r} k_{j,t} [v_j;1]
+ *   and the readout u~_i = a H0 + (1/sqrt d_h) sum_r b_r q_r H1_r + (1/d_h) sum_rt C_rt q_r q_t H2_rt,
+ *   y_i = u~_i[0:d_v] / u~_i[d_v], with a = eps + M_00, b_r = 2 M_{0,g(r)}, C_rt = M_{g(r),g(t)},
+ *   M = L L^T (the expansion of s-bar^T M s-bar; g(r) = s-bar index of dim r's group).
+ *
+ * Version 1 supports d_h = d_v = 64, q/k/v in fp32 or bf16 (fp32 accumulation), y in fp32.
+ *
+ * Layouts (all row-major, contiguous, device memory unless stated otherwise):
+ *   q      [batch, n_q_heads,  T, 64]  dtype of oal_dims.dtype
+ *   k, v   [batch, n_kv_heads, T, 64]
+ *   y      [batch, n_q_heads,  T, 64]  fp32
+ *   state  [batch, n_kv_heads, 2145, 65] fp32: the prefix states of each (sequence, KV head).
+ *          Row 0 = H0; rows 1..64 = H1_r (r = 0..63); rows 65.. = H2_rt for r <= t in
+ *          row-major order of the upper triangle (the symmetric H2 stored once, r < t not
+ *          doubled). Columns 0..63 = components of v, column 64 = the "1" of [v;1].
+ *   For a decode step T = 1 and the T axis is dropped: q [batch, n_q_heads, 64] etc.
+ *
+ * Ownership: the caller allocates and owns every device buffer (params, state, workspace,
+ * q, k, v, y). The library allocates no memory in oal_prefill / oal_decode_step and keeps
+ * no global mutable state. Host arrays passed in oal_head_params are read during the call.
+ *
+ * Streams: every call enqueues work on `stream` and returns; the caller synchronises.
+ * oal_state_init additionally waits for its host-to-device copy before returning.
+ *
+ * Errors: arguments are validated on the host before anything is enqueued; on any error
+ * nothing is enqueued and a status code is returned. HIP launch failures map to OAL_E_HIP.
+ * NaN/Inf in q, k, v propagate to y. eps = 0 together with a singular L can make a
+ * denominator zero; y is then NaN or Inf for that row (kappa > 0 needs eps > 0 or L L^T PD).
+ */
+#ifndef OAL_H
+#define OAL_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    OAL_OK = 0,
+    OAL_E_ARG = 1,          /* null pointer or invalid scalar argument */
+    OAL_E_SHAPE = 2,        /* inconsistent sizes (n_q_heads % n_kv_heads != 0, T < 0, ...) */
+    OAL_E_DTYPE = 3,        /* dtype is not OAL_F32 / OAL_BF16 */
+    OAL_E_ALIGN = 4,        /* a device pointer is not 16-byte aligned */
+    OAL_E_UNSUPPORTED = 5,  /* valid but not implemented (d_h or d_v != 64, chunk size) */
+    OAL_E_HIP = 6           /* a HIP runtime call or kernel launch failed */
+} oal_status;
+
+typedef enum { OAL_F32 = 0, OAL_BF16 = 1 } oal_dtype;
+
+typedef struct {
+    int32_t batch;       /* sequences (>= 0) */
+    int32_t n_q_heads;   /* query heads (>= 1) */
+    int32_t n_kv_heads;  /* KV heads (>= 1, divides n_q_heads) */
+    int32_t d_h;         /* q/k head dim (64) */
+    int32_t d_v;         /* v head dim (64) */
+    int32_t dtype;       /* oal_dtype of q, k, v */
+} oal_dims;
+
+/* Per-query-head kernel parameters (host memory, read during the call).
+ * The group map and L are those of the kernel kappa = eps + s-bar^T L L^T s-bar
+ * (reproduction notes, section "核心公式", kernel display; Figure 2(a) for the bulk + tail
+ * grouping). There is no cap on the number of groups other than G <= d_h. */
+typedef struct {
+    int32_t g_max;               /* max G over heads, 1..64; L's per-head stride is (g_max+1)^2 */
+    const int32_t *n_groups;     /* [n_q_heads]: G_h in 1..d_h and <= g_max */
+    const uint8_t *group_of_dim; /* [n_q_heads][d_h]: config group id of each dim, < G_h;
+                                    config group g is entry g+1 of s-bar. Empty groups allowed. */
+    const float *L;              /* [n_q_heads][g_max+1][g_max+1] row-major; the lower triangle
+                                    (rows/cols 0..G_h) is read, the rest ignored. Row/column 0
+                                    belong to the constant entry of s-bar. Zero or negative
+                                    diagonal entries are accepted. Must be finite. */
+    const float *eps;            /* [n_q_heads]: eps_h >= 0, finite */
+} oal_head_params;
+
+/* Bytes of the device parameter blob (coefficient tables for every query head). */
+size_t oal_params_bytes(const oal_dims *dims);
+
+/* Bytes of the state buffer: batch * n_kv_heads * 2145 * 65 * 4. */
+size_t oal_state_bytes(const oal_dims *dims);
+
+/* Bytes of the scratch buffer oal_prefill needs for T tokens at this chunk size
+ * (per-chunk state snapshots and per-segment partial states). 0 on invalid input. */
+size_t oal_prefill_workspace_bytes(const oal_dims *dims, int32_t T, int32_t chunk);
+
+/* Bytes of the scratch buffer oal_decode_step needs (per-split partial readouts and one
+ * arrival counter per (sequence, KV head, head group)). */
+size_t oal_decode_workspace_bytes(const oal_dims *dims);
+
+/* Build the parameter blob in HOST memory (what oal_state_init uploads). `blob` must hold
+ * oal_params_bytes(dims) bytes. Runs on the CPU only; no device is needed. */
+oal_status oal_params_pack(const oal_dims *dims, const oal_head_params *hp, void *blob,
+                           size_t blob_bytes);
+
+/* Validate the parameters, upload the parameter blob to `params_dev`
+ * (oal_params_bytes(dims) bytes, device) and zero `state_dev` (oal_state_bytes(dims) bytes,
+ * device; may be NULL to leave it untouched). A zero state is an empty prefix. */
+oal_status oal_state_init(const oal_dims *dims, const oal_head_params *hp, void *params_dev,
+                          float *state_dev, hipStream_t stream);
+
+/* Chunked causal prefill of T new tokens per sequence, continuing from `state_dev`.
+ *   chunk      -- chunk length C in {64, 128, 256}: the tokens of a chunk see the state
+ *                 before the chunk plus an exact intra-chunk kernel sum.
+ *   q, k, v    -- [batch, heads, T, 64] of dims->dtype (device).
+ *   state_dev  -- in: prefix states of the tokens before these T; out: states after them.
+ *   workspace  -- oal_prefill_workspace_bytes(dims, T, chunk) bytes of device scratch. Its
+ *                 contents on entry do not matter.
+ *   y          -- [batch, n_q_heads, T, 64] fp32 output (device).
+ * Position i of this call attends to every earlier token of the sequence (those folded
+ * into the input state and tokens 0..i of this call). T = 0 is a no-op. */
+oal_status oal_prefill(const oal_dims *dims, int32_t T, int32_t chunk, const void *q,
+                       const void *k, const void *v, const void *params_dev, float *state_dev,
+                       void *workspace, float *y, hipStream_t stream);
+
+/* oal_prefill for measurement: identical work, and additionally records the caller-owned
+ * events marks[0] on `stream` before the first kernel, marks[1] after the chunk-state scan
+ * kernels and marks[2] after the readout kernel (hipEventElapsedTime between them gives
+ * the per-phase device time). The events are created and destroyed by the caller. */
+oal_status oal_prefill_timed(const oal_dims *dims, int32_t T, int32_t chunk, const void *q,
+                             const void *k, const void *v, const void *params_dev,
+                             float *state_dev, void *workspace, float *y, hipStream_t stream,
+                             hipEvent_t marks[3]);
+
+/* One decode step: appends one token per sequence to the prefix states and reads out the
+ * attention of each query head over all tokens so far (the new one included).
+ *   q [batch, n_q_heads, 64], k, v [batch, n_kv_heads, 64] of dims->dtype (device);
+ *   state_dev updated in place; y [batch, n_q_heads, 64] fp32.
+ *   workspace -- oal_decode_workspace_bytes(dims) bytes of device scratch that must be
+ *                zero-filled before its first use and then left to the library: every call
+ *                returns its counters to zero. Calls that share a workspace must be ordered
+ *                (same stream or synchronised). */
+oal_status oal_decode_step(const oal_dims *dims, const void *q, const void *k, const void *v,
+                           const void *params_dev, float *state_dev, void *workspace, float *y,
+                           hipStream_t stream);
+
+/* Static description of a status code. */
+const char *oal_status_string(oal_status status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* OAL_H */

