@@ -12,6 +12,7 @@
 // lane = row. Every byte of the state is read once and written once. Readout partial sums
 // per split go to the workspace; the last workgroup of a (sequence, KV head) to arrive sums
 // the splits in a fixed order, divides and writes y, then resets the arrival counter.
+// No device-wide fence is used: it would write back the whole L2, full of fresh state rows.
 #include <hip/hip_runtime.h>
 
 #include "oal.h"
@@ -48,7 +49,7 @@ __global__ __launch_bounds__(kThreads) void oal_decode_kernel(
     const int nrows = min(kRows, OAL_NFEAT - f0);
 
     __shared__ float s_k[OAL_D];
-    __shared__ float s_q[MAXH][OAL_D];
+    __shared__ float s_q[MAXH][OAL_D];    // rows >= n_rep stay unread (phi forced to 0)
     __shared__ float s_psi[kRows];
     __shared__ __align__(16) float s_phi[kRows][MAXH];
     __shared__ float s_red[4][MAXH][OAL_V1];
@@ -67,16 +68,17 @@ __global__ __launch_bounds__(kThreads) void oal_decode_kernel(
             int r, t;
             row_dims(f, r, t);
             psi = (r < 0) ? 1.0f : (t < 0 ? s_k[r] : s_k[r] * s_k[t]);
+            float w[MAXH];
+#pragma unroll
+            for (int h = 0; h < MAXH; ++h) {   // all coefficient loads in flight together
+                const OalHeadDev *hd = reinterpret_cast<const OalHeadDev *>(
+                    params + sizeof(OalParamsHeader) + (size_t)(h0 + min(h, n_rep - 1)) * OAL_HEAD_BYTES);
+                w[h] = hd->wdec[f];
+            }
 #pragma unroll
             for (int h = 0; h < MAXH; ++h) {
-                float ph = 0.0f;
-                if (h < n_rep) {
-                    const OalHeadDev *hd = reinterpret_cast<const OalHeadDev *>(
-                        params + sizeof(OalParamsHeader) + (size_t)(h0 + h) * OAL_HEAD_BYTES);
-                    float mono = (r < 0) ? 1.0f : (t < 0 ? s_q[h][r] : s_q[h][r] * s_q[h][t]);
-                    ph = hd->wdec[f] * mono;
-                }
-                s_phi[rr][h] = ph;
+                float mono = (r < 0) ? 1.0f : (t < 0 ? s_q[h][r] : s_q[h][r] * s_q[h][t]);
+                s_phi[rr][h] = h < n_rep ? w[h] * mono : 0.0f;
             }
         } else {
 #pragma unroll
@@ -93,13 +95,13 @@ __global__ __launch_bounds__(kThreads) void oal_decode_kernel(
     for (int h = 0; h < MAXH; ++h) { acc[h] = 0.0f; accd[h] = 0.0f; }
 
     const int rbeg = wave * 64, rend = min(nrows, rbeg + 64);
-    for (int rr = rbeg; rr < rend; rr += 8) {
-        float s[8];
+    for (int rr = rbeg; rr < rend; rr += 16) {
+        float s[16];
 #pragma unroll
-        for (int u = 0; u < 8; ++u)
+        for (int u = 0; u < 16; ++u)
             s[u] = (rr + u < rend) ? S[(size_t)(f0 + rr + u) * OAL_V1 + lane] : 0.0f;
 #pragma unroll
-        for (int u = 0; u < 8; ++u) {
+        for (int u = 0; u < 16; ++u) {
             if (rr + u < rend) {
                 s[u] += s_psi[rr + u] * vv;
                 S[(size_t)(f0 + rr + u) * OAL_V1 + lane] = s[u];
@@ -128,32 +130,41 @@ __global__ __launch_bounds__(kThreads) void oal_decode_kernel(
         if (lane == 0) s_red[wave][h][OAL_D] = x;
     }
     __syncthreads();
+    // Cross-workgroup combine. Partials are written and read with agent-scope atomics, which
+    // are coherent across the XCDs' L2 caches; the workgroup-scope fences order them around
+    // the arrival counter (they wait for the stores to complete) without flushing L2.
     float *mypart = partial + ((size_t)bkv * kSplits + split) * MAXH * OAL_V1;
     for (int idx = tid; idx < n_rep * OAL_V1; idx += kThreads) {
         int h = idx / OAL_V1, c = idx % OAL_V1;
-        mypart[idx] = s_red[0][h][c] + s_red[1][h][c] + s_red[2][h][c] + s_red[3][h][c];
+        __hip_atomic_store(mypart + idx, s_red[0][h][c] + s_red[1][h][c] + s_red[2][h][c] + s_red[3][h][c],
+                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
-    __threadfence();
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
     __syncthreads();
     if (tid == 0) {
-        unsigned int old = atomicAdd(counters + bkv, 1u);
+        unsigned int old = __hip_atomic_fetch_add(counters + bkv, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
         s_last = (old == (unsigned int)(kSplits - 1));
     }
     __syncthreads();
     if (!s_last) return;
-    __threadfence();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
     const float *allpart = partial + (size_t)bkv * kSplits * MAXH * OAL_V1;
+    // all splits are requested at once, then summed in split order (deterministic)
     for (int idx = tid; idx < n_rep * OAL_D; idx += kThreads) {
         int h = idx / OAL_D, c = idx % OAL_D;
-        float num = 0.0f, den = 0.0f;
+        float pn[kSplits], pd[kSplits];
+#pragma unroll
         for (int sp = 0; sp < kSplits; ++sp) {
-            const volatile float *pp = allpart + (size_t)sp * MAXH * OAL_V1 + h * OAL_V1;
-            num += pp[c];
-            den += pp[OAL_D];
+            const float *pp = allpart + (size_t)sp * MAXH * OAL_V1 + h * OAL_V1;
+            pn[sp] = __hip_atomic_load(pp + c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            pd[sp] = __hip_atomic_load(pp + OAL_D, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
+        float num = 0.0f, den = 0.0f;
+#pragma unroll
+        for (int sp = 0; sp < kSplits; ++sp) { num += pn[sp]; den += pd[sp]; }
         y[((size_t)b * n_q_heads + h0 + h) * OAL_D + c] = num / den;
     }
-    if (tid == 0) atomicExch(counters + bkv, 0u);
+    if (tid == 0) __hip_atomic_store(counters + bkv, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
 }
 
 template <typename T, int MAXH>

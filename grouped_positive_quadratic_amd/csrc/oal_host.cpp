@@ -218,7 +218,11 @@ static oal_status prefill_impl(const oal_dims *d, int32_t T, int32_t chunk, cons
     if ((T + chunk - 1) / chunk > 65535) return OAL_E_UNSUPPORTED;
     hipError_t e = oal_launch_prefill(*d, T, chunk, q, k, v, params_dev, state_dev, workspace, y,
                                       stream, marks);
-    return e == hipSuccess ? OAL_OK : OAL_E_HIP;
+    if (e != hipSuccess) {
+        (void)hipGetLastError();   // do not leave a sticky error for the caller's next HIP call
+        return OAL_E_HIP;
+    }
+    return OAL_OK;
 }
 
 oal_status oal_prefill(const oal_dims *d, int32_t T, int32_t chunk, const void *q, const void *k,
@@ -247,7 +251,11 @@ oal_status oal_decode_step(const oal_dims *d, const void *q, const void *k, cons
         !aligned16(state_dev) || !aligned16(workspace) || !aligned16(y))
         return OAL_E_ALIGN;
     hipError_t e = oal_launch_decode(*d, q, k, v, params_dev, state_dev, workspace, y, stream);
-    return e == hipSuccess ? OAL_OK : OAL_E_HIP;
+    if (e != hipSuccess) {
+        (void)hipGetLastError();
+        return OAL_E_HIP;
+    }
+    return OAL_OK;
 }
 
 }  // extern "C"

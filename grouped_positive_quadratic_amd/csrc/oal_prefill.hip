@@ -8,6 +8,8 @@
 //   u~_i = phi_h(q_i) . S_c + sum_{j in chunk c, j <= i} kappa_h(q_i, k_j) [v_j;1]
 //
 // Kernels, in launch order:
+//  0. oal_transpose_kv: K and V copied token-contiguous ([dim][token], zero past T) into
+//     the workspace, so that every later stage reads them with 16-byte coalesced copies.
 //  1. oal_scan<.., kTotals>  (only when the chunks are split into several segments)
 //     per (sequence x KV head, segment, K-step): the state increment of the segment, and
 //     for segment 0 a copy of the incoming state, into `totals`.
@@ -20,8 +22,11 @@
 //     per (sequence x KV head x head group, chunk, 16-query tile): the query heads of one
 //     KV head share every snapshot fragment. Two waves split the 72 K-steps of
 //     phi(Q) . S_c (odd/even rq) and the intra-chunk heads, then combine through LDS and
-//     divide: y = u~[0:64] / u~[64].
+//     divide: y = u~[0:64] / u~[64]. Workgroups of one chunk are placed on one XCD so the
+//     snapshot is fetched into that XCD's L2 once.
 #include <hip/hip_runtime.h>
+
+#include <type_traits>
 
 #include "oal.h"
 #include "oal_device.h"
@@ -32,6 +37,8 @@ namespace {
 constexpr int kScanWaves = 8;                 // K-steps per scan workgroup (72 = 9 x 8)
 constexpr int kScanBlocks = OAL_KSTEPS / kScanWaves;
 constexpr int kTotalsPerLane = 40;            // 2 tiles x 5 column tiles x 4 rows
+constexpr int kXcds = 8;                      // MI355X: workgroups go round-robin to 8 XCDs
+constexpr int kMaxLds = 160 * 1024;           // LDS per CU on gfx950
 enum { kTotals = 0, kSnapshots = 1 };
 
 template <typename T> constexpr int snap_kstep_bytes() { return 4 * 64 * OalFrag<T>::kBytes + 4 * OalFrag<T>::kBytes; }
@@ -46,6 +53,13 @@ __device__ inline void kstep_decode(int s, int &tb, int &rq) {
     rq = s - tb * (tb + 1);
 }
 
+// it-th K-step of one readout wave (rq of one parity): tb has tb+1 of them
+__device__ inline void wave_step(int it, int &tb, int &j) {
+    tb = 0;
+    while ((tb + 1) * (tb + 2) / 2 <= it) ++tb;
+    j = it - tb * (tb + 1) / 2;
+}
+
 // scale of a slot in the snapshot state (relative to H) and its state row; -1 = empty slot
 __device__ inline int slot_row(int tb, int rq, int g, int e, float &scale) {
     int ra, rb;
@@ -57,14 +71,66 @@ __device__ inline int slot_row(int tb, int rq, int g, int e, float &scale) {
     return -1;
 }
 
+typedef unsigned int oal_u32x4 __attribute__((ext_vector_type(4)));   // 16-byte copy unit
+
+__device__ inline oal_u32x4 zero16() {
+    oal_u32x4 z = {0u, 0u, 0u, 0u};
+    return z;
+}
+
 // ------------------------------------------------------------------------------------
-// chunk-state scan
+// 0. K, V -> token-contiguous copies kT, vT [bkv][64][Tpad]
+template <typename T>
+__global__ __launch_bounds__(256) void oal_transpose_kv(int T_len, int Tpad, const T *__restrict__ k,
+                                                        const T *__restrict__ v, T *__restrict__ kT,
+                                                        T *__restrict__ vT) {
+    constexpr int EPU = 16 / (int)sizeof(T);     // elements per 16-byte unit
+    constexpr int UPR = OAL_D / EPU;             // units per token row
+    constexpr int PER = 64 * UPR / 256;          // units per thread per array
+    constexpr int TS = 64 + EPU;                 // tile row (tokens), 16-byte aligned
+    __shared__ __align__(16) T tile[2][OAL_D * TS];
+    const int tok0 = blockIdx.x * 64, bkv = blockIdx.y, tid = threadIdx.x;
+    oal_u32x4 rk[PER], rv[PER];
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+        int u = tid + 256 * j, tok = u % 64, a = u / 64, pos = tok0 + tok;
+        size_t off = ((size_t)bkv * T_len + pos) * OAL_D + a * EPU;
+        rk[j] = pos < T_len ? *reinterpret_cast<const oal_u32x4 *>(k + off) : zero16();
+        rv[j] = pos < T_len ? *reinterpret_cast<const oal_u32x4 *>(v + off) : zero16();
+    }
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+        int u = tid + 256 * j, tok = u % 64, a = u / 64;
+        const T *ek = reinterpret_cast<const T *>(&rk[j]);
+        const T *ev = reinterpret_cast<const T *>(&rv[j]);
+#pragma unroll
+        for (int e = 0; e < EPU; ++e) {
+            tile[0][(a * EPU + e) * TS + tok] = ek[e];
+            tile[1][(a * EPU + e) * TS + tok] = ev[e];
+        }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+        int u = tid + 256 * j, dim = u / (64 / EPU), tu = u % (64 / EPU);
+        size_t off = ((size_t)bkv * OAL_D + dim) * Tpad + tok0 + tu * EPU;
+        *reinterpret_cast<oal_u32x4 *>(kT + off) = *reinterpret_cast<const oal_u32x4 *>(&tile[0][dim * TS + tu * EPU]);
+        *reinterpret_cast<oal_u32x4 *>(vT + off) = *reinterpret_cast<const oal_u32x4 *>(&tile[1][dim * TS + tu * EPU]);
+    }
+}
+
+// ------------------------------------------------------------------------------------
+// 1-2. chunk-state scan
 template <typename T, int C, int MODE>
 __global__ __launch_bounds__(64 * kScanWaves) void oal_scan(
-    int T_len, int nchunks, int nseg, int seg_len, const T *__restrict__ k,
-    const T *__restrict__ v, float *__restrict__ state, float *__restrict__ totals,
+    int T_len, int Tpad, int nchunks, int nseg, int seg_len, const T *__restrict__ kT,
+    const T *__restrict__ vT, float *__restrict__ state, float *__restrict__ totals,
     unsigned char *__restrict__ snap) {
-    constexpr int LD = C + 16 / (int)sizeof(T) * 2;     // padded row (keeps 16-byte alignment)
+    constexpr int EPU = 16 / (int)sizeof(T);
+    constexpr int LD = C + EPU;                         // padded row, 16-byte aligned
+    constexpr int UPR = C / EPU;                        // 16-byte units per row and chunk
+    constexpr int NU = 2 * OAL_D * UPR;                 // K and V rows of one chunk
+    constexpr int PER = (NU + 64 * kScanWaves - 1) / (64 * kScanWaves);
     extern __shared__ __align__(16) unsigned char smem[];
     T *s_kT = reinterpret_cast<T *>(smem);              // [65][LD], row 64 = valid-token ones
     T *s_vT = s_kT + 65 * LD;                           // [64][LD]
@@ -135,18 +201,33 @@ __global__ __launch_bounds__(64 * kScanWaves) void oal_scan(
         } else {
             for (int sg = 0; sg <= sigma; ++sg) {
                 const float *tp = totals_at(sg);
+                float x[kTotalsPerLane];
+#pragma unroll
+                for (int e = 0; e < kTotalsPerLane; ++e) x[e] = tp[e * 64];
 #pragma unroll
                 for (int h = 0; h < 2; ++h)
 #pragma unroll
                     for (int n = 0; n < 5; ++n)
 #pragma unroll
-                        for (int i = 0; i < 4; ++i) acc[h][n][i] += tp[((h * 5 + n) * 4 + i) * 64];
+                        for (int i = 0; i < 4; ++i) acc[h][n][i] += x[(h * 5 + n) * 4 + i];
             }
         }
     }
 
-    const T *kb = k + (size_t)bkv * T_len * OAL_D;
-    const T *vb = v + (size_t)bkv * T_len * OAL_D;
+    static_assert(NU % (64 * kScanWaves) == 0, "chunk staging must tile the workgroup");
+    // staging unit j of this thread: array (K or V), row and 16-byte column of the chunk
+    const T *kTb = kT + (size_t)bkv * OAL_D * Tpad;
+    const T *vTb = vT + (size_t)bkv * OAL_D * Tpad;
+    const T *src_u[PER];
+    T *dst_u[PER];
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+        int u = tid + 64 * kScanWaves * j;
+        int arr = u / (OAL_D * UPR), rem = u % (OAL_D * UPR), row = rem / UPR, cu = rem % UPR;
+        src_u[j] = (arr ? vTb : kTb) + (size_t)row * Tpad + cu * EPU;
+        dst_u[j] = (arr ? s_vT : s_kT) + row * LD + cu * EPU;
+    }
+
     OalFrag<T> ones, zeros;
     {
         float o[8], zz[8];
@@ -157,17 +238,22 @@ __global__ __launch_bounds__(64 * kScanWaves) void oal_scan(
     }
     constexpr int KB = snap_kstep_bytes<T>();
 
+    oal_u32x4 pre[PER];
+    if (c0 < c1) {
+#pragma unroll
+        for (int j = 0; j < PER; ++j) pre[j] = *reinterpret_cast<const oal_u32x4 *>(src_u[j] + (size_t)c0 * C);
+    }
     for (int c = c0; c < c1; ++c) {
         __syncthreads();
-        for (int idx = tid; idx < C * OAL_D; idx += 64 * kScanWaves) {
-            int tok = idx / OAL_D, dim = idx % OAL_D;
-            int pos = c * C + tok;
-            bool ok = pos < T_len;
-            s_kT[dim * LD + tok] = ok ? kb[(size_t)pos * OAL_D + dim] : (T)0.0f;
-            s_vT[dim * LD + tok] = ok ? vb[(size_t)pos * OAL_D + dim] : (T)0.0f;
-            if (dim == 0) s_kT[OAL_D * LD + tok] = ok ? (T)1.0f : (T)0.0f;
-        }
+#pragma unroll
+        for (int j = 0; j < PER; ++j) *reinterpret_cast<oal_u32x4 *>(dst_u[j]) = pre[j];
+        for (int tok = tid; tok < C; tok += 64 * kScanWaves)
+            s_kT[OAL_D * LD + tok] = (c * C + tok < T_len) ? (T)1.0f : (T)0.0f;
         __syncthreads();
+        if (c + 1 < c1) {
+#pragma unroll
+            for (int j = 0; j < PER; ++j) pre[j] = *reinterpret_cast<const oal_u32x4 *>(src_u[j] + (size_t)(c + 1) * C);
+        }
         if (MODE == kSnapshots) {
             unsigned char *sp = snap + (((size_t)bkv * nchunks + c) * OAL_KSTEPS + s) * KB;
 #pragma unroll
@@ -194,10 +280,12 @@ __global__ __launch_bounds__(64 * kScanWaves) void oal_scan(
             OalFrag<T> a[2], bf[4];
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
+                OalFrag<T> xa, xb;
+                xa.load(s_kT + ra[h] * LD + t0);
+                xb.load(s_kT + rb[h] * LD + t0);
                 float x[8];
 #pragma unroll
-                for (int e = 0; e < 8; ++e)
-                    x[e] = sig[h] * (float)s_kT[ra[h] * LD + t0 + e] * (float)s_kT[rb[h] * LD + t0 + e];
+                for (int e = 0; e < 8; ++e) x[e] = sig[h] * (float)xa.v[e] * (float)xb.v[e];
                 a[h].set(x);
             }
 #pragma unroll
@@ -235,23 +323,52 @@ __global__ __launch_bounds__(64 * kScanWaves) void oal_scan(
 }
 
 // ------------------------------------------------------------------------------------
-// readout
-constexpr int kPS = 68;   // padded LDS row of the per-query tables (16-byte aligned rows)
+// 3. readout
+template <typename T, int C, int R> struct ReadoutLayout {
+    static constexpr int EPU = 16 / (int)sizeof(T);
+    static constexpr int QS = OAL_D + EPU;      // q / key row in LDS (16-byte aligned)
+    static constexpr int LDV = C + EPU;         // V^T row
+    static constexpr int DG = 16;               // D block kept in LDS (groups < 16)
+    // byte offsets of the LDS regions
+    static constexpr int O_Q = 0;                                             // T [R*16][QS]
+    static constexpr int O_K = O_Q + R * 16 * QS * (int)sizeof(T);            // T [C][QS]
+    static constexpr int O_V = O_K + C * QS * (int)sizeof(T);                 // T [64][LDV]
+    static constexpr int O_W0 = O_V + OAL_D * LDV * (int)sizeof(T);           // f32 [R][64]
+    static constexpr int O_LIN = O_W0 + R * OAL_D * 4;                        // f32 [R][64]
+    static constexpr int O_D = O_LIN + R * OAL_D * 4;                         // f32 [R][16][16]
+    static constexpr int O_GAM = O_D + R * DG * DG * 4;                       // u8 [R][64]
+    static constexpr int BYTES_MAIN = O_GAM + R * OAL_D;
+    static constexpr int BYTES_X = R * 5 * 4 * 64 * 4;                        // combine buffer
+    static constexpr int BYTES = BYTES_MAIN > BYTES_X ? BYTES_MAIN : BYTES_X;
+    static constexpr int META_UNITS = 16 + 16 + 4 + DG * DG / 4;              // 16-byte units / head
+};
 
 template <typename T, int C, int R>
 __global__ __launch_bounds__(128) void oal_readout(
-    int T_len, int n_q_heads, int n_kv_heads, int nchunks, int n_hgroups,
-    const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ v,
+    int T_len, int Tpad, int n_q_heads, int n_kv_heads, int nchunks, int n_hgroups, int nunits,
+    const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ vT,
     const unsigned char *__restrict__ params, const unsigned char *__restrict__ snap,
     float *__restrict__ y) {
-    constexpr int LDV = C + 16 / (int)sizeof(T) * 2;
+    using Lay = ReadoutLayout<T, C, R>;
+    constexpr int EPU = Lay::EPU, QS = Lay::QS, LDV = Lay::LDV, DG = Lay::DG;
+    constexpr int NQT = C / 16;
+    constexpr int UPQ = OAL_D / EPU;            // 16-byte units per q/k row
     extern __shared__ __align__(16) unsigned char smem[];
-    float *s_p = reinterpret_cast<float *>(smem);      // [R][16][kPS]  w0[r] q_r
-    float *s_q = s_p + R * 16 * kPS;                   // [R][16][kPS]  q_r
-    T *s_vT = reinterpret_cast<T *>(s_q + R * 16 * kPS);   // [64][LDV]
+    T *s_q = reinterpret_cast<T *>(smem + Lay::O_Q);
+    T *s_k = reinterpret_cast<T *>(smem + Lay::O_K);
+    T *s_vT = reinterpret_cast<T *>(smem + Lay::O_V);
+    float *s_w0 = reinterpret_cast<float *>(smem + Lay::O_W0);
+    float *s_lin = reinterpret_cast<float *>(smem + Lay::O_LIN);
+    float *s_D = reinterpret_cast<float *>(smem + Lay::O_D);
+    unsigned char *s_gam = smem + Lay::O_GAM;
 
-    const int qt = blockIdx.x, c = blockIdx.y;
-    const int bkv = blockIdx.z / n_hgroups, hg = blockIdx.z % n_hgroups;
+    // XCD-aware placement: the NQT workgroups of one unit (chunk, KV head, head group)
+    // get block ids congruent mod 8, i.e. the same XCD and L2.
+    const int Lb = blockIdx.x, xcd = Lb % kXcds, i8 = Lb / kXcds;
+    const int unit = xcd + kXcds * (i8 / NQT), qt = i8 % NQT;
+    if (unit >= nunits) return;
+    const int c = unit % nchunks, z = unit / nchunks;
+    const int bkv = z / n_hgroups, hg = z % n_hgroups;
     const int b = bkv / n_kv_heads, kv = bkv % n_kv_heads;
     const int n_rep = n_q_heads / n_kv_heads;
     const int h0 = kv * n_rep + hg * R;
@@ -259,23 +376,103 @@ __global__ __launch_bounds__(128) void oal_readout(
     const int pos0 = c * C + qt * 16;
     if (pos0 >= T_len) return;
 
-    // 1. query tables
-    for (int idx = tid; idx < R * 16 * OAL_D; idx += 128) {
-        int i = idx / (16 * OAL_D), qi = (idx / OAL_D) % 16, r = idx % OAL_D;
-        int pos = pos0 + qi;
-        float qv = pos < T_len ? oal_ld(q + (((size_t)b * n_q_heads + h0 + i) * T_len + pos) * OAL_D + r) : 0.0f;
-        s_q[(i * 16 + qi) * kPS + r] = qv;
-        s_p[(i * 16 + qi) * kPS + r] = head_ptr(params, h0 + i)->w0[r] * qv;
-    }
-    // 2. V^T of this chunk's keys that the tile can see (rounded up to 32; zero past T)
-    const int nkeys = ((qt + 2) / 2) * 32;
-    const T *vb = v + (size_t)bkv * T_len * OAL_D;
-    for (int idx = tid; idx < nkeys * OAL_D; idx += 128) {
-        int key = idx / OAL_D, col = idx % OAL_D;
-        int pos = c * C + key;
-        s_vT[col * LDV + key] = pos < T_len ? vb[(size_t)pos * OAL_D + col] : (T)0.0f;
+    // 1. stage the tile's queries, the chunk's keys and V^T, and the per-head tables the
+    //    K-loop reads (so that no global load is consumed inside it). Loads of a phase are
+    //    all issued before its LDS writes.
+    {
+        constexpr int NQU = R * 16 * UPQ, NKU = C * UPQ, NVU = OAL_D * (C / EPU);
+        constexpr int NMU = R * Lay::META_UNITS;
+        constexpr int NQJ = (NQU + 127) / 128, NKJ = (NKU + 127) / 128, NVJ = (NVU + 127) / 128;
+        constexpr int NMJ = (NMU + 127) / 128;
+        constexpr bool ONE_PHASE = NQJ + NKJ + NVJ + NMJ <= 40;
+        const T *kb = k + (size_t)bkv * T_len * OAL_D;
+        const T *vTb = vT + (size_t)bkv * OAL_D * Tpad + (size_t)c * C;
+        oal_u32x4 rq[NQJ], rk[NKJ], rv[NVJ], rm[NMJ];
+        auto meta_src = [&](int u) -> const oal_u32x4 * {
+            const OalHeadDev *hd = head_ptr(params, h0 + u / Lay::META_UNITS);
+            int w = u % Lay::META_UNITS;
+            if (w < 16) return reinterpret_cast<const oal_u32x4 *>(hd->w0) + w;
+            if ((w -= 16) < 16) return reinterpret_cast<const oal_u32x4 *>(hd->lin) + w;
+            if ((w -= 16) < 4) return reinterpret_cast<const oal_u32x4 *>(hd->gamma) + w;
+            w -= 4;
+            return reinterpret_cast<const oal_u32x4 *>(hd->Dg + (w / (DG / 4)) * OAL_D) + w % (DG / 4);
+        };
+        auto meta_dst = [&](int u) -> oal_u32x4 * {
+            int i = u / Lay::META_UNITS, w = u % Lay::META_UNITS;
+            if (w < 16) return reinterpret_cast<oal_u32x4 *>(s_w0 + i * OAL_D) + w;
+            if ((w -= 16) < 16) return reinterpret_cast<oal_u32x4 *>(s_lin + i * OAL_D) + w;
+            if ((w -= 16) < 4) return reinterpret_cast<oal_u32x4 *>(s_gam + i * OAL_D) + w;
+            w -= 4;
+            return reinterpret_cast<oal_u32x4 *>(s_D + i * DG * DG) + w;
+        };
+#pragma unroll
+        for (int j = 0; j < NQJ; ++j) {
+            int u = tid + 128 * j;
+            int i = u / (16 * UPQ), qi = (u / UPQ) % 16, a = u % UPQ, pos = pos0 + qi;
+            rq[j] = (u < NQU && pos < T_len)
+                ? *reinterpret_cast<const oal_u32x4 *>(q + (((size_t)b * n_q_heads + h0 + i) * T_len + pos) * OAL_D + a * EPU)
+                : zero16();
+        }
+#pragma unroll
+        for (int j = 0; j < NKJ; ++j) {
+            int u = tid + 128 * j, key = u / UPQ, a = u % UPQ, pos = c * C + key;
+            rk[j] = (u < NKU && pos < T_len) ? *reinterpret_cast<const oal_u32x4 *>(kb + (size_t)pos * OAL_D + a * EPU) : zero16();
+        }
+#pragma unroll
+        for (int j = 0; j < NMJ; ++j) {
+            int u = tid + 128 * j;
+            rm[j] = u < NMU ? *meta_src(u) : zero16();
+        }
+        auto load_v = [&]() {
+#pragma unroll
+            for (int j = 0; j < NVJ; ++j) {
+                int u = tid + 128 * j, row = u / (C / EPU), cu = u % (C / EPU);
+                rv[j] = u < NVU ? *reinterpret_cast<const oal_u32x4 *>(vTb + (size_t)row * Tpad + cu * EPU) : zero16();
+            }
+        };
+        auto store_v = [&]() {
+#pragma unroll
+            for (int j = 0; j < NVJ; ++j) {
+                int u = tid + 128 * j, row = u / (C / EPU), cu = u % (C / EPU);
+                if (u < NVU) *reinterpret_cast<oal_u32x4 *>(s_vT + row * LDV + cu * EPU) = rv[j];
+            }
+        };
+        if (ONE_PHASE) load_v();
+#pragma unroll
+        for (int j = 0; j < NQJ; ++j) {
+            int u = tid + 128 * j;
+            int i = u / (16 * UPQ), qi = (u / UPQ) % 16, a = u % UPQ;
+            if (u < NQU) *reinterpret_cast<oal_u32x4 *>(s_q + (i * 16 + qi) * QS + a * EPU) = rq[j];
+        }
+#pragma unroll
+        for (int j = 0; j < NKJ; ++j) {
+            int u = tid + 128 * j, key = u / UPQ, a = u % UPQ;
+            if (u < NKU) *reinterpret_cast<oal_u32x4 *>(s_k + key * QS + a * EPU) = rk[j];
+        }
+#pragma unroll
+        for (int j = 0; j < NMJ; ++j) {
+            int u = tid + 128 * j;
+            if (u < NMU) *meta_dst(u) = rm[j];
+        }
+        if (!ONE_PHASE) load_v();
+        store_v();
     }
     __syncthreads();
+
+    // per-head scalars (uniform)
+    uint32_t corr[R][3];
+    float a_h[R];
+    int bulk_h[R], G_h[R];
+#pragma unroll
+    for (int i = 0; i < R; ++i) {
+        const OalHeadDev *hd = head_ptr(params, h0 + i);
+        corr[i][0] = hd->corr[0];
+        corr[i][1] = hd->corr[1];
+        corr[i][2] = hd->corr[2];
+        a_h[i] = hd->a;
+        bulk_h[i] = hd->bulk;
+        G_h[i] = hd->G;
+    }
 
     oal_f32x4 acc[R][5];
 #pragma unroll
@@ -283,77 +480,106 @@ __global__ __launch_bounds__(128) void oal_readout(
 #pragma unroll
         for (int n = 0; n < 5; ++n) acc[i][n] = oal_splat(0.0f);
 
-    // 3. inter-chunk: phi(Q) . S_c over this wave's 36 K-steps (rq = 2 j + wave)
+    // 2. inter-chunk: phi(Q) . S_c over this wave's 36 K-steps (rq = 2 j + wave); snapshot
+    //    fragments are fetched two K-steps ahead
     constexpr int KB = snap_kstep_bytes<T>();
+    constexpr int NSTEP = OAL_KSTEPS / 2;
     const unsigned char *sbase = snap + ((size_t)bkv * nchunks + c) * OAL_KSTEPS * KB;
-    auto load_b = [&](OalFrag<T> (&bf)[5], int s) {
-        const unsigned char *sp = sbase + (size_t)s * KB;
+    auto load_b = [&](OalFrag<T> (&bf)[5], int it) {
+        int tb2, j2;
+        wave_step(it, tb2, j2);
+        const unsigned char *sp = sbase + (size_t)oal_kstep(tb2, 2 * j2 + wave) * KB;
 #pragma unroll
         for (int n = 0; n < 4; ++n) bf[n].load(sp + (n * 64 + lane) * OalFrag<T>::kBytes);
         if (lr == 0) bf[4].load(sp + (4 * 64 + g) * OalFrag<T>::kBytes);
         else bf[4].zero();
     };
-    {
-        OalFrag<T> bcur[5], bnext[5];
+    // Two copies of the loop, chosen once: with every head at <= 16 groups the correction
+    // block D is read from LDS only, so no global load is consumed inside the loop (which
+    // would also wait for the snapshot prefetches, vmcnt being in order).
+    auto inter = [&](auto big_g) {
+        constexpr bool BIG = decltype(big_g)::value;
+        OalFrag<T> b0[5], b1[5], b2[5];
         float pt[R][8];
-        int tb = 0, j = 0;
-        load_b(bcur, oal_kstep(0, wave));
-        for (int it = 0; it < OAL_KSTEPS / 2; ++it) {
+        load_b(b0, 0);
+        load_b(b1, 1);
+        for (int it = 0; it < NSTEP; ++it) {
+            int tb, j;
+            wave_step(it, tb, j);
             const int rq = 2 * j + wave;
             const int s = oal_kstep(tb, rq);
-            int ntb = tb, nj = j + 1;
-            if (nj > tb) { ntb = tb + 1; nj = 0; }
-            if (it + 1 < OAL_KSTEPS / 2) load_b(bnext, oal_kstep(ntb, 2 * nj + wave));
+            if (it + 2 < NSTEP) load_b(b2, it + 2);
             if (j == 0) {
 #pragma unroll
                 for (int i = 0; i < R; ++i) {
-                    const float4 *pp = reinterpret_cast<const float4 *>(s_p + (i * 16 + lr) * kPS + 8 * tb);
-                    float4 x0 = pp[0], x1 = pp[1];
-                    pt[i][0] = x0.x; pt[i][1] = x0.y; pt[i][2] = x0.z; pt[i][3] = x0.w;
-                    pt[i][4] = x1.x; pt[i][5] = x1.y; pt[i][6] = x1.z; pt[i][7] = x1.w;
+                    OalFrag<T> qv;
+                    const T *qp = s_q + (i * 16 + lr) * QS + 8 * tb;
+                    if (EPU == 8) {
+                        qv.load(qp);
+                    } else {
+                        qv.load4x2(qp, qp + 4);
+                    }
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) pt[i][e] = s_w0[i * OAL_D + 8 * tb + e] * (float)qv.v[e];
                 }
             }
             const bool lin_step = (rq == 2 * tb + 1);
+            const int r = 4 * rq + g;
 #pragma unroll
             for (int i = 0; i < R; ++i) {
-                const OalHeadDev *hd = head_ptr(params, h0 + i);
-                const float *qrow = s_q + (i * 16 + lr) * kPS;
-                const float pr = s_p[(i * 16 + lr) * kPS + 4 * rq + g];
+                const T *qrow = s_q + (i * 16 + lr) * QS;
+                const float qr = (float)qrow[r];
+                const float pr = s_w0[i * OAL_D + r] * qr;
                 float phi[8];
 #pragma unroll
                 for (int e = 0; e < 8; ++e) phi[e] = pr * pt[i][e];
                 if (lin_step) {
                     const int r0 = 8 * tb + 2 * g;
-                    phi[0] = hd->lin[r0] * qrow[r0];
-                    phi[1] = hd->lin[r0 + 1] * qrow[r0 + 1];
-                    if (tb == 0 && g == 0) phi[2] = hd->a;
+                    phi[0] = s_lin[i * OAL_D + r0] * (float)qrow[r0];
+                    phi[1] = s_lin[i * OAL_D + r0 + 1] * (float)qrow[r0 + 1];
+                    if (tb == 0 && g == 0) phi[2] = a_h[i];
                 }
-                if ((hd->corr[s >> 5] >> (s & 31)) & 1u) {
-                    const int r = 4 * rq + g;
-                    const int gr = hd->gamma[r];
-                    const float qr = qrow[r];
+                if ((corr[i][s >> 5] >> (s & 31)) & 1u) {
+                    // pairs of two non-bulk dims: add D[g(r)][g(t)] q_r q_t
+                    const int gr = s_gam[i * OAL_D + r];
+                    if (!BIG) {
 #pragma unroll
-                    for (int e = 0; e < 8; ++e) {
-                        const int t = 8 * tb + e;
-                        const int gt = hd->gamma[t];
-                        if (gt != hd->bulk && r <= t) phi[e] += hd->Dg[gr * OAL_D + gt] * qr * qrow[t];
+                        for (int e = 0; e < 8; ++e) {
+                            const int t = 8 * tb + e;
+                            const int gt = s_gam[i * OAL_D + t];
+                            if (gt != bulk_h[i] && r <= t)
+                                phi[e] += s_D[(i * DG + gr) * DG + gt] * qr * (float)qrow[t];
+                        }
+                    } else {
+                        const float *Dg = head_ptr(params, h0 + i)->Dg;
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) {
+                            const int t = 8 * tb + e;
+                            const int gt = s_gam[i * OAL_D + t];
+                            if (gt != bulk_h[i] && r <= t) phi[e] += Dg[gr * OAL_D + gt] * qr * (float)qrow[t];
+                        }
                     }
                 }
                 OalFrag<T> a;
                 a.set(phi);
 #pragma unroll
-                for (int n = 0; n < 5; ++n) acc[i][n] = oal_mma(a, bcur[n], acc[i][n]);
+                for (int n = 0; n < 5; ++n) acc[i][n] = oal_mma(a, b0[n], acc[i][n]);
             }
 #pragma unroll
-            for (int n = 0; n < 5; ++n) bcur[n] = bnext[n];
-            tb = ntb;
-            j = nj;
+            for (int n = 0; n < 5; ++n) {
+                b0[n] = b1[n];
+                b1[n] = b2[n];
+            }
         }
-    }
+    };
+    bool big_g = false;
+#pragma unroll
+    for (int i = 0; i < R; ++i) big_g |= G_h[i] > DG;
+    if (big_g) inter(std::true_type{});
+    else inter(std::false_type{});
 
-    // 4. intra-chunk: kappa = eps + sum_m z_m^2 with z_m = L00 [m==0] + sum_r Lz[m][r] q_r k_r,
+    // 3. intra-chunk: kappa = eps + sum_m z_m^2 with z_m = L00 [m==0] + sum_r Lz[m][r] q_r k_r,
     //    z_m^T tiles (16 keys x 16 queries) on MFMA, then kappa [V;1] on MFMA.
-    const T *kb = k + (size_t)bkv * T_len * OAL_D;
     OalFrag<T> ones, zeros;
     {
         float o[8], zz[8];
@@ -366,47 +592,57 @@ __global__ __launch_bounds__(128) void oal_readout(
     for (int i = 0; i < R; ++i) {
         if ((i & 1) != wave) continue;
         const OalHeadDev *hd = head_ptr(params, h0 + i);
-        const float *qrow = s_q + (i * 16 + lr) * kPS;
-        oal_f32x4 kap[C / 16];
+        const T *qrow = s_q + (i * 16 + lr) * QS;
+        oal_f32x4 kap[NQT];
+        const float eps = hd->eps, L00 = hd->L00;
 #pragma unroll
-        for (int kt = 0; kt < C / 16; ++kt) kap[kt] = oal_splat(hd->eps);
-        const int G = hd->G;
+        for (int kt = 0; kt < NQT; ++kt) kap[kt] = oal_splat(eps);
+        const int G = G_h[i];
+        auto load_lz = [&](float4 (&lz)[4], int m) {
+            const float4 *p = reinterpret_cast<const float4 *>(hd->Lz + m * OAL_D + 8 * g);
+            lz[0] = p[0];
+            lz[1] = p[1];
+            lz[2] = p[8];
+            lz[3] = p[9];
+        };
+        float4 lzn[4];
+        load_lz(lzn, 0);
         for (int m = 0; m <= G; ++m) {
+            float lzv[16] = {lzn[0].x, lzn[0].y, lzn[0].z, lzn[0].w, lzn[1].x, lzn[1].y, lzn[1].z, lzn[1].w,
+                             lzn[2].x, lzn[2].y, lzn[2].z, lzn[2].w, lzn[3].x, lzn[3].y, lzn[3].z, lzn[3].w};
+            if (m < G) load_lz(lzn, m + 1);
             OalFrag<T> bq[2];
 #pragma unroll
             for (int hh = 0; hh < 2; ++hh) {
                 float x[8];
 #pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    int r = 32 * hh + 8 * g + e;
-                    x[e] = hd->Lz[m * OAL_D + r] * qrow[r];
-                }
+                for (int e = 0; e < 8; ++e) x[e] = lzv[8 * hh + e] * (float)qrow[32 * hh + 8 * g + e];
                 bq[hh].set(x);
             }
-            const oal_f32x4 cinit = oal_splat(m == 0 ? hd->L00 : 0.0f);
+            const oal_f32x4 cinit = oal_splat(m == 0 ? L00 : 0.0f);
 #pragma unroll
-            for (int kt = 0; kt < C / 16; ++kt) {
+            for (int kt = 0; kt < NQT; ++kt) {
                 if (kt <= qt) {
-                    const int kpos = c * C + 16 * kt + lr;
+                    const T *kr = s_k + (16 * kt + lr) * QS + 8 * g;
                     OalFrag<T> ak[2];
-                    if (kpos < T_len) {
-                        ak[0].load(kb + (size_t)kpos * OAL_D + 8 * g);
-                        ak[1].load(kb + (size_t)kpos * OAL_D + 32 + 8 * g);
+                    if (EPU == 8) {
+                        ak[0].load(kr);
+                        ak[1].load(kr + 32);
                     } else {
-                        ak[0].zero();
-                        ak[1].zero();
+                        ak[0].load4x2(kr, kr + 4);
+                        ak[1].load4x2(kr + 32, kr + 36);
                     }
-                    oal_f32x4 z = oal_mma(ak[0], bq[0], cinit);
-                    z = oal_mma(ak[1], bq[1], z);
+                    oal_f32x4 zv = oal_mma(ak[0], bq[0], cinit);
+                    zv = oal_mma(ak[1], bq[1], zv);
 #pragma unroll
-                    for (int ii = 0; ii < 4; ++ii) kap[kt][ii] += z[ii] * z[ii];
+                    for (int ii = 0; ii < 4; ++ii) kap[kt][ii] += zv[ii] * zv[ii];
                 }
             }
         }
         // causal mask (key <= query, key < T), then kappa [V;1]
         const int qpos = pos0 + lr;
 #pragma unroll
-        for (int kt = 0; kt < C / 16; ++kt)
+        for (int kt = 0; kt < NQT; ++kt)
 #pragma unroll
             for (int ii = 0; ii < 4; ++ii) {
                 int kp = c * C + 16 * kt + 4 * g + ii;
@@ -435,7 +671,7 @@ __global__ __launch_bounds__(128) void oal_readout(
         }
     }
 
-    // 5. combine the two waves' partial sums and divide
+    // 4. combine the two waves' partial sums and divide
     __syncthreads();
     float *s_x = reinterpret_cast<float *>(smem);      // [R][5][4][64]
 #pragma unroll
@@ -467,20 +703,14 @@ __global__ __launch_bounds__(128) void oal_readout(
 }
 
 template <typename T, int C>
-size_t scan_lds() { return (size_t)(65 + 64) * (C + 16 / sizeof(T) * 2) * sizeof(T); }
+size_t scan_lds() { return (size_t)(65 + 64) * (C + 16 / sizeof(T)) * sizeof(T); }
 
 template <typename T, int C, int R>
-size_t readout_lds() {
-    size_t tables = (size_t)2 * R * 16 * kPS * sizeof(float);
-    size_t vt = (size_t)64 * (C + 16 / sizeof(T) * 2) * sizeof(T);
-    size_t x = (size_t)R * 5 * 4 * 64 * sizeof(float);
-    size_t a = tables + vt;
-    return a > x ? a : x;
-}
+size_t readout_lds() { return (size_t)ReadoutLayout<T, C, R>::BYTES; }
 
 struct PrefillPlan {
-    int nchunks, nseg, seg_len;
-    size_t snap_bytes, totals_bytes;
+    int nchunks, nseg, seg_len, Tpad;
+    size_t snap_bytes, totals_bytes, kv_bytes;
 };
 
 template <typename T>
@@ -488,6 +718,7 @@ PrefillPlan make_plan(const oal_dims &d, int T_len, int C) {
     PrefillPlan p;
     size_t bkv = (size_t)d.batch * d.n_kv_heads;
     p.nchunks = (T_len + C - 1) / C;
+    p.Tpad = p.nchunks * C;
     int target = 1;
     const char *env = getenv("OAL_NSEG");
     if (env && atoi(env) > 0) {
@@ -501,15 +732,16 @@ PrefillPlan make_plan(const oal_dims &d, int T_len, int C) {
     if (target < 1) target = 1;
     p.seg_len = (p.nchunks + target - 1) / target;
     p.nseg = (p.nchunks + p.seg_len - 1) / p.seg_len;
-    p.snap_bytes = bkv * p.nchunks * OAL_KSTEPS * (size_t)snap_kstep_bytes<T>();
-    p.snap_bytes = (p.snap_bytes + 255) / 256 * 256;
-    p.totals_bytes = p.nseg > 1 ? bkv * p.nseg * OAL_KSTEPS * (size_t)kTotalsPerLane * 64 * sizeof(float) : 0;
+    auto r256 = [](size_t x) { return (x + 255) / 256 * 256; };
+    p.snap_bytes = r256(bkv * p.nchunks * OAL_KSTEPS * (size_t)snap_kstep_bytes<T>());
+    p.totals_bytes = p.nseg > 1 ? r256(bkv * p.nseg * OAL_KSTEPS * (size_t)kTotalsPerLane * 64 * sizeof(float)) : 0;
+    p.kv_bytes = r256(bkv * OAL_D * (size_t)p.Tpad * sizeof(T));
     return p;
 }
 
 template <typename T, int C, int R>
 hipError_t launch_readout(const oal_dims &d, int T_len, const PrefillPlan &p, const void *q,
-                          const void *k, const void *v, const void *params,
+                          const void *k, const T *vT, const void *params,
                           const unsigned char *snap, float *y, hipStream_t stream) {
     int n_rep = d.n_q_heads / d.n_kv_heads;
     int n_hg = n_rep / R;
@@ -518,11 +750,12 @@ hipError_t launch_readout(const oal_dims &d, int T_len, const PrefillPlan &p, co
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
-    dim3 grid(C / 16, p.nchunks, d.batch * d.n_kv_heads * n_hg);
-    hipLaunchKernelGGL(kern, grid, dim3(128), lds, stream, T_len, d.n_q_heads, d.n_kv_heads,
-                       p.nchunks, n_hg, reinterpret_cast<const T *>(q), reinterpret_cast<const T *>(k),
-                       reinterpret_cast<const T *>(v), reinterpret_cast<const unsigned char *>(params),
-                       snap, y);
+    int nunits = p.nchunks * d.batch * d.n_kv_heads * n_hg;
+    int nblocks = kXcds * (C / 16) * ((nunits + kXcds - 1) / kXcds);
+    hipLaunchKernelGGL(kern, dim3(nblocks), dim3(128), lds, stream, T_len, p.Tpad, d.n_q_heads,
+                       d.n_kv_heads, p.nchunks, n_hg, nunits, reinterpret_cast<const T *>(q),
+                       reinterpret_cast<const T *>(k), vT,
+                       reinterpret_cast<const unsigned char *>(params), snap, y);
     return hipGetLastError();
 }
 
@@ -531,38 +764,50 @@ hipError_t launch_all(const oal_dims &d, int T_len, const void *q, const void *k
                       const void *params, float *state, void *ws, float *y, hipStream_t stream,
                       hipEvent_t *marks) {
     PrefillPlan p = make_plan<T>(d, T_len, C);
-    if (marks && hipEventRecord(marks[0], stream) != hipSuccess) return hipErrorUnknown;
     unsigned char *snap = reinterpret_cast<unsigned char *>(ws);
     float *totals = reinterpret_cast<float *>(snap + p.snap_bytes);
+    T *kT = reinterpret_cast<T *>(snap + p.snap_bytes + p.totals_bytes);
+    T *vT = reinterpret_cast<T *>(snap + p.snap_bytes + p.totals_bytes + p.kv_bytes);
     int bkv = d.batch * d.n_kv_heads;
+    hipError_t e;
+    if (marks && (e = hipEventRecord(marks[0], stream)) != hipSuccess) return e;
+    hipLaunchKernelGGL(oal_transpose_kv<T>, dim3(p.Tpad / 64, bkv), dim3(256), 0, stream, T_len, p.Tpad,
+                       reinterpret_cast<const T *>(k), reinterpret_cast<const T *>(v), kT, vT);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
     size_t lds = scan_lds<T, C>();
-    const T *kk = reinterpret_cast<const T *>(k), *vv = reinterpret_cast<const T *>(v);
     if (p.nseg > 1) {
         auto kern = oal_scan<T, C, kTotals>;
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-        if (e != hipSuccess) return e;
+        if ((e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds)) != hipSuccess)
+            return e;
         hipLaunchKernelGGL(kern, dim3(kScanBlocks, p.nseg - 1, bkv), dim3(64 * kScanWaves), lds, stream,
-                           T_len, p.nchunks, p.nseg, p.seg_len, kk, vv, state, totals, snap);
+                           T_len, p.Tpad, p.nchunks, p.nseg, p.seg_len, kT, vT, state, totals, snap);
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
     {
         auto kern = oal_scan<T, C, kSnapshots>;
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-        if (e != hipSuccess) return e;
+        if ((e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds)) != hipSuccess)
+            return e;
         hipLaunchKernelGGL(kern, dim3(kScanBlocks, p.nseg, bkv), dim3(64 * kScanWaves), lds, stream,
-                           T_len, p.nchunks, p.nseg, p.seg_len, kk, vv, state, totals, snap);
+                           T_len, p.Tpad, p.nchunks, p.nseg, p.seg_len, kT, vT, state, totals, snap);
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
-    if (marks && hipEventRecord(marks[1], stream) != hipSuccess) return hipErrorUnknown;
+    if (marks && (e = hipEventRecord(marks[1], stream)) != hipSuccess) return e;
+    // heads per workgroup: the largest R in {8, 7, 4, 2, 1} that divides n_rep and whose
+    // LDS footprint fits one CU
     int n_rep = d.n_q_heads / d.n_kv_heads;
-    hipError_t e;
-    if (n_rep % 8 == 0) e = launch_readout<T, C, 8>(d, T_len, p, q, k, v, params, snap, y, stream);
-    else if (n_rep % 7 == 0) e = launch_readout<T, C, 7>(d, T_len, p, q, k, v, params, snap, y, stream);
-    else if (n_rep % 4 == 0) e = launch_readout<T, C, 4>(d, T_len, p, q, k, v, params, snap, y, stream);
-    else if (n_rep % 2 == 0) e = launch_readout<T, C, 2>(d, T_len, p, q, k, v, params, snap, y, stream);
-    else e = launch_readout<T, C, 1>(d, T_len, p, q, k, v, params, snap, y, stream);
+    auto fits = [](size_t bytes) { return bytes <= (size_t)kMaxLds; };
+    if (n_rep % 8 == 0 && fits(readout_lds<T, C, 8>()))
+        e = launch_readout<T, C, 8>(d, T_len, p, q, k, vT, params, snap, y, stream);
+    else if (n_rep % 7 == 0 && fits(readout_lds<T, C, 7>()))
+        e = launch_readout<T, C, 7>(d, T_len, p, q, k, vT, params, snap, y, stream);
+    else if (n_rep % 4 == 0 && fits(readout_lds<T, C, 4>()))
+        e = launch_readout<T, C, 4>(d, T_len, p, q, k, vT, params, snap, y, stream);
+    else if (n_rep % 2 == 0 && fits(readout_lds<T, C, 2>()))
+        e = launch_readout<T, C, 2>(d, T_len, p, q, k, vT, params, snap, y, stream);
+    else
+        e = launch_readout<T, C, 1>(d, T_len, p, q, k, vT, params, snap, y, stream);
     if (e == hipSuccess && marks) e = hipEventRecord(marks[2], stream);
     return e;
 }
@@ -571,7 +816,7 @@ hipError_t launch_all(const oal_dims &d, int T_len, const void *q, const void *k
 
 size_t oal_prefill_ws_bytes_impl(const oal_dims &d, int T_len, int C) {
     PrefillPlan p = d.dtype == OAL_BF16 ? make_plan<__bf16>(d, T_len, C) : make_plan<float>(d, T_len, C);
-    return p.snap_bytes + p.totals_bytes;
+    return p.snap_bytes + p.totals_bytes + 2 * p.kv_bytes;
 }
 
 hipError_t oal_launch_prefill(const oal_dims &d, int T_len, int C, const void *q, const void *k,
