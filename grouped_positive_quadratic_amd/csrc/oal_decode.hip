@@ -44,7 +44,7 @@ __global__ __launch_bounds__(kThreads) void oal_decode_kernel(
     const int b = bkv / n_kv_heads, kv = bkv % n_kv_heads;
     const int n_rep = n_q_heads / n_kv_heads;
     const int h0 = kv * n_rep;
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
     const int f0 = split * kRows;
     const int nrows = min(kRows, OAL_NFEAT - f0);
 

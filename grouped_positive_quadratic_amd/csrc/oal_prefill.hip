@@ -135,7 +135,7 @@ __global__ __launch_bounds__(64 * kScanWaves) void oal_scan(
     T *s_kT = reinterpret_cast<T *>(smem);              // [65][LD], row 64 = valid-token ones
     T *s_vT = s_kT + 65 * LD;                           // [64][LD]
 
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, g = lane >> 4, lr = lane & 15;
+    const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63, g = lane >> 4, lr = lane & 15;
     const int s = blockIdx.x * kScanWaves + wave;
     const int sigma = blockIdx.y;
     const int bkv = blockIdx.z;
@@ -328,20 +328,64 @@ template <typename T, int C, int R> struct ReadoutLayout {
     static constexpr int EPU = 16 / (int)sizeof(T);
     static constexpr int QS = OAL_D + EPU;      // q / key row in LDS (16-byte aligned)
     static constexpr int LDV = C + EPU;         // V^T row
-    static constexpr int DG = 16;               // D block kept in LDS (groups < 16)
-    // byte offsets of the LDS regions
-    static constexpr int O_Q = 0;                                             // T [R*16][QS]
-    static constexpr int O_K = O_Q + R * 16 * QS * (int)sizeof(T);            // T [C][QS]
-    static constexpr int O_V = O_K + C * QS * (int)sizeof(T);                 // T [64][LDV]
-    static constexpr int O_W0 = O_V + OAL_D * LDV * (int)sizeof(T);           // f32 [R][64]
+    static constexpr int PS = OAL_D + 4;        // fp32 p-table row
+    static constexpr int DG = 8;                // D block kept in LDS (heads with G <= 8)
+    static constexpr int LZR = 8;               // Lz rows m < 8 kept in LDS
+    // Byte offsets. The "union" region holds the fp32 p table during the inter-chunk loop,
+    // then K and V^T of the chunk during the intra-chunk part, then the combine buffer.
+    static constexpr int P_BYTES = R * 16 * PS * 4;
+    static constexpr int KV_BYTES = C * QS * (int)sizeof(T) + OAL_D * LDV * (int)sizeof(T);
+    static constexpr int X_BYTES = R * 5 * 4 * 64 * 4;
+    static constexpr int U_BYTES = P_BYTES > KV_BYTES ? (P_BYTES > X_BYTES ? P_BYTES : X_BYTES)
+                                                      : (KV_BYTES > X_BYTES ? KV_BYTES : X_BYTES);
+    static constexpr int O_U = 0;
+    static constexpr int O_Q = O_U + U_BYTES;                                 // T [R*16][QS]
+    static constexpr int O_W0 = O_Q + R * 16 * QS * (int)sizeof(T);           // f32 [R][64]
     static constexpr int O_LIN = O_W0 + R * OAL_D * 4;                        // f32 [R][64]
-    static constexpr int O_D = O_LIN + R * OAL_D * 4;                         // f32 [R][16][16]
-    static constexpr int O_GAM = O_D + R * DG * DG * 4;                       // u8 [R][64]
-    static constexpr int BYTES_MAIN = O_GAM + R * OAL_D;
-    static constexpr int BYTES_X = R * 5 * 4 * 64 * 4;                        // combine buffer
-    static constexpr int BYTES = BYTES_MAIN > BYTES_X ? BYTES_MAIN : BYTES_X;
-    static constexpr int META_UNITS = 16 + 16 + 4 + DG * DG / 4;              // 16-byte units / head
+    static constexpr int O_D = O_LIN + R * OAL_D * 4;                         // f32 [R][8][8]
+    static constexpr int O_LZ = O_D + R * DG * DG * 4;                        // f32 [R][LZR][64]
+    static constexpr int O_GAM = O_LZ + R * LZR * OAL_D * 4;                  // u8 [R][64]
+    static constexpr int BYTES = O_GAM + R * OAL_D;
+    static constexpr int META_UNITS = 16 + 16 + 4 + DG * DG / 4 + LZR * 16;   // 16-byte units / head
+    static_assert(U_BYTES % 16 == 0 && O_Q % 16 == 0 && O_W0 % 16 == 0 && O_LZ % 16 == 0, "alignment");
 };
+
+// One term z_m of the intra-chunk kernel for a 16-query tile of one head:
+//   z_m^T (16 keys x 16 queries) = K_kt (keys x 64) . (Lz[m] o q)^T + c_m, for key tiles
+//   kt <= qt of the chunk, and kappa[kt] += z_m^2 elementwise.
+// lzv holds Lz[m] at dims 8g..8g+7 (lzv[0..7]) and 32+8g.. (lzv[8..15]); c_m = L00 for m = 0.
+template <typename T, int NQT, int QS>
+__device__ inline void oal_z_step(const float (&lzv)[16], float cm, const T *qrow, const T *s_k, int g,
+                                  int lr, int qt, oal_f32x4 (&kap)[NQT]) {
+    constexpr int EPU = 16 / (int)sizeof(T);
+    OalFrag<T> bq[2];
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+        float x[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[e] = lzv[8 * hh + e] * (float)qrow[32 * hh + 8 * g + e];
+        bq[hh].set(x);
+    }
+    const oal_f32x4 cinit = oal_splat(cm);
+#pragma unroll
+    for (int kt = 0; kt < NQT; ++kt) {
+        if (kt <= qt) {
+            const T *kr = s_k + (16 * kt + lr) * QS + 8 * g;
+            OalFrag<T> ak[2];
+            if (EPU == 8) {
+                ak[0].load(kr);
+                ak[1].load(kr + 32);
+            } else {
+                ak[0].load4x2(kr, kr + 4);
+                ak[1].load4x2(kr + 32, kr + 36);
+            }
+            oal_f32x4 zv = oal_mma(ak[0], bq[0], cinit);
+            zv = oal_mma(ak[1], bq[1], zv);
+#pragma unroll
+            for (int ii = 0; ii < 4; ++ii) kap[kt][ii] += zv[ii] * zv[ii];
+        }
+    }
+}
 
 template <typename T, int C, int R>
 __global__ __launch_bounds__(128) void oal_readout(
@@ -350,16 +394,19 @@ __global__ __launch_bounds__(128) void oal_readout(
     const unsigned char *__restrict__ params, const unsigned char *__restrict__ snap,
     float *__restrict__ y) {
     using Lay = ReadoutLayout<T, C, R>;
-    constexpr int EPU = Lay::EPU, QS = Lay::QS, LDV = Lay::LDV, DG = Lay::DG;
+    constexpr int EPU = Lay::EPU, QS = Lay::QS, LDV = Lay::LDV, DG = Lay::DG, PS = Lay::PS;
     constexpr int NQT = C / 16;
     constexpr int UPQ = OAL_D / EPU;            // 16-byte units per q/k row
     extern __shared__ __align__(16) unsigned char smem[];
+    float *s_p = reinterpret_cast<float *>(smem + Lay::O_U);               // inter: [R*16][PS]
+    T *s_k = reinterpret_cast<T *>(smem + Lay::O_U);                       // intra: [C][QS]
+    T *s_vT = s_k + C * QS;                                                // intra: [64][LDV]
+    float *s_x = reinterpret_cast<float *>(smem + Lay::O_U);               // combine
     T *s_q = reinterpret_cast<T *>(smem + Lay::O_Q);
-    T *s_k = reinterpret_cast<T *>(smem + Lay::O_K);
-    T *s_vT = reinterpret_cast<T *>(smem + Lay::O_V);
     float *s_w0 = reinterpret_cast<float *>(smem + Lay::O_W0);
     float *s_lin = reinterpret_cast<float *>(smem + Lay::O_LIN);
     float *s_D = reinterpret_cast<float *>(smem + Lay::O_D);
+    float *s_lz = reinterpret_cast<float *>(smem + Lay::O_LZ);
     unsigned char *s_gam = smem + Lay::O_GAM;
 
     // XCD-aware placement: the NQT workgroups of one unit (chunk, KV head, head group)
@@ -372,38 +419,37 @@ __global__ __launch_bounds__(128) void oal_readout(
     const int b = bkv / n_kv_heads, kv = bkv % n_kv_heads;
     const int n_rep = n_q_heads / n_kv_heads;
     const int h0 = kv * n_rep + hg * R;
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, g = lane >> 4, lr = lane & 15;
+    const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63, g = lane >> 4, lr = lane & 15;
     const int pos0 = c * C + qt * 16;
     if (pos0 >= T_len) return;
 
-    // 1. stage the tile's queries, the chunk's keys and V^T, and the per-head tables the
-    //    K-loop reads (so that no global load is consumed inside it). Loads of a phase are
-    //    all issued before its LDS writes.
+    // 1. stage the tile's queries and the per-head tables (all loads issued before any LDS
+    //    write), and warm this XCD's L2 with 1/NQT of the chunk's snapshot: the NQT
+    //    workgroups of the unit run side by side on this XCD, so together they bring the
+    //    snapshot in once. The warming loads only feed a value that is never stored.
     {
-        constexpr int NQU = R * 16 * UPQ, NKU = C * UPQ, NVU = OAL_D * (C / EPU);
-        constexpr int NMU = R * Lay::META_UNITS;
-        constexpr int NQJ = (NQU + 127) / 128, NKJ = (NKU + 127) / 128, NVJ = (NVU + 127) / 128;
-        constexpr int NMJ = (NMU + 127) / 128;
-        constexpr bool ONE_PHASE = NQJ + NKJ + NVJ + NMJ <= 40;
-        const T *kb = k + (size_t)bkv * T_len * OAL_D;
-        const T *vTb = vT + (size_t)bkv * OAL_D * Tpad + (size_t)c * C;
-        oal_u32x4 rq[NQJ], rk[NKJ], rv[NVJ], rm[NMJ];
+        constexpr int NQU = R * 16 * UPQ, NMU = R * Lay::META_UNITS;
+        constexpr int NQJ = (NQU + 127) / 128, NMJ = (NMU + 127) / 128;
+        oal_u32x4 rq[NQJ], rm[NMJ];
         auto meta_src = [&](int u) -> const oal_u32x4 * {
             const OalHeadDev *hd = head_ptr(params, h0 + u / Lay::META_UNITS);
             int w = u % Lay::META_UNITS;
             if (w < 16) return reinterpret_cast<const oal_u32x4 *>(hd->w0) + w;
             if ((w -= 16) < 16) return reinterpret_cast<const oal_u32x4 *>(hd->lin) + w;
             if ((w -= 16) < 4) return reinterpret_cast<const oal_u32x4 *>(hd->gamma) + w;
-            w -= 4;
-            return reinterpret_cast<const oal_u32x4 *>(hd->Dg + (w / (DG / 4)) * OAL_D) + w % (DG / 4);
+            if ((w -= 4) < DG * DG / 4)
+                return reinterpret_cast<const oal_u32x4 *>(hd->Dg + (w / (DG / 4)) * OAL_D) + w % (DG / 4);
+            w -= DG * DG / 4;
+            return reinterpret_cast<const oal_u32x4 *>(hd->Lz) + w;
         };
         auto meta_dst = [&](int u) -> oal_u32x4 * {
             int i = u / Lay::META_UNITS, w = u % Lay::META_UNITS;
             if (w < 16) return reinterpret_cast<oal_u32x4 *>(s_w0 + i * OAL_D) + w;
             if ((w -= 16) < 16) return reinterpret_cast<oal_u32x4 *>(s_lin + i * OAL_D) + w;
             if ((w -= 16) < 4) return reinterpret_cast<oal_u32x4 *>(s_gam + i * OAL_D) + w;
-            w -= 4;
-            return reinterpret_cast<oal_u32x4 *>(s_D + i * DG * DG) + w;
+            if ((w -= 4) < DG * DG / 4) return reinterpret_cast<oal_u32x4 *>(s_D + i * DG * DG) + w;
+            w -= DG * DG / 4;
+            return reinterpret_cast<oal_u32x4 *>(s_lz + i * Lay::LZR * OAL_D) + w;
         };
 #pragma unroll
         for (int j = 0; j < NQJ; ++j) {
@@ -414,30 +460,21 @@ __global__ __launch_bounds__(128) void oal_readout(
                 : zero16();
         }
 #pragma unroll
-        for (int j = 0; j < NKJ; ++j) {
-            int u = tid + 128 * j, key = u / UPQ, a = u % UPQ, pos = c * C + key;
-            rk[j] = (u < NKU && pos < T_len) ? *reinterpret_cast<const oal_u32x4 *>(kb + (size_t)pos * OAL_D + a * EPU) : zero16();
-        }
-#pragma unroll
         for (int j = 0; j < NMJ; ++j) {
             int u = tid + 128 * j;
             rm[j] = u < NMU ? *meta_src(u) : zero16();
         }
-        auto load_v = [&]() {
+        constexpr int SNAP_UNITS = OAL_KSTEPS * snap_kstep_bytes<T>() / 16;
+        constexpr int SHARE = (SNAP_UNITS + NQT - 1) / NQT;
+        constexpr int NTJ = (SHARE + 127) / 128;
+        const oal_u32x4 *sn = reinterpret_cast<const oal_u32x4 *>(
+            snap + ((size_t)bkv * nchunks + c) * OAL_KSTEPS * snap_kstep_bytes<T>());
+        oal_u32x4 touch = zero16();
 #pragma unroll
-            for (int j = 0; j < NVJ; ++j) {
-                int u = tid + 128 * j, row = u / (C / EPU), cu = u % (C / EPU);
-                rv[j] = u < NVU ? *reinterpret_cast<const oal_u32x4 *>(vTb + (size_t)row * Tpad + cu * EPU) : zero16();
-            }
-        };
-        auto store_v = [&]() {
-#pragma unroll
-            for (int j = 0; j < NVJ; ++j) {
-                int u = tid + 128 * j, row = u / (C / EPU), cu = u % (C / EPU);
-                if (u < NVU) *reinterpret_cast<oal_u32x4 *>(s_vT + row * LDV + cu * EPU) = rv[j];
-            }
-        };
-        if (ONE_PHASE) load_v();
+        for (int j = 0; j < NTJ; ++j) {
+            int u = qt * SHARE + tid + 128 * j;
+            if (tid + 128 * j < SHARE && u < SNAP_UNITS) touch ^= sn[u];
+        }
 #pragma unroll
         for (int j = 0; j < NQJ; ++j) {
             int u = tid + 128 * j;
@@ -445,30 +482,29 @@ __global__ __launch_bounds__(128) void oal_readout(
             if (u < NQU) *reinterpret_cast<oal_u32x4 *>(s_q + (i * 16 + qi) * QS + a * EPU) = rq[j];
         }
 #pragma unroll
-        for (int j = 0; j < NKJ; ++j) {
-            int u = tid + 128 * j, key = u / UPQ, a = u % UPQ;
-            if (u < NKU) *reinterpret_cast<oal_u32x4 *>(s_k + key * QS + a * EPU) = rk[j];
-        }
-#pragma unroll
         for (int j = 0; j < NMJ; ++j) {
             int u = tid + 128 * j;
             if (u < NMU) *meta_dst(u) = rm[j];
         }
-        if (!ONE_PHASE) load_v();
-        store_v();
+        if (touch.x == 0x9e3779b9u && touch.y == 0x7f4a7c15u && T_len < 0) y[0] = 0.0f;  // never true
+    }
+    __syncthreads();
+    // p table: p = w0[r] q_r (fp32), the rank-1 factor of the quadratic coefficients
+    for (int u = tid; u < R * 16 * OAL_D; u += 128) {
+        int i = u / (16 * OAL_D), qi = (u / OAL_D) % 16, r = u % OAL_D;
+        s_p[(i * 16 + qi) * PS + r] = s_w0[i * OAL_D + r] * (float)s_q[(i * 16 + qi) * QS + r];
     }
     __syncthreads();
 
     // per-head scalars (uniform)
-    uint32_t corr[R][3];
+    uint64_t corr_lo[R], corr_hi[R];   // K-step bits 0..63 and 64..71
     float a_h[R];
     int bulk_h[R], G_h[R];
 #pragma unroll
     for (int i = 0; i < R; ++i) {
         const OalHeadDev *hd = head_ptr(params, h0 + i);
-        corr[i][0] = hd->corr[0];
-        corr[i][1] = hd->corr[1];
-        corr[i][2] = hd->corr[2];
+        corr_lo[i] = (uint64_t)hd->corr[0] | ((uint64_t)hd->corr[1] << 32);
+        corr_hi[i] = hd->corr[2];
         a_h[i] = hd->a;
         bulk_h[i] = hd->bulk;
         G_h[i] = hd->G;
@@ -494,7 +530,7 @@ __global__ __launch_bounds__(128) void oal_readout(
         if (lr == 0) bf[4].load(sp + (4 * 64 + g) * OalFrag<T>::kBytes);
         else bf[4].zero();
     };
-    // Two copies of the loop, chosen once: with every head at <= 16 groups the correction
+    // Two copies of the loop, chosen once: with every head at <= DG groups the correction
     // block D is read from LDS only, so no global load is consumed inside the loop (which
     // would also wait for the snapshot prefetches, vmcnt being in order).
     auto inter = [&](auto big_g) {
@@ -509,55 +545,64 @@ __global__ __launch_bounds__(128) void oal_readout(
             const int rq = 2 * j + wave;
             const int s = oal_kstep(tb, rq);
             if (it + 2 < NSTEP) load_b(b2, it + 2);
+            const int r = 4 * rq + g;
+            // LDS reads of every head first, one wait, then the arithmetic
             if (j == 0) {
 #pragma unroll
                 for (int i = 0; i < R; ++i) {
-                    OalFrag<T> qv;
-                    const T *qp = s_q + (i * 16 + lr) * QS + 8 * tb;
-                    if (EPU == 8) {
-                        qv.load(qp);
-                    } else {
-                        qv.load4x2(qp, qp + 4);
-                    }
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) pt[i][e] = s_w0[i * OAL_D + 8 * tb + e] * (float)qv.v[e];
+                    const float4 *pp = reinterpret_cast<const float4 *>(s_p + (i * 16 + lr) * PS + 8 * tb);
+                    float4 x0 = pp[0], x1 = pp[1];
+                    pt[i][0] = x0.x; pt[i][1] = x0.y; pt[i][2] = x0.z; pt[i][3] = x0.w;
+                    pt[i][4] = x1.x; pt[i][5] = x1.y; pt[i][6] = x1.z; pt[i][7] = x1.w;
                 }
             }
+            float prv[R];
+#pragma unroll
+            for (int i = 0; i < R; ++i) prv[i] = s_p[(i * 16 + lr) * PS + r];
             const bool lin_step = (rq == 2 * tb + 1);
-            const int r = 4 * rq + g;
+            float lin0[R], lin1[R];
+            if (lin_step) {
+                const int r0 = 8 * tb + 2 * g;
+#pragma unroll
+                for (int i = 0; i < R; ++i) {
+                    const T *qrow = s_q + (i * 16 + lr) * QS;
+                    lin0[i] = s_lin[i * OAL_D + r0] * (float)qrow[r0];
+                    lin1[i] = s_lin[i * OAL_D + r0 + 1] * (float)qrow[r0 + 1];
+                }
+            }
 #pragma unroll
             for (int i = 0; i < R; ++i) {
-                const T *qrow = s_q + (i * 16 + lr) * QS;
-                const float qr = (float)qrow[r];
-                const float pr = s_w0[i * OAL_D + r] * qr;
                 float phi[8];
 #pragma unroll
-                for (int e = 0; e < 8; ++e) phi[e] = pr * pt[i][e];
+                for (int e = 0; e < 8; ++e) phi[e] = prv[i] * pt[i][e];
                 if (lin_step) {
-                    const int r0 = 8 * tb + 2 * g;
-                    phi[0] = s_lin[i * OAL_D + r0] * (float)qrow[r0];
-                    phi[1] = s_lin[i * OAL_D + r0 + 1] * (float)qrow[r0 + 1];
+                    phi[0] = lin0[i];
+                    phi[1] = lin1[i];
                     if (tb == 0 && g == 0) phi[2] = a_h[i];
                 }
-                if ((corr[i][s >> 5] >> (s & 31)) & 1u) {
-                    // pairs of two non-bulk dims: add D[g(r)][g(t)] q_r q_t
+                const uint64_t cbit = s < 64 ? (corr_lo[i] >> (s & 63)) : (corr_hi[i] >> ((s - 64) & 63));
+                if (cbit & 1u) {
+                    // pairs of two non-bulk dims: phi += D[g(r)][g(t)] q_r q_t (all loads first)
+                    const T *qrow = s_q + (i * 16 + lr) * QS;
                     const int gr = s_gam[i * OAL_D + r];
-                    if (!BIG) {
+                    const float qr = (float)qrow[r];
+                    int gt[8];
+                    float qtv[8], dv[8];
 #pragma unroll
-                        for (int e = 0; e < 8; ++e) {
-                            const int t = 8 * tb + e;
-                            const int gt = s_gam[i * OAL_D + t];
-                            if (gt != bulk_h[i] && r <= t)
-                                phi[e] += s_D[(i * DG + gr) * DG + gt] * qr * (float)qrow[t];
-                        }
-                    } else {
-                        const float *Dg = head_ptr(params, h0 + i)->Dg;
+                    for (int e = 0; e < 8; ++e) {
+                        gt[e] = s_gam[i * OAL_D + 8 * tb + e];
+                        qtv[e] = (float)qrow[8 * tb + e];
+                    }
 #pragma unroll
-                        for (int e = 0; e < 8; ++e) {
-                            const int t = 8 * tb + e;
-                            const int gt = s_gam[i * OAL_D + t];
-                            if (gt != bulk_h[i] && r <= t) phi[e] += Dg[gr * OAL_D + gt] * qr * (float)qrow[t];
-                        }
+                    for (int e = 0; e < 8; ++e) {
+                        const int gte = gt[e] < DG ? gt[e] : 0;
+                        dv[e] = BIG ? head_ptr(params, h0 + i)->Dg[gr * OAL_D + gt[e]]
+                                    : s_D[(i * DG + (gr < DG ? gr : 0)) * DG + gte];
+                    }
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        const bool on = gt[e] != bulk_h[i] && r <= 8 * tb + e;
+                        phi[e] += on ? dv[e] * qr * qtv[e] : 0.0f;
                     }
                 }
                 OalFrag<T> a;
@@ -578,7 +623,39 @@ __global__ __launch_bounds__(128) void oal_readout(
     if (big_g) inter(std::true_type{});
     else inter(std::false_type{});
 
-    // 3. intra-chunk: kappa = eps + sum_m z_m^2 with z_m = L00 [m==0] + sum_r Lz[m][r] q_r k_r,
+    // 3. stage K and V^T of the keys this tile can see into the region the p table used
+    {
+        const int nkeys = ((qt + 2) / 2) * 32;   // rounded to 32 (<= C)
+        const int nku = nkeys * UPQ, nvu = OAL_D * (nkeys / EPU);
+        constexpr int NKJ = (C * UPQ + 127) / 128, NVJ = (OAL_D * (C / EPU) + 127) / 128;
+        const T *kb = k + (size_t)bkv * T_len * OAL_D;
+        const T *vTb = vT + (size_t)bkv * OAL_D * Tpad + (size_t)c * C;
+        oal_u32x4 rk[NKJ], rv[NVJ];
+#pragma unroll
+        for (int j = 0; j < NKJ; ++j) {
+            int u = tid + 128 * j, key = u / UPQ, a = u % UPQ, pos = c * C + key;
+            rk[j] = (u < nku && pos < T_len) ? *reinterpret_cast<const oal_u32x4 *>(kb + (size_t)pos * OAL_D + a * EPU) : zero16();
+        }
+#pragma unroll
+        for (int j = 0; j < NVJ; ++j) {
+            int u = tid + 128 * j, row = u / (nkeys / EPU), cu = u % (nkeys / EPU);
+            rv[j] = u < nvu ? *reinterpret_cast<const oal_u32x4 *>(vTb + (size_t)row * Tpad + cu * EPU) : zero16();
+        }
+        __syncthreads();    // both waves are done with the p table
+#pragma unroll
+        for (int j = 0; j < NKJ; ++j) {
+            int u = tid + 128 * j, key = u / UPQ, a = u % UPQ;
+            if (u < nku) *reinterpret_cast<oal_u32x4 *>(s_k + key * QS + a * EPU) = rk[j];
+        }
+#pragma unroll
+        for (int j = 0; j < NVJ; ++j) {
+            int u = tid + 128 * j, row = u / (nkeys / EPU), cu = u % (nkeys / EPU);
+            if (u < nvu) *reinterpret_cast<oal_u32x4 *>(s_vT + row * LDV + cu * EPU) = rv[j];
+        }
+        __syncthreads();
+    }
+
+    // 4. intra-chunk: kappa = eps + sum_m z_m^2 with z_m = L00 [m==0] + sum_r Lz[m][r] q_r k_r,
     //    z_m^T tiles (16 keys x 16 queries) on MFMA, then kappa [V;1] on MFMA.
     OalFrag<T> ones, zeros;
     {
@@ -598,45 +675,22 @@ __global__ __launch_bounds__(128) void oal_readout(
 #pragma unroll
         for (int kt = 0; kt < NQT; ++kt) kap[kt] = oal_splat(eps);
         const int G = G_h[i];
-        auto load_lz = [&](float4 (&lz)[4], int m) {
-            const float4 *p = reinterpret_cast<const float4 *>(hd->Lz + m * OAL_D + 8 * g);
-            lz[0] = p[0];
-            lz[1] = p[1];
-            lz[2] = p[8];
-            lz[3] = p[9];
-        };
-        float4 lzn[4];
-        load_lz(lzn, 0);
-        for (int m = 0; m <= G; ++m) {
-            float lzv[16] = {lzn[0].x, lzn[0].y, lzn[0].z, lzn[0].w, lzn[1].x, lzn[1].y, lzn[1].z, lzn[1].w,
-                             lzn[2].x, lzn[2].y, lzn[2].z, lzn[2].w, lzn[3].x, lzn[3].y, lzn[3].z, lzn[3].w};
-            if (m < G) load_lz(lzn, m + 1);
-            OalFrag<T> bq[2];
+        // Lz rows come from LDS when the head has fewer than LZR groups, else from the blob
+        if (G < Lay::LZR) {
+            for (int m = 0; m <= G; ++m) {
+                const float *p = s_lz + (i * Lay::LZR + m) * OAL_D + 8 * g;
+                float lzv[16];
 #pragma unroll
-            for (int hh = 0; hh < 2; ++hh) {
-                float x[8];
-#pragma unroll
-                for (int e = 0; e < 8; ++e) x[e] = lzv[8 * hh + e] * (float)qrow[32 * hh + 8 * g + e];
-                bq[hh].set(x);
+                for (int e = 0; e < 8; ++e) { lzv[e] = p[e]; lzv[8 + e] = p[32 + e]; }
+                oal_z_step<T, NQT, QS>(lzv, m == 0 ? L00 : 0.0f, qrow, s_k, g, lr, qt, kap);
             }
-            const oal_f32x4 cinit = oal_splat(m == 0 ? L00 : 0.0f);
+        } else {
+            for (int m = 0; m <= G; ++m) {
+                const float *p = hd->Lz + m * OAL_D + 8 * g;
+                float lzv[16];
 #pragma unroll
-            for (int kt = 0; kt < NQT; ++kt) {
-                if (kt <= qt) {
-                    const T *kr = s_k + (16 * kt + lr) * QS + 8 * g;
-                    OalFrag<T> ak[2];
-                    if (EPU == 8) {
-                        ak[0].load(kr);
-                        ak[1].load(kr + 32);
-                    } else {
-                        ak[0].load4x2(kr, kr + 4);
-                        ak[1].load4x2(kr + 32, kr + 36);
-                    }
-                    oal_f32x4 zv = oal_mma(ak[0], bq[0], cinit);
-                    zv = oal_mma(ak[1], bq[1], zv);
-#pragma unroll
-                    for (int ii = 0; ii < 4; ++ii) kap[kt][ii] += zv[ii] * zv[ii];
-                }
+                for (int e = 0; e < 8; ++e) { lzv[e] = p[e]; lzv[8 + e] = p[32 + e]; }
+                oal_z_step<T, NQT, QS>(lzv, m == 0 ? L00 : 0.0f, qrow, s_k, g, lr, qt, kap);
             }
         }
         // causal mask (key <= query, key < T), then kappa [V;1]
@@ -671,9 +725,8 @@ __global__ __launch_bounds__(128) void oal_readout(
         }
     }
 
-    // 4. combine the two waves' partial sums and divide
+    // 5. combine the two waves' partial sums and divide
     __syncthreads();
-    float *s_x = reinterpret_cast<float *>(smem);      // [R][5][4][64]
 #pragma unroll
     for (int i = 0; i < R; ++i)
         if ((i & 1) != wave)
