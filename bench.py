@@ -43,6 +43,8 @@ def parse():
     ap.add_argument("--decode-steps", type=int, default=256)
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 256 MiB device copy (reference for HBM byte counters)")
     ap.add_argument("--traffic-json", default=os.path.join(os.path.dirname(os.path.abspath(__file__)),
                                                           "profiles", "traffic.json"))
     return ap.parse_args()
@@ -58,6 +60,15 @@ def main():
         sys.exit(2)
 
     import torch
+    if args.copy_calibration:
+        n = 64 << 20                                     # 64 Mi floats = 256 MiB each way
+        src = torch.ones(n, dtype=torch.float32, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_read": 4 * n, "copy_bytes_written": 4 * n, "launches": 3}))
+        return
     import grouped_positive_quadratic_amd as gpq
     from oal_synth import qwen_like, cfg5_prefix, cfg5_steps
 
@@ -141,13 +152,11 @@ def main():
         dhp = gpq.HeadParamsC.from_params(pre.params)
         dparams, dstate, dws_pre, dws = gpq.alloc_buffers(ddims, 4096, 128)
         gpq.oal_state_init(ddims, dhp, dparams, dstate)
-        pq = torch.zeros((nseq, 14, 4096, D), dtype=torch.bfloat16, device=dev)
         pk = torch.from_numpy(pre.k).to(torch.bfloat16).to(dev).contiguous()
         pv = torch.from_numpy(pre.v).to(torch.bfloat16).to(dev).contiguous()
-        py = torch.empty((nseq, 14, 4096, D), dtype=torch.float32, device=dev)
-        gpq.oal_prefill(ddims, 4096, 128, pq, pk, pv, dparams, dstate, dws_pre, py)
+        gpq.oal_prefill(ddims, 4096, 128, None, pk, pv, dparams, dstate, dws_pre, None)  # state only
         torch.cuda.synchronize()
-        del pq, pk, pv, py, dws_pre
+        del pk, pv, dws_pre
         torch.cuda.empty_cache()
         tq = torch.from_numpy(toks.q).to(torch.bfloat16).to(dev).permute(2, 0, 1, 3).contiguous()
         tk = torch.from_numpy(toks.k).to(torch.bfloat16).to(dev).permute(2, 0, 1, 3).contiguous()

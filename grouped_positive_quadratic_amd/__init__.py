@@ -43,6 +43,10 @@ class oal_head_params(ctypes.Structure):
 
 
 def _load():
+    # torch ships its own HIP runtime. Loading it first makes the dynamic linker bind
+    # liboal.so to that same runtime instance; loaded the other way round, the process would
+    # hold two runtimes and torch's device pointers and streams would be foreign to liboal.
+    import torch  # noqa: F401
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"{LIB_PATH} is missing: build it with "
                           "`python -m grouped_positive_quadratic_amd.build` (hipcc, gfx950)")
@@ -158,6 +162,7 @@ def oal_state_init(dims: oal_dims, params: HeadParamsC, params_dev, state_dev=No
 
 def oal_prefill(dims: oal_dims, T: int, chunk: int, q, k, v, params_dev, state_dev, workspace, y,
                 stream=None):
+    """y=None (and then q may be None) only advances the state."""
     _check("oal_prefill", _lib.oal_prefill(ctypes.byref(dims), int(T), int(chunk), _ptr(q), _ptr(k),
                                            _ptr(v), _ptr(params_dev), _ptr(state_dev),
                                            _ptr(workspace), _ptr(y), _stream(stream)))

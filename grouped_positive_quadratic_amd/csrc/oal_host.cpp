@@ -211,9 +211,10 @@ static oal_status prefill_impl(const oal_dims *d, int32_t T, int32_t chunk, cons
     if (T < 0) return OAL_E_SHAPE;
     if (chunk != 64 && chunk != 128 && chunk != 256) return OAL_E_UNSUPPORTED;
     if (T == 0 || d->batch == 0) return OAL_OK;
-    if (!q || !k || !v || !params_dev || !state_dev || !workspace || !y) return OAL_E_ARG;
-    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(params_dev) ||
-        !aligned16(state_dev) || !aligned16(workspace) || !aligned16(y))
+    // y == NULL: advance the state only (q is then not read and may be NULL)
+    if ((y && !q) || !k || !v || !params_dev || !state_dev || !workspace) return OAL_E_ARG;
+    if ((q && !aligned16(q)) || !aligned16(k) || !aligned16(v) || !aligned16(params_dev) ||
+        !aligned16(state_dev) || !aligned16(workspace) || (y && !aligned16(y)))
         return OAL_E_ALIGN;
     if ((T + chunk - 1) / chunk > 65535) return OAL_E_UNSUPPORTED;
     hipError_t e = oal_launch_prefill(*d, T, chunk, q, k, v, params_dev, state_dev, workspace, y,

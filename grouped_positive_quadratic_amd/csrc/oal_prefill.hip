@@ -847,6 +847,7 @@ hipError_t launch_all(const oal_dims &d, int T_len, const void *q, const void *k
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
     if (marks && (e = hipEventRecord(marks[1], stream)) != hipSuccess) return e;
+    if (!y) return marks ? hipEventRecord(marks[2], stream) : hipSuccess;   // state only
     // heads per workgroup: the largest R in {8, 7, 4, 2, 1} that divides n_rep and whose
     // LDS footprint fits one CU
     int n_rep = d.n_q_heads / d.n_kv_heads;

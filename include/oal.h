@@ -118,7 +118,9 @@ oal_status oal_state_init(const oal_dims *dims, const oal_head_params *hp, void 
  *   state_dev  -- in: prefix states of the tokens before these T; out: states after them.
  *   workspace  -- oal_prefill_workspace_bytes(dims, T, chunk) bytes of device scratch. Its
  *                 contents on entry do not matter.
- *   y          -- [batch, n_q_heads, T, 64] fp32 output (device).
+ *   y          -- [batch, n_q_heads, T, 64] fp32 output (device), or NULL to only advance
+ *                 the state (ingesting a context whose outputs are not needed; q is then
+ *                 not read and may be NULL).
  * Position i of this call attends to every earlier token of the sequence (those folded
  * into the input state and tokens 0..i of this call). T = 0 is a no-op. */
 oal_status oal_prefill(const oal_dims *dims, int32_t T, int32_t chunk, const void *q,

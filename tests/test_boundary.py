@@ -59,7 +59,9 @@ def test_validation_errors_enqueue_nothing():
     assert _code(gpq.oal_prefill, d, 8, 100, *ok, 0) == 5            # chunk
     assert _code(gpq.oal_prefill, d, -1, 64, *ok, 0) == 2            # T < 0
     assert _code(gpq.oal_prefill, d, 0, 64, None, None, None, None, None, None, None, 0) == 0
-    assert _code(gpq.oal_prefill, d, 8, 64, None, A, A, A, A, A, A, 0) == 1   # null q
+    assert _code(gpq.oal_prefill, d, 8, 64, None, A, A, A, A, A, A, 0) == 1   # null q with y
+    assert _code(gpq.oal_prefill, d, 8, 64, None, None, A, A, A, A, None, 0) == 1  # null k
+    assert _code(gpq.oal_prefill, d, 8, 64, A, A, A, A, A, A, A + 4, 0) == 4   # misaligned y
     assert _code(gpq.oal_prefill, d, 8, 64, A + 2, A, A, A, A, A, A, 0) == 4  # misaligned
     assert _code(gpq.oal_prefill, gpq.make_dims(1, 3, 2, "bf16"), 8, 64, *ok, 0) == 2
     assert _code(gpq.oal_prefill, gpq.make_dims(1, 2, 1, 7), 8, 64, *ok, 0) == 3
@@ -205,3 +207,17 @@ def test_blob_reproduces_oracle(inp):
             z[0] += hd["L00"]
             kap = hd["eps"] + np.sum(z * z)
             np.testing.assert_allclose(kap, oracle.kappa(q, k, inp.params, h), rtol=1e-5)
+
+
+def test_one_hip_runtime_per_process():
+    """Importing the binding before torch must not load a second HIP runtime."""
+    import subprocess
+    import sys
+    code = ("import grouped_positive_quadratic_amd, torch\n"
+            "maps = open('/proc/self/maps').read().split('\\n')\n"
+            "paths = {l.split()[-1] for l in maps if 'libamdhip64' in l}\n"
+            "print(len(paths), sorted(paths))\n")
+    out = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, cwd=ROOT,
+                         timeout=300)
+    assert out.returncode == 0, out.stderr
+    assert out.stdout.split()[0] == "1", out.stdout

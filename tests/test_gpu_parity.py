@@ -14,6 +14,7 @@ pytestmark = pytest.mark.gpu
 
 torch = pytest.importorskip("torch")
 from gpu_util import Session, session_for, to_dev, state_error, state_ok, TOL  # noqa: E402
+import grouped_positive_quadratic_amd as gpq  # noqa: E402
 
 
 def _report(name, err):
@@ -93,6 +94,26 @@ def test_prefill_then_decode(dtype):
     _report(f"prefill+decode {dtype}", err)
     assert err <= TOL[dtype]
     assert state_ok(sess.state_np(), inp.k, inp.v, dtype)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_state_only_prefill(dtype):
+    """y = NULL (q = NULL) advances the state exactly as a full prefill does; decode continues."""
+    inp = small(23, 2, 14, 2, 200, dtype=dtype)
+    T0 = 190
+    full = session_for(inp, 64)
+    full.prefill(inp.q[:, :, :T0], inp.k[:, :, :T0], inp.v[:, :, :T0], 64)
+    only = session_for(inp, 64)
+    only.ensure_ws(T0, 64)
+    gpq.oal_prefill(only.dims, T0, 64, None, to_dev(inp.k[:, :, :T0], dtype),
+                    to_dev(inp.v[:, :, :T0], dtype), only.params, only.state, only.ws, None)
+    S_only, S_full = only.state_np(), full.state_np()
+    assert np.array_equal(S_only, S_full)
+    ys = [only.decode(inp.q[:, :, i], inp.k[:, :, i], inp.v[:, :, i]) for i in range(T0, 200)]
+    y = torch.stack(ys, 2).cpu().numpy()
+    err = oracle.row_error(y, oracle.dense(inp.q, inp.k, inp.v, inp.params)[:, :, T0:])
+    _report(f"state-only prefill + decode {dtype}", err)
+    assert err <= TOL[dtype]
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
