@@ -109,15 +109,13 @@ def main():
     readout_flops = FLOP_PER_TOKEN_HEAD * tokens * Hq
     scan_flops = FLOP_PER_TOKEN_HEAD * tokens * Hkv
     achieved = readout_flops / (read_ms * 1e-3) / 1e12
-    traffic = None
+    tj = {}
     if os.path.exists(args.traffic_json):
         try:
             tj = json.load(open(args.traffic_json))
-            key = f"readout_B{B}_T{T}_C{C}"
-            if key in tj:
-                traffic = tj[key]["bytes_per_launch"]
-        except Exception:
-            traffic = None
+        except (OSError, ValueError):
+            tj = {}
+    traffic = tj.get(f"readout_B{B}_T{T}_C{C}", {}).get("bytes_per_launch")
     out = {
         "metric": METRIC,
         "value": tokens / (ms_step * 1e-3),
@@ -177,7 +175,8 @@ def main():
                          "steps": nsteps, "config": {"workload": f"decode {nseq} seqs, 4096-token prefix states, 14q/2kv"},
                          "roofline": {"bound": "hbm", "kernel": "oal_decode_kernel", "achieved": dach,
                                       "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": dach / PEAK_HBM_GBS,
-                                      "traffic": None, "algorithmic_bytes_per_launch": alg}}
+                                      "traffic": tj.get(f"decode_{nseq}seq", {}).get("bytes_per_launch"),
+                                      "algorithmic_bytes_per_launch": alg}}
 
     # ---------------- CPU oracle baseline ----------------
     if not args.no_cpu_baseline:

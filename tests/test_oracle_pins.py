@@ -28,37 +28,29 @@ def _case(seed, B=1, Hq=2, Hkv=1, T=12, d=8, dv=5, g_hi=3, scale=1.0):
 
 
 # --------------------------------------------------------------------------------------
-# 1. A worked example done by hand (d=4 so 1/sqrt(d) = 1/2; dv=2; G=2; T=3).
-#
-#   groups: dims {0,1} -> config g0 (s-bar index 1); dims {2,3} -> g1 (s-bar index 2)
-#   L = [[1,0,0],[0.5,1,0],[0,1,2]], eps = 0.25
-#   z_m = sum_{g>=m} L[g][m] s-bar_g ; kappa = eps + z0^2 + z1^2 + z2^2
-#   i=0,j=0: s-bar=[1,1,1]  -> z=[1.5,2,2]  -> kappa = 0.25+2.25+4+4 = 10.5
-#   i=1,j=0: s-bar=[1,1,1]  -> kappa = 10.5
-#   i=1,j=1: s-bar=[1,0,0]  -> z=[1,0,0]    -> kappa = 1.25
-#   i=2,j=0: s-bar=[1,0,1]  -> z=[1,1,2]    -> kappa = 6.25
-#   i=2,j=1: s-bar=[1,1,-1] -> z=[1.5,0,-2] -> kappa = 6.5
-#   i=2,j=2: s-bar=[1,0,1]  -> kappa = 6.25
-#   y0 = v0 = [1,0]; y1 = (10.5 v0 + 1.25 v1)/11.75 = [42/47, 5/47];
-#   y2 = (6.25 v0 + 6.5 v1 + 6.25 v2)/19 = [0, 1].
+# 1. A worked example done by hand (d=4 so 1/sqrt(d) = 1/2; dv=2; G=2; T=3), stored with
+# its derivation in tests/golden/worked_example_d4.json.
 # Catches: L used untransposed (L s-bar gives 12.5 at (0,0)), a missing 1/sqrt(d), a wrong
 # group offset into s-bar, exclusive causality, a dropped eps.
 
-WQ = np.array([[[[2, 0, 0, 2], [0, 2, 2, 0], [1, -1, 1, 1]]]], float)
-WK = np.array([[[[1, 1, 1, 1], [2, 0, 0, -2], [1, 1, -1, 3]]]], float)
-WV = np.array([[[[1, 0], [0, 1], [-1, 2]]]], float)
-WP = HeadParams(np.array([2], np.int32), np.array([[0, 0, 1, 1]], np.uint8),
-                np.array([[[1, 0, 0], [0.5, 1, 0], [0, 1, 2]]], np.float32),
-                np.array([0.25], np.float32))
+import json as _json
+
+_GOLD = _json.load(open(os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden",
+                                     "worked_example_d4.json")))
+WQ = np.array(_GOLD["q"], float)[None, None]
+WK = np.array(_GOLD["k"], float)[None, None]
+WV = np.array(_GOLD["v"], float)[None, None]
+WP = HeadParams(np.array([_GOLD["n_groups"]], np.int32), np.array([_GOLD["group_of_dim"]], np.uint8),
+                np.array([_GOLD["L"]], np.float32), np.array([_GOLD["eps"]], np.float32))
 
 
 def test_worked_example_by_hand():
     kap = oracle.kappa_matrix(WQ, WK, WP, 0, 0)
-    want = np.array([[10.5, 0, 0], [10.5, 1.25, 0], [6.25, 6.5, 6.25]])
-    np.testing.assert_allclose(kap, want, rtol=0, atol=1e-13)
+    np.testing.assert_allclose(kap, _GOLD["kappa"], rtol=0, atol=1e-13)
     y, den = oracle.dense(WQ, WK, WV, WP, return_den=True)
     np.testing.assert_allclose(y[0, 0], [[1, 0], [42 / 47, 5 / 47], [0, 1]], rtol=0, atol=1e-14)
-    np.testing.assert_allclose(den[0, 0], [10.5, 11.75, 19.0], rtol=0, atol=1e-13)
+    np.testing.assert_allclose(y[0, 0], _GOLD["y"], rtol=0, atol=1e-14)
+    np.testing.assert_allclose(den[0, 0], _GOLD["den"], rtol=0, atol=1e-13)
 
 
 def test_worked_example_state_by_hand():
@@ -68,10 +60,11 @@ def test_worked_example_state_by_hand():
     H = oracle.state(WK, WV)[0, 0]
     d = 4
     idx = lambda r, t: 1 + d + r * d - r * (r - 1) // 2 + (t - r)
-    np.testing.assert_allclose(H[0], [0, 3, 3])
-    np.testing.assert_allclose(H[1], [0, 4, 4])
-    np.testing.assert_allclose(H[idx(3, 3)], [-8, 22, 14])
-    np.testing.assert_allclose(H[idx(0, 3)], [-2, 2, 0])
+    rows = _GOLD["state_rows"]
+    np.testing.assert_allclose(H[0], rows["H0"])
+    np.testing.assert_allclose(H[1], rows["H1_0"])
+    np.testing.assert_allclose(H[idx(3, 3)], rows["H2_3_3"])
+    np.testing.assert_allclose(H[idx(0, 3)], rows["H2_0_3"])
     assert H.shape[0] == 1 + d + d * (d + 1) // 2
 
 
