@@ -9,6 +9,7 @@
 
 #include <cmath>
 #include <cstring>
+#include <utility>
 #include <vector>
 
 #include "oal.h"
@@ -56,7 +57,10 @@ oal_status check_params(const oal_dims *d, const oal_head_params *hp) {
     return OAL_OK;
 }
 
-void pack_head(const oal_head_params *hp, int h, OalHeadDev *out) {
+// Per-head coefficients. D receives the non-bulk remainder D[a][b] (config group ids,
+// G x G, zero where a or b is the bulk group); Mg the group block M[a+1][b+1].
+void pack_head(const oal_head_params *hp, int h, OalHeadDev *out, std::vector<double> &D,
+               std::vector<double> &Mg) {
     const int gm1 = hp->g_max + 1;
     const int G = hp->n_groups[h];
     const float *Lh = hp->L + (size_t)h * gm1 * gm1;
@@ -78,13 +82,21 @@ void pack_head(const oal_head_params *hp, int h, OalHeadDev *out) {
     int bulk = 0;
     for (int g = 1; g < G; ++g)
         if (count[g] > count[bulk]) bulk = g;
-    // rank-1 factor through the bulk column of the group block of M
+    // rank-1 factor through the bulk column of the group block of M (M is PSD, so a zero
+    // M[bulk][bulk] means a zero bulk row and column)
     std::vector<double> w0(G, 0.0);
     double mbb = Mq(bulk, bulk);
     if (mbb > 0.0) {
         double sq = std::sqrt(mbb);
         for (int a = 0; a < G; ++a) w0[a] = Mq(a, bulk) / sq;
     }
+    D.assign((size_t)G * G, 0.0);
+    Mg.assign((size_t)G * G, 0.0);
+    for (int a = 0; a < G; ++a)
+        for (int b = 0; b < G; ++b) {
+            Mg[a * G + b] = Mq(a, b);
+            if (a != bulk && b != bulk) D[a * G + b] = Mq(a, b) - w0[a] * w0[b];
+        }
     std::memset(out, 0, sizeof(OalHeadDev));
     out->G = G;
     out->bulk = bulk;
@@ -96,9 +108,6 @@ void pack_head(const oal_head_params *hp, int h, OalHeadDev *out) {
         out->lin[r] = (float)(2.0 * M[0 * (G + 1) + 1 + gam[r]]);
         out->w0[r] = (float)w0[gam[r]];
     }
-    for (int a = 0; a < G; ++a)
-        for (int b = 0; b < G; ++b)
-            out->Dg[a * OAL_D + b] = (a == bulk || b == bulk) ? 0.0f : (float)(Mq(a, b) - w0[a] * w0[b]);
     for (int m = 0; m <= G; ++m)
         for (int r = 0; r < OAL_D; ++r) {
             int gr = 1 + gam[r];
@@ -110,18 +119,24 @@ void pack_head(const oal_head_params *hp, int h, OalHeadDev *out) {
     for (int r = 0; r < OAL_D; ++r)
         for (int t = r; t < OAL_D; ++t)
             out->wdec[oal_quad_row(r, t)] = (float)((r < t ? 2.0 : 1.0) * Mq(gam[r], gam[t]) / 64.0);
-    // K-steps of the prefill slot order that hold a non-bulk x non-bulk pair
-    for (int tb = 0; tb < 8; ++tb)
-        for (int rq = 0; rq <= 2 * tb + 1; ++rq)
-            for (int g = 0; g < 4; ++g)
-                for (int e = 0; e < 8; ++e) {
-                    int ra, rb;
-                    if (oal_slot_kind(tb, rq, g, e, &ra, &rb) != OAL_SLOT_QUAD) continue;
-                    if (out->Dg[gam[ra] * OAL_D + gam[rb]] != 0.0f) {
-                        int s = oal_kstep(tb, rq);
-                        out->corr[s >> 5] |= 1u << (s & 31);
-                    }
-                }
+}
+
+// Tail pairs of the query heads [h0, h1) of one KV head: every (r <= t) whose remainder
+// D[g(r)][g(t)] is nonzero for at least one of the heads, in (r, t) order.
+std::vector<std::pair<int, int>> tail_pairs(const oal_head_params *hp, int h0, int h1,
+                                            const std::vector<std::vector<double>> &D) {
+    std::vector<std::pair<int, int>> pairs;
+    for (int r = 0; r < OAL_D; ++r)
+        for (int t = r; t < OAL_D; ++t) {
+            bool need = false;
+            for (int h = h0; h < h1 && !need; ++h) {
+                const uint8_t *gam = hp->group_of_dim + (size_t)h * OAL_D;
+                int G = hp->n_groups[h];
+                need = D[h][gam[r] * G + gam[t]] != 0.0;
+            }
+            if (need) pairs.emplace_back(r, t);
+        }
+    return pairs;
 }
 
 }  // namespace
@@ -143,7 +158,8 @@ const char *oal_status_string(oal_status s) {
 
 size_t oal_params_bytes(const oal_dims *d) {
     if (check_dims(d) != OAL_OK) return 0;
-    return sizeof(OalParamsHeader) + (size_t)d->n_q_heads * OAL_HEAD_BYTES;
+    return sizeof(OalParamsHeader) + (size_t)d->n_q_heads * OAL_HEAD_BYTES +
+           (size_t)d->n_kv_heads * OAL_KV_BYTES;
 }
 
 size_t oal_state_bytes(const oal_dims *d) {
@@ -178,8 +194,55 @@ oal_status oal_params_pack(const oal_dims *d, const oal_head_params *hp, void *b
     hdr->d_h = d->d_h;
     hdr->d_v = d->d_v;
     hdr->head_bytes = OAL_HEAD_BYTES;
-    for (int h = 0; h < d->n_q_heads; ++h)
-        pack_head(hp, h, reinterpret_cast<OalHeadDev *>(p + sizeof(OalParamsHeader) + (size_t)h * OAL_HEAD_BYTES));
+    hdr->n_kv_heads = d->n_kv_heads;
+    const int nq = d->n_q_heads, nkv = d->n_kv_heads, n_rep = nq / nkv;
+    auto head = [&](int h) {
+        return reinterpret_cast<OalHeadDev *>(p + sizeof(OalParamsHeader) + (size_t)h * OAL_HEAD_BYTES);
+    };
+    auto kvrec = [&](int kv) {
+        return reinterpret_cast<OalKvDev *>(p + sizeof(OalParamsHeader) + (size_t)nq * OAL_HEAD_BYTES +
+                                            (size_t)kv * OAL_KV_BYTES);
+    };
+    std::vector<std::vector<double>> D(nq), Mg(nq);
+    for (int h = 0; h < nq; ++h) pack_head(hp, h, head(h), D[h], Mg[h]);
+    std::vector<std::vector<std::pair<int, int>>> pairs(nkv);
+    for (int kv = 0; kv < nkv; ++kv) {
+        pairs[kv] = tail_pairs(hp, kv * n_rep, (kv + 1) * n_rep, D);
+        if ((int)pairs[kv].size() > OAL_TAIL_PAIRS) hdr->general = 1;
+    }
+    for (int kv = 0; kv < nkv; ++kv) {
+        OalKvDev *kr = kvrec(kv);
+        if (hdr->general) continue;   // no tail K-steps
+        kr->npairs = (int)pairs[kv].size();
+        kr->nsteps = (kr->npairs + 31) / 32;
+        for (int j = 0; j < kr->npairs; ++j) {
+            kr->ra[j] = (uint8_t)pairs[kv][j].first;
+            kr->rb[j] = (uint8_t)pairs[kv][j].second;
+        }
+        for (int h = kv * n_rep; h < (kv + 1) * n_rep; ++h) {
+            const uint8_t *gam = hp->group_of_dim + (size_t)h * OAL_D;
+            int G = hp->n_groups[h];
+            for (int j = 0; j < kr->npairs; ++j)
+                head(h)->tail[j] = (float)D[h][gam[kr->ra[j]] * G + gam[kr->rb[j]]];
+        }
+    }
+    if (hdr->general) {
+        // every quadratic slot carries its full coefficient; the rank-1 factor becomes 1
+        for (int h = 0; h < nq; ++h) {
+            OalHeadDev *hd = head(h);
+            const uint8_t *gam = hp->group_of_dim + (size_t)h * OAL_D;
+            int G = hp->n_groups[h];
+            for (int r = 0; r < OAL_D; ++r) hd->w0[r] = 1.0f;
+            for (int tb = 0; tb < 8; ++tb)
+                for (int rq = 0; rq <= 2 * tb + 1; ++rq)
+                    for (int g = 0; g < 4; ++g)
+                        for (int e = 0; e < 8; ++e) {
+                            int ra, rb;
+                            if (oal_slot_kind(tb, rq, g, e, &ra, &rb) != OAL_SLOT_QUAD) continue;
+                            hd->wslot[oal_kstep(tb, rq) * 32 + 8 * g + e] = (float)Mg[h][gam[ra] * G + gam[rb]];
+                        }
+        }
+    }
     return OAL_OK;
 }
 

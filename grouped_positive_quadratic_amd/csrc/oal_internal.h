@@ -27,6 +27,9 @@
 #define OAL_NFEAT 2145
 #define OAL_NQUAD 2080
 #define OAL_KSTEPS 72
+#define OAL_TAIL_STEPS 8          // extra K-steps for non-bulk x non-bulk pairs (per KV head)
+#define OAL_TAIL_PAIRS (32 * OAL_TAIL_STEPS)
+#define OAL_SNAP_KSTEPS (OAL_KSTEPS + OAL_TAIL_STEPS)
 #define OAL_PARAMS_MAGIC 0x314C414Fu  // "OAL1"
 #define OAL_MAX_G 64
 
@@ -57,8 +60,12 @@ OAL_HD inline int oal_kstep(int tb, int rq) { return tb * (tb + 1) + rq; }
 
 // Per-query-head coefficient record in the device parameter blob.
 //   Quadratic coefficients M[g(r)+1][g(t)+1] (M = L L^T) are split into a rank-1 part
-//   w0[r] * w0[t] that covers every pair touching the bulk group, and a correction D for
-//   pairs of two non-bulk dims, flagged per K-step in corr.
+//   w0[r] * w0[t] that covers every pair touching the bulk group, and a remainder D for
+//   pairs of two non-bulk dims. The non-bulk pairs of all query heads of a KV head are
+//   listed once per KV head (OalKvDev) and get extra "tail" K-steps in the prefill: tail
+//   slot j carries H2 of pair j (scaled like a quadratic slot) and head h multiplies it by
+//   tail[j] q_r q_t. If some KV head has more than OAL_TAIL_PAIRS such pairs, the blob is
+//   "general": w0 = 1 and the prefill reads the full coefficient of every slot from wslot.
 struct OalHeadDev {
     int32_t G;          // number of groups
     int32_t bulk;       // config id of the group carried by the rank-1 term
@@ -66,13 +73,23 @@ struct OalHeadDev {
     float a;            // eps + M[0][0]: constant-feature coefficient
     float L00;          // L[0][0]: constant part of z_0 = (L^T s-bar)_0
     float pad0[3];
-    uint32_t corr[4];   // bit s (s < 72): K-step s holds a non-bulk x non-bulk pair
     uint8_t gamma[64];  // config group id of each dim
     float lin[64];      // 2 M[0][g(r)+1]: linear coefficient (times q_r H1_r / 8)
-    float w0[64];       // rank-1 factor of dim r's group
-    float Dg[64 * 64];  // D[a][b] = M[a+1][b+1] - w0_a w0_b (config group ids), zero if a or b is bulk
+    float w0[64];       // rank-1 factor of dim r's group (1 in a general blob)
+    float tail[OAL_TAIL_PAIRS];        // D[g(r)][g(t)] for the KV head's tail pair j
     float Lz[65 * 64];  // Lz[m][r] = L[g(r)+1][m] / 8 (zero where g(r)+1 < m), m = 0..64
+    float wslot[OAL_KSTEPS * 32];      // general blob: M[g(r)+1][g(t)+1] per quadratic slot
     float wdec[2176];   // per state row f < 2145: coefficient of mono_f(q) . H_f (unscaled state)
+};
+
+// Per-KV-head record: the union over its query heads of the pairs (r <= t) whose dims are
+// both outside the head's bulk group with a nonzero remainder D.
+struct OalKvDev {
+    int32_t npairs;     // pairs listed
+    int32_t nsteps;     // tail K-steps used: ceil(npairs / 32) (0 in a general blob)
+    int32_t pad[62];
+    uint8_t ra[OAL_TAIL_PAIRS];
+    uint8_t rb[OAL_TAIL_PAIRS];
 };
 
 struct OalParamsHeader {
@@ -81,7 +98,10 @@ struct OalParamsHeader {
     int32_t d_h;
     int32_t d_v;
     int32_t head_bytes;
-    int32_t pad[59];    // 256 bytes
+    int32_t n_kv_heads;
+    int32_t general;    // 1: some KV head has more than OAL_TAIL_PAIRS tail pairs
+    int32_t pad[57];    // 256 bytes
 };
 
 #define OAL_HEAD_BYTES ((int)((sizeof(OalHeadDev) + 255) / 256 * 256))
+#define OAL_KV_BYTES ((int)((sizeof(OalKvDev) + 255) / 256 * 256))

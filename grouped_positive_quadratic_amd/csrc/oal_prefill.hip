@@ -18,11 +18,14 @@
 //     increments of the earlier segments, then walk the segment's chunks writing the state
 //     before each chunk (bf16 or fp32, scaled, in the MFMA operand order of the readout)
 //     and adding psi(K_c)^T [V_c;1] on MFMA. The last segment writes the final state back.
+//     Besides the 72 main K-steps, up to 8 tail K-steps repeat the KV head's non-bulk pairs.
 //  3. oal_readout
-//     per (sequence x KV head x head group, chunk, 16-query tile): the query heads of one
-//     KV head share every snapshot fragment. Two waves split the 72 K-steps of
-//     phi(Q) . S_c (odd/even rq) and the intra-chunk heads, then combine through LDS and
-//     divide: y = u~[0:64] / u~[64]. Workgroups of one chunk are placed on one XCD so the
+//     per (sequence x KV head x head group, chunk, 16-query tile), 4 waves: two head
+//     subsets times two K-step parities. The query heads of one KV head share every
+//     snapshot fragment. The A operand of a main K-step is p_r p_t with p = w0 o q (the
+//     rank-1 part of the group-pair coefficients); the tail K-steps add D q_r q_t for the
+//     non-bulk pairs. Then the intra-chunk kernel sum, a combine through LDS and the
+//     divide y = u~[0:64] / u~[64]. Workgroups of one chunk are placed on one XCD so the
 //     snapshot is fetched into that XCD's L2 once.
 #include <hip/hip_runtime.h>
 
@@ -53,20 +56,32 @@ __device__ inline void kstep_decode(int s, int &tb, int &rq) {
     rq = s - tb * (tb + 1);
 }
 
-// it-th K-step of one readout wave (rq of one parity): tb has tb+1 of them
-__device__ inline void wave_step(int it, int &tb, int &j) {
-    tb = 0;
-    while ((tb + 1) * (tb + 2) / 2 <= it) ++tb;
-    j = it - tb * (tb + 1) / 2;
+__device__ inline const OalKvDev *kv_ptr(const unsigned char *params, int n_q_heads, int kv) {
+    return reinterpret_cast<const OalKvDev *>(params + sizeof(OalParamsHeader) +
+                                              (size_t)n_q_heads * OAL_HEAD_BYTES + (size_t)kv * OAL_KV_BYTES);
 }
 
-// scale of a slot in the snapshot state (relative to H) and its state row; -1 = empty slot
-__device__ inline int slot_row(int tb, int rq, int g, int e, float &scale) {
-    int ra, rb;
-    int kind = oal_slot_kind(tb, rq, g, e, &ra, &rb);
-    if (kind == OAL_SLOT_QUAD) { scale = (ra < rb ? 2.0f : 1.0f) / 64.0f; return oal_quad_row(ra, rb); }
-    if (kind == OAL_SLOT_LIN) { scale = 0.125f; return 1 + ra; }
-    if (kind == OAL_SLOT_CONST) { scale = 1.0f; return 0; }
+// Slot (gs, e) of K-step s (main K-steps s < 72 as (tb, rq); tail K-steps s >= 72 list the
+// KV head's non-bulk pairs): the dims it multiplies (64 = the constant 1), its scale in the
+// snapshot relative to H, and its state row (-1: empty slot, zero in every snapshot).
+__device__ inline int scan_slot(int s, int tb, int rq, const OalKvDev *kvd, int gs, int e, int &ra,
+                                int &rb, float &scale) {
+    if (s < OAL_KSTEPS) {
+        int kind = oal_slot_kind(tb, rq, gs, e, &ra, &rb);
+        if (kind == OAL_SLOT_QUAD) { scale = (ra < rb ? 2.0f : 1.0f) / 64.0f; return oal_quad_row(ra, rb); }
+        if (kind == OAL_SLOT_LIN) { scale = 0.125f; return 1 + ra; }
+        if (kind == OAL_SLOT_CONST) { scale = 1.0f; return 0; }
+        scale = 0.0f;
+        return -1;
+    }
+    const int j = 32 * (s - OAL_KSTEPS) + 8 * gs + e;
+    if (j < kvd->npairs) {
+        ra = kvd->ra[j];
+        rb = kvd->rb[j];
+        scale = (ra < rb ? 2.0f : 1.0f) / 64.0f;
+        return oal_quad_row(ra, rb);
+    }
+    ra = rb = OAL_D;
     scale = 0.0f;
     return -1;
 }
@@ -123,9 +138,9 @@ __global__ __launch_bounds__(256) void oal_transpose_kv(int T_len, int Tpad, con
 // 1-2. chunk-state scan
 template <typename T, int C, int MODE>
 __global__ __launch_bounds__(64 * kScanWaves) void oal_scan(
-    int T_len, int Tpad, int nchunks, int nseg, int seg_len, const T *__restrict__ kT,
-    const T *__restrict__ vT, float *__restrict__ state, float *__restrict__ totals,
-    unsigned char *__restrict__ snap) {
+    int T_len, int Tpad, int nchunks, int nseg, int seg_len, int n_q_heads, int n_kv_heads,
+    const T *__restrict__ kT, const T *__restrict__ vT, const unsigned char *__restrict__ params,
+    float *__restrict__ state, float *__restrict__ totals, unsigned char *__restrict__ snap) {
     constexpr int EPU = 16 / (int)sizeof(T);
     constexpr int LD = C + EPU;                         // padded row, 16-byte aligned
     constexpr int UPR = C / EPU;                        // 16-byte units per row and chunk
@@ -136,25 +151,21 @@ __global__ __launch_bounds__(64 * kScanWaves) void oal_scan(
     T *s_vT = s_kT + 65 * LD;                           // [64][LD]
 
     const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63, g = lane >> 4, lr = lane & 15;
-    const int s = blockIdx.x * kScanWaves + wave;
+    const int s = blockIdx.x * kScanWaves + wave;     // blockIdx.x == 9: tail K-steps
     const int sigma = blockIdx.y;
     const int bkv = blockIdx.z;
-    int tb, rq;
-    kstep_decode(s, tb, rq);
+    const OalKvDev *kvd = kv_ptr(params, n_q_heads, bkv % n_kv_heads);
+    if (blockIdx.x == kScanBlocks && kvd->nsteps == 0) return;     // whole workgroup
+    // waves past the KV head's tail K-steps only help staging the chunks
+    const bool idle = s >= OAL_KSTEPS + kvd->nsteps;
+    int tb = 0, rq = 0;
+    if (s < OAL_KSTEPS) kstep_decode(s, tb, rq);
 
     // A operand (psi^T): this lane's feature row lr of tile h is slot (lr/4, 4h + lr%4)
     int ra[2], rb[2];
     float sig[2];
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-        int a, bb;
-        int kind = oal_slot_kind(tb, rq, lr >> 2, 4 * h + (lr & 3), &a, &bb);
-        ra[h] = a;
-        rb[h] = bb;
-        sig[h] = kind == OAL_SLOT_QUAD ? (a < bb ? 2.0f : 1.0f) / 64.0f
-               : kind == OAL_SLOT_LIN  ? 0.125f
-               : kind == OAL_SLOT_CONST ? 1.0f : 0.0f;
-    }
+    for (int h = 0; h < 2; ++h) scan_slot(s, tb, rq, kvd, lr >> 2, 4 * h + (lr & 3), ra[h], rb[h], sig[h]);
 
     oal_f32x4 acc[2][5];
 #pragma unroll
@@ -171,13 +182,14 @@ __global__ __launch_bounds__(64 * kScanWaves) void oal_scan(
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     float sc;
-                    int f = slot_row(tb, rq, g, 4 * h + i, sc);
+                    int x0, x1;
+                    int f = scan_slot(s, tb, rq, kvd, g, 4 * h + i, x0, x1, sc);
                     int col = n < 4 ? 16 * n + lr : (lr == 0 ? OAL_D : -1);
                     acc[h][n][i] = (f >= 0 && col >= 0) ? Sst[(size_t)f * OAL_V1 + col] * sc : 0.0f;
                 }
     };
     auto totals_at = [&](int idx) {
-        return totals + (((size_t)bkv * nseg + idx) * OAL_KSTEPS + s) * kTotalsPerLane * 64 + lane;
+        return totals + (((size_t)bkv * nseg + idx) * OAL_SNAP_KSTEPS + s) * kTotalsPerLane * 64 + lane;
     };
 
     const int c0 = sigma * seg_len, c1 = min(nchunks, c0 + seg_len);
@@ -254,8 +266,9 @@ __global__ __launch_bounds__(64 * kScanWaves) void oal_scan(
 #pragma unroll
             for (int j = 0; j < PER; ++j) pre[j] = *reinterpret_cast<const oal_u32x4 *>(src_u[j] + (size_t)(c + 1) * C);
         }
+        if (idle) continue;      // after the staging barriers, which every wave joins
         if (MODE == kSnapshots) {
-            unsigned char *sp = snap + (((size_t)bkv * nchunks + c) * OAL_KSTEPS + s) * KB;
+            unsigned char *sp = snap + (((size_t)bkv * nchunks + c) * OAL_SNAP_KSTEPS + s) * KB;
 #pragma unroll
             for (int n = 0; n < 4; ++n) {
                 float x[8];
@@ -299,6 +312,7 @@ __global__ __launch_bounds__(64 * kScanWaves) void oal_scan(
         }
     }
 
+    if (idle) return;
     if (MODE == kTotals) {
         float *tp = totals_at(sigma + 1);
 #pragma unroll
@@ -307,7 +321,7 @@ __global__ __launch_bounds__(64 * kScanWaves) void oal_scan(
             for (int n = 0; n < 5; ++n)
 #pragma unroll
                 for (int i = 0; i < 4; ++i) tp[((h * 5 + n) * 4 + i) * 64] = acc[h][n][i];
-    } else if (sigma == nseg - 1) {
+    } else if (sigma == nseg - 1 && s < OAL_KSTEPS) {   // tail rows duplicate main rows
 #pragma unroll
         for (int h = 0; h < 2; ++h)
 #pragma unroll
@@ -315,7 +329,8 @@ __global__ __launch_bounds__(64 * kScanWaves) void oal_scan(
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     float sc;
-                    int f = slot_row(tb, rq, g, 4 * h + i, sc);
+                    int x0, x1;
+                    int f = scan_slot(s, tb, rq, kvd, g, 4 * h + i, x0, x1, sc);
                     int col = n < 4 ? 16 * n + lr : (lr == 0 ? OAL_D : -1);
                     if (f >= 0 && col >= 0) Sst[(size_t)f * OAL_V1 + col] = acc[h][n][i] / sc;
                 }
@@ -326,10 +341,10 @@ __global__ __launch_bounds__(64 * kScanWaves) void oal_scan(
 // 3. readout
 template <typename T, int C, int R> struct ReadoutLayout {
     static constexpr int EPU = 16 / (int)sizeof(T);
+    static constexpr int RW = (R + 1) / 2;      // heads of one wave pair (head subset)
     static constexpr int QS = OAL_D + EPU;      // q / key row in LDS (16-byte aligned)
     static constexpr int LDV = C + EPU;         // V^T row
     static constexpr int PS = OAL_D + 4;        // fp32 p-table row
-    static constexpr int DG = 8;                // D block kept in LDS (heads with G <= 8)
     static constexpr int LZR = 8;               // Lz rows m < 8 kept in LDS
     // Byte offsets. The "union" region holds the fp32 p table during the inter-chunk loop,
     // then K and V^T of the chunk during the intra-chunk part, then the combine buffer.
@@ -340,14 +355,16 @@ template <typename T, int C, int R> struct ReadoutLayout {
                                                       : (KV_BYTES > X_BYTES ? KV_BYTES : X_BYTES);
     static constexpr int O_U = 0;
     static constexpr int O_Q = O_U + U_BYTES;                                 // T [R*16][QS]
-    static constexpr int O_W0 = O_Q + R * 16 * QS * (int)sizeof(T);           // f32 [R][64]
-    static constexpr int O_LIN = O_W0 + R * OAL_D * 4;                        // f32 [R][64]
-    static constexpr int O_D = O_LIN + R * OAL_D * 4;                         // f32 [R][8][8]
-    static constexpr int O_LZ = O_D + R * DG * DG * 4;                        // f32 [R][LZR][64]
-    static constexpr int O_GAM = O_LZ + R * LZR * OAL_D * 4;                  // u8 [R][64]
-    static constexpr int BYTES = O_GAM + R * OAL_D;
-    static constexpr int META_UNITS = 16 + 16 + 4 + DG * DG / 4 + LZR * 16;   // 16-byte units / head
-    static_assert(U_BYTES % 16 == 0 && O_Q % 16 == 0 && O_W0 % 16 == 0 && O_LZ % 16 == 0, "alignment");
+    static constexpr int O_LIN = O_Q + R * 16 * QS * (int)sizeof(T);         // f32 [R][64]
+    static constexpr int O_W0 = O_LIN + R * OAL_D * 4;                        // f32 [R][64]
+    static constexpr int O_TAIL = O_W0 + R * OAL_D * 4;                       // f32 [R][TAIL_PAIRS]
+    static constexpr int O_LZ = O_TAIL + R * OAL_TAIL_PAIRS * 4;              // f32 [R][LZR][64]
+    static constexpr int O_PAIR = O_LZ + R * LZR * OAL_D * 4;                 // u8 [2][TAIL_PAIRS]
+    static constexpr int BYTES = O_PAIR + 2 * OAL_TAIL_PAIRS;
+    static constexpr int META_UNITS = 16 + 16 + OAL_TAIL_PAIRS / 4 + LZR * 16;   // 16-byte units / head
+    static constexpr int PAIR_UNITS = 2 * OAL_TAIL_PAIRS / 16;
+    static_assert(U_BYTES % 16 == 0 && O_Q % 16 == 0 && O_LIN % 16 == 0 && O_TAIL % 16 == 0 &&
+                  O_LZ % 16 == 0 && O_PAIR % 16 == 0, "alignment");
 };
 
 // One term z_m of the intra-chunk kernel for a 16-query tile of one head:
@@ -387,27 +404,33 @@ __device__ inline void oal_z_step(const float (&lzv)[16], float cm, const T *qro
     }
 }
 
+// Workgroup = (sequence x KV head x head group of R heads, chunk, 16-query tile), 4 waves:
+// wave = (head subset hs, K-step parity par). Subset 0 holds heads 0..RW-1, subset 1 the
+// rest; the two waves of a subset split the K-steps by the parity of rq (and of the tail
+// index), so each snapshot fragment is fetched by the two subsets' waves of that parity
+// from L2/L1 and used for all their heads.
 template <typename T, int C, int R>
-__global__ __launch_bounds__(128) void oal_readout(
+__global__ __launch_bounds__(256, 2) void oal_readout(
     int T_len, int Tpad, int n_q_heads, int n_kv_heads, int nchunks, int n_hgroups, int nunits,
     const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ vT,
     const unsigned char *__restrict__ params, const unsigned char *__restrict__ snap,
     float *__restrict__ y) {
     using Lay = ReadoutLayout<T, C, R>;
-    constexpr int EPU = Lay::EPU, QS = Lay::QS, LDV = Lay::LDV, DG = Lay::DG, PS = Lay::PS;
+    constexpr int EPU = Lay::EPU, QS = Lay::QS, LDV = Lay::LDV, PS = Lay::PS, RW = Lay::RW;
     constexpr int NQT = C / 16;
     constexpr int UPQ = OAL_D / EPU;            // 16-byte units per q/k row
+    constexpr int NMAIN = OAL_KSTEPS / 2;       // main K-steps per parity
     extern __shared__ __align__(16) unsigned char smem[];
     float *s_p = reinterpret_cast<float *>(smem + Lay::O_U);               // inter: [R*16][PS]
     T *s_k = reinterpret_cast<T *>(smem + Lay::O_U);                       // intra: [C][QS]
     T *s_vT = s_k + C * QS;                                                // intra: [64][LDV]
     float *s_x = reinterpret_cast<float *>(smem + Lay::O_U);               // combine
     T *s_q = reinterpret_cast<T *>(smem + Lay::O_Q);
-    float *s_w0 = reinterpret_cast<float *>(smem + Lay::O_W0);
     float *s_lin = reinterpret_cast<float *>(smem + Lay::O_LIN);
-    float *s_D = reinterpret_cast<float *>(smem + Lay::O_D);
+    float *s_w0 = reinterpret_cast<float *>(smem + Lay::O_W0);
+    float *s_tail = reinterpret_cast<float *>(smem + Lay::O_TAIL);
     float *s_lz = reinterpret_cast<float *>(smem + Lay::O_LZ);
-    unsigned char *s_gam = smem + Lay::O_GAM;
+    unsigned char *s_pair = smem + Lay::O_PAIR;
 
     // XCD-aware placement: the NQT workgroups of one unit (chunk, KV head, head group)
     // get block ids congruent mod 8, i.e. the same XCD and L2.
@@ -419,41 +442,52 @@ __global__ __launch_bounds__(128) void oal_readout(
     const int b = bkv / n_kv_heads, kv = bkv % n_kv_heads;
     const int n_rep = n_q_heads / n_kv_heads;
     const int h0 = kv * n_rep + hg * R;
-    const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63, g = lane >> 4, lr = lane & 15;
+    const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+    const int g = lane >> 4, lr = lane & 15;
+    const int hs = wave >> 1, par = wave & 1;
+    const int hb = hs * RW;                       // first local head of this wave's subset
+    const int nh = hs == 0 ? RW : R - RW;         // heads of the subset (0 when R == 1)
     const int pos0 = c * C + qt * 16;
     if (pos0 >= T_len) return;
+    const bool general = reinterpret_cast<const OalParamsHeader *>(params)->general != 0;
+    const OalKvDev *kvd = kv_ptr(params, n_q_heads, kv);
+    const int ntail = general ? 0 : kvd->nsteps;
 
-    // 1. stage the tile's queries and the per-head tables (all loads issued before any LDS
-    //    write), and warm this XCD's L2 with 1/NQT of the chunk's snapshot: the NQT
-    //    workgroups of the unit run side by side on this XCD, so together they bring the
-    //    snapshot in once. The warming loads only feed a value that is never stored.
+    // 1. stage the tile's queries, the per-head tables and the KV head's tail pairs (all
+    //    loads issued before any LDS write), and warm this XCD's L2 with 1/NQT of the
+    //    chunk's snapshot: the NQT workgroups of the unit run side by side on this XCD, so
+    //    together they bring the snapshot in once. The warming loads only feed a value
+    //    that is never stored.
     {
-        constexpr int NQU = R * 16 * UPQ, NMU = R * Lay::META_UNITS;
-        constexpr int NQJ = (NQU + 127) / 128, NMJ = (NMU + 127) / 128;
+        constexpr int NQU = R * 16 * UPQ, NMU = R * Lay::META_UNITS + Lay::PAIR_UNITS;
+        constexpr int NQJ = (NQU + 255) / 256, NMJ = (NMU + 255) / 256;
         oal_u32x4 rq[NQJ], rm[NMJ];
         auto meta_src = [&](int u) -> const oal_u32x4 * {
+            if (u >= R * Lay::META_UNITS) {
+                int w = u - R * Lay::META_UNITS;
+                return w < OAL_TAIL_PAIRS / 16 ? reinterpret_cast<const oal_u32x4 *>(kvd->ra) + w
+                                               : reinterpret_cast<const oal_u32x4 *>(kvd->rb) + (w - OAL_TAIL_PAIRS / 16);
+            }
             const OalHeadDev *hd = head_ptr(params, h0 + u / Lay::META_UNITS);
             int w = u % Lay::META_UNITS;
-            if (w < 16) return reinterpret_cast<const oal_u32x4 *>(hd->w0) + w;
-            if ((w -= 16) < 16) return reinterpret_cast<const oal_u32x4 *>(hd->lin) + w;
-            if ((w -= 16) < 4) return reinterpret_cast<const oal_u32x4 *>(hd->gamma) + w;
-            if ((w -= 4) < DG * DG / 4)
-                return reinterpret_cast<const oal_u32x4 *>(hd->Dg + (w / (DG / 4)) * OAL_D) + w % (DG / 4);
-            w -= DG * DG / 4;
+            if (w < 16) return reinterpret_cast<const oal_u32x4 *>(hd->lin) + w;
+            if ((w -= 16) < 16) return reinterpret_cast<const oal_u32x4 *>(hd->w0) + w;
+            if ((w -= 16) < OAL_TAIL_PAIRS / 4) return reinterpret_cast<const oal_u32x4 *>(hd->tail) + w;
+            w -= OAL_TAIL_PAIRS / 4;
             return reinterpret_cast<const oal_u32x4 *>(hd->Lz) + w;
         };
         auto meta_dst = [&](int u) -> oal_u32x4 * {
+            if (u >= R * Lay::META_UNITS) return reinterpret_cast<oal_u32x4 *>(s_pair) + (u - R * Lay::META_UNITS);
             int i = u / Lay::META_UNITS, w = u % Lay::META_UNITS;
-            if (w < 16) return reinterpret_cast<oal_u32x4 *>(s_w0 + i * OAL_D) + w;
-            if ((w -= 16) < 16) return reinterpret_cast<oal_u32x4 *>(s_lin + i * OAL_D) + w;
-            if ((w -= 16) < 4) return reinterpret_cast<oal_u32x4 *>(s_gam + i * OAL_D) + w;
-            if ((w -= 4) < DG * DG / 4) return reinterpret_cast<oal_u32x4 *>(s_D + i * DG * DG) + w;
-            w -= DG * DG / 4;
+            if (w < 16) return reinterpret_cast<oal_u32x4 *>(s_lin + i * OAL_D) + w;
+            if ((w -= 16) < 16) return reinterpret_cast<oal_u32x4 *>(s_w0 + i * OAL_D) + w;
+            if ((w -= 16) < OAL_TAIL_PAIRS / 4) return reinterpret_cast<oal_u32x4 *>(s_tail + i * OAL_TAIL_PAIRS) + w;
+            w -= OAL_TAIL_PAIRS / 4;
             return reinterpret_cast<oal_u32x4 *>(s_lz + i * Lay::LZR * OAL_D) + w;
         };
 #pragma unroll
         for (int j = 0; j < NQJ; ++j) {
-            int u = tid + 128 * j;
+            int u = tid + 256 * j;
             int i = u / (16 * UPQ), qi = (u / UPQ) % 16, a = u % UPQ, pos = pos0 + qi;
             rq[j] = (u < NQU && pos < T_len)
                 ? *reinterpret_cast<const oal_u32x4 *>(q + (((size_t)b * n_q_heads + h0 + i) * T_len + pos) * OAL_D + a * EPU)
@@ -461,202 +495,231 @@ __global__ __launch_bounds__(128) void oal_readout(
         }
 #pragma unroll
         for (int j = 0; j < NMJ; ++j) {
-            int u = tid + 128 * j;
+            int u = tid + 256 * j;
             rm[j] = u < NMU ? *meta_src(u) : zero16();
         }
         constexpr int SNAP_UNITS = OAL_KSTEPS * snap_kstep_bytes<T>() / 16;
         constexpr int SHARE = (SNAP_UNITS + NQT - 1) / NQT;
-        constexpr int NTJ = (SHARE + 127) / 128;
+        constexpr int NTJ = (SHARE + 255) / 256;
         const oal_u32x4 *sn = reinterpret_cast<const oal_u32x4 *>(
-            snap + ((size_t)bkv * nchunks + c) * OAL_KSTEPS * snap_kstep_bytes<T>());
+            snap + ((size_t)bkv * nchunks + c) * OAL_SNAP_KSTEPS * snap_kstep_bytes<T>());
         oal_u32x4 touch = zero16();
 #pragma unroll
         for (int j = 0; j < NTJ; ++j) {
-            int u = qt * SHARE + tid + 128 * j;
-            if (tid + 128 * j < SHARE && u < SNAP_UNITS) touch ^= sn[u];
+            int u = qt * SHARE + tid + 256 * j;
+            if (tid + 256 * j < SHARE && u < SNAP_UNITS) touch ^= sn[u];
         }
 #pragma unroll
         for (int j = 0; j < NQJ; ++j) {
-            int u = tid + 128 * j;
+            int u = tid + 256 * j;
             int i = u / (16 * UPQ), qi = (u / UPQ) % 16, a = u % UPQ;
             if (u < NQU) *reinterpret_cast<oal_u32x4 *>(s_q + (i * 16 + qi) * QS + a * EPU) = rq[j];
         }
 #pragma unroll
         for (int j = 0; j < NMJ; ++j) {
-            int u = tid + 128 * j;
+            int u = tid + 256 * j;
             if (u < NMU) *meta_dst(u) = rm[j];
         }
         if (touch.x == 0x9e3779b9u && touch.y == 0x7f4a7c15u && T_len < 0) y[0] = 0.0f;  // never true
     }
     __syncthreads();
     // p table: p = w0[r] q_r (fp32), the rank-1 factor of the quadratic coefficients
-    for (int u = tid; u < R * 16 * OAL_D; u += 128) {
+    for (int u = tid; u < R * 16 * OAL_D; u += 256) {
         int i = u / (16 * OAL_D), qi = (u / OAL_D) % 16, r = u % OAL_D;
         s_p[(i * 16 + qi) * PS + r] = s_w0[i * OAL_D + r] * (float)s_q[(i * 16 + qi) * QS + r];
     }
     __syncthreads();
 
-    // per-head scalars (uniform)
-    uint64_t corr_lo[R], corr_hi[R];   // K-step bits 0..63 and 64..71
-    float a_h[R];
-    int bulk_h[R], G_h[R];
+    float a_h[RW];
 #pragma unroll
-    for (int i = 0; i < R; ++i) {
-        const OalHeadDev *hd = head_ptr(params, h0 + i);
-        corr_lo[i] = (uint64_t)hd->corr[0] | ((uint64_t)hd->corr[1] << 32);
-        corr_hi[i] = hd->corr[2];
-        a_h[i] = hd->a;
-        bulk_h[i] = hd->bulk;
-        G_h[i] = hd->G;
-    }
+    for (int li = 0; li < RW; ++li) a_h[li] = li < nh ? head_ptr(params, h0 + hb + li)->a : 0.0f;
 
-    oal_f32x4 acc[R][5];
+    oal_f32x4 acc[RW][5];
 #pragma unroll
-    for (int i = 0; i < R; ++i)
+    for (int li = 0; li < RW; ++li)
 #pragma unroll
-        for (int n = 0; n < 5; ++n) acc[i][n] = oal_splat(0.0f);
+        for (int n = 0; n < 5; ++n) acc[li][n] = oal_splat(0.0f);
 
-    // 2. inter-chunk: phi(Q) . S_c over this wave's 36 K-steps (rq = 2 j + wave); snapshot
-    //    fragments are fetched two K-steps ahead
+    // 2. inter-chunk: phi(Q) . S_c over this wave's K-steps: the 36 main K-steps with
+    //    rq = 2 j + par, then the tail K-steps 2 x + par. Snapshot fragments are fetched two
+    //    steps ahead into a ring of three buffers (the loop is unrolled by three so that the
+    //    ring needs no register moves).
     constexpr int KB = snap_kstep_bytes<T>();
-    constexpr int NSTEP = OAL_KSTEPS / 2;
-    const unsigned char *sbase = snap + ((size_t)bkv * nchunks + c) * OAL_KSTEPS * KB;
-    auto load_b = [&](OalFrag<T> (&bf)[5], int it) {
-        int tb2, j2;
-        wave_step(it, tb2, j2);
-        const unsigned char *sp = sbase + (size_t)oal_kstep(tb2, 2 * j2 + wave) * KB;
+    const unsigned char *sbase = snap + ((size_t)bkv * nchunks + c) * OAL_SNAP_KSTEPS * KB;
+    const int ntot = NMAIN + (ntail + 1 - par) / 2;
+    int ptb = 0, pj = 0, px = 0;                  // prefetch position
+    auto load_next = [&](OalFrag<T> (&bf)[5]) {
+        int sk;
+        if (ptb < 8) {
+            sk = oal_kstep(ptb, 2 * pj + par);
+            if (++pj > ptb) { ++ptb; pj = 0; }
+        } else {
+            sk = OAL_KSTEPS + 2 * px + par;
+            ++px;
+        }
+        const unsigned char *sp = sbase + (size_t)sk * KB;
 #pragma unroll
         for (int n = 0; n < 4; ++n) bf[n].load(sp + (n * 64 + lane) * OalFrag<T>::kBytes);
         if (lr == 0) bf[4].load(sp + (4 * 64 + g) * OalFrag<T>::kBytes);
         else bf[4].zero();
     };
-    // Two copies of the loop, chosen once: with every head at <= DG groups the correction
-    // block D is read from LDS only, so no global load is consumed inside the loop (which
-    // would also wait for the snapshot prefetches, vmcnt being in order).
-    auto inter = [&](auto big_g) {
-        constexpr bool BIG = decltype(big_g)::value;
-        OalFrag<T> b0[5], b1[5], b2[5];
-        float pt[R][8];
-        load_b(b0, 0);
-        load_b(b1, 1);
-        for (int it = 0; it < NSTEP; ++it) {
-            int tb, j;
-            wave_step(it, tb, j);
-            const int rq = 2 * j + wave;
-            const int s = oal_kstep(tb, rq);
-            if (it + 2 < NSTEP) load_b(b2, it + 2);
+    auto inter = [&](auto gen) {
+        constexpr bool GEN = decltype(gen)::value;
+        int tb = 0, j = 0;                        // compute position
+        float pt[RW][8];
+        auto main_step = [&](const OalFrag<T> (&bc)[5]) {
+            const int rq = 2 * j + par;
             const int r = 4 * rq + g;
-            // LDS reads of every head first, one wait, then the arithmetic
             if (j == 0) {
 #pragma unroll
-                for (int i = 0; i < R; ++i) {
-                    const float4 *pp = reinterpret_cast<const float4 *>(s_p + (i * 16 + lr) * PS + 8 * tb);
-                    float4 x0 = pp[0], x1 = pp[1];
-                    pt[i][0] = x0.x; pt[i][1] = x0.y; pt[i][2] = x0.z; pt[i][3] = x0.w;
-                    pt[i][4] = x1.x; pt[i][5] = x1.y; pt[i][6] = x1.z; pt[i][7] = x1.w;
+                for (int li = 0; li < RW; ++li) {
+                    if (li < nh) {
+                        const float4 *pp = reinterpret_cast<const float4 *>(s_p + ((hb + li) * 16 + lr) * PS + 8 * tb);
+                        float4 x0 = pp[0], x1 = pp[1];
+                        pt[li][0] = x0.x; pt[li][1] = x0.y; pt[li][2] = x0.z; pt[li][3] = x0.w;
+                        pt[li][4] = x1.x; pt[li][5] = x1.y; pt[li][6] = x1.z; pt[li][7] = x1.w;
+                    }
                 }
             }
-            float prv[R];
+            float prv[RW];
 #pragma unroll
-            for (int i = 0; i < R; ++i) prv[i] = s_p[(i * 16 + lr) * PS + r];
-            const bool lin_step = (rq == 2 * tb + 1);
-            float lin0[R], lin1[R];
+            for (int li = 0; li < RW; ++li) prv[li] = li < nh ? s_p[((hb + li) * 16 + lr) * PS + r] : 0.0f;
+            const bool lin_step = par == 1 && j == tb;
+            float lin0[RW], lin1[RW];
             if (lin_step) {
                 const int r0 = 8 * tb + 2 * g;
 #pragma unroll
-                for (int i = 0; i < R; ++i) {
-                    const T *qrow = s_q + (i * 16 + lr) * QS;
-                    lin0[i] = s_lin[i * OAL_D + r0] * (float)qrow[r0];
-                    lin1[i] = s_lin[i * OAL_D + r0 + 1] * (float)qrow[r0 + 1];
+                for (int li = 0; li < RW; ++li) {
+                    const T *qrow = s_q + ((hb + li) * 16 + lr) * QS;
+                    lin0[li] = s_lin[(hb + li) * OAL_D + r0] * (float)qrow[r0];
+                    lin1[li] = s_lin[(hb + li) * OAL_D + r0 + 1] * (float)qrow[r0 + 1];
                 }
             }
 #pragma unroll
-            for (int i = 0; i < R; ++i) {
-                float phi[8];
+            for (int li = 0; li < RW; ++li) {
+                if (li < nh) {
+                    float phi[8];
 #pragma unroll
-                for (int e = 0; e < 8; ++e) phi[e] = prv[i] * pt[i][e];
-                if (lin_step) {
-                    phi[0] = lin0[i];
-                    phi[1] = lin1[i];
-                    if (tb == 0 && g == 0) phi[2] = a_h[i];
+                    for (int e = 0; e < 8; ++e) phi[e] = prv[li] * pt[li][e];
+                    if (GEN) {
+                        // general blob: the full coefficient of each slot, from the blob
+                        const float4 *wp = reinterpret_cast<const float4 *>(
+                            head_ptr(params, h0 + hb + li)->wslot + oal_kstep(tb, rq) * 32 + 8 * g);
+                        const float4 w0v = wp[0], w1v = wp[1];
+                        phi[0] *= w0v.x; phi[1] *= w0v.y; phi[2] *= w0v.z; phi[3] *= w0v.w;
+                        phi[4] *= w1v.x; phi[5] *= w1v.y; phi[6] *= w1v.z; phi[7] *= w1v.w;
+                    }
+                    if (lin_step) {
+                        phi[0] = lin0[li];
+                        phi[1] = lin1[li];
+                        if (tb == 0 && g == 0) phi[2] = a_h[li];
+                    }
+                    OalFrag<T> a;
+                    a.set(phi);
+#pragma unroll
+                    for (int n = 0; n < 5; ++n) acc[li][n] = oal_mma(a, bc[n], acc[li][n]);
                 }
-                const uint64_t cbit = s < 64 ? (corr_lo[i] >> (s & 63)) : (corr_hi[i] >> ((s - 64) & 63));
-                if (cbit & 1u) {
-                    // pairs of two non-bulk dims: phi += D[g(r)][g(t)] q_r q_t (all loads first)
-                    const T *qrow = s_q + (i * 16 + lr) * QS;
-                    const int gr = s_gam[i * OAL_D + r];
-                    const float qr = (float)qrow[r];
-                    int gt[8];
-                    float qtv[8], dv[8];
+            }
+            if (++j > tb) { ++tb; j = 0; }
+        };
+        // tail K-step x: slot jj = 32 x + 8 g + e carries pair (ra[jj], rb[jj]); head li adds
+        // tail[jj] q_ra q_rb (zero past the KV head's pairs)
+        auto tail_step = [&](const OalFrag<T> (&bc)[5], int x) {
+            const int j0 = 32 * x + 8 * g;
+            const uint2 pra = *reinterpret_cast<const uint2 *>(s_pair + j0);
+            const uint2 prb = *reinterpret_cast<const uint2 *>(s_pair + OAL_TAIL_PAIRS + j0);
+            int ia[8], ib[8];
 #pragma unroll
-                    for (int e = 0; e < 8; ++e) {
-                        gt[e] = s_gam[i * OAL_D + 8 * tb + e];
-                        qtv[e] = (float)qrow[8 * tb + e];
-                    }
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) {
-                        const int gte = gt[e] < DG ? gt[e] : 0;
-                        dv[e] = BIG ? head_ptr(params, h0 + i)->Dg[gr * OAL_D + gt[e]]
-                                    : s_D[(i * DG + (gr < DG ? gr : 0)) * DG + gte];
-                    }
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) {
-                        const bool on = gt[e] != bulk_h[i] && r <= 8 * tb + e;
-                        phi[e] += on ? dv[e] * qr * qtv[e] : 0.0f;
-                    }
-                }
-                OalFrag<T> a;
-                a.set(phi);
-#pragma unroll
-                for (int n = 0; n < 5; ++n) acc[i][n] = oal_mma(a, b0[n], acc[i][n]);
+            for (int e = 0; e < 8; ++e) {
+                ia[e] = ((e < 4 ? pra.x : pra.y) >> (8 * (e & 3))) & 0xff;
+                ib[e] = ((e < 4 ? prb.x : prb.y) >> (8 * (e & 3))) & 0xff;
             }
 #pragma unroll
-            for (int n = 0; n < 5; ++n) {
-                b0[n] = b1[n];
-                b1[n] = b2[n];
+            for (int li = 0; li < RW; ++li) {
+                if (li < nh) {
+                    const T *qrow = s_q + ((hb + li) * 16 + lr) * QS;
+                    const float4 *cp = reinterpret_cast<const float4 *>(s_tail + (hb + li) * OAL_TAIL_PAIRS + j0);
+                    float4 c0 = cp[0], c1 = cp[1];
+                    float cf[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
+                    float qa[8], qb[8];
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) { qa[e] = (float)qrow[ia[e]]; qb[e] = (float)qrow[ib[e]]; }
+                    float phi[8];
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) phi[e] = cf[e] * qa[e] * qb[e];
+                    OalFrag<T> a;
+                    a.set(phi);
+#pragma unroll
+                    for (int n = 0; n < 5; ++n) acc[li][n] = oal_mma(a, bc[n], acc[li][n]);
+                }
+            }
+        };
+        static_assert(NMAIN % 3 == 0, "the main loop is unrolled by three");
+        OalFrag<T> b0[5], b1[5], b2[5];
+        load_next(b0);
+        load_next(b1);
+        for (int it = 0; it < NMAIN; it += 3) {
+            load_next(b2);
+            main_step(b0);
+            if (it + 3 < ntot) load_next(b0);
+            main_step(b1);
+            if (it + 4 < ntot) load_next(b1);
+            main_step(b2);
+        }
+        // tail K-steps (b0 and b1 already hold the first two)
+        for (int x = 0; x < ntot - NMAIN; x += 3) {
+            if (NMAIN + x + 2 < ntot) load_next(b2);
+            tail_step(b0, 2 * x + par);
+            if (x + 1 < ntot - NMAIN) {
+                if (NMAIN + x + 3 < ntot) load_next(b0);
+                tail_step(b1, 2 * (x + 1) + par);
+            }
+            if (x + 2 < ntot - NMAIN) {
+                if (NMAIN + x + 4 < ntot) load_next(b1);
+                tail_step(b2, 2 * (x + 2) + par);
             }
         }
     };
-    bool big_g = false;
-#pragma unroll
-    for (int i = 0; i < R; ++i) big_g |= G_h[i] > DG;
-    if (big_g) inter(std::true_type{});
-    else inter(std::false_type{});
+    if (nh > 0) {
+        if (general) inter(std::true_type{});
+        else inter(std::false_type{});
+    }
 
     // 3. stage K and V^T of the keys this tile can see into the region the p table used
     {
         const int nkeys = ((qt + 2) / 2) * 32;   // rounded to 32 (<= C)
         const int nku = nkeys * UPQ, nvu = OAL_D * (nkeys / EPU);
-        constexpr int NKJ = (C * UPQ + 127) / 128, NVJ = (OAL_D * (C / EPU) + 127) / 128;
+        constexpr int NKJ = (C * UPQ + 255) / 256, NVJ = (OAL_D * (C / EPU) + 255) / 256;
         const T *kb = k + (size_t)bkv * T_len * OAL_D;
         const T *vTb = vT + (size_t)bkv * OAL_D * Tpad + (size_t)c * C;
         oal_u32x4 rk[NKJ], rv[NVJ];
 #pragma unroll
         for (int j = 0; j < NKJ; ++j) {
-            int u = tid + 128 * j, key = u / UPQ, a = u % UPQ, pos = c * C + key;
+            int u = tid + 256 * j, key = u / UPQ, a = u % UPQ, pos = c * C + key;
             rk[j] = (u < nku && pos < T_len) ? *reinterpret_cast<const oal_u32x4 *>(kb + (size_t)pos * OAL_D + a * EPU) : zero16();
         }
 #pragma unroll
         for (int j = 0; j < NVJ; ++j) {
-            int u = tid + 128 * j, row = u / (nkeys / EPU), cu = u % (nkeys / EPU);
+            int u = tid + 256 * j, row = u / (nkeys / EPU), cu = u % (nkeys / EPU);
             rv[j] = u < nvu ? *reinterpret_cast<const oal_u32x4 *>(vTb + (size_t)row * Tpad + cu * EPU) : zero16();
         }
-        __syncthreads();    // both waves are done with the p table
+        __syncthreads();    // every wave is done with the p table
 #pragma unroll
         for (int j = 0; j < NKJ; ++j) {
-            int u = tid + 128 * j, key = u / UPQ, a = u % UPQ;
+            int u = tid + 256 * j, key = u / UPQ, a = u % UPQ;
             if (u < nku) *reinterpret_cast<oal_u32x4 *>(s_k + key * QS + a * EPU) = rk[j];
         }
 #pragma unroll
         for (int j = 0; j < NVJ; ++j) {
-            int u = tid + 128 * j, row = u / (nkeys / EPU), cu = u % (nkeys / EPU);
+            int u = tid + 256 * j, row = u / (nkeys / EPU), cu = u % (nkeys / EPU);
             if (u < nvu) *reinterpret_cast<oal_u32x4 *>(s_vT + row * LDV + cu * EPU) = rv[j];
         }
         __syncthreads();
     }
 
     // 4. intra-chunk: kappa = eps + sum_m z_m^2 with z_m = L00 [m==0] + sum_r Lz[m][r] q_r k_r,
-    //    z_m^T tiles (16 keys x 16 queries) on MFMA, then kappa [V;1] on MFMA.
+    //    z_m^T tiles (16 keys x 16 queries) on MFMA, then kappa [V;1] on MFMA. Local head li
+    //    of a subset is done by the subset's wave with parity li & 1.
     OalFrag<T> ones, zeros;
     {
         float o[8], zz[8];
@@ -666,15 +729,16 @@ __global__ __launch_bounds__(128) void oal_readout(
         zeros.set(zz);
     }
 #pragma unroll
-    for (int i = 0; i < R; ++i) {
-        if ((i & 1) != wave) continue;
+    for (int li = 0; li < RW; ++li) {
+        if (li >= nh || (li & 1) != par) continue;
+        const int i = hb + li;
         const OalHeadDev *hd = head_ptr(params, h0 + i);
         const T *qrow = s_q + (i * 16 + lr) * QS;
         oal_f32x4 kap[NQT];
         const float eps = hd->eps, L00 = hd->L00;
 #pragma unroll
         for (int kt = 0; kt < NQT; ++kt) kap[kt] = oal_splat(eps);
-        const int G = G_h[i];
+        const int G = hd->G;
         // Lz rows come from LDS when the head has fewer than LZR groups, else from the blob
         if (G < Lay::LZR) {
             for (int m = 0; m <= G; ++m) {
@@ -718,38 +782,39 @@ __global__ __launch_bounds__(128) void oal_readout(
                     const T *vr = s_vT + (16 * n + lr) * LDV + 32 * p + 4 * g;
                     OalFrag<T> bv;
                     bv.load4x2(vr, vr + 16);
-                    acc[i][n] = oal_mma(a, bv, acc[i][n]);
+                    acc[li][n] = oal_mma(a, bv, acc[li][n]);
                 }
-                acc[i][4] = oal_mma(a, lr == 0 ? ones : zeros, acc[i][4]);
+                acc[li][4] = oal_mma(a, lr == 0 ? ones : zeros, acc[li][4]);
             }
         }
     }
 
-    // 5. combine the two waves' partial sums and divide
+    // 5. combine the two parities' partial sums and divide
     __syncthreads();
 #pragma unroll
-    for (int i = 0; i < R; ++i)
-        if ((i & 1) != wave)
+    for (int li = 0; li < RW; ++li)
+        if (li < nh && (li & 1) != par)
 #pragma unroll
             for (int n = 0; n < 5; ++n)
 #pragma unroll
-                for (int ii = 0; ii < 4; ++ii) s_x[((i * 5 + n) * 4 + ii) * 64 + lane] = acc[i][n][ii];
+                for (int ii = 0; ii < 4; ++ii) s_x[(((hb + li) * 5 + n) * 4 + ii) * 64 + lane] = acc[li][n][ii];
     __syncthreads();
 #pragma unroll
-    for (int i = 0; i < R; ++i) {
-        if ((i & 1) != wave) continue;
+    for (int li = 0; li < RW; ++li) {
+        if (li >= nh || (li & 1) != par) continue;
+        const int i = hb + li;
 #pragma unroll
         for (int n = 0; n < 5; ++n)
 #pragma unroll
-            for (int ii = 0; ii < 4; ++ii) acc[i][n][ii] += s_x[((i * 5 + n) * 4 + ii) * 64 + lane];
+            for (int ii = 0; ii < 4; ++ii) acc[li][n][ii] += s_x[((i * 5 + n) * 4 + ii) * 64 + lane];
         float *yh = y + ((size_t)b * n_q_heads + h0 + i) * T_len * OAL_D;
 #pragma unroll
         for (int ii = 0; ii < 4; ++ii) {
-            float den = __shfl(acc[i][4][ii], lane & 48);
+            float den = __shfl(acc[li][4][ii], lane & 48);
             int pos = pos0 + 4 * g + ii;
             if (pos < T_len) {
 #pragma unroll
-                for (int n = 0; n < 4; ++n) yh[(size_t)pos * OAL_D + 16 * n + lr] = acc[i][n][ii] / den;
+                for (int n = 0; n < 4; ++n) yh[(size_t)pos * OAL_D + 16 * n + lr] = acc[li][n][ii] / den;
             }
         }
     }
@@ -786,8 +851,8 @@ PrefillPlan make_plan(const oal_dims &d, int T_len, int C) {
     p.seg_len = (p.nchunks + target - 1) / target;
     p.nseg = (p.nchunks + p.seg_len - 1) / p.seg_len;
     auto r256 = [](size_t x) { return (x + 255) / 256 * 256; };
-    p.snap_bytes = r256(bkv * p.nchunks * OAL_KSTEPS * (size_t)snap_kstep_bytes<T>());
-    p.totals_bytes = p.nseg > 1 ? r256(bkv * p.nseg * OAL_KSTEPS * (size_t)kTotalsPerLane * 64 * sizeof(float)) : 0;
+    p.snap_bytes = r256(bkv * p.nchunks * OAL_SNAP_KSTEPS * (size_t)snap_kstep_bytes<T>());
+    p.totals_bytes = p.nseg > 1 ? r256(bkv * p.nseg * OAL_SNAP_KSTEPS * (size_t)kTotalsPerLane * 64 * sizeof(float)) : 0;
     p.kv_bytes = r256(bkv * OAL_D * (size_t)p.Tpad * sizeof(T));
     return p;
 }
@@ -805,7 +870,7 @@ hipError_t launch_readout(const oal_dims &d, int T_len, const PrefillPlan &p, co
     if (e != hipSuccess) return e;
     int nunits = p.nchunks * d.batch * d.n_kv_heads * n_hg;
     int nblocks = kXcds * (C / 16) * ((nunits + kXcds - 1) / kXcds);
-    hipLaunchKernelGGL(kern, dim3(nblocks), dim3(128), lds, stream, T_len, p.Tpad, d.n_q_heads,
+    hipLaunchKernelGGL(kern, dim3(nblocks), dim3(256), lds, stream, T_len, p.Tpad, d.n_q_heads,
                        d.n_kv_heads, p.nchunks, n_hg, nunits, reinterpret_cast<const T *>(q),
                        reinterpret_cast<const T *>(k), vT,
                        reinterpret_cast<const unsigned char *>(params), snap, y);
@@ -833,8 +898,9 @@ hipError_t launch_all(const oal_dims &d, int T_len, const void *q, const void *k
         if ((e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds)) != hipSuccess)
             return e;
-        hipLaunchKernelGGL(kern, dim3(kScanBlocks, p.nseg - 1, bkv), dim3(64 * kScanWaves), lds, stream,
-                           T_len, p.Tpad, p.nchunks, p.nseg, p.seg_len, kT, vT, state, totals, snap);
+        hipLaunchKernelGGL(kern, dim3(kScanBlocks + 1, p.nseg - 1, bkv), dim3(64 * kScanWaves), lds, stream,
+                           T_len, p.Tpad, p.nchunks, p.nseg, p.seg_len, d.n_q_heads, d.n_kv_heads, kT, vT,
+                           reinterpret_cast<const unsigned char *>(params), state, totals, snap);
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
     {
@@ -842,8 +908,9 @@ hipError_t launch_all(const oal_dims &d, int T_len, const void *q, const void *k
         if ((e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds)) != hipSuccess)
             return e;
-        hipLaunchKernelGGL(kern, dim3(kScanBlocks, p.nseg, bkv), dim3(64 * kScanWaves), lds, stream,
-                           T_len, p.Tpad, p.nchunks, p.nseg, p.seg_len, kT, vT, state, totals, snap);
+        hipLaunchKernelGGL(kern, dim3(kScanBlocks + 1, p.nseg, bkv), dim3(64 * kScanWaves), lds, stream,
+                           T_len, p.Tpad, p.nchunks, p.nseg, p.seg_len, d.n_q_heads, d.n_kv_heads, kT, vT,
+                           reinterpret_cast<const unsigned char *>(params), state, totals, snap);
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
     if (marks && (e = hipEventRecord(marks[1], stream)) != hipSuccess) return e;

@@ -15,7 +15,7 @@ import numpy as np
 import pytest
 
 import oracle
-from oal_synth import small, cfg1, HeadParams, random_params
+from oal_synth import small, cfg1, qwen_like, HeadParams, random_params, draw_L
 
 gpq = pytest.importorskip("grouped_positive_quadratic_amd")
 
@@ -99,17 +99,26 @@ def test_param_validation():
 # ---- the blob, parsed with the record layout of the kernels --------------------------------
 
 HEAD_DT = np.dtype([("G", "<i4"), ("bulk", "<i4"), ("eps", "<f4"), ("a", "<f4"), ("L00", "<f4"),
-                    ("pad0", "<f4", 3), ("corr", "<u4", 4), ("gamma", "u1", 64),
-                    ("lin", "<f4", 64), ("w0", "<f4", 64), ("Dg", "<f4", (64, 64)),
-                    ("Lz", "<f4", (65, 64)), ("wdec", "<f4", 2176)])
+                    ("pad0", "<f4", 3), ("gamma", "u1", 64),
+                    ("lin", "<f4", 64), ("w0", "<f4", 64), ("tail", "<f4", 256),
+                    ("Lz", "<f4", (65, 64)), ("wslot", "<f4", 72 * 32), ("wdec", "<f4", 2176)])
 HEAD_BYTES = (HEAD_DT.itemsize + 255) // 256 * 256
+KV_DT = np.dtype([("npairs", "<i4"), ("nsteps", "<i4"), ("pad", "<i4", 62), ("ra", "u1", 256),
+                  ("rb", "u1", 256)])
+KV_BYTES = (KV_DT.itemsize + 255) // 256 * 256
 
 
-def parse(blob, n_heads):
-    assert blob.size == 256 + n_heads * HEAD_BYTES
-    assert blob[:4].view("<u4")[0] == 0x314C414F
-    return [np.frombuffer(blob[256 + h * HEAD_BYTES: 256 + h * HEAD_BYTES + HEAD_DT.itemsize].tobytes(),
-                          HEAD_DT)[0] for h in range(n_heads)]
+def parse(blob, n_heads, n_kv):
+    """header flag 'general', per-head records, per-KV-head tail-pair records"""
+    assert blob.size == 256 + n_heads * HEAD_BYTES + n_kv * KV_BYTES
+    hdr = blob[:256].view("<i4")
+    assert blob[:4].view("<u4")[0] == 0x314C414F and hdr[1] == n_heads and hdr[5] == n_kv
+    heads = [np.frombuffer(blob[256 + h * HEAD_BYTES: 256 + h * HEAD_BYTES + HEAD_DT.itemsize].tobytes(),
+                           HEAD_DT)[0] for h in range(n_heads)]
+    o = 256 + n_heads * HEAD_BYTES
+    kvs = [np.frombuffer(blob[o + kv * KV_BYTES: o + kv * KV_BYTES + KV_DT.itemsize].tobytes(), KV_DT)[0]
+           for kv in range(n_kv)]
+    return int(hdr[6]), heads, kvs
 
 
 def quad_row(r, t):
@@ -143,16 +152,39 @@ def mono(q, f):
 def _cases():
     yield small(7, B=1, Hq=3, Hkv=1, T=40, dtype="f32", g_hi=6)
     yield small(8, B=1, Hq=2, Hkv=1, T=40, dtype="f32", g_hi=2, allow_empty=True)
+    yield small(9, B=1, Hq=4, Hkv=2, T=40, dtype="f32", g_hi=12)
     c = cfg1()
     c.q, c.k, c.v = c.q[:, :, :48], c.k[:, :, :48], c.v[:, :, :48]
     yield c
+    yield qwen_like(1, 40, 5, n_q_heads=4, n_kv_heads=2, name="qwen_like_small")
+    # every dim its own group: far more non-bulk pairs than tail K-steps hold
+    g = small(10, B=1, Hq=2, Hkv=1, T=40, dtype="f32")
+    rng = np.random.default_rng(10)
+    g.params = HeadParams(np.full(2, 64, np.int32), np.tile(np.arange(64, dtype=np.uint8), (2, 1)),
+                          np.stack([draw_L(rng, 64, 64) for _ in range(2)]), np.full(2, 1e-3, np.float32))
+    g.name = "g64"
+    yield g
+
+
+def test_blob_modes():
+    """Bulk-plus-small-tail groupings use tail K-steps; scattered groupings fall back to the
+    general blob (full coefficient per slot)."""
+    modes = {}
+    for inp in _cases():
+        B, Hq, Hkv, T, d, dv = inp.dims
+        general, _, kvs = parse(gpq.oal_params_pack(gpq.make_dims(B, Hq, Hkv, "f32"),
+                                                    gpq.HeadParamsC.from_params(inp.params)), Hq, Hkv)
+        modes[inp.name] = (general, [int(k["nsteps"]) for k in kvs])
+    assert modes["g64"][0] == 1 and modes["g64"][1] == [0]
+    assert modes["cfg1"] == (0, [1])                    # tail dims 60..63: 10 pairs
+    assert modes["qwen_like_small"][0] == 0 and min(modes["qwen_like_small"][1]) >= 1
 
 
 @pytest.mark.parametrize("inp", list(_cases()), ids=lambda c: c.name)
 def test_blob_reproduces_oracle(inp):
     B, Hq, Hkv, T, d, dv = inp.dims
     dims = gpq.make_dims(B, Hq, Hkv, "f32")
-    heads = parse(gpq.oal_params_pack(dims, gpq.HeadParamsC.from_params(inp.params)), Hq)
+    general, heads, kvs = parse(gpq.oal_params_pack(dims, gpq.HeadParamsC.from_params(inp.params)), Hq, Hkv)
     H = oracle.state(inp.k, inp.v)                       # [B,Hkv,2145,65] fp64
     y_ref, den_ref = oracle.dense(inp.q, inp.k, inp.v, inp.params, return_den=True)
     n_rep = Hq // Hkv
@@ -173,15 +205,15 @@ def test_blob_reproduces_oracle(inp):
     assert sorted(seen) == list(range(2145))
     for h in range(Hq):
         hd = heads[h]
+        kvd = kvs[h // n_rep]
         q = inp.q[0, h, i].astype(np.float64)
         Hs = H[0, h // n_rep]
         # decode form: u = sum_f wdec[f] mono_f(q) H_f
         u = sum(float(hd["wdec"][f]) * mono(q, f) * Hs[f] for f in range(2145))
         np.testing.assert_allclose(u[:64] / u[64], y_ref[0, h, i], rtol=0, atol=2e-5)
         np.testing.assert_allclose(u[64], den_ref[0, h, i], rtol=2e-5)
-        # prefill slot form: scaled state x (rank-1 + flagged correction | lin | const)
-        corr = int(hd["corr"][0]) | int(hd["corr"][1]) << 32 | int(hd["corr"][2]) << 64
-        gam = hd["gamma"]
+        # prefill slot form on the scaled state: main slots (rank-1 p_a p_b, or the general
+        # coefficient), linear, constant, then the KV head's tail pairs
         p = hd["w0"].astype(np.float64) * q
         u2 = np.zeros(65)
         for tb in range(8):
@@ -192,13 +224,20 @@ def test_blob_reproduces_oracle(inp):
                         kind, a, b = slot(tb, rq, g, e)
                         if kind == "quad":
                             phi = p[a] * p[b]
-                            if (corr >> s) & 1 and gam[b] != hd["bulk"]:
-                                phi += float(hd["Dg"][gam[a], gam[b]]) * q[a] * q[b]
+                            if general:
+                                phi *= float(hd["wslot"][s * 32 + 8 * g + e])
                             u2 += phi * Hs[quad_row(a, b)] * (2.0 if a < b else 1.0) / 64
                         elif kind == "lin":
                             u2 += float(hd["lin"][a]) * q[a] * Hs[1 + a] / 8
                         elif kind == "const":
                             u2 += float(hd["a"]) * Hs[0]
+        if general:
+            assert kvd["nsteps"] == 0
+        else:
+            assert kvd["nsteps"] == (kvd["npairs"] + 31) // 32 <= 8
+            for j in range(kvd["npairs"]):
+                a, b = int(kvd["ra"][j]), int(kvd["rb"][j])
+                u2 += float(hd["tail"][j]) * q[a] * q[b] * Hs[quad_row(a, b)] * (2.0 if a < b else 1.0) / 64
         np.testing.assert_allclose(u2[:64] / u2[64], y_ref[0, h, i], rtol=0, atol=2e-5)
         # intra-chunk form: kappa = eps + sum_m (L00 [m==0] + sum_r Lz[m][r] q_r k_r)^2
         for j in (0, i // 2, i):

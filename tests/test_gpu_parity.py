@@ -8,7 +8,7 @@ import numpy as np
 import pytest
 
 import oracle
-from oal_synth import small, cfg1, cfg2, HeadParams, round_bf16
+from oal_synth import small, cfg1, cfg2, qwen_like, HeadParams, round_bf16, draw_L
 
 pytestmark = pytest.mark.gpu
 
@@ -206,6 +206,65 @@ def test_degenerate_params(name):
         err = oracle.row_error(y, oracle.dense(inp.q, inp.k, inp.v, inp.params))
         _report(f"degenerate {name} C={chunk}", err)
         assert err <= TOL["bf16"]
+
+
+# --- bulk + small-tail groupings: the tail K-steps of the prefill ---------------------------
+
+def _bulk_tail_params(seed, n_heads, tails, n_tail_groups):
+    """Head h: tail dims tails[h] split into n_tail_groups groups (ids 1..), bulk = the rest (id 0)."""
+    rng = np.random.default_rng(seed)
+    G = 1 + n_tail_groups
+    gamma = np.zeros((n_heads, 64), np.uint8)
+    for h in range(n_heads):
+        t = np.asarray(tails[h], dtype=np.int64)
+        lab = np.concatenate([np.arange(1, G), rng.integers(1, G, size=max(0, len(t) - (G - 1)))])
+        gamma[h, t] = lab[: len(t)]
+    L = np.stack([draw_L(rng, G, G) for _ in range(n_heads)])
+    return HeadParams(np.full(n_heads, G, np.int32), gamma, L, np.full(n_heads, 1e-3, np.float32))
+
+
+@pytest.mark.parametrize("chunk", [64, 128, 256])
+def test_tail_path_gqa(chunk):
+    """Qwen-shaped heads (bulk + 2-5 tail groups), 2 sequences, ragged T, then decode."""
+    inp = qwen_like(2, 333 + 3, 41, name="qwen_small")
+    T0 = 333
+    sess = session_for(inp, chunk)
+    y0 = sess.prefill(inp.q[:, :, :T0], inp.k[:, :, :T0], inp.v[:, :, :T0], chunk)
+    ys = [sess.decode(inp.q[:, :, i], inp.k[:, :, i], inp.v[:, :, i]) for i in range(T0, T0 + 3)]
+    y = np.concatenate([y0.cpu().numpy(), torch.stack(ys, 2).cpu().numpy()], axis=2)
+    err = oracle.row_error(y, oracle.dense(inp.q, inp.k, inp.v, inp.params))
+    _report(f"tail path qwen-shaped C={chunk}", err)
+    assert err <= TOL["bf16"]
+    assert state_ok(sess.state_np(), inp.k, inp.v, "bf16")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_tail_path_eight_steps(dtype):
+    """22 tail dims per head (253 pairs: all 8 tail K-steps) on one KV head, none on the other."""
+    inp = small(42, 1, 8, 2, 290, dtype=dtype)
+    tails = [list(range(20, 42))] * 4 + [[]] * 4
+    inp.params = _bulk_tail_params(42, 8, tails, 3)
+    inp.params.n_groups[4:] = 1
+    inp.params.group_of_dim[4:] = 0
+    for chunk in (64, 128):
+        sess = session_for(inp, chunk)
+        y = sess.prefill(inp.q, inp.k, inp.v, chunk).cpu().numpy()
+        err = oracle.row_error(y, oracle.dense(inp.q, inp.k, inp.v, inp.params))
+        _report(f"tail path 8 steps {dtype} C={chunk}", err)
+        assert err <= TOL[dtype]
+        assert state_ok(sess.state_np(), inp.k, inp.v, dtype)
+
+
+def test_tail_union_differs_per_head():
+    """Heads of one KV head with different tail dims: the tail list is their union."""
+    inp = small(43, 1, 7, 1, 260, dtype="bf16")
+    rng = np.random.default_rng(43)
+    tails = [sorted(rng.choice(64, size=rng.integers(2, 6), replace=False)) for _ in range(7)]
+    inp.params = _bulk_tail_params(43, 7, tails, 2)
+    y = session_for(inp, 128).prefill(inp.q, inp.k, inp.v, 128).cpu().numpy()
+    err = oracle.row_error(y, oracle.dense(inp.q, inp.k, inp.v, inp.params))
+    _report("tail union over heads", err)
+    assert err <= TOL["bf16"]
 
 
 # --- the Qwen2.5-0.5B-shaped workload at full size ----------------------------------------
