@@ -8,17 +8,13 @@
 //   u~_i = phi_h(q_i) . S_c + sum_{j in chunk c, j <= i} kappa_h(q_i, k_j) [v_j;1]
 //
 // Kernels, in launch order:
-//  0. oal_transpose_kv: K and V copied token-contiguous ([dim][token], zero past T) into
-//     the workspace, so that every later stage reads them with 16-byte coalesced copies.
-//  1. oal_scan<.., kTotals>  (only when the chunks are split into several segments)
-//     per (sequence x KV head, segment, K-step): the state increment of the segment, and
-//     for segment 0 a copy of the incoming state, into `totals`.
-//  2. oal_scan<.., kSnapshots>
-//     per (sequence x KV head, segment, K-step): start from the incoming state plus the
-//     increments of the earlier segments, then walk the segment's chunks writing the state
-//     before each chunk (bf16 or fp32, scaled, in the MFMA operand order of the readout)
-//     and adding psi(K_c)^T [V_c;1] on MFMA. The last segment writes the final state back.
+//  1. oal_scan_delta: per (sequence x KV head, chunk, K-step), in parallel, the chunk's state
+//     increment psi(K_c)^T [V_c;1] on MFMA (fp32), from K and V staged transposed in LDS.
 //     Besides the 72 main K-steps, up to 8 tail K-steps repeat the KV head's non-bulk pairs.
+//     It also writes V^T of each chunk for the readout.
+//  2. oal_scan_prefix: per state fragment, the running sum over chunks from the incoming
+//     state: the snapshot before each chunk (scaled, bf16 or fp32, in the MFMA operand order
+//     of the readout) and the final state.
 //  3. oal_readout
 //     per (sequence x KV head x head group, chunk, 16-query tile), 4 waves: two head
 //     subsets times two K-step parities. The query heads of one KV head share every
@@ -39,10 +35,8 @@ namespace {
 
 constexpr int kScanWaves = 8;                 // K-steps per scan workgroup (72 = 9 x 8)
 constexpr int kScanBlocks = OAL_KSTEPS / kScanWaves;
-constexpr int kTotalsPerLane = 40;            // 2 tiles x 5 column tiles x 4 rows
 constexpr int kXcds = 8;                      // MI355X: workgroups go round-robin to 8 XCDs
 constexpr int kMaxLds = 160 * 1024;           // LDS per CU on gfx950
-enum { kTotals = 0, kSnapshots = 1 };
 
 template <typename T> constexpr int snap_kstep_bytes() { return 4 * 64 * OalFrag<T>::kBytes + 4 * OalFrag<T>::kBytes; }
 
@@ -61,31 +55,6 @@ __device__ inline const OalKvDev *kv_ptr(const unsigned char *params, int n_q_he
                                               (size_t)n_q_heads * OAL_HEAD_BYTES + (size_t)kv * OAL_KV_BYTES);
 }
 
-// Slot (gs, e) of K-step s (main K-steps s < 72 as (tb, rq); tail K-steps s >= 72 list the
-// KV head's non-bulk pairs): the dims it multiplies (64 = the constant 1), its scale in the
-// snapshot relative to H, and its state row (-1: empty slot, zero in every snapshot).
-__device__ inline int scan_slot(int s, int tb, int rq, const OalKvDev *kvd, int gs, int e, int &ra,
-                                int &rb, float &scale) {
-    if (s < OAL_KSTEPS) {
-        int kind = oal_slot_kind(tb, rq, gs, e, &ra, &rb);
-        if (kind == OAL_SLOT_QUAD) { scale = (ra < rb ? 2.0f : 1.0f) / 64.0f; return oal_quad_row(ra, rb); }
-        if (kind == OAL_SLOT_LIN) { scale = 0.125f; return 1 + ra; }
-        if (kind == OAL_SLOT_CONST) { scale = 1.0f; return 0; }
-        scale = 0.0f;
-        return -1;
-    }
-    const int j = 32 * (s - OAL_KSTEPS) + 8 * gs + e;
-    if (j < kvd->npairs) {
-        ra = kvd->ra[j];
-        rb = kvd->rb[j];
-        scale = (ra < rb ? 2.0f : 1.0f) / 64.0f;
-        return oal_quad_row(ra, rb);
-    }
-    ra = rb = OAL_D;
-    scale = 0.0f;
-    return -1;
-}
-
 typedef unsigned int oal_u32x4 __attribute__((ext_vector_type(4)));   // 16-byte copy unit
 
 __device__ inline oal_u32x4 zero16() {
@@ -94,152 +63,155 @@ __device__ inline oal_u32x4 zero16() {
 }
 
 // ------------------------------------------------------------------------------------
-// 0. K, V -> token-contiguous copies kT, vT [bkv][64][Tpad]
-template <typename T>
-__global__ __launch_bounds__(256) void oal_transpose_kv(int T_len, int Tpad, const T *__restrict__ k,
-                                                        const T *__restrict__ v, T *__restrict__ kT,
-                                                        T *__restrict__ vT) {
-    constexpr int EPU = 16 / (int)sizeof(T);     // elements per 16-byte unit
-    constexpr int UPR = OAL_D / EPU;             // units per token row
-    constexpr int PER = 64 * UPR / 256;          // units per thread per array
-    constexpr int TS = 64 + EPU;                 // tile row (tokens), 16-byte aligned
-    __shared__ __align__(16) T tile[2][OAL_D * TS];
-    const int tok0 = blockIdx.x * 64, bkv = blockIdx.y, tid = threadIdx.x;
-    oal_u32x4 rk[PER], rv[PER];
-#pragma unroll
-    for (int j = 0; j < PER; ++j) {
-        int u = tid + 256 * j, tok = u % 64, a = u / 64, pos = tok0 + tok;
-        size_t off = ((size_t)bkv * T_len + pos) * OAL_D + a * EPU;
-        rk[j] = pos < T_len ? *reinterpret_cast<const oal_u32x4 *>(k + off) : zero16();
-        rv[j] = pos < T_len ? *reinterpret_cast<const oal_u32x4 *>(v + off) : zero16();
+// 1-2. chunk-state scan
+//
+// Each wave owns one K-step s: 32 state rows ("slots") x 80 columns (64 of v, the "1"
+// column and 15 zero columns) in two 16-row MFMA tiles. A-operand row lr of tile h is slot
+// (lr / 4, 4 h + lr % 4); accumulator rows 4 g + i of tile h are slots (g, 4 h + i). The
+// 8 accumulator values of lane (g, lr) and column tile n form "fragment" n * 64 + lane
+// (n < 4) or 256 + g (n = 4, lanes lr = 0): the B-operand fragment of the readout.
+// 1. oal_scan_delta: every (chunk, K-step) increment psi(K_c)^T [V_c;1] in parallel, fp32.
+// 2. oal_scan_prefix: per fragment, the running sum over chunks starting from the incoming
+//    state: the snapshot before each chunk (scaled, bf16 or fp32) and the final state.
+constexpr int kRowOnes = OAL_D;       // staged K^T row of valid-token ones
+constexpr int kRowZero = OAL_D + 1;   // staged K^T row of zeros (empty slots)
+
+// Slot (gs, e) of K-step s: the two K^T rows whose product is its feature, the state row
+// (-1: empty) and the snapshot scale. Tail K-steps take their pair from (pa, pb).
+__device__ inline int scan_slot(int s, int tb, int rq, int npairs, int pa, int pb, int gs, int e,
+                                int &ra, int &rb, float &scale) {
+    if (s < OAL_KSTEPS) {
+        int a, b;
+        int kind = oal_slot_kind(tb, rq, gs, e, &a, &b);
+        if (kind == OAL_SLOT_QUAD) { ra = a; rb = b; scale = (a < b ? 2.0f : 1.0f) / 64.0f; return oal_quad_row(a, b); }
+        if (kind == OAL_SLOT_LIN) { ra = a; rb = kRowOnes; scale = 0.125f; return 1 + a; }
+        if (kind == OAL_SLOT_CONST) { ra = kRowOnes; rb = kRowOnes; scale = 1.0f; return 0; }
+        ra = rb = kRowZero;
+        scale = 0.0f;
+        return -1;
     }
+    const int j = 32 * (s - OAL_KSTEPS) + 8 * gs + e;
+    if (j < npairs) {
+        ra = pa;
+        rb = pb;
+        scale = (pa < pb ? 2.0f : 1.0f) / 64.0f;
+        return oal_quad_row(pa, pb);
+    }
+    ra = rb = kRowZero;
+    scale = 0.0f;
+    return -1;
+}
+
+// 8 products x[e] = a[e] * b[e] of two staged rows (exact in fp32 for bf16 rows)
+template <typename T>
+__device__ inline void row_products(const OalFrag<T> &a, const OalFrag<T> &b, float (&x)[8]) {
 #pragma unroll
-    for (int j = 0; j < PER; ++j) {
-        int u = tid + 256 * j, tok = u % 64, a = u / 64;
-        const T *ek = reinterpret_cast<const T *>(&rk[j]);
-        const T *ev = reinterpret_cast<const T *>(&rv[j]);
+    for (int e = 0; e < 8; ++e) x[e] = (float)a.v[e] * (float)b.v[e];
+}
+
+constexpr int kFrags = 4 * 64 + 4;                   // fragments per K-step
+constexpr int kDeltaStep = kFrags * 8;                // fp32 per (chunk, K-step)
+
+// Slot tables of one fragment's lane: its 8 state rows and snapshot scales (rows j = 4 h + i
+// are slots (g, 4 h + i)), and the two K^T rows of the A-operand rows (lr / 4, 4 h + lr % 4).
+__device__ inline void slot_tables(int s, const OalKvDev *kvd, int g, int lr, int (&frow)[8],
+                                   float (&fsc)[8], int (&ra)[2], int (&rb)[2]) {
+    int tb = 0, rq = 0;
+    if (s < OAL_KSTEPS) kstep_decode(s, tb, rq);
+    const int npairs = kvd->npairs;
+    int pa[10], pb[10];
 #pragma unroll
-        for (int e = 0; e < EPU; ++e) {
-            tile[0][(a * EPU + e) * TS + tok] = ek[e];
-            tile[1][(a * EPU + e) * TS + tok] = ev[e];
+    for (int u = 0; u < 10; ++u) { pa[u] = 0; pb[u] = 0; }
+    if (s >= OAL_KSTEPS) {       // tail pairs: all loads issued together
+        const int x = s - OAL_KSTEPS;
+#pragma unroll
+        for (int u = 0; u < 10; ++u) {
+            const int gs = u < 8 ? g : lr >> 2, e = u < 8 ? u : 4 * (u - 8) + (lr & 3);
+            const int j = 32 * x + 8 * gs + e;
+            pa[u] = kvd->ra[j];
+            pb[u] = kvd->rb[j];
         }
     }
-    __syncthreads();
 #pragma unroll
-    for (int j = 0; j < PER; ++j) {
-        int u = tid + 256 * j, dim = u / (64 / EPU), tu = u % (64 / EPU);
-        size_t off = ((size_t)bkv * OAL_D + dim) * Tpad + tok0 + tu * EPU;
-        *reinterpret_cast<oal_u32x4 *>(kT + off) = *reinterpret_cast<const oal_u32x4 *>(&tile[0][dim * TS + tu * EPU]);
-        *reinterpret_cast<oal_u32x4 *>(vT + off) = *reinterpret_cast<const oal_u32x4 *>(&tile[1][dim * TS + tu * EPU]);
+    for (int j = 0; j < 8; ++j) {
+        int a, b;
+        frow[j] = scan_slot(s, tb, rq, npairs, pa[j], pb[j], g, j, a, b, fsc[j]);
+    }
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        float sc;
+        scan_slot(s, tb, rq, npairs, pa[8 + h], pb[8 + h], lr >> 2, 4 * h + (lr & 3), ra[h], rb[h], sc);
     }
 }
 
-// ------------------------------------------------------------------------------------
-// 1-2. chunk-state scan
-template <typename T, int C, int MODE>
-__global__ __launch_bounds__(64 * kScanWaves) void oal_scan(
-    int T_len, int Tpad, int nchunks, int nseg, int seg_len, int n_q_heads, int n_kv_heads,
-    const T *__restrict__ kT, const T *__restrict__ vT, const unsigned char *__restrict__ params,
-    float *__restrict__ state, float *__restrict__ totals, unsigned char *__restrict__ snap) {
+// grid (K-step blocks + 1 tail block, chunks, sequence x KV head); 8 waves, one K-step each.
+// The chunk's K and V are staged transposed in LDS ([dim][token]); workgroups of K-step
+// block 0 also write V^T of the chunk for the readout.
+template <typename T, int C>
+__global__ __launch_bounds__(64 * kScanWaves) void oal_scan_delta(
+    int T_len, int Tpad, int nchunks, int n_q_heads, int n_kv_heads, const T *__restrict__ k,
+    const T *__restrict__ v, const unsigned char *__restrict__ params, float *__restrict__ delta,
+    T *__restrict__ vT) {
     constexpr int EPU = 16 / (int)sizeof(T);
     constexpr int LD = C + EPU;                         // padded row, 16-byte aligned
-    constexpr int UPR = C / EPU;                        // 16-byte units per row and chunk
-    constexpr int NU = 2 * OAL_D * UPR;                 // K and V rows of one chunk
-    constexpr int PER = (NU + 64 * kScanWaves - 1) / (64 * kScanWaves);
-    extern __shared__ __align__(16) unsigned char smem[];
-    T *s_kT = reinterpret_cast<T *>(smem);              // [65][LD], row 64 = valid-token ones
-    T *s_vT = s_kT + 65 * LD;                           // [64][LD]
-
-    const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63, g = lane >> 4, lr = lane & 15;
-    const int s = blockIdx.x * kScanWaves + wave;     // blockIdx.x == 9: tail K-steps
-    const int sigma = blockIdx.y;
-    const int bkv = blockIdx.z;
-    const OalKvDev *kvd = kv_ptr(params, n_q_heads, bkv % n_kv_heads);
-    if (blockIdx.x == kScanBlocks && kvd->nsteps == 0) return;     // whole workgroup
-    // waves past the KV head's tail K-steps only help staging the chunks
-    const bool idle = s >= OAL_KSTEPS + kvd->nsteps;
-    int tb = 0, rq = 0;
-    if (s < OAL_KSTEPS) kstep_decode(s, tb, rq);
-
-    // A operand (psi^T): this lane's feature row lr of tile h is slot (lr/4, 4h + lr%4)
-    int ra[2], rb[2];
-    float sig[2];
-#pragma unroll
-    for (int h = 0; h < 2; ++h) scan_slot(s, tb, rq, kvd, lr >> 2, 4 * h + (lr & 3), ra[h], rb[h], sig[h]);
-
-    oal_f32x4 acc[2][5];
-#pragma unroll
-    for (int h = 0; h < 2; ++h)
-#pragma unroll
-        for (int n = 0; n < 5; ++n) acc[h][n] = oal_splat(0.0f);
-
-    float *Sst = state + (size_t)bkv * OAL_NFEAT * OAL_V1;
-    auto read_state = [&]() {
-#pragma unroll
-        for (int h = 0; h < 2; ++h)
-#pragma unroll
-            for (int n = 0; n < 5; ++n)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    float sc;
-                    int x0, x1;
-                    int f = scan_slot(s, tb, rq, kvd, g, 4 * h + i, x0, x1, sc);
-                    int col = n < 4 ? 16 * n + lr : (lr == 0 ? OAL_D : -1);
-                    acc[h][n][i] = (f >= 0 && col >= 0) ? Sst[(size_t)f * OAL_V1 + col] * sc : 0.0f;
-                }
-    };
-    auto totals_at = [&](int idx) {
-        return totals + (((size_t)bkv * nseg + idx) * OAL_SNAP_KSTEPS + s) * kTotalsPerLane * 64 + lane;
-    };
-
-    const int c0 = sigma * seg_len, c1 = min(nchunks, c0 + seg_len);
-    if (MODE == kTotals) {
-        if (sigma == 0) {
-            read_state();
-            float *tp = totals_at(0);
-#pragma unroll
-            for (int h = 0; h < 2; ++h)
-#pragma unroll
-                for (int n = 0; n < 5; ++n)
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        tp[((h * 5 + n) * 4 + i) * 64] = acc[h][n][i];
-                        acc[h][n][i] = 0.0f;
-                    }
-        }
-    } else {
-        if (nseg == 1) {
-            read_state();
-        } else {
-            for (int sg = 0; sg <= sigma; ++sg) {
-                const float *tp = totals_at(sg);
-                float x[kTotalsPerLane];
-#pragma unroll
-                for (int e = 0; e < kTotalsPerLane; ++e) x[e] = tp[e * 64];
-#pragma unroll
-                for (int h = 0; h < 2; ++h)
-#pragma unroll
-                    for (int n = 0; n < 5; ++n)
-#pragma unroll
-                        for (int i = 0; i < 4; ++i) acc[h][n][i] += x[(h * 5 + n) * 4 + i];
-            }
-        }
-    }
-
+    constexpr int UPT = OAL_D / EPU;                    // 16-byte units per token row
+    constexpr int NU = 2 * C * UPT;                     // K and V units of one chunk
+    constexpr int PER = NU / (64 * kScanWaves);
     static_assert(NU % (64 * kScanWaves) == 0, "chunk staging must tile the workgroup");
-    // staging unit j of this thread: array (K or V), row and 16-byte column of the chunk
-    const T *kTb = kT + (size_t)bkv * OAL_D * Tpad;
-    const T *vTb = vT + (size_t)bkv * OAL_D * Tpad;
-    const T *src_u[PER];
-    T *dst_u[PER];
-#pragma unroll
-    for (int j = 0; j < PER; ++j) {
-        int u = tid + 64 * kScanWaves * j;
-        int arr = u / (OAL_D * UPR), rem = u % (OAL_D * UPR), row = rem / UPR, cu = rem % UPR;
-        src_u[j] = (arr ? vTb : kTb) + (size_t)row * Tpad + cu * EPU;
-        dst_u[j] = (arr ? s_vT : s_kT) + row * LD + cu * EPU;
-    }
+    extern __shared__ __align__(16) unsigned char smem[];
+    T *s_kT = reinterpret_cast<T *>(smem);              // [66][LD]: rows 64 ones, 65 zeros
+    T *s_vT = s_kT + 66 * LD;                           // [64][LD]
 
+    const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+    const int g = lane >> 4, lr = lane & 15;
+    const int s = blockIdx.x * kScanWaves + wave;
+    const int c = blockIdx.y, bkv = blockIdx.z;
+    const OalKvDev *kvd = kv_ptr(params, n_q_heads, bkv % n_kv_heads);
+    const int nsteps = kvd->nsteps;
+    if (blockIdx.x == kScanBlocks && nsteps == 0) return;     // whole workgroup
+    const bool idle = s >= OAL_KSTEPS + nsteps;             // only helps staging
+
+    // stage: unit u = (array, 16-byte column a, token); consecutive lanes take consecutive
+    // tokens, so the transposed 2- or 4-byte LDS writes of a wave are consecutive
+    {
+        oal_u32x4 r[PER];
+#pragma unroll
+        for (int j = 0; j < PER; ++j) {
+            const int u = tid + 64 * kScanWaves * j;
+            const int arr = u / (C * UPT), rem = u % (C * UPT), a = rem / C, tok = rem % C;
+            const int pos = c * C + tok;
+            const T *src = (arr ? v : k) + ((size_t)bkv * T_len + pos) * OAL_D + a * EPU;
+            r[j] = pos < T_len ? *reinterpret_cast<const oal_u32x4 *>(src) : zero16();
+        }
+#pragma unroll
+        for (int j = 0; j < PER; ++j) {
+            const int u = tid + 64 * kScanWaves * j;
+            const int arr = u / (C * UPT), rem = u % (C * UPT), a = rem / C, tok = rem % C;
+            const T *el = reinterpret_cast<const T *>(&r[j]);
+            T *dst = (arr ? s_vT : s_kT) + (a * EPU) * LD + tok;
+#pragma unroll
+            for (int e = 0; e < EPU; ++e) dst[e * LD] = el[e];
+        }
+        for (int tok = tid; tok < C; tok += 64 * kScanWaves) {
+            s_kT[kRowOnes * LD + tok] = (c * C + tok < T_len) ? (T)1.0f : (T)0.0f;
+            s_kT[kRowZero * LD + tok] = (T)0.0f;
+        }
+    }
+    __syncthreads();
+    if (blockIdx.x == 0) {
+        constexpr int NVU = OAL_D * C / EPU;
+        T *vTb = vT + (size_t)bkv * OAL_D * Tpad + (size_t)c * C;
+        for (int u = tid; u < NVU; u += 64 * kScanWaves) {
+            const int row = u / (C / EPU), cu = u % (C / EPU);
+            *reinterpret_cast<oal_u32x4 *>(vTb + (size_t)row * Tpad + cu * EPU) =
+                *reinterpret_cast<const oal_u32x4 *>(s_vT + row * LD + cu * EPU);
+        }
+    }
+    if (idle) return;
+
+    int frow[8], ra[2], rb[2];
+    float fsc[8];
+    slot_tables(s, kvd, g, lr, frow, fsc, ra, rb);
     OalFrag<T> ones, zeros;
     {
         float o[8], zz[8];
@@ -248,92 +220,104 @@ __global__ __launch_bounds__(64 * kScanWaves) void oal_scan(
         ones.set(o);
         zeros.set(zz);
     }
+    oal_f32x4 acc[2][5];
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int n = 0; n < 5; ++n) acc[h][n] = oal_splat(0.0f);
+#pragma unroll
+    for (int sb = 0; sb < C / 32; ++sb) {
+        const int t0 = 32 * sb + 8 * g;
+        OalFrag<T> a[2], bf[4];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            OalFrag<T> xa, xb;
+            xa.load(s_kT + ra[h] * LD + t0);
+            xb.load(s_kT + rb[h] * LD + t0);
+            float x[8];
+            row_products(xa, xb, x);
+            a[h].set(x);
+        }
+#pragma unroll
+        for (int n = 0; n < 4; ++n) bf[n].load(s_vT + (16 * n + lr) * LD + t0);
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+#pragma unroll
+            for (int n = 0; n < 4; ++n) acc[h][n] = oal_mma(a[h], bf[n], acc[h][n]);
+            acc[h][4] = oal_mma(a[h], lr == 0 ? ones : zeros, acc[h][4]);
+        }
+    }
+    float *dp = delta + ((size_t)(bkv * nchunks + c) * OAL_SNAP_KSTEPS + s) * kDeltaStep;
+#pragma unroll
+    for (int n = 0; n < 5; ++n) {
+        if (n == 4 && lr != 0) continue;
+        float4 *q4 = reinterpret_cast<float4 *>(dp + (n < 4 ? n * 64 + lane : 256 + g) * 8);
+        q4[0] = make_float4(acc[0][n][0], acc[0][n][1], acc[0][n][2], acc[0][n][3]);
+        q4[1] = make_float4(acc[1][n][0], acc[1][n][1], acc[1][n][2], acc[1][n][3]);
+    }
+}
+
+// one thread per (sequence x KV head, K-step, fragment): the state before each chunk is the
+// incoming state plus the earlier chunks' increments (fp32, in chunk order)
+template <typename T>
+__global__ __launch_bounds__(256) void oal_scan_prefix(int nchunks, int n_q_heads, int n_kv_heads, int n_bkv,
+                                                       const unsigned char *__restrict__ params,
+                                                       const float *__restrict__ delta,
+                                                       float *__restrict__ state, unsigned char *__restrict__ snap) {
     constexpr int KB = snap_kstep_bytes<T>();
+    const size_t idx = (size_t)blockIdx.x * 256 + threadIdx.x;
+    if (idx >= (size_t)n_bkv * OAL_SNAP_KSTEPS * kFrags) return;
+    const int f = (int)(idx % kFrags);
+    const int s = (int)((idx / kFrags) % OAL_SNAP_KSTEPS);
+    const int bkv = (int)(idx / ((size_t)kFrags * OAL_SNAP_KSTEPS));
+    const OalKvDev *kvd = kv_ptr(params, n_q_heads, bkv % n_kv_heads);
+    if (s >= OAL_KSTEPS + kvd->nsteps) return;
+    const int n = f < 256 ? f >> 6 : 4;
+    const int lane = f < 256 ? f & 63 : (f - 256) << 4;   // for n = 4: lane (g, lr = 0)
+    const int g = lane >> 4, lr = lane & 15;
+    const int col = n < 4 ? 16 * n + lr : OAL_D;
+    int frow[8], ra[2], rb[2];
+    float fsc[8];
+    slot_tables(s, kvd, g, lr, frow, fsc, ra, rb);
 
-    oal_u32x4 pre[PER];
-    if (c0 < c1) {
+    float *Sst = state + (size_t)bkv * OAL_NFEAT * OAL_V1;
+    float S[8];
 #pragma unroll
-        for (int j = 0; j < PER; ++j) pre[j] = *reinterpret_cast<const oal_u32x4 *>(src_u[j] + (size_t)c0 * C);
+    for (int j = 0; j < 8; ++j) {
+        const float xv = Sst[(size_t)(frow[j] >= 0 ? frow[j] : 0) * OAL_V1 + col];
+        S[j] = frow[j] >= 0 ? xv : 0.0f;
     }
-    for (int c = c0; c < c1; ++c) {
-        __syncthreads();
+    const float *dp = delta + ((size_t)bkv * nchunks * OAL_SNAP_KSTEPS + s) * kDeltaStep + f * 8;
+    unsigned char *sp = snap + ((size_t)bkv * nchunks * OAL_SNAP_KSTEPS + s) * KB + (size_t)f * OalFrag<T>::kBytes;
+    constexpr size_t DSTRIDE = (size_t)OAL_SNAP_KSTEPS * kDeltaStep, SSTRIDE = (size_t)OAL_SNAP_KSTEPS * KB;
+    for (int c0 = 0; c0 < nchunks; c0 += 4) {
+        float4 d[4][2];
 #pragma unroll
-        for (int j = 0; j < PER; ++j) *reinterpret_cast<oal_u32x4 *>(dst_u[j]) = pre[j];
-        for (int tok = tid; tok < C; tok += 64 * kScanWaves)
-            s_kT[OAL_D * LD + tok] = (c * C + tok < T_len) ? (T)1.0f : (T)0.0f;
-        __syncthreads();
-        if (c + 1 < c1) {
-#pragma unroll
-            for (int j = 0; j < PER; ++j) pre[j] = *reinterpret_cast<const oal_u32x4 *>(src_u[j] + (size_t)(c + 1) * C);
-        }
-        if (idle) continue;      // after the staging barriers, which every wave joins
-        if (MODE == kSnapshots) {
-            unsigned char *sp = snap + (((size_t)bkv * nchunks + c) * OAL_SNAP_KSTEPS + s) * KB;
-#pragma unroll
-            for (int n = 0; n < 4; ++n) {
-                float x[8];
-#pragma unroll
-                for (int i = 0; i < 4; ++i) { x[i] = acc[0][n][i]; x[4 + i] = acc[1][n][i]; }
-                OalFrag<T> f;
-                f.set(x);
-                f.store(sp + (n * 64 + lane) * OalFrag<T>::kBytes);
-            }
-            if (lr == 0) {
-                float x[8];
-#pragma unroll
-                for (int i = 0; i < 4; ++i) { x[i] = acc[0][4][i]; x[4 + i] = acc[1][4][i]; }
-                OalFrag<T> f;
-                f.set(x);
-                f.store(sp + (4 * 64 + g) * OalFrag<T>::kBytes);
+        for (int u = 0; u < 4; ++u) {
+            if (c0 + u < nchunks) {
+                const float4 *q4 = reinterpret_cast<const float4 *>(dp + (size_t)(c0 + u) * DSTRIDE);
+                d[u][0] = q4[0];
+                d[u][1] = q4[1];
             }
         }
 #pragma unroll
-        for (int sb = 0; sb < C / 32; ++sb) {
-            const int t0 = 32 * sb + 8 * g;
-            OalFrag<T> a[2], bf[4];
-#pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                OalFrag<T> xa, xb;
-                xa.load(s_kT + ra[h] * LD + t0);
-                xb.load(s_kT + rb[h] * LD + t0);
+        for (int u = 0; u < 4; ++u) {
+            if (c0 + u < nchunks) {
                 float x[8];
 #pragma unroll
-                for (int e = 0; e < 8; ++e) x[e] = sig[h] * (float)xa.v[e] * (float)xb.v[e];
-                a[h].set(x);
-            }
-#pragma unroll
-            for (int n = 0; n < 4; ++n) bf[n].load(s_vT + (16 * n + lr) * LD + t0);
-#pragma unroll
-            for (int h = 0; h < 2; ++h) {
-#pragma unroll
-                for (int n = 0; n < 4; ++n) acc[h][n] = oal_mma(a[h], bf[n], acc[h][n]);
-                acc[h][4] = oal_mma(a[h], lr == 0 ? ones : zeros, acc[h][4]);
+                for (int j = 0; j < 8; ++j) x[j] = S[j] * fsc[j];
+                OalFrag<T> fr;
+                fr.set(x);
+                fr.store(sp + (size_t)(c0 + u) * SSTRIDE);
+                S[0] += d[u][0].x; S[1] += d[u][0].y; S[2] += d[u][0].z; S[3] += d[u][0].w;
+                S[4] += d[u][1].x; S[5] += d[u][1].y; S[6] += d[u][1].z; S[7] += d[u][1].w;
             }
         }
     }
-
-    if (idle) return;
-    if (MODE == kTotals) {
-        float *tp = totals_at(sigma + 1);
+    if (s < OAL_KSTEPS) {      // tail rows duplicate main rows
 #pragma unroll
-        for (int h = 0; h < 2; ++h)
-#pragma unroll
-            for (int n = 0; n < 5; ++n)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) tp[((h * 5 + n) * 4 + i) * 64] = acc[h][n][i];
-    } else if (sigma == nseg - 1 && s < OAL_KSTEPS) {   // tail rows duplicate main rows
-#pragma unroll
-        for (int h = 0; h < 2; ++h)
-#pragma unroll
-            for (int n = 0; n < 5; ++n)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    float sc;
-                    int x0, x1;
-                    int f = scan_slot(s, tb, rq, kvd, g, 4 * h + i, x0, x1, sc);
-                    int col = n < 4 ? 16 * n + lr : (lr == 0 ? OAL_D : -1);
-                    if (f >= 0 && col >= 0) Sst[(size_t)f * OAL_V1 + col] = acc[h][n][i] / sc;
-                }
+        for (int j = 0; j < 8; ++j)
+            if (frow[j] >= 0) Sst[(size_t)frow[j] * OAL_V1 + col] = S[j];
     }
 }
 
@@ -821,14 +805,14 @@ __global__ __launch_bounds__(256, 2) void oal_readout(
 }
 
 template <typename T, int C>
-size_t scan_lds() { return (size_t)(65 + 64) * (C + 16 / sizeof(T)) * sizeof(T); }
+size_t scan_lds() { return (size_t)(66 + 64) * (C + 16 / sizeof(T)) * sizeof(T); }
 
 template <typename T, int C, int R>
 size_t readout_lds() { return (size_t)ReadoutLayout<T, C, R>::BYTES; }
 
 struct PrefillPlan {
-    int nchunks, nseg, seg_len, Tpad;
-    size_t snap_bytes, totals_bytes, kv_bytes;
+    int nchunks, Tpad;
+    size_t snap_bytes, delta_bytes, vt_bytes;
 };
 
 template <typename T>
@@ -837,23 +821,10 @@ PrefillPlan make_plan(const oal_dims &d, int T_len, int C) {
     size_t bkv = (size_t)d.batch * d.n_kv_heads;
     p.nchunks = (T_len + C - 1) / C;
     p.Tpad = p.nchunks * C;
-    int target = 1;
-    const char *env = getenv("OAL_NSEG");
-    if (env && atoi(env) > 0) {
-        target = atoi(env);
-    } else {
-        size_t waves = bkv * OAL_KSTEPS;
-        target = (int)((1024 + waves / 2) / waves);
-        if (target < 1) target = 1;
-    }
-    if (target > p.nchunks) target = p.nchunks;
-    if (target < 1) target = 1;
-    p.seg_len = (p.nchunks + target - 1) / target;
-    p.nseg = (p.nchunks + p.seg_len - 1) / p.seg_len;
     auto r256 = [](size_t x) { return (x + 255) / 256 * 256; };
     p.snap_bytes = r256(bkv * p.nchunks * OAL_SNAP_KSTEPS * (size_t)snap_kstep_bytes<T>());
-    p.totals_bytes = p.nseg > 1 ? r256(bkv * p.nseg * OAL_SNAP_KSTEPS * (size_t)kTotalsPerLane * 64 * sizeof(float)) : 0;
-    p.kv_bytes = r256(bkv * OAL_D * (size_t)p.Tpad * sizeof(T));
+    p.delta_bytes = r256(bkv * p.nchunks * OAL_SNAP_KSTEPS * (size_t)kDeltaStep * sizeof(float));
+    p.vt_bytes = r256(bkv * OAL_D * (size_t)p.Tpad * sizeof(T));
     return p;
 }
 
@@ -883,34 +854,27 @@ hipError_t launch_all(const oal_dims &d, int T_len, const void *q, const void *k
                       hipEvent_t *marks) {
     PrefillPlan p = make_plan<T>(d, T_len, C);
     unsigned char *snap = reinterpret_cast<unsigned char *>(ws);
-    float *totals = reinterpret_cast<float *>(snap + p.snap_bytes);
-    T *kT = reinterpret_cast<T *>(snap + p.snap_bytes + p.totals_bytes);
-    T *vT = reinterpret_cast<T *>(snap + p.snap_bytes + p.totals_bytes + p.kv_bytes);
-    int bkv = d.batch * d.n_kv_heads;
+    float *delta = reinterpret_cast<float *>(snap + p.snap_bytes);
+    T *vT = reinterpret_cast<T *>(snap + p.snap_bytes + p.delta_bytes);
+    const int bkv = d.batch * d.n_kv_heads;
+    const unsigned char *pb = reinterpret_cast<const unsigned char *>(params);
     hipError_t e;
     if (marks && (e = hipEventRecord(marks[0], stream)) != hipSuccess) return e;
-    hipLaunchKernelGGL(oal_transpose_kv<T>, dim3(p.Tpad / 64, bkv), dim3(256), 0, stream, T_len, p.Tpad,
-                       reinterpret_cast<const T *>(k), reinterpret_cast<const T *>(v), kT, vT);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-    size_t lds = scan_lds<T, C>();
-    if (p.nseg > 1) {
-        auto kern = oal_scan<T, C, kTotals>;
+    {
+        auto kern = oal_scan_delta<T, C>;
+        size_t lds = scan_lds<T, C>();
         if ((e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds)) != hipSuccess)
             return e;
-        hipLaunchKernelGGL(kern, dim3(kScanBlocks + 1, p.nseg - 1, bkv), dim3(64 * kScanWaves), lds, stream,
-                           T_len, p.Tpad, p.nchunks, p.nseg, p.seg_len, d.n_q_heads, d.n_kv_heads, kT, vT,
-                           reinterpret_cast<const unsigned char *>(params), state, totals, snap);
+        hipLaunchKernelGGL(kern, dim3(kScanBlocks + 1, p.nchunks, bkv), dim3(64 * kScanWaves), lds, stream,
+                           T_len, p.Tpad, p.nchunks, d.n_q_heads, d.n_kv_heads, reinterpret_cast<const T *>(k),
+                           reinterpret_cast<const T *>(v), pb, delta, vT);
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
     {
-        auto kern = oal_scan<T, C, kSnapshots>;
-        if ((e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
-                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds)) != hipSuccess)
-            return e;
-        hipLaunchKernelGGL(kern, dim3(kScanBlocks + 1, p.nseg, bkv), dim3(64 * kScanWaves), lds, stream,
-                           T_len, p.Tpad, p.nchunks, p.nseg, p.seg_len, d.n_q_heads, d.n_kv_heads, kT, vT,
-                           reinterpret_cast<const unsigned char *>(params), state, totals, snap);
+        const size_t nthr = (size_t)bkv * OAL_SNAP_KSTEPS * kFrags;
+        hipLaunchKernelGGL(oal_scan_prefix<T>, dim3((unsigned)((nthr + 255) / 256)), dim3(256), 0, stream,
+                           p.nchunks, d.n_q_heads, d.n_kv_heads, bkv, pb, delta, state, snap);
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
     if (marks && (e = hipEventRecord(marks[1], stream)) != hipSuccess) return e;
@@ -937,7 +901,7 @@ hipError_t launch_all(const oal_dims &d, int T_len, const void *q, const void *k
 
 size_t oal_prefill_ws_bytes_impl(const oal_dims &d, int T_len, int C) {
     PrefillPlan p = d.dtype == OAL_BF16 ? make_plan<__bf16>(d, T_len, C) : make_plan<float>(d, T_len, C);
-    return p.snap_bytes + p.totals_bytes + 2 * p.kv_bytes;
+    return p.snap_bytes + p.delta_bytes + p.vt_bytes;
 }
 
 hipError_t oal_launch_prefill(const oal_dims &d, int T_len, int C, const void *q, const void *k,
