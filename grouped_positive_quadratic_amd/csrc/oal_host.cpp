@@ -208,22 +208,31 @@ oal_status oal_params_pack(const oal_dims *d, const oal_head_params *hp, void *b
     std::vector<std::vector<std::pair<int, int>>> pairs(nkv);
     for (int kv = 0; kv < nkv; ++kv) {
         pairs[kv] = tail_pairs(hp, kv * n_rep, (kv + 1) * n_rep, D);
-        if ((int)pairs[kv].size() > OAL_TAIL_PAIRS) hdr->general = 1;
+        if ((int)pairs[kv].size() > OAL_TAIL_PAIRS - OAL_TAIL_FIXED) hdr->general = 1;
     }
     for (int kv = 0; kv < nkv; ++kv) {
         OalKvDev *kr = kvrec(kv);
-        if (hdr->general) continue;   // no tail K-steps
-        kr->npairs = (int)pairs[kv].size();
+        // entries 0..63: linear feature r = (r, 64); 64: the constant (64, 64); then the
+        // non-bulk pairs (none in a general blob)
+        const int np = hdr->general ? 0 : (int)pairs[kv].size();
+        kr->npairs = OAL_TAIL_FIXED + np;
         kr->nsteps = (kr->npairs + 31) / 32;
-        for (int j = 0; j < kr->npairs; ++j) {
-            kr->ra[j] = (uint8_t)pairs[kv][j].first;
-            kr->rb[j] = (uint8_t)pairs[kv][j].second;
+        for (int j = 0; j <= OAL_D; ++j) {
+            kr->ra[j] = (uint8_t)j;
+            kr->rb[j] = (uint8_t)OAL_D;
+        }
+        for (int m = 0; m < np; ++m) {
+            kr->ra[OAL_TAIL_FIXED + m] = (uint8_t)pairs[kv][m].first;
+            kr->rb[OAL_TAIL_FIXED + m] = (uint8_t)pairs[kv][m].second;
         }
         for (int h = kv * n_rep; h < (kv + 1) * n_rep; ++h) {
+            OalHeadDev *hd = head(h);
             const uint8_t *gam = hp->group_of_dim + (size_t)h * OAL_D;
             int G = hp->n_groups[h];
-            for (int j = 0; j < kr->npairs; ++j)
-                head(h)->tail[j] = (float)D[h][gam[kr->ra[j]] * G + gam[kr->rb[j]]];
+            for (int r = 0; r < OAL_D; ++r) hd->tail[r] = hd->lin[r];
+            hd->tail[OAL_D] = hd->a;
+            for (int m = 0; m < np; ++m)
+                hd->tail[OAL_TAIL_FIXED + m] = (float)D[h][gam[pairs[kv][m].first] * G + gam[pairs[kv][m].second]];
         }
     }
     if (hdr->general) {

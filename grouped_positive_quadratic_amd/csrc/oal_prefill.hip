@@ -76,30 +76,42 @@ __device__ inline oal_u32x4 zero16() {
 constexpr int kRowOnes = OAL_D;       // staged K^T row of valid-token ones
 constexpr int kRowZero = OAL_D + 1;   // staged K^T row of zeros (empty slots)
 
-// Slot (gs, e) of K-step s: the two K^T rows whose product is its feature, the state row
-// (-1: empty) and the snapshot scale. Tail K-steps take their pair from (pa, pb).
+// Slot (gs, e) of K-step s: the two K^T rows whose product is its feature (row 64: ones),
+// the state row (-1: empty) and the snapshot scale; own = the slot is the one that writes
+// its state row back (main quadratic slots, and the linear/constant tail entries, which
+// appear nowhere else). Tail K-steps take their entry from (pa, pb).
 __device__ inline int scan_slot(int s, int tb, int rq, int npairs, int pa, int pb, int gs, int e,
-                                int &ra, int &rb, float &scale) {
+                                int &ra, int &rb, float &scale, bool &own) {
+    own = false;
     if (s < OAL_KSTEPS) {
         int a, b;
-        int kind = oal_slot_kind(tb, rq, gs, e, &a, &b);
-        if (kind == OAL_SLOT_QUAD) { ra = a; rb = b; scale = (a < b ? 2.0f : 1.0f) / 64.0f; return oal_quad_row(a, b); }
-        if (kind == OAL_SLOT_LIN) { ra = a; rb = kRowOnes; scale = 0.125f; return 1 + a; }
-        if (kind == OAL_SLOT_CONST) { ra = kRowOnes; rb = kRowOnes; scale = 1.0f; return 0; }
+        if (oal_slot_kind(tb, rq, gs, e, &a, &b) == OAL_SLOT_QUAD) {
+            ra = a;
+            rb = b;
+            scale = (a < b ? 2.0f : 1.0f) / 64.0f;
+            own = true;
+            return oal_quad_row(a, b);
+        }
         ra = rb = kRowZero;
         scale = 0.0f;
         return -1;
     }
     const int j = 32 * (s - OAL_KSTEPS) + 8 * gs + e;
-    if (j < npairs) {
-        ra = pa;
-        rb = pb;
-        scale = (pa < pb ? 2.0f : 1.0f) / 64.0f;
-        return oal_quad_row(pa, pb);
+    if (j >= npairs) {
+        ra = rb = kRowZero;
+        scale = 0.0f;
+        return -1;
     }
-    ra = rb = kRowZero;
-    scale = 0.0f;
-    return -1;
+    ra = pa;
+    rb = pb;
+    own = j < OAL_TAIL_FIXED;
+    if (pb == OAL_D) {
+        if (pa == OAL_D) { scale = 1.0f; return 0; }     // constant
+        scale = 0.125f;                                 // linear feature pa
+        return 1 + pa;
+    }
+    scale = (pa < pb ? 2.0f : 1.0f) / 64.0f;
+    return oal_quad_row(pa, pb);
 }
 
 // 8 products x[e] = a[e] * b[e] of two staged rows (exact in fp32 for bf16 rows)
@@ -115,7 +127,7 @@ constexpr int kDeltaStep = kFrags * 8;                // fp32 per (chunk, K-step
 // Slot tables of one fragment's lane: its 8 state rows and snapshot scales (rows j = 4 h + i
 // are slots (g, 4 h + i)), and the two K^T rows of the A-operand rows (lr / 4, 4 h + lr % 4).
 __device__ inline void slot_tables(int s, const OalKvDev *kvd, int g, int lr, int (&frow)[8],
-                                   float (&fsc)[8], int (&ra)[2], int (&rb)[2]) {
+                                   float (&fsc)[8], bool (&fown)[8], int (&ra)[2], int (&rb)[2]) {
     int tb = 0, rq = 0;
     if (s < OAL_KSTEPS) kstep_decode(s, tb, rq);
     const int npairs = kvd->npairs;
@@ -135,12 +147,24 @@ __device__ inline void slot_tables(int s, const OalKvDev *kvd, int g, int lr, in
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
         int a, b;
-        frow[j] = scan_slot(s, tb, rq, npairs, pa[j], pb[j], g, j, a, b, fsc[j]);
+        frow[j] = scan_slot(s, tb, rq, npairs, pa[j], pb[j], g, j, a, b, fsc[j], fown[j]);
     }
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
         float sc;
-        scan_slot(s, tb, rq, npairs, pa[8 + h], pb[8 + h], lr >> 2, 4 * h + (lr & 3), ra[h], rb[h], sc);
+        bool ow;
+        scan_slot(s, tb, rq, npairs, pa[8 + h], pb[8 + h], lr >> 2, 4 * h + (lr & 3), ra[h], rb[h], sc, ow);
+    }
+}
+
+// the 8 accumulator values of each fragment of this lane, contiguous (fragment layout)
+__device__ inline void store_frags(float *dp, const oal_f32x4 (&acc)[2][5], int lane, int g, int lr) {
+#pragma unroll
+    for (int n = 0; n < 5; ++n) {
+        if (n == 4 && lr != 0) continue;
+        float4 *q4 = reinterpret_cast<float4 *>(dp + (n < 4 ? n * 64 + lane : 256 + g) * 8);
+        q4[0] = make_float4(acc[0][n][0], acc[0][n][1], acc[0][n][2], acc[0][n][3]);
+        q4[1] = make_float4(acc[1][n][0], acc[1][n][1], acc[1][n][2], acc[1][n][3]);
     }
 }
 
@@ -150,8 +174,8 @@ __device__ inline void slot_tables(int s, const OalKvDev *kvd, int g, int lr, in
 template <typename T, int C>
 __global__ __launch_bounds__(64 * kScanWaves) void oal_scan_delta(
     int T_len, int Tpad, int nchunks, int n_q_heads, int n_kv_heads, const T *__restrict__ k,
-    const T *__restrict__ v, const unsigned char *__restrict__ params, float *__restrict__ delta,
-    T *__restrict__ vT) {
+    const T *__restrict__ v, const unsigned char *__restrict__ params, const float *__restrict__ state,
+    float *__restrict__ delta, float *__restrict__ tinit, T *__restrict__ vT) {
     constexpr int EPU = 16 / (int)sizeof(T);
     constexpr int LD = C + EPU;                         // padded row, 16-byte aligned
     constexpr int UPT = OAL_D / EPU;                    // 16-byte units per token row
@@ -211,7 +235,8 @@ __global__ __launch_bounds__(64 * kScanWaves) void oal_scan_delta(
 
     int frow[8], ra[2], rb[2];
     float fsc[8];
-    slot_tables(s, kvd, g, lr, frow, fsc, ra, rb);
+    bool fown[8];
+    slot_tables(s, kvd, g, lr, frow, fsc, fown, ra, rb);
     OalFrag<T> ones, zeros;
     {
         float o[8], zz[8];
@@ -247,13 +272,23 @@ __global__ __launch_bounds__(64 * kScanWaves) void oal_scan_delta(
             acc[h][4] = oal_mma(a[h], lr == 0 ? ones : zeros, acc[h][4]);
         }
     }
-    float *dp = delta + ((size_t)(bkv * nchunks + c) * OAL_SNAP_KSTEPS + s) * kDeltaStep;
+    store_frags(delta + ((size_t)(bkv * nchunks + c) * OAL_SNAP_KSTEPS + s) * kDeltaStep, acc, lane, g, lr);
+    if (s >= OAL_KSTEPS && c == 0) {
+        // incoming state of the tail slots, read here because the prefix kernel overwrites
+        // the state rows (some of which the tail pairs repeat) while other threads read
+        const float *Sst = state + (size_t)bkv * OAL_NFEAT * OAL_V1;
 #pragma unroll
-    for (int n = 0; n < 5; ++n) {
-        if (n == 4 && lr != 0) continue;
-        float4 *q4 = reinterpret_cast<float4 *>(dp + (n < 4 ? n * 64 + lane : 256 + g) * 8);
-        q4[0] = make_float4(acc[0][n][0], acc[0][n][1], acc[0][n][2], acc[0][n][3]);
-        q4[1] = make_float4(acc[1][n][0], acc[1][n][1], acc[1][n][2], acc[1][n][3]);
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int n = 0; n < 5; ++n)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int f = frow[4 * h + i];
+                    const int col = n < 4 ? 16 * n + lr : OAL_D;
+                    const float xv = Sst[(size_t)(f >= 0 ? f : 0) * OAL_V1 + col];
+                    acc[h][n][i] = f >= 0 ? xv : 0.0f;
+                }
+        store_frags(tinit + ((size_t)bkv * OAL_TAIL_STEPS + (s - OAL_KSTEPS)) * kDeltaStep, acc, lane, g, lr);
     }
 }
 
@@ -263,6 +298,7 @@ template <typename T>
 __global__ __launch_bounds__(256) void oal_scan_prefix(int nchunks, int n_q_heads, int n_kv_heads, int n_bkv,
                                                        const unsigned char *__restrict__ params,
                                                        const float *__restrict__ delta,
+                                                       const float *__restrict__ tinit,
                                                        float *__restrict__ state, unsigned char *__restrict__ snap) {
     constexpr int KB = snap_kstep_bytes<T>();
     const size_t idx = (size_t)blockIdx.x * 256 + threadIdx.x;
@@ -278,14 +314,25 @@ __global__ __launch_bounds__(256) void oal_scan_prefix(int nchunks, int n_q_head
     const int col = n < 4 ? 16 * n + lr : OAL_D;
     int frow[8], ra[2], rb[2];
     float fsc[8];
-    slot_tables(s, kvd, g, lr, frow, fsc, ra, rb);
+    bool fown[8];
+    slot_tables(s, kvd, g, lr, frow, fsc, fown, ra, rb);
 
+    // incoming state: main slots read the rows they own (and later overwrite); tail slots
+    // take the copy the increment kernel made
     float *Sst = state + (size_t)bkv * OAL_NFEAT * OAL_V1;
     float S[8];
+    if (s < OAL_KSTEPS) {
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-        const float xv = Sst[(size_t)(frow[j] >= 0 ? frow[j] : 0) * OAL_V1 + col];
-        S[j] = frow[j] >= 0 ? xv : 0.0f;
+        for (int j = 0; j < 8; ++j) {
+            const float xv = Sst[(size_t)(frow[j] >= 0 ? frow[j] : 0) * OAL_V1 + col];
+            S[j] = frow[j] >= 0 ? xv : 0.0f;
+        }
+    } else {
+        const float4 *t4 = reinterpret_cast<const float4 *>(
+            tinit + ((size_t)bkv * OAL_TAIL_STEPS + (s - OAL_KSTEPS)) * kDeltaStep + f * 8);
+        const float4 a0 = t4[0], a1 = t4[1];
+        S[0] = a0.x; S[1] = a0.y; S[2] = a0.z; S[3] = a0.w;
+        S[4] = a1.x; S[5] = a1.y; S[6] = a1.z; S[7] = a1.w;
     }
     const float *dp = delta + ((size_t)bkv * nchunks * OAL_SNAP_KSTEPS + s) * kDeltaStep + f * 8;
     unsigned char *sp = snap + ((size_t)bkv * nchunks * OAL_SNAP_KSTEPS + s) * KB + (size_t)f * OalFrag<T>::kBytes;
@@ -314,11 +361,9 @@ __global__ __launch_bounds__(256) void oal_scan_prefix(int nchunks, int n_q_head
             }
         }
     }
-    if (s < OAL_KSTEPS) {      // tail rows duplicate main rows
 #pragma unroll
-        for (int j = 0; j < 8; ++j)
-            if (frow[j] >= 0) Sst[(size_t)frow[j] * OAL_V1 + col] = S[j];
-    }
+    for (int j = 0; j < 8; ++j)     // tail pairs duplicate main rows: only owners write
+        if (fown[j]) Sst[(size_t)frow[j] * OAL_V1 + col] = S[j];
 }
 
 // ------------------------------------------------------------------------------------
@@ -338,16 +383,15 @@ template <typename T, int C, int R> struct ReadoutLayout {
     static constexpr int U_BYTES = P_BYTES > KV_BYTES ? (P_BYTES > X_BYTES ? P_BYTES : X_BYTES)
                                                       : (KV_BYTES > X_BYTES ? KV_BYTES : X_BYTES);
     static constexpr int O_U = 0;
-    static constexpr int O_Q = O_U + U_BYTES;                                 // T [R*16][QS]
-    static constexpr int O_LIN = O_Q + R * 16 * QS * (int)sizeof(T);         // f32 [R][64]
-    static constexpr int O_W0 = O_LIN + R * OAL_D * 4;                        // f32 [R][64]
+    static constexpr int O_Q = O_U + U_BYTES;                                 // T [R*16][QS], col 64 = 1
+    static constexpr int O_W0 = O_Q + R * 16 * QS * (int)sizeof(T);          // f32 [R][64]
     static constexpr int O_TAIL = O_W0 + R * OAL_D * 4;                       // f32 [R][TAIL_PAIRS]
     static constexpr int O_LZ = O_TAIL + R * OAL_TAIL_PAIRS * 4;              // f32 [R][LZR][64]
     static constexpr int O_PAIR = O_LZ + R * LZR * OAL_D * 4;                 // u8 [2][TAIL_PAIRS]
     static constexpr int BYTES = O_PAIR + 2 * OAL_TAIL_PAIRS;
-    static constexpr int META_UNITS = 16 + 16 + OAL_TAIL_PAIRS / 4 + LZR * 16;   // 16-byte units / head
+    static constexpr int META_UNITS = 16 + OAL_TAIL_PAIRS / 4 + LZR * 16;   // 16-byte units / head
     static constexpr int PAIR_UNITS = 2 * OAL_TAIL_PAIRS / 16;
-    static_assert(U_BYTES % 16 == 0 && O_Q % 16 == 0 && O_LIN % 16 == 0 && O_TAIL % 16 == 0 &&
+    static_assert(U_BYTES % 16 == 0 && O_Q % 16 == 0 && O_W0 % 16 == 0 && O_TAIL % 16 == 0 &&
                   O_LZ % 16 == 0 && O_PAIR % 16 == 0, "alignment");
 };
 
@@ -410,7 +454,6 @@ __global__ __launch_bounds__(256, 2) void oal_readout(
     T *s_vT = s_k + C * QS;                                                // intra: [64][LDV]
     float *s_x = reinterpret_cast<float *>(smem + Lay::O_U);               // combine
     T *s_q = reinterpret_cast<T *>(smem + Lay::O_Q);
-    float *s_lin = reinterpret_cast<float *>(smem + Lay::O_LIN);
     float *s_w0 = reinterpret_cast<float *>(smem + Lay::O_W0);
     float *s_tail = reinterpret_cast<float *>(smem + Lay::O_TAIL);
     float *s_lz = reinterpret_cast<float *>(smem + Lay::O_LZ);
@@ -435,7 +478,7 @@ __global__ __launch_bounds__(256, 2) void oal_readout(
     if (pos0 >= T_len) return;
     const bool general = reinterpret_cast<const OalParamsHeader *>(params)->general != 0;
     const OalKvDev *kvd = kv_ptr(params, n_q_heads, kv);
-    const int ntail = general ? 0 : kvd->nsteps;
+    const int ntail = kvd->nsteps;                // >= 3: linear features and the constant
 
     // 1. stage the tile's queries, the per-head tables and the KV head's tail pairs (all
     //    loads issued before any LDS write), and warm this XCD's L2 with 1/NQT of the
@@ -454,8 +497,7 @@ __global__ __launch_bounds__(256, 2) void oal_readout(
             }
             const OalHeadDev *hd = head_ptr(params, h0 + u / Lay::META_UNITS);
             int w = u % Lay::META_UNITS;
-            if (w < 16) return reinterpret_cast<const oal_u32x4 *>(hd->lin) + w;
-            if ((w -= 16) < 16) return reinterpret_cast<const oal_u32x4 *>(hd->w0) + w;
+            if (w < 16) return reinterpret_cast<const oal_u32x4 *>(hd->w0) + w;
             if ((w -= 16) < OAL_TAIL_PAIRS / 4) return reinterpret_cast<const oal_u32x4 *>(hd->tail) + w;
             w -= OAL_TAIL_PAIRS / 4;
             return reinterpret_cast<const oal_u32x4 *>(hd->Lz) + w;
@@ -463,8 +505,7 @@ __global__ __launch_bounds__(256, 2) void oal_readout(
         auto meta_dst = [&](int u) -> oal_u32x4 * {
             if (u >= R * Lay::META_UNITS) return reinterpret_cast<oal_u32x4 *>(s_pair) + (u - R * Lay::META_UNITS);
             int i = u / Lay::META_UNITS, w = u % Lay::META_UNITS;
-            if (w < 16) return reinterpret_cast<oal_u32x4 *>(s_lin + i * OAL_D) + w;
-            if ((w -= 16) < 16) return reinterpret_cast<oal_u32x4 *>(s_w0 + i * OAL_D) + w;
+            if (w < 16) return reinterpret_cast<oal_u32x4 *>(s_w0 + i * OAL_D) + w;
             if ((w -= 16) < OAL_TAIL_PAIRS / 4) return reinterpret_cast<oal_u32x4 *>(s_tail + i * OAL_TAIL_PAIRS) + w;
             w -= OAL_TAIL_PAIRS / 4;
             return reinterpret_cast<oal_u32x4 *>(s_lz + i * Lay::LZR * OAL_D) + w;
@@ -505,6 +546,8 @@ __global__ __launch_bounds__(256, 2) void oal_readout(
             if (u < NMU) *meta_dst(u) = rm[j];
         }
         if (touch.x == 0x9e3779b9u && touch.y == 0x7f4a7c15u && T_len < 0) y[0] = 0.0f;  // never true
+        // q_64 = 1: the second factor of the linear and constant tail entries
+        for (int u = tid; u < R * 16; u += 256) s_q[u * QS + OAL_D] = (T)1.0f;
     }
     __syncthreads();
     // p table: p = w0[r] q_r (fp32), the rank-1 factor of the quadratic coefficients
@@ -514,10 +557,6 @@ __global__ __launch_bounds__(256, 2) void oal_readout(
     }
     __syncthreads();
 
-    float a_h[RW];
-#pragma unroll
-    for (int li = 0; li < RW; ++li) a_h[li] = li < nh ? head_ptr(params, h0 + hb + li)->a : 0.0f;
-
     oal_f32x4 acc[RW][5];
 #pragma unroll
     for (int li = 0; li < RW; ++li)
@@ -525,9 +564,9 @@ __global__ __launch_bounds__(256, 2) void oal_readout(
         for (int n = 0; n < 5; ++n) acc[li][n] = oal_splat(0.0f);
 
     // 2. inter-chunk: phi(Q) . S_c over this wave's K-steps: the 36 main K-steps with
-    //    rq = 2 j + par, then the tail K-steps 2 x + par. Snapshot fragments are fetched two
-    //    steps ahead into a ring of three buffers (the loop is unrolled by three so that the
-    //    ring needs no register moves).
+    //    rq = 2 j + par, then the tail K-steps 2 x + par. Snapshot fragments are fetched one
+    //    step ahead into two buffers (the loop is unrolled by two so that they need no
+    //    register moves); the other wave of the SIMD covers the remaining latency.
     constexpr int KB = snap_kstep_bytes<T>();
     const unsigned char *sbase = snap + ((size_t)bkv * nchunks + c) * OAL_SNAP_KSTEPS * KB;
     const int ntot = NMAIN + (ntail + 1 - par) / 2;
@@ -544,70 +583,57 @@ __global__ __launch_bounds__(256, 2) void oal_readout(
         const unsigned char *sp = sbase + (size_t)sk * KB;
 #pragma unroll
         for (int n = 0; n < 4; ++n) bf[n].load(sp + (n * 64 + lane) * OalFrag<T>::kBytes);
-        if (lr == 0) bf[4].load(sp + (4 * 64 + g) * OalFrag<T>::kBytes);
-        else bf[4].zero();
+        // column 64 ("1" of [v;1]): every lane reads its lane group's fragment, so all 16
+        // columns of the fifth tile carry the denominator
+        bf[4].load(sp + (4 * 64 + g) * OalFrag<T>::kBytes);
     };
-    auto inter = [&](auto gen) {
-        constexpr bool GEN = decltype(gen)::value;
+    // NH: heads of this wave's subset (compile time); GEN: general blob
+    auto inter = [&](auto nh_c, auto gen_c) {
+        constexpr int NH = decltype(nh_c)::value;
+        constexpr bool GEN = decltype(gen_c)::value;
         int tb = 0, j = 0;                        // compute position
-        float pt[RW][8];
+        float pt[NH][8];
+        auto load_pt = [&]() {
+#pragma unroll
+            for (int li = 0; li < NH; ++li) {
+                const float4 *pp = reinterpret_cast<const float4 *>(s_p + ((hb + li) * 16 + lr) * PS + 8 * tb);
+                const float4 x0 = pp[0], x1 = pp[1];
+                pt[li][0] = x0.x; pt[li][1] = x0.y; pt[li][2] = x0.z; pt[li][3] = x0.w;
+                pt[li][4] = x1.x; pt[li][5] = x1.y; pt[li][6] = x1.z; pt[li][7] = x1.w;
+            }
+        };
+        auto gen_mul = [&](int li, int rq, float (&phi)[8]) {
+            if (GEN) {   // general blob: the full coefficient of each slot, from the blob
+                const float4 *wp = reinterpret_cast<const float4 *>(
+                    head_ptr(params, h0 + hb + li)->wslot + oal_kstep(tb, rq) * 32 + 8 * g);
+                const float4 w0v = wp[0], w1v = wp[1];
+                phi[0] *= w0v.x; phi[1] *= w0v.y; phi[2] *= w0v.z; phi[3] *= w0v.w;
+                phi[4] *= w1v.x; phi[5] *= w1v.y; phi[6] *= w1v.z; phi[7] *= w1v.w;
+            }
+        };
+        // main K-step: A = p_r p_t (times the slot coefficient in a general blob)
         auto main_step = [&](const OalFrag<T> (&bc)[5]) {
             const int rq = 2 * j + par;
             const int r = 4 * rq + g;
-            if (j == 0) {
+            if (j == 0) load_pt();
+            float prv[NH];
 #pragma unroll
-                for (int li = 0; li < RW; ++li) {
-                    if (li < nh) {
-                        const float4 *pp = reinterpret_cast<const float4 *>(s_p + ((hb + li) * 16 + lr) * PS + 8 * tb);
-                        float4 x0 = pp[0], x1 = pp[1];
-                        pt[li][0] = x0.x; pt[li][1] = x0.y; pt[li][2] = x0.z; pt[li][3] = x0.w;
-                        pt[li][4] = x1.x; pt[li][5] = x1.y; pt[li][6] = x1.z; pt[li][7] = x1.w;
-                    }
-                }
-            }
-            float prv[RW];
+            for (int li = 0; li < NH; ++li) prv[li] = s_p[((hb + li) * 16 + lr) * PS + r];
 #pragma unroll
-            for (int li = 0; li < RW; ++li) prv[li] = li < nh ? s_p[((hb + li) * 16 + lr) * PS + r] : 0.0f;
-            const bool lin_step = par == 1 && j == tb;
-            float lin0[RW], lin1[RW];
-            if (lin_step) {
-                const int r0 = 8 * tb + 2 * g;
+            for (int li = 0; li < NH; ++li) {
+                float phi[8];
 #pragma unroll
-                for (int li = 0; li < RW; ++li) {
-                    const T *qrow = s_q + ((hb + li) * 16 + lr) * QS;
-                    lin0[li] = s_lin[(hb + li) * OAL_D + r0] * (float)qrow[r0];
-                    lin1[li] = s_lin[(hb + li) * OAL_D + r0 + 1] * (float)qrow[r0 + 1];
-                }
-            }
+                for (int e = 0; e < 8; ++e) phi[e] = prv[li] * pt[li][e];
+                gen_mul(li, rq, phi);
+                OalFrag<T> a;
+                a.set(phi);
 #pragma unroll
-            for (int li = 0; li < RW; ++li) {
-                if (li < nh) {
-                    float phi[8];
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) phi[e] = prv[li] * pt[li][e];
-                    if (GEN) {
-                        // general blob: the full coefficient of each slot, from the blob
-                        const float4 *wp = reinterpret_cast<const float4 *>(
-                            head_ptr(params, h0 + hb + li)->wslot + oal_kstep(tb, rq) * 32 + 8 * g);
-                        const float4 w0v = wp[0], w1v = wp[1];
-                        phi[0] *= w0v.x; phi[1] *= w0v.y; phi[2] *= w0v.z; phi[3] *= w0v.w;
-                        phi[4] *= w1v.x; phi[5] *= w1v.y; phi[6] *= w1v.z; phi[7] *= w1v.w;
-                    }
-                    if (lin_step) {
-                        phi[0] = lin0[li];
-                        phi[1] = lin1[li];
-                        if (tb == 0 && g == 0) phi[2] = a_h[li];
-                    }
-                    OalFrag<T> a;
-                    a.set(phi);
-#pragma unroll
-                    for (int n = 0; n < 5; ++n) acc[li][n] = oal_mma(a, bc[n], acc[li][n]);
-                }
+                for (int n = 0; n < 5; ++n) acc[li][n] = oal_mma(a, bc[n], acc[li][n]);
             }
             if (++j > tb) { ++tb; j = 0; }
         };
-        // tail K-step x: slot jj = 32 x + 8 g + e carries pair (ra[jj], rb[jj]); head li adds
-        // tail[jj] q_ra q_rb (zero past the KV head's pairs)
+        // tail K-step x: slot jj = 32 x + 8 g + e carries entry (ra[jj], rb[jj]); head li adds
+        // tail[jj] q_ra q_rb with q_64 = 1 (zero past the KV head's entries)
         auto tail_step = [&](const OalFrag<T> (&bc)[5], int x) {
             const int j0 = 32 * x + 8 * g;
             const uint2 pra = *reinterpret_cast<const uint2 *>(s_pair + j0);
@@ -619,54 +645,47 @@ __global__ __launch_bounds__(256, 2) void oal_readout(
                 ib[e] = ((e < 4 ? prb.x : prb.y) >> (8 * (e & 3))) & 0xff;
             }
 #pragma unroll
-            for (int li = 0; li < RW; ++li) {
-                if (li < nh) {
-                    const T *qrow = s_q + ((hb + li) * 16 + lr) * QS;
-                    const float4 *cp = reinterpret_cast<const float4 *>(s_tail + (hb + li) * OAL_TAIL_PAIRS + j0);
-                    float4 c0 = cp[0], c1 = cp[1];
-                    float cf[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
-                    float qa[8], qb[8];
+            for (int li = 0; li < NH; ++li) {
+                const T *qrow = s_q + ((hb + li) * 16 + lr) * QS;
+                const float4 *cp = reinterpret_cast<const float4 *>(s_tail + (hb + li) * OAL_TAIL_PAIRS + j0);
+                const float4 c0 = cp[0], c1 = cp[1];
+                const float cf[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
+                float phi[8];
 #pragma unroll
-                    for (int e = 0; e < 8; ++e) { qa[e] = (float)qrow[ia[e]]; qb[e] = (float)qrow[ib[e]]; }
-                    float phi[8];
+                for (int e = 0; e < 8; ++e) phi[e] = cf[e] * (float)qrow[ia[e]] * (float)qrow[ib[e]];
+                OalFrag<T> a;
+                a.set(phi);
 #pragma unroll
-                    for (int e = 0; e < 8; ++e) phi[e] = cf[e] * qa[e] * qb[e];
-                    OalFrag<T> a;
-                    a.set(phi);
-#pragma unroll
-                    for (int n = 0; n < 5; ++n) acc[li][n] = oal_mma(a, bc[n], acc[li][n]);
-                }
+                for (int n = 0; n < 5; ++n) acc[li][n] = oal_mma(a, bc[n], acc[li][n]);
             }
         };
-        static_assert(NMAIN % 3 == 0, "the main loop is unrolled by three");
-        OalFrag<T> b0[5], b1[5], b2[5];
+        static_assert(NMAIN % 2 == 0, "the main loop is unrolled by two");
+        OalFrag<T> b0[5], b1[5];
         load_next(b0);
-        load_next(b1);
-        for (int it = 0; it < NMAIN; it += 3) {
-            load_next(b2);
+        for (int it = 0; it < NMAIN; it += 2) {
+            load_next(b1);
             main_step(b0);
-            if (it + 3 < ntot) load_next(b0);
+            if (it + 2 < ntot) load_next(b0);
             main_step(b1);
-            if (it + 4 < ntot) load_next(b1);
-            main_step(b2);
         }
-        // tail K-steps (b0 and b1 already hold the first two)
-        for (int x = 0; x < ntot - NMAIN; x += 3) {
-            if (NMAIN + x + 2 < ntot) load_next(b2);
+        // tail K-steps (b0 already holds the first)
+        for (int x = 0; x < ntot - NMAIN; x += 2) {
+            if (NMAIN + x + 1 < ntot) load_next(b1);
             tail_step(b0, 2 * x + par);
             if (x + 1 < ntot - NMAIN) {
-                if (NMAIN + x + 3 < ntot) load_next(b0);
+                if (NMAIN + x + 2 < ntot) load_next(b0);
                 tail_step(b1, 2 * (x + 1) + par);
-            }
-            if (x + 2 < ntot - NMAIN) {
-                if (NMAIN + x + 4 < ntot) load_next(b1);
-                tail_step(b2, 2 * (x + 2) + par);
             }
         }
     };
-    if (nh > 0) {
-        if (general) inter(std::true_type{});
-        else inter(std::false_type{});
+    using RWc = std::integral_constant<int, RW>;
+    using RBc = std::integral_constant<int, (R - RW > 0 ? R - RW : 1)>;
+    if (hs == 0) {
+        if (general) inter(RWc{}, std::true_type{});
+        else inter(RWc{}, std::false_type{});
+    } else if (R - RW > 0) {
+        if (general) inter(RBc{}, std::true_type{});
+        else inter(RBc{}, std::false_type{});
     }
 
     // 3. stage K and V^T of the keys this tile can see into the region the p table used
@@ -812,7 +831,7 @@ size_t readout_lds() { return (size_t)ReadoutLayout<T, C, R>::BYTES; }
 
 struct PrefillPlan {
     int nchunks, Tpad;
-    size_t snap_bytes, delta_bytes, vt_bytes;
+    size_t snap_bytes, delta_bytes, tinit_bytes, vt_bytes;
 };
 
 template <typename T>
@@ -824,6 +843,7 @@ PrefillPlan make_plan(const oal_dims &d, int T_len, int C) {
     auto r256 = [](size_t x) { return (x + 255) / 256 * 256; };
     p.snap_bytes = r256(bkv * p.nchunks * OAL_SNAP_KSTEPS * (size_t)snap_kstep_bytes<T>());
     p.delta_bytes = r256(bkv * p.nchunks * OAL_SNAP_KSTEPS * (size_t)kDeltaStep * sizeof(float));
+    p.tinit_bytes = r256(bkv * OAL_TAIL_STEPS * (size_t)kDeltaStep * sizeof(float));
     p.vt_bytes = r256(bkv * OAL_D * (size_t)p.Tpad * sizeof(T));
     return p;
 }
@@ -855,7 +875,8 @@ hipError_t launch_all(const oal_dims &d, int T_len, const void *q, const void *k
     PrefillPlan p = make_plan<T>(d, T_len, C);
     unsigned char *snap = reinterpret_cast<unsigned char *>(ws);
     float *delta = reinterpret_cast<float *>(snap + p.snap_bytes);
-    T *vT = reinterpret_cast<T *>(snap + p.snap_bytes + p.delta_bytes);
+    float *tinit = reinterpret_cast<float *>(snap + p.snap_bytes + p.delta_bytes);
+    T *vT = reinterpret_cast<T *>(snap + p.snap_bytes + p.delta_bytes + p.tinit_bytes);
     const int bkv = d.batch * d.n_kv_heads;
     const unsigned char *pb = reinterpret_cast<const unsigned char *>(params);
     hipError_t e;
@@ -868,13 +889,13 @@ hipError_t launch_all(const oal_dims &d, int T_len, const void *q, const void *k
             return e;
         hipLaunchKernelGGL(kern, dim3(kScanBlocks + 1, p.nchunks, bkv), dim3(64 * kScanWaves), lds, stream,
                            T_len, p.Tpad, p.nchunks, d.n_q_heads, d.n_kv_heads, reinterpret_cast<const T *>(k),
-                           reinterpret_cast<const T *>(v), pb, delta, vT);
+                           reinterpret_cast<const T *>(v), pb, state, delta, tinit, vT);
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
     {
         const size_t nthr = (size_t)bkv * OAL_SNAP_KSTEPS * kFrags;
         hipLaunchKernelGGL(oal_scan_prefix<T>, dim3((unsigned)((nthr + 255) / 256)), dim3(256), 0, stream,
-                           p.nchunks, d.n_q_heads, d.n_kv_heads, bkv, pb, delta, state, snap);
+                           p.nchunks, d.n_q_heads, d.n_kv_heads, bkv, pb, delta, tinit, state, snap);
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
     if (marks && (e = hipEventRecord(marks[1], stream)) != hipSuccess) return e;
@@ -901,7 +922,7 @@ hipError_t launch_all(const oal_dims &d, int T_len, const void *q, const void *k
 
 size_t oal_prefill_ws_bytes_impl(const oal_dims &d, int T_len, int C) {
     PrefillPlan p = d.dtype == OAL_BF16 ? make_plan<__bf16>(d, T_len, C) : make_plan<float>(d, T_len, C);
-    return p.snap_bytes + p.delta_bytes + p.vt_bytes;
+    return p.snap_bytes + p.delta_bytes + p.tinit_bytes + p.vt_bytes;
 }
 
 hipError_t oal_launch_prefill(const oal_dims &d, int T_len, int C, const void *q, const void *k,

@@ -126,13 +126,10 @@ def quad_row(r, t):
 
 
 def slot(tb, rq, g, e):
+    """main prefill slot: quadratic (r, t) with r <= t, else empty"""
     r, t = 4 * rq + g, 8 * tb + e
     if r <= t:
         return "quad", r, t
-    if rq == 2 * tb + 1 and e < 2:
-        return "lin", 8 * tb + 2 * g + e, None
-    if tb == 0 and rq == 1 and g == 0 and e == 2:
-        return "const", None, None
     return "empty", None, None
 
 
@@ -175,9 +172,9 @@ def test_blob_modes():
         general, _, kvs = parse(gpq.oal_params_pack(gpq.make_dims(B, Hq, Hkv, "f32"),
                                                     gpq.HeadParamsC.from_params(inp.params)), Hq, Hkv)
         modes[inp.name] = (general, [int(k["nsteps"]) for k in kvs])
-    assert modes["g64"][0] == 1 and modes["g64"][1] == [0]
-    assert modes["cfg1"] == (0, [1])                    # tail dims 60..63: 10 pairs
-    assert modes["qwen_like_small"][0] == 0 and min(modes["qwen_like_small"][1]) >= 1
+    assert modes["g64"][0] == 1 and modes["g64"][1] == [3]     # linear + constant only
+    assert modes["cfg1"] == (0, [3])                    # 65 + 10 pairs of dims 60..63
+    assert modes["qwen_like_small"][0] == 0 and min(modes["qwen_like_small"][1]) >= 3
 
 
 @pytest.mark.parametrize("inp", list(_cases()), ids=lambda c: c.name)
@@ -189,7 +186,8 @@ def test_blob_reproduces_oracle(inp):
     y_ref, den_ref = oracle.dense(inp.q, inp.k, inp.v, inp.params, return_den=True)
     n_rep = Hq // Hkv
     i = T - 1
-    # every slot of the prefill order holds exactly one feature (or none)
+    # the main slots hold every quadratic feature once; tail entries 0..64 of every KV head
+    # hold the linear features and the constant
     seen = []
     for tb in range(8):
         for rq in range(2 * tb + 2):
@@ -198,11 +196,10 @@ def test_blob_reproduces_oracle(inp):
                     kind, a, b = slot(tb, rq, g, e)
                     if kind == "quad":
                         seen.append(quad_row(a, b))
-                    elif kind == "lin":
-                        seen.append(1 + a)
-                    elif kind == "const":
-                        seen.append(0)
-    assert sorted(seen) == list(range(2145))
+    assert sorted(seen) == list(range(65, 2145))
+    for kvd in kvs:
+        assert list(kvd["ra"][:65]) == list(range(65)) and list(kvd["rb"][:65]) == [64] * 65
+        assert kvd["npairs"] >= 65 and kvd["nsteps"] == (kvd["npairs"] + 31) // 32 <= 8
     for h in range(Hq):
         hd = heads[h]
         kvd = kvs[h // n_rep]
@@ -213,7 +210,7 @@ def test_blob_reproduces_oracle(inp):
         np.testing.assert_allclose(u[:64] / u[64], y_ref[0, h, i], rtol=0, atol=2e-5)
         np.testing.assert_allclose(u[64], den_ref[0, h, i], rtol=2e-5)
         # prefill slot form on the scaled state: main slots (rank-1 p_a p_b, or the general
-        # coefficient), linear, constant, then the KV head's tail pairs
+        # coefficient), then the KV head's tail entries tail[j] q_a q_b with q_64 = 1
         p = hd["w0"].astype(np.float64) * q
         u2 = np.zeros(65)
         for tb in range(8):
@@ -227,17 +224,18 @@ def test_blob_reproduces_oracle(inp):
                             if general:
                                 phi *= float(hd["wslot"][s * 32 + 8 * g + e])
                             u2 += phi * Hs[quad_row(a, b)] * (2.0 if a < b else 1.0) / 64
-                        elif kind == "lin":
-                            u2 += float(hd["lin"][a]) * q[a] * Hs[1 + a] / 8
-                        elif kind == "const":
-                            u2 += float(hd["a"]) * Hs[0]
         if general:
-            assert kvd["nsteps"] == 0
-        else:
-            assert kvd["nsteps"] == (kvd["npairs"] + 31) // 32 <= 8
-            for j in range(kvd["npairs"]):
-                a, b = int(kvd["ra"][j]), int(kvd["rb"][j])
-                u2 += float(hd["tail"][j]) * q[a] * q[b] * Hs[quad_row(a, b)] * (2.0 if a < b else 1.0) / 64
+            assert kvd["npairs"] == 65
+        qx = np.append(q, 1.0)
+        for j in range(kvd["npairs"]):
+            a, b = int(kvd["ra"][j]), int(kvd["rb"][j])
+            if b == 64 and a == 64:
+                row, sc = 0, 1.0
+            elif b == 64:
+                row, sc = 1 + a, 1 / 8
+            else:
+                row, sc = quad_row(a, b), (2.0 if a < b else 1.0) / 64
+            u2 += float(hd["tail"][j]) * qx[a] * qx[b] * Hs[row] * sc
         np.testing.assert_allclose(u2[:64] / u2[64], y_ref[0, h, i], rtol=0, atol=2e-5)
         # intra-chunk form: kappa = eps + sum_m (L00 [m==0] + sum_r Lz[m][r] q_r k_r)^2
         for j in (0, i // 2, i):
