@@ -384,14 +384,13 @@ template <typename T, int C, int R> struct ReadoutLayout {
                                                       : (KV_BYTES > X_BYTES ? KV_BYTES : X_BYTES);
     static constexpr int O_U = 0;
     static constexpr int O_Q = O_U + U_BYTES;                                 // T [R*16][QS], col 64 = 1
-    static constexpr int O_W0 = O_Q + R * 16 * QS * (int)sizeof(T);          // f32 [R][64]
-    static constexpr int O_TAIL = O_W0 + R * OAL_D * 4;                       // f32 [R][TAIL_PAIRS]
+    static constexpr int O_TAIL = O_Q + R * 16 * QS * (int)sizeof(T);        // f32 [R][TAIL_PAIRS]
     static constexpr int O_LZ = O_TAIL + R * OAL_TAIL_PAIRS * 4;              // f32 [R][LZR][64]
     static constexpr int O_PAIR = O_LZ + R * LZR * OAL_D * 4;                 // u8 [2][TAIL_PAIRS]
     static constexpr int BYTES = O_PAIR + 2 * OAL_TAIL_PAIRS;
-    static constexpr int META_UNITS = 16 + OAL_TAIL_PAIRS / 4 + LZR * 16;   // 16-byte units / head
+    static constexpr int META_UNITS = OAL_TAIL_PAIRS / 4 + LZR * 16;   // 16-byte units / head
     static constexpr int PAIR_UNITS = 2 * OAL_TAIL_PAIRS / 16;
-    static_assert(U_BYTES % 16 == 0 && O_Q % 16 == 0 && O_W0 % 16 == 0 && O_TAIL % 16 == 0 &&
+    static_assert(U_BYTES % 16 == 0 && O_Q % 16 == 0 && O_TAIL % 16 == 0 &&
                   O_LZ % 16 == 0 && O_PAIR % 16 == 0, "alignment");
 };
 
@@ -454,7 +453,6 @@ __global__ __launch_bounds__(256, 2) void oal_readout(
     T *s_vT = s_k + C * QS;                                                // intra: [64][LDV]
     float *s_x = reinterpret_cast<float *>(smem + Lay::O_U);               // combine
     T *s_q = reinterpret_cast<T *>(smem + Lay::O_Q);
-    float *s_w0 = reinterpret_cast<float *>(smem + Lay::O_W0);
     float *s_tail = reinterpret_cast<float *>(smem + Lay::O_TAIL);
     float *s_lz = reinterpret_cast<float *>(smem + Lay::O_LZ);
     unsigned char *s_pair = smem + Lay::O_PAIR;
@@ -489,6 +487,7 @@ __global__ __launch_bounds__(256, 2) void oal_readout(
         constexpr int NQU = R * 16 * UPQ, NMU = R * Lay::META_UNITS + Lay::PAIR_UNITS;
         constexpr int NQJ = (NQU + 255) / 256, NMJ = (NMU + 255) / 256;
         oal_u32x4 rq[NQJ], rm[NMJ];
+        float4 rw[NQJ][EPU / 4];    // w0 of the staged q unit's dims
         auto meta_src = [&](int u) -> const oal_u32x4 * {
             if (u >= R * Lay::META_UNITS) {
                 int w = u - R * Lay::META_UNITS;
@@ -497,16 +496,14 @@ __global__ __launch_bounds__(256, 2) void oal_readout(
             }
             const OalHeadDev *hd = head_ptr(params, h0 + u / Lay::META_UNITS);
             int w = u % Lay::META_UNITS;
-            if (w < 16) return reinterpret_cast<const oal_u32x4 *>(hd->w0) + w;
-            if ((w -= 16) < OAL_TAIL_PAIRS / 4) return reinterpret_cast<const oal_u32x4 *>(hd->tail) + w;
+            if (w < OAL_TAIL_PAIRS / 4) return reinterpret_cast<const oal_u32x4 *>(hd->tail) + w;
             w -= OAL_TAIL_PAIRS / 4;
             return reinterpret_cast<const oal_u32x4 *>(hd->Lz) + w;
         };
         auto meta_dst = [&](int u) -> oal_u32x4 * {
             if (u >= R * Lay::META_UNITS) return reinterpret_cast<oal_u32x4 *>(s_pair) + (u - R * Lay::META_UNITS);
             int i = u / Lay::META_UNITS, w = u % Lay::META_UNITS;
-            if (w < 16) return reinterpret_cast<oal_u32x4 *>(s_w0 + i * OAL_D) + w;
-            if ((w -= 16) < OAL_TAIL_PAIRS / 4) return reinterpret_cast<oal_u32x4 *>(s_tail + i * OAL_TAIL_PAIRS) + w;
+            if (w < OAL_TAIL_PAIRS / 4) return reinterpret_cast<oal_u32x4 *>(s_tail + i * OAL_TAIL_PAIRS) + w;
             w -= OAL_TAIL_PAIRS / 4;
             return reinterpret_cast<oal_u32x4 *>(s_lz + i * Lay::LZR * OAL_D) + w;
         };
@@ -517,6 +514,9 @@ __global__ __launch_bounds__(256, 2) void oal_readout(
             rq[j] = (u < NQU && pos < T_len)
                 ? *reinterpret_cast<const oal_u32x4 *>(q + (((size_t)b * n_q_heads + h0 + i) * T_len + pos) * OAL_D + a * EPU)
                 : zero16();
+            const float4 *wp = reinterpret_cast<const float4 *>(head_ptr(params, h0 + (u < NQU ? i : 0))->w0 + a * EPU);
+#pragma unroll
+            for (int k4 = 0; k4 < EPU / 4; ++k4) rw[j][k4] = wp[k4];
         }
 #pragma unroll
         for (int j = 0; j < NMJ; ++j) {
@@ -538,7 +538,16 @@ __global__ __launch_bounds__(256, 2) void oal_readout(
         for (int j = 0; j < NQJ; ++j) {
             int u = tid + 256 * j;
             int i = u / (16 * UPQ), qi = (u / UPQ) % 16, a = u % UPQ;
-            if (u < NQU) *reinterpret_cast<oal_u32x4 *>(s_q + (i * 16 + qi) * QS + a * EPU) = rq[j];
+            if (u < NQU) {
+                *reinterpret_cast<oal_u32x4 *>(s_q + (i * 16 + qi) * QS + a * EPU) = rq[j];
+                // p table: p = w0[r] q_r (fp32), the rank-1 factor of the quadratic coefficients
+                const T *el = reinterpret_cast<const T *>(&rq[j]);
+                float4 *pp = reinterpret_cast<float4 *>(s_p + (i * 16 + qi) * PS + a * EPU);
+#pragma unroll
+                for (int k4 = 0; k4 < EPU / 4; ++k4)
+                    pp[k4] = make_float4(rw[j][k4].x * (float)el[4 * k4], rw[j][k4].y * (float)el[4 * k4 + 1],
+                                         rw[j][k4].z * (float)el[4 * k4 + 2], rw[j][k4].w * (float)el[4 * k4 + 3]);
+            }
         }
 #pragma unroll
         for (int j = 0; j < NMJ; ++j) {
@@ -548,12 +557,6 @@ __global__ __launch_bounds__(256, 2) void oal_readout(
         if (touch.x == 0x9e3779b9u && touch.y == 0x7f4a7c15u && T_len < 0) y[0] = 0.0f;  // never true
         // q_64 = 1: the second factor of the linear and constant tail entries
         for (int u = tid; u < R * 16; u += 256) s_q[u * QS + OAL_D] = (T)1.0f;
-    }
-    __syncthreads();
-    // p table: p = w0[r] q_r (fp32), the rank-1 factor of the quadratic coefficients
-    for (int u = tid; u < R * 16 * OAL_D; u += 256) {
-        int i = u / (16 * OAL_D), qi = (u / OAL_D) % 16, r = u % OAL_D;
-        s_p[(i * 16 + qi) * PS + r] = s_w0[i * OAL_D + r] * (float)s_q[(i * 16 + qi) * QS + r];
     }
     __syncthreads();
 
@@ -813,11 +816,14 @@ __global__ __launch_bounds__(256, 2) void oal_readout(
         float *yh = y + ((size_t)b * n_q_heads + h0 + i) * T_len * OAL_D;
 #pragma unroll
         for (int ii = 0; ii < 4; ++ii) {
-            float den = __shfl(acc[li][4][ii], lane & 48);
+            // 1 / den: hardware reciprocal refined by one Newton-Raphson step
+            const float den = __shfl(acc[li][4][ii], lane & 48);
+            float rd = __builtin_amdgcn_rcpf(den);
+            rd = rd * (2.0f - den * rd);
             int pos = pos0 + 4 * g + ii;
             if (pos < T_len) {
 #pragma unroll
-                for (int n = 0; n < 4; ++n) yh[(size_t)pos * OAL_D + 16 * n + lr] = acc[li][n][ii] / den;
+                for (int n = 0; n < 4; ++n) yh[(size_t)pos * OAL_D + 16 * n + lr] = acc[li][n][ii] * rd;
             }
         }
     }
