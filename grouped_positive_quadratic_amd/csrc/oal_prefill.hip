@@ -8,23 +8,25 @@
 //   u~_i = phi_h(q_i) . S_c + sum_{j in chunk c, j <= i} kappa_h(q_i, k_j) [v_j;1]
 //
 // Kernels, in launch order:
+//  0. oal_intra: per (chunk x 16-query tile, sequence x KV head) the exact intra-chunk kernel
+//     sums of every query head, kappa [V;1] unnormalised, on MFMA (independent of the state).
 //  1. oal_scan_delta: per (sequence x KV head, chunk, K-step), in parallel, the chunk's state
 //     increment psi(K_c)^T [V_c;1] on MFMA (fp32), from K and V staged transposed in LDS.
-//     Besides the 72 main K-steps, up to 8 tail K-steps repeat the KV head's non-bulk pairs.
-//     It also writes V^T of each chunk for the readout.
+//     Besides the 72 main K-steps, up to 8 tail K-steps carry the linear features, the
+//     constant and the KV head's non-bulk pairs.
 //  2. oal_scan_prefix: per state fragment, the running sum over chunks from the incoming
 //     state: the snapshot before each chunk (scaled, bf16 or fp32, in the MFMA operand order
 //     of the readout) and the final state.
-//  3. oal_readout
-//     per (sequence x KV head x head group, chunk, 16-query tile), 4 waves: two head
-//     subsets times two K-step parities. The query heads of one KV head share every
+//  3. oal_readout: per (sequence x KV head x head group, chunk, 16-query tile), 4 waves: two
+//     head subsets times two K-step parities. The query heads of one KV head share every
 //     snapshot fragment. The A operand of a main K-step is p_r p_t with p = w0 o q (the
-//     rank-1 part of the group-pair coefficients); the tail K-steps add D q_r q_t for the
-//     non-bulk pairs. Then the intra-chunk kernel sum, a combine through LDS and the
-//     divide y = u~[0:64] / u~[64]. Workgroups of one chunk are placed on one XCD so the
-//     snapshot is fetched into that XCD's L2 once.
+//     rank-1 part of the group-pair coefficients); the tail K-steps add tail[j] q_a q_b.
+//     The two parities and the intra-chunk sum are combined and divided,
+//     y = u~[0:64] / u~[64]. Workgroups of one chunk are placed on one XCD so the snapshot is
+//     fetched into that XCD's L2 once.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <type_traits>
 
 #include "oal.h"
@@ -169,13 +171,12 @@ __device__ inline void store_frags(float *dp, const oal_f32x4 (&acc)[2][5], int 
 }
 
 // grid (K-step blocks + 1 tail block, chunks, sequence x KV head); 8 waves, one K-step each.
-// The chunk's K and V are staged transposed in LDS ([dim][token]); workgroups of K-step
-// block 0 also write V^T of the chunk for the readout.
+// The chunk's K and V are staged transposed in LDS ([dim][token]).
 template <typename T, int C>
 __global__ __launch_bounds__(64 * kScanWaves) void oal_scan_delta(
-    int T_len, int Tpad, int nchunks, int n_q_heads, int n_kv_heads, const T *__restrict__ k,
+    int T_len, int nchunks, int n_q_heads, int n_kv_heads, const T *__restrict__ k,
     const T *__restrict__ v, const unsigned char *__restrict__ params, const float *__restrict__ state,
-    float *__restrict__ delta, float *__restrict__ tinit, T *__restrict__ vT) {
+    float *__restrict__ delta, float *__restrict__ tinit) {
     constexpr int EPU = 16 / (int)sizeof(T);
     constexpr int LD = C + EPU;                         // padded row, 16-byte aligned
     constexpr int UPT = OAL_D / EPU;                    // 16-byte units per token row
@@ -222,15 +223,6 @@ __global__ __launch_bounds__(64 * kScanWaves) void oal_scan_delta(
         }
     }
     __syncthreads();
-    if (blockIdx.x == 0) {
-        constexpr int NVU = OAL_D * C / EPU;
-        T *vTb = vT + (size_t)bkv * OAL_D * Tpad + (size_t)c * C;
-        for (int u = tid; u < NVU; u += 64 * kScanWaves) {
-            const int row = u / (C / EPU), cu = u % (C / EPU);
-            *reinterpret_cast<oal_u32x4 *>(vTb + (size_t)row * Tpad + cu * EPU) =
-                *reinterpret_cast<const oal_u32x4 *>(s_vT + row * LD + cu * EPU);
-        }
-    }
     if (idle) return;
 
     int frow[8], ra[2], rb[2];
@@ -366,40 +358,13 @@ __global__ __launch_bounds__(256) void oal_scan_prefix(int nchunks, int n_q_head
         if (fown[j]) Sst[(size_t)frow[j] * OAL_V1 + col] = S[j];
 }
 
-// ------------------------------------------------------------------------------------
-// 3. readout
-template <typename T, int C, int R> struct ReadoutLayout {
-    static constexpr int EPU = 16 / (int)sizeof(T);
-    static constexpr int RW = (R + 1) / 2;      // heads of one wave pair (head subset)
-    static constexpr int QS = OAL_D + EPU;      // q / key row in LDS (16-byte aligned)
-    static constexpr int LDV = C + EPU;         // V^T row
-    static constexpr int PS = OAL_D + 4;        // fp32 p-table row
-    static constexpr int LZR = 8;               // Lz rows m < 8 kept in LDS
-    // Byte offsets. The "union" region holds the fp32 p table during the inter-chunk loop,
-    // then K and V^T of the chunk during the intra-chunk part, then the combine buffer.
-    static constexpr int P_BYTES = R * 16 * PS * 4;
-    static constexpr int KV_BYTES = C * QS * (int)sizeof(T) + OAL_D * LDV * (int)sizeof(T);
-    static constexpr int X_BYTES = R * 5 * 4 * 64 * 4;
-    static constexpr int U_BYTES = P_BYTES > KV_BYTES ? (P_BYTES > X_BYTES ? P_BYTES : X_BYTES)
-                                                      : (KV_BYTES > X_BYTES ? KV_BYTES : X_BYTES);
-    static constexpr int O_U = 0;
-    static constexpr int O_Q = O_U + U_BYTES;                                 // T [R*16][QS], col 64 = 1
-    static constexpr int O_TAIL = O_Q + R * 16 * QS * (int)sizeof(T);        // f32 [R][TAIL_PAIRS]
-    static constexpr int O_LZ = O_TAIL + R * OAL_TAIL_PAIRS * 4;              // f32 [R][LZR][64]
-    static constexpr int O_PAIR = O_LZ + R * LZR * OAL_D * 4;                 // u8 [2][TAIL_PAIRS]
-    static constexpr int BYTES = O_PAIR + 2 * OAL_TAIL_PAIRS;
-    static constexpr int META_UNITS = OAL_TAIL_PAIRS / 4 + LZR * 16;   // 16-byte units / head
-    static constexpr int PAIR_UNITS = 2 * OAL_TAIL_PAIRS / 16;
-    static_assert(U_BYTES % 16 == 0 && O_Q % 16 == 0 && O_TAIL % 16 == 0 &&
-                  O_LZ % 16 == 0 && O_PAIR % 16 == 0, "alignment");
-};
-
 // One term z_m of the intra-chunk kernel for a 16-query tile of one head:
 //   z_m^T (16 keys x 16 queries) = K_kt (keys x 64) . (Lz[m] o q)^T + c_m, for key tiles
 //   kt <= qt of the chunk, and kappa[kt] += z_m^2 elementwise.
-// lzv holds Lz[m] at dims 8g..8g+7 (lzv[0..7]) and 32+8g.. (lzv[8..15]); c_m = L00 for m = 0.
+// lzv holds Lz[m] at dims 8g..8g+7 (lzv[0..7]) and 32+8g.. (lzv[8..15]), qv the query at the
+// same dims; c_m = L00 for m = 0.
 template <typename T, int NQT, int QS>
-__device__ inline void oal_z_step(const float (&lzv)[16], float cm, const T *qrow, const T *s_k, int g,
+__device__ inline void oal_z_step(const float (&lzv)[16], float cm, const float (&qv)[16], const T *s_k, int g,
                                   int lr, int qt, oal_f32x4 (&kap)[NQT]) {
     constexpr int EPU = 16 / (int)sizeof(T);
     OalFrag<T> bq[2];
@@ -407,7 +372,7 @@ __device__ inline void oal_z_step(const float (&lzv)[16], float cm, const T *qro
     for (int hh = 0; hh < 2; ++hh) {
         float x[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) x[e] = lzv[8 * hh + e] * (float)qrow[32 * hh + 8 * g + e];
+        for (int e = 0; e < 8; ++e) x[e] = lzv[8 * hh + e] * qv[8 * hh + e];
         bq[hh].set(x);
     }
     const oal_f32x4 cinit = oal_splat(cm);
@@ -431,6 +396,241 @@ __device__ inline void oal_z_step(const float (&lzv)[16], float cm, const T *qro
     }
 }
 
+constexpr int kIntraLzr = 8;          // Lz rows m < 8 staged in LDS ...
+constexpr int kIntraLzHeads = 16;     // ... for the first 16 query heads of a KV head
+constexpr int kFragFloats = 5 * 4 * 64;   // one 16 x 80 accumulator tile, fragment order
+
+template <typename T, int C> struct IntraLayout {
+    static constexpr int EPU = 16 / (int)sizeof(T);
+    static constexpr int QS = OAL_D + EPU;      // key row in LDS (16-byte aligned)
+    static constexpr int LDV = C + EPU;         // V^T row
+    static constexpr int O_K = 0;                                             // T [C][QS]
+    static constexpr int O_VT = O_K + C * QS * (int)sizeof(T);                // T [64][LDV]
+    static constexpr int O_LZ = O_VT + OAL_D * LDV * (int)sizeof(T);          // f32 [n_rep][8][64]
+    static size_t bytes(int n_rep) { return (size_t)O_LZ + (size_t)n_rep * kIntraLzr * OAL_D * 4; }
+    static_assert(O_VT % 16 == 0 && O_LZ % 16 == 0, "alignment");
+};
+
+// ------------------------------------------------------------------------------------
+// 3. intra-chunk kernel sum
+// Workgroup = (chunk x 16-query tile, sequence x KV head), 8 waves, wave w takes the query
+// heads w, w + 8, ... of the KV head. Per head: kappa = eps + sum_m z_m^2 over the chunk's
+// key tiles (z_m^T tiles on MFMA, every key tile of the chunk computed and the causal mask
+// applied after, so the tiles form independent MFMA chains), then kappa [V;1] on MFMA (keys
+// in a permuted order on both operands). The unnormalised 16 x 65 result goes to uintra in
+// accumulator-fragment order; the readout adds it before the divide.
+constexpr int kIntraWaves = 8;
+template <typename T, int C>
+__global__ __launch_bounds__(64 * kIntraWaves) __attribute__((amdgpu_waves_per_eu(4))) void oal_intra(int T_len, int n_q_heads, int n_kv_heads, int nchunks, int n_bkv,
+                                                               const T *__restrict__ q, const T *__restrict__ k,
+                                                               const T *__restrict__ v, const unsigned char *__restrict__ params,
+                                                               float *__restrict__ uintra) {
+    using Lay = IntraLayout<T, C>;
+    constexpr int EPU = Lay::EPU, QS = Lay::QS, LDV = Lay::LDV;
+    constexpr int NQT = C / 16;
+    constexpr int UPQ = OAL_D / EPU;
+    constexpr int NTH = 64 * kIntraWaves;
+    extern __shared__ __align__(16) unsigned char smem[];
+    T *s_k = reinterpret_cast<T *>(smem + Lay::O_K);
+    T *s_vT = reinterpret_cast<T *>(smem + Lay::O_VT);
+    float *s_lz = reinterpret_cast<float *>(smem + Lay::O_LZ);
+
+    // XCD-aware placement: the NQT tiles of one (chunk, sequence x KV head) get block ids
+    // congruent mod 8, i.e. the same XCD, so its K and V are fetched into one L2
+    const int Lb = blockIdx.x, xcd = Lb % kXcds, i8 = Lb / kXcds;
+    const int unit = xcd + kXcds * (i8 / NQT), qt = i8 % NQT;
+    if (unit >= nchunks * n_bkv) return;
+    const int c = unit % nchunks, bkv = unit / nchunks;
+    const int b = bkv / n_kv_heads, kv = bkv % n_kv_heads;
+    const int n_rep = n_q_heads / n_kv_heads, h0 = kv * n_rep;
+    const int pos0 = c * C + qt * 16;
+    if (pos0 >= T_len) return;
+    const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+    const int g = lane >> 4, lr = lane & 15;
+    const int qpos = pos0 + lr;
+
+    // this wave's first head's query (row lr of the tile, dims 8g.. and 32 + 8g..), fetched
+    // before the staging
+    auto load_q = [&](int i, OalFrag<T> (&qf)[2]) {
+        const T *qr = q + (((size_t)b * n_q_heads + h0 + i) * T_len + (qpos < T_len ? qpos : 0)) * OAL_D + 8 * g;
+        qf[0].load(qr);
+        qf[1].load(qr + 32);
+    };
+    OalFrag<T> qf[2];
+    if (wave < n_rep) load_q(wave, qf);
+
+    // stage every key of the chunk (zero past T), V^T of them, and Lz rows of every head;
+    // all loads are issued before the first LDS write
+    {
+        constexpr int NKU = C * UPQ;                      // 16-byte units of K (and of V)
+        constexpr int NKJ = (NKU + NTH - 1) / NTH;
+        constexpr int NLJ = (kIntraLzHeads * kIntraLzr * OAL_D / 4 + NTH - 1) / NTH;
+        const T *kb = k + (size_t)bkv * T_len * OAL_D;
+        const T *vb = v + (size_t)bkv * T_len * OAL_D;
+        const int nlz = min(n_rep, kIntraLzHeads) * kIntraLzr * OAL_D / 4;
+        oal_u32x4 rk[NKJ], rv[NKJ];
+        float4 rl[NLJ];
+#pragma unroll
+        for (int j = 0; j < NKJ; ++j) {
+            const int u = tid + NTH * j, key = u % C, a = u / C, pos = c * C + key;
+            const bool ok = u < NKU && pos < T_len;
+            rk[j] = ok ? *reinterpret_cast<const oal_u32x4 *>(kb + (size_t)pos * OAL_D + a * EPU) : zero16();
+            rv[j] = ok ? *reinterpret_cast<const oal_u32x4 *>(vb + (size_t)pos * OAL_D + a * EPU) : zero16();
+        }
+#pragma unroll
+        for (int j = 0; j < NLJ; ++j) {
+            const int u = tid + NTH * j;
+            const int i = u / (kIntraLzr * OAL_D / 4), w = u % (kIntraLzr * OAL_D / 4);
+            rl[j] = u < nlz ? reinterpret_cast<const float4 *>(head_ptr(params, h0 + i)->Lz)[w]
+                            : make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+#pragma unroll
+        for (int j = 0; j < NKJ; ++j) {
+            const int u = tid + NTH * j, key = u % C, a = u / C;
+            if (u < NKU) {
+                *reinterpret_cast<oal_u32x4 *>(s_k + key * QS + a * EPU) = rk[j];
+                const T *el = reinterpret_cast<const T *>(&rv[j]);
+#pragma unroll
+                for (int e = 0; e < EPU; ++e) s_vT[(a * EPU + e) * LDV + key] = el[e];
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < NLJ; ++j) {
+            const int u = tid + NTH * j;
+            if (u < nlz) reinterpret_cast<float4 *>(s_lz)[u] = rl[j];
+        }
+    }
+    __syncthreads();
+
+    OalFrag<T> ones, zeros;
+    {
+        float o[8], zz[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) { o[e] = 1.0f; zz[e] = 0.0f; }
+        ones.set(o);
+        zeros.set(zz);
+    }
+    const int ntiles = nchunks * NQT;
+    for (int i = wave; i < n_rep; i += kIntraWaves) {
+        if (i != wave) load_q(i, qf);
+        const OalHeadDev *hd = head_ptr(params, h0 + i);
+        const int G = hd->G;
+        const float eps = hd->eps, L00 = hd->L00;
+        float qv[16];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            qv[e] = qpos < T_len ? (float)qf[0].v[e] : 0.0f;
+            qv[8 + e] = qpos < T_len ? (float)qf[1].v[e] : 0.0f;
+        }
+        oal_f32x4 kap[NQT];
+#pragma unroll
+        for (int kt = 0; kt < NQT; ++kt) kap[kt] = oal_splat(eps);
+        for (int m = 0; m <= G; ++m) {
+            float lzv[16];
+            if (G < kIntraLzr && i < kIntraLzHeads) {
+                const float *p = s_lz + (i * kIntraLzr + m) * OAL_D + 8 * g;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) { lzv[e] = p[e]; lzv[8 + e] = p[32 + e]; }
+            } else {
+                const float *p = hd->Lz + m * OAL_D + 8 * g;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) { lzv[e] = p[e]; lzv[8 + e] = p[32 + e]; }
+            }
+            // z_m^T (16 keys x 16 queries) = K_kt . (Lz[m] o q)^T + c_m for every key tile
+            OalFrag<T> bq[2];
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh) {
+                float x[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) x[e] = lzv[8 * hh + e] * qv[8 * hh + e];
+                bq[hh].set(x);
+            }
+            const oal_f32x4 cinit = oal_splat(m == 0 ? L00 : 0.0f);
+            // key tiles are re-read from LDS for every z term (an opaque offset keeps the
+            // compiler from holding all of them in registers)
+            int koff = (lr * QS + 8 * g) * (int)sizeof(T);
+            asm volatile("" : "+v"(koff));
+#pragma unroll
+            for (int kt = 0; kt < NQT; ++kt) {
+                const T *kr = reinterpret_cast<const T *>(reinterpret_cast<const unsigned char *>(s_k) + koff) + 16 * kt * QS;
+                OalFrag<T> ak[2];
+                if (EPU == 8) {
+                    ak[0].load(kr);
+                    ak[1].load(kr + 32);
+                } else {
+                    ak[0].load4x2(kr, kr + 4);
+                    ak[1].load4x2(kr + 32, kr + 36);
+                }
+                // the two halves of the 64 dims as independent MFMAs, added after
+                const oal_f32x4 za = oal_mma(ak[0], bq[0], cinit);
+                const oal_f32x4 zb = oal_mma(ak[1], bq[1], oal_splat(0.0f));
+#pragma unroll
+                for (int ii = 0; ii < 4; ++ii) {
+                    const float zz = za[ii] + zb[ii];
+                    kap[kt][ii] += zz * zz;
+                }
+            }
+        }
+        // causal mask (key <= query, key < T), then kappa [V;1]
+#pragma unroll
+        for (int kt = 0; kt < NQT; ++kt)
+#pragma unroll
+            for (int ii = 0; ii < 4; ++ii) {
+                const int kp = c * C + 16 * kt + 4 * g + ii;
+                if (!(kp <= qpos && kp < T_len)) kap[kt][ii] = 0.0f;
+            }
+        oal_f32x4 acc[5];
+#pragma unroll
+        for (int n = 0; n < 5; ++n) acc[n] = oal_splat(0.0f);
+#pragma unroll
+        for (int p = 0; p < C / 32; ++p) {
+            float x[8];
+#pragma unroll
+            for (int ii = 0; ii < 4; ++ii) {
+                x[ii] = kap[2 * p][ii];
+                x[4 + ii] = kap[2 * p + 1][ii];
+            }
+            OalFrag<T> a;
+            a.set(x);
+#pragma unroll
+            for (int n = 0; n < 4; ++n) {
+                const T *vr = s_vT + (16 * n + lr) * LDV + 32 * p + 4 * g;
+                OalFrag<T> bv;
+                bv.load4x2(vr, vr + 16);
+                acc[n] = oal_mma(a, bv, acc[n]);
+            }
+            acc[4] = oal_mma(a, lr == 0 ? ones : zeros, acc[4]);
+        }
+        float *up = uintra + (((size_t)b * n_q_heads + h0 + i) * ntiles + c * NQT + qt) * kFragFloats + lane;
+#pragma unroll
+        for (int n = 0; n < 5; ++n)
+#pragma unroll
+            for (int ii = 0; ii < 4; ++ii) up[(n * 4 + ii) * 64] = acc[n][ii];
+    }
+}
+
+// ------------------------------------------------------------------------------------
+// 4. readout
+template <typename T, int C, int R> struct ReadoutLayout {
+    static constexpr int EPU = 16 / (int)sizeof(T);
+    static constexpr int RW = (R + 1) / 2;      // heads of one wave pair (head subset)
+    static constexpr int QS = OAL_D + EPU;      // q row in LDS (16-byte aligned)
+    static constexpr int PS = OAL_D + 4;        // fp32 p-table row
+    // Byte offsets. The "union" region holds the fp32 p table during the inter-chunk loop,
+    // then the combine buffer.
+    static constexpr int P_BYTES = R * 16 * PS * 4;
+    static constexpr int X_BYTES = R * 5 * 4 * 64 * 4;
+    static constexpr int U_BYTES = P_BYTES > X_BYTES ? P_BYTES : X_BYTES;
+    static constexpr int O_U = 0;
+    static constexpr int O_Q = O_U + U_BYTES;                                 // T [R*16][QS], col 64 = 1
+    static constexpr int O_TAIL = O_Q + R * 16 * QS * (int)sizeof(T);        // f32 [R][TAIL_PAIRS]
+    static constexpr int O_PAIR = O_TAIL + R * OAL_TAIL_PAIRS * 4;            // u8 [2][TAIL_PAIRS]
+    static constexpr int BYTES = O_PAIR + 2 * OAL_TAIL_PAIRS;
+    static constexpr int META_UNITS = OAL_TAIL_PAIRS / 4;                    // 16-byte units / head
+    static constexpr int PAIR_UNITS = 2 * OAL_TAIL_PAIRS / 16;
+    static_assert(U_BYTES % 16 == 0 && O_Q % 16 == 0 && O_TAIL % 16 == 0 && O_PAIR % 16 == 0, "alignment");
+};
+
 // Workgroup = (sequence x KV head x head group of R heads, chunk, 16-query tile), 4 waves:
 // wave = (head subset hs, K-step parity par). Subset 0 holds heads 0..RW-1, subset 1 the
 // rest; the two waves of a subset split the K-steps by the parity of rq (and of the tail
@@ -438,23 +638,19 @@ __device__ inline void oal_z_step(const float (&lzv)[16], float cm, const T *qro
 // from L2/L1 and used for all their heads.
 template <typename T, int C, int R>
 __global__ __launch_bounds__(256, 2) void oal_readout(
-    int T_len, int Tpad, int n_q_heads, int n_kv_heads, int nchunks, int n_hgroups, int nunits,
-    const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ vT,
-    const unsigned char *__restrict__ params, const unsigned char *__restrict__ snap,
-    float *__restrict__ y) {
+    int T_len, int n_q_heads, int n_kv_heads, int nchunks, int n_hgroups, int nunits,
+    const T *__restrict__ q, const unsigned char *__restrict__ params,
+    const unsigned char *__restrict__ snap, const float *__restrict__ uintra, float *__restrict__ y) {
     using Lay = ReadoutLayout<T, C, R>;
-    constexpr int EPU = Lay::EPU, QS = Lay::QS, LDV = Lay::LDV, PS = Lay::PS, RW = Lay::RW;
+    constexpr int EPU = Lay::EPU, QS = Lay::QS, PS = Lay::PS, RW = Lay::RW;
     constexpr int NQT = C / 16;
     constexpr int UPQ = OAL_D / EPU;            // 16-byte units per q/k row
     constexpr int NMAIN = OAL_KSTEPS / 2;       // main K-steps per parity
     extern __shared__ __align__(16) unsigned char smem[];
     float *s_p = reinterpret_cast<float *>(smem + Lay::O_U);               // inter: [R*16][PS]
-    T *s_k = reinterpret_cast<T *>(smem + Lay::O_U);                       // intra: [C][QS]
-    T *s_vT = s_k + C * QS;                                                // intra: [64][LDV]
     float *s_x = reinterpret_cast<float *>(smem + Lay::O_U);               // combine
     T *s_q = reinterpret_cast<T *>(smem + Lay::O_Q);
     float *s_tail = reinterpret_cast<float *>(smem + Lay::O_TAIL);
-    float *s_lz = reinterpret_cast<float *>(smem + Lay::O_LZ);
     unsigned char *s_pair = smem + Lay::O_PAIR;
 
     // XCD-aware placement: the NQT workgroups of one unit (chunk, KV head, head group)
@@ -495,17 +691,12 @@ __global__ __launch_bounds__(256, 2) void oal_readout(
                                                : reinterpret_cast<const oal_u32x4 *>(kvd->rb) + (w - OAL_TAIL_PAIRS / 16);
             }
             const OalHeadDev *hd = head_ptr(params, h0 + u / Lay::META_UNITS);
-            int w = u % Lay::META_UNITS;
-            if (w < OAL_TAIL_PAIRS / 4) return reinterpret_cast<const oal_u32x4 *>(hd->tail) + w;
-            w -= OAL_TAIL_PAIRS / 4;
-            return reinterpret_cast<const oal_u32x4 *>(hd->Lz) + w;
+            return reinterpret_cast<const oal_u32x4 *>(hd->tail) + u % Lay::META_UNITS;
         };
         auto meta_dst = [&](int u) -> oal_u32x4 * {
             if (u >= R * Lay::META_UNITS) return reinterpret_cast<oal_u32x4 *>(s_pair) + (u - R * Lay::META_UNITS);
             int i = u / Lay::META_UNITS, w = u % Lay::META_UNITS;
-            if (w < OAL_TAIL_PAIRS / 4) return reinterpret_cast<oal_u32x4 *>(s_tail + i * OAL_TAIL_PAIRS) + w;
-            w -= OAL_TAIL_PAIRS / 4;
-            return reinterpret_cast<oal_u32x4 *>(s_lz + i * Lay::LZR * OAL_D) + w;
+            return reinterpret_cast<oal_u32x4 *>(s_tail + i * OAL_TAIL_PAIRS) + w;
         };
 #pragma unroll
         for (int j = 0; j < NQJ; ++j) {
@@ -691,111 +882,7 @@ __global__ __launch_bounds__(256, 2) void oal_readout(
         else inter(RBc{}, std::false_type{});
     }
 
-    // 3. stage K and V^T of the keys this tile can see into the region the p table used
-    {
-        const int nkeys = ((qt + 2) / 2) * 32;   // rounded to 32 (<= C)
-        const int nku = nkeys * UPQ, nvu = OAL_D * (nkeys / EPU);
-        constexpr int NKJ = (C * UPQ + 255) / 256, NVJ = (OAL_D * (C / EPU) + 255) / 256;
-        const T *kb = k + (size_t)bkv * T_len * OAL_D;
-        const T *vTb = vT + (size_t)bkv * OAL_D * Tpad + (size_t)c * C;
-        oal_u32x4 rk[NKJ], rv[NVJ];
-#pragma unroll
-        for (int j = 0; j < NKJ; ++j) {
-            int u = tid + 256 * j, key = u / UPQ, a = u % UPQ, pos = c * C + key;
-            rk[j] = (u < nku && pos < T_len) ? *reinterpret_cast<const oal_u32x4 *>(kb + (size_t)pos * OAL_D + a * EPU) : zero16();
-        }
-#pragma unroll
-        for (int j = 0; j < NVJ; ++j) {
-            int u = tid + 256 * j, row = u / (nkeys / EPU), cu = u % (nkeys / EPU);
-            rv[j] = u < nvu ? *reinterpret_cast<const oal_u32x4 *>(vTb + (size_t)row * Tpad + cu * EPU) : zero16();
-        }
-        __syncthreads();    // every wave is done with the p table
-#pragma unroll
-        for (int j = 0; j < NKJ; ++j) {
-            int u = tid + 256 * j, key = u / UPQ, a = u % UPQ;
-            if (u < nku) *reinterpret_cast<oal_u32x4 *>(s_k + key * QS + a * EPU) = rk[j];
-        }
-#pragma unroll
-        for (int j = 0; j < NVJ; ++j) {
-            int u = tid + 256 * j, row = u / (nkeys / EPU), cu = u % (nkeys / EPU);
-            if (u < nvu) *reinterpret_cast<oal_u32x4 *>(s_vT + row * LDV + cu * EPU) = rv[j];
-        }
-        __syncthreads();
-    }
-
-    // 4. intra-chunk: kappa = eps + sum_m z_m^2 with z_m = L00 [m==0] + sum_r Lz[m][r] q_r k_r,
-    //    z_m^T tiles (16 keys x 16 queries) on MFMA, then kappa [V;1] on MFMA. Local head li
-    //    of a subset is done by the subset's wave with parity li & 1.
-    OalFrag<T> ones, zeros;
-    {
-        float o[8], zz[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) { o[e] = 1.0f; zz[e] = 0.0f; }
-        ones.set(o);
-        zeros.set(zz);
-    }
-#pragma unroll
-    for (int li = 0; li < RW; ++li) {
-        if (li >= nh || (li & 1) != par) continue;
-        const int i = hb + li;
-        const OalHeadDev *hd = head_ptr(params, h0 + i);
-        const T *qrow = s_q + (i * 16 + lr) * QS;
-        oal_f32x4 kap[NQT];
-        const float eps = hd->eps, L00 = hd->L00;
-#pragma unroll
-        for (int kt = 0; kt < NQT; ++kt) kap[kt] = oal_splat(eps);
-        const int G = hd->G;
-        // Lz rows come from LDS when the head has fewer than LZR groups, else from the blob
-        if (G < Lay::LZR) {
-            for (int m = 0; m <= G; ++m) {
-                const float *p = s_lz + (i * Lay::LZR + m) * OAL_D + 8 * g;
-                float lzv[16];
-#pragma unroll
-                for (int e = 0; e < 8; ++e) { lzv[e] = p[e]; lzv[8 + e] = p[32 + e]; }
-                oal_z_step<T, NQT, QS>(lzv, m == 0 ? L00 : 0.0f, qrow, s_k, g, lr, qt, kap);
-            }
-        } else {
-            for (int m = 0; m <= G; ++m) {
-                const float *p = hd->Lz + m * OAL_D + 8 * g;
-                float lzv[16];
-#pragma unroll
-                for (int e = 0; e < 8; ++e) { lzv[e] = p[e]; lzv[8 + e] = p[32 + e]; }
-                oal_z_step<T, NQT, QS>(lzv, m == 0 ? L00 : 0.0f, qrow, s_k, g, lr, qt, kap);
-            }
-        }
-        // causal mask (key <= query, key < T), then kappa [V;1]
-        const int qpos = pos0 + lr;
-#pragma unroll
-        for (int kt = 0; kt < NQT; ++kt)
-#pragma unroll
-            for (int ii = 0; ii < 4; ++ii) {
-                int kp = c * C + 16 * kt + 4 * g + ii;
-                if (!(kt <= qt && kp <= qpos && kp < T_len)) kap[kt][ii] = 0.0f;
-            }
-#pragma unroll
-        for (int p = 0; p < C / 32; ++p) {
-            if (2 * p <= qt) {
-                float x[8];
-#pragma unroll
-                for (int ii = 0; ii < 4; ++ii) {
-                    x[ii] = kap[2 * p][ii];
-                    x[4 + ii] = kap[2 * p + 1][ii];
-                }
-                OalFrag<T> a;
-                a.set(x);
-#pragma unroll
-                for (int n = 0; n < 4; ++n) {
-                    const T *vr = s_vT + (16 * n + lr) * LDV + 32 * p + 4 * g;
-                    OalFrag<T> bv;
-                    bv.load4x2(vr, vr + 16);
-                    acc[li][n] = oal_mma(a, bv, acc[li][n]);
-                }
-                acc[li][4] = oal_mma(a, lr == 0 ? ones : zeros, acc[li][4]);
-            }
-        }
-    }
-
-    // 5. combine the two parities' partial sums and divide
+    // 2. combine the two parities' partial sums and the intra-chunk sum, and divide
     __syncthreads();
 #pragma unroll
     for (int li = 0; li < RW; ++li)
@@ -805,14 +892,16 @@ __global__ __launch_bounds__(256, 2) void oal_readout(
 #pragma unroll
                 for (int ii = 0; ii < 4; ++ii) s_x[(((hb + li) * 5 + n) * 4 + ii) * 64 + lane] = acc[li][n][ii];
     __syncthreads();
+    const int ntiles = nchunks * NQT;
 #pragma unroll
     for (int li = 0; li < RW; ++li) {
         if (li >= nh || (li & 1) != par) continue;
         const int i = hb + li;
+        const float *up = uintra + (((size_t)b * n_q_heads + h0 + i) * ntiles + c * NQT + qt) * kFragFloats + lane;
 #pragma unroll
         for (int n = 0; n < 5; ++n)
 #pragma unroll
-            for (int ii = 0; ii < 4; ++ii) acc[li][n][ii] += s_x[((i * 5 + n) * 4 + ii) * 64 + lane];
+            for (int ii = 0; ii < 4; ++ii) acc[li][n][ii] += s_x[((i * 5 + n) * 4 + ii) * 64 + lane] + up[(n * 4 + ii) * 64];
         float *yh = y + ((size_t)b * n_q_heads + h0 + i) * T_len * OAL_D;
 #pragma unroll
         for (int ii = 0; ii < 4; ++ii) {
@@ -837,7 +926,7 @@ size_t readout_lds() { return (size_t)ReadoutLayout<T, C, R>::BYTES; }
 
 struct PrefillPlan {
     int nchunks, Tpad;
-    size_t snap_bytes, delta_bytes, tinit_bytes, vt_bytes;
+    size_t snap_bytes, delta_bytes, tinit_bytes, uintra_bytes;
 };
 
 template <typename T>
@@ -850,14 +939,14 @@ PrefillPlan make_plan(const oal_dims &d, int T_len, int C) {
     p.snap_bytes = r256(bkv * p.nchunks * OAL_SNAP_KSTEPS * (size_t)snap_kstep_bytes<T>());
     p.delta_bytes = r256(bkv * p.nchunks * OAL_SNAP_KSTEPS * (size_t)kDeltaStep * sizeof(float));
     p.tinit_bytes = r256(bkv * OAL_TAIL_STEPS * (size_t)kDeltaStep * sizeof(float));
-    p.vt_bytes = r256(bkv * OAL_D * (size_t)p.Tpad * sizeof(T));
+    p.uintra_bytes = r256((size_t)d.batch * d.n_q_heads * (p.Tpad / 16) * (size_t)kFragFloats * sizeof(float));
     return p;
 }
 
 template <typename T, int C, int R>
 hipError_t launch_readout(const oal_dims &d, int T_len, const PrefillPlan &p, const void *q,
-                          const void *k, const T *vT, const void *params,
-                          const unsigned char *snap, float *y, hipStream_t stream) {
+                          const void *params, const unsigned char *snap, const float *uintra, float *y,
+                          hipStream_t stream) {
     int n_rep = d.n_q_heads / d.n_kv_heads;
     int n_hg = n_rep / R;
     size_t lds = readout_lds<T, C, R>();
@@ -867,10 +956,9 @@ hipError_t launch_readout(const oal_dims &d, int T_len, const PrefillPlan &p, co
     if (e != hipSuccess) return e;
     int nunits = p.nchunks * d.batch * d.n_kv_heads * n_hg;
     int nblocks = kXcds * (C / 16) * ((nunits + kXcds - 1) / kXcds);
-    hipLaunchKernelGGL(kern, dim3(nblocks), dim3(256), lds, stream, T_len, p.Tpad, d.n_q_heads,
-                       d.n_kv_heads, p.nchunks, n_hg, nunits, reinterpret_cast<const T *>(q),
-                       reinterpret_cast<const T *>(k), vT,
-                       reinterpret_cast<const unsigned char *>(params), snap, y);
+    hipLaunchKernelGGL(kern, dim3(nblocks), dim3(256), lds, stream, T_len, d.n_q_heads, d.n_kv_heads,
+                       p.nchunks, n_hg, nunits, reinterpret_cast<const T *>(q),
+                       reinterpret_cast<const unsigned char *>(params), snap, uintra, y);
     return hipGetLastError();
 }
 
@@ -882,11 +970,25 @@ hipError_t launch_all(const oal_dims &d, int T_len, const void *q, const void *k
     unsigned char *snap = reinterpret_cast<unsigned char *>(ws);
     float *delta = reinterpret_cast<float *>(snap + p.snap_bytes);
     float *tinit = reinterpret_cast<float *>(snap + p.snap_bytes + p.delta_bytes);
-    T *vT = reinterpret_cast<T *>(snap + p.snap_bytes + p.delta_bytes + p.tinit_bytes);
+    float *uintra = reinterpret_cast<float *>(snap + p.snap_bytes + p.delta_bytes + p.tinit_bytes);
     const int bkv = d.batch * d.n_kv_heads;
     const unsigned char *pb = reinterpret_cast<const unsigned char *>(params);
     hipError_t e;
     if (marks && (e = hipEventRecord(marks[0], stream)) != hipSuccess) return e;
+    if (y) {   // intra-chunk sums: independent of the state scan
+        using IL = IntraLayout<T, C>;
+        const size_t lds = IL::bytes(std::min(d.n_q_heads / d.n_kv_heads, kIntraLzHeads));
+        auto kern = oal_intra<T, C>;
+        if ((e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds)) != hipSuccess)
+            return e;
+        const int nunits = p.nchunks * bkv;
+        const int nblocks = kXcds * (C / 16) * ((nunits + kXcds - 1) / kXcds);
+        hipLaunchKernelGGL(kern, dim3(nblocks), dim3(64 * kIntraWaves), lds, stream, T_len,
+                           d.n_q_heads, d.n_kv_heads, p.nchunks, bkv, reinterpret_cast<const T *>(q),
+                           reinterpret_cast<const T *>(k), reinterpret_cast<const T *>(v), pb, uintra);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
     {
         auto kern = oal_scan_delta<T, C>;
         size_t lds = scan_lds<T, C>();
@@ -894,8 +996,8 @@ hipError_t launch_all(const oal_dims &d, int T_len, const void *q, const void *k
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds)) != hipSuccess)
             return e;
         hipLaunchKernelGGL(kern, dim3(kScanBlocks + 1, p.nchunks, bkv), dim3(64 * kScanWaves), lds, stream,
-                           T_len, p.Tpad, p.nchunks, d.n_q_heads, d.n_kv_heads, reinterpret_cast<const T *>(k),
-                           reinterpret_cast<const T *>(v), pb, state, delta, tinit, vT);
+                           T_len, p.nchunks, d.n_q_heads, d.n_kv_heads, reinterpret_cast<const T *>(k),
+                           reinterpret_cast<const T *>(v), pb, state, delta, tinit);
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
     {
@@ -911,15 +1013,15 @@ hipError_t launch_all(const oal_dims &d, int T_len, const void *q, const void *k
     int n_rep = d.n_q_heads / d.n_kv_heads;
     auto fits = [](size_t bytes) { return bytes <= (size_t)kMaxLds; };
     if (n_rep % 8 == 0 && fits(readout_lds<T, C, 8>()))
-        e = launch_readout<T, C, 8>(d, T_len, p, q, k, vT, params, snap, y, stream);
+        e = launch_readout<T, C, 8>(d, T_len, p, q, params, snap, uintra, y, stream);
     else if (n_rep % 7 == 0 && fits(readout_lds<T, C, 7>()))
-        e = launch_readout<T, C, 7>(d, T_len, p, q, k, vT, params, snap, y, stream);
+        e = launch_readout<T, C, 7>(d, T_len, p, q, params, snap, uintra, y, stream);
     else if (n_rep % 4 == 0 && fits(readout_lds<T, C, 4>()))
-        e = launch_readout<T, C, 4>(d, T_len, p, q, k, vT, params, snap, y, stream);
+        e = launch_readout<T, C, 4>(d, T_len, p, q, params, snap, uintra, y, stream);
     else if (n_rep % 2 == 0 && fits(readout_lds<T, C, 2>()))
-        e = launch_readout<T, C, 2>(d, T_len, p, q, k, vT, params, snap, y, stream);
+        e = launch_readout<T, C, 2>(d, T_len, p, q, params, snap, uintra, y, stream);
     else
-        e = launch_readout<T, C, 1>(d, T_len, p, q, k, vT, params, snap, y, stream);
+        e = launch_readout<T, C, 1>(d, T_len, p, q, params, snap, uintra, y, stream);
     if (e == hipSuccess && marks) e = hipEventRecord(marks[2], stream);
     return e;
 }
@@ -928,7 +1030,7 @@ hipError_t launch_all(const oal_dims &d, int T_len, const void *q, const void *k
 
 size_t oal_prefill_ws_bytes_impl(const oal_dims &d, int T_len, int C) {
     PrefillPlan p = d.dtype == OAL_BF16 ? make_plan<__bf16>(d, T_len, C) : make_plan<float>(d, T_len, C);
-    return p.snap_bytes + p.delta_bytes + p.tinit_bytes + p.vt_bytes;
+    return p.snap_bytes + p.delta_bytes + p.tinit_bytes + p.uintra_bytes;
 }
 
 hipError_t oal_launch_prefill(const oal_dims &d, int T_len, int C, const void *q, const void *k,
