@@ -17,6 +17,7 @@ LIB_PATH = os.path.join(_PKG, "liboal.so")
 
 OAL_F32, OAL_BF16 = 0, 1
 NFEAT, V1, D = 2145, 65, 64
+STATE_STRIDE = 139456          # floats per (sequence, KV head) block of the state buffer
 STATUS = {0: "OAL_OK", 1: "OAL_E_ARG", 2: "OAL_E_SHAPE", 3: "OAL_E_DTYPE", 4: "OAL_E_ALIGN",
           5: "OAL_E_UNSUPPORTED", 6: "OAL_E_HIP"}
 EXPORTED = ("oal_params_bytes", "oal_state_bytes", "oal_prefill_workspace_bytes",
@@ -185,6 +186,11 @@ def oal_decode_step(dims: oal_dims, q, k, v, params_dev, state_dev, workspace, y
 
 
 # ---- buffer helper (torch allocations sized by the library) ------------------------------
+
+def state_view(state, batch: int, n_kv_heads: int):
+    """[batch, n_kv_heads, 2145, 65] view of a state buffer (drops each block's padding)."""
+    return state.view(batch, n_kv_heads, STATE_STRIDE)[:, :, : NFEAT * V1].reshape(batch, n_kv_heads, NFEAT, V1)
+
 
 def alloc_buffers(dims: oal_dims, T: int = 0, chunk: int = 128, device: str = "cuda"):
     """Allocate params, state, prefill workspace and a zeroed decode workspace (uint8/fp32 tensors)."""

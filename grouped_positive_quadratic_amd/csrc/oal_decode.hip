@@ -88,7 +88,7 @@ __global__ __launch_bounds__(kThreads) void oal_decode_kernel(
     }
     __syncthreads();
 
-    float *S = state + (size_t)bkv * OAL_NFEAT * OAL_V1;
+    float *S = state + (size_t)bkv * OAL_STATE_STRIDE;
     const float vv = oal_ld(v + (size_t)bkv * OAL_D + lane);
     float acc[MAXH], accd[MAXH];
 #pragma unroll

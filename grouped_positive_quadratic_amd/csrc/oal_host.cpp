@@ -164,7 +164,7 @@ size_t oal_params_bytes(const oal_dims *d) {
 
 size_t oal_state_bytes(const oal_dims *d) {
     if (check_dims(d) != OAL_OK) return 0;
-    return (size_t)d->batch * d->n_kv_heads * OAL_NFEAT * OAL_V1 * sizeof(float);
+    return (size_t)d->batch * d->n_kv_heads * OAL_STATE_STRIDE * sizeof(float);
 }
 
 size_t oal_prefill_workspace_bytes(const oal_dims *d, int32_t T, int32_t chunk) {

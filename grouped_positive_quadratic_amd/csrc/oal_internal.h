@@ -22,6 +22,8 @@
 
 #include <stdint.h>
 
+#include "oal.h"
+
 #define OAL_D 64
 #define OAL_V1 65
 #define OAL_NFEAT 2145
@@ -33,6 +35,7 @@
 #define OAL_SNAP_KSTEPS (OAL_KSTEPS + OAL_TAIL_STEPS)
 #define OAL_PARAMS_MAGIC 0x314C414Fu  // "OAL1"
 #define OAL_MAX_G 64
+static_assert(OAL_STATE_STRIDE % 64 == 0 && OAL_STATE_STRIDE >= OAL_NFEAT * OAL_V1, "state block stride");
 
 #if defined(__HIPCC__)
 #define OAL_HD __host__ __device__

@@ -268,7 +268,7 @@ __global__ __launch_bounds__(64 * kScanWaves) void oal_scan_delta(
     if (s >= OAL_KSTEPS && c == 0) {
         // incoming state of the tail slots, read here because the prefix kernel overwrites
         // the state rows (some of which the tail pairs repeat) while other threads read
-        const float *Sst = state + (size_t)bkv * OAL_NFEAT * OAL_V1;
+        const float *Sst = state + (size_t)bkv * OAL_STATE_STRIDE;
 #pragma unroll
         for (int h = 0; h < 2; ++h)
 #pragma unroll
@@ -311,7 +311,7 @@ __global__ __launch_bounds__(256) void oal_scan_prefix(int nchunks, int n_q_head
 
     // incoming state: main slots read the rows they own (and later overwrite); tail slots
     // take the copy the increment kernel made
-    float *Sst = state + (size_t)bkv * OAL_NFEAT * OAL_V1;
+    float *Sst = state + (size_t)bkv * OAL_STATE_STRIDE;
     float S[8];
     if (s < OAL_KSTEPS) {
 #pragma unroll

@@ -20,10 +20,13 @@
  *   q      [batch, n_q_heads,  T, 64]  dtype of oal_dims.dtype
  *   k, v   [batch, n_kv_heads, T, 64]
  *   y      [batch, n_q_heads,  T, 64]  fp32
- *   state  [batch, n_kv_heads, 2145, 65] fp32: the prefix states of each (sequence, KV head).
- *          Row 0 = H0; rows 1..64 = H1_r (r = 0..63); rows 65.. = H2_rt for r <= t in
- *          row-major order of the upper triangle (the symmetric H2 stored once, r < t not
- *          doubled). Columns 0..63 = components of v, column 64 = the "1" of [v;1].
+ *   state  [batch, n_kv_heads] blocks of OAL_STATE_STRIDE (139456) fp32, one per (sequence,
+ *          KV head), 256-byte aligned: the block's first 2145 * 65 floats are the prefix
+ *          state, a [2145, 65] row-major matrix, the last 31 floats are padding (zero after
+ *          oal_state_init; the kernels keep them finite). Row 0 = H0; rows 1..64 = H1_r
+ *          (r = 0..63); rows 65.. = H2_rt for r <= t in row-major order of the upper triangle
+ *          (the symmetric H2 stored once, r < t not doubled). Columns 0..63 = components of
+ *          v, column 64 = the "1" of [v;1].
  *   For a decode step T = 1 and the T axis is dropped: q [batch, n_q_heads, 64] etc.
  *
  * Ownership: the caller allocates and owns every device buffer (params, state, workspace,
@@ -89,7 +92,10 @@ typedef struct {
 /* Bytes of the device parameter blob (coefficient tables for every query head). */
 size_t oal_params_bytes(const oal_dims *dims);
 
-/* Bytes of the state buffer: batch * n_kv_heads * 2145 * 65 * 4. */
+/* Floats per (sequence, KV head) block of the state buffer: 2145 * 65 rounded up to 64. */
+#define OAL_STATE_STRIDE 139456
+
+/* Bytes of the state buffer: batch * n_kv_heads * OAL_STATE_STRIDE * 4. */
 size_t oal_state_bytes(const oal_dims *dims);
 
 /* Bytes of the scratch buffer oal_prefill needs for T tokens at this chunk size

@@ -44,7 +44,7 @@ class Session:
 
     def state_np(self):
         torch.cuda.synchronize()
-        return self.state.cpu().numpy().reshape(self.B, self.Hkv, 2145, 65).astype(np.float64)
+        return gpq.state_view(self.state, self.B, self.Hkv).cpu().numpy().astype(np.float64)
 
 
 def session_for(inp, chunk=128):
