@@ -50,6 +50,22 @@ def parse():
     return ap.parse_args()
 
 
+def measured_traffic(tj, key):
+    """HBM bytes per launch from the stored FETCH_SIZE/WRITE_SIZE counters, or None when the
+    kernel's source file has changed since they were taken (the stored sha256 differs)."""
+    import hashlib
+    rec = tj.get(key)
+    if not rec or "source" not in rec:
+        return None
+    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "grouped_positive_quadratic_amd",
+                        "csrc", rec["source"])
+    try:
+        digest = hashlib.sha256(open(path, "rb").read()).hexdigest()
+    except OSError:
+        return None
+    return rec["bytes_per_launch"] if digest == rec.get("source_sha256") else None
+
+
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -115,7 +131,7 @@ def main():
             tj = json.load(open(args.traffic_json))
         except (OSError, ValueError):
             tj = {}
-    traffic = tj.get(f"readout_B{B}_T{T}_C{C}", {}).get("bytes_per_launch")
+    traffic = measured_traffic(tj, f"readout_B{B}_T{T}_C{C}")
     out = {
         "metric": METRIC,
         "value": tokens / (ms_step * 1e-3),
@@ -135,7 +151,7 @@ def main():
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
                      "traffic": traffic, "avg_ms": read_ms,
                      "algorithmic_flops_per_launch": readout_flops},
-        "phases_ms": {"scan": scan_ms, "readout": read_ms},
+        "phases_ms": {"intra_and_scan": scan_ms, "readout": read_ms},
         "prefill_algorithmic_tflops": (readout_flops + scan_flops) / (ms_step * 1e-3) / 1e12,
     }
     del q, k, v, y, ws, state, params
@@ -175,7 +191,7 @@ def main():
                          "steps": nsteps, "config": {"workload": f"decode {nseq} seqs, 4096-token prefix states, 14q/2kv"},
                          "roofline": {"bound": "hbm", "kernel": "oal_decode_kernel", "achieved": dach,
                                       "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": dach / PEAK_HBM_GBS,
-                                      "traffic": tj.get(f"decode_{nseq}seq", {}).get("bytes_per_launch"),
+                                      "traffic": measured_traffic(tj, f"decode_{nseq}seq"),
                                       "algorithmic_bytes_per_launch": alg}}
 
     # ---------------- CPU oracle baseline ----------------
