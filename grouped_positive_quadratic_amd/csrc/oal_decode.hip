@@ -6,13 +6,17 @@
 //   y_h = u~_h[0:64] / u~_h[64]
 // with psi(k) = [1, k_r, k_r k_t (r <= t)] and phi_h(q) = wdec_h o [1, q_r, q_r q_t].
 //
-// The state row f of a KV head holds 65 floats. Workgroup (split, bkv) owns rows
-// [256 split, 256 split + 256): wave w walks 64 of them with lane c on column c (one
-// coalesced 256-byte row read and write per step), then column 64 of the same rows with
-// lane = row. Every byte of the state is read once and written once. Readout partial sums
-// per split go to the workspace; the last workgroup of a (sequence, KV head) to arrive sums
-// the splits in a fixed order, divides and writes y, then resets the arrival counter.
-// No device-wide fence is used: it would write back the whole L2, full of fresh state rows.
+// The state row f of a KV head holds 65 floats. Workgroup (split, bkv) owns 192 rows; wave w
+// walks 48 of them in batches of 16 with lane c on column c (one coalesced 256-byte row read
+// and write per row) and column 64 of the batch's rows on lanes 0..15, so each cache line is
+// touched within one batch and fetched from HBM once. The next batch is loaded while the
+// current one is updated, and the first batch is requested together with everything the
+// set-up reads (k, q, v, decode coefficients): the set-up costs one memory round trip, spent
+// while the first rows arrive. Every byte of the state is read once and written once.
+// Readout partial sums per split go to the workspace; the last workgroup of a (sequence, KV
+// head) to arrive sums the splits in a fixed order, divides and writes y, then resets the
+// arrival counter. No device-wide fence is used: it would write back the whole L2, full of
+// fresh state rows.
 #include <hip/hip_runtime.h>
 
 #include "oal.h"
@@ -21,9 +25,13 @@
 
 namespace {
 
-constexpr int kRows = 256;          // state rows per workgroup
+constexpr int kRows = 192;                  // state rows per workgroup (12 splits: 6 workgroups per CU at 128 KV heads)
 constexpr int kThreads = 256;
+constexpr int kRowsPerWave = kRows / 4;
 constexpr int kSplits = (OAL_NFEAT + kRows - 1) / kRows;
+constexpr int kBatch = 16;                  // rows per load batch of a wave
+static_assert(kRows % 4 == 0 && kRows <= 2 * kThreads, "rows per workgroup");
+static_assert(8 * OAL_D % kThreads == 0, "query staging");
 
 __device__ inline void row_dims(int f, int &r, int &t) {
     if (f == 0) { r = -1; t = -1; return; }
@@ -49,59 +57,91 @@ __global__ __launch_bounds__(kThreads) void oal_decode_kernel(
     const int nrows = min(kRows, OAL_NFEAT - f0);
 
     __shared__ float s_k[OAL_D];
-    __shared__ float s_q[MAXH][OAL_D];    // rows >= n_rep stay unread (phi forced to 0)
+    __shared__ float s_q[MAXH][OAL_D];
     __shared__ float s_psi[kRows];
     __shared__ __align__(16) float s_phi[kRows][MAXH];
     __shared__ float s_red[4][MAXH][OAL_V1];
     __shared__ int s_last;
 
-    if (tid < OAL_D) s_k[tid] = oal_ld(k + (size_t)bkv * OAL_D + tid);
-    for (int idx = tid; idx < n_rep * OAL_D; idx += kThreads)
-        s_q[idx / OAL_D][idx % OAL_D] = oal_ld(q + ((size_t)b * n_q_heads + h0) * OAL_D + idx);
-    __syncthreads();
+    float *S = state + (size_t)bkv * OAL_STATE_STRIDE;
+    const int rbeg = wave * kRowsPerWave, rend = min(nrows, rbeg + kRowsPerWave);
+    // one batch: 16 rows with lane = column, and column 64 of the same rows on lanes 0..15
+    auto load_batch = [&](int rr, float *x, float &x64) {
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u)
+            x[u] = (rr + u < rend) ? S[(size_t)(f0 + rr + u) * OAL_V1 + lane] : 0.0f;
+        x64 = (lane < kBatch && rr + lane < rend) ? S[(size_t)(f0 + rr + lane) * OAL_V1 + OAL_D] : 0.0f;
+    };
 
-    // features of this workgroup's rows: psi (key) and phi_h (query, with coefficient)
-    for (int rr = tid; rr < kRows; rr += kThreads) {
-        int f = f0 + rr;
-        float psi = 0.0f;
-        if (rr < nrows) {
-            int r, t;
-            row_dims(f, r, t);
-            psi = (r < 0) ? 1.0f : (t < 0 ? s_k[r] : s_k[r] * s_k[t]);
-            float w[MAXH];
+    // 1. every global load of the set-up in one round trip: the first state batch, k, the
+    //    queries, v, and the decode coefficients of this thread's rows
+    float s[kBatch], s64;
+    load_batch(rbeg, s, s64);
+    const float kk = tid < OAL_D ? oal_ld(k + (size_t)bkv * OAL_D + tid) : 0.0f;
+    const T *qb = q + ((size_t)b * n_q_heads + h0) * OAL_D;
+    constexpr int kQIters = MAXH * OAL_D / kThreads;
+    float qv[kQIters];
 #pragma unroll
-            for (int h = 0; h < MAXH; ++h) {   // all coefficient loads in flight together
-                const OalHeadDev *hd = reinterpret_cast<const OalHeadDev *>(
-                    params + sizeof(OalParamsHeader) + (size_t)(h0 + min(h, n_rep - 1)) * OAL_HEAD_BYTES);
-                w[h] = hd->wdec[f];
-            }
+    for (int it = 0; it < kQIters; ++it)
+        qv[it] = tid + it * kThreads < n_rep * OAL_D ? oal_ld(qb + tid + it * kThreads) : 0.0f;
+    const float vv = oal_ld(v + (size_t)bkv * OAL_D + lane);
+    constexpr int kRowIters = (kRows + kThreads - 1) / kThreads;
+    float w[kRowIters][MAXH];
 #pragma unroll
-            for (int h = 0; h < MAXH; ++h) {
-                float mono = (r < 0) ? 1.0f : (t < 0 ? s_q[h][r] : s_q[h][r] * s_q[h][t]);
-                s_phi[rr][h] = h < n_rep ? w[h] * mono : 0.0f;
-            }
-        } else {
+    for (int it = 0; it < kRowIters; ++it) {
+        const int rr = tid + it * kThreads;
 #pragma unroll
-            for (int h = 0; h < MAXH; ++h) s_phi[rr][h] = 0.0f;
+        for (int h = 0; h < MAXH; ++h) {
+            const OalHeadDev *hd = reinterpret_cast<const OalHeadDev *>(
+                params + sizeof(OalParamsHeader) + (size_t)(h0 + min(h, n_rep - 1)) * OAL_HEAD_BYTES);
+            w[it][h] = (rr < nrows && h < n_rep) ? hd->wdec[f0 + rr] : 0.0f;
         }
-        s_psi[rr] = psi;
+    }
+    if (tid < OAL_D) s_k[tid] = kk;
+#pragma unroll
+    for (int it = 0; it < kQIters; ++it) {
+        const int idx = tid + it * kThreads;
+        if (idx < n_rep * OAL_D) s_q[idx / OAL_D][idx % OAL_D] = qv[it];
     }
     __syncthreads();
 
-    float *S = state + (size_t)bkv * OAL_STATE_STRIDE;
-    const float vv = oal_ld(v + (size_t)bkv * OAL_D + lane);
+    // 2. features of this workgroup's rows: psi (key) and phi_h (query, with coefficient)
+#pragma unroll
+    for (int it = 0; it < kRowIters; ++it) {
+        const int rr = tid + it * kThreads;
+        if (rr < kRows) {
+            float psi = 0.0f;
+            float ph[MAXH];
+#pragma unroll
+            for (int h = 0; h < MAXH; ++h) ph[h] = 0.0f;
+            if (rr < nrows) {
+                int r, t;
+                row_dims(f0 + rr, r, t);
+                psi = (r < 0) ? 1.0f : (t < 0 ? s_k[r] : s_k[r] * s_k[t]);
+#pragma unroll
+                for (int h = 0; h < MAXH; ++h) {
+                    float mono = (r < 0) ? 1.0f : (t < 0 ? s_q[h][r] : s_q[h][r] * s_q[h][t]);
+                    ph[h] = w[it][h] * mono;
+                }
+            }
+#pragma unroll
+            for (int h = 0; h < MAXH; ++h) s_phi[rr][h] = ph[h];
+            s_psi[rr] = psi;
+        }
+    }
+    __syncthreads();
+
+    // 3. stream the rows: S += psi [v;1], written back; readout sums of the updated rows.
+    //    The next batch is in flight while the current one is updated.
     float acc[MAXH], accd[MAXH];
 #pragma unroll
     for (int h = 0; h < MAXH; ++h) { acc[h] = 0.0f; accd[h] = 0.0f; }
-
-    const int rbeg = wave * 64, rend = min(nrows, rbeg + 64);
-    for (int rr = rbeg; rr < rend; rr += 16) {
-        float s[16];
+    for (int rr = rbeg; rr < rend; rr += kBatch) {
+        float sn[kBatch], sn64 = 0.0f;
+        const bool more = rr + kBatch < rend;
+        if (more) load_batch(rr + kBatch, sn, sn64);
 #pragma unroll
-        for (int u = 0; u < 16; ++u)
-            s[u] = (rr + u < rend) ? S[(size_t)(f0 + rr + u) * OAL_V1 + lane] : 0.0f;
-#pragma unroll
-        for (int u = 0; u < 16; ++u) {
+        for (int u = 0; u < kBatch; ++u) {
             if (rr + u < rend) {
                 s[u] += s_psi[rr + u] * vv;
                 S[(size_t)(f0 + rr + u) * OAL_V1 + lane] = s[u];
@@ -109,16 +149,16 @@ __global__ __launch_bounds__(kThreads) void oal_decode_kernel(
                 for (int h = 0; h < MAXH; ++h) acc[h] += s_phi[rr + u][h] * s[u];
             }
         }
-    }
-    // column 64 ("1" of [v;1]) of the same rows, lane = row
-    {
-        int rr = rbeg + lane;
-        if (rr < rend) {
-            float *p = S + (size_t)(f0 + rr) * OAL_V1 + OAL_D;
-            float s = *p + s_psi[rr];
-            *p = s;
+        if (lane < kBatch && rr + lane < rend) {
+            s64 += s_psi[rr + lane];
+            S[(size_t)(f0 + rr + lane) * OAL_V1 + OAL_D] = s64;
 #pragma unroll
-            for (int h = 0; h < MAXH; ++h) accd[h] += s_phi[rr][h] * s;
+            for (int h = 0; h < MAXH; ++h) accd[h] += s_phi[rr + lane][h] * s64;
+        }
+        if (more) {
+#pragma unroll
+            for (int u = 0; u < kBatch; ++u) s[u] = sn[u];
+            s64 = sn64;
         }
     }
 #pragma unroll
@@ -130,9 +170,9 @@ __global__ __launch_bounds__(kThreads) void oal_decode_kernel(
         if (lane == 0) s_red[wave][h][OAL_D] = x;
     }
     __syncthreads();
-    // Cross-workgroup combine. Partials are written and read with agent-scope atomics, which
-    // are coherent across the XCDs' L2 caches; the workgroup-scope fences order them around
-    // the arrival counter (they wait for the stores to complete) without flushing L2.
+    // 4. cross-workgroup combine. Partials are written and read with agent-scope atomics, which
+    //    are coherent across the XCDs' L2 caches; the workgroup-scope fences order them around
+    //    the arrival counter (they wait for the stores to complete) without flushing L2.
     float *mypart = partial + ((size_t)bkv * kSplits + split) * MAXH * OAL_V1;
     for (int idx = tid; idx < n_rep * OAL_V1; idx += kThreads) {
         int h = idx / OAL_V1, c = idx % OAL_V1;
@@ -142,7 +182,7 @@ __global__ __launch_bounds__(kThreads) void oal_decode_kernel(
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
     __syncthreads();
     if (tid == 0) {
-        unsigned int old = __hip_atomic_fetch_add(counters + bkv, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+        unsigned int old = __hip_atomic_fetch_add(counters + bkv, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         s_last = (old == (unsigned int)(kSplits - 1));
     }
     __syncthreads();
@@ -164,7 +204,7 @@ __global__ __launch_bounds__(kThreads) void oal_decode_kernel(
         for (int sp = 0; sp < kSplits; ++sp) { num += pn[sp]; den += pd[sp]; }
         y[((size_t)b * n_q_heads + h0 + h) * OAL_D + c] = num / den;
     }
-    if (tid == 0) __hip_atomic_store(counters + bkv, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+    if (tid == 0) __hip_atomic_store(counters + bkv, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 template <typename T, int MAXH>
