@@ -8,12 +8,14 @@
 //   u~_i = phi_h(q_i) . S_c + sum_{j in chunk c, j <= i} kappa_h(q_i, k_j) [v_j;1]
 //
 // Kernels, in launch order:
-//  0. oal_intra: per (chunk x 16-query tile, sequence x KV head) the exact intra-chunk kernel
-//     sums of every query head, kappa [V;1] unnormalised, on MFMA (independent of the state).
-//  1. oal_scan_delta: per (sequence x KV head, chunk, K-step), in parallel, the chunk's state
-//     increment psi(K_c)^T [V_c;1] on MFMA (fp32), from K and V staged transposed in LDS.
-//     Besides the 72 main K-steps, up to 8 tail K-steps carry the linear features, the
-//     constant and the KV head's non-bulk pairs.
+//  1. oal_intra_delta, two independent parts in one launch (oal_scan_delta alone when only
+//     the state is wanted):
+//     - per (chunk x 16-query tile, sequence x KV head) the exact intra-chunk kernel sums of
+//       every query head, kappa [V;1] unnormalised, on MFMA;
+//     - per (sequence x KV head, chunk, K-step), in parallel, the chunk's state increment
+//       psi(K_c)^T [V_c;1] on MFMA (fp32), from K and V staged transposed in LDS. Besides
+//       the 72 main K-steps, up to 8 tail K-steps carry the linear features, the constant
+//       and the KV head's non-bulk pairs.
 //  2. oal_scan_prefix: per state fragment, the running sum over chunks from the incoming
 //     state: the snapshot before each chunk (scaled, bf16 or fp32, in the MFMA operand order
 //     of the readout) and the final state.
@@ -173,8 +175,8 @@ __device__ inline void store_frags(float *dp, const oal_f32x4 (&acc)[2][5], int 
 // grid (K-step blocks + 1 tail block, chunks, sequence x KV head); 8 waves, one K-step each.
 // The chunk's K and V are staged transposed in LDS ([dim][token]).
 template <typename T, int C>
-__global__ __launch_bounds__(64 * kScanWaves) void oal_scan_delta(
-    int T_len, int nchunks, int n_q_heads, int n_kv_heads, const T *__restrict__ k,
+__device__ __forceinline__ void scan_delta_block(
+    int bx, int c, int bkv, int T_len, int nchunks, int n_q_heads, int n_kv_heads, const T *__restrict__ k,
     const T *__restrict__ v, const unsigned char *__restrict__ params, const float *__restrict__ state,
     float *__restrict__ delta, float *__restrict__ tinit) {
     constexpr int EPU = 16 / (int)sizeof(T);
@@ -189,11 +191,10 @@ __global__ __launch_bounds__(64 * kScanWaves) void oal_scan_delta(
 
     const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
     const int g = lane >> 4, lr = lane & 15;
-    const int s = blockIdx.x * kScanWaves + wave;
-    const int c = blockIdx.y, bkv = blockIdx.z;
+    const int s = bx * kScanWaves + wave;
     const OalKvDev *kvd = kv_ptr(params, n_q_heads, bkv % n_kv_heads);
     const int nsteps = kvd->nsteps;
-    if (blockIdx.x == kScanBlocks && nsteps == 0) return;     // whole workgroup
+    if (bx == kScanBlocks && nsteps == 0) return;     // whole workgroup
     const bool idle = s >= OAL_KSTEPS + nsteps;             // only helps staging
 
     // stage: unit u = (array, 16-byte column a, token); consecutive lanes take consecutive
@@ -284,6 +285,15 @@ __global__ __launch_bounds__(64 * kScanWaves) void oal_scan_delta(
     }
 }
 
+template <typename T, int C>
+__global__ __launch_bounds__(64 * kScanWaves) void oal_scan_delta(
+    int T_len, int nchunks, int n_q_heads, int n_kv_heads, const T *__restrict__ k,
+    const T *__restrict__ v, const unsigned char *__restrict__ params, const float *__restrict__ state,
+    float *__restrict__ delta, float *__restrict__ tinit) {
+    scan_delta_block<T, C>(blockIdx.x, blockIdx.y, blockIdx.z, T_len, nchunks, n_q_heads, n_kv_heads, k, v,
+                           params, state, delta, tinit);
+}
+
 // one thread per (sequence x KV head, K-step, fragment): the state before each chunk is the
 // incoming state plus the earlier chunks' increments (fp32, in chunk order)
 template <typename T>
@@ -327,7 +337,9 @@ __global__ __launch_bounds__(256) void oal_scan_prefix(int nchunks, int n_q_head
         S[4] = a1.x; S[5] = a1.y; S[6] = a1.z; S[7] = a1.w;
     }
     const float *dp = delta + ((size_t)bkv * nchunks * OAL_SNAP_KSTEPS + s) * kDeltaStep + f * 8;
-    unsigned char *sp = snap + ((size_t)bkv * nchunks * OAL_SNAP_KSTEPS + s) * KB + (size_t)f * OalFrag<T>::kBytes;
+    // snap == nullptr: only the final state is wanted (no readout follows)
+    unsigned char *sp = snap ? snap + ((size_t)bkv * nchunks * OAL_SNAP_KSTEPS + s) * KB + (size_t)f * OalFrag<T>::kBytes
+                             : nullptr;
     constexpr size_t DSTRIDE = (size_t)OAL_SNAP_KSTEPS * kDeltaStep, SSTRIDE = (size_t)OAL_SNAP_KSTEPS * KB;
     for (int c0 = 0; c0 < nchunks; c0 += 4) {
         float4 d[4][2];
@@ -342,12 +354,14 @@ __global__ __launch_bounds__(256) void oal_scan_prefix(int nchunks, int n_q_head
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
             if (c0 + u < nchunks) {
-                float x[8];
+                if (sp) {
+                    float x[8];
 #pragma unroll
-                for (int j = 0; j < 8; ++j) x[j] = S[j] * fsc[j];
-                OalFrag<T> fr;
-                fr.set(x);
-                fr.store(sp + (size_t)(c0 + u) * SSTRIDE);
+                    for (int j = 0; j < 8; ++j) x[j] = S[j] * fsc[j];
+                    OalFrag<T> fr;
+                    fr.set(x);
+                    fr.store(sp + (size_t)(c0 + u) * SSTRIDE);
+                }
                 S[0] += d[u][0].x; S[1] += d[u][0].y; S[2] += d[u][0].z; S[3] += d[u][0].w;
                 S[4] += d[u][1].x; S[5] += d[u][1].y; S[6] += d[u][1].z; S[7] += d[u][1].w;
             }
@@ -421,10 +435,10 @@ template <typename T, int C> struct IntraLayout {
 // accumulator-fragment order; the readout adds it before the divide.
 constexpr int kIntraWaves = 8;
 template <typename T, int C>
-__global__ __launch_bounds__(64 * kIntraWaves) __attribute__((amdgpu_waves_per_eu(4))) void oal_intra(int T_len, int n_q_heads, int n_kv_heads, int nchunks, int n_bkv,
-                                                               const T *__restrict__ q, const T *__restrict__ k,
-                                                               const T *__restrict__ v, const unsigned char *__restrict__ params,
-                                                               float *__restrict__ uintra) {
+__device__ __forceinline__ void intra_block(int Lb, int T_len, int n_q_heads, int n_kv_heads, int nchunks, int n_bkv,
+                                            const T *__restrict__ q, const T *__restrict__ k,
+                                            const T *__restrict__ v, const unsigned char *__restrict__ params,
+                                            float *__restrict__ uintra) {
     using Lay = IntraLayout<T, C>;
     constexpr int EPU = Lay::EPU, QS = Lay::QS, LDV = Lay::LDV;
     constexpr int NQT = C / 16;
@@ -437,7 +451,7 @@ __global__ __launch_bounds__(64 * kIntraWaves) __attribute__((amdgpu_waves_per_e
 
     // XCD-aware placement: the NQT tiles of one (chunk, sequence x KV head) get block ids
     // congruent mod 8, i.e. the same XCD, so its K and V are fetched into one L2
-    const int Lb = blockIdx.x, xcd = Lb % kXcds, i8 = Lb / kXcds;
+    const int xcd = Lb % kXcds, i8 = Lb / kXcds;
     const int unit = xcd + kXcds * (i8 / NQT), qt = i8 % NQT;
     if (unit >= nchunks * n_bkv) return;
     const int c = unit % nchunks, bkv = unit / nchunks;
@@ -606,6 +620,32 @@ __global__ __launch_bounds__(64 * kIntraWaves) __attribute__((amdgpu_waves_per_e
         for (int n = 0; n < 5; ++n)
 #pragma unroll
             for (int ii = 0; ii < 4; ++ii) up[(n * 4 + ii) * 64] = acc[n][ii];
+    }
+}
+
+// The intra-chunk sums and the chunk increments in one launch: they are independent, the
+// first is bound by MFMA chain latency and the second by staging and stores, so sharing the
+// CUs overlaps them. Blocks [0, n_intra) are intra-chunk blocks (the longer ones, dispatched
+// first; n_intra is a multiple of 8, so their XCD placement is the one described above); the
+// rest are increment blocks (K-step block fastest, then chunk, then sequence x KV head).
+template <typename T, int C>
+__global__ __launch_bounds__(64 * kIntraWaves) __attribute__((amdgpu_waves_per_eu(4))) void oal_intra_delta(
+    int T_len, int n_q_heads, int n_kv_heads, int nchunks, int n_bkv, int n_delta, const T *__restrict__ q,
+    const T *__restrict__ k, const T *__restrict__ v, const unsigned char *__restrict__ params,
+    const float *__restrict__ state, float *__restrict__ delta, float *__restrict__ tinit,
+    float *__restrict__ uintra) {
+    static_assert(kScanWaves == kIntraWaves, "one workgroup shape for both parts");
+    const int n_intra = (int)gridDim.x - n_delta;
+    const int id = blockIdx.x;
+    if (id < n_intra) {
+        intra_block<T, C>(id, T_len, n_q_heads, n_kv_heads, nchunks, n_bkv, q, k, v, params, uintra);
+    } else {
+        constexpr int NB = kScanBlocks + 1;
+        const int j = id - n_intra;
+        const int bx = j % NB, rest = j / NB, c = rest % nchunks, bkv = rest / nchunks;
+        if (bkv >= n_bkv) return;
+        scan_delta_block<T, C>(bx, c, bkv, T_len, nchunks, n_q_heads, n_kv_heads, k, v, params, state, delta,
+                               tinit);
     }
 }
 
@@ -975,21 +1015,22 @@ hipError_t launch_all(const oal_dims &d, int T_len, const void *q, const void *k
     const unsigned char *pb = reinterpret_cast<const unsigned char *>(params);
     hipError_t e;
     if (marks && (e = hipEventRecord(marks[0], stream)) != hipSuccess) return e;
-    if (y) {   // intra-chunk sums: independent of the state scan
+    if (y) {   // intra-chunk sums and chunk increments in one launch
         using IL = IntraLayout<T, C>;
-        const size_t lds = IL::bytes(std::min(d.n_q_heads / d.n_kv_heads, kIntraLzHeads));
-        auto kern = oal_intra<T, C>;
+        const size_t lds = std::max(IL::bytes(std::min(d.n_q_heads / d.n_kv_heads, kIntraLzHeads)), scan_lds<T, C>());
+        auto kern = oal_intra_delta<T, C>;
         if ((e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds)) != hipSuccess)
             return e;
         const int nunits = p.nchunks * bkv;
-        const int nblocks = kXcds * (C / 16) * ((nunits + kXcds - 1) / kXcds);
-        hipLaunchKernelGGL(kern, dim3(nblocks), dim3(64 * kIntraWaves), lds, stream, T_len,
-                           d.n_q_heads, d.n_kv_heads, p.nchunks, bkv, reinterpret_cast<const T *>(q),
-                           reinterpret_cast<const T *>(k), reinterpret_cast<const T *>(v), pb, uintra);
+        const int n_intra = kXcds * (C / 16) * ((nunits + kXcds - 1) / kXcds);
+        const int n_delta = (kScanBlocks + 1) * p.nchunks * bkv;
+        hipLaunchKernelGGL(kern, dim3(n_intra + n_delta), dim3(64 * kIntraWaves), lds, stream, T_len,
+                           d.n_q_heads, d.n_kv_heads, p.nchunks, bkv, n_delta, reinterpret_cast<const T *>(q),
+                           reinterpret_cast<const T *>(k), reinterpret_cast<const T *>(v), pb, state, delta,
+                           tinit, uintra);
         if ((e = hipGetLastError()) != hipSuccess) return e;
-    }
-    {
+    } else {   // state only: the increments alone
         auto kern = oal_scan_delta<T, C>;
         size_t lds = scan_lds<T, C>();
         if ((e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
@@ -1003,7 +1044,7 @@ hipError_t launch_all(const oal_dims &d, int T_len, const void *q, const void *k
     {
         const size_t nthr = (size_t)bkv * OAL_SNAP_KSTEPS * kFrags;
         hipLaunchKernelGGL(oal_scan_prefix<T>, dim3((unsigned)((nthr + 255) / 256)), dim3(256), 0, stream,
-                           p.nchunks, d.n_q_heads, d.n_kv_heads, bkv, pb, delta, tinit, state, snap);
+                           p.nchunks, d.n_q_heads, d.n_kv_heads, bkv, pb, delta, tinit, state, y ? snap : nullptr);
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
     if (marks && (e = hipEventRecord(marks[1], stream)) != hipSuccess) return e;
