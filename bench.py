@@ -30,6 +30,7 @@ D, V1, NFEAT = 64, 65, 2145
 FLOP_PER_TOKEN_HEAD = 2 * NFEAT * V1          # 278,850: one feature-space contraction
 PEAK_BF16_TFLOPS = 2500.0                     # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0                         # MI355X HBM3E
+PHASE_EVERY = 4                               # timed steps with per-kernel events
 
 
 def parse():
@@ -105,23 +106,31 @@ def main():
     k = torch.from_numpy(inp.k).to(torch.bfloat16).to(dev).contiguous()
     v = torch.from_numpy(inp.v).to(torch.bfloat16).to(dev).contiguous()
     y = torch.empty((B, Hq, T, D), dtype=torch.float32, device=dev)
-    marks = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
-    for mk in marks:
+    # Per-kernel times come from events recorded around the kernels on the launch stream, in
+    # every PHASE_EVERY-th timed step only: each recorded event costs a few microseconds of
+    # device time between two kernels (fence-free timing events, still a marker packet), which
+    # would otherwise be counted in ms_per_step.
+    timed_steps = [i for i in range(args.steps) if i % PHASE_EVERY == 0]
+    marks = {i: [gpq.TimingEvent() for _ in range(3)] for i in timed_steps}
+    for mk in marks.values():
         for m in mk:
             m.record(stream)          # create the underlying events
     for _ in range(args.warmup):
         gpq.oal_prefill(dims, T, C, q, k, v, params, state, ws, y)
     torch.cuda.synchronize()
-    t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t_start, t_end = gpq.TimingEvent(), gpq.TimingEvent()
     t_start.record(stream)
     for i in range(args.steps):
-        gpq.oal_prefill_timed(dims, T, C, q, k, v, params, state, ws, y, marks[i])
+        if i in marks:
+            gpq.oal_prefill_timed(dims, T, C, q, k, v, params, state, ws, y, marks[i])
+        else:
+            gpq.oal_prefill(dims, T, C, q, k, v, params, state, ws, y)
     t_end.record(stream)
     torch.cuda.synchronize()
     ms_total = t_start.elapsed_time(t_end)
     ms_step = ms_total / args.steps
-    scan_ms = float(np.mean([mk[0].elapsed_time(mk[1]) for mk in marks]))
-    read_ms = float(np.mean([mk[1].elapsed_time(mk[2]) for mk in marks]))
+    scan_ms = float(np.mean([mk[0].elapsed_time(mk[1]) for mk in marks.values()]))
+    read_ms = float(np.mean([mk[1].elapsed_time(mk[2]) for mk in marks.values()]))
     tokens = B * T
     readout_flops = FLOP_PER_TOKEN_HEAD * tokens * Hq
     scan_flops = FLOP_PER_TOKEN_HEAD * tokens * Hkv
@@ -152,7 +161,9 @@ def main():
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
                      "traffic": traffic, "avg_ms": read_ms,
                      "algorithmic_flops_per_launch": readout_flops},
-        "phases_ms": {"intra_and_scan": scan_ms, "readout": read_ms},
+        "phases_ms": {"intra_and_scan": scan_ms, "readout": read_ms,
+                      "sampled_steps": len(marks), "note": "events around the kernels in every "
+                      f"{PHASE_EVERY}th timed step"},
         "prefill_algorithmic_tflops": (readout_flops + scan_flops) / (ms_step * 1e-3) / 1e12,
     }
     del q, k, v, y, ws, state, params

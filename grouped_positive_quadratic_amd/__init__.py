@@ -3,7 +3,7 @@
 Every entry point has the name of the C function in ``include/oal.h`` that it calls. Device
 buffers are torch tensors on the GPU (torch provides memory and streams, nothing else);
 all computation happens in the library's HIP kernels. Importing this module fails loudly
-when the library has not been built (``python -m grouped_positive_quadratic_amd.build``).
+when the library has not been built (``python grouped_positive_quadratic_amd/build.py``).
 """
 from __future__ import annotations
 
@@ -22,7 +22,8 @@ STATUS = {0: "OAL_OK", 1: "OAL_E_ARG", 2: "OAL_E_SHAPE", 3: "OAL_E_DTYPE", 4: "O
           5: "OAL_E_UNSUPPORTED", 6: "OAL_E_HIP"}
 EXPORTED = ("oal_params_bytes", "oal_state_bytes", "oal_prefill_workspace_bytes",
             "oal_decode_workspace_bytes", "oal_params_pack", "oal_state_init", "oal_prefill",
-            "oal_prefill_timed", "oal_decode_step", "oal_status_string")
+            "oal_prefill_timed", "oal_decode_step", "oal_status_string", "oal_timing_event_create",
+            "oal_timing_event_destroy", "oal_timing_event_record", "oal_timing_elapsed_ms")
 
 
 class OALError(RuntimeError):
@@ -50,7 +51,7 @@ def _load():
     import torch  # noqa: F401
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"{LIB_PATH} is missing: build it with "
-                          "`python -m grouped_positive_quadratic_amd.build` (hipcc, gfx950)")
+                          "`python grouped_positive_quadratic_amd/build.py` (hipcc, gfx950)")
     lib = ctypes.CDLL(LIB_PATH)
     P, I, S = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
     dp = ctypes.POINTER(oal_dims)
@@ -68,6 +69,11 @@ def _load():
     lib.oal_decode_step.argtypes = [dp, P, P, P, P, P, P, P, P]
     lib.oal_decode_step.restype = ctypes.c_int
     lib.oal_status_string.argtypes, lib.oal_status_string.restype = [ctypes.c_int], ctypes.c_char_p
+    lib.oal_timing_event_create.argtypes, lib.oal_timing_event_create.restype = [ctypes.POINTER(P)], ctypes.c_int
+    lib.oal_timing_event_destroy.argtypes, lib.oal_timing_event_destroy.restype = [P], ctypes.c_int
+    lib.oal_timing_event_record.argtypes, lib.oal_timing_event_record.restype = [P, P], ctypes.c_int
+    lib.oal_timing_elapsed_ms.argtypes = [P, P, ctypes.POINTER(ctypes.c_float)]
+    lib.oal_timing_elapsed_ms.restype = ctypes.c_int
     return lib
 
 
@@ -177,6 +183,31 @@ def oal_prefill_timed(dims: oal_dims, T: int, chunk: int, q, k, v, params_dev, s
     _check("oal_prefill_timed", _lib.oal_prefill_timed(
         ctypes.byref(dims), int(T), int(chunk), _ptr(q), _ptr(k), _ptr(v), _ptr(params_dev),
         _ptr(state_dev), _ptr(workspace), _ptr(y), _stream(stream), handles))
+
+
+class TimingEvent:
+    """A HIP event from oal_timing_event_create (no system-scope release when recorded)."""
+
+    def __init__(self):
+        h = ctypes.c_void_p()
+        _check("oal_timing_event_create", _lib.oal_timing_event_create(ctypes.byref(h)))
+        self.cuda_event = h.value
+
+    def record(self, stream=None):
+        _check("oal_timing_event_record", _lib.oal_timing_event_record(ctypes.c_void_p(self.cuda_event),
+                                                                       _stream(stream)))
+
+    def elapsed_time(self, end: "TimingEvent") -> float:
+        ms = ctypes.c_float()
+        _check("oal_timing_elapsed_ms", _lib.oal_timing_elapsed_ms(ctypes.c_void_p(self.cuda_event),
+                                                                   ctypes.c_void_p(end.cuda_event),
+                                                                   ctypes.byref(ms)))
+        return float(ms.value)
+
+    def __del__(self):
+        if getattr(self, "cuda_event", None) and _lib is not None:
+            _lib.oal_timing_event_destroy(ctypes.c_void_p(self.cuda_event))
+            self.cuda_event = None
 
 
 def oal_decode_step(dims: oal_dims, q, k, v, params_dev, state_dev, workspace, y, stream=None):

@@ -331,4 +331,41 @@ oal_status oal_decode_step(const oal_dims *d, const void *q, const void *k, cons
     return OAL_OK;
 }
 
+oal_status oal_timing_event_create(hipEvent_t *event) {
+    if (!event) return OAL_E_ARG;
+    if (hipEventCreateWithFlags(event, hipEventDisableSystemFence) != hipSuccess) {
+        (void)hipGetLastError();
+        *event = nullptr;
+        return OAL_E_HIP;
+    }
+    return OAL_OK;
+}
+
+oal_status oal_timing_event_destroy(hipEvent_t event) {
+    if (!event) return OAL_OK;
+    if (hipEventDestroy(event) != hipSuccess) {
+        (void)hipGetLastError();
+        return OAL_E_HIP;
+    }
+    return OAL_OK;
+}
+
+oal_status oal_timing_event_record(hipEvent_t event, hipStream_t stream) {
+    if (!event) return OAL_E_ARG;
+    if (hipEventRecord(event, stream) != hipSuccess) {
+        (void)hipGetLastError();
+        return OAL_E_HIP;
+    }
+    return OAL_OK;
+}
+
+oal_status oal_timing_elapsed_ms(hipEvent_t start, hipEvent_t end, float *ms) {
+    if (!start || !end || !ms) return OAL_E_ARG;
+    if (hipEventSynchronize(end) != hipSuccess || hipEventElapsedTime(ms, start, end) != hipSuccess) {
+        (void)hipGetLastError();
+        return OAL_E_HIP;
+    }
+    return OAL_OK;
+}
+
 }  // extern "C"

@@ -136,7 +136,8 @@ oal_status oal_prefill(const oal_dims *dims, int32_t T, int32_t chunk, const voi
 /* oal_prefill for measurement: identical work, and additionally records the caller-owned
  * events marks[0] on `stream` before the first kernel, marks[1] after the chunk-state scan
  * kernels and marks[2] after the readout kernel (hipEventElapsedTime between them gives
- * the per-phase device time). The events are created and destroyed by the caller. */
+ * the per-phase device time). The events are created and destroyed by the caller; events
+ * from oal_timing_event_create keep the recording cheap. */
 oal_status oal_prefill_timed(const oal_dims *dims, int32_t T, int32_t chunk, const void *q,
                              const void *k, const void *v, const void *params_dev,
                              float *state_dev, void *workspace, float *y, hipStream_t stream,
@@ -153,6 +154,22 @@ oal_status oal_prefill_timed(const oal_dims *dims, int32_t T, int32_t chunk, con
 oal_status oal_decode_step(const oal_dims *dims, const void *q, const void *k, const void *v,
                            const void *params_dev, float *state_dev, void *workspace, float *y,
                            hipStream_t stream);
+
+/* Timing events for oal_prefill_timed and for bracketing a timed region. A default HIP event
+ * performs a system-scope release when it is recorded, which writes back the L2: between two
+ * kernels that leave many dirty lines that costs several microseconds and would be counted
+ * as kernel time. These events are created with hipEventDisableSystemFence: their timestamps
+ * are the same, only the release is skipped, so they must not be used to order memory
+ * accesses with the host.
+ *   oal_timing_event_create  -- *event receives a new event (OAL_E_HIP on failure).
+ *   oal_timing_event_destroy -- releases it (NULL is accepted).
+ *   oal_timing_event_record  -- records it on `stream`.
+ *   oal_timing_elapsed_ms    -- waits for `end` to complete, then *ms = time from start to
+ *                               end; both must have been recorded. */
+oal_status oal_timing_event_create(hipEvent_t *event);
+oal_status oal_timing_event_destroy(hipEvent_t event);
+oal_status oal_timing_event_record(hipEvent_t event, hipStream_t stream);
+oal_status oal_timing_elapsed_ms(hipEvent_t start, hipEvent_t end, float *ms);
 
 /* Static description of a status code. */
 const char *oal_status_string(oal_status status);

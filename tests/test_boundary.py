@@ -258,3 +258,16 @@ def test_one_hip_runtime_per_process():
                          timeout=300)
     assert out.returncode == 0, out.stderr
     assert out.stdout.split()[0] == "1", out.stdout
+
+
+def test_build_entry_does_not_need_the_library():
+    """__graft_entry__.build() reaches the builder without importing the package, so a fresh
+    checkout (no liboal.so yet) or a stale library can be rebuilt."""
+    import subprocess
+    import sys
+    code = ("import sys, __graft_entry__ as g; b = g._library_builder(); "
+            "assert callable(b.build); "
+            "assert 'grouped_positive_quadratic_amd' not in sys.modules, 'package imported'")
+    r = subprocess.run([sys.executable, "-c", code], cwd=os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 0, r.stderr

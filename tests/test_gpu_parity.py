@@ -297,3 +297,21 @@ def test_cfg2_full():
         _report(f"cfg2 T=4096 C={chunk}", err)
         assert err <= TOL["bf16"]
         assert state_ok(sess.state_np(), inp.k, inp.v, "bf16")
+
+
+def test_prefill_timed_with_timing_events():
+    """oal_prefill_timed with the library's fence-free timing events: same output as
+    oal_prefill, phases ordered and positive."""
+    inp = qwen_like(1, 300, 2, name="timed")
+    a, b = session_for(inp), session_for(inp)
+    y_ref = a.prefill(inp.q, inp.k, inp.v)
+    q, k, v = (to_dev(x, inp.dtype) for x in (inp.q, inp.k, inp.v))
+    y = torch.empty_like(y_ref)
+    marks = [gpq.TimingEvent() for _ in range(3)]
+    b.ensure_ws(300, 128)
+    gpq.oal_prefill_timed(b.dims, 300, 128, q, k, v, b.params, b.state, b.ws, y, marks)
+    t_scan, t_read = marks[0].elapsed_time(marks[1]), marks[1].elapsed_time(marks[2])
+    print(f"[timed] scan {t_scan * 1e3:.1f} us, readout {t_read * 1e3:.1f} us", flush=True)
+    assert t_scan > 0 and t_read > 0
+    assert torch.equal(y, y_ref)
+    assert np.array_equal(a.state_np(), b.state_np())
