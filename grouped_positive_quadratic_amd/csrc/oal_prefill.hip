@@ -341,18 +341,22 @@ __global__ __launch_bounds__(256) void oal_scan_prefix(int nchunks, int n_q_head
     unsigned char *sp = snap ? snap + ((size_t)bkv * nchunks * OAL_SNAP_KSTEPS + s) * KB + (size_t)f * OalFrag<T>::kBytes
                              : nullptr;
     constexpr size_t DSTRIDE = (size_t)OAL_SNAP_KSTEPS * kDeltaStep, SSTRIDE = (size_t)OAL_SNAP_KSTEPS * KB;
-    for (int c0 = 0; c0 < nchunks; c0 += 4) {
-        float4 d[4][2];
+    // chunks in batches of PB; the next batch's increments are requested before the current
+    // batch is summed (two buffers, the loop unrolled by two batches)
+    constexpr int PB = 8;
+    auto load_batch = [&](int c0, float4 (&d)[PB][2]) {
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
+        for (int u = 0; u < PB; ++u) {
             if (c0 + u < nchunks) {
                 const float4 *q4 = reinterpret_cast<const float4 *>(dp + (size_t)(c0 + u) * DSTRIDE);
                 d[u][0] = q4[0];
                 d[u][1] = q4[1];
             }
         }
+    };
+    auto run_batch = [&](int c0, const float4 (&d)[PB][2]) {
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
+        for (int u = 0; u < PB; ++u) {
             if (c0 + u < nchunks) {
                 if (sp) {
                     float x[8];
@@ -366,6 +370,15 @@ __global__ __launch_bounds__(256) void oal_scan_prefix(int nchunks, int n_q_head
                 S[4] += d[u][1].x; S[5] += d[u][1].y; S[6] += d[u][1].z; S[7] += d[u][1].w;
             }
         }
+    };
+    float4 da[PB][2], db[PB][2];
+    load_batch(0, da);
+    for (int c0 = 0; c0 < nchunks; c0 += 2 * PB) {
+        if (c0 + PB < nchunks) load_batch(c0 + PB, db);
+        run_batch(c0, da);
+        if (c0 + PB >= nchunks) break;
+        if (c0 + 2 * PB < nchunks) load_batch(c0 + 2 * PB, da);
+        run_batch(c0 + PB, db);
     }
 #pragma unroll
     for (int j = 0; j < 8; ++j)     // tail pairs duplicate main rows: only owners write
