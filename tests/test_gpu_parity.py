@@ -315,3 +315,85 @@ def test_prefill_timed_with_timing_events():
     assert t_scan > 0 and t_read > 0
     assert torch.equal(y, y_ref)
     assert np.array_equal(a.state_np(), b.state_np())
+
+
+# --- the other workloads at full size: sampled rows against the oracle ---------------------
+
+def _sample_positions(T, chunk, rng, n_random=6):
+    """Sequence start and end, both sides of chunk boundaries, and random positions."""
+    pos = {0, 1, chunk - 1, chunk, 2 * chunk - 1, T // 2 - 1, T // 2, T - 2, T - 1}
+    pos.update(int(x) for x in rng.integers(0, T, size=n_random))
+    return sorted(p for p in pos if 0 <= p < T)
+
+
+@pytest.mark.parametrize("chunk", [64, 128, 256])
+def test_cfg3_batch8_sampled(chunk):
+    """B=8 x T=4096 (32k tokens), the chunk sizes of the sweep; 16 rows per (sequence, head)
+    against the oracle, and the final states of every sequence (one chunk size)."""
+    from oal_synth import cfg3
+    inp = cfg3()
+    B, Hq, Hkv, T, _, _ = inp.dims
+    sess = session_for(inp, chunk)
+    y = sess.prefill(inp.q, inp.k, inp.v, chunk).cpu().numpy()
+    rng = np.random.default_rng(30 + chunk)
+    rows = [(b, h, i) for b in range(B) for h in range(Hq) for i in _sample_positions(T, chunk, rng)]
+    ref = oracle.dense_rows(inp.q, inp.k, inp.v, inp.params, rows)
+    got = np.stack([y[b, h, i] for b, h, i in rows])
+    err = oracle.row_error(got, ref)
+    _report(f"cfg3 B=8 T=4096 C={chunk} ({len(rows)} sampled rows)", err)
+    assert np.isfinite(y).all()
+    assert err <= TOL["bf16"]
+    if chunk == 128:
+        assert state_ok(sess.state_np(), inp.k, inp.v, "bf16")
+
+
+def test_cfg4_long_context_sampled():
+    """T=32768, chunk 128 (the launch configuration of the benchmark's prefill): sampled rows
+    across the whole sequence, and the final state."""
+    from oal_synth import cfg4
+    inp = cfg4()
+    B, Hq, Hkv, T, _, _ = inp.dims
+    sess = session_for(inp, 128)
+    y = sess.prefill(inp.q, inp.k, inp.v, 128).cpu().numpy()
+    rng = np.random.default_rng(44)
+    rows = [(0, h, i) for h in range(Hq) for i in _sample_positions(T, 128, rng, n_random=10)]
+    ref = oracle.dense_rows(inp.q, inp.k, inp.v, inp.params, rows)
+    got = np.stack([y[b, h, i] for b, h, i in rows])
+    err = oracle.row_error(got, ref)
+    _report(f"cfg4 T=32768 ({len(rows)} sampled rows)", err)
+    assert np.isfinite(y).all()
+    assert err <= TOL["bf16"]
+    assert state_ok(sess.state_np(), inp.k, inp.v, "bf16")
+
+
+def test_cfg5_decode_64_sequences_sampled():
+    """The decode workload as the benchmark runs it: 64 sequences whose states are built by a
+    state-only prefill of 4096 tokens, then 256 decode steps. Outputs of 8 sequences at
+    several steps, and their final states, against the oracle over prefix + steps."""
+    from oal_synth import cfg5_prefix, cfg5_steps
+    nseq, steps, T0 = 64, 256, 4096
+    pre, tok = cfg5_prefix(n_seq=nseq), cfg5_steps(n_seq=nseq, steps=steps)
+    sess = Session(nseq, 14, 2, "bf16", pre.params, T0, 128)
+    k = to_dev(pre.k, "bf16")
+    v = to_dev(pre.v, "bf16")
+    gpq.oal_prefill(sess.dims, T0, 128, None, k, v, sess.params, sess.state, sess.ws, None)
+    del k, v
+    tq, tk, tv = (to_dev(x, "bf16").permute(2, 0, 1, 3).contiguous() for x in (tok.q, tok.k, tok.v))
+    ys = []
+    for s in range(steps):
+        ys.append(sess.decode(tq[s], tk[s], tv[s]))
+    y = torch.stack(ys).cpu().numpy()                 # [steps, nseq, 14, 64]
+    assert np.isfinite(y).all()
+    sel = [0, 9, 18, 27, 36, 45, 54, 63]              # sequences checked against the oracle
+    check_steps = [0, 1, 127, 255]
+    q_all = np.concatenate([np.zeros_like(pre.q[sel]), tok.q[sel]], axis=2)
+    k_all = np.concatenate([pre.k[sel], tok.k[sel]], axis=2)
+    v_all = np.concatenate([pre.v[sel], tok.v[sel]], axis=2)
+    rows = [(bi, h, T0 + s) for bi in range(len(sel)) for h in range(14) for s in check_steps]
+    ref = oracle.dense_rows(q_all, k_all, v_all, pre.params, rows)
+    got = np.stack([y[s - T0, sel[bi], h] for bi, h, s in rows])
+    err = oracle.row_error(got, ref)
+    _report(f"cfg5 decode 64 seqs x 256 steps ({len(rows)} sampled outputs)", err)
+    assert err <= TOL["bf16"]
+    S = sess.state_np()[sel[:2]]
+    assert state_ok(S, k_all[:2], v_all[:2], "bf16")
