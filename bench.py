@@ -45,6 +45,8 @@ def parse():
     ap.add_argument("--decode-steps", type=int, default=256)
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-scaling", action="store_true",
+                    help="skip the B=8 x T=4096 chunk sweep and the T=32768 prefill")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 256 MiB device copy (reference for HBM byte counters)")
     ap.add_argument("--traffic-json", default=os.path.join(os.path.dirname(os.path.abspath(__file__)),
@@ -168,6 +170,43 @@ def main():
     }
     del q, k, v, y, ws, state, params
     torch.cuda.empty_cache()
+
+    # ---------------- the other prefill workloads (context, not the headline) ----------------
+    if not args.no_scaling:
+        def prefill_rate(inp, C, reps):
+            Bx, Hqx, Hkvx, Tx, _, _ = inp.dims
+            dx = gpq.make_dims(Bx, Hqx, Hkvx, "bf16")
+            px, sx, wx, _ = gpq.alloc_buffers(dx, Tx, C)
+            gpq.oal_state_init(dx, gpq.HeadParamsC.from_params(inp.params), px, sx)
+            qx, kx, vx = (torch.from_numpy(a).to(torch.bfloat16).to(dev).contiguous() for a in (inp.q, inp.k, inp.v))
+            yx = torch.empty((Bx, Hqx, Tx, D), dtype=torch.float32, device=dev)
+            gpq.oal_prefill(dx, Tx, C, qx, kx, vx, px, sx, wx, yx)      # warm-up
+            torch.cuda.synchronize()
+            e0, e1 = gpq.TimingEvent(), gpq.TimingEvent()
+            e0.record(stream)
+            for _ in range(reps):
+                gpq.oal_prefill(dx, Tx, C, qx, kx, vx, px, sx, wx, yx)
+            e1.record(stream)
+            ms = e0.elapsed_time(e1) / reps
+            del px, sx, wx, qx, kx, vx, yx
+            torch.cuda.empty_cache()
+            return Bx * Tx / (ms * 1e-3), ms
+        from oal_synth import cfg3, cfg4
+        c3 = cfg3()
+        batch8 = {}
+        for C in (64, 128, 256):
+            r, ms = prefill_rate(c3, C, 5)
+            batch8[f"chunk{C}"] = {"tokens_per_s": r, "ms_per_call": ms}
+        del c3
+        c4 = cfg4()
+        r4, ms4 = prefill_rate(c4, 128, 3)
+        del c4
+        out["prefill_other_workloads"] = {
+            "B8_T4096": {"workload": "prefill B=8 T=4096 14q/2kv bf16, one call per step", **batch8},
+            "B1_T32768": {"workload": "prefill B=1 T=32768 14q/2kv bf16, chunk 128", "tokens_per_s": r4,
+                          "ms_per_call": ms4,
+                          "vs_T4096_tokens_per_s": r4 / out["value"]},
+        }
 
     # ---------------- decode ----------------
     if not args.no_decode:
