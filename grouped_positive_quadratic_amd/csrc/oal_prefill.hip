@@ -462,29 +462,30 @@ __device__ __forceinline__ void intra_block(int Lb, int T_len, int n_q_heads, in
     T *s_vT = reinterpret_cast<T *>(smem + Lay::O_VT);
     float *s_lz = reinterpret_cast<float *>(smem + Lay::O_LZ);
 
-    // XCD-aware placement: the NQT tiles of one (chunk, sequence x KV head) get block ids
-    // congruent mod 8, i.e. the same XCD, so its K and V are fetched into one L2
+    // A workgroup takes the query tiles pi and NQT - 1 - pi of a chunk: key tiles past the
+    // diagonal are skipped, and every workgroup then has NQT + 1 key tiles of work.
+    // XCD-aware placement: the NQT / 2 workgroups of one (chunk, sequence x KV head) get
+    // block ids congruent mod 8, i.e. the same XCD, so its K and V are fetched into one L2.
+    constexpr int NPAIR = NQT / 2;
     const int xcd = Lb % kXcds, i8 = Lb / kXcds;
-    const int unit = xcd + kXcds * (i8 / NQT), qt = i8 % NQT;
+    const int unit = xcd + kXcds * (i8 / NPAIR), pi = i8 % NPAIR;
     if (unit >= nchunks * n_bkv) return;
     const int c = unit % nchunks, bkv = unit / nchunks;
     const int b = bkv / n_kv_heads, kv = bkv % n_kv_heads;
     const int n_rep = n_q_heads / n_kv_heads, h0 = kv * n_rep;
-    const int pos0 = c * C + qt * 16;
-    if (pos0 >= T_len) return;
+    if (c * C + pi * 16 >= T_len) return;       // the pair's other tile lies further on
     const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
     const int g = lane >> 4, lr = lane & 15;
-    const int qpos = pos0 + lr;
 
-    // this wave's first head's query (row lr of the tile, dims 8g.. and 32 + 8g..), fetched
-    // before the staging
-    auto load_q = [&](int i, OalFrag<T> (&qf)[2]) {
+    // query row lr of tile qt for head i (dims 8g.. and 32 + 8g..)
+    auto load_q = [&](int i, int qt, OalFrag<T> (&qf)[2]) {
+        const int qpos = c * C + qt * 16 + lr;
         const T *qr = q + (((size_t)b * n_q_heads + h0 + i) * T_len + (qpos < T_len ? qpos : 0)) * OAL_D + 8 * g;
         qf[0].load(qr);
         qf[1].load(qr + 32);
     };
     OalFrag<T> qf[2];
-    if (wave < n_rep) load_q(wave, qf);
+    if (wave < n_rep) load_q(wave, pi, qf);     // fetched before the staging
 
     // stage every key of the chunk (zero past T), V^T of them, and Lz rows of every head;
     // all loads are issued before the first LDS write
@@ -538,8 +539,10 @@ __device__ __forceinline__ void intra_block(int Lb, int T_len, int n_q_heads, in
         zeros.set(zz);
     }
     const int ntiles = nchunks * NQT;
-    for (int i = wave; i < n_rep; i += kIntraWaves) {
-        if (i != wave) load_q(i, qf);
+    // one head and query tile: NK = qt + 1 key tiles (compile time)
+    auto tile = [&](auto nk_c, int i, int qt) {
+        constexpr int NK = decltype(nk_c)::value;
+        const int qpos = c * C + qt * 16 + lr;
         const OalHeadDev *hd = head_ptr(params, h0 + i);
         const int G = hd->G;
         const float eps = hd->eps, L00 = hd->L00;
@@ -549,9 +552,9 @@ __device__ __forceinline__ void intra_block(int Lb, int T_len, int n_q_heads, in
             qv[e] = qpos < T_len ? (float)qf[0].v[e] : 0.0f;
             qv[8 + e] = qpos < T_len ? (float)qf[1].v[e] : 0.0f;
         }
-        oal_f32x4 kap[NQT];
+        oal_f32x4 kap[NK + (NK & 1)];          // even count: key tiles go to the MFMA in pairs
 #pragma unroll
-        for (int kt = 0; kt < NQT; ++kt) kap[kt] = oal_splat(eps);
+        for (int kt = 0; kt < NK + (NK & 1); ++kt) kap[kt] = oal_splat(eps);
         for (int m = 0; m <= G; ++m) {
             float lzv[16];
             if (G < kIntraLzr && i < kIntraLzHeads) {
@@ -578,7 +581,7 @@ __device__ __forceinline__ void intra_block(int Lb, int T_len, int n_q_heads, in
             int koff = (lr * QS + 8 * g) * (int)sizeof(T);
             asm volatile("" : "+v"(koff));
 #pragma unroll
-            for (int kt = 0; kt < NQT; ++kt) {
+            for (int kt = 0; kt < NK; ++kt) {
                 const T *kr = reinterpret_cast<const T *>(reinterpret_cast<const unsigned char *>(s_k) + koff) + 16 * kt * QS;
                 OalFrag<T> ak[2];
                 if (EPU == 8) {
@@ -600,17 +603,17 @@ __device__ __forceinline__ void intra_block(int Lb, int T_len, int n_q_heads, in
         }
         // causal mask (key <= query, key < T), then kappa [V;1]
 #pragma unroll
-        for (int kt = 0; kt < NQT; ++kt)
+        for (int kt = 0; kt < NK + (NK & 1); ++kt)
 #pragma unroll
             for (int ii = 0; ii < 4; ++ii) {
                 const int kp = c * C + 16 * kt + 4 * g + ii;
-                if (!(kp <= qpos && kp < T_len)) kap[kt][ii] = 0.0f;
+                if (!(kt < NK && kp <= qpos && kp < T_len)) kap[kt][ii] = 0.0f;
             }
         oal_f32x4 acc[5];
 #pragma unroll
         for (int n = 0; n < 5; ++n) acc[n] = oal_splat(0.0f);
 #pragma unroll
-        for (int p = 0; p < C / 32; ++p) {
+        for (int p = 0; p < (NK + 1) / 2; ++p) {
             float x[8];
 #pragma unroll
             for (int ii = 0; ii < 4; ++ii) {
@@ -633,6 +636,40 @@ __device__ __forceinline__ void intra_block(int Lb, int T_len, int n_q_heads, in
         for (int n = 0; n < 5; ++n)
 #pragma unroll
             for (int ii = 0; ii < 4; ++ii) up[(n * 4 + ii) * 64] = acc[n][ii];
+    };
+    static_assert(NQT % 2 == 0 && NQT <= 16, "tile pairs");
+    for (int i = wave; i < n_rep; i += kIntraWaves) {
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt) {
+            const int qt = tt == 0 ? pi : NQT - 1 - pi;
+            if (c * C + qt * 16 >= T_len) break;
+            if (i != wave || tt == 1) load_q(i, qt, qf);
+            // NK = qt + 1 (the first tile of a pair has qt < NQT / 2, the second qt >= NQT / 2)
+            auto run = [&](auto qt_c) { tile(std::integral_constant<int, decltype(qt_c)::value + 1>{}, i, qt); };
+            if (tt == 0) {
+                switch (qt) {
+                    case 0: run(std::integral_constant<int, 0>{}); break;
+                    case 1: run(std::integral_constant<int, 1 % NQT>{}); break;
+                    case 2: run(std::integral_constant<int, 2 % NQT>{}); break;
+                    case 3: run(std::integral_constant<int, 3 % NQT>{}); break;
+                    case 4: run(std::integral_constant<int, 4 % NQT>{}); break;
+                    case 5: run(std::integral_constant<int, 5 % NQT>{}); break;
+                    case 6: run(std::integral_constant<int, 6 % NQT>{}); break;
+                    default: run(std::integral_constant<int, 7 % NQT>{}); break;
+                }
+            } else {
+                switch (NQT - 1 - qt) {
+                    case 0: run(std::integral_constant<int, NQT - 1>{}); break;
+                    case 1: run(std::integral_constant<int, (NQT - 2 + 16) % 16 % NQT>{}); break;
+                    case 2: run(std::integral_constant<int, (NQT - 3 + 16) % 16 % NQT>{}); break;
+                    case 3: run(std::integral_constant<int, (NQT - 4 + 16) % 16 % NQT>{}); break;
+                    case 4: run(std::integral_constant<int, (NQT - 5 + 16) % 16 % NQT>{}); break;
+                    case 5: run(std::integral_constant<int, (NQT - 6 + 16) % 16 % NQT>{}); break;
+                    case 6: run(std::integral_constant<int, (NQT - 7 + 16) % 16 % NQT>{}); break;
+                    default: run(std::integral_constant<int, (NQT - 8 + 16) % 16 % NQT>{}); break;
+                }
+            }
+        }
     }
 }
 
@@ -1036,7 +1073,7 @@ hipError_t launch_all(const oal_dims &d, int T_len, const void *q, const void *k
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds)) != hipSuccess)
             return e;
         const int nunits = p.nchunks * bkv;
-        const int n_intra = kXcds * (C / 16) * ((nunits + kXcds - 1) / kXcds);
+        const int n_intra = kXcds * (C / 32) * ((nunits + kXcds - 1) / kXcds);   // tile pairs
         const int n_delta = (kScanBlocks + 1) * p.nchunks * bkv;
         hipLaunchKernelGGL(kern, dim3(n_intra + n_delta), dim3(64 * kIntraWaves), lds, stream, T_len,
                            d.n_q_heads, d.n_kv_heads, p.nchunks, bkv, n_delta, reinterpret_cast<const T *>(q),
