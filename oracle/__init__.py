@@ -10,7 +10,9 @@ Wraps ``oal_oracle.c`` (fp64 loops, OpenMP over output rows) through ctypes:
 * ``dense_rows``  -- the same definition for selected rows (b, h, i);
 * ``kappa``/``kappa_matrix`` -- kappa = eps + ||L^T s-bar||^2 for pairs;
 * ``recurrence``  -- the H0/H1/H2 recurrence of the same section with full d x d H2;
-* ``state``       -- the prefix states with H2 as an upper triangle (the library's layout).
+* ``state``       -- the prefix states with H2 as an upper triangle (the library's layout);
+* ``contribution`` -- the causal contribution score chi of every q/k dim per prompt and its
+                     mean over prompts (same section, first display), O(T^2) over pairs.
 """
 from __future__ import annotations
 
@@ -51,6 +53,7 @@ def _load():
         lib.oal_oracle_kappa.argtypes = [I, I, I, P, P, ctypes.c_double, P, P]
         lib.oal_oracle_kappa.restype = ctypes.c_double
         lib.oal_oracle_kappa_matrix.argtypes = [I, I, I, I, I, P, P, P, P, I, P, P, I, I, P]
+        lib.oal_oracle_contribution.argtypes = [I, I, I, I, I, P, P, P, P]
         lib.oal_oracle_num_threads.restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -164,6 +167,24 @@ def kappa_matrix(q, k, params, b: int, h: int):
     if rc:
         raise ValueError(f"oal_oracle_kappa_matrix: bad arguments (code {rc})")
     return kap
+
+
+def contribution(q, k):
+    """chi [B,Hq,d] and chi_mean [Hq,d] (fp64): mean over the T(T+1)/2 causal pairs of
+    |q_ir k_jr| / sqrt(d) per prompt, query head and dim; chi_mean averages over prompts."""
+    lib = _load()
+    q, k = _f64(q), _f64(k)
+    B, Hq, T, d = q.shape
+    Hkv = k.shape[1]
+    if k.shape != (B, Hkv, T, d):
+        raise ValueError("contribution: k must be [B, Hkv, T, d] with q's B, T, d")
+    chi = np.empty((B, Hq, d))
+    chi_mean = np.empty((Hq, d))
+    rc = lib.oal_oracle_contribution(B, Hq, Hkv, T, d, _ptr(q), _ptr(k), _ptr(chi),
+                                     _ptr(chi_mean))
+    if rc:
+        raise ValueError(f"oal_oracle_contribution: bad arguments (code {rc})")
+    return chi, chi_mean
 
 
 def row_error(y, y_ref):

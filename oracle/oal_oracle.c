@@ -282,3 +282,44 @@ int oal_oracle_state(int B, int Hkv, int T, int d, int dv, const double *k, cons
     }
     return 0;
 }
+
+/*
+ * Causal contribution score of every q/k dim (section "核心公式", first display; the
+ * "逐 prompt 因果贡献统计" node of the flowchart), for each prompt p (a sequence of the
+ * batch) and query head h with KV head kv = h / (Hq / Hkv):
+ *   chi[p,h,r]   = (1/|Omega_p|) * sum over causal pairs (i, j <= i) of |q[p,h,i,r] k[p,kv,j,r] / sqrt(d)|
+ *   chi_mean[h,r] = (1/B) * sum_p chi[p,h,r]
+ * |Omega_p| is read as the number of causal pairs of the prompt, T (T+1) / 2. The sum is
+ * the plain double loop over pairs, O(T^2 d) per (p, h).
+ *   q [B, Hq, T, d], k [B, Hkv, T, d]; chi [B, Hq, d] out; chi_mean [Hq, d] out (may be NULL).
+ */
+int oal_oracle_contribution(int B, int Hq, int Hkv, int T, int d, const double *q,
+                            const double *k, double *chi, double *chi_mean) {
+    if (B < 1 || Hq <= 0 || Hkv <= 0 || T < 1 || d <= 0 || d > 64) return 1;
+    if (Hq % Hkv) return 2;
+    int rep = Hq / Hkv;
+    double n_pairs = (double)T * (double)(T + 1) / 2.0;
+    double sqrt_d = sqrt((double)d);
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int bh = 0; bh < B * Hq; ++bh) {
+        int b = bh / Hq, h = bh % Hq, kv = h / rep;
+        const double *qb = q + (size_t)bh * T * d;
+        const double *kb = k + ((size_t)b * Hkv + kv) * T * d;
+        double acc[64];
+        for (int r = 0; r < d; ++r) acc[r] = 0.0;
+        for (int i = 0; i < T; ++i)
+            for (int j = 0; j <= i; ++j)
+                for (int r = 0; r < d; ++r)
+                    acc[r] += fabs(qb[(size_t)i * d + r] * kb[(size_t)j * d + r] / sqrt_d);
+        for (int r = 0; r < d; ++r) chi[(size_t)bh * d + r] = acc[r] / n_pairs;
+    }
+    if (chi_mean) {
+        for (int h = 0; h < Hq; ++h)
+            for (int r = 0; r < d; ++r) {
+                double s = 0.0;
+                for (int b = 0; b < B; ++b) s += chi[((size_t)b * Hq + h) * d + r];
+                chi_mean[(size_t)h * d + r] = s / B;
+            }
+    }
+    return 0;
+}

@@ -280,3 +280,143 @@ def test_pins_catch_planted_mistakes(name, tmp_path):
         assert not ok, f"planted mistake {name} passed the worked-example pin"
     finally:
         oracle._lib = saved
+
+
+# --------------------------------------------------------------------------------------
+# 11. Causal contribution score chi (section "核心公式", first display): the mean over the
+# T(T+1)/2 causal pairs of |q_ir k_jr| / sqrt(d), per prompt, query head and dim, and its
+# mean over prompts. The oracle is the double loop over pairs; the pins below fix it by a
+# hand-worked example, closed forms and an independent factorisation.
+
+_CGOLD = _json.load(open(os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden",
+                                      "contribution_example_d4.json")))
+CQ = np.array(_CGOLD["q"], float)[:, None]
+CK = np.array(_CGOLD["k"], float)[:, None]
+
+
+def test_contribution_worked_example_by_hand():
+    # Catches: a dropped absolute value, anti-causal or all-pairs sums, a T^2 normaliser,
+    # a missing 1/sqrt(d), a wrong prompt average.
+    chi, chi_mean = oracle.contribution(CQ, CK)
+    np.testing.assert_allclose(chi[:, 0], _CGOLD["chi"], rtol=0, atol=1e-15)
+    np.testing.assert_allclose(chi_mean[0], _CGOLD["chi_mean"], rtol=0, atol=1e-15)
+
+
+def test_contribution_constant_inputs_closed_form():
+    # q_ir = a_r and k_jr = c_r for every token: every pair contributes |a_r c_r| / sqrt(d),
+    # so the mean over pairs is that value whatever T is (catches any normaliser other
+    # than the pair count, and a missing or doubled 1/sqrt(d)).
+    rng = np.random.default_rng(3)
+    d = 16
+    a, c = rng.standard_normal(d), rng.standard_normal(d)
+    for T in (1, 2, 7, 40):
+        q = np.broadcast_to(a, (1, 1, T, d)).copy()
+        k = np.broadcast_to(c, (1, 1, T, d)).copy()
+        chi, _ = oracle.contribution(q, k)
+        np.testing.assert_allclose(chi[0, 0], np.abs(a * c) / 4.0, rtol=1e-13, atol=0)
+
+
+def test_contribution_matches_prefix_factorisation():
+    # Independent evaluation: sum_{j<=i} |q_ir k_jr| = |q_ir| * (inclusive prefix sum of
+    # |k_jr|), summed over i (a cumulative sum instead of the pair loop).
+    rng = np.random.default_rng(4)
+    B, Hq, Hkv, T, d = 2, 6, 2, 33, 8
+    q = rng.standard_normal((B, Hq, T, d))
+    k = rng.standard_normal((B, Hkv, T, d))
+    chi, chi_mean = oracle.contribution(q, k)
+    kpre = np.cumsum(np.abs(k), axis=2)
+    kv_of = np.arange(Hq) // (Hq // Hkv)
+    ref = (np.abs(q) * kpre[:, kv_of]).sum(axis=2) / np.sqrt(d) / (T * (T + 1) / 2)
+    np.testing.assert_allclose(chi, ref, rtol=1e-13, atol=0)
+    np.testing.assert_allclose(chi_mean, ref.mean(axis=0), rtol=1e-13, atol=0)
+
+
+def test_contribution_single_token_and_causality():
+    # T = 1: the only pair is (0, 0). Changing k at the last position changes only the pair
+    # (T-1, T-1): the difference is |q_{T-1}| * (|k'| - |k|) / sqrt(d) / |Omega|.
+    rng = np.random.default_rng(5)
+    q = rng.standard_normal((1, 1, 1, 8))
+    k = rng.standard_normal((1, 1, 1, 8))
+    chi, _ = oracle.contribution(q, k)
+    np.testing.assert_allclose(chi[0, 0], np.abs(q[0, 0, 0] * k[0, 0, 0]) / np.sqrt(8), rtol=1e-15)
+    T = 10
+    q = rng.standard_normal((1, 1, T, 8))
+    k = rng.standard_normal((1, 1, T, 8))
+    k2 = k.copy()
+    k2[0, 0, T - 1] *= 3.0
+    c1, _ = oracle.contribution(q, k)
+    c2, _ = oracle.contribution(q, k2)
+    expect = np.abs(q[0, 0, T - 1]) * 2.0 * np.abs(k[0, 0, T - 1]) / np.sqrt(8) / (T * (T + 1) / 2)
+    np.testing.assert_allclose(c2[0, 0] - c1[0, 0], expect, rtol=1e-10, atol=1e-15)
+
+
+def test_contribution_invariances():
+    # Sign flips of q or k entries leave chi unchanged, scaling q by s scales it by |s|,
+    # and permuting the dims permutes it.
+    rng = np.random.default_rng(6)
+    q = rng.standard_normal((2, 2, 9, 8))
+    k = rng.standard_normal((2, 1, 9, 8))
+    chi, _ = oracle.contribution(q, k)
+    sq = rng.choice([-1.0, 1.0], size=q.shape)
+    sk = rng.choice([-1.0, 1.0], size=k.shape)
+    np.testing.assert_allclose(oracle.contribution(q * sq, k * sk)[0], chi, rtol=1e-14)
+    np.testing.assert_allclose(oracle.contribution(-2.5 * q, k)[0], 2.5 * chi, rtol=1e-14)
+    perm = rng.permutation(8)
+    np.testing.assert_allclose(oracle.contribution(q[..., perm], k[..., perm])[0], chi[..., perm],
+                               rtol=1e-14)
+
+
+def test_contribution_gqa_map_closed_form():
+    # Query head h reads KV head h // (Hq/Hkv): with q = 1 and KV head m's keys all equal
+    # to m+1, chi of head h is (h // rep + 1) / sqrt(d) in every dim.
+    Hq, Hkv, T, d = 6, 3, 5, 4
+    q = np.ones((1, Hq, T, d))
+    k = np.stack([np.full((T, d), m + 1.0) for m in range(Hkv)])[None]
+    chi, _ = oracle.contribution(q, k)
+    expect = (np.arange(Hq) // (Hq // Hkv) + 1.0) / 2.0
+    np.testing.assert_allclose(chi[0], np.repeat(expect[:, None], d, axis=1), rtol=1e-15)
+
+
+CHI_MUTATIONS = {
+    "chi_no_abs": ("acc[r] += fabs(qb[(size_t)i * d + r] * kb[(size_t)j * d + r] / sqrt_d);",
+                   "acc[r] += (qb[(size_t)i * d + r] * kb[(size_t)j * d + r] / sqrt_d);"),
+    "chi_anticausal": ("for (int j = 0; j <= i; ++j)\n                for (int r = 0; r < d; ++r)\n"
+                       "                    acc[r] +=",
+                       "for (int j = i; j < T; ++j)\n                for (int r = 0; r < d; ++r)\n"
+                       "                    acc[r] +="),
+    "chi_square_norm": ("double n_pairs = (double)T * (double)(T + 1) / 2.0;",
+                        "double n_pairs = (double)T * (double)T;"),
+    "chi_no_sqrt_d": ("double sqrt_d = sqrt((double)d);", "double sqrt_d = 1.0;"),
+    "chi_gqa_modulo": ("int b = bh / Hq, h = bh % Hq, kv = h / rep;",
+                       "int b = bh / Hq, h = bh % Hq, kv = h % Hkv;"),
+    "chi_mean_sum": ("chi_mean[(size_t)h * d + r] = s / B;", "chi_mean[(size_t)h * d + r] = s;"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(CHI_MUTATIONS))
+def test_contribution_pins_catch_planted_mistakes(name, tmp_path):
+    if shutil.which("gcc") is None:
+        pytest.skip("gcc not available")
+    src = open(oracle._SRC).read()
+    old, new = CHI_MUTATIONS[name]
+    assert src.count(old) == 1, f"mutation anchor for {name} not found"
+    mfile = tmp_path / "mut.c"
+    mfile.write_text(src.replace(old, new))
+    so = tmp_path / "libmut.so"
+    subprocess.check_call(["gcc", "-O1", "-fPIC", "-shared", "-o", str(so), str(mfile), "-lm"])
+    lib = ctypes.CDLL(str(so))
+    saved = oracle._lib
+    try:
+        oracle._lib = None
+        real = oracle._load()
+        lib.oal_oracle_contribution.argtypes = real.oal_oracle_contribution.argtypes
+        oracle._lib = lib
+        failed = []
+        for test in (test_contribution_worked_example_by_hand, test_contribution_gqa_map_closed_form):
+            try:
+                test()
+            except AssertionError:
+                failed.append(test.__name__)
+        assert failed, f"planted mistake {name} passed the contribution pins"
+    finally:
+        oracle._lib = saved
