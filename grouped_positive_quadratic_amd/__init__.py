@@ -23,7 +23,8 @@ STATUS = {0: "OAL_OK", 1: "OAL_E_ARG", 2: "OAL_E_SHAPE", 3: "OAL_E_DTYPE", 4: "O
 EXPORTED = ("oal_params_bytes", "oal_state_bytes", "oal_prefill_workspace_bytes",
             "oal_decode_workspace_bytes", "oal_params_pack", "oal_state_init", "oal_prefill",
             "oal_prefill_timed", "oal_decode_step", "oal_status_string", "oal_timing_event_create",
-            "oal_timing_event_destroy", "oal_timing_event_record", "oal_timing_elapsed_ms")
+            "oal_timing_event_destroy", "oal_timing_event_record", "oal_timing_elapsed_ms",
+            "oal_contribution_workspace_bytes", "oal_contribution")
 
 
 class OALError(RuntimeError):
@@ -74,6 +75,9 @@ def _load():
     lib.oal_timing_event_record.argtypes, lib.oal_timing_event_record.restype = [P, P], ctypes.c_int
     lib.oal_timing_elapsed_ms.argtypes = [P, P, ctypes.POINTER(ctypes.c_float)]
     lib.oal_timing_elapsed_ms.restype = ctypes.c_int
+    lib.oal_contribution_workspace_bytes.argtypes = [dp, I]
+    lib.oal_contribution_workspace_bytes.restype = S
+    lib.oal_contribution.argtypes, lib.oal_contribution.restype = [dp, I, P, P, P, P, P, P], ctypes.c_int
     return lib
 
 
@@ -214,6 +218,18 @@ def oal_decode_step(dims: oal_dims, q, k, v, params_dev, state_dev, workspace, y
     _check("oal_decode_step", _lib.oal_decode_step(ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v),
                                                    _ptr(params_dev), _ptr(state_dev),
                                                    _ptr(workspace), _ptr(y), _stream(stream)))
+
+
+def oal_contribution_workspace_bytes(dims: oal_dims, T: int) -> int:
+    return int(_lib.oal_contribution_workspace_bytes(ctypes.byref(dims), int(T)))
+
+
+def oal_contribution(dims: oal_dims, T: int, q, k, workspace, chi, chi_mean=None, stream=None):
+    """Causal contribution scores chi [batch, n_q_heads, 64] and (unless chi_mean is None)
+    their prompt mean [n_q_heads, 64], both fp32 device tensors written by the library."""
+    _check("oal_contribution", _lib.oal_contribution(ctypes.byref(dims), int(T), _ptr(q), _ptr(k),
+                                                     _ptr(workspace), _ptr(chi), _ptr(chi_mean),
+                                                     _stream(stream)))
 
 
 # ---- buffer helper (torch allocations sized by the library) ------------------------------

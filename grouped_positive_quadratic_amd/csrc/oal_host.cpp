@@ -21,6 +21,9 @@ hipError_t oal_launch_prefill(const oal_dims &d, int T_len, int C, const void *q
                               const void *v, const void *params, float *state, void *ws, float *y,
                               hipStream_t stream, hipEvent_t *marks);
 size_t oal_decode_ws_bytes_impl(const oal_dims &d);
+hipError_t oal_launch_contribution(const oal_dims &d, int T_len, const void *q, const void *k, void *ws,
+                                   float *chi, float *chi_mean, hipStream_t stream);
+size_t oal_contribution_ws_bytes_impl(const oal_dims &d, int T_len);
 size_t oal_prefill_ws_bytes_impl(const oal_dims &d, int T_len, int C);
 
 namespace {
@@ -324,6 +327,28 @@ oal_status oal_decode_step(const oal_dims *d, const void *q, const void *k, cons
         !aligned16(state_dev) || !aligned16(workspace) || !aligned16(y))
         return OAL_E_ALIGN;
     hipError_t e = oal_launch_decode(*d, q, k, v, params_dev, state_dev, workspace, y, stream);
+    if (e != hipSuccess) {
+        (void)hipGetLastError();
+        return OAL_E_HIP;
+    }
+    return OAL_OK;
+}
+
+size_t oal_contribution_workspace_bytes(const oal_dims *d, int32_t T) {
+    if (check_dims(d) != OAL_OK || T < 1 || d->batch < 1) return 0;
+    return oal_contribution_ws_bytes_impl(*d, T);
+}
+
+oal_status oal_contribution(const oal_dims *d, int32_t T, const void *q, const void *k,
+                            void *workspace, float *chi, float *chi_mean, hipStream_t stream) {
+    oal_status st = check_dims(d);
+    if (st != OAL_OK) return st;
+    if (T < 1 || d->batch < 1) return OAL_E_SHAPE;
+    if (!q || !k || !workspace || !chi) return OAL_E_ARG;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(workspace) || !aligned16(chi) ||
+        (chi_mean && !aligned16(chi_mean)))
+        return OAL_E_ALIGN;
+    hipError_t e = oal_launch_contribution(*d, T, q, k, workspace, chi, chi_mean, stream);
     if (e != hipSuccess) {
         (void)hipGetLastError();
         return OAL_E_HIP;

@@ -155,6 +155,28 @@ oal_status oal_decode_step(const oal_dims *dims, const void *q, const void *k, c
                            const void *params_dev, float *state_dev, void *workspace, float *y,
                            hipStream_t stream);
 
+/* Causal contribution scores of the q/k dims (reproduction notes, section "核心公式", first
+ * display; the per-prompt causal statistics that feed the tail grouping in the method's
+ * flowchart). For every prompt p (a sequence of the batch), query head h (KV head
+ * kv = h / (n_q_heads / n_kv_heads)) and dim r:
+ *   chi[p,h,r]    = (1/|Omega_p|) sum_{i} sum_{j<=i} |q[p,h,i,r] k[p,kv,j,r]| / sqrt(d_h),
+ *                   |Omega_p| = T (T+1) / 2, the number of causal pairs of the prompt;
+ *   chi_mean[h,r] = (1/batch) sum_p chi[p,h,r]   (the average over prompts).
+ * The pair sum is evaluated in linear time as sum_i |q_ir| * (prefix sum of |k_jr| up to i),
+ * in fp32.
+ *   T          -- tokens per prompt (equal lengths), >= 1.
+ *   q, k       -- [batch, n_q_heads, T, 64] and [batch, n_kv_heads, T, 64] of dims->dtype
+ *                 (device). v is not involved; dims->d_v must still be valid (64).
+ *   workspace  -- oal_contribution_workspace_bytes(dims, T) bytes of device scratch (per-chunk
+ *                 partial sums); its contents on entry do not matter.
+ *   chi        -- [batch, n_q_heads, 64] fp32 out (device).
+ *   chi_mean   -- [n_q_heads, 64] fp32 out (device), or NULL to skip the prompt average.
+ * batch >= 1 and T >= 1 are required (OAL_E_SHAPE otherwise): the averages are over a
+ * non-empty set. */
+size_t oal_contribution_workspace_bytes(const oal_dims *dims, int32_t T);
+oal_status oal_contribution(const oal_dims *dims, int32_t T, const void *q, const void *k,
+                            void *workspace, float *chi, float *chi_mean, hipStream_t stream);
+
 /* Timing events for oal_prefill_timed and for bracketing a timed region. A default HIP event
  * performs a system-scope release when it is recorded, which writes back the L2: between two
  * kernels that leave many dirty lines that costs several microseconds and would be counted

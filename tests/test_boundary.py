@@ -42,6 +42,13 @@ def test_sizes():
     bad = gpq.make_dims(1, 14, 3, "bf16")
     assert gpq.oal_state_bytes(bad) == 0
     assert gpq.oal_decode_workspace_bytes(gpq.make_dims(1, 17, 1, "bf16")) == 0
+    # contribution scores: per (sequence, KV head, 64-token chunk) a K sum and per query
+    # head two 64-float partials
+    assert gpq.oal_contribution_workspace_bytes(d, 4096) == 3 * 2 * 64 * (1 + 2 * 7) * 64 * 4
+    assert gpq.oal_contribution_workspace_bytes(d, 65) == 3 * 2 * 2 * 15 * 64 * 4
+    assert gpq.oal_contribution_workspace_bytes(d, 0) == 0
+    assert gpq.oal_contribution_workspace_bytes(gpq.make_dims(0, 14, 2, "bf16"), 64) == 0
+    assert gpq.oal_contribution_workspace_bytes(bad, 64) == 0
 
 
 def _code(fn, *args):
@@ -70,6 +77,15 @@ def test_validation_errors_enqueue_nothing():
     assert _code(gpq.oal_decode_step, d, A, A, A, A + 8, A, A, A, 0) == 4
     assert _code(gpq.oal_decode_step, gpq.make_dims(1, 17, 1, "bf16"), *([A] * 7), 0) == 5
     assert _code(gpq.oal_decode_step, gpq.make_dims(0, 2, 1, "bf16"), *([None] * 7), 0) == 0
+    c4 = (A, A, A, A, A)   # q, k, workspace, chi, chi_mean
+    assert _code(gpq.oal_contribution, d, 0, *c4, 0) == 2                  # T < 1
+    assert _code(gpq.oal_contribution, gpq.make_dims(0, 2, 1, "bf16"), 8, *c4, 0) == 2
+    assert _code(gpq.oal_contribution, d, 8, None, A, A, A, A, 0) == 1
+    assert _code(gpq.oal_contribution, d, 8, A, A, None, A, None, 0) == 1  # no workspace
+    assert _code(gpq.oal_contribution, d, 8, A, A, A, A + 4, A, 0) == 4
+    assert _code(gpq.oal_contribution, d, 8, A, A, A, A, A + 4, 0) == 4
+    assert _code(gpq.oal_contribution, gpq.make_dims(1, 2, 1, 7), 8, *c4, 0) == 3
+    assert _code(gpq.oal_contribution, gpq.make_dims(1, 2, 1, "bf16", d_h=32), 8, *c4, 0) == 5
 
 
 def test_param_validation():
