@@ -10,10 +10,13 @@ Decode: 64 sequences whose prefix states were built by oal_prefill from 4096 syn
 tokens each; then --warmup untimed and --decode-steps timed oal_decode_step calls (one token
 per sequence each).
 
+Contribution scores: oal_contribution (the per-dim causal statistic chi and its prompt
+mean) over a calibration batch of 8 prompts x 4096 tokens, timed over 50 back-to-back calls.
+
 Prints one JSON line. `value` is prefill tokens/s; `roofline` is the readout kernel
 (the dominant one) against the bf16 MFMA peak; `decode` holds decode tokens/s and the
-decode kernel against HBM peak; `cpu_baseline` is the fp64 CPU oracle on the full prefill
-batch, timed on this host.
+decode kernel against HBM peak; `contribution` the chi kernel against HBM peak;
+`cpu_baseline` is the fp64 CPU oracle on the full prefill batch, timed on this host.
 """
 from __future__ import annotations
 
@@ -45,6 +48,8 @@ def parse():
     ap.add_argument("--decode-steps", type=int, default=256)
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-contribution", action="store_true",
+                    help="skip the contribution-score (chi) measurement")
     ap.add_argument("--no-scaling", action="store_true",
                     help="skip the B=8 x T=4096 chunk sweep and the T=32768 prefill")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -171,6 +176,14 @@ def main():
     del q, k, v, y, ws, state, params
     torch.cuda.empty_cache()
 
+    cache = {}
+
+    def get_cfg3():
+        if "cfg3" not in cache:
+            from oal_synth import cfg3
+            cache["cfg3"] = cfg3()
+        return cache["cfg3"]
+
     # ---------------- the other prefill workloads (context, not the headline) ----------------
     if not args.no_scaling:
         def prefill_rate(inp, C, reps):
@@ -191,13 +204,12 @@ def main():
             del px, sx, wx, qx, kx, vx, yx
             torch.cuda.empty_cache()
             return Bx * Tx / (ms * 1e-3), ms
-        from oal_synth import cfg3, cfg4
-        c3 = cfg3()
+        from oal_synth import cfg4
+        c3 = get_cfg3()
         batch8 = {}
         for C in (64, 128, 256):
             r, ms = prefill_rate(c3, C, 5)
             batch8[f"chunk{C}"] = {"tokens_per_s": r, "ms_per_call": ms}
-        del c3
         c4 = cfg4()
         r4, ms4 = prefill_rate(c4, 128, 3)
         del c4
@@ -207,6 +219,40 @@ def main():
                           "ms_per_call": ms4,
                           "vs_T4096_tokens_per_s": r4 / out["value"]},
         }
+
+    # ---------------- contribution scores (chi) on a calibration batch ----------------
+    if not args.no_contribution:
+        c3 = get_cfg3()
+        Bc, Hqc, Hkvc, Tc, _, _ = c3.dims
+        cd = gpq.make_dims(Bc, Hqc, Hkvc, "bf16")
+        cq, ck = (torch.from_numpy(a).to(torch.bfloat16).to(dev).contiguous() for a in (c3.q, c3.k))
+        cws = torch.empty(gpq.oal_contribution_workspace_bytes(cd, Tc), dtype=torch.uint8, device=dev)
+        chi = torch.empty((Bc, Hqc, D), dtype=torch.float32, device=dev)
+        chi_mean = torch.empty((Hqc, D), dtype=torch.float32, device=dev)
+        for _ in range(3):
+            gpq.oal_contribution(cd, Tc, cq, ck, cws, chi, chi_mean)
+        torch.cuda.synchronize()
+        reps = 50
+        e0, e1 = gpq.TimingEvent(), gpq.TimingEvent()
+        e0.record(stream)
+        for _ in range(reps):
+            gpq.oal_contribution(cd, Tc, cq, ck, cws, chi, chi_mean)
+        e1.record(stream)
+        cms = e0.elapsed_time(e1) / reps
+        cbytes = (Bc * (Hqc + Hkvc) * Tc * D * 2          # q and k read once
+                  + (Bc * Hqc + Hqc) * D * 4)              # chi and its prompt mean written
+        cach = cbytes / (cms * 1e-3) / 1e9
+        out["contribution"] = {
+            "workload": f"causal contribution scores chi, B={Bc} prompts x T={Tc}, {Hqc}q/{Hkvc}kv, bf16",
+            "value": Bc * Tc / (cms * 1e-3), "unit": "tokens/s", "ms_per_call": cms, "calls": reps,
+            "roofline": {"bound": "hbm", "kernel": "oal_chi_kernel (the call's one launch)",
+                         "achieved": cach, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                         "frac": cach / PEAK_HBM_GBS,
+                         "traffic": measured_traffic(tj, f"contribution_B{Bc}_T{Tc}"),
+                         "algorithmic_bytes_per_launch": cbytes}}
+        del cq, ck, cws, chi, chi_mean
+        torch.cuda.empty_cache()
+    cache.clear()
 
     # ---------------- decode ----------------
     if not args.no_decode:

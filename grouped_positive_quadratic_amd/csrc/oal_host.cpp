@@ -335,7 +335,7 @@ oal_status oal_decode_step(const oal_dims *d, const void *q, const void *k, cons
 }
 
 size_t oal_contribution_workspace_bytes(const oal_dims *d, int32_t T) {
-    if (check_dims(d) != OAL_OK || T < 1 || d->batch < 1) return 0;
+    if (check_dims(d) != OAL_OK || T < 1 || T > OAL_CHI_MAX_T || d->batch < 1) return 0;
     return oal_contribution_ws_bytes_impl(*d, T);
 }
 
@@ -344,6 +344,7 @@ oal_status oal_contribution(const oal_dims *d, int32_t T, const void *q, const v
     oal_status st = check_dims(d);
     if (st != OAL_OK) return st;
     if (T < 1 || d->batch < 1) return OAL_E_SHAPE;
+    if (T > OAL_CHI_MAX_T) return OAL_E_UNSUPPORTED;
     if (!q || !k || !workspace || !chi) return OAL_E_ARG;
     if (!aligned16(q) || !aligned16(k) || !aligned16(workspace) || !aligned16(chi) ||
         (chi_mean && !aligned16(chi_mean)))

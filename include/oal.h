@@ -149,8 +149,10 @@ oal_status oal_prefill_timed(const oal_dims *dims, int32_t T, int32_t chunk, con
  *   state_dev updated in place; y [batch, n_q_heads, 64] fp32.
  *   workspace -- oal_decode_workspace_bytes(dims) bytes of device scratch that must be
  *                zero-filled before its first use and then left to the library: every call
- *                returns its counters to zero. Calls that share a workspace must be ordered
- *                (same stream or synchronised). */
+ *                returns its counters to zero. The layout depends on dims: a workspace
+ *                serves calls of one shape, and must be zero-filled again before it serves
+ *                another. Calls that share a workspace must be ordered (same stream or
+ *                synchronised). */
 oal_status oal_decode_step(const oal_dims *dims, const void *q, const void *k, const void *v,
                            const void *params_dev, float *state_dev, void *workspace, float *y,
                            hipStream_t stream);
@@ -163,16 +165,23 @@ oal_status oal_decode_step(const oal_dims *dims, const void *q, const void *k, c
  *                   |Omega_p| = T (T+1) / 2, the number of causal pairs of the prompt;
  *   chi_mean[h,r] = (1/batch) sum_p chi[p,h,r]   (the average over prompts).
  * The pair sum is evaluated in linear time as sum_i |q_ir| * (prefix sum of |k_jr| up to i),
- * in fp32.
+ * in fp32, in a fixed order (repeated calls give identical bits).
  *   T          -- tokens per prompt (equal lengths), >= 1.
  *   q, k       -- [batch, n_q_heads, T, 64] and [batch, n_kv_heads, T, 64] of dims->dtype
  *                 (device). v is not involved; dims->d_v must still be valid (64).
- *   workspace  -- oal_contribution_workspace_bytes(dims, T) bytes of device scratch (per-chunk
- *                 partial sums); its contents on entry do not matter.
+ *   workspace  -- oal_contribution_workspace_bytes(dims, T) bytes of device scratch (arrival
+ *                 counters and per-range partial sums) that must be zero-filled before its
+ *                 first use and then left to the library: every call returns its counters to
+ *                 zero (the partial sums need no initialisation). The layout depends on
+ *                 dims and T: a workspace serves calls of one shape, and must be zero-filled
+ *                 again before it serves another. Calls that share a workspace must be
+ *                 ordered (same stream or synchronised).
  *   chi        -- [batch, n_q_heads, 64] fp32 out (device).
  *   chi_mean   -- [n_q_heads, 64] fp32 out (device), or NULL to skip the prompt average.
  * batch >= 1 and T >= 1 are required (OAL_E_SHAPE otherwise): the averages are over a
- * non-empty set. */
+ * non-empty set. T > OAL_CHI_MAX_T gives OAL_E_UNSUPPORTED (a sequence's rows are addressed
+ * with 32-bit byte offsets). */
+#define OAL_CHI_MAX_T (1 << 22)
 size_t oal_contribution_workspace_bytes(const oal_dims *dims, int32_t T);
 oal_status oal_contribution(const oal_dims *dims, int32_t T, const void *q, const void *k,
                             void *workspace, float *chi, float *chi_mean, hipStream_t stream);

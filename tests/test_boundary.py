@@ -42,10 +42,13 @@ def test_sizes():
     bad = gpq.make_dims(1, 14, 3, "bf16")
     assert gpq.oal_state_bytes(bad) == 0
     assert gpq.oal_decode_workspace_bytes(gpq.make_dims(1, 17, 1, "bf16")) == 0
-    # contribution scores: per (sequence, KV head, 64-token chunk) a K sum and per query
-    # head two 64-float partials
-    assert gpq.oal_contribution_workspace_bytes(d, 4096) == 3 * 2 * 64 * (1 + 2 * 7) * 64 * 4
-    assert gpq.oal_contribution_workspace_bytes(d, 65) == 3 * 2 * 2 * 15 * 64 * 4
+    # contribution scores: arrival counters, one 128-byte line per (sequence, query head) and
+    # per query head, then per (sequence, query head, 512-token range) three 64-float
+    # partials (bf16; 256-token ranges for fp32)
+    cb = (3 * 14 + 14) * 128
+    assert gpq.oal_contribution_workspace_bytes(d, 4096) == cb + 3 * 14 * 8 * 3 * 64 * 4
+    assert gpq.oal_contribution_workspace_bytes(d, 65) == cb + 3 * 14 * 1 * 3 * 64 * 4
+    assert gpq.oal_contribution_workspace_bytes(gpq.make_dims(3, 14, 2, "f32"), 4096) == cb + 3 * 14 * 16 * 3 * 64 * 4
     assert gpq.oal_contribution_workspace_bytes(d, 0) == 0
     assert gpq.oal_contribution_workspace_bytes(gpq.make_dims(0, 14, 2, "bf16"), 64) == 0
     assert gpq.oal_contribution_workspace_bytes(bad, 64) == 0
@@ -79,6 +82,8 @@ def test_validation_errors_enqueue_nothing():
     assert _code(gpq.oal_decode_step, gpq.make_dims(0, 2, 1, "bf16"), *([None] * 7), 0) == 0
     c4 = (A, A, A, A, A)   # q, k, workspace, chi, chi_mean
     assert _code(gpq.oal_contribution, d, 0, *c4, 0) == 2                  # T < 1
+    assert _code(gpq.oal_contribution, d, (1 << 22) + 1, *c4, 0) == 5      # above the max T
+    assert gpq.oal_contribution_workspace_bytes(d, (1 << 22) + 1) == 0
     assert _code(gpq.oal_contribution, gpq.make_dims(0, 2, 1, "bf16"), 8, *c4, 0) == 2
     assert _code(gpq.oal_contribution, d, 8, None, A, A, A, A, 0) == 1
     assert _code(gpq.oal_contribution, d, 8, A, A, None, A, None, 0) == 1  # no workspace

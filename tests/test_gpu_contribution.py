@@ -46,10 +46,12 @@ def run_chi(q, k, dtype, with_mean=True, ws_fill=None):
     dims = gpq.make_dims(B, Hq, Hkv, dtype)
     qd = q if isinstance(q, torch.Tensor) else to_dev(q, dtype)
     kd = k if isinstance(k, torch.Tensor) else to_dev(k, dtype)
-    ws = torch.empty(max(gpq.oal_contribution_workspace_bytes(dims, T), 16), dtype=torch.uint8,
+    ws = torch.zeros(max(gpq.oal_contribution_workspace_bytes(dims, T), 16), dtype=torch.uint8,
                      device="cuda")
     if ws_fill is not None:
-        ws.view(torch.float32)[: ws.numel() // 4].fill_(ws_fill)
+        # only the arrival counters (a 128-byte line per (prompt, head) and per head) must start at zero
+        cbytes = -(-(B * Hq + Hq) * 128 // 256) * 256
+        ws[cbytes:].view(torch.float32).fill_(ws_fill)
     chi = torch.empty((B, Hq, 64), dtype=torch.float32, device="cuda")
     chi_mean = torch.empty((Hq, 64), dtype=torch.float32, device="cuda") if with_mean else None
     gpq.oal_contribution(dims, T, qd, kd, ws, chi, chi_mean)
@@ -76,7 +78,29 @@ def test_contribution_small(shape, dtype):
     assert e <= chi_tol(T) and em <= chi_tol(T, B)
 
 
-def test_contribution_workspace_contents_do_not_matter_and_repeat_bitwise():
+def test_contribution_workspace_reuse_and_repeat_bitwise():
+    # one workspace serves successive calls of one shape (new data each time): the partial
+    # sums may hold anything on entry and the counters come back to zero after each call
+    dims = gpq.make_dims(3, 14, 2, "bf16")
+    ws = torch.zeros(gpq.oal_contribution_workspace_bytes(dims, 1500), dtype=torch.uint8, device="cuda")
+    first = None
+    for seed in (78, 79, 78):
+        x = small(seed, 3, 14, 2, 1500, "bf16")
+        chi = torch.empty((3, 14, 64), dtype=torch.float32, device="cuda")
+        chi_mean = torch.empty((14, 64), dtype=torch.float32, device="cuda")
+        gpq.oal_contribution(dims, 1500, to_dev(x.q, "bf16"), to_dev(x.k, "bf16"), ws, chi, chi_mean)
+        ref, ref_mean = oracle.contribution(x.q, x.k)
+        got = chi.cpu().numpy()
+        assert rel_err(got, ref) <= chi_tol(1500)
+        assert rel_err(chi_mean.cpu().numpy(), ref_mean) <= chi_tol(1500, 3)
+        if first is None:
+            first = got
+    assert np.array_equal(first, got)
+    cb = -(-(3 * 14 + 14) * 128 // 256) * 256
+    assert int(ws[:cb].count_nonzero()) == 0
+
+
+def test_contribution_partials_contents_do_not_matter_and_repeat_bitwise():
     inp = small(77, 2, 14, 2, 333, "bf16")
     a, am = run_chi(inp.q, inp.k, "bf16", ws_fill=float("nan"))
     b, bm = run_chi(inp.q, inp.k, "bf16", ws_fill=1e30)
