@@ -235,8 +235,18 @@ def oal_contribution(dims: oal_dims, T: int, q, k, workspace, chi, chi_mean=None
 # ---- buffer helper (torch allocations sized by the library) ------------------------------
 
 def state_view(state, batch: int, n_kv_heads: int):
-    """[batch, n_kv_heads, 2145, 65] view of a state buffer (drops each block's padding)."""
-    return state.view(batch, n_kv_heads, STATE_STRIDE)[:, :, : NFEAT * V1].reshape(batch, n_kv_heads, NFEAT, V1)
+    """[batch, n_kv_heads, 2145, 65] copy of the prefix states H in a state buffer: each
+    block holds columns 0..63 as a [2145, 64] row-major matrix, then column 64 (2145 floats)."""
+    import torch
+    blk = state.view(batch, n_kv_heads, STATE_STRIDE)
+    main = blk[:, :, : NFEAT * D].reshape(batch, n_kv_heads, NFEAT, D)
+    den = blk[:, :, NFEAT * D: NFEAT * V1].reshape(batch, n_kv_heads, NFEAT, 1)
+    return torch.cat([main, den], dim=3)
+
+
+def state_index(f: int, c: int) -> int:
+    """Offset of H[f][c] inside one state block (the C macro OAL_STATE_INDEX)."""
+    return f * D + c if c < D else NFEAT * D + f
 
 
 def alloc_buffers(dims: oal_dims, T: int = 0, chunk: int = 128, device: str = "cuda"):

@@ -6,10 +6,13 @@
 //   y_h = u~_h[0:64] / u~_h[64]
 // with psi(k) = [1, k_r, k_r k_t (r <= t)] and phi_h(q) = wdec_h o [1, q_r, q_r q_t].
 //
-// The state row f of a KV head holds 65 floats. Workgroup (split, bkv) owns 192 rows; wave w
-// walks 48 of them in batches of 16 with lane c on column c (one coalesced 256-byte row read
-// and write per row) and column 64 of the batch's rows on lanes 0..15, so each cache line is
-// touched within one batch and fetched from HBM once. The next batch is loaded while the
+// The state row f of a KV head holds 65 floats: 64 in a 256-byte row of the v part and one
+// in the separate column-64 vector (the state layout keeps the v part line-aligned).
+// Workgroup (split, bkv) owns 192 rows; wave w walks 48 of them in batches of 16 with lane c
+// on column c (one aligned 256-byte row read and write per row) and the batch's 16
+// column-64 entries (64 contiguous bytes) on lanes 0..15. With 260-byte rows (column 64
+// inline) the rows straddled cache lines and the kernel wrote 17% more bytes than the state
+// holds; the split layout brought a step from 31-32 to 30 us. The next batch is loaded while the
 // current one is updated, and the first batch is requested together with everything the
 // set-up reads (k, q, v, decode coefficients): the set-up costs one memory round trip, spent
 // while the first rows arrive. Every byte of the state is read once and written once.
@@ -69,8 +72,8 @@ __global__ __launch_bounds__(kThreads) void oal_decode_kernel(
     auto load_batch = [&](int rr, float *x, float &x64) {
 #pragma unroll
         for (int u = 0; u < kBatch; ++u)
-            x[u] = (rr + u < rend) ? S[(size_t)(f0 + rr + u) * OAL_V1 + lane] : 0.0f;
-        x64 = (lane < kBatch && rr + lane < rend) ? S[(size_t)(f0 + rr + lane) * OAL_V1 + OAL_D] : 0.0f;
+            x[u] = (rr + u < rend) ? S[(size_t)(f0 + rr + u) * OAL_D + lane] : 0.0f;
+        x64 = (lane < kBatch && rr + lane < rend) ? S[(size_t)OAL_NFEAT * OAL_D + f0 + rr + lane] : 0.0f;
     };
 
     // 1. every global load of the set-up in one round trip: the first state batch, k, the
@@ -144,14 +147,14 @@ __global__ __launch_bounds__(kThreads) void oal_decode_kernel(
         for (int u = 0; u < kBatch; ++u) {
             if (rr + u < rend) {
                 s[u] += s_psi[rr + u] * vv;
-                S[(size_t)(f0 + rr + u) * OAL_V1 + lane] = s[u];
+                S[(size_t)(f0 + rr + u) * OAL_D + lane] = s[u];
 #pragma unroll
                 for (int h = 0; h < MAXH; ++h) acc[h] += s_phi[rr + u][h] * s[u];
             }
         }
         if (lane < kBatch && rr + lane < rend) {
             s64 += s_psi[rr + lane];
-            S[(size_t)(f0 + rr + lane) * OAL_V1 + OAL_D] = s64;
+            S[(size_t)OAL_NFEAT * OAL_D + f0 + rr + lane] = s64;
 #pragma unroll
             for (int h = 0; h < MAXH; ++h) accd[h] += s_phi[rr + lane][h] * s64;
         }

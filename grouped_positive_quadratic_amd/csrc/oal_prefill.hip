@@ -278,7 +278,7 @@ __device__ __forceinline__ void scan_delta_block(
                 for (int i = 0; i < 4; ++i) {
                     const int f = frow[4 * h + i];
                     const int col = n < 4 ? 16 * n + lr : OAL_D;
-                    const float xv = Sst[(size_t)(f >= 0 ? f : 0) * OAL_V1 + col];
+                    const float xv = Sst[OAL_STATE_INDEX(f >= 0 ? f : 0, col)];
                     acc[h][n][i] = f >= 0 ? xv : 0.0f;
                 }
         store_frags(tinit + ((size_t)bkv * OAL_TAIL_STEPS + (s - OAL_KSTEPS)) * kDeltaStep, acc, lane, g, lr);
@@ -326,7 +326,7 @@ __global__ __launch_bounds__(256) void oal_scan_prefix(int nchunks, int n_q_head
     if (s < OAL_KSTEPS) {
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-            const float xv = Sst[(size_t)(frow[j] >= 0 ? frow[j] : 0) * OAL_V1 + col];
+            const float xv = Sst[OAL_STATE_INDEX(frow[j] >= 0 ? frow[j] : 0, col)];
             S[j] = frow[j] >= 0 ? xv : 0.0f;
         }
     } else {
@@ -382,7 +382,7 @@ __global__ __launch_bounds__(256) void oal_scan_prefix(int nchunks, int n_q_head
     }
 #pragma unroll
     for (int j = 0; j < 8; ++j)     // tail pairs duplicate main rows: only owners write
-        if (fown[j]) Sst[(size_t)frow[j] * OAL_V1 + col] = S[j];
+        if (fown[j]) Sst[OAL_STATE_INDEX(frow[j], col)] = S[j];
 }
 
 // One term z_m of the intra-chunk kernel for a 16-query tile of one head:
@@ -703,7 +703,9 @@ __global__ __launch_bounds__(64 * kIntraWaves) __attribute__((amdgpu_waves_per_e
 // 4. readout
 template <typename T, int C, int R> struct ReadoutLayout {
     static constexpr int EPU = 16 / (int)sizeof(T);
+    static constexpr int NT = 256;              // threads: 2 head subsets x 2 parities
     static constexpr int RW = (R + 1) / 2;      // heads of one wave pair (head subset)
+    static constexpr int DEP = 2;               // snapshot K-steps held per wave (ring)
     static constexpr int QS = OAL_D + EPU;      // q row in LDS (16-byte aligned)
     static constexpr int PS = OAL_D + 4;        // fp32 p-table row
     // Byte offsets. The "union" region holds the fp32 p table during the inter-chunk loop,
@@ -725,14 +727,16 @@ template <typename T, int C, int R> struct ReadoutLayout {
 // wave = (head subset hs, K-step parity par). Subset 0 holds heads 0..RW-1, subset 1 the
 // rest; the two waves of a subset split the K-steps by the parity of rq (and of the tail
 // index), so each snapshot fragment is fetched by the two subsets' waves of that parity
-// from L2/L1 and used for all their heads.
+// from L2/L1 and used for all their heads. (Measured alternatives: one subset of all R
+// heads per wave, accumulators in AGPRs at one wave per SIMD, and a snapshot ring three
+// K-steps deep were both no faster.)
 template <typename T, int C, int R>
 __global__ __launch_bounds__(256, 2) void oal_readout(
     int T_len, int n_q_heads, int n_kv_heads, int nchunks, int n_hgroups, int nunits,
     const T *__restrict__ q, const unsigned char *__restrict__ params,
     const unsigned char *__restrict__ snap, const float *__restrict__ uintra, float *__restrict__ y) {
     using Lay = ReadoutLayout<T, C, R>;
-    constexpr int EPU = Lay::EPU, QS = Lay::QS, PS = Lay::PS, RW = Lay::RW;
+    constexpr int EPU = Lay::EPU, QS = Lay::QS, PS = Lay::PS, RW = Lay::RW, NT = Lay::NT;
     constexpr int NQT = C / 16;
     constexpr int UPQ = OAL_D / EPU;            // 16-byte units per q/k row
     constexpr int NMAIN = OAL_KSTEPS / 2;       // main K-steps per parity
@@ -771,7 +775,7 @@ __global__ __launch_bounds__(256, 2) void oal_readout(
     //    that is never stored.
     {
         constexpr int NQU = R * 16 * UPQ, NMU = R * Lay::META_UNITS + Lay::PAIR_UNITS;
-        constexpr int NQJ = (NQU + 255) / 256, NMJ = (NMU + 255) / 256;
+        constexpr int NQJ = (NQU + NT - 1) / NT, NMJ = (NMU + NT - 1) / NT;
         oal_u32x4 rq[NQJ], rm[NMJ];
         float4 rw[NQJ][EPU / 4];    // w0 of the staged q unit's dims
         auto meta_src = [&](int u) -> const oal_u32x4 * {
@@ -790,7 +794,7 @@ __global__ __launch_bounds__(256, 2) void oal_readout(
         };
 #pragma unroll
         for (int j = 0; j < NQJ; ++j) {
-            int u = tid + 256 * j;
+            int u = tid + NT * j;
             int i = u / (16 * UPQ), qi = (u / UPQ) % 16, a = u % UPQ, pos = pos0 + qi;
             rq[j] = (u < NQU && pos < T_len)
                 ? *reinterpret_cast<const oal_u32x4 *>(q + (((size_t)b * n_q_heads + h0 + i) * T_len + pos) * OAL_D + a * EPU)
@@ -801,23 +805,23 @@ __global__ __launch_bounds__(256, 2) void oal_readout(
         }
 #pragma unroll
         for (int j = 0; j < NMJ; ++j) {
-            int u = tid + 256 * j;
+            int u = tid + NT * j;
             rm[j] = u < NMU ? *meta_src(u) : zero16();
         }
         constexpr int SNAP_UNITS = OAL_KSTEPS * snap_kstep_bytes<T>() / 16;
         constexpr int SHARE = (SNAP_UNITS + NQT - 1) / NQT;
-        constexpr int NTJ = (SHARE + 255) / 256;
+        constexpr int NTJ = (SHARE + NT - 1) / NT;
         const oal_u32x4 *sn = reinterpret_cast<const oal_u32x4 *>(
             snap + ((size_t)bkv * nchunks + c) * OAL_SNAP_KSTEPS * snap_kstep_bytes<T>());
         oal_u32x4 touch = zero16();
 #pragma unroll
         for (int j = 0; j < NTJ; ++j) {
-            int u = qt * SHARE + tid + 256 * j;
-            if (tid + 256 * j < SHARE && u < SNAP_UNITS) touch ^= sn[u];
+            int u = qt * SHARE + tid + NT * j;
+            if (tid + NT * j < SHARE && u < SNAP_UNITS) touch ^= sn[u];
         }
 #pragma unroll
         for (int j = 0; j < NQJ; ++j) {
-            int u = tid + 256 * j;
+            int u = tid + NT * j;
             int i = u / (16 * UPQ), qi = (u / UPQ) % 16, a = u % UPQ;
             if (u < NQU) {
                 *reinterpret_cast<oal_u32x4 *>(s_q + (i * 16 + qi) * QS + a * EPU) = rq[j];
@@ -832,12 +836,12 @@ __global__ __launch_bounds__(256, 2) void oal_readout(
         }
 #pragma unroll
         for (int j = 0; j < NMJ; ++j) {
-            int u = tid + 256 * j;
+            int u = tid + NT * j;
             if (u < NMU) *meta_dst(u) = rm[j];
         }
         if (touch.x == 0x9e3779b9u && touch.y == 0x7f4a7c15u && T_len < 0) y[0] = 0.0f;  // never true
         // q_64 = 1: the second factor of the linear and constant tail entries
-        for (int u = tid; u < R * 16; u += 256) s_q[u * QS + OAL_D] = (T)1.0f;
+        for (int u = tid; u < R * 16; u += NT) s_q[u * QS + OAL_D] = (T)1.0f;
     }
     __syncthreads();
 
@@ -848,9 +852,9 @@ __global__ __launch_bounds__(256, 2) void oal_readout(
         for (int n = 0; n < 5; ++n) acc[li][n] = oal_splat(0.0f);
 
     // 2. inter-chunk: phi(Q) . S_c over this wave's K-steps: the 36 main K-steps with
-    //    rq = 2 j + par, then the tail K-steps 2 x + par. Snapshot fragments are fetched one
-    //    step ahead into two buffers (the loop is unrolled by two so that they need no
-    //    register moves); the other wave of the SIMD covers the remaining latency.
+    //    rq = 2 j + par, then the tail K-steps 2 x + par. Snapshot fragments are fetched
+    //    DEP - 1 steps ahead into a ring of DEP buffers (the loop is unrolled by DEP so that
+    //    they need no register moves).
     constexpr int KB = snap_kstep_bytes<T>();
     const unsigned char *sbase = snap + ((size_t)bkv * nchunks + c) * OAL_SNAP_KSTEPS * KB;
     const int ntot = NMAIN + (ntail + 1 - par) / 2;
@@ -896,6 +900,13 @@ __global__ __launch_bounds__(256, 2) void oal_readout(
             }
         };
         // main K-step: A = p_r p_t (times the slot coefficient in a general blob)
+        auto make_a = [&](int li, int rq, float pr, OalFrag<T> &a) {
+            float phi[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) phi[e] = pr * pt[li][e];
+            gen_mul(li, rq, phi);
+            a.set(phi);
+        };
         auto main_step = [&](const OalFrag<T> (&bc)[5]) {
             const int rq = 2 * j + par;
             const int r = 4 * rq + g;
@@ -903,16 +914,25 @@ __global__ __launch_bounds__(256, 2) void oal_readout(
             float prv[NH];
 #pragma unroll
             for (int li = 0; li < NH; ++li) prv[li] = s_p[((hb + li) * 16 + lr) * PS + r];
+            // the next head's operand is formed while this head's MFMAs run (two buffers;
+            // bf16: the scheduler is told to alternate one MFMA with three VALU ops)
+            OalFrag<T> a[2];
+            make_a(0, rq, prv[0], a[0]);
 #pragma unroll
             for (int li = 0; li < NH; ++li) {
-                float phi[8];
+                if (li + 1 < NH) make_a(li + 1, rq, prv[li + 1], a[(li + 1) & 1]);
 #pragma unroll
-                for (int e = 0; e < 8; ++e) phi[e] = prv[li] * pt[li][e];
-                gen_mul(li, rq, phi);
-                OalFrag<T> a;
-                a.set(phi);
+                for (int n = 0; n < 5; ++n) acc[li][n] = oal_mma(a[li & 1], bc[n], acc[li][n]);
+                if constexpr (sizeof(T) == 2) {
+                    if (li + 1 < NH) {
 #pragma unroll
-                for (int n = 0; n < 5; ++n) acc[li][n] = oal_mma(a, bc[n], acc[li][n]);
+                        for (int n = 0; n < 4; ++n) {
+                            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                            __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
+                        }
+                        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                    }
+                }
             }
             if (++j > tb) { ++tb; j = 0; }
         };
@@ -943,22 +963,26 @@ __global__ __launch_bounds__(256, 2) void oal_readout(
                 for (int n = 0; n < 5; ++n) acc[li][n] = oal_mma(a, bc[n], acc[li][n]);
             }
         };
-        static_assert(NMAIN % 2 == 0, "the main loop is unrolled by two");
-        OalFrag<T> b0[5], b1[5];
-        load_next(b0);
-        for (int it = 0; it < NMAIN; it += 2) {
-            load_next(b1);
-            main_step(b0);
-            if (it + 2 < ntot) load_next(b0);
-            main_step(b1);
+        constexpr int DEP = Lay::DEP;
+        static_assert(NMAIN % DEP == 0, "the main loop is unrolled by DEP");
+        OalFrag<T> bq[DEP][5];
+#pragma unroll
+        for (int d = 0; d + 1 < DEP; ++d) load_next(bq[d]);      // ntot > NMAIN >= DEP - 1
+        for (int it = 0; it < NMAIN; it += DEP) {
+#pragma unroll
+            for (int u = 0; u < DEP; ++u) {
+                if (it + u + DEP - 1 < ntot) load_next(bq[(u + DEP - 1) % DEP]);
+                main_step(bq[u]);
+            }
         }
-        // tail K-steps (b0 already holds the first)
-        for (int x = 0; x < ntot - NMAIN; x += 2) {
-            if (NMAIN + x + 1 < ntot) load_next(b1);
-            tail_step(b0, 2 * x + par);
-            if (x + 1 < ntot - NMAIN) {
-                if (NMAIN + x + 2 < ntot) load_next(b0);
-                tail_step(b1, 2 * (x + 1) + par);
+        // tail K-steps: step NMAIN + x sits in buffer x % DEP (NMAIN is a multiple of DEP)
+        for (int x = 0; x < ntot - NMAIN; x += DEP) {
+#pragma unroll
+            for (int u = 0; u < DEP; ++u) {
+                if (x + u < ntot - NMAIN) {
+                    if (NMAIN + x + u + DEP - 1 < ntot) load_next(bq[(u + DEP - 1) % DEP]);
+                    tail_step(bq[u], 2 * (x + u) + par);
+                }
             }
         }
     };
@@ -1046,7 +1070,7 @@ hipError_t launch_readout(const oal_dims &d, int T_len, const PrefillPlan &p, co
     if (e != hipSuccess) return e;
     int nunits = p.nchunks * d.batch * d.n_kv_heads * n_hg;
     int nblocks = kXcds * (C / 16) * ((nunits + kXcds - 1) / kXcds);
-    hipLaunchKernelGGL(kern, dim3(nblocks), dim3(256), lds, stream, T_len, d.n_q_heads, d.n_kv_heads,
+    hipLaunchKernelGGL(kern, dim3(nblocks), dim3(ReadoutLayout<T, C, R>::NT), lds, stream, T_len, d.n_q_heads, d.n_kv_heads,
                        p.nchunks, n_hg, nunits, reinterpret_cast<const T *>(q),
                        reinterpret_cast<const unsigned char *>(params), snap, uintra, y);
     return hipGetLastError();

@@ -21,12 +21,15 @@
  *   k, v   [batch, n_kv_heads, T, 64]
  *   y      [batch, n_q_heads,  T, 64]  fp32
  *   state  [batch, n_kv_heads] blocks of OAL_STATE_STRIDE (139456) fp32, one per (sequence,
- *          KV head), 256-byte aligned: the block's first 2145 * 65 floats are the prefix
- *          state, a [2145, 65] row-major matrix, the last 31 floats are padding (zero after
- *          oal_state_init; the kernels keep them finite). Row 0 = H0; rows 1..64 = H1_r
- *          (r = 0..63); rows 65.. = H2_rt for r <= t in row-major order of the upper triangle
- *          (the symmetric H2 stored once, r < t not doubled). Columns 0..63 = components of
- *          v, column 64 = the "1" of [v;1].
+ *          KV head), 256-byte aligned. The prefix state is a [2145, 65] matrix H (feature
+ *          row f, column c) stored in two parts: columns 0..63 (the components of v) as a
+ *          [2145, 64] row-major matrix in the first 2145 * 64 floats (256-byte rows), then
+ *          column 64 (the "1" of [v;1], the denominators' state) as 2145 contiguous floats;
+ *          H[f][c] is at f * 64 + c for c < 64 and at 2145 * 64 + f for c = 64
+ *          (OAL_STATE_INDEX). The last 31 floats are padding (zero after oal_state_init; the
+ *          kernels keep them finite). Row 0 = H0; rows 1..64 = H1_r (r = 0..63); rows 65.. =
+ *          H2_rt for r <= t in row-major order of the upper triangle (the symmetric H2
+ *          stored once, r < t not doubled).
  *   For a decode step T = 1 and the T axis is dropped: q [batch, n_q_heads, 64] etc.
  *
  * Ownership: the caller allocates and owns every device buffer (params, state, workspace,
@@ -94,6 +97,8 @@ size_t oal_params_bytes(const oal_dims *dims);
 
 /* Floats per (sequence, KV head) block of the state buffer: 2145 * 65 rounded up to 64. */
 #define OAL_STATE_STRIDE 139456
+/* Offset in a state block of H[f][c] (feature row f < 2145, column c <= 64). */
+#define OAL_STATE_INDEX(f, c) ((c) < 64 ? (size_t)(f) * 64 + (size_t)(c) : (size_t)2145 * 64 + (size_t)(f))
 
 /* Bytes of the state buffer: batch * n_kv_heads * OAL_STATE_STRIDE * 4. */
 size_t oal_state_bytes(const oal_dims *dims);

@@ -397,3 +397,29 @@ def test_cfg5_decode_64_sequences_sampled():
     assert err <= TOL["bf16"]
     S = sess.state_np()[sel[:2]]
     assert state_ok(S, k_all[:2], v_all[:2], "bf16")
+
+
+def test_state_layout_raw_offsets():
+    # One decode step from an empty state: H0 = [v;1], H1_r = k_r [v;1], H2_rt = k_r k_t [v;1].
+    # Read the raw buffer at the documented offsets (v part [2145, 64] row-major, then the
+    # column-64 vector) for each (sequence, KV head) block.
+    rng = np.random.default_rng(91)
+    B, Hq, Hkv = 2, 4, 2
+    q = round_bf16(rng.standard_normal((B, Hq, 64)))
+    k = round_bf16(rng.standard_normal((B, Hkv, 64)))
+    v = round_bf16(rng.standard_normal((B, Hkv, 64)))
+    p = small(91, B, Hq, Hkv, 4).params
+    sess = Session(B, Hq, Hkv, "bf16", p)
+    sess.decode(q, k, v)
+    torch.cuda.synchronize()
+    raw = sess.state.view(B, Hkv, gpq.STATE_STRIDE).cpu().numpy().astype(np.float64)
+    for b in range(B):
+        for kv in range(Hkv):
+            blk, kk, vv = raw[b, kv], k[b, kv].astype(np.float64), v[b, kv].astype(np.float64)
+            # rows: H0; H1_5; H2_(2,3) at 65 + idx(2,3), idx(r,t) = 64 r - r(r-1)/2 + (t - r)
+            for f, mono in ((0, 1.0), (6, kk[5]), (65 + 2 * 64 - 1 + 1, kk[2] * kk[3])):
+                for c in (0, 17, 63):
+                    assert abs(blk[gpq.state_index(f, c)] - mono * vv[c]) <= 1e-6 * (1 + abs(mono * vv[c]))
+                assert abs(blk[gpq.state_index(f, 64)] - mono) <= 1e-6 * (1 + abs(mono))
+                assert gpq.state_index(f, 64) == 2145 * 64 + f
+            assert np.all(blk[2145 * 65:] == 0.0)
