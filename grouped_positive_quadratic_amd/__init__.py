@@ -24,7 +24,7 @@ EXPORTED = ("oal_params_bytes", "oal_state_bytes", "oal_prefill_workspace_bytes"
             "oal_decode_workspace_bytes", "oal_params_pack", "oal_state_init", "oal_prefill",
             "oal_prefill_timed", "oal_decode_step", "oal_status_string", "oal_timing_event_create",
             "oal_timing_event_destroy", "oal_timing_event_record", "oal_timing_elapsed_ms",
-            "oal_contribution_workspace_bytes", "oal_contribution")
+            "oal_contribution_workspace_bytes", "oal_contribution", "oal_decode_step_indexed")
 
 
 class OALError(RuntimeError):
@@ -69,6 +69,8 @@ def _load():
     lib.oal_prefill_timed.restype = ctypes.c_int
     lib.oal_decode_step.argtypes = [dp, P, P, P, P, P, P, P, P]
     lib.oal_decode_step.restype = ctypes.c_int
+    lib.oal_decode_step_indexed.argtypes = [dp, P, I, P, P, P, P, P, P, P, P]
+    lib.oal_decode_step_indexed.restype = ctypes.c_int
     lib.oal_status_string.argtypes, lib.oal_status_string.restype = [ctypes.c_int], ctypes.c_char_p
     lib.oal_timing_event_create.argtypes, lib.oal_timing_event_create.restype = [ctypes.POINTER(P)], ctypes.c_int
     lib.oal_timing_event_destroy.argtypes, lib.oal_timing_event_destroy.restype = [P], ctypes.c_int
@@ -230,6 +232,14 @@ def oal_contribution(dims: oal_dims, T: int, q, k, workspace, chi, chi_mean=None
     _check("oal_contribution", _lib.oal_contribution(ctypes.byref(dims), int(T), _ptr(q), _ptr(k),
                                                      _ptr(workspace), _ptr(chi), _ptr(chi_mean),
                                                      _stream(stream)))
+
+
+def oal_decode_step_indexed(dims: oal_dims, slots, pool_size: int, q, k, v, params_dev, state_pool,
+                            workspace, y, stream=None):
+    """Decode step on pool blocks: slots is a device int32 tensor [batch]."""
+    _check("oal_decode_step_indexed", _lib.oal_decode_step_indexed(
+        ctypes.byref(dims), _ptr(slots), int(pool_size), _ptr(q), _ptr(k), _ptr(v), _ptr(params_dev),
+        _ptr(state_pool), _ptr(workspace), _ptr(y), _stream(stream)))
 
 
 # ---- buffer helper (torch allocations sized by the library) ------------------------------

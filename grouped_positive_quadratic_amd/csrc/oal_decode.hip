@@ -49,7 +49,8 @@ template <typename T, int MAXH>
 __global__ __launch_bounds__(kThreads) void oal_decode_kernel(
     int n_q_heads, int n_kv_heads, const T *__restrict__ q, const T *__restrict__ k,
     const T *__restrict__ v, const unsigned char *__restrict__ params, float *__restrict__ state,
-    float *__restrict__ partial, unsigned int *__restrict__ counters, float *__restrict__ y) {
+    const int *__restrict__ slots, int pool_size, float *__restrict__ partial,
+    unsigned int *__restrict__ counters, float *__restrict__ y) {
     const int split = blockIdx.x;
     const int bkv = blockIdx.y;
     const int b = bkv / n_kv_heads, kv = bkv % n_kv_heads;
@@ -57,7 +58,11 @@ __global__ __launch_bounds__(kThreads) void oal_decode_kernel(
     const int h0 = kv * n_rep;
     const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
     const int f0 = split * kRows;
-    const int nrows = min(kRows, OAL_NFEAT - f0);
+    // state block: sequence b's own, or pool block slots[b] (indexed decode). A slot outside
+    // the pool streams no rows: the sequence's sums stay zero and its y is 0/0 = NaN.
+    const int sb = slots ? slots[b] : b;
+    const bool valid = sb >= 0 && sb < pool_size;
+    const int nrows = valid ? min(kRows, OAL_NFEAT - f0) : 0;
 
     __shared__ float s_k[OAL_D];
     __shared__ float s_q[MAXH][OAL_D];
@@ -66,7 +71,7 @@ __global__ __launch_bounds__(kThreads) void oal_decode_kernel(
     __shared__ float s_red[4][MAXH][OAL_V1];
     __shared__ int s_last;
 
-    float *S = state + (size_t)bkv * OAL_STATE_STRIDE;
+    float *S = state + ((size_t)(valid ? sb : 0) * n_kv_heads + kv) * OAL_STATE_STRIDE;
     const int rbeg = wave * kRowsPerWave, rend = min(nrows, rbeg + kRowsPerWave);
     // one batch: 16 rows with lane = column, and column 64 of the same rows on lanes 0..15
     auto load_batch = [&](int rr, float *x, float &x64) {
@@ -212,7 +217,8 @@ __global__ __launch_bounds__(kThreads) void oal_decode_kernel(
 
 template <typename T, int MAXH>
 hipError_t launch(const oal_dims &d, const void *q, const void *k, const void *v,
-                  const void *params, float *state, void *ws, float *y, hipStream_t stream) {
+                  const void *params, float *state, const int *slots, int pool_size, void *ws, float *y,
+                  hipStream_t stream) {
     int bkv = d.batch * d.n_kv_heads;
     unsigned int *counters = reinterpret_cast<unsigned int *>(ws);
     size_t cbytes = ((size_t)bkv * sizeof(unsigned int) + 255) / 256 * 256;
@@ -221,7 +227,8 @@ hipError_t launch(const oal_dims &d, const void *q, const void *k, const void *v
     hipLaunchKernelGGL((oal_decode_kernel<T, MAXH>), grid, dim3(kThreads), 0, stream, d.n_q_heads,
                        d.n_kv_heads, reinterpret_cast<const T *>(q), reinterpret_cast<const T *>(k),
                        reinterpret_cast<const T *>(v),
-                       reinterpret_cast<const unsigned char *>(params), state, partial, counters, y);
+                       reinterpret_cast<const unsigned char *>(params), state, slots, pool_size, partial,
+                       counters, y);
     return hipGetLastError();
 }
 
@@ -234,13 +241,14 @@ size_t oal_decode_ws_bytes_impl(const oal_dims &d) {
 }
 
 hipError_t oal_launch_decode(const oal_dims &d, const void *q, const void *k, const void *v,
-                             const void *params, float *state, void *ws, float *y,
-                             hipStream_t stream) {
+                             const void *params, float *state, const int *slots, int pool_size, void *ws,
+                             float *y, hipStream_t stream) {
     int n_rep = d.n_q_heads / d.n_kv_heads;
+    if (!slots) pool_size = d.batch;
     if (d.dtype == OAL_BF16) {
-        if (n_rep <= 8) return launch<__bf16, 8>(d, q, k, v, params, state, ws, y, stream);
-        return launch<__bf16, 16>(d, q, k, v, params, state, ws, y, stream);
+        if (n_rep <= 8) return launch<__bf16, 8>(d, q, k, v, params, state, slots, pool_size, ws, y, stream);
+        return launch<__bf16, 16>(d, q, k, v, params, state, slots, pool_size, ws, y, stream);
     }
-    if (n_rep <= 8) return launch<float, 8>(d, q, k, v, params, state, ws, y, stream);
-    return launch<float, 16>(d, q, k, v, params, state, ws, y, stream);
+    if (n_rep <= 8) return launch<float, 8>(d, q, k, v, params, state, slots, pool_size, ws, y, stream);
+    return launch<float, 16>(d, q, k, v, params, state, slots, pool_size, ws, y, stream);
 }

@@ -16,7 +16,8 @@
 #include "oal_internal.h"
 
 hipError_t oal_launch_decode(const oal_dims &d, const void *q, const void *k, const void *v,
-                             const void *params, float *state, void *ws, float *y, hipStream_t stream);
+                             const void *params, float *state, const int *slots, int pool_size, void *ws,
+                             float *y, hipStream_t stream);
 hipError_t oal_launch_prefill(const oal_dims &d, int T_len, int C, const void *q, const void *k,
                               const void *v, const void *params, float *state, void *ws, float *y,
                               hipStream_t stream, hipEvent_t *marks);
@@ -326,7 +327,27 @@ oal_status oal_decode_step(const oal_dims *d, const void *q, const void *k, cons
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(params_dev) ||
         !aligned16(state_dev) || !aligned16(workspace) || !aligned16(y))
         return OAL_E_ALIGN;
-    hipError_t e = oal_launch_decode(*d, q, k, v, params_dev, state_dev, workspace, y, stream);
+    hipError_t e = oal_launch_decode(*d, q, k, v, params_dev, state_dev, nullptr, 0, workspace, y, stream);
+    if (e != hipSuccess) {
+        (void)hipGetLastError();
+        return OAL_E_HIP;
+    }
+    return OAL_OK;
+}
+
+oal_status oal_decode_step_indexed(const oal_dims *d, const int32_t *slots, int32_t pool_size,
+                                   const void *q, const void *k, const void *v, const void *params_dev,
+                                   float *state_pool, void *workspace, float *y, hipStream_t stream) {
+    oal_status st = check_dims(d);
+    if (st != OAL_OK) return st;
+    if (d->n_q_heads / d->n_kv_heads > 16) return OAL_E_UNSUPPORTED;
+    if (pool_size < 1) return OAL_E_SHAPE;
+    if (d->batch == 0) return OAL_OK;
+    if (!slots || !q || !k || !v || !params_dev || !state_pool || !workspace || !y) return OAL_E_ARG;
+    if ((reinterpret_cast<uintptr_t>(slots) & 3u) || !aligned16(q) || !aligned16(k) || !aligned16(v) ||
+        !aligned16(params_dev) || !aligned16(state_pool) || !aligned16(workspace) || !aligned16(y))
+        return OAL_E_ALIGN;
+    hipError_t e = oal_launch_decode(*d, q, k, v, params_dev, state_pool, slots, pool_size, workspace, y, stream);
     if (e != hipSuccess) {
         (void)hipGetLastError();
         return OAL_E_HIP;

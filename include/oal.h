@@ -191,6 +191,28 @@ size_t oal_contribution_workspace_bytes(const oal_dims *dims, int32_t T);
 oal_status oal_contribution(const oal_dims *dims, int32_t T, const void *q, const void *k,
                             void *workspace, float *chi, float *chi_mean, hipStream_t stream);
 
+/* Decode step for sequences whose states live in a pool (serving: a batch of active
+ * sequences over a larger set of state blocks). Sequence b of the batch uses pool block
+ * slots[b]; otherwise identical to oal_decode_step (same kernels, same results bit for bit
+ * as oal_decode_step on a state buffer holding those blocks in batch order).
+ *   slots      -- [batch] int32 (device, 4-byte aligned): pool block of each sequence. The
+ *                 slots of one call must be distinct (two sequences on one block race).
+ *                 A slot outside [0, pool_size) is not an error: that sequence's state is not
+ *                 touched and its y is NaN (the kernels check every slot).
+ *   pool_size  -- blocks in the pool, >= 1 (OAL_E_SHAPE otherwise).
+ *   state_pool -- [pool_size, n_kv_heads] blocks of OAL_STATE_STRIDE floats, the state
+ *                 layout above (a state buffer with batch = pool_size); updated in place at
+ *                 the slots of the batch, every other block left as it is.
+ *   workspace  -- oal_decode_workspace_bytes(dims) bytes, same contract as oal_decode_step
+ *                 (dims->batch is the number of active sequences, not the pool size).
+ * q, k, v, y, params_dev: as in oal_decode_step, indexed by the batch position b. A pool is
+ * filled by oal_state_init (batch = pool_size) or by oal_prefill on one block (batch = 1,
+ * state_dev = the block's address). */
+oal_status oal_decode_step_indexed(const oal_dims *dims, const int32_t *slots, int32_t pool_size,
+                                   const void *q, const void *k, const void *v,
+                                   const void *params_dev, float *state_pool, void *workspace,
+                                   float *y, hipStream_t stream);
+
 /* Timing events for oal_prefill_timed and for bracketing a timed region. A default HIP event
  * performs a system-scope release when it is recorded, which writes back the L2: between two
  * kernels that leave many dirty lines that costs several microseconds and would be counted

@@ -80,6 +80,13 @@ def test_validation_errors_enqueue_nothing():
     assert _code(gpq.oal_decode_step, d, A, A, A, A + 8, A, A, A, 0) == 4
     assert _code(gpq.oal_decode_step, gpq.make_dims(1, 17, 1, "bf16"), *([A] * 7), 0) == 5
     assert _code(gpq.oal_decode_step, gpq.make_dims(0, 2, 1, "bf16"), *([None] * 7), 0) == 0
+    ix = (A, A, A, A, A, A, A)   # q, k, v, params, pool, workspace, y
+    assert _code(gpq.oal_decode_step_indexed, d, A, 0, *ix, 0) == 2         # empty pool
+    assert _code(gpq.oal_decode_step_indexed, d, None, 4, *ix, 0) == 1      # no slots
+    assert _code(gpq.oal_decode_step_indexed, d, A + 2, 4, *ix, 0) == 4     # misaligned slots
+    assert _code(gpq.oal_decode_step_indexed, d, A, 4, A, A, A, A, A + 8, A, A, 0) == 4
+    assert _code(gpq.oal_decode_step_indexed, gpq.make_dims(1, 17, 1, "bf16"), A, 4, *ix, 0) == 5
+    assert _code(gpq.oal_decode_step_indexed, gpq.make_dims(0, 2, 1, "bf16"), None, 4, *([None] * 7), 0) == 0
     c4 = (A, A, A, A, A)   # q, k, workspace, chi, chi_mean
     assert _code(gpq.oal_contribution, d, 0, *c4, 0) == 2                  # T < 1
     assert _code(gpq.oal_contribution, d, (1 << 22) + 1, *c4, 0) == 5      # above the max T

@@ -1,0 +1,121 @@
+"""GPU: decode over a state pool (oal_decode_step_indexed) against the plain decode step and
+the oracle. The indexed step runs the same kernels on pool blocks chosen per sequence, so its
+outputs and updated blocks must equal, bit for bit, those of oal_decode_step on a state buffer
+holding the same blocks in batch order; blocks not in the batch stay untouched."""
+import numpy as np
+import pytest
+
+import oracle
+from oal_synth import small, qwen_like
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+from gpu_util import Session, to_dev, TOL  # noqa: E402
+import grouped_positive_quadratic_amd as gpq  # noqa: E402
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.fail("GPU tests need a GPU")
+
+
+def _pool_from_prefix(inp, T0, chunk=128):
+    """Pool with one block per sequence of `inp`, filled by a prefill of its first T0 tokens."""
+    B, Hq, Hkv, _, _, _ = inp.dims
+    pool = Session(B, Hq, Hkv, inp.dtype, inp.params, T0, chunk)
+    gpq.oal_prefill(pool.dims, T0, chunk, None, to_dev(inp.k[:, :, :T0], inp.dtype),
+                    to_dev(inp.v[:, :, :T0], inp.dtype), pool.params, pool.state, pool.ws, None)
+    torch.cuda.synchronize()
+    return pool
+
+
+def _blocks(state, idx, Hkv):
+    return state.view(-1, Hkv, gpq.STATE_STRIDE)[idx].clone()
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_indexed_decode_matches_plain_decode_and_oracle(dtype):
+    P, Hq, Hkv, T0, steps = 6, 4, 2, 150, 3
+    inp = small(501, P, Hq, Hkv, T0 + steps, dtype)
+    pool = _pool_from_prefix(inp, T0)
+    slots_l = [4, 0, 2]
+    slots = torch.tensor(slots_l, dtype=torch.int32, device="cuda")
+    untouched = [1, 3, 5]
+    before = _blocks(pool.state, untouched, Hkv)
+    # reference: a plain state buffer holding the three blocks in batch order
+    ref = Session(3, Hq, Hkv, dtype, inp.params)
+    ref.state.view(3, Hkv, gpq.STATE_STRIDE).copy_(_blocks(pool.state, slots_l, Hkv))
+    dims = gpq.make_dims(3, Hq, Hkv, dtype)
+    dws = torch.zeros(gpq.oal_decode_workspace_bytes(dims), dtype=torch.uint8, device="cuda")
+    for st in range(steps):
+        i = T0 + st
+        q = to_dev(inp.q[slots_l, :, i], dtype)
+        k = to_dev(inp.k[slots_l, :, i], dtype)
+        v = to_dev(inp.v[slots_l, :, i], dtype)
+        y = torch.empty((3, Hq, 64), dtype=torch.float32, device="cuda")
+        gpq.oal_decode_step_indexed(dims, slots, P, q, k, v, pool.params, pool.state, dws, y)
+        y_ref = ref.decode(q, k, v)
+        torch.cuda.synchronize()
+        assert torch.equal(y, y_ref), f"step {st}: indexed and plain decode differ"
+        rows = [(j, h, i) for j in range(3) for h in range(Hq)]
+        want = oracle.dense_rows(inp.q[slots_l], inp.k[slots_l], inp.v[slots_l], inp.params, rows)
+        err = oracle.row_error(y.cpu().numpy().reshape(-1, 64), want)
+        print(f"[parity] indexed decode {dtype} step {st}: err={err:.2e}", flush=True)
+        assert err <= TOL[dtype]
+    assert torch.equal(_blocks(pool.state, slots_l, Hkv), ref.state.view(3, Hkv, gpq.STATE_STRIDE))
+    assert torch.equal(_blocks(pool.state, untouched, Hkv), before)
+
+
+def test_indexed_decode_slot_outside_pool_gives_nan_and_touches_nothing():
+    P, Hq, Hkv, T0 = 3, 4, 2, 64
+    inp = small(502, P, Hq, Hkv, T0 + 1, "bf16")
+    pool = _pool_from_prefix(inp, T0)
+    before = pool.state.clone()
+    slots_l = [1, 7, -1]
+    slots = torch.tensor(slots_l, dtype=torch.int32, device="cuda")
+    dims = gpq.make_dims(3, Hq, Hkv, "bf16")
+    dws = torch.zeros(gpq.oal_decode_workspace_bytes(dims), dtype=torch.uint8, device="cuda")
+    src = [1, 0, 2]       # token rows fed to the three batch positions
+    q, k, v = (to_dev(x[src, :, T0], "bf16") for x in (inp.q, inp.k, inp.v))
+    y = torch.empty((3, Hq, 64), dtype=torch.float32, device="cuda")
+    gpq.oal_decode_step_indexed(dims, slots, P, q, k, v, pool.params, pool.state, dws, y)
+    torch.cuda.synchronize()
+    yc = y.cpu().numpy()
+    assert np.isnan(yc[1]).all() and np.isnan(yc[2]).all() and np.isfinite(yc[0]).all()
+    blocks = pool.state.view(P, Hkv, gpq.STATE_STRIDE)
+    assert torch.equal(blocks[[0, 2]], before.view(P, Hkv, gpq.STATE_STRIDE)[[0, 2]])
+    want = oracle.dense_rows(inp.q[[1]], inp.k[[1]], inp.v[[1]], inp.params, [(0, h, T0) for h in range(Hq)])
+    assert oracle.row_error(yc[0], want) <= TOL["bf16"]
+    assert int(dws[:256].count_nonzero()) == 0      # counters returned to zero
+
+
+def test_indexed_decode_serving_shape_bitwise():
+    # 64 active sequences over a pool of 96 blocks (14q/2kv, bf16), slots in shuffled order
+    P, B, T0 = 96, 64, 256
+    inp = qwen_like(P, T0 + 1, 7, name="pool")
+    pool = _pool_from_prefix(inp, T0)
+    rng = np.random.default_rng(8)
+    slots_l = [int(x) for x in rng.permutation(P)[:B]]
+    slots = torch.tensor(slots_l, dtype=torch.int32, device="cuda")
+    others = sorted(set(range(P)) - set(slots_l))
+    before = _blocks(pool.state, others, 2)
+    ref = Session(B, 14, 2, "bf16", inp.params)
+    ref.state.view(B, 2, gpq.STATE_STRIDE).copy_(_blocks(pool.state, slots_l, 2))
+    q, k, v = (to_dev(x[slots_l, :, T0], "bf16") for x in (inp.q, inp.k, inp.v))
+    dims = gpq.make_dims(B, 14, 2, "bf16")
+    dws = torch.zeros(gpq.oal_decode_workspace_bytes(dims), dtype=torch.uint8, device="cuda")
+    y = torch.empty((B, 14, 64), dtype=torch.float32, device="cuda")
+    gpq.oal_decode_step_indexed(dims, slots, P, q, k, v, pool.params, pool.state, dws, y)
+    y_ref = ref.decode(q, k, v)
+    torch.cuda.synchronize()
+    assert torch.equal(y, y_ref)
+    assert torch.equal(_blocks(pool.state, slots_l, 2), ref.state.view(B, 2, gpq.STATE_STRIDE))
+    assert torch.equal(_blocks(pool.state, others, 2), before)
+    rows = [(j, h, T0) for j in (0, 31, 63) for h in (0, 7, 13)]
+    sel = [slots_l[j] for j in (0, 31, 63)]
+    want = oracle.dense_rows(inp.q[sel], inp.k[sel], inp.v[sel], inp.params,
+                             [(n, h, T0) for n in range(3) for h in (0, 7, 13)])
+    got = np.stack([y[j, h].cpu().numpy() for j, h, _ in rows])
+    assert oracle.row_error(got, want) <= TOL["bf16"]
