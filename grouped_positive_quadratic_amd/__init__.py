@@ -24,7 +24,8 @@ EXPORTED = ("oal_params_bytes", "oal_state_bytes", "oal_prefill_workspace_bytes"
             "oal_decode_workspace_bytes", "oal_params_pack", "oal_state_init", "oal_prefill",
             "oal_prefill_timed", "oal_decode_step", "oal_status_string", "oal_timing_event_create",
             "oal_timing_event_destroy", "oal_timing_event_record", "oal_timing_elapsed_ms",
-            "oal_contribution_workspace_bytes", "oal_contribution", "oal_decode_step_indexed")
+            "oal_contribution_workspace_bytes", "oal_contribution", "oal_decode_step_indexed",
+            "oal_prefill_varlen")
 
 
 class OALError(RuntimeError):
@@ -67,6 +68,8 @@ def _load():
     lib.oal_prefill.restype = ctypes.c_int
     lib.oal_prefill_timed.argtypes = [dp, I, I, P, P, P, P, P, P, P, P, ctypes.POINTER(P)]
     lib.oal_prefill_timed.restype = ctypes.c_int
+    lib.oal_prefill_varlen.argtypes = [dp, I, P, I, P, P, P, P, P, P, P, P]
+    lib.oal_prefill_varlen.restype = ctypes.c_int
     lib.oal_decode_step.argtypes = [dp, P, P, P, P, P, P, P, P]
     lib.oal_decode_step.restype = ctypes.c_int
     lib.oal_decode_step_indexed.argtypes = [dp, P, I, P, P, P, P, P, P, P, P]
@@ -179,6 +182,14 @@ def oal_prefill(dims: oal_dims, T: int, chunk: int, q, k, v, params_dev, state_d
     _check("oal_prefill", _lib.oal_prefill(ctypes.byref(dims), int(T), int(chunk), _ptr(q), _ptr(k),
                                            _ptr(v), _ptr(params_dev), _ptr(state_dev),
                                            _ptr(workspace), _ptr(y), _stream(stream)))
+
+
+def oal_prefill_varlen(dims: oal_dims, T: int, lengths, chunk: int, q, k, v, params_dev, state_dev,
+                       workspace, y, stream=None):
+    """Ragged batch padded to T: lengths is a device int32 tensor [batch]."""
+    _check("oal_prefill_varlen", _lib.oal_prefill_varlen(
+        ctypes.byref(dims), int(T), _ptr(lengths), int(chunk), _ptr(q), _ptr(k), _ptr(v),
+        _ptr(params_dev), _ptr(state_dev), _ptr(workspace), _ptr(y), _stream(stream)))
 
 
 def oal_prefill_timed(dims: oal_dims, T: int, chunk: int, q, k, v, params_dev, state_dev, workspace,

@@ -173,12 +173,18 @@ __device__ inline void store_frags(float *dp, const oal_f32x4 (&acc)[2][5], int 
 }
 
 // grid (K-step blocks + 1 tail block, chunks, sequence x KV head); 8 waves, one K-step each.
+// Tokens of sequence b: all T_len of the padded batch, or lens[b] clamped to [0, T_len] for a
+// ragged batch (tokens past it count as absent: zero features, no output rows).
+__device__ __forceinline__ int oal_seq_len(const int *__restrict__ lens, int b, int T_len) {
+    return lens ? min(max(lens[b], 0), T_len) : T_len;
+}
+
 // The chunk's K and V are staged transposed in LDS ([dim][token]).
 template <typename T, int C>
 __device__ __forceinline__ void scan_delta_block(
-    int bx, int c, int bkv, int T_len, int nchunks, int n_q_heads, int n_kv_heads, const T *__restrict__ k,
-    const T *__restrict__ v, const unsigned char *__restrict__ params, const float *__restrict__ state,
-    float *__restrict__ delta, float *__restrict__ tinit) {
+    int bx, int c, int bkv, int T_len, const int *__restrict__ lens, int nchunks, int n_q_heads, int n_kv_heads,
+    const T *__restrict__ k, const T *__restrict__ v, const unsigned char *__restrict__ params,
+    const float *__restrict__ state, float *__restrict__ delta, float *__restrict__ tinit) {
     constexpr int EPU = 16 / (int)sizeof(T);
     constexpr int LD = C + EPU;                         // padded row, 16-byte aligned
     constexpr int UPT = OAL_D / EPU;                    // 16-byte units per token row
@@ -195,6 +201,7 @@ __device__ __forceinline__ void scan_delta_block(
     const OalKvDev *kvd = kv_ptr(params, n_q_heads, bkv % n_kv_heads);
     const int nsteps = kvd->nsteps;
     if (bx == kScanBlocks && nsteps == 0) return;     // whole workgroup
+    const int Tb = oal_seq_len(lens, bkv / n_kv_heads, T_len);
     const bool idle = s >= OAL_KSTEPS + nsteps;             // only helps staging
 
     // stage: unit u = (array, 16-byte column a, token); consecutive lanes take consecutive
@@ -207,7 +214,7 @@ __device__ __forceinline__ void scan_delta_block(
             const int arr = u / (C * UPT), rem = u % (C * UPT), a = rem / C, tok = rem % C;
             const int pos = c * C + tok;
             const T *src = (arr ? v : k) + ((size_t)bkv * T_len + pos) * OAL_D + a * EPU;
-            r[j] = pos < T_len ? *reinterpret_cast<const oal_u32x4 *>(src) : zero16();
+            r[j] = pos < Tb ? *reinterpret_cast<const oal_u32x4 *>(src) : zero16();
         }
 #pragma unroll
         for (int j = 0; j < PER; ++j) {
@@ -219,7 +226,7 @@ __device__ __forceinline__ void scan_delta_block(
             for (int e = 0; e < EPU; ++e) dst[e * LD] = el[e];
         }
         for (int tok = tid; tok < C; tok += 64 * kScanWaves) {
-            s_kT[kRowOnes * LD + tok] = (c * C + tok < T_len) ? (T)1.0f : (T)0.0f;
+            s_kT[kRowOnes * LD + tok] = (c * C + tok < Tb) ? (T)1.0f : (T)0.0f;
             s_kT[kRowZero * LD + tok] = (T)0.0f;
         }
     }
@@ -287,11 +294,11 @@ __device__ __forceinline__ void scan_delta_block(
 
 template <typename T, int C>
 __global__ __launch_bounds__(64 * kScanWaves) void oal_scan_delta(
-    int T_len, int nchunks, int n_q_heads, int n_kv_heads, const T *__restrict__ k,
+    int T_len, const int *__restrict__ lens, int nchunks, int n_q_heads, int n_kv_heads, const T *__restrict__ k,
     const T *__restrict__ v, const unsigned char *__restrict__ params, const float *__restrict__ state,
     float *__restrict__ delta, float *__restrict__ tinit) {
-    scan_delta_block<T, C>(blockIdx.x, blockIdx.y, blockIdx.z, T_len, nchunks, n_q_heads, n_kv_heads, k, v,
-                           params, state, delta, tinit);
+    scan_delta_block<T, C>(blockIdx.x, blockIdx.y, blockIdx.z, T_len, lens, nchunks, n_q_heads, n_kv_heads, k,
+                           v, params, state, delta, tinit);
 }
 
 // one thread per (sequence x KV head, K-step, fragment): the state before each chunk is the
@@ -448,7 +455,8 @@ template <typename T, int C> struct IntraLayout {
 // accumulator-fragment order; the readout adds it before the divide.
 constexpr int kIntraWaves = 8;
 template <typename T, int C>
-__device__ __forceinline__ void intra_block(int Lb, int T_len, int n_q_heads, int n_kv_heads, int nchunks, int n_bkv,
+__device__ __forceinline__ void intra_block(int Lb, int T_len, const int *__restrict__ lens, int n_q_heads,
+                                            int n_kv_heads, int nchunks, int n_bkv,
                                             const T *__restrict__ q, const T *__restrict__ k,
                                             const T *__restrict__ v, const unsigned char *__restrict__ params,
                                             float *__restrict__ uintra) {
@@ -473,14 +481,15 @@ __device__ __forceinline__ void intra_block(int Lb, int T_len, int n_q_heads, in
     const int c = unit % nchunks, bkv = unit / nchunks;
     const int b = bkv / n_kv_heads, kv = bkv % n_kv_heads;
     const int n_rep = n_q_heads / n_kv_heads, h0 = kv * n_rep;
-    if (c * C + pi * 16 >= T_len) return;       // the pair's other tile lies further on
+    const int Tb = oal_seq_len(lens, b, T_len);
+    if (c * C + pi * 16 >= Tb) return;          // the pair's other tile lies further on
     const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
     const int g = lane >> 4, lr = lane & 15;
 
     // query row lr of tile qt for head i (dims 8g.. and 32 + 8g..)
     auto load_q = [&](int i, int qt, OalFrag<T> (&qf)[2]) {
         const int qpos = c * C + qt * 16 + lr;
-        const T *qr = q + (((size_t)b * n_q_heads + h0 + i) * T_len + (qpos < T_len ? qpos : 0)) * OAL_D + 8 * g;
+        const T *qr = q + (((size_t)b * n_q_heads + h0 + i) * T_len + (qpos < Tb ? qpos : 0)) * OAL_D + 8 * g;
         qf[0].load(qr);
         qf[1].load(qr + 32);
     };
@@ -501,7 +510,7 @@ __device__ __forceinline__ void intra_block(int Lb, int T_len, int n_q_heads, in
 #pragma unroll
         for (int j = 0; j < NKJ; ++j) {
             const int u = tid + NTH * j, key = u % C, a = u / C, pos = c * C + key;
-            const bool ok = u < NKU && pos < T_len;
+            const bool ok = u < NKU && pos < Tb;
             rk[j] = ok ? *reinterpret_cast<const oal_u32x4 *>(kb + (size_t)pos * OAL_D + a * EPU) : zero16();
             rv[j] = ok ? *reinterpret_cast<const oal_u32x4 *>(vb + (size_t)pos * OAL_D + a * EPU) : zero16();
         }
@@ -549,8 +558,8 @@ __device__ __forceinline__ void intra_block(int Lb, int T_len, int n_q_heads, in
         float qv[16];
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-            qv[e] = qpos < T_len ? (float)qf[0].v[e] : 0.0f;
-            qv[8 + e] = qpos < T_len ? (float)qf[1].v[e] : 0.0f;
+            qv[e] = qpos < Tb ? (float)qf[0].v[e] : 0.0f;
+            qv[8 + e] = qpos < Tb ? (float)qf[1].v[e] : 0.0f;
         }
         oal_f32x4 kap[NK + (NK & 1)];          // even count: key tiles go to the MFMA in pairs
 #pragma unroll
@@ -607,7 +616,7 @@ __device__ __forceinline__ void intra_block(int Lb, int T_len, int n_q_heads, in
 #pragma unroll
             for (int ii = 0; ii < 4; ++ii) {
                 const int kp = c * C + 16 * kt + 4 * g + ii;
-                if (!(kt < NK && kp <= qpos && kp < T_len)) kap[kt][ii] = 0.0f;
+                if (!(kt < NK && kp <= qpos && kp < Tb)) kap[kt][ii] = 0.0f;
             }
         oal_f32x4 acc[5];
 #pragma unroll
@@ -642,7 +651,7 @@ __device__ __forceinline__ void intra_block(int Lb, int T_len, int n_q_heads, in
 #pragma unroll
         for (int tt = 0; tt < 2; ++tt) {
             const int qt = tt == 0 ? pi : NQT - 1 - pi;
-            if (c * C + qt * 16 >= T_len) break;
+            if (c * C + qt * 16 >= Tb) break;
             if (i != wave || tt == 1) load_q(i, qt, qf);
             // NK = qt + 1 (the first tile of a pair has qt < NQT / 2, the second qt >= NQT / 2)
             auto run = [&](auto qt_c) { tile(std::integral_constant<int, decltype(qt_c)::value + 1>{}, i, qt); };
@@ -680,22 +689,22 @@ __device__ __forceinline__ void intra_block(int Lb, int T_len, int n_q_heads, in
 // rest are increment blocks (K-step block fastest, then chunk, then sequence x KV head).
 template <typename T, int C>
 __global__ __launch_bounds__(64 * kIntraWaves) __attribute__((amdgpu_waves_per_eu(4))) void oal_intra_delta(
-    int T_len, int n_q_heads, int n_kv_heads, int nchunks, int n_bkv, int n_delta, const T *__restrict__ q,
-    const T *__restrict__ k, const T *__restrict__ v, const unsigned char *__restrict__ params,
-    const float *__restrict__ state, float *__restrict__ delta, float *__restrict__ tinit,
-    float *__restrict__ uintra) {
+    int T_len, const int *__restrict__ lens, int n_q_heads, int n_kv_heads, int nchunks, int n_bkv, int n_delta,
+    const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ v,
+    const unsigned char *__restrict__ params, const float *__restrict__ state, float *__restrict__ delta,
+    float *__restrict__ tinit, float *__restrict__ uintra) {
     static_assert(kScanWaves == kIntraWaves, "one workgroup shape for both parts");
     const int n_intra = (int)gridDim.x - n_delta;
     const int id = blockIdx.x;
     if (id < n_intra) {
-        intra_block<T, C>(id, T_len, n_q_heads, n_kv_heads, nchunks, n_bkv, q, k, v, params, uintra);
+        intra_block<T, C>(id, T_len, lens, n_q_heads, n_kv_heads, nchunks, n_bkv, q, k, v, params, uintra);
     } else {
         constexpr int NB = kScanBlocks + 1;
         const int j = id - n_intra;
         const int bx = j % NB, rest = j / NB, c = rest % nchunks, bkv = rest / nchunks;
         if (bkv >= n_bkv) return;
-        scan_delta_block<T, C>(bx, c, bkv, T_len, nchunks, n_q_heads, n_kv_heads, k, v, params, state, delta,
-                               tinit);
+        scan_delta_block<T, C>(bx, c, bkv, T_len, lens, nchunks, n_q_heads, n_kv_heads, k, v, params, state,
+                               delta, tinit);
     }
 }
 
@@ -732,7 +741,7 @@ template <typename T, int C, int R> struct ReadoutLayout {
 // K-steps deep were both no faster.)
 template <typename T, int C, int R>
 __global__ __launch_bounds__(256, 2) void oal_readout(
-    int T_len, int n_q_heads, int n_kv_heads, int nchunks, int n_hgroups, int nunits,
+    int T_len, const int *__restrict__ lens, int n_q_heads, int n_kv_heads, int nchunks, int n_hgroups, int nunits,
     const T *__restrict__ q, const unsigned char *__restrict__ params,
     const unsigned char *__restrict__ snap, const float *__restrict__ uintra, float *__restrict__ y) {
     using Lay = ReadoutLayout<T, C, R>;
@@ -763,7 +772,8 @@ __global__ __launch_bounds__(256, 2) void oal_readout(
     const int hb = hs * RW;                       // first local head of this wave's subset
     const int nh = hs == 0 ? RW : R - RW;         // heads of the subset (0 when R == 1)
     const int pos0 = c * C + qt * 16;
-    if (pos0 >= T_len) return;
+    const int Tb = oal_seq_len(lens, b, T_len);
+    if (pos0 >= Tb) return;
     const bool general = reinterpret_cast<const OalParamsHeader *>(params)->general != 0;
     const OalKvDev *kvd = kv_ptr(params, n_q_heads, kv);
     const int ntail = kvd->nsteps;                // >= 3: linear features and the constant
@@ -796,7 +806,7 @@ __global__ __launch_bounds__(256, 2) void oal_readout(
         for (int j = 0; j < NQJ; ++j) {
             int u = tid + NT * j;
             int i = u / (16 * UPQ), qi = (u / UPQ) % 16, a = u % UPQ, pos = pos0 + qi;
-            rq[j] = (u < NQU && pos < T_len)
+            rq[j] = (u < NQU && pos < Tb)
                 ? *reinterpret_cast<const oal_u32x4 *>(q + (((size_t)b * n_q_heads + h0 + i) * T_len + pos) * OAL_D + a * EPU)
                 : zero16();
             const float4 *wp = reinterpret_cast<const float4 *>(head_ptr(params, h0 + (u < NQU ? i : 0))->w0 + a * EPU);
@@ -1024,7 +1034,7 @@ __global__ __launch_bounds__(256, 2) void oal_readout(
             float rd = __builtin_amdgcn_rcpf(den);
             rd = rd * (2.0f - den * rd);
             int pos = pos0 + 4 * g + ii;
-            if (pos < T_len) {
+            if (pos < Tb) {
 #pragma unroll
                 for (int n = 0; n < 4; ++n) yh[(size_t)pos * OAL_D + 16 * n + lr] = acc[li][n][ii] * rd;
             }
@@ -1058,7 +1068,7 @@ PrefillPlan make_plan(const oal_dims &d, int T_len, int C) {
 }
 
 template <typename T, int C, int R>
-hipError_t launch_readout(const oal_dims &d, int T_len, const PrefillPlan &p, const void *q,
+hipError_t launch_readout(const oal_dims &d, int T_len, const int *lens, const PrefillPlan &p, const void *q,
                           const void *params, const unsigned char *snap, const float *uintra, float *y,
                           hipStream_t stream) {
     int n_rep = d.n_q_heads / d.n_kv_heads;
@@ -1070,14 +1080,14 @@ hipError_t launch_readout(const oal_dims &d, int T_len, const PrefillPlan &p, co
     if (e != hipSuccess) return e;
     int nunits = p.nchunks * d.batch * d.n_kv_heads * n_hg;
     int nblocks = kXcds * (C / 16) * ((nunits + kXcds - 1) / kXcds);
-    hipLaunchKernelGGL(kern, dim3(nblocks), dim3(ReadoutLayout<T, C, R>::NT), lds, stream, T_len, d.n_q_heads, d.n_kv_heads,
+    hipLaunchKernelGGL(kern, dim3(nblocks), dim3(ReadoutLayout<T, C, R>::NT), lds, stream, T_len, lens, d.n_q_heads, d.n_kv_heads,
                        p.nchunks, n_hg, nunits, reinterpret_cast<const T *>(q),
                        reinterpret_cast<const unsigned char *>(params), snap, uintra, y);
     return hipGetLastError();
 }
 
 template <typename T, int C>
-hipError_t launch_all(const oal_dims &d, int T_len, const void *q, const void *k, const void *v,
+hipError_t launch_all(const oal_dims &d, int T_len, const int *lens, const void *q, const void *k, const void *v,
                       const void *params, float *state, void *ws, float *y, hipStream_t stream,
                       hipEvent_t *marks) {
     PrefillPlan p = make_plan<T>(d, T_len, C);
@@ -1099,7 +1109,7 @@ hipError_t launch_all(const oal_dims &d, int T_len, const void *q, const void *k
         const int nunits = p.nchunks * bkv;
         const int n_intra = kXcds * (C / 32) * ((nunits + kXcds - 1) / kXcds);   // tile pairs
         const int n_delta = (kScanBlocks + 1) * p.nchunks * bkv;
-        hipLaunchKernelGGL(kern, dim3(n_intra + n_delta), dim3(64 * kIntraWaves), lds, stream, T_len,
+        hipLaunchKernelGGL(kern, dim3(n_intra + n_delta), dim3(64 * kIntraWaves), lds, stream, T_len, lens,
                            d.n_q_heads, d.n_kv_heads, p.nchunks, bkv, n_delta, reinterpret_cast<const T *>(q),
                            reinterpret_cast<const T *>(k), reinterpret_cast<const T *>(v), pb, state, delta,
                            tinit, uintra);
@@ -1111,7 +1121,7 @@ hipError_t launch_all(const oal_dims &d, int T_len, const void *q, const void *k
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds)) != hipSuccess)
             return e;
         hipLaunchKernelGGL(kern, dim3(kScanBlocks + 1, p.nchunks, bkv), dim3(64 * kScanWaves), lds, stream,
-                           T_len, p.nchunks, d.n_q_heads, d.n_kv_heads, reinterpret_cast<const T *>(k),
+                           T_len, lens, p.nchunks, d.n_q_heads, d.n_kv_heads, reinterpret_cast<const T *>(k),
                            reinterpret_cast<const T *>(v), pb, state, delta, tinit);
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
@@ -1128,15 +1138,15 @@ hipError_t launch_all(const oal_dims &d, int T_len, const void *q, const void *k
     int n_rep = d.n_q_heads / d.n_kv_heads;
     auto fits = [](size_t bytes) { return bytes <= (size_t)kMaxLds; };
     if (n_rep % 8 == 0 && fits(readout_lds<T, C, 8>()))
-        e = launch_readout<T, C, 8>(d, T_len, p, q, params, snap, uintra, y, stream);
+        e = launch_readout<T, C, 8>(d, T_len, lens, p, q, params, snap, uintra, y, stream);
     else if (n_rep % 7 == 0 && fits(readout_lds<T, C, 7>()))
-        e = launch_readout<T, C, 7>(d, T_len, p, q, params, snap, uintra, y, stream);
+        e = launch_readout<T, C, 7>(d, T_len, lens, p, q, params, snap, uintra, y, stream);
     else if (n_rep % 4 == 0 && fits(readout_lds<T, C, 4>()))
-        e = launch_readout<T, C, 4>(d, T_len, p, q, params, snap, uintra, y, stream);
+        e = launch_readout<T, C, 4>(d, T_len, lens, p, q, params, snap, uintra, y, stream);
     else if (n_rep % 2 == 0 && fits(readout_lds<T, C, 2>()))
-        e = launch_readout<T, C, 2>(d, T_len, p, q, params, snap, uintra, y, stream);
+        e = launch_readout<T, C, 2>(d, T_len, lens, p, q, params, snap, uintra, y, stream);
     else
-        e = launch_readout<T, C, 1>(d, T_len, p, q, params, snap, uintra, y, stream);
+        e = launch_readout<T, C, 1>(d, T_len, lens, p, q, params, snap, uintra, y, stream);
     if (e == hipSuccess && marks) e = hipEventRecord(marks[2], stream);
     return e;
 }
@@ -1148,15 +1158,15 @@ size_t oal_prefill_ws_bytes_impl(const oal_dims &d, int T_len, int C) {
     return p.snap_bytes + p.delta_bytes + p.tinit_bytes + p.uintra_bytes;
 }
 
-hipError_t oal_launch_prefill(const oal_dims &d, int T_len, int C, const void *q, const void *k,
+hipError_t oal_launch_prefill(const oal_dims &d, int T_len, const int *lens, int C, const void *q, const void *k,
                               const void *v, const void *params, float *state, void *ws, float *y,
                               hipStream_t stream, hipEvent_t *marks) {
     if (d.dtype == OAL_BF16) {
-        if (C == 64) return launch_all<__bf16, 64>(d, T_len, q, k, v, params, state, ws, y, stream, marks);
-        if (C == 128) return launch_all<__bf16, 128>(d, T_len, q, k, v, params, state, ws, y, stream, marks);
-        return launch_all<__bf16, 256>(d, T_len, q, k, v, params, state, ws, y, stream, marks);
+        if (C == 64) return launch_all<__bf16, 64>(d, T_len, lens, q, k, v, params, state, ws, y, stream, marks);
+        if (C == 128) return launch_all<__bf16, 128>(d, T_len, lens, q, k, v, params, state, ws, y, stream, marks);
+        return launch_all<__bf16, 256>(d, T_len, lens, q, k, v, params, state, ws, y, stream, marks);
     }
-    if (C == 64) return launch_all<float, 64>(d, T_len, q, k, v, params, state, ws, y, stream, marks);
-    if (C == 128) return launch_all<float, 128>(d, T_len, q, k, v, params, state, ws, y, stream, marks);
-    return launch_all<float, 256>(d, T_len, q, k, v, params, state, ws, y, stream, marks);
+    if (C == 64) return launch_all<float, 64>(d, T_len, lens, q, k, v, params, state, ws, y, stream, marks);
+    if (C == 128) return launch_all<float, 128>(d, T_len, lens, q, k, v, params, state, ws, y, stream, marks);
+    return launch_all<float, 256>(d, T_len, lens, q, k, v, params, state, ws, y, stream, marks);
 }

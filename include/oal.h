@@ -148,6 +148,17 @@ oal_status oal_prefill_timed(const oal_dims *dims, int32_t T, int32_t chunk, con
                              float *state_dev, void *workspace, float *y, hipStream_t stream,
                              hipEvent_t marks[3]);
 
+/* oal_prefill for a ragged batch (sequences of different lengths, padded to T): sequence b
+ * takes the first lengths[b] tokens of its rows of q, k, v ([batch, heads, T, 64], as in
+ * oal_prefill) and its state advances by that many tokens; y rows at positions >= lengths[b]
+ * are not written. Same kernels, chunk sizes and workspace as oal_prefill with this T.
+ *   lengths -- [batch] int32 (device, 4-byte aligned); each value is clamped to [0, T] in
+ *              the kernels (0 leaves the sequence's state unchanged).
+ * A batch whose lengths are all T gives the results of oal_prefill. */
+oal_status oal_prefill_varlen(const oal_dims *dims, int32_t T, const int32_t *lengths, int32_t chunk,
+                              const void *q, const void *k, const void *v, const void *params_dev,
+                              float *state_dev, void *workspace, float *y, hipStream_t stream);
+
 /* One decode step: appends one token per sequence to the prefix states and reads out the
  * attention of each query head over all tokens so far (the new one included).
  *   q [batch, n_q_heads, 64], k, v [batch, n_kv_heads, 64] of dims->dtype (device);

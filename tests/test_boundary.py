@@ -80,6 +80,10 @@ def test_validation_errors_enqueue_nothing():
     assert _code(gpq.oal_decode_step, d, A, A, A, A + 8, A, A, A, 0) == 4
     assert _code(gpq.oal_decode_step, gpq.make_dims(1, 17, 1, "bf16"), *([A] * 7), 0) == 5
     assert _code(gpq.oal_decode_step, gpq.make_dims(0, 2, 1, "bf16"), *([None] * 7), 0) == 0
+    assert _code(gpq.oal_prefill_varlen, d, 8, None, 64, *ok, 0) == 1           # no lengths
+    assert _code(gpq.oal_prefill_varlen, d, 8, A + 2, 64, *ok, 0) == 4          # misaligned lengths
+    assert _code(gpq.oal_prefill_varlen, d, 8, A, 100, *ok, 0) == 5             # chunk
+    assert _code(gpq.oal_prefill_varlen, d, 0, None, 64, *([None] * 7), 0) == 0  # T = 0: no-op
     ix = (A, A, A, A, A, A, A)   # q, k, v, params, pool, workspace, y
     assert _code(gpq.oal_decode_step_indexed, d, A, 0, *ix, 0) == 2         # empty pool
     assert _code(gpq.oal_decode_step_indexed, d, None, 4, *ix, 0) == 1      # no slots

@@ -119,3 +119,90 @@ def test_indexed_decode_serving_shape_bitwise():
                              [(n, h, T0) for n in range(3) for h in (0, 7, 13)])
     got = np.stack([y[j, h].cpu().numpy() for j, h, _ in rows])
     assert oracle.row_error(got, want) <= TOL["bf16"]
+
+
+# ---------------------------------------------------------------------------------------
+# ragged prefill (oal_prefill_varlen): sequence b of a batch padded to T takes lengths[b] tokens
+
+def _varlen_run(inp, lengths, chunk, sentinel=7.0):
+    B, Hq, Hkv, T, _, _ = inp.dims
+    sess = Session(B, Hq, Hkv, inp.dtype, inp.params, T, chunk)
+    lens = torch.tensor(lengths, dtype=torch.int32, device="cuda")
+    y = torch.full((B, Hq, T, 64), sentinel, dtype=torch.float32, device="cuda")
+    gpq.oal_prefill_varlen(sess.dims, T, lens, chunk, to_dev(inp.q, inp.dtype), to_dev(inp.k, inp.dtype),
+                           to_dev(inp.v, inp.dtype), sess.params, sess.state, sess.ws, y)
+    torch.cuda.synchronize()
+    return sess, y.cpu().numpy()
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("chunk", [64, 128])
+def test_varlen_prefill_small(dtype, chunk):
+    lengths = [300, 129, 1, 0, 64]
+    inp = small(601, len(lengths), 4, 2, 300, dtype)
+    sess, y = _varlen_run(inp, lengths, chunk)
+    S = sess.state_np()
+    from gpu_util import state_ok
+    for b, L in enumerate(lengths):
+        assert np.all(y[b, :, L:] == 7.0), f"sequence {b}: rows past its length were written"
+        if L == 0:
+            assert np.all(S[b] == 0.0)
+            continue
+        sl = slice(b, b + 1)
+        ref = oracle.dense(inp.q[sl, :, :L], inp.k[sl, :, :L], inp.v[sl, :, :L], inp.params)
+        err = oracle.row_error(y[sl, :, :L], ref)
+        print(f"[parity] varlen {dtype} C={chunk} seq {b} len {L}: err={err:.2e}", flush=True)
+        assert err <= TOL[dtype]
+        assert state_ok(S[sl], inp.k[sl, :, :L], inp.v[sl, :, :L], dtype)
+
+
+def test_varlen_full_lengths_equal_plain_prefill_and_clamping():
+    inp = small(602, 3, 14, 2, 257, "bf16")
+    B, Hq, Hkv, T, _, _ = inp.dims
+    # lengths above T are clamped to T, negative ones to 0
+    sess, y = _varlen_run(inp, [T, T + 50, -3], 128)
+    plain = Session(B, Hq, Hkv, "bf16", inp.params, T, 128)
+    y_plain = plain.prefill(inp.q, inp.k, inp.v, 128).cpu().numpy()
+    assert np.array_equal(y[:2], y_plain[:2])
+    S, S_plain = sess.state_np(), plain.state_np()
+    assert np.array_equal(S[:2], S_plain[:2]) and np.all(S[2] == 0.0) and np.all(y[2] == 7.0)
+
+
+def test_varlen_then_decode():
+    lengths = [200, 77]
+    inp = small(603, 2, 4, 2, 201, "bf16")
+    sess, _ = _varlen_run(inp, lengths, 128)
+    # next token of each sequence = its token at position lengths[b]
+    q = to_dev(np.stack([inp.q[b, :, L] for b, L in enumerate(lengths)]), "bf16")
+    k = to_dev(np.stack([inp.k[b, :, L] for b, L in enumerate(lengths)]), "bf16")
+    v = to_dev(np.stack([inp.v[b, :, L] for b, L in enumerate(lengths)]), "bf16")
+    yd = sess.decode(q, k, v).cpu().numpy()
+    for b, L in enumerate(lengths):
+        sl = slice(b, b + 1)
+        want = oracle.dense_rows(inp.q[sl, :, :L + 1], inp.k[sl, :, :L + 1], inp.v[sl, :, :L + 1],
+                                 inp.params, [(0, h, L) for h in range(4)])
+        assert oracle.row_error(yd[b], want) <= TOL["bf16"]
+
+
+def test_varlen_batch8_4096_sampled():
+    # ragged serving batch at the layer's full size: 8 sequences padded to 4096 tokens
+    inp = qwen_like(8, 4096, 11, name="ragged", per_seq_seeds=[1100 + b for b in range(8)])
+    lengths = [4096, 1, 4095, 2048, 129, 3000, 64, 1777]
+    sess, y = _varlen_run(inp, lengths, 128)
+    rng = np.random.default_rng(12)
+    for b, L in enumerate(lengths):
+        assert np.all(y[b, :, L:] == 7.0)
+        pos = sorted({0, L - 1, *rng.integers(0, L, size=3).tolist()})
+        heads = (0, 7, 13)
+        sl = slice(b, b + 1)
+        want = oracle.dense_rows(inp.q[sl, :, :L], inp.k[sl, :, :L], inp.v[sl, :, :L], inp.params,
+                                 [(0, h, i) for h in heads for i in pos])
+        got = np.stack([y[b, h, i] for h in heads for i in pos])
+        err = oracle.row_error(got, want)
+        print(f"[parity] varlen B=8x4096 seq {b} len {L}: err={err:.2e}", flush=True)
+        assert err <= TOL["bf16"]
+    from gpu_util import state_ok
+    S = sess.state_np()
+    for b in (3, 6):
+        L = lengths[b]
+        assert state_ok(S[b:b + 1], inp.k[b:b + 1, :, :L], inp.v[b:b + 1, :, :L], "bf16")
