@@ -96,3 +96,33 @@ def test_decode_loop_graph_replays_match_eager():
         for s in range(steps):
             assert torch.equal(ys[s], ys_ref[s]), f"replay {rep} step {s}"
         assert torch.equal(base.state, end_ref)
+
+
+def test_concurrent_streams_match_sequential():
+    # independent sequences on two streams at once (their own params, states, workspaces):
+    # the library keeps no global mutable state, so results equal those of sequential calls
+    B, Hq, Hkv, T = 2, 14, 2, 513
+    ins = [small(811 + i, B, Hq, Hkv, T + 1, "bf16") for i in range(2)]
+    seq_out = []
+    for inp in ins:
+        s = Session(B, Hq, Hkv, "bf16", inp.params, T, 128)
+        y = s.prefill(inp.q[:, :, :T], inp.k[:, :, :T], inp.v[:, :, :T], 128)
+        yd = s.decode(inp.q[:, :, T], inp.k[:, :, T], inp.v[:, :, T])
+        torch.cuda.synchronize()
+        seq_out.append((y.clone(), yd.clone(), s.state.clone()))
+    sessions = [Session(B, Hq, Hkv, "bf16", inp.params, T, 128) for inp in ins]
+    dev = [tuple(to_dev(x[:, :, :T], "bf16") for x in (inp.q, inp.k, inp.v)) for inp in ins]
+    dev1 = [tuple(to_dev(x[:, :, T], "bf16") for x in (inp.q, inp.k, inp.v)) for inp in ins]
+    ys = [torch.empty((B, Hq, T, 64), dtype=torch.float32, device="cuda") for _ in ins]
+    yds = [torch.empty((B, Hq, 64), dtype=torch.float32, device="cuda") for _ in ins]
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    for i, st in enumerate(streams):
+        with torch.cuda.stream(st):
+            s = sessions[i]
+            gpq.oal_prefill(s.dims, T, 128, *dev[i], s.params, s.state, s.ws, ys[i], stream=st)
+            gpq.oal_decode_step(s.dims, *dev1[i], s.params, s.state, s.dws, yds[i], stream=st)
+    torch.cuda.synchronize()
+    for i in range(2):
+        assert torch.equal(ys[i], seq_out[i][0]) and torch.equal(yds[i], seq_out[i][1])
+        assert torch.equal(sessions[i].state, seq_out[i][2])
