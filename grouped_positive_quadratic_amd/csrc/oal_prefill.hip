@@ -496,6 +496,14 @@ __device__ __forceinline__ void intra_block(int Lb, int T_len, const int *__rest
     };
     OalFrag<T> qf[2];
     if (wave < n_rep) load_q(wave, pi, qf);     // fetched before the staging
+    // the head's scalars (group count, eps, L00), also requested before the staging: read at
+    // the start of a tile they put a memory round trip in front of every tile
+    struct HeadScalars { int G; float eps, L00; };
+    auto head_scalars = [&](int i) {
+        const OalHeadDev *hd = head_ptr(params, h0 + i);
+        return HeadScalars{hd->G, hd->eps, hd->L00};
+    };
+    HeadScalars hsc = head_scalars(wave < n_rep ? wave : 0);
 
     // stage every key of the chunk (zero past T), V^T of them, and Lz rows of every head;
     // all loads are issued before the first LDS write
@@ -554,8 +562,8 @@ __device__ __forceinline__ void intra_block(int Lb, int T_len, const int *__rest
         constexpr int NK = decltype(nk_c)::value;
         const int qpos = c * C + qt * 16 + lr;
         const OalHeadDev *hd = head_ptr(params, h0 + i);
-        const int G = hd->G;
-        const float eps = hd->eps, L00 = hd->L00;
+        const int G = hsc.G;
+        const float eps = hsc.eps, L00 = hsc.L00;
         float qv[16];
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
@@ -649,6 +657,7 @@ __device__ __forceinline__ void intra_block(int Lb, int T_len, const int *__rest
     };
     static_assert(NQT % 2 == 0 && NQT <= 16, "tile pairs");
     for (int i = wave; i < n_rep; i += kIntraWaves) {
+        if (i != wave) hsc = head_scalars(i);
 #pragma unroll
         for (int tt = 0; tt < 2; ++tt) {
             const int qt = tt == 0 ? pi : NQT - 1 - pi;
