@@ -12,7 +12,9 @@ Wraps ``oal_oracle.c`` (fp64 loops, OpenMP over output rows) through ctypes:
 * ``recurrence``  -- the H0/H1/H2 recurrence of the same section with full d x d H2;
 * ``state``       -- the prefix states with H2 as an upper triangle (the library's layout);
 * ``contribution`` -- the causal contribution score chi of every q/k dim per prompt and its
-                     mean over prompts (same section, first display), O(T^2) over pairs.
+                     mean over prompts (same section, first display), O(T^2) over pairs;
+* ``backward``    -- gradients of the dense definition (dq, dk, dv, dL, deps) for an upstream
+                     gradient dy, by the chain rule through every causal pair.
 """
 from __future__ import annotations
 
@@ -54,6 +56,7 @@ def _load():
         lib.oal_oracle_kappa.restype = ctypes.c_double
         lib.oal_oracle_kappa_matrix.argtypes = [I, I, I, I, I, P, P, P, P, I, P, P, I, I, P]
         lib.oal_oracle_contribution.argtypes = [I, I, I, I, I, P, P, P, P]
+        lib.oal_oracle_backward.argtypes = [I, I, I, I, I, I, P, P, P, P, P, I, P, P, P, P, P, P, P, P]
         lib.oal_oracle_num_threads.restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -185,6 +188,25 @@ def contribution(q, k):
     if rc:
         raise ValueError(f"oal_oracle_contribution: bad arguments (code {rc})")
     return chi, chi_mean
+
+
+def backward(q, k, v, params, dy):
+    """Gradients (dq, dk, dv, dL, deps) of sum(dy * y) for y = dense(q, k, v, params), fp64.
+    dL has the shape of params.L (lower triangle of rows/cols 0..G_h, the rest zero)."""
+    lib = _load()
+    q, k, v, dy = _f64(q), _f64(k), _f64(v), _f64(dy)
+    B, Hq, T, d = q.shape
+    Hkv, dv = k.shape[1], v.shape[-1]
+    ng, gam, gmax, L, eps = _params(params)
+    dq, dk, dvo = np.empty_like(q), np.empty_like(k), np.empty_like(v)
+    dL = np.empty_like(L)
+    deps = np.empty(Hq)
+    rc = lib.oal_oracle_backward(B, Hq, Hkv, T, d, dv, _ptr(q), _ptr(k), _ptr(v), _ptr(ng),
+                                 _ptr(gam), gmax, _ptr(L), _ptr(eps), _ptr(dy), _ptr(dq),
+                                 _ptr(dk), _ptr(dvo), _ptr(dL), _ptr(deps))
+    if rc:
+        raise ValueError(f"oal_oracle_backward: bad arguments (code {rc})")
+    return dq, dk, dvo, dL, deps
 
 
 def row_error(y, y_ref):

@@ -323,3 +323,112 @@ int oal_oracle_contribution(int B, int Hq, int Hkv, int T, int d, const double *
     }
     return 0;
 }
+
+/*
+ * Gradients of the dense definition (section "核心公式": s-bar, kappa and readout displays)
+ * for an upstream gradient dy = dLoss/dy, by the chain rule through every causal pair:
+ *   y_i = num_i / den_i,  num_i = sum_{j<=i} kappa_ij v_j,  den_i = sum_{j<=i} kappa_ij
+ *   dnum_i = dy_i / den_i,  dden_i = -(dy_i . y_i) / den_i
+ *   per pair (j <= i):  dkappa = dnum_i . v_j + dden_i;  dv_j += kappa_ij dnum_i;  deps += dkappa
+ *   kappa = eps + sum_m z_m^2,  z_m = sum_{g >= m} L[g][m] s-bar_g
+ *     dz_m = 2 z_m dkappa;  dL[g][m] += s-bar_g dz_m (g >= m);  ds-bar_g = sum_{m <= g} L[g][m] dz_m
+ *   s-bar_{1+gamma(r)} collects q_r k_r / sqrt(d):  dq_ir += ds-bar_{1+gamma(r)} k_jr / sqrt(d),
+ *                                                   dk_jr += ds-bar_{1+gamma(r)} q_ir / sqrt(d)
+ * Inputs as in oal_oracle_dense plus dy [B,Hq,T,dv]. Outputs: dq [B,Hq,T,d], dk [B,Hkv,T,d],
+ * dv_out [B,Hkv,T,dv], dL [Hq,(g_max+1)^2] (lower triangle rows/cols 0..G_h; the rest zero),
+ * deps [Hq]. Parallel over (sequence, KV head); per-(sequence, head) partials of dL and deps
+ * are summed in sequence order afterwards.
+ */
+int oal_oracle_backward(int B, int Hq, int Hkv, int T, int d, int dv, const double *q,
+                        const double *k, const double *v, const int *n_groups,
+                        const uint8_t *group_of_dim, int g_max, const double *L, const double *eps,
+                        const double *dy, double *dq, double *dk, double *dv_out, double *dL,
+                        double *deps) {
+    int rc = check_args(B, Hq, Hkv, T, d, dv, n_groups, group_of_dim, g_max);
+    if (rc || dv > 1024) return rc ? rc : 5;
+    const int rep = Hq / Hkv, gm1 = g_max + 1;
+    const double inv_sqrt_d = 1.0 / sqrt((double)d);
+    double *dL_part = (double *)calloc((size_t)B * Hq * gm1 * gm1, sizeof(double));
+    double *de_part = (double *)calloc((size_t)B * Hq, sizeof(double));
+    if (!dL_part || !de_part) { free(dL_part); free(de_part); return 6; }
+    memset(dq, 0, (size_t)B * Hq * T * d * sizeof(double));
+    memset(dk, 0, (size_t)B * Hkv * T * d * sizeof(double));
+    memset(dv_out, 0, (size_t)B * Hkv * T * dv * sizeof(double));
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int bk = 0; bk < B * Hkv; ++bk) {
+        const int b = bk / Hkv, kv = bk % Hkv;
+        const double *kb = k + (size_t)bk * T * d;
+        const double *vb = v + (size_t)bk * T * dv;
+        double *dkb = dk + (size_t)bk * T * d;
+        double *dvb = dv_out + (size_t)bk * T * dv;
+        double yrow[1024], dnum[1024];
+        for (int h = kv * rep; h < (kv + 1) * rep; ++h) {
+            const int G = n_groups[h];
+            const double *Lh = L + (size_t)h * gm1 * gm1;
+            const uint8_t *gam = group_of_dim + (size_t)h * d;
+            double *dLh = dL_part + ((size_t)b * Hq + h) * gm1 * gm1;
+            double de = 0.0;
+            for (int i = 0; i < T; ++i) {
+                const double *qi = q + (((size_t)b * Hq + h) * T + i) * d;
+                double *dqi = dq + (((size_t)b * Hq + h) * T + i) * d;
+                const double *dyi = dy + (((size_t)b * Hq + h) * T + i) * dv;
+                double den;
+                dense_row(Hq, Hkv, T, d, dv, b, h, i, q, k, v, n_groups, group_of_dim, g_max, L,
+                          eps, yrow, &den);
+                double dden = 0.0;
+                for (int c = 0; c < dv; ++c) {
+                    dnum[c] = dyi[c] / den;
+                    dden -= dyi[c] * yrow[c];
+                }
+                dden /= den;
+                for (int j = 0; j <= i; ++j) {
+                    const double *kj = kb + (size_t)j * d;
+                    double sbar[65 + 1], z[65 + 1], dsbar[65 + 1];
+                    sbar[0] = 1.0;
+                    for (int g = 1; g <= G; ++g) sbar[g] = 0.0;
+                    for (int r = 0; r < d; ++r) sbar[1 + gam[r]] += qi[r] * kj[r] * inv_sqrt_d;
+                    double kap = eps[h];
+                    for (int m = 0; m <= G; ++m) {
+                        z[m] = 0.0;
+                        for (int g = m; g <= G; ++g) z[m] += Lh[g * gm1 + m] * sbar[g];
+                        kap += z[m] * z[m];
+                    }
+                    double dkap = dden;
+                    for (int c = 0; c < dv; ++c) {
+                        dkap += dnum[c] * vb[(size_t)j * dv + c];
+                        dvb[(size_t)j * dv + c] += kap * dnum[c];
+                    }
+                    de += dkap;
+                    for (int g = 0; g <= G; ++g) dsbar[g] = 0.0;
+                    for (int m = 0; m <= G; ++m) {
+                        const double dz = 2.0 * z[m] * dkap;
+                        for (int g = m; g <= G; ++g) {
+                            dLh[g * gm1 + m] += sbar[g] * dz;
+                            dsbar[g] += Lh[g * gm1 + m] * dz;
+                        }
+                    }
+                    double *dkj = dkb + (size_t)j * d;
+                    for (int r = 0; r < d; ++r) {
+                        const double ds = dsbar[1 + gam[r]] * inv_sqrt_d;
+                        dqi[r] += ds * kj[r];
+                        dkj[r] += ds * qi[r];
+                    }
+                }
+            }
+            de_part[(size_t)b * Hq + h] = de;
+        }
+    }
+    for (int h = 0; h < Hq; ++h) {
+        double de = 0.0;
+        for (int e = 0; e < gm1 * gm1; ++e) dL[(size_t)h * gm1 * gm1 + e] = 0.0;
+        for (int b = 0; b < B; ++b) {
+            de += de_part[(size_t)b * Hq + h];
+            for (int e = 0; e < gm1 * gm1; ++e)
+                dL[(size_t)h * gm1 * gm1 + e] += dL_part[((size_t)b * Hq + h) * gm1 * gm1 + e];
+        }
+        deps[h] = de;
+    }
+    free(dL_part);
+    free(de_part);
+    return 0;
+}

@@ -248,7 +248,8 @@ MUTATIONS = {
     "no_inv_sqrt_d": ("sbar[g] *= inv_sqrt_d;", "sbar[g] *= 1.0;"),
     "group_offset": ("sbar[1 + group_of_dim[r]] += q[r] * k[r];",
                      "sbar[group_of_dim[r]] += q[r] * k[r];"),
-    "exclusive_causal": ("for (int j = 0; j <= i; ++j) {", "for (int j = 0; j < i || j == 0; ++j) {"),
+    "exclusive_causal": ("for (int j = 0; j <= i; ++j) {               /* causal, inclusive: j <= i */",
+                         "for (int j = 0; j < i || j == 0; ++j) {"),
     "dropped_eps": ("double kap = eps;", "double kap = 0.0;"),
 }
 
@@ -418,5 +419,138 @@ def test_contribution_pins_catch_planted_mistakes(name, tmp_path):
             except AssertionError:
                 failed.append(test.__name__)
         assert failed, f"planted mistake {name} passed the contribution pins"
+    finally:
+        oracle._lib = saved
+
+
+# --------------------------------------------------------------------------------------
+# 12. Backward of the dense definition (oracle.backward): gradients of sum(dy * y) with
+# respect to q, k, v, L and eps, pinned by central finite differences of oracle.dense (fp64;
+# L and eps as fp64 arrays so that the perturbations are exact), a closed form for L = 0,
+# and the scale invariance of y under (L, eps) -> (a L, a^2 eps).
+
+def _bwd_case(seed, B=1, Hq=2, Hkv=1, T=5, d=4, dv=3, g_hi=3):
+    q, k, v, p = _case(seed, B, Hq, Hkv, T, d, dv, g_hi=g_hi)
+    p64 = HeadParams(p.n_groups, p.group_of_dim, p.L.astype(np.float64), p.eps.astype(np.float64) + 0.05)
+    dy = np.random.default_rng(seed + 1).standard_normal((B, Hq, T, dv))
+    return q, k, v, p64, dy
+
+
+def _loss(q, k, v, p, dy):
+    return float((oracle.dense(q, k, v, p) * dy).sum())
+
+
+def _fd(f, x, idx, h=1e-6):
+    xp, xm = x.copy(), x.copy()
+    xp[idx] += h
+    xm[idx] -= h
+    return (f(xp) - f(xm)) / (2 * h)
+
+
+@pytest.mark.parametrize("seed", [31, 32])
+def test_backward_matches_finite_differences(seed):
+    # Catches: a wrong sign or missing term in the denominator gradient, a dropped factor 2
+    # of dz, a missing 1/sqrt(d), a transposed L index, dk/dv sums over the wrong pairs.
+    q, k, v, p, dy = _bwd_case(seed)
+    dq, dk, dv, dL, deps = oracle.backward(q, k, v, p, dy)
+    rng = np.random.default_rng(seed + 2)
+    checks = []
+    for arr, grad, name in ((q, dq, "q"), (k, dk, "k"), (v, dv, "v")):
+        for _ in range(6):
+            idx = tuple(int(rng.integers(0, s)) for s in arr.shape)
+            if name == "q":
+                f = lambda x: _loss(x, k, v, p, dy)
+            elif name == "k":
+                f = lambda x: _loss(q, x, v, p, dy)
+            else:
+                f = lambda x: _loss(q, k, x, p, dy)
+            checks.append((name, idx, _fd(f, arr, idx), grad[idx]))
+    for h in range(p.L.shape[0]):
+        G = int(p.n_groups[h])
+        for a in range(G + 1):
+            for c in range(a + 1):
+                def f(x, h=h, a=a, c=c):
+                    return _loss(q, k, v, HeadParams(p.n_groups, p.group_of_dim, x, p.eps), dy)
+                checks.append(("L", (h, a, c), _fd(f, p.L, (h, a, c)), dL[h, a, c]))
+        def fe(x):
+            return _loss(q, k, v, HeadParams(p.n_groups, p.group_of_dim, p.L, x), dy)
+        checks.append(("eps", (h,), _fd(fe, p.eps, (h,)), deps[h]))
+    for name, idx, num, ana in checks:
+        assert abs(num - ana) <= 1e-6 * (1.0 + abs(num)), (name, idx, num, ana)
+    # entries outside each head's lower triangle carry no gradient
+    for h in range(p.L.shape[0]):
+        G = int(p.n_groups[h])
+        mask = np.tril(np.ones_like(dL[h]))
+        mask[G + 1:, :] = 0
+        assert np.all(dL[h][mask == 0] == 0.0)
+
+
+def test_backward_l_zero_closed_form():
+    # L = 0: kappa = eps for every pair, y_i is the prefix mean of v, so dv_j = sum_{i>=j}
+    # dy_i / (i+1), dq = dk = 0, and deps = 0 (y does not depend on a constant kernel's size).
+    q, k, v, p, dy = _bwd_case(41, Hq=2, T=6)
+    pz = HeadParams(p.n_groups, p.group_of_dim, np.zeros_like(p.L), p.eps)
+    dq, dk, dv, dL, deps = oracle.backward(q, k, v, pz, dy)
+    T = q.shape[2]
+    want = np.zeros_like(v)
+    for h in range(2):
+        for j in range(T):
+            want[0, 0, j] += sum(dy[0, h, i] / (i + 1) for i in range(j, T))
+    np.testing.assert_allclose(dv, want, rtol=1e-12, atol=1e-14)
+    assert np.abs(dq).max() == 0.0 and np.abs(dk).max() == 0.0
+    np.testing.assert_allclose(deps, 0.0, atol=1e-12)
+    assert np.abs(dL).max() == 0.0
+
+
+def test_backward_scale_invariance():
+    # y(a L, a^2 eps) = y(L, eps), so d/da at a = 1: sum(L * dL) + 2 eps deps = 0 per head.
+    q, k, v, p, dy = _bwd_case(43, Hq=3, Hkv=1, T=7, d=8, dv=4)
+    _, _, _, dL, deps = oracle.backward(q, k, v, p, dy)
+    for h in range(3):
+        s = float((p.L[h] * dL[h]).sum() + 2 * p.eps[h] * deps[h])
+        scale = float(np.abs(p.L[h] * dL[h]).sum() + abs(2 * p.eps[h] * deps[h]))
+        assert abs(s) <= 1e-10 * max(scale, 1.0), (h, s, scale)
+
+
+BWD_MUTATIONS = {
+    "bwd_dden_sign": ("dden -= dyi[c] * yrow[c];", "dden += dyi[c] * yrow[c];"),
+    "bwd_no_factor_2": ("const double dz = 2.0 * z[m] * dkap;", "const double dz = z[m] * dkap;"),
+    "bwd_no_inv_sqrt_d": ("const double ds = dsbar[1 + gam[r]] * inv_sqrt_d;",
+                          "const double ds = dsbar[1 + gam[r]];"),
+    "bwd_L_transposed": ("dsbar[g] += Lh[g * gm1 + m] * dz;", "dsbar[g] += Lh[m * gm1 + g] * dz;"),
+    "bwd_dv_no_kappa": ("dvb[(size_t)j * dv + c] += kap * dnum[c];", "dvb[(size_t)j * dv + c] += dnum[c];"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(BWD_MUTATIONS))
+def test_backward_pins_catch_planted_mistakes(name, tmp_path):
+    if shutil.which("gcc") is None:
+        pytest.skip("gcc not available")
+    src = open(oracle._SRC).read()
+    old, new = BWD_MUTATIONS[name]
+    assert src.count(old) == 1, f"mutation anchor for {name} not found"
+    mfile = tmp_path / "mut.c"
+    mfile.write_text(src.replace(old, new))
+    so = tmp_path / "libmut.so"
+    subprocess.check_call(["gcc", "-O1", "-fPIC", "-shared", "-o", str(so), str(mfile), "-lm"])
+    lib = ctypes.CDLL(str(so))
+    saved = oracle._lib
+    try:
+        oracle._lib = None
+        real = oracle._load()
+        for fn in ("oal_oracle_backward", "oal_oracle_dense", "oal_oracle_kappa"):
+            getattr(lib, fn).argtypes = getattr(real, fn).argtypes
+        lib.oal_oracle_kappa.restype = ctypes.c_double
+        # the mutant library's forward is the real one (only the backward was changed): the
+        # finite-difference pin must fail against the mutant's backward
+        oracle._lib = lib
+        failed = []
+        for test, args in ((test_backward_matches_finite_differences, (31,)),
+                           (test_backward_l_zero_closed_form, ()), (test_backward_scale_invariance, ())):
+            try:
+                test(*args)
+            except AssertionError:
+                failed.append(test.__name__)
+        assert failed, f"planted mistake {name} passed the backward pins"
     finally:
         oracle._lib = saved
