@@ -1077,19 +1077,25 @@ PrefillPlan make_plan(const oal_dims &d, int T_len, int C) {
     return p;
 }
 
-// Raise a kernel's dynamic-LDS limit to max_lds once per device (the attribute is set from
-// the host; after the first call no HIP call other than the launch is made, so a call can be
-// captured into a graph). `done` is the caller's per-kernel record of devices already set.
+// Raise a kernel's dynamic-LDS limit to `lds` bytes when a call needs more than the device's
+// current setting (the attribute is set from the host; once a shape has run, a call of that
+// shape makes no HIP call besides its launches, so it can be captured into a graph).
+// `set_bytes` is the caller's per-kernel record of the limit set on each device.
+constexpr int kMaxDevices = 64;
 template <typename K>
-hipError_t ensure_lds_limit(K kern, size_t max_lds, std::atomic<unsigned long long> &done) {
+hipError_t ensure_lds_limit(K kern, size_t lds, std::atomic<int> (&set_bytes)[kMaxDevices]) {
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return e;
-    const unsigned long long bit = dev < 64 ? (1ull << dev) : 0ull;
-    if (bit && (done.load(std::memory_order_acquire) & bit)) return hipSuccess;
+    const bool tracked = dev >= 0 && dev < kMaxDevices;
+    if (tracked && set_bytes[dev].load(std::memory_order_acquire) >= (int)lds) return hipSuccess;
     e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
-                            (int)max_lds);
-    if (e == hipSuccess && bit) done.fetch_or(bit, std::memory_order_acq_rel);
+                            (int)lds);
+    if (e == hipSuccess && tracked) {
+        int cur = set_bytes[dev].load(std::memory_order_acquire);
+        while (cur < (int)lds && !set_bytes[dev].compare_exchange_weak(cur, (int)lds, std::memory_order_acq_rel)) {
+        }
+    }
     return e;
 }
 
@@ -1101,7 +1107,7 @@ hipError_t launch_readout(const oal_dims &d, int T_len, const int *lens, const P
     int n_hg = n_rep / R;
     size_t lds = readout_lds<T, C, R>();
     auto kern = oal_readout<T, C, R>;
-    static std::atomic<unsigned long long> lds_set{0};
+    static std::atomic<int> lds_set[kMaxDevices];
     hipError_t e = ensure_lds_limit(kern, lds, lds_set);
     if (e != hipSuccess) return e;
     int nunits = p.nchunks * d.batch * d.n_kv_heads * n_hg;
@@ -1129,9 +1135,8 @@ hipError_t launch_all(const oal_dims &d, int T_len, const int *lens, const void 
         using IL = IntraLayout<T, C>;
         const size_t lds = std::max(IL::bytes(std::min(d.n_q_heads / d.n_kv_heads, kIntraLzHeads)), scan_lds<T, C>());
         auto kern = oal_intra_delta<T, C>;
-        static std::atomic<unsigned long long> lds_set{0};
-        const size_t lds_max = std::max(IL::bytes(kIntraLzHeads), scan_lds<T, C>());
-        if ((e = ensure_lds_limit(kern, lds_max, lds_set)) != hipSuccess) return e;
+        static std::atomic<int> lds_set[kMaxDevices];
+        if ((e = ensure_lds_limit(kern, lds, lds_set)) != hipSuccess) return e;
         const int nunits = p.nchunks * bkv;
         const int n_intra = kXcds * (C / 32) * ((nunits + kXcds - 1) / kXcds);   // tile pairs
         const int n_delta = (kScanBlocks + 1) * p.nchunks * bkv;
@@ -1143,7 +1148,7 @@ hipError_t launch_all(const oal_dims &d, int T_len, const int *lens, const void 
     } else {   // state only: the increments alone
         auto kern = oal_scan_delta<T, C>;
         size_t lds = scan_lds<T, C>();
-        static std::atomic<unsigned long long> lds_set{0};
+        static std::atomic<int> lds_set[kMaxDevices];
         if ((e = ensure_lds_limit(kern, lds, lds_set)) != hipSuccess) return e;
         hipLaunchKernelGGL(kern, dim3(kScanBlocks + 1, p.nchunks, bkv), dim3(64 * kScanWaves), lds, stream,
                            T_len, lens, p.nchunks, d.n_q_heads, d.n_kv_heads, reinterpret_cast<const T *>(k),
