@@ -25,7 +25,7 @@ EXPORTED = ("oal_params_bytes", "oal_state_bytes", "oal_prefill_workspace_bytes"
             "oal_prefill_timed", "oal_decode_step", "oal_status_string", "oal_timing_event_create",
             "oal_timing_event_destroy", "oal_timing_event_record", "oal_timing_elapsed_ms",
             "oal_contribution_workspace_bytes", "oal_contribution", "oal_decode_step_indexed",
-            "oal_prefill_varlen")
+            "oal_prefill_varlen", "oal_prefill_packed")
 
 
 class OALError(RuntimeError):
@@ -70,6 +70,8 @@ def _load():
     lib.oal_prefill_timed.restype = ctypes.c_int
     lib.oal_prefill_varlen.argtypes = [dp, I, P, I, P, P, P, P, P, P, P, P]
     lib.oal_prefill_varlen.restype = ctypes.c_int
+    lib.oal_prefill_packed.argtypes = [dp, I, P, ctypes.c_int64, I, P, P, P, P, P, P, P, P]
+    lib.oal_prefill_packed.restype = ctypes.c_int
     lib.oal_decode_step.argtypes = [dp, P, P, P, P, P, P, P, P]
     lib.oal_decode_step.restype = ctypes.c_int
     lib.oal_decode_step_indexed.argtypes = [dp, P, I, P, P, P, P, P, P, P, P]
@@ -190,6 +192,15 @@ def oal_prefill_varlen(dims: oal_dims, T: int, lengths, chunk: int, q, k, v, par
     _check("oal_prefill_varlen", _lib.oal_prefill_varlen(
         ctypes.byref(dims), int(T), _ptr(lengths), int(chunk), _ptr(q), _ptr(k), _ptr(v),
         _ptr(params_dev), _ptr(state_dev), _ptr(workspace), _ptr(y), _stream(stream)))
+
+
+def oal_prefill_packed(dims: oal_dims, T: int, cu_seqlens, total_tokens: int, chunk: int, q, k, v,
+                       params_dev, state_dev, workspace, y, stream=None):
+    """Packed ragged batch: q, y [n_q_heads, total, 64], k, v [n_kv_heads, total, 64];
+    cu_seqlens is a device int32 tensor [batch + 1]."""
+    _check("oal_prefill_packed", _lib.oal_prefill_packed(
+        ctypes.byref(dims), int(T), _ptr(cu_seqlens), int(total_tokens), int(chunk), _ptr(q), _ptr(k),
+        _ptr(v), _ptr(params_dev), _ptr(state_dev), _ptr(workspace), _ptr(y), _stream(stream)))
 
 
 def oal_prefill_timed(dims: oal_dims, T: int, chunk: int, q, k, v, params_dev, state_dev, workspace,

@@ -18,7 +18,8 @@
 hipError_t oal_launch_decode(const oal_dims &d, const void *q, const void *k, const void *v,
                              const void *params, float *state, const int *slots, int pool_size, void *ws,
                              float *y, hipStream_t stream);
-hipError_t oal_launch_prefill(const oal_dims &d, int T_len, const int *lens, int C, const void *q, const void *k,
+hipError_t oal_launch_prefill(const oal_dims &d, int T_len, const int *lens, const int *cu, long long total, int C,
+                              const void *q, const void *k,
                               const void *v, const void *params, float *state, void *ws, float *y,
                               hipStream_t stream, hipEvent_t *marks);
 size_t oal_decode_ws_bytes_impl(const oal_dims &d);
@@ -278,10 +279,10 @@ oal_status oal_state_init(const oal_dims *d, const oal_head_params *hp, void *pa
     return OAL_OK;
 }
 
-static oal_status prefill_impl(const oal_dims *d, int32_t T, const int32_t *lens, int32_t chunk,
-                               const void *q, const void *k, const void *v, const void *params_dev,
-                               float *state_dev, void *workspace, float *y, hipStream_t stream,
-                               hipEvent_t *marks) {
+static oal_status prefill_impl(const oal_dims *d, int32_t T, const int32_t *lens, const int32_t *cu,
+                               int64_t total, int32_t chunk, const void *q, const void *k, const void *v,
+                               const void *params_dev, float *state_dev, void *workspace, float *y,
+                               hipStream_t stream, hipEvent_t *marks) {
     oal_status st = check_dims(d);
     if (st != OAL_OK) return st;
     if (T < 0) return OAL_E_SHAPE;
@@ -291,11 +292,11 @@ static oal_status prefill_impl(const oal_dims *d, int32_t T, const int32_t *lens
     if ((y && !q) || !k || !v || !params_dev || !state_dev || !workspace) return OAL_E_ARG;
     if ((q && !aligned16(q)) || !aligned16(k) || !aligned16(v) || !aligned16(params_dev) ||
         !aligned16(state_dev) || !aligned16(workspace) || (y && !aligned16(y)) ||
-        (reinterpret_cast<uintptr_t>(lens) & 3u))
+        (reinterpret_cast<uintptr_t>(lens) & 3u) || (reinterpret_cast<uintptr_t>(cu) & 3u))
         return OAL_E_ALIGN;
     if ((T + chunk - 1) / chunk > 65535) return OAL_E_UNSUPPORTED;
-    hipError_t e = oal_launch_prefill(*d, T, lens, chunk, q, k, v, params_dev, state_dev, workspace, y,
-                                      stream, marks);
+    hipError_t e = oal_launch_prefill(*d, T, lens, cu, (long long)total, chunk, q, k, v, params_dev, state_dev,
+                                      workspace, y, stream, marks);
     if (e != hipSuccess) {
         (void)hipGetLastError();   // do not leave a sticky error for the caller's next HIP call
         return OAL_E_HIP;
@@ -306,7 +307,8 @@ static oal_status prefill_impl(const oal_dims *d, int32_t T, const int32_t *lens
 oal_status oal_prefill(const oal_dims *d, int32_t T, int32_t chunk, const void *q, const void *k,
                        const void *v, const void *params_dev, float *state_dev, void *workspace,
                        float *y, hipStream_t stream) {
-    return prefill_impl(d, T, nullptr, chunk, q, k, v, params_dev, state_dev, workspace, y, stream, nullptr);
+    return prefill_impl(d, T, nullptr, nullptr, 0, chunk, q, k, v, params_dev, state_dev, workspace, y, stream,
+                        nullptr);
 }
 
 oal_status oal_prefill_timed(const oal_dims *d, int32_t T, int32_t chunk, const void *q,
@@ -314,14 +316,29 @@ oal_status oal_prefill_timed(const oal_dims *d, int32_t T, int32_t chunk, const 
                              float *state_dev, void *workspace, float *y, hipStream_t stream,
                              hipEvent_t marks[3]) {
     if (!marks || !marks[0] || !marks[1] || !marks[2]) return OAL_E_ARG;
-    return prefill_impl(d, T, nullptr, chunk, q, k, v, params_dev, state_dev, workspace, y, stream, marks);
+    return prefill_impl(d, T, nullptr, nullptr, 0, chunk, q, k, v, params_dev, state_dev, workspace, y, stream,
+                        marks);
 }
 
 oal_status oal_prefill_varlen(const oal_dims *d, int32_t T, const int32_t *lengths, int32_t chunk,
                               const void *q, const void *k, const void *v, const void *params_dev,
                               float *state_dev, void *workspace, float *y, hipStream_t stream) {
     if (!lengths && check_dims(d) == OAL_OK && T > 0 && d->batch > 0) return OAL_E_ARG;
-    return prefill_impl(d, T, lengths, chunk, q, k, v, params_dev, state_dev, workspace, y, stream, nullptr);
+    return prefill_impl(d, T, lengths, nullptr, 0, chunk, q, k, v, params_dev, state_dev, workspace, y, stream,
+                        nullptr);
+}
+
+oal_status oal_prefill_packed(const oal_dims *d, int32_t T, const int32_t *cu_seqlens, int64_t total_tokens,
+                              int32_t chunk, const void *q, const void *k, const void *v,
+                              const void *params_dev, float *state_dev, void *workspace, float *y,
+                              hipStream_t stream) {
+    if (total_tokens < 0) return OAL_E_SHAPE;
+    if (check_dims(d) == OAL_OK && T > 0 && d->batch > 0) {
+        if (!cu_seqlens) return OAL_E_ARG;
+        if (total_tokens == 0) return OAL_OK;     // every sequence is empty
+    }
+    return prefill_impl(d, T, nullptr, cu_seqlens, total_tokens, chunk, q, k, v, params_dev, state_dev,
+                        workspace, y, stream, nullptr);
 }
 
 oal_status oal_decode_step(const oal_dims *d, const void *q, const void *k, const void *v,

@@ -174,16 +174,33 @@ __device__ inline void store_frags(float *dp, const oal_f32x4 (&acc)[2][5], int 
 }
 
 // grid (K-step blocks + 1 tail block, chunks, sequence x KV head); 8 waves, one K-step each.
-// Tokens of sequence b: all T_len of the padded batch, or lens[b] clamped to [0, T_len] for a
-// ragged batch (tokens past it count as absent: zero features, no output rows).
-__device__ __forceinline__ int oal_seq_len(const int *__restrict__ lens, int b, int T_len) {
-    return lens ? min(max(lens[b], 0), T_len) : T_len;
-}
+// Where the tokens of sequence b are, and how many there are. Three layouts:
+//  - padded batch [batch, heads, T, 64]: all T_len tokens (lens == cu == NULL);
+//  - ragged padded batch: the same layout, lens[b] tokens (clamped to [0, T_len]);
+//  - packed [heads, total, 64]: sequence b is rows cu[b] .. cu[b+1] - 1 of every head's plane
+//    (offset clamped to [0, total], length to [0, min(T_len, total - offset)]).
+// Tokens past a sequence's length count as absent: zero features, no output rows.
+struct OalSeqLayout {
+    const int *lens;
+    const int *cu;
+    long long total;
+    __device__ __forceinline__ long long base(int b) const {
+        return min(max((long long)cu[b], 0ll), total);
+    }
+    __device__ __forceinline__ int len(int b, int T_len) const {
+        if (cu) return (int)max(0ll, min((long long)cu[b + 1] - base(b), min((long long)T_len, total - base(b))));
+        return lens ? min(max(lens[b], 0), T_len) : T_len;
+    }
+    // first row (token) of (sequence b, head h) in a tensor with n_heads heads
+    __device__ __forceinline__ size_t row0(int b, int h, int n_heads, int T_len) const {
+        return cu ? (size_t)h * (size_t)total + (size_t)base(b) : ((size_t)b * n_heads + h) * (size_t)T_len;
+    }
+};
 
 // The chunk's K and V are staged transposed in LDS ([dim][token]).
 template <typename T, int C>
 __device__ __forceinline__ void scan_delta_block(
-    int bx, int c, int bkv, int T_len, const int *__restrict__ lens, int nchunks, int n_q_heads, int n_kv_heads,
+    int bx, int c, int bkv, int T_len, OalSeqLayout sl, int nchunks, int n_q_heads, int n_kv_heads,
     const T *__restrict__ k, const T *__restrict__ v, const unsigned char *__restrict__ params,
     const float *__restrict__ state, float *__restrict__ delta, float *__restrict__ tinit) {
     constexpr int EPU = 16 / (int)sizeof(T);
@@ -202,7 +219,8 @@ __device__ __forceinline__ void scan_delta_block(
     const OalKvDev *kvd = kv_ptr(params, n_q_heads, bkv % n_kv_heads);
     const int nsteps = kvd->nsteps;
     if (bx == kScanBlocks && nsteps == 0) return;     // whole workgroup
-    const int Tb = oal_seq_len(lens, bkv / n_kv_heads, T_len);
+    const int Tb = sl.len(bkv / n_kv_heads, T_len);
+    const size_t krow0 = sl.row0(bkv / n_kv_heads, bkv % n_kv_heads, n_kv_heads, T_len);
     const bool idle = s >= OAL_KSTEPS + nsteps;             // only helps staging
 
     // stage: unit u = (array, 16-byte column a, token); consecutive lanes take consecutive
@@ -214,7 +232,7 @@ __device__ __forceinline__ void scan_delta_block(
             const int u = tid + 64 * kScanWaves * j;
             const int arr = u / (C * UPT), rem = u % (C * UPT), a = rem / C, tok = rem % C;
             const int pos = c * C + tok;
-            const T *src = (arr ? v : k) + ((size_t)bkv * T_len + pos) * OAL_D + a * EPU;
+            const T *src = (arr ? v : k) + (krow0 + pos) * OAL_D + a * EPU;
             r[j] = pos < Tb ? *reinterpret_cast<const oal_u32x4 *>(src) : zero16();
         }
 #pragma unroll
@@ -295,10 +313,10 @@ __device__ __forceinline__ void scan_delta_block(
 
 template <typename T, int C>
 __global__ __launch_bounds__(64 * kScanWaves) void oal_scan_delta(
-    int T_len, const int *__restrict__ lens, int nchunks, int n_q_heads, int n_kv_heads, const T *__restrict__ k,
+    int T_len, OalSeqLayout sl, int nchunks, int n_q_heads, int n_kv_heads, const T *__restrict__ k,
     const T *__restrict__ v, const unsigned char *__restrict__ params, const float *__restrict__ state,
     float *__restrict__ delta, float *__restrict__ tinit) {
-    scan_delta_block<T, C>(blockIdx.x, blockIdx.y, blockIdx.z, T_len, lens, nchunks, n_q_heads, n_kv_heads, k,
+    scan_delta_block<T, C>(blockIdx.x, blockIdx.y, blockIdx.z, T_len, sl, nchunks, n_q_heads, n_kv_heads, k,
                            v, params, state, delta, tinit);
 }
 
@@ -456,7 +474,7 @@ template <typename T, int C> struct IntraLayout {
 // accumulator-fragment order; the readout adds it before the divide.
 constexpr int kIntraWaves = 8;
 template <typename T, int C>
-__device__ __forceinline__ void intra_block(int Lb, int T_len, const int *__restrict__ lens, int n_q_heads,
+__device__ __forceinline__ void intra_block(int Lb, int T_len, OalSeqLayout sl, int n_q_heads,
                                             int n_kv_heads, int nchunks, int n_bkv,
                                             const T *__restrict__ q, const T *__restrict__ k,
                                             const T *__restrict__ v, const unsigned char *__restrict__ params,
@@ -482,7 +500,7 @@ __device__ __forceinline__ void intra_block(int Lb, int T_len, const int *__rest
     const int c = unit % nchunks, bkv = unit / nchunks;
     const int b = bkv / n_kv_heads, kv = bkv % n_kv_heads;
     const int n_rep = n_q_heads / n_kv_heads, h0 = kv * n_rep;
-    const int Tb = oal_seq_len(lens, b, T_len);
+    const int Tb = sl.len(b, T_len);
     if (c * C + pi * 16 >= Tb) return;          // the pair's other tile lies further on
     const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
     const int g = lane >> 4, lr = lane & 15;
@@ -490,7 +508,7 @@ __device__ __forceinline__ void intra_block(int Lb, int T_len, const int *__rest
     // query row lr of tile qt for head i (dims 8g.. and 32 + 8g..)
     auto load_q = [&](int i, int qt, OalFrag<T> (&qf)[2]) {
         const int qpos = c * C + qt * 16 + lr;
-        const T *qr = q + (((size_t)b * n_q_heads + h0 + i) * T_len + (qpos < Tb ? qpos : 0)) * OAL_D + 8 * g;
+        const T *qr = q + (sl.row0(b, h0 + i, n_q_heads, T_len) + (qpos < Tb ? qpos : 0)) * OAL_D + 8 * g;
         qf[0].load(qr);
         qf[1].load(qr + 32);
     };
@@ -511,8 +529,8 @@ __device__ __forceinline__ void intra_block(int Lb, int T_len, const int *__rest
         constexpr int NKU = C * UPQ;                      // 16-byte units of K (and of V)
         constexpr int NKJ = (NKU + NTH - 1) / NTH;
         constexpr int NLJ = (kIntraLzHeads * kIntraLzr * OAL_D / 4 + NTH - 1) / NTH;
-        const T *kb = k + (size_t)bkv * T_len * OAL_D;
-        const T *vb = v + (size_t)bkv * T_len * OAL_D;
+        const T *kb = k + sl.row0(b, kv, n_kv_heads, T_len) * OAL_D;
+        const T *vb = v + sl.row0(b, kv, n_kv_heads, T_len) * OAL_D;
         const int nlz = min(n_rep, kIntraLzHeads) * kIntraLzr * OAL_D / 4;
         oal_u32x4 rk[NKJ], rv[NKJ];
         float4 rl[NLJ];
@@ -699,7 +717,7 @@ __device__ __forceinline__ void intra_block(int Lb, int T_len, const int *__rest
 // rest are increment blocks (K-step block fastest, then chunk, then sequence x KV head).
 template <typename T, int C>
 __global__ __launch_bounds__(64 * kIntraWaves) __attribute__((amdgpu_waves_per_eu(4))) void oal_intra_delta(
-    int T_len, const int *__restrict__ lens, int n_q_heads, int n_kv_heads, int nchunks, int n_bkv, int n_delta,
+    int T_len, OalSeqLayout sl, int n_q_heads, int n_kv_heads, int nchunks, int n_bkv, int n_delta,
     const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ v,
     const unsigned char *__restrict__ params, const float *__restrict__ state, float *__restrict__ delta,
     float *__restrict__ tinit, float *__restrict__ uintra) {
@@ -707,13 +725,13 @@ __global__ __launch_bounds__(64 * kIntraWaves) __attribute__((amdgpu_waves_per_e
     const int n_intra = (int)gridDim.x - n_delta;
     const int id = blockIdx.x;
     if (id < n_intra) {
-        intra_block<T, C>(id, T_len, lens, n_q_heads, n_kv_heads, nchunks, n_bkv, q, k, v, params, uintra);
+        intra_block<T, C>(id, T_len, sl, n_q_heads, n_kv_heads, nchunks, n_bkv, q, k, v, params, uintra);
     } else {
         constexpr int NB = kScanBlocks + 1;
         const int j = id - n_intra;
         const int bx = j % NB, rest = j / NB, c = rest % nchunks, bkv = rest / nchunks;
         if (bkv >= n_bkv) return;
-        scan_delta_block<T, C>(bx, c, bkv, T_len, lens, nchunks, n_q_heads, n_kv_heads, k, v, params, state,
+        scan_delta_block<T, C>(bx, c, bkv, T_len, sl, nchunks, n_q_heads, n_kv_heads, k, v, params, state,
                                delta, tinit);
     }
 }
@@ -751,7 +769,7 @@ template <typename T, int C, int R> struct ReadoutLayout {
 // K-steps deep were both no faster.)
 template <typename T, int C, int R>
 __global__ __launch_bounds__(256, 2) void oal_readout(
-    int T_len, const int *__restrict__ lens, int n_q_heads, int n_kv_heads, int nchunks, int n_hgroups, int nunits,
+    int T_len, OalSeqLayout sl, int n_q_heads, int n_kv_heads, int nchunks, int n_hgroups, int nunits,
     const T *__restrict__ q, const unsigned char *__restrict__ params,
     const unsigned char *__restrict__ snap, const float *__restrict__ uintra, float *__restrict__ y) {
     using Lay = ReadoutLayout<T, C, R>;
@@ -782,7 +800,7 @@ __global__ __launch_bounds__(256, 2) void oal_readout(
     const int hb = hs * RW;                       // first local head of this wave's subset
     const int nh = hs == 0 ? RW : R - RW;         // heads of the subset (0 when R == 1)
     const int pos0 = c * C + qt * 16;
-    const int Tb = oal_seq_len(lens, b, T_len);
+    const int Tb = sl.len(b, T_len);
     if (pos0 >= Tb) return;
     const bool general = reinterpret_cast<const OalParamsHeader *>(params)->general != 0;
     const OalKvDev *kvd = kv_ptr(params, n_q_heads, kv);
@@ -817,7 +835,7 @@ __global__ __launch_bounds__(256, 2) void oal_readout(
             int u = tid + NT * j;
             int i = u / (16 * UPQ), qi = (u / UPQ) % 16, a = u % UPQ, pos = pos0 + qi;
             rq[j] = (u < NQU && pos < Tb)
-                ? *reinterpret_cast<const oal_u32x4 *>(q + (((size_t)b * n_q_heads + h0 + i) * T_len + pos) * OAL_D + a * EPU)
+                ? *reinterpret_cast<const oal_u32x4 *>(q + (sl.row0(b, h0 + i, n_q_heads, T_len) + pos) * OAL_D + a * EPU)
                 : zero16();
             const float4 *wp = reinterpret_cast<const float4 *>(head_ptr(params, h0 + (u < NQU ? i : 0))->w0 + a * EPU);
 #pragma unroll
@@ -1036,7 +1054,7 @@ __global__ __launch_bounds__(256, 2) void oal_readout(
         for (int n = 0; n < 5; ++n)
 #pragma unroll
             for (int ii = 0; ii < 4; ++ii) acc[li][n][ii] += s_x[((i * 5 + n) * 4 + ii) * 64 + lane] + up[(n * 4 + ii) * 64];
-        float *yh = y + ((size_t)b * n_q_heads + h0 + i) * T_len * OAL_D;
+        float *yh = y + sl.row0(b, h0 + i, n_q_heads, T_len) * OAL_D;
 #pragma unroll
         for (int ii = 0; ii < 4; ++ii) {
             // 1 / den: hardware reciprocal refined by one Newton-Raphson step
@@ -1100,7 +1118,7 @@ hipError_t ensure_lds_limit(K kern, size_t lds, std::atomic<int> (&set_bytes)[kM
 }
 
 template <typename T, int C, int R>
-hipError_t launch_readout(const oal_dims &d, int T_len, const int *lens, const PrefillPlan &p, const void *q,
+hipError_t launch_readout(const oal_dims &d, int T_len, OalSeqLayout sl, const PrefillPlan &p, const void *q,
                           const void *params, const unsigned char *snap, const float *uintra, float *y,
                           hipStream_t stream) {
     int n_rep = d.n_q_heads / d.n_kv_heads;
@@ -1112,14 +1130,14 @@ hipError_t launch_readout(const oal_dims &d, int T_len, const int *lens, const P
     if (e != hipSuccess) return e;
     int nunits = p.nchunks * d.batch * d.n_kv_heads * n_hg;
     int nblocks = kXcds * (C / 16) * ((nunits + kXcds - 1) / kXcds);
-    hipLaunchKernelGGL(kern, dim3(nblocks), dim3(ReadoutLayout<T, C, R>::NT), lds, stream, T_len, lens, d.n_q_heads, d.n_kv_heads,
+    hipLaunchKernelGGL(kern, dim3(nblocks), dim3(ReadoutLayout<T, C, R>::NT), lds, stream, T_len, sl, d.n_q_heads, d.n_kv_heads,
                        p.nchunks, n_hg, nunits, reinterpret_cast<const T *>(q),
                        reinterpret_cast<const unsigned char *>(params), snap, uintra, y);
     return hipGetLastError();
 }
 
 template <typename T, int C>
-hipError_t launch_all(const oal_dims &d, int T_len, const int *lens, const void *q, const void *k, const void *v,
+hipError_t launch_all(const oal_dims &d, int T_len, OalSeqLayout sl, const void *q, const void *k, const void *v,
                       const void *params, float *state, void *ws, float *y, hipStream_t stream,
                       hipEvent_t *marks) {
     PrefillPlan p = make_plan<T>(d, T_len, C);
@@ -1140,7 +1158,7 @@ hipError_t launch_all(const oal_dims &d, int T_len, const int *lens, const void 
         const int nunits = p.nchunks * bkv;
         const int n_intra = kXcds * (C / 32) * ((nunits + kXcds - 1) / kXcds);   // tile pairs
         const int n_delta = (kScanBlocks + 1) * p.nchunks * bkv;
-        hipLaunchKernelGGL(kern, dim3(n_intra + n_delta), dim3(64 * kIntraWaves), lds, stream, T_len, lens,
+        hipLaunchKernelGGL(kern, dim3(n_intra + n_delta), dim3(64 * kIntraWaves), lds, stream, T_len, sl,
                            d.n_q_heads, d.n_kv_heads, p.nchunks, bkv, n_delta, reinterpret_cast<const T *>(q),
                            reinterpret_cast<const T *>(k), reinterpret_cast<const T *>(v), pb, state, delta,
                            tinit, uintra);
@@ -1151,7 +1169,7 @@ hipError_t launch_all(const oal_dims &d, int T_len, const int *lens, const void 
         static std::atomic<int> lds_set[kMaxDevices];
         if ((e = ensure_lds_limit(kern, lds, lds_set)) != hipSuccess) return e;
         hipLaunchKernelGGL(kern, dim3(kScanBlocks + 1, p.nchunks, bkv), dim3(64 * kScanWaves), lds, stream,
-                           T_len, lens, p.nchunks, d.n_q_heads, d.n_kv_heads, reinterpret_cast<const T *>(k),
+                           T_len, sl, p.nchunks, d.n_q_heads, d.n_kv_heads, reinterpret_cast<const T *>(k),
                            reinterpret_cast<const T *>(v), pb, state, delta, tinit);
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
@@ -1168,15 +1186,15 @@ hipError_t launch_all(const oal_dims &d, int T_len, const int *lens, const void 
     int n_rep = d.n_q_heads / d.n_kv_heads;
     auto fits = [](size_t bytes) { return bytes <= (size_t)kMaxLds; };
     if (n_rep % 8 == 0 && fits(readout_lds<T, C, 8>()))
-        e = launch_readout<T, C, 8>(d, T_len, lens, p, q, params, snap, uintra, y, stream);
+        e = launch_readout<T, C, 8>(d, T_len, sl, p, q, params, snap, uintra, y, stream);
     else if (n_rep % 7 == 0 && fits(readout_lds<T, C, 7>()))
-        e = launch_readout<T, C, 7>(d, T_len, lens, p, q, params, snap, uintra, y, stream);
+        e = launch_readout<T, C, 7>(d, T_len, sl, p, q, params, snap, uintra, y, stream);
     else if (n_rep % 4 == 0 && fits(readout_lds<T, C, 4>()))
-        e = launch_readout<T, C, 4>(d, T_len, lens, p, q, params, snap, uintra, y, stream);
+        e = launch_readout<T, C, 4>(d, T_len, sl, p, q, params, snap, uintra, y, stream);
     else if (n_rep % 2 == 0 && fits(readout_lds<T, C, 2>()))
-        e = launch_readout<T, C, 2>(d, T_len, lens, p, q, params, snap, uintra, y, stream);
+        e = launch_readout<T, C, 2>(d, T_len, sl, p, q, params, snap, uintra, y, stream);
     else
-        e = launch_readout<T, C, 1>(d, T_len, lens, p, q, params, snap, uintra, y, stream);
+        e = launch_readout<T, C, 1>(d, T_len, sl, p, q, params, snap, uintra, y, stream);
     if (e == hipSuccess && marks) e = hipEventRecord(marks[2], stream);
     return e;
 }
@@ -1188,15 +1206,16 @@ size_t oal_prefill_ws_bytes_impl(const oal_dims &d, int T_len, int C) {
     return p.snap_bytes + p.delta_bytes + p.tinit_bytes + p.uintra_bytes;
 }
 
-hipError_t oal_launch_prefill(const oal_dims &d, int T_len, const int *lens, int C, const void *q, const void *k,
-                              const void *v, const void *params, float *state, void *ws, float *y,
-                              hipStream_t stream, hipEvent_t *marks) {
+hipError_t oal_launch_prefill(const oal_dims &d, int T_len, const int *lens, const int *cu, long long total, int C,
+                              const void *q, const void *k, const void *v, const void *params, float *state,
+                              void *ws, float *y, hipStream_t stream, hipEvent_t *marks) {
+    const OalSeqLayout sl{lens, cu, total};
     if (d.dtype == OAL_BF16) {
-        if (C == 64) return launch_all<__bf16, 64>(d, T_len, lens, q, k, v, params, state, ws, y, stream, marks);
-        if (C == 128) return launch_all<__bf16, 128>(d, T_len, lens, q, k, v, params, state, ws, y, stream, marks);
-        return launch_all<__bf16, 256>(d, T_len, lens, q, k, v, params, state, ws, y, stream, marks);
+        if (C == 64) return launch_all<__bf16, 64>(d, T_len, sl, q, k, v, params, state, ws, y, stream, marks);
+        if (C == 128) return launch_all<__bf16, 128>(d, T_len, sl, q, k, v, params, state, ws, y, stream, marks);
+        return launch_all<__bf16, 256>(d, T_len, sl, q, k, v, params, state, ws, y, stream, marks);
     }
-    if (C == 64) return launch_all<float, 64>(d, T_len, lens, q, k, v, params, state, ws, y, stream, marks);
-    if (C == 128) return launch_all<float, 128>(d, T_len, lens, q, k, v, params, state, ws, y, stream, marks);
-    return launch_all<float, 256>(d, T_len, lens, q, k, v, params, state, ws, y, stream, marks);
+    if (C == 64) return launch_all<float, 64>(d, T_len, sl, q, k, v, params, state, ws, y, stream, marks);
+    if (C == 128) return launch_all<float, 128>(d, T_len, sl, q, k, v, params, state, ws, y, stream, marks);
+    return launch_all<float, 256>(d, T_len, sl, q, k, v, params, state, ws, y, stream, marks);
 }

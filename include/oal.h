@@ -159,6 +159,24 @@ oal_status oal_prefill_varlen(const oal_dims *dims, int32_t T, const int32_t *le
                               const void *q, const void *k, const void *v, const void *params_dev,
                               float *state_dev, void *workspace, float *y, hipStream_t stream);
 
+/* oal_prefill for a packed ragged batch: the sequences are concatenated along the token axis,
+ * sequence b being tokens cu_seqlens[b] .. cu_seqlens[b+1] - 1 of every head.
+ *   cu_seqlens   -- [batch + 1] int32 (device, 4-byte aligned), nondecreasing, from 0 to
+ *                   total_tokens. The kernels clamp each offset to [0, total_tokens] and each
+ *                   length to [0, min(T, total_tokens - offset)].
+ *   total_tokens -- tokens in the packed tensors (>= 0; 0 is a no-op).
+ *   T            -- at least the longest sequence (a longer one is cut to its first T tokens);
+ *                   it sizes the chunk grid and the workspace, oal_prefill_workspace_bytes(dims,
+ *                   T, chunk).
+ *   q, y         -- [n_q_heads, total_tokens, 64] (q of dims->dtype, y fp32);
+ *   k, v         -- [n_kv_heads, total_tokens, 64].
+ * Sequence b's state advances by its length; its y rows are written, no others. Results equal
+ * those of oal_prefill_varlen on the same sequences padded to T, bit for bit. */
+oal_status oal_prefill_packed(const oal_dims *dims, int32_t T, const int32_t *cu_seqlens,
+                              int64_t total_tokens, int32_t chunk, const void *q, const void *k,
+                              const void *v, const void *params_dev, float *state_dev,
+                              void *workspace, float *y, hipStream_t stream);
+
 /* One decode step: appends one token per sequence to the prefix states and reads out the
  * attention of each query head over all tokens so far (the new one included).
  *   q [batch, n_q_heads, 64], k, v [batch, n_kv_heads, 64] of dims->dtype (device);

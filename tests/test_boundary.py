@@ -84,6 +84,10 @@ def test_validation_errors_enqueue_nothing():
     assert _code(gpq.oal_prefill_varlen, d, 8, A + 2, 64, *ok, 0) == 4          # misaligned lengths
     assert _code(gpq.oal_prefill_varlen, d, 8, A, 100, *ok, 0) == 5             # chunk
     assert _code(gpq.oal_prefill_varlen, d, 0, None, 64, *([None] * 7), 0) == 0  # T = 0: no-op
+    assert _code(gpq.oal_prefill_packed, d, 8, None, 100, 64, *ok, 0) == 1      # no offsets
+    assert _code(gpq.oal_prefill_packed, d, 8, A, -1, 64, *ok, 0) == 2          # negative total
+    assert _code(gpq.oal_prefill_packed, d, 8, A + 2, 100, 64, *ok, 0) == 4     # misaligned offsets
+    assert _code(gpq.oal_prefill_packed, d, 8, A, 0, 64, *([None] * 7), 0) == 0  # no tokens: no-op
     ix = (A, A, A, A, A, A, A)   # q, k, v, params, pool, workspace, y
     assert _code(gpq.oal_decode_step_indexed, d, A, 0, *ix, 0) == 2         # empty pool
     assert _code(gpq.oal_decode_step_indexed, d, None, 4, *ix, 0) == 1      # no slots

@@ -206,3 +206,84 @@ def test_varlen_batch8_4096_sampled():
     for b in (3, 6):
         L = lengths[b]
         assert state_ok(S[b:b + 1], inp.k[b:b + 1, :, :L], inp.v[b:b + 1, :, :L], "bf16")
+
+
+# ---------------------------------------------------------------------------------------
+# packed ragged prefill (oal_prefill_packed): sequences concatenated along the token axis
+
+def _pack(x, lengths, starts, total):
+    """[B, H, T, d] padded -> [H, total, d] packed at the given starts."""
+    B, H, T, d = x.shape
+    out = np.zeros((H, total, d), dtype=x.dtype)
+    for b, (L, s0) in enumerate(zip(lengths, starts)):
+        out[:, s0:s0 + L] = x[b, :, :L]
+    return out
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_packed_prefill_equals_varlen(dtype):
+    lengths = [300, 129, 1, 0, 64]
+    B, T = len(lengths), 300
+    inp = small(701, B, 4, 2, T, dtype)
+    starts = np.concatenate([[0], np.cumsum(lengths)[:-1]]).tolist()
+    total = int(sum(lengths)) + 37            # 37 trailing rows that belong to no sequence
+    cu = torch.tensor(starts + [sum(lengths)], dtype=torch.int32, device="cuda")
+    qp, kp, vp = (to_dev(_pack(x, lengths, starts, total), dtype) for x in (inp.q, inp.k, inp.v))
+    sess = Session(B, 4, 2, dtype, inp.params, T, 128)
+    yp = torch.full((4, total, 64), 7.0, dtype=torch.float32, device="cuda")
+    gpq.oal_prefill_packed(sess.dims, T, cu, total, 128, qp, kp, vp, sess.params, sess.state, sess.ws, yp)
+    torch.cuda.synchronize()
+    ref_sess, y_ref = _varlen_run(inp, lengths, 128)
+    ypn = yp.cpu().numpy()
+    for b, (L, s0) in enumerate(zip(lengths, starts)):
+        assert np.array_equal(ypn[:, s0:s0 + L], y_ref[b, :, :L]), f"sequence {b} differs from the padded run"
+    assert np.all(ypn[:, sum(lengths):] == 7.0), "rows outside every sequence were written"
+    assert torch.equal(sess.state, ref_sess.state)
+
+
+def test_packed_prefill_inconsistent_offsets_are_clamped():
+    # offsets that run backwards or past the end give empty or shortened sequences, never an
+    # access outside the packed tensors: cu = [30, 30, 20, 500] over 80 rows gives sequence 0
+    # empty, sequence 1 empty (negative length), sequence 2 rows 20..79 (its length 480 cut to
+    # min(T, 80 - 20) = 60)
+    B, T, total = 3, 64, 80
+    inp = small(702, B, 2, 1, T, "bf16")
+    cu = torch.tensor([30, 30, 20, 500], dtype=torch.int32, device="cuda")
+    rows = lambda x: np.concatenate([np.zeros_like(x[2, :, :20]), x[2, :, :60]], axis=1)
+    q, k, v = (to_dev(rows(x), "bf16") for x in (inp.q, inp.k, inp.v))
+    sess = Session(B, 2, 1, "bf16", inp.params, T, 64)
+    y = torch.full((2, total, 64), 7.0, dtype=torch.float32, device="cuda")
+    gpq.oal_prefill_packed(sess.dims, T, cu, total, 64, q, k, v, sess.params, sess.state, sess.ws, y)
+    torch.cuda.synchronize()
+    S = sess.state_np()
+    assert np.all(S[0] == 0.0) and np.all(S[1] == 0.0)
+    yn = y.cpu().numpy()
+    assert np.all(yn[:, :20] == 7.0)
+    ref = oracle.dense(inp.q[2:3, :, :60], inp.k[2:3, :, :60], inp.v[2:3, :, :60], inp.params)
+    assert oracle.row_error(yn[None, :, 20:80], ref) <= TOL["bf16"]
+    from gpu_util import state_ok
+    assert state_ok(S[2:3], inp.k[2:3, :, :60], inp.v[2:3, :, :60], "bf16")
+
+
+def test_packed_prefill_serving_shape():
+    # 8 sequences of mixed lengths packed into 14q/2kv tensors, B = 8, T = 4096
+    lengths = [4096, 1, 4095, 2048, 129, 3000, 64, 1777]
+    inp = qwen_like(8, 4096, 11, name="ragged", per_seq_seeds=[1100 + b for b in range(8)])
+    starts = np.concatenate([[0], np.cumsum(lengths)[:-1]]).tolist()
+    total = int(sum(lengths))
+    cu = torch.tensor(starts + [total], dtype=torch.int32, device="cuda")
+    qp, kp, vp = (to_dev(_pack(x, lengths, starts, total), "bf16") for x in (inp.q, inp.k, inp.v))
+    sess = Session(8, 14, 2, "bf16", inp.params, 4096, 128)
+    yp = torch.empty((14, total, 64), dtype=torch.float32, device="cuda")
+    gpq.oal_prefill_packed(sess.dims, 4096, cu, total, 128, qp, kp, vp, sess.params, sess.state, sess.ws, yp)
+    torch.cuda.synchronize()
+    ypn = yp.cpu().numpy()
+    rng = np.random.default_rng(13)
+    for b, (L, s0) in enumerate(zip(lengths, starts)):
+        pos = sorted({0, L - 1, *rng.integers(0, L, size=2).tolist()})
+        heads = (0, 13)
+        sl = slice(b, b + 1)
+        want = oracle.dense_rows(inp.q[sl, :, :L], inp.k[sl, :, :L], inp.v[sl, :, :L], inp.params,
+                                 [(0, h, i) for h in heads for i in pos])
+        got = np.stack([ypn[h, s0 + i] for h in heads for i in pos])
+        assert oracle.row_error(got, want) <= TOL["bf16"]
