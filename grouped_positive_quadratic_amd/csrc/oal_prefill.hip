@@ -26,6 +26,9 @@
 //     The two parities and the intra-chunk sum are combined and divided,
 //     y = u~[0:64] / u~[64]. Workgroups of one chunk are placed on one XCD so the snapshot is
 //     fetched into that XCD's L2 once.
+// Sequences come as a padded batch [batch, heads, T, 64], the same with per-sequence
+// lengths, or packed [heads, total, 64] with cumulative offsets (OalSeqLayout below); the
+// chunk grid covers T tokens per sequence and tokens past a sequence's length are absent.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
