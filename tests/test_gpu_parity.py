@@ -66,6 +66,10 @@ SMALL = [  # seed, B, Hq, Hkv, T, chunk
     (15, 1, 8, 1, 129, 256),
     (16, 2, 3, 1, 64, 64),
     (17, 1, 14, 2, 520, 64),
+    (18, 1, 16, 1, 150, 128),   # 16 query heads per KV head: two readout head groups, two heads per intra wave
+    (19, 1, 12, 1, 130, 64),    # 12 per KV head: readout head groups of 4
+    (20, 2, 5, 1, 90, 128),     # 5 per KV head: head groups of 1
+    (21, 1, 6, 6, 70, 64),      # one query head per KV head (no GQA)
 ]
 
 
@@ -80,6 +84,23 @@ def test_prefill_small(case, dtype):
     _report(f"prefill {dtype} {case}", err)
     assert err <= TOL[dtype]
     assert state_ok(sess.state_np(), inp.k, inp.v, dtype)
+
+
+@pytest.mark.parametrize("shape", [(16, 1), (12, 2), (6, 6)], ids=["H16x1", "H12x2", "H6x6"])
+def test_prefill_then_decode_head_counts(shape):
+    # decode with more than 8 query heads per KV head (the 16-head decode kernel) and without
+    # GQA, after a prefill of the same sequences
+    Hq, Hkv = shape
+    inp = small(25, 2, Hq, Hkv, 140, dtype="bf16")
+    T0 = 120
+    sess = session_for(inp, 64)
+    y0 = sess.prefill(inp.q[:, :, :T0], inp.k[:, :, :T0], inp.v[:, :, :T0], 64)
+    ys = [sess.decode(inp.q[:, :, i], inp.k[:, :, i], inp.v[:, :, i]) for i in range(T0, 140)]
+    y = np.concatenate([y0.cpu().numpy(), torch.stack(ys, 2).cpu().numpy()], axis=2)
+    err = oracle.row_error(y, oracle.dense(inp.q, inp.k, inp.v, inp.params))
+    _report(f"prefill+decode H{Hq}x{Hkv}", err)
+    assert err <= TOL["bf16"]
+    assert state_ok(sess.state_np(), inp.k, inp.v, "bf16")
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
