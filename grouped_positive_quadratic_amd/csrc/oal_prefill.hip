@@ -12,7 +12,7 @@
 //     the state is wanted):
 //     - per (chunk x 16-query tile, sequence x KV head) the exact intra-chunk kernel sums of
 //       every query head, kappa [V;1] unnormalised, on MFMA;
-//     - per (sequence x KV head, chunk, 16 K-steps: two per wave), in parallel, the chunk's
+//     - per (sequence x KV head, chunk, 32 K-steps: four per wave), in parallel, the chunk's
 //       state increment psi(K_c)^T [V_c;1] on MFMA (fp32), from K and V staged transposed
 //       in LDS. Besides
 //       the 72 main K-steps, up to 8 tail K-steps carry the linear features, the constant
@@ -43,9 +43,10 @@
 namespace {
 
 constexpr int kScanWaves = 8;                 // waves per increment workgroup
-// K-steps per wave of an increment workgroup: two halve the workgroups that stage the same
-// chunk's K and V (B = 8 x 4096: intra + scan 291 -> 279 us; B = 1 unchanged)
-constexpr int kScanKPW = 2;
+// K-steps per wave of an increment workgroup: fewer workgroups stage the same chunk's K and
+// V (measured, intra + scan: one per wave 45 us at B = 1 x 4096 and 291 us at B = 8 x 4096;
+// two 43-45 / 278; four 41 / 270)
+constexpr int kScanKPW = 4;
 // increment workgroups per (sequence x KV head, chunk): every main and tail K-step
 constexpr int kDeltaBlocks = (OAL_SNAP_KSTEPS + kScanWaves * kScanKPW - 1) / (kScanWaves * kScanKPW);
 constexpr int kXcds = 8;                      // MI355X: workgroups go round-robin to 8 XCDs
