@@ -43,6 +43,7 @@
 namespace {
 
 constexpr int kScanWaves = 8;                 // waves per increment workgroup
+constexpr int kCUs = 256;                      // MI355X compute units
 // K-steps per wave of an increment workgroup: fewer workgroups stage the same chunk's K and
 // V (measured, intra + scan: one per wave 45 us at B = 1 x 4096 and 291 us at B = 8 x 4096;
 // two 43-45 / 278; four 41 / 270)
@@ -382,7 +383,7 @@ __global__ __launch_bounds__(256) void oal_scan_prefix(int nchunks, int n_q_head
     constexpr size_t DSTRIDE = (size_t)OAL_SNAP_KSTEPS * kDeltaStep, SSTRIDE = (size_t)OAL_SNAP_KSTEPS * KB;
     // chunks in batches of PB; the next batch's increments are requested before the current
     // batch is summed (two buffers, the loop unrolled by two batches)
-    constexpr int PB = 8;
+    constexpr int PB = 4;
     auto load_batch = [&](int c0, float4 (&d)[PB][2]) {
 #pragma unroll
         for (int u = 0; u < PB; ++u) {
@@ -782,7 +783,7 @@ template <typename T, int C, int R> struct ReadoutLayout {
 // K-steps deep were both no faster.)
 template <typename T, int C, int R>
 __global__ __launch_bounds__(256, 2) void oal_readout(
-    int T_len, OalSeqLayout sl, int n_q_heads, int n_kv_heads, int nchunks, int n_hgroups, int nunits,
+    int T_len, OalSeqLayout sl, int n_q_heads, int n_kv_heads, int nchunks, int n_hgroups, int nunits, int warm,
     const T *__restrict__ q, const unsigned char *__restrict__ params,
     const unsigned char *__restrict__ snap, const float *__restrict__ uintra, float *__restrict__ y) {
     using Lay = ReadoutLayout<T, C, R>;
@@ -820,9 +821,9 @@ __global__ __launch_bounds__(256, 2) void oal_readout(
     const int ntail = kvd->nsteps;                // >= 3: linear features and the constant
 
     // 1. stage the tile's queries, the per-head tables and the KV head's tail pairs (all
-    //    loads issued before any LDS write), and warm this XCD's L2 with 1/NQT of the
-    //    chunk's snapshot: the NQT workgroups of the unit run side by side on this XCD, so
-    //    together they bring the snapshot in once. The warming loads only feed a value
+    //    loads issued before any LDS write), and (when warm != 0) warm this XCD's L2 with
+    //    1/NQT of the chunk's snapshot: the NQT workgroups of the unit run side by side on
+    //    this XCD, so together they bring the snapshot in once. The warming loads only feed a value
     //    that is never stored.
     {
         constexpr int NQU = R * 16 * UPQ, NMU = R * Lay::META_UNITS + Lay::PAIR_UNITS;
@@ -868,7 +869,7 @@ __global__ __launch_bounds__(256, 2) void oal_readout(
 #pragma unroll
         for (int j = 0; j < NTJ; ++j) {
             int u = qt * SHARE + tid + NT * j;
-            if (tid + NT * j < SHARE && u < SNAP_UNITS) touch ^= sn[u];
+            if (warm && tid + NT * j < SHARE && u < SNAP_UNITS) touch ^= sn[u];
         }
 #pragma unroll
         for (int j = 0; j < NQJ; ++j) {
@@ -1143,8 +1144,12 @@ hipError_t launch_readout(const oal_dims &d, int T_len, OalSeqLayout sl, const P
     if (e != hipSuccess) return e;
     int nunits = p.nchunks * d.batch * d.n_kv_heads * n_hg;
     int nblocks = kXcds * (C / 16) * ((nunits + kXcds - 1) / kXcds);
+    // L2 warm-up of each chunk's snapshot at staging: it pays when workgroups run in several
+    // rounds (B = 8 x 4096: 1% faster), not when all are resident at once (B = 1 x 4096:
+    // 2 us slower), so it is on above two workgroups per CU
+    const int warm = nblocks > 2 * kCUs;
     hipLaunchKernelGGL(kern, dim3(nblocks), dim3(ReadoutLayout<T, C, R>::NT), lds, stream, T_len, sl, d.n_q_heads, d.n_kv_heads,
-                       p.nchunks, n_hg, nunits, reinterpret_cast<const T *>(q),
+                       p.nchunks, n_hg, nunits, warm, reinterpret_cast<const T *>(q),
                        reinterpret_cast<const unsigned char *>(params), snap, uintra, y);
     return hipGetLastError();
 }
