@@ -25,7 +25,8 @@ EXPORTED = ("oal_params_bytes", "oal_state_bytes", "oal_prefill_workspace_bytes"
             "oal_prefill_timed", "oal_decode_step", "oal_status_string", "oal_timing_event_create",
             "oal_timing_event_destroy", "oal_timing_event_record", "oal_timing_elapsed_ms",
             "oal_contribution_workspace_bytes", "oal_contribution", "oal_decode_step_indexed",
-            "oal_prefill_varlen", "oal_prefill_packed")
+            "oal_prefill_varlen", "oal_prefill_packed", "oal_prefill_backward_workspace_bytes",
+            "oal_prefill_backward")
 
 
 class OALError(RuntimeError):
@@ -85,6 +86,10 @@ def _load():
     lib.oal_contribution_workspace_bytes.argtypes = [dp, I]
     lib.oal_contribution_workspace_bytes.restype = S
     lib.oal_contribution.argtypes, lib.oal_contribution.restype = [dp, I, P, P, P, P, P, P], ctypes.c_int
+    lib.oal_prefill_backward_workspace_bytes.argtypes = [dp, I, I]
+    lib.oal_prefill_backward_workspace_bytes.restype = S
+    lib.oal_prefill_backward.argtypes = [dp, I, I, P, P, P, P, P, P, P, P, P, P]
+    lib.oal_prefill_backward.restype = ctypes.c_int
     return lib
 
 
@@ -254,6 +259,20 @@ def oal_contribution(dims: oal_dims, T: int, q, k, workspace, chi, chi_mean=None
     _check("oal_contribution", _lib.oal_contribution(ctypes.byref(dims), int(T), _ptr(q), _ptr(k),
                                                      _ptr(workspace), _ptr(chi), _ptr(chi_mean),
                                                      _stream(stream)))
+
+
+def oal_prefill_backward_workspace_bytes(dims: oal_dims, T: int, chunk: int) -> int:
+    return int(_lib.oal_prefill_backward_workspace_bytes(ctypes.byref(dims), int(T), int(chunk)))
+
+
+def oal_prefill_backward(dims: oal_dims, T: int, chunk: int, q, k, v, dy, params_dev, workspace,
+                         dq, dk, dv, stream=None):
+    """Gradients dq [batch, n_q_heads, T, 64], dk, dv [batch, n_kv_heads, T, 64] (fp32 device
+    tensors written by the library) of sum(dy * y) for the prefill of T tokens from an empty
+    prefix."""
+    _check("oal_prefill_backward", _lib.oal_prefill_backward(
+        ctypes.byref(dims), int(T), int(chunk), _ptr(q), _ptr(k), _ptr(v), _ptr(dy),
+        _ptr(params_dev), _ptr(workspace), _ptr(dq), _ptr(dk), _ptr(dv), _stream(stream)))
 
 
 def oal_decode_step_indexed(dims: oal_dims, slots, pool_size: int, q, k, v, params_dev, state_pool,

@@ -11,7 +11,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "liboal.so")
-SOURCES = ["oal_host.cpp", "oal_decode.hip", "oal_prefill.hip", "oal_contrib.hip"]
+SOURCES = ["oal_host.cpp", "oal_decode.hip", "oal_prefill.hip", "oal_contrib.hip", "oal_backward.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["-O3", "--offload-arch=gfx950", "-fPIC", "-std=c++17",
          "-I", os.path.join(ROOT, "include"), "-I", CSRC,
@@ -31,7 +31,7 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(jobs: int = 4) -> str:
+def build(jobs: int = 5) -> str:
     """Compile every source for gfx950 and link liboal.so (always recompiles)."""
     os.makedirs(BUILD, exist_ok=True)
     with ThreadPoolExecutor(max_workers=jobs) as ex:

@@ -1,0 +1,668 @@
+// oal_backward.hip -- gfx950 kernels of the prefill backward: dq, dk, dv of sum(dy * y) for
+// the causal attention y of a prefill from an empty prefix.
+//
+// The forward (reproduction notes of arXiv 2610.13674, section "核心公式": the kernel kappa,
+// the H-state recurrence and the readout u~ = phi(q) . H, y = u~[0:64] / u~[64]) is
+//   u_i = sum_{j <= i} kappa_ij [v_j; 1],  kappa_ij = phi_h(q_i) . psi(k_j)
+// with psi(k) = [1, k_r, k_r k_t (r <= t)] and phi_h(q) = wdec_h o [1, q_r, q_r q_t]. Its
+// backward, by the chain rule through the chunked form of the same sum:
+//   g_i       = (dy_i / den_i, -(dy_i . y_i) / den_i)          (65 values per query and head)
+//   dkappa_ij = g_i . [v_j; 1]
+//   dq_i = Jphi_h(q_i)^T (S_c g_i)         + sum_{j <= i, same chunk} dkappa_ij dkappa_ij/dq_i
+//   dv_j = (R_c^T psi(k_j))[0:64]          + sum_h sum_{i >= j, same chunk} kappa_ij g_i[0:64]
+//   dk_j = Jpsi(k_j)^T (R_c [v_j; 1])      + sum_h sum_{i >= j, same chunk} dkappa_ij dkappa_ij/dk_j
+// where S_c sums psi(k_j) [v_j; 1]^T over the chunks before c (the forward's prefix state) and
+// R_c sums phi_h(q_i) g_i^T over the chunks after c and the query heads h of the KV head.
+// Inside a chunk kappa is taken from its z-terms, as in the forward's intra-chunk part:
+//   z_m = [m = 0] L00 + sum_r Lz[m][r] q_r k_r,   kappa = eps + sum_{m <= G} z_m^2,
+//   dkappa/dq_r = 2 k_r sum_m z_m Lz[m][r]        (and the same with q and k exchanged).
+//
+// Every kernel computes in fp32 (inputs of either dtype are widened on load). State rows are
+// read with wave-uniform addresses through the constant address space, so they arrive in
+// scalar registers and feed the FMAs directly; the per-lane operand (a query or key row) is
+// in LDS or in registers. The work is fp32 VALU: with packed fp32 off, the bound is the
+// non-packed FMA rate (256 CUs x 4 SIMDs x 16 lanes x 2 flops x 2.4 GHz = 78.6 TFLOP/s).
+//
+// Launch order (all on the caller's stream):
+//   1. oal_bwd_increments<keys>:    per chunk psi(K_c)^T [V_c; 1]           -> workspace states
+//   2. oal_bwd_scan (forward):      exclusive prefix over chunks: S_c
+//   3. oal_bwd_readout_g:           u_i (inter + intra), y, den -> g_i     -> workspace g
+//   4. oal_bwd_dq:                  dq
+//   5. oal_bwd_increments<queries>: per chunk sum_h phi_h(Q_c)^T G_c       -> workspace states
+//   6. oal_bwd_scan (reverse):      exclusive suffix over chunks: R_c
+//   7. oal_bwd_dv, oal_bwd_dk:      dv, dk
+#include <hip/hip_runtime.h>
+
+#include "oal_device.h"
+#include "oal_internal.h"
+
+namespace {
+
+constexpr int kThreads = 256;                 // four waves
+constexpr int kFeatBlock = 64;                // features per increment workgroup
+constexpr int kMBlock = 8;                    // z-terms kept in registers at a time
+
+typedef const float __attribute__((address_space(4))) cfloat;   // wave-uniform reads
+
+__device__ inline const OalHeadDev *bwd_head(const unsigned char *params, int h) {
+    return reinterpret_cast<const OalHeadDev *>(params + sizeof(OalParamsHeader) + (size_t)h * OAL_HEAD_BYTES);
+}
+
+__device__ inline const cfloat *uni(const float *p) { return (const cfloat *)p; }
+
+__device__ inline int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
+
+// first feature of the quadratic row r, minus r: feature (r, t) is quad_base(r) + t
+__device__ inline int quad_base(int r) { return 1 + OAL_D + r * OAL_D - (r * (r - 1)) / 2 - r; }
+
+// x = S[f][0:64] . g[0:64] + S[f][64] g[64] (S rows wave-uniform)
+__device__ inline float row_dot(const cfloat *S, const cfloat *Sd, int f, const float (&g)[65]) {
+    const cfloat *row = S + (size_t)f * OAL_D;
+    float x0 = Sd[f] * g[64], x1 = 0.0f, x2 = 0.0f, x3 = 0.0f;
+#pragma unroll
+    for (int c = 0; c < 64; c += 4) {
+        x0 += row[c] * g[c];
+        x1 += row[c + 1] * g[c + 1];
+        x2 += row[c + 2] * g[c + 2];
+        x3 += row[c + 3] * g[c + 3];
+    }
+    return (x0 + x1) + (x2 + x3);
+}
+
+// acc[0:NC] += a S[f][0:NC] (NC = 64 or 65, column 64 from the separate vector)
+template <int NC>
+__device__ inline void row_axpy(float (&acc)[NC], float a, const cfloat *S, const cfloat *Sd, int f) {
+    const cfloat *row = S + (size_t)f * OAL_D;
+#pragma unroll
+    for (int c = 0; c < 64; ++c) acc[c] += a * row[c];
+    if constexpr (NC == 65) acc[64] += a * Sd[f];
+}
+
+// z-terms m0 .. m0 + NB - 1 of the pair (x, y): z_m = [m = 0] L00 + sum_r Lz[m][r] x_r y_r.
+// x is lane-distinct (stride-65 LDS row), y wave-uniform (LDS row, broadcast). Rows of Lz
+// past the head's G are zero, so a block may run past G; blocks never pass row 64.
+template <int NB>
+__device__ inline void z_block(const OalHeadDev *hd, int m0, const float *x, const float *y, float (&z)[NB]) {
+    const cfloat *Lz = uni(hd->Lz) + m0 * OAL_D;
+#pragma unroll
+    for (int mm = 0; mm < NB; ++mm) z[mm] = 0.0f;
+    if (m0 == 0) z[0] = hd->L00;
+#pragma unroll 8
+    for (int r = 0; r < OAL_D; ++r) {
+        const float p = x[r] * y[r];
+#pragma unroll
+        for (int mm = 0; mm < NB; ++mm) z[mm] += Lz[mm * OAL_D + r] * p;
+    }
+}
+
+// kappa of the pair (x, y) (same operand placement as z_block): blocks of kMBlock z-terms
+// cover m = 0 .. 63; row 64 exists only when G = 64.
+__device__ inline float pair_kappa(const OalHeadDev *hd, int G, const float *x, const float *y) {
+    float kap = hd->eps;
+    for (int m0 = 0; m0 <= min(G, 63); m0 += kMBlock) {
+        float z[kMBlock];
+        z_block<kMBlock>(hd, m0, x, y, z);
+#pragma unroll
+        for (int mm = 0; mm < kMBlock; ++mm) kap += z[mm] * z[mm];
+    }
+    if (G == 64) {
+        float z[1];
+        z_block<1>(hd, 64, x, y, z);
+        kap += z[0] * z[0];
+    }
+    return kap;
+}
+
+template <int NB>
+__device__ inline void grad_block(const OalHeadDev *hd, int m0, float e, const float *x, const float *y,
+                                  float (&acc)[64]) {
+    float z[NB];
+    z_block<NB>(hd, m0, x, y, z);
+    const cfloat *Lz = uni(hd->Lz) + m0 * OAL_D;
+#pragma unroll
+    for (int mm = 0; mm < NB; ++mm) z[mm] *= 2.0f * e;
+#pragma unroll
+    for (int r = 0; r < OAL_D; ++r) {
+        float s = 0.0f;
+#pragma unroll
+        for (int mm = 0; mm < NB; ++mm) s += z[mm] * Lz[mm * OAL_D + r];
+        acc[r] += s * y[r];
+    }
+}
+
+// acc[r] += e * y[r] * 2 sum_m z_m Lz[m][r]: the pair's dkappa/dx scaled by e (dkappa), with
+// x the lane's operand and y the other side's row (wave-uniform).
+__device__ inline void pair_grad(const OalHeadDev *hd, int G, float e, const float *x, const float *y,
+                                 float (&acc)[64]) {
+    for (int m0 = 0; m0 <= min(G, 63); m0 += kMBlock) grad_block<kMBlock>(hd, m0, e, x, y, acc);
+    if (G == 64) grad_block<1>(hd, 64, e, x, y, acc);
+}
+
+// Stage 64 rows (tokens t0 .. t0 + 63, zero past T) of a [*, T, 64] tensor into LDS with the
+// given row stride, as fp32; column 64 (if the stride has room) gets `one`.
+template <typename T>
+__device__ inline void stage_rows(float *dst, int stride, const T *src, size_t row0, int t0, int T_len, float one) {
+    for (int e = threadIdx.x; e < 64 * 64; e += kThreads) {
+        const int n = e >> 6, col = e & 63;
+        dst[n * stride + col] = t0 + n < T_len ? oal_ld(src + (row0 + t0 + n) * OAL_D + col) : 0.0f;
+    }
+    if (stride > 64 && threadIdx.x < 64) dst[threadIdx.x * stride + 64] = one;
+}
+
+// Stage 64 rows of g (64 values from gv, the 65th from gd; zero past T) with row stride 68.
+__device__ inline void stage_g(float *dst, const float *gv, const float *gd, size_t row0, int t0, int T_len) {
+    for (int e = threadIdx.x; e < 64 * 64; e += kThreads) {
+        const int n = e >> 6, col = e & 63;
+        dst[n * 68 + col] = t0 + n < T_len ? gv[(row0 + t0 + n) * OAL_D + col] : 0.0f;
+    }
+    if (threadIdx.x < 64) dst[threadIdx.x * 68 + 64] = t0 + (int)threadIdx.x < T_len ? gd[row0 + t0 + threadIdx.x] : 0.0f;
+}
+
+// ---------------------------------------------------------------------------------------------
+// 1 / 5. Per-chunk increments of one (sequence, KV head): out_c[f][col] = sum_n a_n(f) b_n[col]
+//   keys:    a_n = psi_f(k_n),                 b_n = [v_n; 1]   (n over the chunk's keys)
+//   queries: a_n = wdec_h[f] mono_f(q_n),      b_n = g_n        (n over the chunk's queries of
+//                                                                every head h of the KV head)
+// Workgroup = (64 features, chunk, sequence x KV head); thread = (feature, quarter of the 64
+// value columns); the feature's dims are fixed per thread, rows are staged 64 at a time.
+template <typename T, bool QSIDE>
+__global__ __launch_bounds__(kThreads) void oal_bwd_increments(int T_len, int C, int nch, int n_q_heads,
+                                                                int n_kv_heads, const T *__restrict__ x,
+                                                                const T *__restrict__ v, const float *__restrict__ gv,
+                                                                const float *__restrict__ gd,
+                                                                const unsigned char *__restrict__ params,
+                                                                float *__restrict__ st) {
+    __shared__ float xs[64 * 65];
+    __shared__ __align__(16) float bs[64 * 68];
+    const int tid = threadIdx.x, fl = tid >> 2, cq = tid & 3;
+    const int f = blockIdx.x * kFeatBlock + fl;
+    const int c = blockIdx.y, bkv = blockIdx.z;
+    const int b = bkv / n_kv_heads, kv = bkv % n_kv_heads, n_rep = n_q_heads / n_kv_heads;
+    int ia = OAL_D, ib = OAL_D;                    // dims of feature f; dim 64 reads the 1
+    if (f >= 1 && f <= OAL_D) {
+        ia = f - 1;
+    } else if (f > OAL_D && f < OAL_NFEAT) {
+        int idx = f - 1 - OAL_D, r = 0;
+        while (idx >= OAL_D - r) { idx -= OAL_D - r; ++r; }
+        ia = r;
+        ib = r + idx;
+    }
+    float acc[16], acc64 = 0.0f;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) acc[e] = 0.0f;
+    const int nsrc = QSIDE ? n_rep : 1;
+    const int tend = min(c * C + C, T_len);
+    for (int hs = 0; hs < nsrc; ++hs) {
+        const int h = kv * n_rep + hs;
+        const float w = QSIDE ? (f < OAL_NFEAT ? bwd_head(params, h)->wdec[f] : 0.0f) : 1.0f;
+        const size_t row0 = QSIDE ? ((size_t)b * n_q_heads + h) * T_len : ((size_t)b * n_kv_heads + kv) * T_len;
+        for (int t0 = c * C; t0 < tend; t0 += 64) {
+            __syncthreads();                       // the previous tile is consumed
+            stage_rows(xs, 65, x, row0, t0, T_len, 1.0f);
+            if constexpr (QSIDE) {
+                stage_g(bs, gv, gd, row0, t0, T_len);
+            } else {
+                stage_rows(bs, 68, v, row0, t0, T_len, 0.0f);
+                if (tid < 64) bs[tid * 68 + 64] = t0 + tid < T_len ? 1.0f : 0.0f;
+            }
+            __syncthreads();
+            for (int n = 0; n < 64; ++n) {
+                const float a = w * xs[n * 65 + ia] * xs[n * 65 + ib];
+                const float4 *br = reinterpret_cast<const float4 *>(bs + n * 68 + cq * 16);
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    const float4 bb = br[u];
+                    acc[4 * u] += a * bb.x;
+                    acc[4 * u + 1] += a * bb.y;
+                    acc[4 * u + 2] += a * bb.z;
+                    acc[4 * u + 3] += a * bb.w;
+                }
+                acc64 += a * bs[n * 68 + 64];
+            }
+        }
+    }
+    if (f < OAL_NFEAT) {
+        float *out = st + ((size_t)bkv * nch + c) * OAL_STATE_STRIDE;
+        float4 *o = reinterpret_cast<float4 *>(out + (size_t)f * OAL_D + cq * 16);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) o[u] = make_float4(acc[4 * u], acc[4 * u + 1], acc[4 * u + 2], acc[4 * u + 3]);
+        if (cq == 0) out[(size_t)OAL_NFEAT * OAL_D + f] = acc64;
+    }
+}
+
+// 2 / 6. Exclusive prefix (reverse = 0) or suffix (reverse = 1) sum over the chunks of each
+// (sequence x KV head), in place; one thread per state element.
+__global__ __launch_bounds__(kThreads) void oal_bwd_scan(int nch, int reverse, float *__restrict__ st) {
+    const int e = blockIdx.x * kThreads + threadIdx.x;
+    if (e >= OAL_NFEAT * OAL_V1) return;
+    float *p = st + (size_t)blockIdx.y * nch * OAL_STATE_STRIDE + e;
+    float run = 0.0f;
+#pragma unroll 4
+    for (int i = 0; i < nch; ++i) {
+        const size_t o = (size_t)(reverse ? nch - 1 - i : i) * OAL_STATE_STRIDE;
+        const float t = p[o];
+        p[o] = run;
+        run += t;
+    }
+}
+
+// Keys of the chunk that query lane i of tile qt sees, tile kt: all of an earlier tile, up to
+// and including its own position in its own tile.
+__device__ inline bool sees(int kt, int qt, int jj, int i) { return kt < qt || jj <= i; }
+
+// 3. u_i = phi_h(q_i) . S_c + sum_{j <= i in the chunk} kappa_ij [v_j; 1]; y = u[0:64] / u[64];
+//    g_i = (dy_i / den, -(dy_i . y_i) / den). Workgroup = (64-query tile, head, sequence);
+//    lane = query, the four waves split the feature rows r = w (mod 4) and the keys.
+template <typename T>
+__global__ __launch_bounds__(kThreads) void oal_bwd_readout_g(int T_len, int C, int nch, int n_q_heads,
+                                                               int n_kv_heads, const T *__restrict__ q,
+                                                               const T *__restrict__ k, const T *__restrict__ v,
+                                                               const float *__restrict__ dy,
+                                                               const unsigned char *__restrict__ params,
+                                                               const float *__restrict__ st, float *__restrict__ gv,
+                                                               float *__restrict__ gd) {
+    __shared__ float xq[64 * 65];
+    __shared__ float ks[64 * 64];
+    __shared__ __align__(16) float vs[64 * 68];
+    const int tpc = C / 64, c = blockIdx.x / tpc, qt = blockIdx.x % tpc;
+    const int h = blockIdx.y, b = blockIdx.z, n_rep = n_q_heads / n_kv_heads, kv = h / n_rep;
+    const int i = threadIdx.x & 63, w = wave_id();
+    const int t0 = c * C + qt * 64, t = t0 + i;
+    const bool valid = t < T_len;
+    const OalHeadDev *hd = bwd_head(params, h);
+    const cfloat *wd = uni(hd->wdec);
+    const int G = hd->G;
+    const size_t qrow = ((size_t)b * n_q_heads + h) * T_len, krow = ((size_t)b * n_kv_heads + kv) * T_len;
+    stage_rows(xq, 65, q, qrow, t0, T_len, 1.0f);
+    __syncthreads();
+    const float *xi = xq + i * 65;
+
+    float acc[65];
+#pragma unroll
+    for (int e = 0; e < 65; ++e) acc[e] = 0.0f;
+    if (c > 0) {                                   // S_0 = 0
+        const float *Sg = st + ((size_t)((size_t)b * n_kv_heads + kv) * nch + c) * OAL_STATE_STRIDE;
+        const cfloat *S = uni(Sg), *Sd = uni(Sg + (size_t)OAL_NFEAT * OAL_D);
+        if (w == 0) row_axpy<65>(acc, wd[0], S, Sd, 0);
+        for (int r = w; r < OAL_D; r += 4) {
+            const float qr = xi[r];
+            row_axpy<65>(acc, wd[1 + r] * qr, S, Sd, 1 + r);
+            const int base = quad_base(r);
+            for (int tt = r; tt < OAL_D; ++tt) row_axpy<65>(acc, wd[base + tt] * qr * xi[tt], S, Sd, base + tt);
+        }
+    }
+    for (int kt = 0; kt <= qt; ++kt) {
+        const int k0 = c * C + kt * 64;
+        __syncthreads();
+        stage_rows(ks, 64, k, krow, k0, T_len, 0.0f);
+        stage_rows(vs, 68, v, krow, k0, T_len, 1.0f);
+        __syncthreads();
+        if (valid) {
+            for (int jj = w; jj < 64; jj += 4) {
+                if (!sees(kt, qt, jj, i)) continue;
+                const float kap = pair_kappa(hd, G, xi, ks + jj * 64);
+                const float4 *vr = reinterpret_cast<const float4 *>(vs + jj * 68);
+#pragma unroll
+                for (int u = 0; u < 16; ++u) {
+                    const float4 vv = vr[u];
+                    acc[4 * u] += kap * vv.x;
+                    acc[4 * u + 1] += kap * vv.y;
+                    acc[4 * u + 2] += kap * vv.z;
+                    acc[4 * u + 3] += kap * vv.w;
+                }
+                acc[64] += kap;
+            }
+        }
+    }
+    // wave 0 collects the other waves' partial sums
+    float *red = vs;
+    for (int s = 1; s < 4; ++s) {
+        __syncthreads();
+        if (w == s) {
+#pragma unroll
+            for (int e = 0; e < 65; ++e) red[i * 65 + e] = acc[e];
+        }
+        __syncthreads();
+        if (w == 0) {
+#pragma unroll
+            for (int e = 0; e < 65; ++e) acc[e] += red[i * 65 + e];
+        }
+    }
+    if (w == 0 && valid) {
+        const float inv = 1.0f / acc[64];
+        const float *dyr = dy + (qrow + t) * OAL_D;
+        float *gr = gv + (qrow + t) * OAL_D;
+        float dot = 0.0f;
+#pragma unroll
+        for (int e = 0; e < 64; e += 4) {
+            const float4 d4 = *reinterpret_cast<const float4 *>(dyr + e);
+            dot += d4.x * (acc[e] * inv) + d4.y * (acc[e + 1] * inv) + d4.z * (acc[e + 2] * inv) +
+                   d4.w * (acc[e + 3] * inv);
+            *reinterpret_cast<float4 *>(gr + e) = make_float4(d4.x * inv, d4.y * inv, d4.z * inv, d4.w * inv);
+        }
+        gd[qrow + t] = -dot * inv;
+    }
+}
+
+// 4. dq_i = Jphi_h(q_i)^T (S_c g_i) + intra-chunk pairs. Workgroup = (64-query tile, head,
+//    sequence); lane = query; wave w takes the feature rows r = w (mod 4) and the keys
+//    j = w (mod 4). Per quadratic feature (r, t): x = S_c[f] . g, then dq_t += wdec x q_r and
+//    dq_r += wdec x q_t (t = r gives the 2 of the square). dq_t is a register (t unrolled);
+//    the row's dq_r, owned by one wave, goes to LDS.
+template <typename T>
+__global__ __launch_bounds__(kThreads) void oal_bwd_dq(int T_len, int C, int nch, int n_q_heads, int n_kv_heads,
+                                                        const T *__restrict__ q, const T *__restrict__ k,
+                                                        const T *__restrict__ v, const unsigned char *__restrict__ params,
+                                                        const float *__restrict__ st, const float *__restrict__ gv,
+                                                        const float *__restrict__ gd, float *__restrict__ dq) {
+    __shared__ float xq[64 * 65];
+    __shared__ float dql[64 * 65];
+    __shared__ float ks[64 * 64];
+    __shared__ __align__(16) float vs[64 * 68];
+    const int tpc = C / 64, c = blockIdx.x / tpc, qt = blockIdx.x % tpc;
+    const int h = blockIdx.y, b = blockIdx.z, n_rep = n_q_heads / n_kv_heads, kv = h / n_rep;
+    const int i = threadIdx.x & 63, w = wave_id();
+    const int t0 = c * C + qt * 64, t = t0 + i;
+    const bool valid = t < T_len;
+    const OalHeadDev *hd = bwd_head(params, h);
+    const cfloat *wd = uni(hd->wdec);
+    const int G = hd->G;
+    const size_t qrow = ((size_t)b * n_q_heads + h) * T_len, krow = ((size_t)b * n_kv_heads + kv) * T_len;
+    stage_rows(xq, 65, q, qrow, t0, T_len, 1.0f);
+    for (int e = threadIdx.x; e < 64 * 65; e += kThreads) dql[e] = 0.0f;
+    float g[65];
+#pragma unroll
+    for (int e = 0; e < 64; e += 4) {
+        const float4 g4 = valid ? *reinterpret_cast<const float4 *>(gv + (qrow + t) * OAL_D + e) : make_float4(0, 0, 0, 0);
+        g[e] = g4.x; g[e + 1] = g4.y; g[e + 2] = g4.z; g[e + 3] = g4.w;
+    }
+    g[64] = valid ? gd[qrow + t] : 0.0f;
+    __syncthreads();
+    const float *xi = xq + i * 65;
+
+    float d[64];
+#pragma unroll
+    for (int e = 0; e < 64; ++e) d[e] = 0.0f;
+    if (c > 0) {
+        const float *Sg = st + ((size_t)((size_t)b * n_kv_heads + kv) * nch + c) * OAL_STATE_STRIDE;
+        const cfloat *S = uni(Sg), *Sd = uni(Sg + (size_t)OAL_NFEAT * OAL_D);
+        for (int r = w; r < OAL_D; r += 4) {
+            const float qr = xi[r];
+            float dr = wd[1 + r] * row_dot(S, Sd, 1 + r, g);
+            const int base = quad_base(r);
+#pragma unroll
+            for (int tt = 0; tt < OAL_D; ++tt) {
+                if (tt >= r) {
+                    const float wx = wd[base + tt] * row_dot(S, Sd, base + tt, g);
+                    d[tt] += wx * qr;
+                    dr += wx * xi[tt];
+                }
+            }
+            dql[i * 65 + r] += dr;
+        }
+    }
+    for (int kt = 0; kt <= qt; ++kt) {
+        const int k0 = c * C + kt * 64;
+        __syncthreads();
+        stage_rows(ks, 64, k, krow, k0, T_len, 0.0f);
+        stage_rows(vs, 68, v, krow, k0, T_len, 1.0f);
+        __syncthreads();
+        if (valid) {
+            for (int jj = w; jj < 64; jj += 4) {
+                if (!sees(kt, qt, jj, i)) continue;
+                const float4 *vr = reinterpret_cast<const float4 *>(vs + jj * 68);
+                float e0 = g[64], e1 = 0.0f;
+#pragma unroll
+                for (int u = 0; u < 16; ++u) {
+                    const float4 vv = vr[u];
+                    e0 += g[4 * u] * vv.x + g[4 * u + 2] * vv.z;
+                    e1 += g[4 * u + 1] * vv.y + g[4 * u + 3] * vv.w;
+                }
+                pair_grad(hd, G, e0 + e1, xi, ks + jj * 64, d);
+            }
+        }
+    }
+    for (int s = 0; s < 4; ++s) {
+        __syncthreads();
+        if (w == s) {
+#pragma unroll
+            for (int e = 0; e < 64; ++e) dql[i * 65 + e] += d[e];
+        }
+    }
+    __syncthreads();
+    if (valid) {
+        float *o = dq + (qrow + t) * OAL_D + w * 16;
+        const float *src = dql + i * 65 + w * 16;
+#pragma unroll
+        for (int e = 0; e < 16; e += 4)
+            *reinterpret_cast<float4 *>(o + e) = make_float4(src[e], src[e + 1], src[e + 2], src[e + 3]);
+    }
+}
+
+// 7a. dv_j = (R_c^T psi(k_j))[0:64] + sum_h sum_{i >= j in the chunk} kappa_ij g_i[0:64].
+//     Workgroup = (64-key tile, KV head, sequence); lane = key; waves split the feature rows
+//     and, inside the chunk, the queries i = w (mod 4).
+template <typename T>
+__global__ __launch_bounds__(kThreads) void oal_bwd_dv(int T_len, int C, int nch, int n_q_heads, int n_kv_heads,
+                                                        const T *__restrict__ q, const T *__restrict__ k,
+                                                        const unsigned char *__restrict__ params,
+                                                        const float *__restrict__ st, const float *__restrict__ gv,
+                                                        const float *__restrict__ gd, float *__restrict__ dv) {
+    __shared__ float xk[64 * 65];
+    __shared__ float qs[64 * 64];
+    __shared__ __align__(16) float gs[64 * 68];
+    const int tpc = C / 64, c = blockIdx.x / tpc, kt = blockIdx.x % tpc;
+    const int kv = blockIdx.y, b = blockIdx.z, n_rep = n_q_heads / n_kv_heads;
+    const int j = threadIdx.x & 63, w = wave_id();
+    const int t0 = c * C + kt * 64, t = t0 + j;
+    const bool valid = t < T_len;
+    const size_t krow = ((size_t)b * n_kv_heads + kv) * T_len;
+    stage_rows(xk, 65, k, krow, t0, T_len, 1.0f);
+    __syncthreads();
+    const float *xj = xk + j * 65;
+
+    float acc[64];
+#pragma unroll
+    for (int e = 0; e < 64; ++e) acc[e] = 0.0f;
+    if (c < nch - 1) {                             // R of the last chunk is 0
+        const float *Rg = st + ((size_t)((size_t)b * n_kv_heads + kv) * nch + c) * OAL_STATE_STRIDE;
+        const cfloat *R = uni(Rg), *Rd = uni(Rg + (size_t)OAL_NFEAT * OAL_D);
+        if (w == 0) row_axpy<64>(acc, 1.0f, R, Rd, 0);
+        for (int r = w; r < OAL_D; r += 4) {
+            const float kr = xj[r];
+            row_axpy<64>(acc, kr, R, Rd, 1 + r);
+            const int base = quad_base(r);
+            for (int tt = r; tt < OAL_D; ++tt) row_axpy<64>(acc, kr * xj[tt], R, Rd, base + tt);
+        }
+    }
+    for (int hs = 0; hs < n_rep; ++hs) {
+        const int h = kv * n_rep + hs;
+        const OalHeadDev *hd = bwd_head(params, h);
+        const int G = hd->G;
+        const size_t qrow = ((size_t)b * n_q_heads + h) * T_len;
+        for (int qt = kt; qt < tpc; ++qt) {
+            const int q0 = c * C + qt * 64;
+            if (q0 >= T_len) break;
+            __syncthreads();
+            stage_rows(qs, 64, q, qrow, q0, T_len, 0.0f);
+            stage_g(gs, gv, gd, qrow, q0, T_len);
+            __syncthreads();
+            if (valid) {
+                for (int ii = w; ii < 64; ii += 4) {
+                    if (!sees(kt, qt, j, ii)) continue;   // key j of tile kt, query ii of tile qt
+                    const float kap = pair_kappa(hd, G, xj, qs + ii * 64);
+                    const float4 *gr = reinterpret_cast<const float4 *>(gs + ii * 68);
+#pragma unroll
+                    for (int u = 0; u < 16; ++u) {
+                        const float4 gg = gr[u];
+                        acc[4 * u] += kap * gg.x;
+                        acc[4 * u + 1] += kap * gg.y;
+                        acc[4 * u + 2] += kap * gg.z;
+                        acc[4 * u + 3] += kap * gg.w;
+                    }
+                }
+            }
+        }
+    }
+    float *red = gs;
+    for (int s = 1; s < 4; ++s) {
+        __syncthreads();
+        if (w == s) {
+#pragma unroll
+            for (int e = 0; e < 64; ++e) red[j * 65 + e] = acc[e];
+        }
+        __syncthreads();
+        if (w == 0) {
+#pragma unroll
+            for (int e = 0; e < 64; ++e) acc[e] += red[j * 65 + e];
+        }
+    }
+    if (w == 0 && valid) {
+        float *o = dv + (krow + t) * OAL_D;
+#pragma unroll
+        for (int e = 0; e < 64; e += 4)
+            *reinterpret_cast<float4 *>(o + e) = make_float4(acc[e], acc[e + 1], acc[e + 2], acc[e + 3]);
+    }
+}
+
+// 7b. dk_j = Jpsi(k_j)^T (R_c [v_j; 1]) + sum_h sum_{i >= j in the chunk} dkappa_ij dkappa/dk_j.
+//     Same decomposition as oal_bwd_dq with the roles of q and k (and S and R) exchanged;
+//     psi has no coefficients.
+template <typename T>
+__global__ __launch_bounds__(kThreads) void oal_bwd_dk(int T_len, int C, int nch, int n_q_heads, int n_kv_heads,
+                                                        const T *__restrict__ q, const T *__restrict__ k,
+                                                        const T *__restrict__ v, const unsigned char *__restrict__ params,
+                                                        const float *__restrict__ st, const float *__restrict__ gv,
+                                                        const float *__restrict__ gd, float *__restrict__ dk) {
+    __shared__ float xk[64 * 65];
+    __shared__ float dkl[64 * 65];
+    __shared__ float qs[64 * 64];
+    __shared__ __align__(16) float gs[64 * 68];
+    const int tpc = C / 64, c = blockIdx.x / tpc, kt = blockIdx.x % tpc;
+    const int kv = blockIdx.y, b = blockIdx.z, n_rep = n_q_heads / n_kv_heads;
+    const int j = threadIdx.x & 63, w = wave_id();
+    const int t0 = c * C + kt * 64, t = t0 + j;
+    const bool valid = t < T_len;
+    const size_t krow = ((size_t)b * n_kv_heads + kv) * T_len;
+    stage_rows(xk, 65, k, krow, t0, T_len, 1.0f);
+    for (int e = threadIdx.x; e < 64 * 65; e += kThreads) dkl[e] = 0.0f;
+    float vj[65];
+#pragma unroll
+    for (int e = 0; e < 64; ++e) vj[e] = valid ? oal_ld(v + (krow + t) * OAL_D + e) : 0.0f;
+    vj[64] = 1.0f;
+    __syncthreads();
+    const float *xj = xk + j * 65;
+
+    float d[64];
+#pragma unroll
+    for (int e = 0; e < 64; ++e) d[e] = 0.0f;
+    if (c < nch - 1) {
+        const float *Rg = st + ((size_t)((size_t)b * n_kv_heads + kv) * nch + c) * OAL_STATE_STRIDE;
+        const cfloat *R = uni(Rg), *Rd = uni(Rg + (size_t)OAL_NFEAT * OAL_D);
+        for (int r = w; r < OAL_D; r += 4) {
+            const float kr = xj[r];
+            float dr = row_dot(R, Rd, 1 + r, vj);
+            const int base = quad_base(r);
+#pragma unroll
+            for (int tt = 0; tt < OAL_D; ++tt) {
+                if (tt >= r) {
+                    const float y = row_dot(R, Rd, base + tt, vj);
+                    d[tt] += y * kr;
+                    dr += y * xj[tt];
+                }
+            }
+            dkl[j * 65 + r] += dr;
+        }
+    }
+    for (int hs = 0; hs < n_rep; ++hs) {
+        const int h = kv * n_rep + hs;
+        const OalHeadDev *hd = bwd_head(params, h);
+        const int G = hd->G;
+        const size_t qrow = ((size_t)b * n_q_heads + h) * T_len;
+        for (int qt = kt; qt < tpc; ++qt) {
+            const int q0 = c * C + qt * 64;
+            if (q0 >= T_len) break;
+            __syncthreads();
+            stage_rows(qs, 64, q, qrow, q0, T_len, 0.0f);
+            stage_g(gs, gv, gd, qrow, q0, T_len);
+            __syncthreads();
+            if (valid) {
+                for (int ii = w; ii < 64; ii += 4) {
+                    if (!sees(kt, qt, j, ii)) continue;
+                    const float4 *gr = reinterpret_cast<const float4 *>(gs + ii * 68);
+                    float e0 = gs[ii * 68 + 64], e1 = 0.0f;
+#pragma unroll
+                    for (int u = 0; u < 16; ++u) {
+                        const float4 gg = gr[u];
+                        e0 += gg.x * vj[4 * u] + gg.z * vj[4 * u + 2];
+                        e1 += gg.y * vj[4 * u + 1] + gg.w * vj[4 * u + 3];
+                    }
+                    pair_grad(hd, G, e0 + e1, xj, qs + ii * 64, d);
+                }
+            }
+        }
+    }
+    for (int s = 0; s < 4; ++s) {
+        __syncthreads();
+        if (w == s) {
+#pragma unroll
+            for (int e = 0; e < 64; ++e) dkl[j * 65 + e] += d[e];
+        }
+    }
+    __syncthreads();
+    if (valid) {
+        float *o = dk + (krow + t) * OAL_D + w * 16;
+        const float *src = dkl + j * 65 + w * 16;
+#pragma unroll
+        for (int e = 0; e < 16; e += 4)
+            *reinterpret_cast<float4 *>(o + e) = make_float4(src[e], src[e + 1], src[e + 2], src[e + 3]);
+    }
+}
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+template <typename T>
+hipError_t launch_backward(const oal_dims &d, int T_len, int C, const void *q_, const void *k_, const void *v_,
+                           const float *dy, const unsigned char *params, void *ws, float *dq, float *dk, float *dv,
+                           hipStream_t stream) {
+    const T *q = static_cast<const T *>(q_), *k = static_cast<const T *>(k_), *v = static_cast<const T *>(v_);
+    const int B = d.batch, Hq = d.n_q_heads, Hkv = d.n_kv_heads;
+    const int nch = (T_len + C - 1) / C, tpc = C / 64;
+    float *st = static_cast<float *>(ws);
+    float *gv = reinterpret_cast<float *>(static_cast<unsigned char *>(ws) +
+                                          align256((size_t)B * Hkv * nch * OAL_STATE_STRIDE * 4));
+    float *gd = reinterpret_cast<float *>(reinterpret_cast<unsigned char *>(gv) + align256((size_t)B * Hq * T_len * 64 * 4));
+    const dim3 blk(kThreads);
+    const dim3 g_inc((OAL_NFEAT + kFeatBlock - 1) / kFeatBlock, nch, B * Hkv);
+    const dim3 g_scan((OAL_NFEAT * OAL_V1 + kThreads - 1) / kThreads, B * Hkv);
+    const dim3 g_q(nch * tpc, Hq, B), g_k(nch * tpc, Hkv, B);
+    hipLaunchKernelGGL((oal_bwd_increments<T, false>), g_inc, blk, 0, stream, T_len, C, nch, Hq, Hkv, k, v,
+                       (const float *)nullptr, (const float *)nullptr, params, st);
+    hipLaunchKernelGGL(oal_bwd_scan, g_scan, blk, 0, stream, nch, 0, st);
+    hipLaunchKernelGGL(oal_bwd_readout_g<T>, g_q, blk, 0, stream, T_len, C, nch, Hq, Hkv, q, k, v, dy, params, st,
+                       gv, gd);
+    hipLaunchKernelGGL(oal_bwd_dq<T>, g_q, blk, 0, stream, T_len, C, nch, Hq, Hkv, q, k, v, params, st, gv, gd, dq);
+    hipLaunchKernelGGL((oal_bwd_increments<T, true>), g_inc, blk, 0, stream, T_len, C, nch, Hq, Hkv, q,
+                       (const T *)nullptr, gv, gd, params, st);
+    hipLaunchKernelGGL(oal_bwd_scan, g_scan, blk, 0, stream, nch, 1, st);
+    hipLaunchKernelGGL(oal_bwd_dv<T>, g_k, blk, 0, stream, T_len, C, nch, Hq, Hkv, q, k, params, st, gv, gd, dv);
+    hipLaunchKernelGGL(oal_bwd_dk<T>, g_k, blk, 0, stream, T_len, C, nch, Hq, Hkv, q, k, v, params, st, gv, gd, dk);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+size_t oal_backward_ws_bytes_impl(const oal_dims &d, int T_len, int C) {
+    const size_t nch = (size_t)(T_len + C - 1) / C;
+    return align256((size_t)d.batch * d.n_kv_heads * nch * OAL_STATE_STRIDE * 4) +
+           align256((size_t)d.batch * d.n_q_heads * T_len * 64 * 4) + align256((size_t)d.batch * d.n_q_heads * T_len * 4);
+}
+
+hipError_t oal_launch_backward(const oal_dims &d, int T_len, int C, const void *q, const void *k, const void *v,
+                               const float *dy, const void *params, void *ws, float *dq, float *dk, float *dv,
+                               hipStream_t stream) {
+    const unsigned char *p = static_cast<const unsigned char *>(params);
+    if (d.dtype == OAL_BF16)
+        return launch_backward<__bf16>(d, T_len, C, q, k, v, dy, p, ws, dq, dk, dv, stream);
+    return launch_backward<float>(d, T_len, C, q, k, v, dy, p, ws, dq, dk, dv, stream);
+}

@@ -27,6 +27,10 @@ hipError_t oal_launch_contribution(const oal_dims &d, int T_len, const void *q, 
                                    float *chi, float *chi_mean, hipStream_t stream);
 size_t oal_contribution_ws_bytes_impl(const oal_dims &d, int T_len);
 size_t oal_prefill_ws_bytes_impl(const oal_dims &d, int T_len, int C);
+hipError_t oal_launch_backward(const oal_dims &d, int T_len, int C, const void *q, const void *k, const void *v,
+                               const float *dy, const void *params, void *ws, float *dq, float *dk, float *dv,
+                               hipStream_t stream);
+size_t oal_backward_ws_bytes_impl(const oal_dims &d, int T_len, int C);
 
 namespace {
 
@@ -396,6 +400,37 @@ oal_status oal_contribution(const oal_dims *d, int32_t T, const void *q, const v
         (chi_mean && !aligned16(chi_mean)))
         return OAL_E_ALIGN;
     hipError_t e = oal_launch_contribution(*d, T, q, k, workspace, chi, chi_mean, stream);
+    if (e != hipSuccess) {
+        (void)hipGetLastError();
+        return OAL_E_HIP;
+    }
+    return OAL_OK;
+}
+
+static bool backward_shape_ok(const oal_dims *d, int32_t T, int32_t chunk) {
+    return (T + chunk - 1) / chunk <= 65535 && d->n_q_heads <= 65535;
+}
+
+size_t oal_prefill_backward_workspace_bytes(const oal_dims *d, int32_t T, int32_t chunk) {
+    if (check_dims(d) != OAL_OK || T < 0 || (chunk != 64 && chunk != 128 && chunk != 256)) return 0;
+    if (!backward_shape_ok(d, T, chunk)) return 0;
+    return oal_backward_ws_bytes_impl(*d, T, chunk);
+}
+
+oal_status oal_prefill_backward(const oal_dims *d, int32_t T, int32_t chunk, const void *q, const void *k,
+                                const void *v, const float *dy, const void *params_dev, void *workspace,
+                                float *dq, float *dk, float *dv, hipStream_t stream) {
+    oal_status st = check_dims(d);
+    if (st != OAL_OK) return st;
+    if (T < 0) return OAL_E_SHAPE;
+    if (chunk != 64 && chunk != 128 && chunk != 256) return OAL_E_UNSUPPORTED;
+    if (T == 0 || d->batch == 0) return OAL_OK;
+    if (!backward_shape_ok(d, T, chunk)) return OAL_E_UNSUPPORTED;
+    if (!q || !k || !v || !dy || !params_dev || !workspace || !dq || !dk || !dv) return OAL_E_ARG;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(dy) || !aligned16(params_dev) ||
+        !aligned16(workspace) || !aligned16(dq) || !aligned16(dk) || !aligned16(dv))
+        return OAL_E_ALIGN;
+    hipError_t e = oal_launch_backward(*d, T, chunk, q, k, v, dy, params_dev, workspace, dq, dk, dv, stream);
     if (e != hipSuccess) {
         (void)hipGetLastError();
         return OAL_E_HIP;

@@ -220,6 +220,32 @@ size_t oal_contribution_workspace_bytes(const oal_dims *dims, int32_t T);
 oal_status oal_contribution(const oal_dims *dims, int32_t T, const void *q, const void *k,
                             void *workspace, float *chi, float *chi_mean, hipStream_t stream);
 
+/* Backward of oal_prefill from an empty prefix (reproduction notes of arXiv 2610.13674,
+ * section "核心公式": kappa, the H-state recurrence and the readout; the gradients follow by
+ * the chain rule through the chunked form). For y = oal_prefill(q, k, v) of T tokens per
+ * sequence starting from a zero state, and the loss sum(dy * y), it writes
+ *   dq [batch, n_q_heads, T, 64], dk and dv [batch, n_kv_heads, T, 64], all fp32 (device).
+ * The coefficients (L, eps) receive no gradient here. The forward quantities it needs (the
+ * prefix states, y and the normaliser per query) are recomputed in fp32 from q, k, v; the
+ * caller passes no saved output.
+ *   T          -- tokens per sequence (equal lengths), >= 0; T = 0 or batch = 0 is a no-op.
+ *   chunk      -- 64, 128 or 256: tokens per chunk of the chunked form.
+ *   q, k, v    -- as for oal_prefill ([batch, heads, T, 64] of dims->dtype, device).
+ *   dy         -- [batch, n_q_heads, T, 64] fp32 (device).
+ *   params_dev -- the blob oal_state_init uploaded.
+ *   workspace  -- oal_prefill_backward_workspace_bytes(dims, T, chunk) bytes of device scratch
+ *                 (per-chunk states, one block of OAL_STATE_STRIDE floats per sequence, KV
+ *                 head and chunk, then the per-query readout gradients); contents on entry
+ *                 do not matter.
+ * All arithmetic is fp32 whatever dims->dtype is (bf16 inputs are widened on load). Every
+ * pointer must be 16-byte aligned (OAL_E_ALIGN). More than 65535 chunks per sequence or
+ * more than 65535 query heads give OAL_E_UNSUPPORTED. */
+size_t oal_prefill_backward_workspace_bytes(const oal_dims *dims, int32_t T, int32_t chunk);
+oal_status oal_prefill_backward(const oal_dims *dims, int32_t T, int32_t chunk, const void *q,
+                                const void *k, const void *v, const float *dy,
+                                const void *params_dev, void *workspace, float *dq, float *dk,
+                                float *dv, hipStream_t stream);
+
 /* Decode step for sequences whose states live in a pool (serving: a batch of active
  * sequences over a larger set of state blocks). Sequence b of the batch uses pool block
  * slots[b]; otherwise identical to oal_decode_step (same kernels, same results bit for bit

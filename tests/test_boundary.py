@@ -52,6 +52,16 @@ def test_sizes():
     assert gpq.oal_contribution_workspace_bytes(d, 0) == 0
     assert gpq.oal_contribution_workspace_bytes(gpq.make_dims(0, 14, 2, "bf16"), 64) == 0
     assert gpq.oal_contribution_workspace_bytes(bad, 64) == 0
+    # backward: per-chunk states per (sequence, KV head), then g (64 + 1 floats per query)
+    al = lambda x: -(-x // 256) * 256
+    assert gpq.oal_prefill_backward_workspace_bytes(d, 4096, 64) == (
+        al(3 * 2 * 64 * 139456 * 4) + al(3 * 14 * 4096 * 64 * 4) + al(3 * 14 * 4096 * 4))
+    assert gpq.oal_prefill_backward_workspace_bytes(d, 130, 128) == (
+        al(3 * 2 * 2 * 139456 * 4) + al(3 * 14 * 130 * 64 * 4) + al(3 * 14 * 130 * 4))
+    assert gpq.oal_prefill_backward_workspace_bytes(d, 4096, 100) == 0
+    assert gpq.oal_prefill_backward_workspace_bytes(d, -1, 64) == 0
+    assert gpq.oal_prefill_backward_workspace_bytes(d, 64 * 65536, 64) == 0
+    assert gpq.oal_prefill_backward_workspace_bytes(bad, 64, 64) == 0
 
 
 def _code(fn, *args):
@@ -106,6 +116,16 @@ def test_validation_errors_enqueue_nothing():
     assert _code(gpq.oal_contribution, d, 8, A, A, A, A, A + 4, 0) == 4
     assert _code(gpq.oal_contribution, gpq.make_dims(1, 2, 1, 7), 8, *c4, 0) == 3
     assert _code(gpq.oal_contribution, gpq.make_dims(1, 2, 1, "bf16", d_h=32), 8, *c4, 0) == 5
+    b9 = (A, A, A, A, A, A, A, A, A)   # q, k, v, dy, params, workspace, dq, dk, dv
+    assert _code(gpq.oal_prefill_backward, d, 8, 100, *b9, 0) == 5            # chunk
+    assert _code(gpq.oal_prefill_backward, d, -1, 64, *b9, 0) == 2            # T < 0
+    assert _code(gpq.oal_prefill_backward, d, 0, 64, *([None] * 9), 0) == 0   # T = 0: no-op
+    assert _code(gpq.oal_prefill_backward, gpq.make_dims(0, 2, 1, "bf16"), 8, 64, *([None] * 9), 0) == 0
+    assert _code(gpq.oal_prefill_backward, d, 8, 64, A, A, A, None, A, A, A, A, A, 0) == 1   # no dy
+    assert _code(gpq.oal_prefill_backward, d, 8, 64, A, A, A, A, A, None, A, A, A, 0) == 1   # no workspace
+    assert _code(gpq.oal_prefill_backward, d, 8, 64, A, A, A, A, A, A, A, A, A + 4, 0) == 4  # misaligned dv
+    assert _code(gpq.oal_prefill_backward, d, 64 * 65536, 64, *b9, 0) == 5    # > 65535 chunks
+    assert _code(gpq.oal_prefill_backward, gpq.make_dims(1, 3, 2, "bf16"), 8, 64, *b9, 0) == 2
 
 
 def test_param_validation():

@@ -1,0 +1,169 @@
+"""GPU parity of the prefill backward (oal_prefill_backward) against the oracle backward.
+
+The oracle differentiates the dense O(T^2) definition in fp64 (pinned by finite differences,
+the L = 0 closed form and the scale invariance in the CPU suite); the library runs the
+chunked linear-time form in fp32 on the same (dtype-exact) inputs. The error measure is
+blockwise: per (sequence, head) slice of dq, dk or dv, max |x - x*| / max |x*|.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from oal_synth import small, HeadParams
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+from gpu_util import to_dev  # noqa: E402
+import grouped_positive_quadratic_amd as gpq  # noqa: E402
+
+# fp32 arithmetic throughout (the inputs are exact in fp32 for both dtypes)
+BWD_TOL = 2e-4
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.fail("GPU tests need a GPU")
+
+
+def run_backward(inp, dy, chunk):
+    B, Hq, Hkv, T, _, _ = inp.dims
+    dims = gpq.make_dims(B, Hq, Hkv, inp.dtype)
+    hp = gpq.HeadParamsC.from_params(inp.params)
+    params = torch.empty(max(gpq.oal_params_bytes(dims), 16), dtype=torch.uint8, device="cuda")
+    gpq.oal_state_init(dims, hp, params, None)
+    q, k, v = (to_dev(x, inp.dtype) for x in (inp.q, inp.k, inp.v))
+    dyd = torch.from_numpy(np.ascontiguousarray(dy, np.float32)).cuda()
+    ws = torch.empty(max(gpq.oal_prefill_backward_workspace_bytes(dims, T, chunk), 16), dtype=torch.uint8,
+                     device="cuda")
+    dq = torch.full((B, Hq, T, 64), np.nan, dtype=torch.float32, device="cuda")
+    dk = torch.full((B, Hkv, T, 64), np.nan, dtype=torch.float32, device="cuda")
+    dv = torch.full((B, Hkv, T, 64), np.nan, dtype=torch.float32, device="cuda")
+    gpq.oal_prefill_backward(dims, T, chunk, q, k, v, dyd, params, ws, dq, dk, dv)
+    torch.cuda.synchronize()
+    return dq.cpu().numpy(), dk.cpu().numpy(), dv.cpu().numpy()
+
+
+def slice_err(x, ref):
+    """max over (sequence, head) slices of max |x - ref| / max |ref|; a slice whose reference
+    is below 1e-3 of the tensor's largest entry is measured against that 1e-3 instead."""
+    x = np.asarray(x, np.float64)
+    num = np.abs(x - ref).reshape(ref.shape[0], ref.shape[1], -1).max(-1)
+    den = np.abs(ref).reshape(ref.shape[0], ref.shape[1], -1).max(-1)
+    return float((num / np.maximum(den, max(1e-3 * den.max(), 1e-300))).max())
+
+
+def check(inp, chunk, seed, tol=BWD_TOL, name=""):
+    B, Hq, Hkv, T, _, _ = inp.dims
+    dy = np.random.default_rng(seed).normal(0.0, 1.0, (B, Hq, T, 64)).astype(np.float32)
+    dq, dk, dv = run_backward(inp, dy, chunk)
+    rq, rk, rv, _, _ = oracle.backward(inp.q, inp.k, inp.v, inp.params, dy)
+    if T == 1:
+        # one token: y = v_0 whatever q and k are, so dq = dk = 0; both sides hold rounding
+        # residue of dkappa = g . [v; 1] (a difference of two equal terms)
+        scale = np.abs(dy).max() * np.abs(inp.v).max()
+        assert np.abs(rq).max() <= 1e-12 * scale and np.abs(rk).max() <= 1e-12 * scale
+        assert np.abs(dq).max() <= 1e-5 * scale and np.abs(dk).max() <= 1e-5 * scale
+        rq, rk = dq, dk
+    e = (slice_err(dq, rq), slice_err(dk, rk), slice_err(dv, rv))
+    print(f"[parity] backward {name} {inp.dims[:4]} C={chunk} {inp.dtype}: "
+          f"dq={e[0]:.2e} dk={e[1]:.2e} dv={e[2]:.2e} tol={tol:.0e}", flush=True)
+    assert np.isfinite(dq).all() and np.isfinite(dk).all() and np.isfinite(dv).all()
+    assert max(e) <= tol
+    return dq, dk, dv
+
+
+SMALL = [  # seed, B, Hq, Hkv, T, chunk: ragged tails, one token, several chunks, n_rep 1/4/7/16
+    (41, 1, 7, 1, 200, 64),
+    (42, 2, 4, 2, 77, 128),
+    (43, 1, 2, 1, 1, 64),
+    (44, 1, 8, 1, 300, 256),
+    (45, 2, 3, 1, 64, 64),
+    (46, 1, 14, 2, 330, 64),
+    (47, 1, 16, 1, 130, 128),
+    (48, 1, 3, 3, 150, 64),
+]
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("case", SMALL, ids=[f"s{c[0]}" for c in SMALL])
+def test_backward_small(case, dtype):
+    seed, B, Hq, Hkv, T, chunk = case
+    check(small(seed, B, Hq, Hkv, T, dtype), chunk, seed + 1000)
+
+
+@pytest.mark.parametrize("chunk", [64, 128, 256])
+def test_backward_chunk_sizes_agree(chunk):
+    """Same inputs at every chunk size: each against the oracle."""
+    check(small(51, 1, 7, 1, 260, "bf16"), chunk, 51)
+
+
+def test_backward_many_groups():
+    """64 groups (one per dim): the z-terms run in several register blocks."""
+    rng = np.random.default_rng(52)
+    inp = small(52, 1, 2, 1, 150, dtype="bf16", g_hi=2)
+    G = 64
+    L = np.zeros((2, G + 1, G + 1), np.float32)
+    for h in range(2):
+        L[h] = np.tril(rng.normal(0, 0.3, (G + 1, G + 1)))
+        np.fill_diagonal(L[h], np.abs(np.diag(L[h])) + 0.1)
+    inp.params = HeadParams(np.full(2, G, np.int32),
+                            np.stack([rng.permutation(64), np.arange(64)]).astype(np.uint8), L,
+                            np.full(2, 1e-3, np.float32))
+    check(inp, 64, 52, name="g64")
+
+
+def test_backward_l_zero_closed_form():
+    """L = 0: kappa = eps, y_i is the prefix mean of v, so dq = dk = 0 and
+    dv_j = sum_{i >= j} dy_i / (i + 1) summed over the query heads of the KV head."""
+    inp = small(53, 1, 4, 1, 150, "bf16")
+    inp.params.L[:] = 0.0
+    inp.params.eps[:] = 0.5
+    B, Hq, Hkv, T, _, _ = inp.dims
+    dy = np.random.default_rng(53).normal(0.0, 1.0, (B, Hq, T, 64)).astype(np.float32)
+    dq, dk, dv = run_backward(inp, dy, 64)
+    assert np.all(dq == 0.0) and np.all(dk == 0.0)
+    w = dy.astype(np.float64) / np.arange(1, T + 1)[None, None, :, None]
+    ref = np.flip(np.cumsum(np.flip(w, 2), 2), 2).sum(1, keepdims=True)
+    assert slice_err(dv, ref) <= BWD_TOL
+
+
+def test_backward_deterministic():
+    inp = small(54, 1, 7, 1, 200, "bf16")
+    dy = np.random.default_rng(54).normal(0.0, 1.0, (1, 7, 200, 64)).astype(np.float32)
+    a = run_backward(inp, dy, 64)
+    b = run_backward(inp, dy, 64)
+    for x, y in zip(a, b):
+        assert np.array_equal(x, y)
+
+
+def test_backward_matches_forward_directional_derivative():
+    """<dq, e_q> + <dk, e_k> + <dv, e_v> equals the derivative of sum(dy * y) along
+    (e_q, e_k, e_v), y being the dense definition in fp64 (central difference, step 1e-3)."""
+    inp = small(55, 1, 4, 1, 96, "f32")
+    B, Hq, Hkv, T, _, _ = inp.dims
+    rng = np.random.default_rng(55)
+    dy = rng.normal(0.0, 1.0, (B, Hq, T, 64)).astype(np.float32)
+    dq, dk, dv = run_backward(inp, dy, 64)
+    eq, ek, ev = (rng.normal(0.0, 1.0, x.shape).astype(np.float64) for x in (inp.q, inp.k, inp.v))
+    pred = float((dq * eq).sum() + (dk * ek).sum() + (dv * ev).sum())
+    h = 1e-3
+
+    def loss(s):
+        y = oracle.dense(inp.q + s * eq, inp.k + s * ek, inp.v + s * ev, inp.params)
+        return float((dy * y).sum())
+
+    fd = (loss(h) - loss(-h)) / (2 * h)
+    print(f"[parity] backward directional: pred={pred:.6e} fd={fd:.6e}", flush=True)
+    assert abs(pred - fd) <= 1e-3 * max(1.0, abs(fd))
+
+
+def test_backward_empty_and_validation():
+    dims = gpq.make_dims(1, 2, 1, "f32")
+    x = torch.zeros(16, dtype=torch.float32, device="cuda")
+    ws = torch.zeros(16, dtype=torch.uint8, device="cuda")
+    # T = 0: no-op
+    gpq.oal_prefill_backward(dims, 0, 64, x, x, x, x, ws, ws, x, x, x)
+    with pytest.raises(gpq.OALError, match="OAL_E_UNSUPPORTED"):
+        gpq.oal_prefill_backward(dims, 10, 32, x, x, x, x, ws, ws, x, x, x)
