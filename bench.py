@@ -15,7 +15,8 @@ mean) over a calibration batch of 8 prompts x 4096 tokens, timed over 50 back-to
 
 Prints one JSON line. `value` is prefill tokens/s; `roofline` is the readout kernel
 (the dominant one) against the bf16 MFMA peak; `decode` holds decode tokens/s and the
-decode kernel against HBM peak; `contribution` the chi kernel against HBM peak;
+decode kernel against HBM peak; `contribution` the chi kernel against HBM peak; `backward` the
+prefill backward (dq, dk, dv) of the headline workload against the fp32 vector peak;
 `cpu_baseline` is the fp64 CPU oracle on the full prefill batch, timed on this host.
 """
 from __future__ import annotations
@@ -33,6 +34,7 @@ D, V1, NFEAT = 64, 65, 2145
 FLOP_PER_TOKEN_HEAD = 2 * NFEAT * V1          # 278,850: one feature-space contraction
 PEAK_BF16_TFLOPS = 2500.0                     # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0                         # MI355X HBM3E
+PEAK_FP32_TFLOPS = 157.3                      # MI355X fp32 vector (packed FMA; 78.6 without)
 PHASE_EVERY = 4                               # timed steps with per-kernel events
 
 
@@ -50,6 +52,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-contribution", action="store_true",
                     help="skip the contribution-score (chi) measurement")
+    ap.add_argument("--no-backward", action="store_true",
+                    help="skip the prefill-backward measurement")
     ap.add_argument("--no-scaling", action="store_true",
                     help="skip the B=8 x T=4096 chunk sweep and the T=32768 prefill")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -275,6 +279,48 @@ def main():
         del cq, ck, cws, chi, chi_mean
         torch.cuda.empty_cache()
     cache.clear()
+
+    # ---------------- prefill backward on the headline workload ----------------
+    if not args.no_backward:
+        bi = qwen_like(1, 4096, 2, name="cfg2")
+        Bb, Hqb, Hkvb, Tb, _, _ = bi.dims
+        Cb = 64
+        bd = gpq.make_dims(Bb, Hqb, Hkvb, "bf16")
+        bparams = torch.empty(gpq.oal_params_bytes(bd), dtype=torch.uint8, device=dev)
+        gpq.oal_state_init(bd, gpq.HeadParamsC.from_params(bi.params), bparams, None)
+        bq, bk, bv = (torch.from_numpy(a).to(torch.bfloat16).to(dev).contiguous() for a in (bi.q, bi.k, bi.v))
+        gen = torch.Generator(device=dev)
+        gen.manual_seed(7)
+        bdy = torch.randn((Bb, Hqb, Tb, D), generator=gen, dtype=torch.float32, device=dev)
+        bws = torch.empty(gpq.oal_prefill_backward_workspace_bytes(bd, Tb, Cb), dtype=torch.uint8, device=dev)
+        bdq = torch.empty((Bb, Hqb, Tb, D), dtype=torch.float32, device=dev)
+        bdk = torch.empty((Bb, Hkvb, Tb, D), dtype=torch.float32, device=dev)
+        bdv = torch.empty_like(bdk)
+        for _ in range(2):
+            gpq.oal_prefill_backward(bd, Tb, Cb, bq, bk, bv, bdy, bparams, bws, bdq, bdk, bdv)
+        torch.cuda.synchronize()
+        reps = 5
+        e0, e1 = gpq.TimingEvent(), gpq.TimingEvent()
+        e0.record(stream)
+        for _ in range(reps):
+            gpq.oal_prefill_backward(bd, Tb, Cb, bq, bk, bv, bdy, bparams, bws, bdq, bdk, bdv)
+        e1.record(stream)
+        bms = e0.elapsed_time(e1) / reps
+        # algorithmic fp32 work: six state-sized contractions of 2 * 2145 * 65 flops per token --
+        # per query head: the readout u, S g and the query increment; per KV head: the key
+        # increment, R^T psi(k) and R [v; 1]
+        bflops = (3 * Bb * Hqb + 3 * Bb * Hkvb) * Tb * 2 * 2145 * 65
+        bach = bflops / (bms * 1e-3) / 1e12
+        out["backward"] = {
+            "workload": f"prefill backward (dq, dk, dv) from an empty prefix, B={Bb} T={Tb} "
+                        f"{Hqb}q/{Hkvb}kv, bf16 inputs, fp32 arithmetic, chunk {Cb}",
+            "value": Bb * Tb / (bms * 1e-3), "unit": "tokens/s", "ms_per_call": bms, "calls": reps,
+            "roofline": {"bound": "alu", "kernel": "the call's eight fp32 launches together",
+                         "achieved": bach, "peak": PEAK_FP32_TFLOPS, "unit": "TFLOP/s",
+                         "frac": bach / PEAK_FP32_TFLOPS, "traffic": None,
+                         "algorithmic_flops_per_call": bflops}}
+        del bq, bk, bv, bdy, bws, bdq, bdk, bdv, bparams
+        torch.cuda.empty_cache()
 
     # ---------------- decode ----------------
     if not args.no_decode:
