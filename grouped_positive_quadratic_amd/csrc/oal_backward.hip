@@ -27,10 +27,12 @@
 //   1. oal_bwd_increments<keys>:    per chunk psi(K_c)^T [V_c; 1]           -> workspace states
 //   2. oal_bwd_scan (forward):      exclusive prefix over chunks: S_c
 //   3. oal_bwd_readout_g:           u_i (inter + intra), y, den -> g_i     -> workspace g
-//   4. oal_bwd_dq:                  dq
-//   5. oal_bwd_increments<queries>: per chunk sum_h phi_h(Q_c)^T G_c       -> workspace states
-//   6. oal_bwd_scan (reverse):      exclusive suffix over chunks: R_c
-//   7. oal_bwd_dv, oal_bwd_dk:      dv, dk
+//   4. oal_bwd_dq_inter, _intra:    dq (state part, then the pairs inside the chunk)
+//   5. oal_bwd_dkv_intra:           dk, dv partials of the pairs inside the chunk
+//   6. oal_bwd_increments<queries>: per chunk sum_h phi_h(Q_c)^T G_c       -> workspace states
+//   7. oal_bwd_scan (reverse):      exclusive suffix over chunks: R_c
+//   8. oal_bwd_dk_inter, _dv_inter: dk, dv partials of the state part
+//   9. oal_bwd_kv_reduce:           dk, dv (the partials added in a fixed order)
 #include <hip/hip_runtime.h>
 
 #include "oal_device.h"
@@ -128,6 +130,37 @@ __device__ inline void grad_block(const OalHeadDev *hd, int m0, float e, const f
         for (int mm = 0; mm < NB; ++mm) s += z[mm] * Lz[mm * OAL_D + r];
         acc[r] += s * y[r];
     }
+}
+
+// Both at once for one pair: returns kappa and adds e * dkappa/dx to acc (one z per block).
+template <int NB>
+__device__ inline float kappa_grad_block(const OalHeadDev *hd, int m0, float e, const float *x, const float *y,
+                                         float (&acc)[64]) {
+    float z[NB];
+    z_block<NB>(hd, m0, x, y, z);
+    const cfloat *Lz = uni(hd->Lz) + m0 * OAL_D;
+    float kap = 0.0f;
+#pragma unroll
+    for (int mm = 0; mm < NB; ++mm) {
+        kap += z[mm] * z[mm];
+        z[mm] *= 2.0f * e;
+    }
+#pragma unroll
+    for (int r = 0; r < OAL_D; ++r) {
+        float s = 0.0f;
+#pragma unroll
+        for (int mm = 0; mm < NB; ++mm) s += z[mm] * Lz[mm * OAL_D + r];
+        acc[r] += s * y[r];
+    }
+    return kap;
+}
+
+__device__ inline float pair_kappa_grad(const OalHeadDev *hd, int G, float e, const float *x, const float *y,
+                                        float (&acc)[64]) {
+    float kap = hd->eps;
+    for (int m0 = 0; m0 <= min(G, 63); m0 += kMBlock) kap += kappa_grad_block<kMBlock>(hd, m0, e, x, y, acc);
+    if (G == 64) kap += kappa_grad_block<1>(hd, 64, e, x, y, acc);
+    return kap;
 }
 
 // acc[r] += e * y[r] * 2 sum_m z_m Lz[m][r]: the pair's dkappa/dx scaled by e (dkappa), with
@@ -288,6 +321,7 @@ __global__ __launch_bounds__(kThreads) void oal_bwd_readout_g(int T_len, int C, 
             const float qr = xi[r];
             row_axpy<65>(acc, wd[1 + r] * qr, S, Sd, 1 + r);
             const int base = quad_base(r);
+#pragma unroll 4
             for (int tt = r; tt < OAL_D; ++tt) row_axpy<65>(acc, wd[base + tt] * qr * xi[tt], S, Sd, base + tt);
         }
     }
@@ -344,30 +378,26 @@ __global__ __launch_bounds__(kThreads) void oal_bwd_readout_g(int T_len, int C, 
     }
 }
 
-// 4. dq_i = Jphi_h(q_i)^T (S_c g_i) + intra-chunk pairs. Workgroup = (64-query tile, head,
-//    sequence); lane = query; wave w takes the feature rows r = w (mod 4) and the keys
-//    j = w (mod 4). Per quadratic feature (r, t): x = S_c[f] . g, then dq_t += wdec x q_r and
-//    dq_r += wdec x q_t (t = r gives the 2 of the square). dq_t is a register (t unrolled);
-//    the row's dq_r, owned by one wave, goes to LDS.
+// 4a. dq_i = Jphi_h(q_i)^T (S_c g_i) (the state part). Workgroup = (64-query tile, head,
+//     sequence); lane = query; wave w takes the feature rows r = w (mod 4). Per quadratic
+//     feature (r, t): x = S_c[f] . g, then dq_t += wdec x q_r and dq_r += wdec x q_t (t = r
+//     gives the 2 of the square). dq_t is a register (t unrolled); the row's dq_r, owned by
+//     one wave, goes to LDS.
 template <typename T>
-__global__ __launch_bounds__(kThreads) void oal_bwd_dq(int T_len, int C, int nch, int n_q_heads, int n_kv_heads,
-                                                        const T *__restrict__ q, const T *__restrict__ k,
-                                                        const T *__restrict__ v, const unsigned char *__restrict__ params,
-                                                        const float *__restrict__ st, const float *__restrict__ gv,
-                                                        const float *__restrict__ gd, float *__restrict__ dq) {
+__global__ __launch_bounds__(kThreads) void oal_bwd_dq_inter(int T_len, int C, int nch, int n_q_heads,
+                                                              int n_kv_heads, const T *__restrict__ q,
+                                                              const unsigned char *__restrict__ params,
+                                                              const float *__restrict__ st, const float *__restrict__ gv,
+                                                              const float *__restrict__ gd, float *__restrict__ dq) {
     __shared__ float xq[64 * 65];
     __shared__ float dql[64 * 65];
-    __shared__ float ks[64 * 64];
-    __shared__ __align__(16) float vs[64 * 68];
     const int tpc = C / 64, c = blockIdx.x / tpc, qt = blockIdx.x % tpc;
     const int h = blockIdx.y, b = blockIdx.z, n_rep = n_q_heads / n_kv_heads, kv = h / n_rep;
     const int i = threadIdx.x & 63, w = wave_id();
     const int t0 = c * C + qt * 64, t = t0 + i;
     const bool valid = t < T_len;
-    const OalHeadDev *hd = bwd_head(params, h);
-    const cfloat *wd = uni(hd->wdec);
-    const int G = hd->G;
-    const size_t qrow = ((size_t)b * n_q_heads + h) * T_len, krow = ((size_t)b * n_kv_heads + kv) * T_len;
+    const cfloat *wd = uni(bwd_head(params, h)->wdec);
+    const size_t qrow = ((size_t)b * n_q_heads + h) * T_len;
     stage_rows(xq, 65, q, qrow, t0, T_len, 1.0f);
     for (int e = threadIdx.x; e < 64 * 65; e += kThreads) dql[e] = 0.0f;
     float g[65];
@@ -383,7 +413,7 @@ __global__ __launch_bounds__(kThreads) void oal_bwd_dq(int T_len, int C, int nch
     float d[64];
 #pragma unroll
     for (int e = 0; e < 64; ++e) d[e] = 0.0f;
-    if (c > 0) {
+    if (c > 0) {                                   // S_0 = 0
         const float *Sg = st + ((size_t)((size_t)b * n_kv_heads + kv) * nch + c) * OAL_STATE_STRIDE;
         const cfloat *S = uni(Sg), *Sd = uni(Sg + (size_t)OAL_NFEAT * OAL_D);
         for (int r = w; r < OAL_D; r += 4) {
@@ -401,6 +431,54 @@ __global__ __launch_bounds__(kThreads) void oal_bwd_dq(int T_len, int C, int nch
             dql[i * 65 + r] += dr;
         }
     }
+    for (int s = 0; s < 4; ++s) {
+        __syncthreads();
+        if (w == s) {
+#pragma unroll
+            for (int e = 0; e < 64; ++e) dql[i * 65 + e] += d[e];
+        }
+    }
+    __syncthreads();
+    if (valid) {
+        float *o = dq + (qrow + t) * OAL_D + w * 16;
+        const float *src = dql + i * 65 + w * 16;
+#pragma unroll
+        for (int e = 0; e < 16; e += 4)
+            *reinterpret_cast<float4 *>(o + e) = make_float4(src[e], src[e + 1], src[e + 2], src[e + 3]);
+    }
+}
+
+// 4b. dq_i += sum_{j <= i in the chunk} dkappa_ij dkappa_ij/dq_i, dkappa_ij = g_i . [v_j; 1].
+//     Same workgroups as 4a (launched after it); the four waves take the keys j = w (mod 4).
+template <typename T>
+__global__ __launch_bounds__(kThreads) void oal_bwd_dq_intra(int T_len, int C, int n_q_heads, int n_kv_heads,
+                                                              const T *__restrict__ q, const T *__restrict__ k,
+                                                              const T *__restrict__ v, const unsigned char *__restrict__ params,
+                                                              const float *__restrict__ gv, const float *__restrict__ gd,
+                                                              float *__restrict__ dq) {
+    __shared__ float xq[64 * 65];
+    __shared__ float ks[64 * 64];
+    __shared__ __align__(16) float vs[64 * 68];
+    const int tpc = C / 64, c = blockIdx.x / tpc, qt = blockIdx.x % tpc;
+    const int h = blockIdx.y, b = blockIdx.z, n_rep = n_q_heads / n_kv_heads, kv = h / n_rep;
+    const int i = threadIdx.x & 63, w = wave_id();
+    const int t0 = c * C + qt * 64, t = t0 + i;
+    const bool valid = t < T_len;
+    const OalHeadDev *hd = bwd_head(params, h);
+    const int G = hd->G;
+    const size_t qrow = ((size_t)b * n_q_heads + h) * T_len, krow = ((size_t)b * n_kv_heads + kv) * T_len;
+    stage_rows(xq, 65, q, qrow, t0, T_len, 1.0f);
+    float g[65];
+#pragma unroll
+    for (int e = 0; e < 64; e += 4) {
+        const float4 g4 = valid ? *reinterpret_cast<const float4 *>(gv + (qrow + t) * OAL_D + e) : make_float4(0, 0, 0, 0);
+        g[e] = g4.x; g[e + 1] = g4.y; g[e + 2] = g4.z; g[e + 3] = g4.w;
+    }
+    g[64] = valid ? gd[qrow + t] : 0.0f;
+    const float *xi = xq + i * 65;
+    float d[64];
+#pragma unroll
+    for (int e = 0; e < 64; ++e) d[e] = 0.0f;
     for (int kt = 0; kt <= qt; ++kt) {
         const int k0 = c * C + kt * 64;
         __syncthreads();
@@ -422,128 +500,56 @@ __global__ __launch_bounds__(kThreads) void oal_bwd_dq(int T_len, int C, int nch
             }
         }
     }
+    float *red = vs;
     for (int s = 0; s < 4; ++s) {
         __syncthreads();
         if (w == s) {
 #pragma unroll
-            for (int e = 0; e < 64; ++e) dql[i * 65 + e] += d[e];
+            for (int e = 0; e < 64; ++e) red[i * 65 + e] = (s == 0 ? 0.0f : red[i * 65 + e]) + d[e];
         }
     }
     __syncthreads();
     if (valid) {
         float *o = dq + (qrow + t) * OAL_D + w * 16;
-        const float *src = dql + i * 65 + w * 16;
+        const float *src = red + i * 65 + w * 16;
 #pragma unroll
-        for (int e = 0; e < 16; e += 4)
-            *reinterpret_cast<float4 *>(o + e) = make_float4(src[e], src[e + 1], src[e + 2], src[e + 3]);
+        for (int e = 0; e < 16; e += 4) {
+            float4 x = *reinterpret_cast<float4 *>(o + e);
+            x.x += src[e]; x.y += src[e + 1]; x.z += src[e + 2]; x.w += src[e + 3];
+            *reinterpret_cast<float4 *>(o + e) = x;
+        }
     }
 }
 
-// 7a. dv_j = (R_c^T psi(k_j))[0:64] + sum_h sum_{i >= j in the chunk} kappa_ij g_i[0:64].
-//     Workgroup = (64-key tile, KV head, sequence); lane = key; waves split the feature rows
-//     and, inside the chunk, the queries i = w (mod 4).
-template <typename T>
-__global__ __launch_bounds__(kThreads) void oal_bwd_dv(int T_len, int C, int nch, int n_q_heads, int n_kv_heads,
-                                                        const T *__restrict__ q, const T *__restrict__ k,
-                                                        const unsigned char *__restrict__ params,
-                                                        const float *__restrict__ st, const float *__restrict__ gv,
-                                                        const float *__restrict__ gd, float *__restrict__ dv) {
-    __shared__ float xk[64 * 65];
-    __shared__ float qs[64 * 64];
-    __shared__ __align__(16) float gs[64 * 68];
-    const int tpc = C / 64, c = blockIdx.x / tpc, kt = blockIdx.x % tpc;
-    const int kv = blockIdx.y, b = blockIdx.z, n_rep = n_q_heads / n_kv_heads;
-    const int j = threadIdx.x & 63, w = wave_id();
-    const int t0 = c * C + kt * 64, t = t0 + j;
-    const bool valid = t < T_len;
-    const size_t krow = ((size_t)b * n_kv_heads + kv) * T_len;
-    stage_rows(xk, 65, k, krow, t0, T_len, 1.0f);
-    __syncthreads();
-    const float *xj = xk + j * 65;
+// 7. dk and dv. Each 64-key tile is covered by:
+//    - kInterSplits workgroups of oal_bwd_dk_inter and of oal_bwd_dv_inter: the 32 waves of the
+//      splits (worker 4 p + w) take the feature-row pairs {worker, 63 - worker} (65 features
+//      each) of the state part: dv_j += psi_f(k_j) R_c[f][0:64], dk_j += (R_c[f] . [v_j; 1])
+//      dpsi_f/dk_j;
+//    - one workgroup of oal_bwd_dkv_intra per query head h of the KV head: the pairs inside the
+//      chunk, i >= j, with the waves on the queries i = w (mod 4): dv_j += kappa_ij g_i[0:64],
+//      dk_j += dkappa_ij dkappa_ij/dk_j.
+//    Each writes a partial row of 128 floats (dk, then dv) per key into part[slot]: slots
+//    0 .. kInterSplits-1 the state parts (dk_inter the first half, dv_inter the second),
+//    then one slot per query head. oal_bwd_kv_reduce adds the slots in order.
+constexpr int kInterSplits = 8;
 
-    float acc[64];
-#pragma unroll
-    for (int e = 0; e < 64; ++e) acc[e] = 0.0f;
-    if (c < nch - 1) {                             // R of the last chunk is 0
-        const float *Rg = st + ((size_t)((size_t)b * n_kv_heads + kv) * nch + c) * OAL_STATE_STRIDE;
-        const cfloat *R = uni(Rg), *Rd = uni(Rg + (size_t)OAL_NFEAT * OAL_D);
-        if (w == 0) row_axpy<64>(acc, 1.0f, R, Rd, 0);
-        for (int r = w; r < OAL_D; r += 4) {
-            const float kr = xj[r];
-            row_axpy<64>(acc, kr, R, Rd, 1 + r);
-            const int base = quad_base(r);
-            for (int tt = r; tt < OAL_D; ++tt) row_axpy<64>(acc, kr * xj[tt], R, Rd, base + tt);
-        }
-    }
-    for (int hs = 0; hs < n_rep; ++hs) {
-        const int h = kv * n_rep + hs;
-        const OalHeadDev *hd = bwd_head(params, h);
-        const int G = hd->G;
-        const size_t qrow = ((size_t)b * n_q_heads + h) * T_len;
-        for (int qt = kt; qt < tpc; ++qt) {
-            const int q0 = c * C + qt * 64;
-            if (q0 >= T_len) break;
-            __syncthreads();
-            stage_rows(qs, 64, q, qrow, q0, T_len, 0.0f);
-            stage_g(gs, gv, gd, qrow, q0, T_len);
-            __syncthreads();
-            if (valid) {
-                for (int ii = w; ii < 64; ii += 4) {
-                    if (!sees(kt, qt, j, ii)) continue;   // key j of tile kt, query ii of tile qt
-                    const float kap = pair_kappa(hd, G, xj, qs + ii * 64);
-                    const float4 *gr = reinterpret_cast<const float4 *>(gs + ii * 68);
-#pragma unroll
-                    for (int u = 0; u < 16; ++u) {
-                        const float4 gg = gr[u];
-                        acc[4 * u] += kap * gg.x;
-                        acc[4 * u + 1] += kap * gg.y;
-                        acc[4 * u + 2] += kap * gg.z;
-                        acc[4 * u + 3] += kap * gg.w;
-                    }
-                }
-            }
-        }
-    }
-    float *red = gs;
-    for (int s = 1; s < 4; ++s) {
-        __syncthreads();
-        if (w == s) {
-#pragma unroll
-            for (int e = 0; e < 64; ++e) red[j * 65 + e] = acc[e];
-        }
-        __syncthreads();
-        if (w == 0) {
-#pragma unroll
-            for (int e = 0; e < 64; ++e) acc[e] += red[j * 65 + e];
-        }
-    }
-    if (w == 0 && valid) {
-        float *o = dv + (krow + t) * OAL_D;
-#pragma unroll
-        for (int e = 0; e < 64; e += 4)
-            *reinterpret_cast<float4 *>(o + e) = make_float4(acc[e], acc[e + 1], acc[e + 2], acc[e + 3]);
-    }
+__device__ inline float *part_row(float *part, int slot, size_t rows, size_t row) {
+    return part + ((size_t)slot * rows + row) * 128;
 }
 
-// 7b. dk_j = Jpsi(k_j)^T (R_c [v_j; 1]) + sum_h sum_{i >= j in the chunk} dkappa_ij dkappa/dk_j.
-//     Same decomposition as oal_bwd_dq with the roles of q and k (and S and R) exchanged;
-//     psi has no coefficients.
 template <typename T>
-__global__ __launch_bounds__(kThreads) void oal_bwd_dk(int T_len, int C, int nch, int n_q_heads, int n_kv_heads,
-                                                        const T *__restrict__ q, const T *__restrict__ k,
-                                                        const T *__restrict__ v, const unsigned char *__restrict__ params,
-                                                        const float *__restrict__ st, const float *__restrict__ gv,
-                                                        const float *__restrict__ gd, float *__restrict__ dk) {
+__global__ __launch_bounds__(kThreads) void oal_bwd_dk_inter(int T_len, int C, int nch, int n_kv_heads,
+                                                              const T *__restrict__ k, const T *__restrict__ v,
+                                                              const float *__restrict__ st, float *__restrict__ part) {
     __shared__ float xk[64 * 65];
     __shared__ float dkl[64 * 65];
-    __shared__ float qs[64 * 64];
-    __shared__ __align__(16) float gs[64 * 68];
     const int tpc = C / 64, c = blockIdx.x / tpc, kt = blockIdx.x % tpc;
-    const int kv = blockIdx.y, b = blockIdx.z, n_rep = n_q_heads / n_kv_heads;
-    const int j = threadIdx.x & 63, w = wave_id();
+    const int p = blockIdx.y % kInterSplits, kv = blockIdx.y / kInterSplits, b = blockIdx.z;
+    const int j = threadIdx.x & 63, w = wave_id(), worker = p * 4 + w;
     const int t0 = c * C + kt * 64, t = t0 + j;
     const bool valid = t < T_len;
-    const size_t krow = ((size_t)b * n_kv_heads + kv) * T_len;
+    const size_t krow = ((size_t)b * n_kv_heads + kv) * T_len, rows = (size_t)gridDim.z * n_kv_heads * T_len;
     stage_rows(xk, 65, k, krow, t0, T_len, 1.0f);
     for (int e = threadIdx.x; e < 64 * 65; e += kThreads) dkl[e] = 0.0f;
     float vj[65];
@@ -552,54 +558,31 @@ __global__ __launch_bounds__(kThreads) void oal_bwd_dk(int T_len, int C, int nch
     vj[64] = 1.0f;
     __syncthreads();
     const float *xj = xk + j * 65;
-
     float d[64];
 #pragma unroll
     for (int e = 0; e < 64; ++e) d[e] = 0.0f;
-    if (c < nch - 1) {
+    if (c < nch - 1) {                             // R of the last chunk is 0
         const float *Rg = st + ((size_t)((size_t)b * n_kv_heads + kv) * nch + c) * OAL_STATE_STRIDE;
         const cfloat *R = uni(Rg), *Rd = uni(Rg + (size_t)OAL_NFEAT * OAL_D);
-        for (int r = w; r < OAL_D; r += 4) {
+        for (int half = 0; half < 2; ++half) {
+            const int r = half ? 63 - worker : worker;
             const float kr = xj[r];
-            float dr = row_dot(R, Rd, 1 + r, vj);
             const int base = quad_base(r);
+            float dr = row_dot(R, Rd, 1 + r, vj);  // linear feature: d psi / d k_r = 1
+            // blocks of 8 columns t, the columns t < r of r's block masked (as in dq)
 #pragma unroll
-            for (int tt = 0; tt < OAL_D; ++tt) {
-                if (tt >= r) {
-                    const float y = row_dot(R, Rd, base + tt, vj);
-                    d[tt] += y * kr;
-                    dr += y * xj[tt];
-                }
-            }
-            dkl[j * 65 + r] += dr;
-        }
-    }
-    for (int hs = 0; hs < n_rep; ++hs) {
-        const int h = kv * n_rep + hs;
-        const OalHeadDev *hd = bwd_head(params, h);
-        const int G = hd->G;
-        const size_t qrow = ((size_t)b * n_q_heads + h) * T_len;
-        for (int qt = kt; qt < tpc; ++qt) {
-            const int q0 = c * C + qt * 64;
-            if (q0 >= T_len) break;
-            __syncthreads();
-            stage_rows(qs, 64, q, qrow, q0, T_len, 0.0f);
-            stage_g(gs, gv, gd, qrow, q0, T_len);
-            __syncthreads();
-            if (valid) {
-                for (int ii = w; ii < 64; ii += 4) {
-                    if (!sees(kt, qt, j, ii)) continue;
-                    const float4 *gr = reinterpret_cast<const float4 *>(gs + ii * 68);
-                    float e0 = gs[ii * 68 + 64], e1 = 0.0f;
+            for (int tb = 0; tb < 8; ++tb) {
+                if (tb >= (r >> 3)) {
 #pragma unroll
-                    for (int u = 0; u < 16; ++u) {
-                        const float4 gg = gr[u];
-                        e0 += gg.x * vj[4 * u] + gg.z * vj[4 * u + 2];
-                        e1 += gg.y * vj[4 * u + 1] + gg.w * vj[4 * u + 3];
+                    for (int e = 0; e < 8; ++e) {
+                        const int tt = tb * 8 + e;
+                        const float y = (tt >= r ? 1.0f : 0.0f) * row_dot(R, Rd, base + tt, vj);
+                        d[tt] += y * kr;
+                        dr += y * xj[tt];
                     }
-                    pair_grad(hd, G, e0 + e1, xj, qs + ii * 64, d);
                 }
             }
+            dkl[j * 65 + r] += dr;                 // row r belongs to this wave alone
         }
     }
     for (int s = 0; s < 4; ++s) {
@@ -611,12 +594,153 @@ __global__ __launch_bounds__(kThreads) void oal_bwd_dk(int T_len, int C, int nch
     }
     __syncthreads();
     if (valid) {
-        float *o = dk + (krow + t) * OAL_D + w * 16;
+        float *o = part_row(part, p, rows, krow + t) + w * 16;
         const float *src = dkl + j * 65 + w * 16;
 #pragma unroll
         for (int e = 0; e < 16; e += 4)
             *reinterpret_cast<float4 *>(o + e) = make_float4(src[e], src[e + 1], src[e + 2], src[e + 3]);
     }
+}
+
+template <typename T>
+__global__ __launch_bounds__(kThreads) void oal_bwd_dv_inter(int T_len, int C, int nch, int n_kv_heads,
+                                                              const T *__restrict__ k, const float *__restrict__ st,
+                                                              float *__restrict__ part) {
+    __shared__ float xk[64 * 65];
+    __shared__ float red[64 * 65];
+    const int tpc = C / 64, c = blockIdx.x / tpc, kt = blockIdx.x % tpc;
+    const int p = blockIdx.y % kInterSplits, kv = blockIdx.y / kInterSplits, b = blockIdx.z;
+    const int j = threadIdx.x & 63, w = wave_id(), worker = p * 4 + w;
+    const int t0 = c * C + kt * 64, t = t0 + j;
+    const bool valid = t < T_len;
+    const size_t krow = ((size_t)b * n_kv_heads + kv) * T_len, rows = (size_t)gridDim.z * n_kv_heads * T_len;
+    stage_rows(xk, 65, k, krow, t0, T_len, 1.0f);
+    __syncthreads();
+    const float *xj = xk + j * 65;
+    float a[64];
+#pragma unroll
+    for (int e = 0; e < 64; ++e) a[e] = 0.0f;
+    if (c < nch - 1) {
+        const float *Rg = st + ((size_t)((size_t)b * n_kv_heads + kv) * nch + c) * OAL_STATE_STRIDE;
+        const cfloat *R = uni(Rg), *Rd = uni(Rg + (size_t)OAL_NFEAT * OAL_D);
+        if (worker == 0) row_axpy<64>(a, 1.0f, R, Rd, 0);      // constant feature
+        for (int half = 0; half < 2; ++half) {
+            const int r = half ? 63 - worker : worker;
+            const float kr = xj[r];
+            const int base = quad_base(r);
+            row_axpy<64>(a, kr, R, Rd, 1 + r);
+#pragma unroll 4
+            for (int tt = r; tt < OAL_D; ++tt) row_axpy<64>(a, kr * xj[tt], R, Rd, base + tt);
+        }
+    }
+    for (int s = 0; s < 4; ++s) {
+        __syncthreads();
+        if (w == s) {
+#pragma unroll
+            for (int e = 0; e < 64; ++e) red[j * 65 + e] = (s == 0 ? 0.0f : red[j * 65 + e]) + a[e];
+        }
+    }
+    __syncthreads();
+    if (valid) {
+        float *o = part_row(part, p, rows, krow + t) + 64 + w * 16;
+        const float *src = red + j * 65 + w * 16;
+#pragma unroll
+        for (int e = 0; e < 16; e += 4)
+            *reinterpret_cast<float4 *>(o + e) = make_float4(src[e], src[e + 1], src[e + 2], src[e + 3]);
+    }
+}
+
+template <typename T>
+__global__ __launch_bounds__(kThreads) void oal_bwd_dkv_intra(int T_len, int C, int n_q_heads, int n_kv_heads,
+                                                               const T *__restrict__ q, const T *__restrict__ k,
+                                                               const T *__restrict__ v,
+                                                               const unsigned char *__restrict__ params,
+                                                               const float *__restrict__ gv, const float *__restrict__ gd,
+                                                               float *__restrict__ part) {
+    __shared__ float xk[64 * 65];
+    __shared__ float xv[64 * 65];
+    __shared__ float qs[64 * 64];
+    __shared__ __align__(16) float gs[64 * 68];
+    const int tpc = C / 64, c = blockIdx.x / tpc, kt = blockIdx.x % tpc;
+    const int n_rep = n_q_heads / n_kv_heads;
+    const int hs = blockIdx.y % n_rep, kv = blockIdx.y / n_rep, b = blockIdx.z, h = kv * n_rep + hs;
+    const int j = threadIdx.x & 63, w = wave_id();
+    const int t0 = c * C + kt * 64, t = t0 + j;
+    const bool valid = t < T_len;
+    const size_t krow = ((size_t)b * n_kv_heads + kv) * T_len, rows = (size_t)gridDim.z * n_kv_heads * T_len;
+    const size_t qrow = ((size_t)b * n_q_heads + h) * T_len;
+    const OalHeadDev *hd = bwd_head(params, h);
+    const int G = hd->G;
+    stage_rows(xk, 65, k, krow, t0, T_len, 1.0f);
+    stage_rows(xv, 65, v, krow, t0, T_len, 1.0f);
+    const float *xj = xk + j * 65, *vjl = xv + j * 65;
+    float d[64], a[64];
+#pragma unroll
+    for (int e = 0; e < 64; ++e) d[e] = a[e] = 0.0f;
+    for (int qt = kt; qt < tpc; ++qt) {
+        const int q0 = c * C + qt * 64;
+        if (q0 >= T_len) break;
+        __syncthreads();
+        stage_rows(qs, 64, q, qrow, q0, T_len, 0.0f);
+        stage_g(gs, gv, gd, qrow, q0, T_len);
+        __syncthreads();
+        if (valid) {
+            for (int ii = w; ii < 64; ii += 4) {
+                if (!sees(kt, qt, j, ii)) continue;   // key j of tile kt, query ii of tile qt
+                const float *gr = gs + ii * 68;
+                float e0 = gr[64], e1 = 0.0f;
+#pragma unroll
+                for (int u = 0; u < 64; u += 2) {
+                    e0 += gr[u] * vjl[u];
+                    e1 += gr[u + 1] * vjl[u + 1];
+                }
+                const float kap = pair_kappa_grad(hd, G, e0 + e1, xj, qs + ii * 64, d);
+                const float4 *g4 = reinterpret_cast<const float4 *>(gr);
+#pragma unroll
+                for (int u = 0; u < 16; ++u) {
+                    const float4 gg = g4[u];
+                    a[4 * u] += kap * gg.x;
+                    a[4 * u + 1] += kap * gg.y;
+                    a[4 * u + 2] += kap * gg.z;
+                    a[4 * u + 3] += kap * gg.w;
+                }
+            }
+        }
+    }
+    float *dkr = xv, *dvr = gs;                     // reuse: the v and g tiles are consumed
+    for (int s = 0; s < 4; ++s) {
+        __syncthreads();
+        if (w == s) {
+#pragma unroll
+            for (int e = 0; e < 64; ++e) {
+                dkr[j * 65 + e] = (s == 0 ? 0.0f : dkr[j * 65 + e]) + d[e];
+                dvr[j * 65 + e] = (s == 0 ? 0.0f : dvr[j * 65 + e]) + a[e];
+            }
+        }
+    }
+    __syncthreads();
+    if (valid) {
+        float *o = part_row(part, kInterSplits + hs, rows, krow + t) + w * 32;
+        const float *src = (w < 2 ? dkr : dvr) + j * 65 + (w & 1) * 32;
+#pragma unroll
+        for (int e = 0; e < 32; e += 4)
+            *reinterpret_cast<float4 *>(o + e) = make_float4(src[e], src[e + 1], src[e + 2], src[e + 3]);
+    }
+}
+
+// Sum the nslots partial rows in slot order: dk, dv [rows][64] from part [slot][rows][128].
+__global__ __launch_bounds__(kThreads) void oal_bwd_kv_reduce(size_t rows, int nslots, const float *__restrict__ part,
+                                                              float *__restrict__ dk, float *__restrict__ dv) {
+    const size_t e = (size_t)blockIdx.x * kThreads + threadIdx.x;   // one float4 of a row
+    if (e >= rows * 32) return;
+    const size_t row = e / 32, col = (e % 32) * 4;
+    float4 s = *reinterpret_cast<const float4 *>(part + row * 128 + col);
+    for (int p = 1; p < nslots; ++p) {
+        const float4 x = *reinterpret_cast<const float4 *>(part + ((size_t)p * rows + row) * 128 + col);
+        s.x += x.x; s.y += x.y; s.z += x.z; s.w += x.w;
+    }
+    float *o = col < 64 ? dk + row * 64 + col : dv + row * 64 + (col - 64);
+    *reinterpret_cast<float4 *>(o) = s;
 }
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -632,21 +756,28 @@ hipError_t launch_backward(const oal_dims &d, int T_len, int C, const void *q_, 
     float *gv = reinterpret_cast<float *>(static_cast<unsigned char *>(ws) +
                                           align256((size_t)B * Hkv * nch * OAL_STATE_STRIDE * 4));
     float *gd = reinterpret_cast<float *>(reinterpret_cast<unsigned char *>(gv) + align256((size_t)B * Hq * T_len * 64 * 4));
+    float *part = reinterpret_cast<float *>(reinterpret_cast<unsigned char *>(gd) + align256((size_t)B * Hq * T_len * 4));
+    const size_t kvrows = (size_t)B * Hkv * T_len;
     const dim3 blk(kThreads);
     const dim3 g_inc((OAL_NFEAT + kFeatBlock - 1) / kFeatBlock, nch, B * Hkv);
     const dim3 g_scan((OAL_NFEAT * OAL_V1 + kThreads - 1) / kThreads, B * Hkv);
-    const dim3 g_q(nch * tpc, Hq, B), g_k(nch * tpc, Hkv, B);
+    const dim3 g_q(nch * tpc, Hq, B), g_ki(nch * tpc, Hkv * kInterSplits, B), g_kh(nch * tpc, Hq, B);
+    const dim3 g_red((unsigned)((kvrows * 32 + kThreads - 1) / kThreads));
+    const int nslots = kInterSplits + Hq / Hkv;
     hipLaunchKernelGGL((oal_bwd_increments<T, false>), g_inc, blk, 0, stream, T_len, C, nch, Hq, Hkv, k, v,
                        (const float *)nullptr, (const float *)nullptr, params, st);
     hipLaunchKernelGGL(oal_bwd_scan, g_scan, blk, 0, stream, nch, 0, st);
     hipLaunchKernelGGL(oal_bwd_readout_g<T>, g_q, blk, 0, stream, T_len, C, nch, Hq, Hkv, q, k, v, dy, params, st,
                        gv, gd);
-    hipLaunchKernelGGL(oal_bwd_dq<T>, g_q, blk, 0, stream, T_len, C, nch, Hq, Hkv, q, k, v, params, st, gv, gd, dq);
+    hipLaunchKernelGGL(oal_bwd_dq_inter<T>, g_q, blk, 0, stream, T_len, C, nch, Hq, Hkv, q, params, st, gv, gd, dq);
+    hipLaunchKernelGGL(oal_bwd_dq_intra<T>, g_q, blk, 0, stream, T_len, C, Hq, Hkv, q, k, v, params, gv, gd, dq);
+    hipLaunchKernelGGL(oal_bwd_dkv_intra<T>, g_kh, blk, 0, stream, T_len, C, Hq, Hkv, q, k, v, params, gv, gd, part);
     hipLaunchKernelGGL((oal_bwd_increments<T, true>), g_inc, blk, 0, stream, T_len, C, nch, Hq, Hkv, q,
                        (const T *)nullptr, gv, gd, params, st);
     hipLaunchKernelGGL(oal_bwd_scan, g_scan, blk, 0, stream, nch, 1, st);
-    hipLaunchKernelGGL(oal_bwd_dv<T>, g_k, blk, 0, stream, T_len, C, nch, Hq, Hkv, q, k, params, st, gv, gd, dv);
-    hipLaunchKernelGGL(oal_bwd_dk<T>, g_k, blk, 0, stream, T_len, C, nch, Hq, Hkv, q, k, v, params, st, gv, gd, dk);
+    hipLaunchKernelGGL(oal_bwd_dk_inter<T>, g_ki, blk, 0, stream, T_len, C, nch, Hkv, k, v, st, part);
+    hipLaunchKernelGGL(oal_bwd_dv_inter<T>, g_ki, blk, 0, stream, T_len, C, nch, Hkv, k, st, part);
+    hipLaunchKernelGGL(oal_bwd_kv_reduce, g_red, blk, 0, stream, kvrows, nslots, part, dk, dv);
     return hipGetLastError();
 }
 
@@ -655,7 +786,8 @@ hipError_t launch_backward(const oal_dims &d, int T_len, int C, const void *q_, 
 size_t oal_backward_ws_bytes_impl(const oal_dims &d, int T_len, int C) {
     const size_t nch = (size_t)(T_len + C - 1) / C;
     return align256((size_t)d.batch * d.n_kv_heads * nch * OAL_STATE_STRIDE * 4) +
-           align256((size_t)d.batch * d.n_q_heads * T_len * 64 * 4) + align256((size_t)d.batch * d.n_q_heads * T_len * 4);
+           align256((size_t)d.batch * d.n_q_heads * T_len * 64 * 4) + align256((size_t)d.batch * d.n_q_heads * T_len * 4) +
+           align256((size_t)(kInterSplits + d.n_q_heads / d.n_kv_heads) * d.batch * d.n_kv_heads * T_len * 128 * 4);
 }
 
 hipError_t oal_launch_backward(const oal_dims &d, int T_len, int C, const void *q, const void *k, const void *v,
