@@ -296,14 +296,16 @@ def main():
         bdq = torch.empty((Bb, Hqb, Tb, D), dtype=torch.float32, device=dev)
         bdk = torch.empty((Bb, Hkvb, Tb, D), dtype=torch.float32, device=dev)
         bdv = torch.empty_like(bdk)
+        bdL = torch.empty((Hqb, 65, 65), dtype=torch.float32, device=dev)
+        bde = torch.empty((Hqb,), dtype=torch.float32, device=dev)
         for _ in range(2):
-            gpq.oal_prefill_backward(bd, Tb, Cb, bq, bk, bv, bdy, bparams, bws, bdq, bdk, bdv)
+            gpq.oal_prefill_backward(bd, Tb, Cb, bq, bk, bv, bdy, bparams, bws, bdq, bdk, bdv, bdL, bde)
         torch.cuda.synchronize()
         reps = 5
         e0, e1 = gpq.TimingEvent(), gpq.TimingEvent()
         e0.record(stream)
         for _ in range(reps):
-            gpq.oal_prefill_backward(bd, Tb, Cb, bq, bk, bv, bdy, bparams, bws, bdq, bdk, bdv)
+            gpq.oal_prefill_backward(bd, Tb, Cb, bq, bk, bv, bdy, bparams, bws, bdq, bdk, bdv, bdL, bde)
         e1.record(stream)
         bms = e0.elapsed_time(e1) / reps
         # algorithmic fp32 work: six state-sized contractions of 2 * 2145 * 65 flops per token --
@@ -312,14 +314,14 @@ def main():
         bflops = (3 * Bb * Hqb + 3 * Bb * Hkvb) * Tb * 2 * 2145 * 65
         bach = bflops / (bms * 1e-3) / 1e12
         out["backward"] = {
-            "workload": f"prefill backward (dq, dk, dv) from an empty prefix, B={Bb} T={Tb} "
+            "workload": f"prefill backward (dq, dk, dv, dL, deps) from an empty prefix, B={Bb} T={Tb} "
                         f"{Hqb}q/{Hkvb}kv, bf16 inputs, fp32 arithmetic, chunk {Cb}",
             "value": Bb * Tb / (bms * 1e-3), "unit": "tokens/s", "ms_per_call": bms, "calls": reps,
-            "roofline": {"bound": "alu", "kernel": "the call's eight fp32 launches together",
+            "roofline": {"bound": "alu", "kernel": "the call's fp32 launches together",
                          "achieved": bach, "peak": PEAK_FP32_TFLOPS, "unit": "TFLOP/s",
                          "frac": bach / PEAK_FP32_TFLOPS, "traffic": None,
                          "algorithmic_flops_per_call": bflops}}
-        del bq, bk, bv, bdy, bws, bdq, bdk, bdv, bparams
+        del bq, bk, bv, bdy, bws, bdq, bdk, bdv, bdL, bde, bparams
         torch.cuda.empty_cache()
 
     # ---------------- decode ----------------

@@ -88,7 +88,7 @@ def _load():
     lib.oal_contribution.argtypes, lib.oal_contribution.restype = [dp, I, P, P, P, P, P, P], ctypes.c_int
     lib.oal_prefill_backward_workspace_bytes.argtypes = [dp, I, I]
     lib.oal_prefill_backward_workspace_bytes.restype = S
-    lib.oal_prefill_backward.argtypes = [dp, I, I, P, P, P, P, P, P, P, P, P, P]
+    lib.oal_prefill_backward.argtypes = [dp, I, I, P, P, P, P, P, P, P, P, P, P, P, P]
     lib.oal_prefill_backward.restype = ctypes.c_int
     return lib
 
@@ -266,13 +266,15 @@ def oal_prefill_backward_workspace_bytes(dims: oal_dims, T: int, chunk: int) -> 
 
 
 def oal_prefill_backward(dims: oal_dims, T: int, chunk: int, q, k, v, dy, params_dev, workspace,
-                         dq, dk, dv, stream=None):
+                         dq, dk, dv, dL=None, deps=None, stream=None):
     """Gradients dq [batch, n_q_heads, T, 64], dk, dv [batch, n_kv_heads, T, 64] (fp32 device
     tensors written by the library) of sum(dy * y) for the prefill of T tokens from an empty
-    prefix."""
+    prefix; with dL [n_q_heads, 65, 65] and deps [n_q_heads] (fp32 device tensors, or both
+    None) also the coefficient gradients."""
     _check("oal_prefill_backward", _lib.oal_prefill_backward(
         ctypes.byref(dims), int(T), int(chunk), _ptr(q), _ptr(k), _ptr(v), _ptr(dy),
-        _ptr(params_dev), _ptr(workspace), _ptr(dq), _ptr(dk), _ptr(dv), _stream(stream)))
+        _ptr(params_dev), _ptr(workspace), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dL), _ptr(deps),
+        _stream(stream)))
 
 
 def oal_decode_step_indexed(dims: oal_dims, slots, pool_size: int, q, k, v, params_dev, state_pool,

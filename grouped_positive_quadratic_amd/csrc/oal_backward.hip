@@ -33,6 +33,8 @@
 //   7. oal_bwd_scan (reverse):      exclusive suffix over chunks: R_c
 //   8. oal_bwd_dk_inter, _dv_inter: dk, dv partials of the state part
 //   9. oal_bwd_kv_reduce:           dk, dv (the partials added in a fixed order)
+// With coefficient gradients, also oal_bwd_dw_intra (before 6), the per-head partials of 6,
+// and oal_bwd_coef (after 6): dL, deps.
 #include <hip/hip_runtime.h>
 
 #include "oal_device.h"
@@ -195,7 +197,8 @@ __device__ inline void stage_g(float *dst, const float *gv, const float *gd, siz
 // 1 / 5. Per-chunk increments of one (sequence, KV head): out_c[f][col] = sum_n a_n(f) b_n[col]
 //   keys:    a_n = psi_f(k_n),                 b_n = [v_n; 1]   (n over the chunk's keys)
 //   queries: a_n = wdec_h[f] mono_f(q_n),      b_n = g_n        (n over the chunk's queries of
-//                                                                every head h of the KV head)
+//                                                                every head h of the KV head);
+//            with dwp, also the state part of each head's coefficient gradient (see below)
 // Workgroup = (64 features, chunk, sequence x KV head); thread = (feature, quarter of the 64
 // value columns); the feature's dims are fixed per thread, rows are staged 64 at a time.
 template <typename T, bool QSIDE>
@@ -204,7 +207,7 @@ __global__ __launch_bounds__(kThreads) void oal_bwd_increments(int T_len, int C,
                                                                 const T *__restrict__ v, const float *__restrict__ gv,
                                                                 const float *__restrict__ gd,
                                                                 const unsigned char *__restrict__ params,
-                                                                float *__restrict__ st) {
+                                                                float *__restrict__ st, float *__restrict__ dwp) {
     __shared__ float xs[64 * 65];
     __shared__ __align__(16) float bs[64 * 68];
     const int tid = threadIdx.x, fl = tid >> 2, cq = tid & 3;
@@ -223,12 +226,31 @@ __global__ __launch_bounds__(kThreads) void oal_bwd_increments(int T_len, int C,
     float acc[16], acc64 = 0.0f;
 #pragma unroll
     for (int e = 0; e < 16; ++e) acc[e] = 0.0f;
+    float *out = st + ((size_t)bkv * nch + c) * OAL_STATE_STRIDE;
+    // queries with dwp: the state S_c this kernel overwrites, for the coefficient gradient
+    // dw_h[f] = sum_{i in chunk} mono_f(q_i) (S_c g_i)[f] = S_c[f] . (sum_i mono_f(q_i) g_i)
+    const bool coef = QSIDE && dwp != nullptr;
+    float sv[16], s64 = 0.0f;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) sv[e] = 0.0f;
+    if (coef && f < OAL_NFEAT) {
+        const float4 *sp = reinterpret_cast<const float4 *>(out + (size_t)f * OAL_D + cq * 16);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const float4 x4 = sp[u];
+            sv[4 * u] = x4.x; sv[4 * u + 1] = x4.y; sv[4 * u + 2] = x4.z; sv[4 * u + 3] = x4.w;
+        }
+        if (cq == 0) s64 = out[(size_t)OAL_NFEAT * OAL_D + f];
+    }
     const int nsrc = QSIDE ? n_rep : 1;
     const int tend = min(c * C + C, T_len);
     for (int hs = 0; hs < nsrc; ++hs) {
         const int h = kv * n_rep + hs;
         const float w = QSIDE ? (f < OAL_NFEAT ? bwd_head(params, h)->wdec[f] : 0.0f) : 1.0f;
         const size_t row0 = QSIDE ? ((size_t)b * n_q_heads + h) * T_len : ((size_t)b * n_kv_heads + kv) * T_len;
+        float ah[16], ah64 = 0.0f;                 // this head's sum of mono_f(x_n) b_n
+#pragma unroll
+        for (int e = 0; e < 16; ++e) ah[e] = 0.0f;
         for (int t0 = c * C; t0 < tend; t0 += 64) {
             __syncthreads();                       // the previous tile is consumed
             stage_rows(xs, 65, x, row0, t0, T_len, 1.0f);
@@ -240,22 +262,33 @@ __global__ __launch_bounds__(kThreads) void oal_bwd_increments(int T_len, int C,
             }
             __syncthreads();
             for (int n = 0; n < 64; ++n) {
-                const float a = w * xs[n * 65 + ia] * xs[n * 65 + ib];
+                const float a = xs[n * 65 + ia] * xs[n * 65 + ib];
                 const float4 *br = reinterpret_cast<const float4 *>(bs + n * 68 + cq * 16);
 #pragma unroll
                 for (int u = 0; u < 4; ++u) {
                     const float4 bb = br[u];
-                    acc[4 * u] += a * bb.x;
-                    acc[4 * u + 1] += a * bb.y;
-                    acc[4 * u + 2] += a * bb.z;
-                    acc[4 * u + 3] += a * bb.w;
+                    ah[4 * u] += a * bb.x;
+                    ah[4 * u + 1] += a * bb.y;
+                    ah[4 * u + 2] += a * bb.z;
+                    ah[4 * u + 3] += a * bb.w;
                 }
-                acc64 += a * bs[n * 68 + 64];
+                ah64 += a * bs[n * 68 + 64];
             }
+        }
+#pragma unroll
+        for (int e = 0; e < 16; ++e) acc[e] += w * ah[e];
+        acc64 += w * ah64;
+        if (coef) {
+            float pdw = cq == 0 ? s64 * ah64 : 0.0f;
+#pragma unroll
+            for (int e = 0; e < 16; ++e) pdw += sv[e] * ah[e];
+            pdw += __shfl_xor(pdw, 1);             // the four column quarters of feature f
+            pdw += __shfl_xor(pdw, 2);
+            if (cq == 0 && f < OAL_NFEAT)
+                dwp[(((size_t)b * n_q_heads + h) * nch + c) * OAL_NFEAT + f] = pdw;
         }
     }
     if (f < OAL_NFEAT) {
-        float *out = st + ((size_t)bkv * nch + c) * OAL_STATE_STRIDE;
         float4 *o = reinterpret_cast<float4 *>(out + (size_t)f * OAL_D + cq * 16);
 #pragma unroll
         for (int u = 0; u < 4; ++u) o[u] = make_float4(acc[4 * u], acc[4 * u + 1], acc[4 * u + 2], acc[4 * u + 3]);
@@ -743,12 +776,197 @@ __global__ __launch_bounds__(kThreads) void oal_bwd_kv_reduce(size_t rows, int n
     *reinterpret_cast<float4 *>(o) = s;
 }
 
+// 10. Coefficient gradients. kappa_ij = sum_f wdec_h[f] mono_f(q_i) mono_f(k_j), so the
+//     gradient of the coefficient of feature f is dw_h[f] = sum_{j <= i} dkappa_ij mono_f(q_i)
+//     mono_f(k_j): its pairs across chunks come from the query increments above (S_c against
+//     the head's sum of mono_f(q_i) g_i), the pairs inside a chunk from oal_bwd_dw_intra. With
+//     kappa = eps + sbar^T M sbar (M = L L^T), dLoss/dM[g][g'] = sum dkappa sbar_g sbar_g' is a
+//     sum of dw over the features whose dims lie in groups g and g' (oal_bwd_coef), then
+//     dL = 2 (dLoss/dM) L and deps = dLoss/dM[0][0].
+//
+// Pairs inside chunk c for head h: workgroup = (chunk, head, sequence); thread = features
+// f = tid + 256 u. Per (query tile, key tile) pair: the tile of dkappa (masked to j <= i)
+// in LDS, then per feature dw += sum_i mono_f(q_i) sum_j dkappa_ij psi_f(k_j).
+template <typename T>
+__global__ __launch_bounds__(kThreads) void oal_bwd_dw_intra(int T_len, int C, int nch, int n_q_heads,
+                                                              int n_kv_heads, const T *__restrict__ q,
+                                                              const T *__restrict__ k, const T *__restrict__ v,
+                                                              const float *__restrict__ gv, const float *__restrict__ gd,
+                                                              float *__restrict__ dwp) {
+    constexpr int NU = (OAL_NFEAT + kThreads - 1) / kThreads;
+    __shared__ __align__(16) float ta[64 * 68];   // g tile, then the query tile
+    __shared__ float tb[64 * 65];                  // v tile, then the key tile
+    __shared__ __align__(16) float dk[64 * 68];   // dkappa tile
+    const int tpc = C / 64, c = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+    const int n_rep = n_q_heads / n_kv_heads, kv = h / n_rep, tid = threadIdx.x;
+    const size_t qrow = ((size_t)b * n_q_heads + h) * T_len, krow = ((size_t)b * n_kv_heads + kv) * T_len;
+    int fa[NU], fb[NU];                            // dims of the thread's features (64 reads the 1)
+#pragma unroll
+    for (int u = 0; u < NU; ++u) {
+        const int f = tid + kThreads * u;
+        fa[u] = OAL_D;
+        fb[u] = OAL_D;
+        if (f >= 1 && f <= OAL_D) {
+            fa[u] = f - 1;
+        } else if (f > OAL_D && f < OAL_NFEAT) {
+            int idx = f - 1 - OAL_D, r = 0;
+            while (idx >= OAL_D - r) { idx -= OAL_D - r; ++r; }
+            fa[u] = r;
+            fb[u] = r + idx;
+        }
+    }
+    float acc[NU];
+#pragma unroll
+    for (int u = 0; u < NU; ++u) acc[u] = 0.0f;
+    for (int qt = 0; qt < tpc; ++qt) {
+        const int q0 = c * C + qt * 64;
+        if (q0 >= T_len) break;
+        for (int kt = 0; kt <= qt; ++kt) {
+            const int k0 = c * C + kt * 64;
+            __syncthreads();
+            stage_g(ta, gv, gd, qrow, q0, T_len);
+            stage_rows(tb, 65, v, krow, k0, T_len, 1.0f);
+            __syncthreads();
+            for (int e = tid; e < 64 * 64; e += kThreads) {
+                const int i = e >> 6, j = e & 63;
+                float x = 0.0f;
+                if (kt < qt || j <= i) {
+                    const float *gi = ta + i * 68, *vj = tb + j * 65;
+                    float x1 = 0.0f;
+                    for (int cc = 0; cc < 64; cc += 2) {
+                        x += gi[cc] * vj[cc];
+                        x1 += gi[cc + 1] * vj[cc + 1];
+                    }
+                    x += x1 + gi[64];
+                }
+                dk[i * 68 + j] = x;
+            }
+            __syncthreads();
+            stage_rows(ta, 65, q, qrow, q0, T_len, 1.0f);
+            stage_rows(tb, 65, k, krow, k0, T_len, 1.0f);
+            __syncthreads();
+            // two features per pass over the dkappa rows (each row read once per pair)
+#pragma unroll 1
+            for (int u = 0; u < NU; u += 2) {
+                if (tid + kThreads * u >= OAL_NFEAT) break;
+                const int a0 = fa[u], b0 = fb[u];
+                const int a1 = u + 1 < NU ? fa[u + 1] : OAL_D, b1 = u + 1 < NU ? fb[u + 1] : OAL_D;
+                float p0[64], p1[64];
+#pragma unroll
+                for (int j = 0; j < 64; ++j) {
+                    p0[j] = tb[j * 65 + a0] * tb[j * 65 + b0];
+                    p1[j] = tb[j * 65 + a1] * tb[j * 65 + b1];
+                }
+                float s0 = 0.0f, s1 = 0.0f;
+#pragma unroll 2
+                for (int i = 0; i < 64; ++i) {
+                    const float4 *dr = reinterpret_cast<const float4 *>(dk + i * 68);
+                    float y0 = 0.0f, y1 = 0.0f, z0 = 0.0f, z1 = 0.0f;
+#pragma unroll
+                    for (int jj = 0; jj < 16; ++jj) {
+                        const float4 d4 = dr[jj];
+                        y0 += d4.x * p0[4 * jj] + d4.z * p0[4 * jj + 2];
+                        y1 += d4.y * p0[4 * jj + 1] + d4.w * p0[4 * jj + 3];
+                        z0 += d4.x * p1[4 * jj] + d4.z * p1[4 * jj + 2];
+                        z1 += d4.y * p1[4 * jj + 1] + d4.w * p1[4 * jj + 3];
+                    }
+                    const float *qi = ta + i * 65;
+                    s0 += qi[a0] * qi[b0] * (y0 + y1);
+                    s1 += qi[a1] * qi[b1] * (z0 + z1);
+                }
+                acc[u] += s0;
+                if (u + 1 < NU) acc[u + 1] += s1;
+            }
+        }
+    }
+#pragma unroll
+    for (int u = 0; u < NU; ++u) {
+        const int f = tid + kThreads * u;
+        if (f < OAL_NFEAT) dwp[(((size_t)b * n_q_heads + h) * nch + c) * OAL_NFEAT + f] = acc[u];
+    }
+}
+
+// dw_h[f]: the partials summed over sequences and chunks (state part, then the pairs inside
+// chunks, in a fixed order). Thread = (feature, head).
+__global__ __launch_bounds__(kThreads) void oal_bwd_dw_sum(int batch, int nch, int n_q_heads,
+                                                            const float *__restrict__ dwp, float *__restrict__ dwt) {
+    const int f = blockIdx.x * kThreads + threadIdx.x, h = blockIdx.y;
+    if (f >= OAL_NFEAT) return;
+    const size_t half = (size_t)batch * n_q_heads * nch * OAL_NFEAT;
+    float s = 0.0f;
+    for (int part = 0; part < 2; ++part)
+        for (int b = 0; b < batch; ++b) {
+            const float *p = dwp + part * half + ((size_t)b * n_q_heads + h) * nch * OAL_NFEAT + f;
+#pragma unroll 8
+            for (int c = 0; c < nch; ++c) s += p[(size_t)c * OAL_NFEAT];
+        }
+    dwt[(size_t)h * OAL_NFEAT + f] = s;
+}
+
+// Per head: dLoss/dM from dw; dL = 2 (dLoss/dM) L, deps.
+//   dLoss/dM[0][0] = dw[constant]; [0][g] = [g][0] = sum_{r in g} dw[linear r] / 8;
+//   [g][g'] = sum_{r in g, t in g'} dw[quad(min(r,t), max(r,t))] / 64
+// (sbar_0 = 1, sbar_g = sum_{r in group g-1} q_r k_r / 8). First each dim r sums its row of
+// quadratic features by the group of the other dim (rs[r][g']), then each entry adds the rows
+// of its group; both loops are branch-free and in a fixed order.
+__global__ __launch_bounds__(kThreads) void oal_bwd_coef(const unsigned char *__restrict__ params,
+                                                          const float *__restrict__ dwt, float *__restrict__ dL,
+                                                          float *__restrict__ deps) {
+    __shared__ float dw[2176];
+    __shared__ float rs[64 * 65];
+    __shared__ float gm[65 * 65];
+    __shared__ int gid[64];                        // group id + 1 of each dim
+    const int h = blockIdx.x, tid = threadIdx.x;
+    const OalHeadDev *hd = bwd_head(params, h);
+    const int G = hd->G, n = G + 1;
+    if (tid < 64) gid[tid] = hd->gamma[tid] + 1;
+    for (int f = tid; f < OAL_NFEAT; f += kThreads) dw[f] = dwt[(size_t)h * OAL_NFEAT + f];
+    for (int e = tid; e < 64 * 65; e += kThreads) rs[e] = 0.0f;
+    __syncthreads();
+    if (tid < 64) {
+        const int r = tid;
+        for (int t = 0; t < OAL_D; ++t) {
+            const float x = dw[r <= t ? quad_base(r) + t : quad_base(t) + r];
+            rs[r * 65 + gid[t]] += x;              // row r belongs to this thread alone
+        }
+    }
+    __syncthreads();
+    for (int e = tid; e < n * n; e += kThreads) {
+        const int g = e / n, g2 = e % n;
+        float x = 0.0f;
+        if (g == 0 && g2 == 0) {
+            x = dw[0];
+        } else if (g == 0 || g2 == 0) {
+            const int gg = g + g2;
+#pragma unroll 8
+            for (int r = 0; r < OAL_D; ++r) x += gid[r] == gg ? dw[1 + r] : 0.0f;
+            x *= 0.125f;
+        } else {
+#pragma unroll 8
+            for (int r = 0; r < OAL_D; ++r) x += gid[r] == g ? rs[r * 65 + g2] : 0.0f;
+            x *= 1.0f / 64.0f;
+        }
+        gm[g * 65 + g2] = x;
+    }
+    __syncthreads();
+    for (int e = tid; e < 65 * 65; e += kThreads) {
+        const int a = e / 65, m = e % 65;
+        float x = 0.0f;
+        if (a <= G && m <= a) {
+            for (int g2 = m; g2 <= G; ++g2) x += gm[a * 65 + g2] * hd->Lt[g2 * 65 + m];
+            x *= 2.0f;
+        }
+        dL[(size_t)h * 65 * 65 + e] = x;
+    }
+    if (tid == 0) deps[h] = gm[0];
+}
+
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 template <typename T>
 hipError_t launch_backward(const oal_dims &d, int T_len, int C, const void *q_, const void *k_, const void *v_,
                            const float *dy, const unsigned char *params, void *ws, float *dq, float *dk, float *dv,
-                           hipStream_t stream) {
+                           float *dL, float *deps, hipStream_t stream) {
     const T *q = static_cast<const T *>(q_), *k = static_cast<const T *>(k_), *v = static_cast<const T *>(v_);
     const int B = d.batch, Hq = d.n_q_heads, Hkv = d.n_kv_heads;
     const int nch = (T_len + C - 1) / C, tpc = C / 64;
@@ -758,6 +976,9 @@ hipError_t launch_backward(const oal_dims &d, int T_len, int C, const void *q_, 
     float *gd = reinterpret_cast<float *>(reinterpret_cast<unsigned char *>(gv) + align256((size_t)B * Hq * T_len * 64 * 4));
     float *part = reinterpret_cast<float *>(reinterpret_cast<unsigned char *>(gd) + align256((size_t)B * Hq * T_len * 4));
     const size_t kvrows = (size_t)B * Hkv * T_len;
+    float *dwp = reinterpret_cast<float *>(reinterpret_cast<unsigned char *>(part) +
+                                           align256((size_t)(kInterSplits + Hq / Hkv) * kvrows * 128 * 4));
+    const bool coef = dL != nullptr;
     const dim3 blk(kThreads);
     const dim3 g_inc((OAL_NFEAT + kFeatBlock - 1) / kFeatBlock, nch, B * Hkv);
     const dim3 g_scan((OAL_NFEAT * OAL_V1 + kThreads - 1) / kThreads, B * Hkv);
@@ -765,15 +986,24 @@ hipError_t launch_backward(const oal_dims &d, int T_len, int C, const void *q_, 
     const dim3 g_red((unsigned)((kvrows * 32 + kThreads - 1) / kThreads));
     const int nslots = kInterSplits + Hq / Hkv;
     hipLaunchKernelGGL((oal_bwd_increments<T, false>), g_inc, blk, 0, stream, T_len, C, nch, Hq, Hkv, k, v,
-                       (const float *)nullptr, (const float *)nullptr, params, st);
+                       (const float *)nullptr, (const float *)nullptr, params, st, (float *)nullptr);
     hipLaunchKernelGGL(oal_bwd_scan, g_scan, blk, 0, stream, nch, 0, st);
     hipLaunchKernelGGL(oal_bwd_readout_g<T>, g_q, blk, 0, stream, T_len, C, nch, Hq, Hkv, q, k, v, dy, params, st,
                        gv, gd);
     hipLaunchKernelGGL(oal_bwd_dq_inter<T>, g_q, blk, 0, stream, T_len, C, nch, Hq, Hkv, q, params, st, gv, gd, dq);
     hipLaunchKernelGGL(oal_bwd_dq_intra<T>, g_q, blk, 0, stream, T_len, C, Hq, Hkv, q, k, v, params, gv, gd, dq);
     hipLaunchKernelGGL(oal_bwd_dkv_intra<T>, g_kh, blk, 0, stream, T_len, C, Hq, Hkv, q, k, v, params, gv, gd, part);
+    if (coef)
+        hipLaunchKernelGGL(oal_bwd_dw_intra<T>, dim3(nch, Hq, B), blk, 0, stream, T_len, C, nch, Hq, Hkv, q, k, v,
+                           gv, gd, dwp + (size_t)B * Hq * nch * OAL_NFEAT);
     hipLaunchKernelGGL((oal_bwd_increments<T, true>), g_inc, blk, 0, stream, T_len, C, nch, Hq, Hkv, q,
-                       (const T *)nullptr, gv, gd, params, st);
+                       (const T *)nullptr, gv, gd, params, st, coef ? dwp : (float *)nullptr);
+    if (coef) {
+        float *dwt = dwp + 2 * (size_t)B * Hq * nch * OAL_NFEAT;
+        hipLaunchKernelGGL(oal_bwd_dw_sum, dim3((OAL_NFEAT + kThreads - 1) / kThreads, Hq), blk, 0, stream, B, nch,
+                           Hq, dwp, dwt);
+        hipLaunchKernelGGL(oal_bwd_coef, dim3(Hq), blk, 0, stream, params, dwt, dL, deps);
+    }
     hipLaunchKernelGGL(oal_bwd_scan, g_scan, blk, 0, stream, nch, 1, st);
     hipLaunchKernelGGL(oal_bwd_dk_inter<T>, g_ki, blk, 0, stream, T_len, C, nch, Hkv, k, v, st, part);
     hipLaunchKernelGGL(oal_bwd_dv_inter<T>, g_ki, blk, 0, stream, T_len, C, nch, Hkv, k, st, part);
@@ -787,14 +1017,15 @@ size_t oal_backward_ws_bytes_impl(const oal_dims &d, int T_len, int C) {
     const size_t nch = (size_t)(T_len + C - 1) / C;
     return align256((size_t)d.batch * d.n_kv_heads * nch * OAL_STATE_STRIDE * 4) +
            align256((size_t)d.batch * d.n_q_heads * T_len * 64 * 4) + align256((size_t)d.batch * d.n_q_heads * T_len * 4) +
-           align256((size_t)(kInterSplits + d.n_q_heads / d.n_kv_heads) * d.batch * d.n_kv_heads * T_len * 128 * 4);
+           align256((size_t)(kInterSplits + d.n_q_heads / d.n_kv_heads) * d.batch * d.n_kv_heads * T_len * 128 * 4) +
+           align256(((size_t)2 * d.batch * nch + 1) * d.n_q_heads * OAL_NFEAT * 4);
 }
 
 hipError_t oal_launch_backward(const oal_dims &d, int T_len, int C, const void *q, const void *k, const void *v,
                                const float *dy, const void *params, void *ws, float *dq, float *dk, float *dv,
-                               hipStream_t stream) {
+                               float *dL, float *deps, hipStream_t stream) {
     const unsigned char *p = static_cast<const unsigned char *>(params);
     if (d.dtype == OAL_BF16)
-        return launch_backward<__bf16>(d, T_len, C, q, k, v, dy, p, ws, dq, dk, dv, stream);
-    return launch_backward<float>(d, T_len, C, q, k, v, dy, p, ws, dq, dk, dv, stream);
+        return launch_backward<__bf16>(d, T_len, C, q, k, v, dy, p, ws, dq, dk, dv, dL, deps, stream);
+    return launch_backward<float>(d, T_len, C, q, k, v, dy, p, ws, dq, dk, dv, dL, deps, stream);
 }

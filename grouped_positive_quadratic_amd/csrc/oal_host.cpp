@@ -29,7 +29,7 @@ size_t oal_contribution_ws_bytes_impl(const oal_dims &d, int T_len);
 size_t oal_prefill_ws_bytes_impl(const oal_dims &d, int T_len, int C);
 hipError_t oal_launch_backward(const oal_dims &d, int T_len, int C, const void *q, const void *k, const void *v,
                                const float *dy, const void *params, void *ws, float *dq, float *dk, float *dv,
-                               hipStream_t stream);
+                               float *dL, float *deps, hipStream_t stream);
 size_t oal_backward_ws_bytes_impl(const oal_dims &d, int T_len, int C);
 
 namespace {
@@ -122,6 +122,8 @@ void pack_head(const oal_head_params *hp, int h, OalHeadDev *out, std::vector<do
             int gr = 1 + gam[r];
             out->Lz[m * OAL_D + r] = gr >= m ? (float)(L[gr * (G + 1) + m] / 8.0) : 0.0f;
         }
+    for (int a = 0; a <= G; ++a)
+        for (int b = 0; b <= a; ++b) out->Lt[a * 65 + b] = (float)L[a * (G + 1) + b];
     // decode coefficients per state row
     out->wdec[0] = out->a;
     for (int r = 0; r < OAL_D; ++r) out->wdec[1 + r] = (float)(2.0 * M[1 + gam[r]] / 8.0);
@@ -419,18 +421,21 @@ size_t oal_prefill_backward_workspace_bytes(const oal_dims *d, int32_t T, int32_
 
 oal_status oal_prefill_backward(const oal_dims *d, int32_t T, int32_t chunk, const void *q, const void *k,
                                 const void *v, const float *dy, const void *params_dev, void *workspace,
-                                float *dq, float *dk, float *dv, hipStream_t stream) {
+                                float *dq, float *dk, float *dv, float *dL, float *deps, hipStream_t stream) {
     oal_status st = check_dims(d);
     if (st != OAL_OK) return st;
     if (T < 0) return OAL_E_SHAPE;
     if (chunk != 64 && chunk != 128 && chunk != 256) return OAL_E_UNSUPPORTED;
     if (T == 0 || d->batch == 0) return OAL_OK;
     if (!backward_shape_ok(d, T, chunk)) return OAL_E_UNSUPPORTED;
-    if (!q || !k || !v || !dy || !params_dev || !workspace || !dq || !dk || !dv) return OAL_E_ARG;
+    if (!q || !k || !v || !dy || !params_dev || !workspace || !dq || !dk || !dv || (!dL != !deps))
+        return OAL_E_ARG;
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(dy) || !aligned16(params_dev) ||
-        !aligned16(workspace) || !aligned16(dq) || !aligned16(dk) || !aligned16(dv))
+        !aligned16(workspace) || !aligned16(dq) || !aligned16(dk) || !aligned16(dv) ||
+        (reinterpret_cast<uintptr_t>(dL) & 3u) || (reinterpret_cast<uintptr_t>(deps) & 3u))
         return OAL_E_ALIGN;
-    hipError_t e = oal_launch_backward(*d, T, chunk, q, k, v, dy, params_dev, workspace, dq, dk, dv, stream);
+    hipError_t e = oal_launch_backward(*d, T, chunk, q, k, v, dy, params_dev, workspace, dq, dk, dv, dL, deps,
+                                       stream);
     if (e != hipSuccess) {
         (void)hipGetLastError();
         return OAL_E_HIP;

@@ -83,6 +83,7 @@ struct OalHeadDev {
     float Lz[65 * 64];  // Lz[m][r] = L[g(r)+1][m] / 8 (zero where g(r)+1 < m), m = 0..64
     float wslot[OAL_KSTEPS * 32];      // general blob: M[g(r)+1][g(t)+1] per quadratic slot
     float wdec[2176];   // per state row f < 2145: coefficient of mono_f(q) . H_f (unscaled state)
+    float Lt[65 * 65];  // L[a][b] for b <= a <= G (row stride 65), zero elsewhere
 };
 
 // Per-KV-head record: the tail list. Entries 0..64: linear features and the constant;

@@ -225,7 +225,12 @@ oal_status oal_contribution(const oal_dims *dims, int32_t T, const void *q, cons
  * the chain rule through the chunked form). For y = oal_prefill(q, k, v) of T tokens per
  * sequence starting from a zero state, and the loss sum(dy * y), it writes
  *   dq [batch, n_q_heads, T, 64], dk and dv [batch, n_kv_heads, T, 64], all fp32 (device).
- * The coefficients (L, eps) receive no gradient here. The forward quantities it needs (the
+ * and, unless dL and deps are NULL, the gradients of the kernel coefficients of every query
+ * head (summed over the batch):
+ *   dL   [n_q_heads][65][65] fp32 (device, 4-byte aligned): entry [h][a][b] is dLoss/dL[a][b]
+ *        of head h for b <= a <= n_groups[h]; every other entry is written as 0;
+ *   deps [n_q_heads] fp32 (device, 4-byte aligned): dLoss/deps.
+ * (Both NULL, or both given: OAL_E_ARG otherwise.) The forward quantities it needs (the
  * prefix states, y and the normaliser per query) are recomputed in fp32 from q, k, v; the
  * caller passes no saved output.
  *   T          -- tokens per sequence (equal lengths), >= 0; T = 0 or batch = 0 is a no-op.
@@ -235,8 +240,8 @@ oal_status oal_contribution(const oal_dims *dims, int32_t T, const void *q, cons
  *   params_dev -- the blob oal_state_init uploaded.
  *   workspace  -- oal_prefill_backward_workspace_bytes(dims, T, chunk) bytes of device scratch
  *                 (per-chunk states, one block of OAL_STATE_STRIDE floats per sequence, KV
- *                 head and chunk; the per-query readout gradients; partial key gradients);
- *                 contents on entry do not matter.
+ *                 head and chunk; the per-query readout gradients; partial key gradients;
+ *                 partial coefficient gradients); contents on entry do not matter.
  * All arithmetic is fp32 whatever dims->dtype is (bf16 inputs are widened on load). Every
  * pointer must be 16-byte aligned (OAL_E_ALIGN). More than 65535 chunks per sequence or
  * more than 65535 query heads give OAL_E_UNSUPPORTED. */
@@ -244,7 +249,7 @@ size_t oal_prefill_backward_workspace_bytes(const oal_dims *dims, int32_t T, int
 oal_status oal_prefill_backward(const oal_dims *dims, int32_t T, int32_t chunk, const void *q,
                                 const void *k, const void *v, const float *dy,
                                 const void *params_dev, void *workspace, float *dq, float *dk,
-                                float *dv, hipStream_t stream);
+                                float *dv, float *dL, float *deps, hipStream_t stream);
 
 /* Decode step for sequences whose states live in a pool (serving: a batch of active
  * sequences over a larger set of state blocks). Sequence b of the batch uses pool block

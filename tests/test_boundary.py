@@ -53,14 +53,14 @@ def test_sizes():
     assert gpq.oal_contribution_workspace_bytes(gpq.make_dims(0, 14, 2, "bf16"), 64) == 0
     assert gpq.oal_contribution_workspace_bytes(bad, 64) == 0
     # backward: per-chunk states per (sequence, KV head), g (64 + 1 floats per query), then
-    # 8 + n_rep partial (dk, dv) rows of 128 floats per key
+    # 8 + n_rep partial (dk, dv) rows of 128 floats per key, two per-chunk coefficient partials and their sum per head
     al = lambda x: -(-x // 256) * 256
     assert gpq.oal_prefill_backward_workspace_bytes(d, 4096, 64) == (
         al(3 * 2 * 64 * 139456 * 4) + al(3 * 14 * 4096 * 64 * 4) + al(3 * 14 * 4096 * 4) +
-        al((8 + 7) * 3 * 2 * 4096 * 128 * 4))
+        al((8 + 7) * 3 * 2 * 4096 * 128 * 4) + al((2 * 3 * 64 + 1) * 14 * 2145 * 4))
     assert gpq.oal_prefill_backward_workspace_bytes(d, 130, 128) == (
         al(3 * 2 * 2 * 139456 * 4) + al(3 * 14 * 130 * 64 * 4) + al(3 * 14 * 130 * 4) +
-        al((8 + 7) * 3 * 2 * 130 * 128 * 4))
+        al((8 + 7) * 3 * 2 * 130 * 128 * 4) + al((2 * 3 * 2 + 1) * 14 * 2145 * 4))
     assert gpq.oal_prefill_backward_workspace_bytes(d, 4096, 100) == 0
     assert gpq.oal_prefill_backward_workspace_bytes(d, -1, 64) == 0
     assert gpq.oal_prefill_backward_workspace_bytes(d, 64 * 65536, 64) == 0
@@ -119,14 +119,16 @@ def test_validation_errors_enqueue_nothing():
     assert _code(gpq.oal_contribution, d, 8, A, A, A, A, A + 4, 0) == 4
     assert _code(gpq.oal_contribution, gpq.make_dims(1, 2, 1, 7), 8, *c4, 0) == 3
     assert _code(gpq.oal_contribution, gpq.make_dims(1, 2, 1, "bf16", d_h=32), 8, *c4, 0) == 5
-    b9 = (A, A, A, A, A, A, A, A, A)   # q, k, v, dy, params, workspace, dq, dk, dv
+    b9 = (A, A, A, A, A, A, A, A, A, None, None)   # q, k, v, dy, params, workspace, dq, dk, dv, dL, deps
     assert _code(gpq.oal_prefill_backward, d, 8, 100, *b9, 0) == 5            # chunk
     assert _code(gpq.oal_prefill_backward, d, -1, 64, *b9, 0) == 2            # T < 0
-    assert _code(gpq.oal_prefill_backward, d, 0, 64, *([None] * 9), 0) == 0   # T = 0: no-op
-    assert _code(gpq.oal_prefill_backward, gpq.make_dims(0, 2, 1, "bf16"), 8, 64, *([None] * 9), 0) == 0
-    assert _code(gpq.oal_prefill_backward, d, 8, 64, A, A, A, None, A, A, A, A, A, 0) == 1   # no dy
-    assert _code(gpq.oal_prefill_backward, d, 8, 64, A, A, A, A, A, None, A, A, A, 0) == 1   # no workspace
-    assert _code(gpq.oal_prefill_backward, d, 8, 64, A, A, A, A, A, A, A, A, A + 4, 0) == 4  # misaligned dv
+    assert _code(gpq.oal_prefill_backward, d, 0, 64, *([None] * 11), 0) == 0   # T = 0: no-op
+    assert _code(gpq.oal_prefill_backward, gpq.make_dims(0, 2, 1, "bf16"), 8, 64, *([None] * 11), 0) == 0
+    assert _code(gpq.oal_prefill_backward, d, 8, 64, A, A, A, None, A, A, A, A, A, None, None, 0) == 1   # no dy
+    assert _code(gpq.oal_prefill_backward, d, 8, 64, A, A, A, A, A, None, A, A, A, None, None, 0) == 1   # no ws
+    assert _code(gpq.oal_prefill_backward, d, 8, 64, A, A, A, A, A, A, A, A, A + 4, None, None, 0) == 4  # dv
+    assert _code(gpq.oal_prefill_backward, d, 8, 64, A, A, A, A, A, A, A, A, A, A, None, 0) == 1   # dL alone
+    assert _code(gpq.oal_prefill_backward, d, 8, 64, A, A, A, A, A, A, A, A, A, A, A + 2, 0) == 4  # deps
     assert _code(gpq.oal_prefill_backward, d, 64 * 65536, 64, *b9, 0) == 5    # > 65535 chunks
     assert _code(gpq.oal_prefill_backward, gpq.make_dims(1, 3, 2, "bf16"), 8, 64, *b9, 0) == 2
 
@@ -160,7 +162,8 @@ def test_param_validation():
 HEAD_DT = np.dtype([("G", "<i4"), ("bulk", "<i4"), ("eps", "<f4"), ("a", "<f4"), ("L00", "<f4"),
                     ("pad0", "<f4", 3), ("gamma", "u1", 64),
                     ("lin", "<f4", 64), ("w0", "<f4", 64), ("tail", "<f4", 256),
-                    ("Lz", "<f4", (65, 64)), ("wslot", "<f4", 72 * 32), ("wdec", "<f4", 2176)])
+                    ("Lz", "<f4", (65, 64)), ("wslot", "<f4", 72 * 32), ("wdec", "<f4", 2176),
+                    ("Lt", "<f4", (65, 65))])
 HEAD_BYTES = (HEAD_DT.itemsize + 255) // 256 * 256
 KV_DT = np.dtype([("npairs", "<i4"), ("nsteps", "<i4"), ("pad", "<i4", 62), ("ra", "u1", 256),
                   ("rb", "u1", 256)])

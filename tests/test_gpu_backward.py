@@ -19,6 +19,11 @@ import grouped_positive_quadratic_amd as gpq  # noqa: E402
 
 # fp32 arithmetic throughout (the inputs are exact in fp32 for both dtypes)
 BWD_TOL = 2e-4
+# dL and deps sum dkappa_ij sbar sbar^T over every causal pair, and each query's dkappa row is
+# orthogonal to its kappa row (sum_j kappa_ij dkappa_ij = g_i . u_i = 0): the result is a small
+# difference of large terms, so the same fp32 roundings give a larger error relative to it.
+# Measured up to 1.1e-4 over these cases; the bound keeps a margin of about 9 over that.
+COEF_TOL = 1e-3
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -27,7 +32,7 @@ def _need_gpu():
         pytest.fail("GPU tests need a GPU")
 
 
-def run_backward(inp, dy, chunk):
+def run_backward(inp, dy, chunk, coef=True):
     B, Hq, Hkv, T, _, _ = inp.dims
     dims = gpq.make_dims(B, Hq, Hkv, inp.dtype)
     hp = gpq.HeadParamsC.from_params(inp.params)
@@ -40,9 +45,23 @@ def run_backward(inp, dy, chunk):
     dq = torch.full((B, Hq, T, 64), np.nan, dtype=torch.float32, device="cuda")
     dk = torch.full((B, Hkv, T, 64), np.nan, dtype=torch.float32, device="cuda")
     dv = torch.full((B, Hkv, T, 64), np.nan, dtype=torch.float32, device="cuda")
-    gpq.oal_prefill_backward(dims, T, chunk, q, k, v, dyd, params, ws, dq, dk, dv)
+    dL = torch.full((Hq, 65, 65), np.nan, dtype=torch.float32, device="cuda") if coef else None
+    deps = torch.full((Hq,), np.nan, dtype=torch.float32, device="cuda") if coef else None
+    gpq.oal_prefill_backward(dims, T, chunk, q, k, v, dyd, params, ws, dq, dk, dv, dL, deps)
     torch.cuda.synchronize()
-    return dq.cpu().numpy(), dk.cpu().numpy(), dv.cpu().numpy()
+    out = (dq.cpu().numpy(), dk.cpu().numpy(), dv.cpu().numpy())
+    return out + ((dL.cpu().numpy(), deps.cpu().numpy()) if coef else ())
+
+
+def coef_err(dL, deps, rL, reps):
+    """Per head: max(|dL - dL*|, |deps - deps*|) / max(|dL*|, |deps*|); dL [Hq, 65, 65] against
+    the oracle's [Hq, g+1, g+1], everything outside the oracle's block must be exactly 0."""
+    gm1 = rL.shape[1]
+    assert np.all(dL[:, gm1:, :] == 0.0) and np.all(dL[:, :, gm1:] == 0.0)
+    a = dL[:, :gm1, :gm1].astype(np.float64)
+    num = np.maximum(np.abs(a - rL).reshape(len(rL), -1).max(-1), np.abs(deps - reps))
+    den = np.maximum(np.abs(rL).reshape(len(rL), -1).max(-1), np.abs(reps))
+    return float((num / np.maximum(den, 1e-300)).max())
 
 
 def slice_err(x, ref):
@@ -57,8 +76,9 @@ def slice_err(x, ref):
 def check(inp, chunk, seed, tol=BWD_TOL, name=""):
     B, Hq, Hkv, T, _, _ = inp.dims
     dy = np.random.default_rng(seed).normal(0.0, 1.0, (B, Hq, T, 64)).astype(np.float32)
-    dq, dk, dv = run_backward(inp, dy, chunk)
-    rq, rk, rv, _, _ = oracle.backward(inp.q, inp.k, inp.v, inp.params, dy)
+    dq, dk, dv, dL, deps = run_backward(inp, dy, chunk)
+    rq, rk, rv, rL, reps = oracle.backward(inp.q, inp.k, inp.v, inp.params, dy)
+    ec = coef_err(dL, deps, rL, reps) if T > 1 else 0.0
     if T == 1:
         # one token: y = v_0 whatever q and k are, so dq = dk = 0; both sides hold rounding
         # residue of dkappa = g . [v; 1] (a difference of two equal terms)
@@ -66,11 +86,19 @@ def check(inp, chunk, seed, tol=BWD_TOL, name=""):
         assert np.abs(rq).max() <= 1e-12 * scale and np.abs(rk).max() <= 1e-12 * scale
         assert np.abs(dq).max() <= 1e-5 * scale and np.abs(dk).max() <= 1e-5 * scale
         rq, rk = dq, dk
+        # the coefficient gradients are 2 dkappa sbar sbar^T L and dkappa: residue as well,
+        # |sbar_g| <= 64 max|q| max|k| / 8
+        sb = 1.0 + 8.0 * np.abs(inp.q).max() * np.abs(inp.k).max()
+        bound = 1e-5 * scale * 2.0 * sb * sb * max(1.0, np.abs(inp.params.L).max())
+        assert np.abs(rL).max() <= 1e-9 * bound and np.abs(dL).max() <= bound
+        assert np.abs(deps).max() <= 1e-5 * scale
+        ec = 0.0
     e = (slice_err(dq, rq), slice_err(dk, rk), slice_err(dv, rv))
     print(f"[parity] backward {name} {inp.dims[:4]} C={chunk} {inp.dtype}: "
-          f"dq={e[0]:.2e} dk={e[1]:.2e} dv={e[2]:.2e} tol={tol:.0e}", flush=True)
+          f"dq={e[0]:.2e} dk={e[1]:.2e} dv={e[2]:.2e} dL,deps={ec:.2e} tol={tol:.0e}/{COEF_TOL:.0e}",
+          flush=True)
     assert np.isfinite(dq).all() and np.isfinite(dk).all() and np.isfinite(dv).all()
-    assert max(e) <= tol
+    assert max(e) <= tol and ec <= COEF_TOL
     return dq, dk, dv
 
 
@@ -122,8 +150,10 @@ def test_backward_l_zero_closed_form():
     inp.params.eps[:] = 0.5
     B, Hq, Hkv, T, _, _ = inp.dims
     dy = np.random.default_rng(53).normal(0.0, 1.0, (B, Hq, T, 64)).astype(np.float32)
-    dq, dk, dv = run_backward(inp, dy, 64)
-    assert np.all(dq == 0.0) and np.all(dk == 0.0)
+    dq, dk, dv, dL, deps = run_backward(inp, dy, 64)
+    assert np.all(dq == 0.0) and np.all(dk == 0.0) and np.all(dL == 0.0)
+    # deps = sum of dkappa over all pairs = sum_i g_i . u_i = sum_i (dy.y - dy.y) / den = 0
+    assert np.abs(deps).max() <= 1e-5 * np.abs(dy).sum(axis=(0, 2, 3)).max()
     w = dy.astype(np.float64) / np.arange(1, T + 1)[None, None, :, None]
     ref = np.flip(np.cumsum(np.flip(w, 2), 2), 2).sum(1, keepdims=True)
     assert slice_err(dv, ref) <= BWD_TOL
@@ -134,6 +164,7 @@ def test_backward_deterministic():
     dy = np.random.default_rng(54).normal(0.0, 1.0, (1, 7, 200, 64)).astype(np.float32)
     a = run_backward(inp, dy, 64)
     b = run_backward(inp, dy, 64)
+    assert len(a) == 5
     for x, y in zip(a, b):
         assert np.array_equal(x, y)
 
@@ -145,7 +176,7 @@ def test_backward_matches_forward_directional_derivative():
     B, Hq, Hkv, T, _, _ = inp.dims
     rng = np.random.default_rng(55)
     dy = rng.normal(0.0, 1.0, (B, Hq, T, 64)).astype(np.float32)
-    dq, dk, dv = run_backward(inp, dy, 64)
+    dq, dk, dv = run_backward(inp, dy, 64, coef=False)
     eq, ek, ev = (rng.normal(0.0, 1.0, x.shape).astype(np.float64) for x in (inp.q, inp.k, inp.v))
     pred = float((dq * eq).sum() + (dk * ek).sum() + (dv * ev).sum())
     h = 1e-3
@@ -157,6 +188,24 @@ def test_backward_matches_forward_directional_derivative():
     fd = (loss(h) - loss(-h)) / (2 * h)
     print(f"[parity] backward directional: pred={pred:.6e} fd={fd:.6e}", flush=True)
     assert abs(pred - fd) <= 1e-3 * max(1.0, abs(fd))
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_backward_coefficient_scale_invariance(dtype):
+    """y is unchanged under (L, eps) -> (a L, a^2 eps), so d/da at a = 1 vanishes:
+    sum L o dL + 2 eps deps = 0 per head (checked on the library's own gradients)."""
+    inp = small(56, 1, 7, 1, 200, dtype)
+    B, Hq, Hkv, T, _, _ = inp.dims
+    dy = np.random.default_rng(56).normal(0.0, 1.0, (B, Hq, T, 64)).astype(np.float32)
+    _, _, _, dL, deps = run_backward(inp, dy, 64)
+    p = inp.params
+    for h in range(Hq):
+        G = int(p.n_groups[h])
+        Lh = np.tril(p.L[h][: G + 1, : G + 1]).astype(np.float64)
+        terms = Lh * dL[h, : G + 1, : G + 1]
+        total = terms.sum() + 2.0 * float(p.eps[h]) * float(deps[h])
+        scale = np.abs(terms).sum() + 2.0 * abs(float(p.eps[h]) * float(deps[h]))
+        assert abs(total) <= 1e-4 * scale, (h, total, scale)
 
 
 def test_backward_empty_and_validation():
