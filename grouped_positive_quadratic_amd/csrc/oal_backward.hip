@@ -1,5 +1,6 @@
-// oal_backward.hip -- gfx950 kernels of the prefill backward: dq, dk, dv of sum(dy * y) for
-// the causal attention y of a prefill from an empty prefix.
+// oal_backward.hip -- gfx950 kernels of the prefill backward: dq, dk, dv (and the gradients of
+// the kernel coefficients L, eps) of sum(dy * y) for the causal attention y of a prefill from
+// an empty prefix.
 //
 // The forward (reproduction notes of arXiv 2610.13674, section "核心公式": the kernel kappa,
 // the H-state recurrence and the readout u~ = phi(q) . H, y = u~[0:64] / u~[64]) is
