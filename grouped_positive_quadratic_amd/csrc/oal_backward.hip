@@ -28,7 +28,8 @@
 //   1. oal_bwd_increments<keys>:    per chunk psi(K_c)^T [V_c; 1]           -> workspace states
 //   2. oal_bwd_scan (forward):      exclusive prefix over chunks: S_c
 //   3. oal_bwd_readout_g:           u_i (inter + intra), y, den -> g_i     -> workspace g
-//   4. oal_bwd_dq_inter, _intra:    dq (state part, then the pairs inside the chunk)
+//   4. oal_bwd_dq_inter, oal_bwd_sum_parts, oal_bwd_dq_intra: dq (state part in four row
+//      splits, their sum, then the pairs inside the chunk)
 //   5. oal_bwd_dkv_intra:           dk, dv partials of the pairs inside the chunk
 //   6. oal_bwd_increments<queries>: per chunk sum_h phi_h(Q_c)^T G_c       -> workspace states
 //   7. oal_bwd_scan (reverse):      exclusive suffix over chunks: R_c
@@ -412,74 +413,114 @@ __global__ __launch_bounds__(kThreads) void oal_bwd_readout_g(int T_len, int C, 
     }
 }
 
-// 4a. dq_i = Jphi_h(q_i)^T (S_c g_i) (the state part). Workgroup = (64-query tile, head,
-//     sequence); lane = query; wave w takes the feature rows r = w (mod 4). Per quadratic
-//     feature (r, t): x = S_c[f] . g, then dq_t += wdec x q_r and dq_r += wdec x q_t (t = r
-//     gives the 2 of the square). dq_t is a register (t unrolled); the row's dq_r, owned by
-//     one wave, goes to LDS.
+// 4a. dq_i = Jphi_h(q_i)^T (S_c g_i) (the state part). Workgroup = (64-query tile, four query
+//     heads of one KV head -- one per wave --, row split p, sequence); lane = query. Split p
+//     takes the feature rows r = p (mod kDqSplits): per row, the block of state rows it needs
+//     (the linear feature 1 + r and the quadratic (r, t), t >= r) is staged once in LDS and
+//     read by the four heads. Per quadratic feature: x = S_c[f] . g, then dq_t += wdec x q_r and
+//     dq_r += wdec x q_t (t = r gives the 2 of the square); dq_t and q_t are registers (t
+//     unrolled), q_r and dq_r picked out of those by selection. Each split writes its partial
+//     dq; oal_bwd_sum_parts adds them in order.
+constexpr int kDqSplits = 4;
+constexpr int kDqHeads = 4;
+
+__device__ inline float lds_dot(const float *row, const float (&g)[65]) {
+    const float4 *r4 = reinterpret_cast<const float4 *>(row);
+    float x0 = row[64] * g[64], x1 = 0.0f, x2 = 0.0f, x3 = 0.0f;
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+        const float4 s4 = r4[u];
+        x0 += s4.x * g[4 * u];
+        x1 += s4.y * g[4 * u + 1];
+        x2 += s4.z * g[4 * u + 2];
+        x3 += s4.w * g[4 * u + 3];
+    }
+    return (x0 + x1) + (x2 + x3);
+}
+
 template <typename T>
 __global__ __launch_bounds__(kThreads) void oal_bwd_dq_inter(int T_len, int C, int nch, int n_q_heads,
                                                               int n_kv_heads, const T *__restrict__ q,
                                                               const unsigned char *__restrict__ params,
                                                               const float *__restrict__ st, const float *__restrict__ gv,
-                                                              const float *__restrict__ gd, float *__restrict__ dq) {
-    __shared__ float xq[64 * 65];
-    __shared__ float dql[64 * 65];
+                                                              const float *__restrict__ gd, float *__restrict__ dqp) {
+    __shared__ __align__(16) float sb[65 * 68];     // slot 0: feature 1 + r; slot 1 + k: (r, r + k)
     const int tpc = C / 64, c = blockIdx.x / tpc, qt = blockIdx.x % tpc;
-    const int h = blockIdx.y, b = blockIdx.z, n_rep = n_q_heads / n_kv_heads, kv = h / n_rep;
-    const int i = threadIdx.x & 63, w = wave_id();
+    const int n_rep = n_q_heads / n_kv_heads, ngrp = (n_rep + kDqHeads - 1) / kDqHeads;
+    const int p = blockIdx.y % kDqSplits, grp = (blockIdx.y / kDqSplits) % ngrp;
+    const int kv = blockIdx.y / (kDqSplits * ngrp), b = blockIdx.z;
+    const int i = threadIdx.x & 63, w = wave_id(), hs = grp * kDqHeads + w;
+    const bool active = hs < n_rep;                 // wave-uniform
+    const int h = kv * n_rep + (active ? hs : 0);
     const int t0 = c * C + qt * 64, t = t0 + i;
-    const bool valid = t < T_len;
-    const cfloat *wd = uni(bwd_head(params, h)->wdec);
+    const bool valid = active && t < T_len;
     const size_t qrow = ((size_t)b * n_q_heads + h) * T_len;
-    stage_rows(xq, 65, q, qrow, t0, T_len, 1.0f);
-    for (int e = threadIdx.x; e < 64 * 65; e += kThreads) dql[e] = 0.0f;
-    float g[65];
+    const cfloat *wd = uni(bwd_head(params, h)->wdec);
+    float qv[64], g[65], d[64];
+#pragma unroll
+    for (int e = 0; e < 64; ++e) {
+        qv[e] = valid ? oal_ld(q + (qrow + t) * OAL_D + e) : 0.0f;
+        d[e] = 0.0f;
+    }
 #pragma unroll
     for (int e = 0; e < 64; e += 4) {
         const float4 g4 = valid ? *reinterpret_cast<const float4 *>(gv + (qrow + t) * OAL_D + e) : make_float4(0, 0, 0, 0);
         g[e] = g4.x; g[e + 1] = g4.y; g[e + 2] = g4.z; g[e + 3] = g4.w;
     }
     g[64] = valid ? gd[qrow + t] : 0.0f;
-    __syncthreads();
-    const float *xi = xq + i * 65;
-
-    float d[64];
-#pragma unroll
-    for (int e = 0; e < 64; ++e) d[e] = 0.0f;
-    if (c > 0) {                                   // S_0 = 0
-        const float *Sg = st + ((size_t)((size_t)b * n_kv_heads + kv) * nch + c) * OAL_STATE_STRIDE;
-        const cfloat *S = uni(Sg), *Sd = uni(Sg + (size_t)OAL_NFEAT * OAL_D);
-        for (int r = w; r < OAL_D; r += 4) {
-            const float qr = xi[r];
-            float dr = wd[1 + r] * row_dot(S, Sd, 1 + r, g);
-            const int base = quad_base(r);
-#pragma unroll
-            for (int tt = 0; tt < OAL_D; ++tt) {
-                if (tt >= r) {
-                    const float wx = wd[base + tt] * row_dot(S, Sd, base + tt, g);
-                    d[tt] += wx * qr;
-                    dr += wx * xi[tt];
-                }
+    if (c > 0) {                                    // S_0 = 0
+        const float *S = st + ((size_t)((size_t)b * n_kv_heads + kv) * nch + c) * OAL_STATE_STRIDE;
+        const float *Sd = S + (size_t)OAL_NFEAT * OAL_D;
+        for (int r = p; r < OAL_D; r += kDqSplits) {
+            const int base = quad_base(r), nslot = OAL_D + 1 - r;
+            __syncthreads();                        // the previous block is consumed
+            for (int e = threadIdx.x; e < nslot * 16; e += kThreads) {
+                const int k = e >> 4, c4 = (e & 15) * 4;
+                const int f = k == 0 ? 1 + r : base + r + k - 1;
+                *reinterpret_cast<float4 *>(sb + k * 68 + c4) = *reinterpret_cast<const float4 *>(S + (size_t)f * OAL_D + c4);
             }
-            dql[i * 65 + r] += dr;
-        }
-    }
-    for (int s = 0; s < 4; ++s) {
-        __syncthreads();
-        if (w == s) {
+            if (threadIdx.x < nslot) {
+                const int k = threadIdx.x;
+                sb[k * 68 + 64] = Sd[k == 0 ? 1 + r : base + r + k - 1];
+            }
+            __syncthreads();
+            if (active) {
+                float qr = 0.0f;                    // qv[r] by selection: a dynamic index would
+#pragma unroll                                      // move the arrays to scratch memory
+                for (int e = 0; e < 64; ++e) qr = e == r ? qv[e] : qr;
+                float dr = wd[1 + r] * lds_dot(sb, g);
 #pragma unroll
-            for (int e = 0; e < 64; ++e) dql[i * 65 + e] += d[e];
+                for (int tt = 0; tt < OAL_D; ++tt) {
+                    if (tt >= r) {
+                        const float wx = wd[base + tt] * lds_dot(sb + (tt - r + 1) * 68, g);
+                        d[tt] += wx * qr;
+                        dr += wx * qv[tt];
+                    }
+                }
+#pragma unroll
+                for (int e = 0; e < 64; ++e) d[e] += e == r ? dr : 0.0f;
+            }
         }
     }
-    __syncthreads();
     if (valid) {
-        float *o = dq + (qrow + t) * OAL_D + w * 16;
-        const float *src = dql + i * 65 + w * 16;
+        float *o = dqp + ((size_t)p * gridDim.z * n_q_heads * T_len + qrow + t) * OAL_D;
 #pragma unroll
-        for (int e = 0; e < 16; e += 4)
-            *reinterpret_cast<float4 *>(o + e) = make_float4(src[e], src[e + 1], src[e + 2], src[e + 3]);
+        for (int e = 0; e < 64; e += 4) *reinterpret_cast<float4 *>(o + e) = make_float4(d[e], d[e + 1], d[e + 2], d[e + 3]);
     }
+}
+
+// out[n] = sum_{s < nparts} parts[s][n] in order (n counted in float4s).
+__global__ __launch_bounds__(kThreads) void oal_bwd_sum_parts(size_t n4, int nparts, const float *__restrict__ parts,
+                                                              float *__restrict__ out) {
+    const size_t e = (size_t)blockIdx.x * kThreads + threadIdx.x;
+    if (e >= n4) return;
+    const float4 *p4 = reinterpret_cast<const float4 *>(parts);
+    float4 s = p4[e];
+    for (int k = 1; k < nparts; ++k) {
+        const float4 x = p4[(size_t)k * n4 + e];
+        s.x += x.x; s.y += x.y; s.z += x.z; s.w += x.w;
+    }
+    reinterpret_cast<float4 *>(out)[e] = s;
 }
 
 // 4b. dq_i += sum_{j <= i in the chunk} dkappa_ij dkappa_ij/dq_i, dkappa_ij = g_i . [v_j; 1].
@@ -980,6 +1021,8 @@ hipError_t launch_backward(const oal_dims &d, int T_len, int C, const void *q_, 
     float *dwp = reinterpret_cast<float *>(reinterpret_cast<unsigned char *>(part) +
                                            align256((size_t)(kInterSplits + Hq / Hkv) * kvrows * 128 * 4));
     const bool coef = dL != nullptr;
+    float *dqp = reinterpret_cast<float *>(reinterpret_cast<unsigned char *>(dwp) +
+                                           align256(((size_t)2 * B * nch + 1) * Hq * OAL_NFEAT * 4));
     const dim3 blk(kThreads);
     const dim3 g_inc((OAL_NFEAT + kFeatBlock - 1) / kFeatBlock, nch, B * Hkv);
     const dim3 g_scan((OAL_NFEAT * OAL_V1 + kThreads - 1) / kThreads, B * Hkv);
@@ -991,7 +1034,14 @@ hipError_t launch_backward(const oal_dims &d, int T_len, int C, const void *q_, 
     hipLaunchKernelGGL(oal_bwd_scan, g_scan, blk, 0, stream, nch, 0, st);
     hipLaunchKernelGGL(oal_bwd_readout_g<T>, g_q, blk, 0, stream, T_len, C, nch, Hq, Hkv, q, k, v, dy, params, st,
                        gv, gd);
-    hipLaunchKernelGGL(oal_bwd_dq_inter<T>, g_q, blk, 0, stream, T_len, C, nch, Hq, Hkv, q, params, st, gv, gd, dq);
+    {
+        const int ngrp = (Hq / Hkv + kDqHeads - 1) / kDqHeads;
+        const size_t n4 = (size_t)B * Hq * T_len * 16;
+        hipLaunchKernelGGL(oal_bwd_dq_inter<T>, dim3(nch * tpc, Hkv * ngrp * kDqSplits, B), blk, 0, stream, T_len, C,
+                           nch, Hq, Hkv, q, params, st, gv, gd, dqp);
+        hipLaunchKernelGGL(oal_bwd_sum_parts, dim3((unsigned)((n4 + kThreads - 1) / kThreads)), blk, 0, stream, n4,
+                           kDqSplits, dqp, dq);
+    }
     hipLaunchKernelGGL(oal_bwd_dq_intra<T>, g_q, blk, 0, stream, T_len, C, Hq, Hkv, q, k, v, params, gv, gd, dq);
     hipLaunchKernelGGL(oal_bwd_dkv_intra<T>, g_kh, blk, 0, stream, T_len, C, Hq, Hkv, q, k, v, params, gv, gd, part);
     if (coef)
@@ -1019,7 +1069,8 @@ size_t oal_backward_ws_bytes_impl(const oal_dims &d, int T_len, int C) {
     return align256((size_t)d.batch * d.n_kv_heads * nch * OAL_STATE_STRIDE * 4) +
            align256((size_t)d.batch * d.n_q_heads * T_len * 64 * 4) + align256((size_t)d.batch * d.n_q_heads * T_len * 4) +
            align256((size_t)(kInterSplits + d.n_q_heads / d.n_kv_heads) * d.batch * d.n_kv_heads * T_len * 128 * 4) +
-           align256(((size_t)2 * d.batch * nch + 1) * d.n_q_heads * OAL_NFEAT * 4);
+           align256(((size_t)2 * d.batch * nch + 1) * d.n_q_heads * OAL_NFEAT * 4) +
+           align256((size_t)kDqSplits * d.batch * d.n_q_heads * T_len * 64 * 4);
 }
 
 hipError_t oal_launch_backward(const oal_dims &d, int T_len, int C, const void *q, const void *k, const void *v,
