@@ -319,8 +319,14 @@ __global__ __launch_bounds__(kThreads) void oal_bwd_scan(int nch, int reverse, f
 __device__ inline bool sees(int kt, int qt, int jj, int i) { return kt < qt || jj <= i; }
 
 // 3. u_i = phi_h(q_i) . S_c + sum_{j <= i in the chunk} kappa_ij [v_j; 1]; y = u[0:64] / u[64];
-//    g_i = (dy_i / den, -(dy_i . y_i) / den). Workgroup = (64-query tile, head, sequence);
-//    lane = query, the four waves split the feature rows r = w (mod 4) and the keys.
+//    g_i = (dy_i / den, -(dy_i . y_i) / den). Workgroup = (64-query tile, head, sequence).
+//    State part on fp32 MFMA (v_mfma_f32_16x16x4_f32): U = phi(Q) S_c, wave w computing the
+//    queries 16 w .. 16 w + 15 against 80 columns (five 16 x 16 tiles; the fifth holds the
+//    column 64 of S_c, the normaliser) with K over the features in blocks of 64, each block
+//    of S_c staged once in LDS. A operand: lane l holds phi_f(q) of query l % 16 and feature
+//    f = 4 K-step + l / 16, built from the query tile, the head's coefficients and the dims of
+//    f (LDS tables); B operand: S_c[f][col], col = 16 tile + l % 16. The result goes to an LDS
+//    tile. Pairs inside the chunk: lane = query, the four waves split the keys.
 template <typename T>
 __global__ __launch_bounds__(kThreads) void oal_bwd_readout_g(int T_len, int C, int nch, int n_q_heads,
                                                                int n_kv_heads, const T *__restrict__ q,
@@ -330,36 +336,103 @@ __global__ __launch_bounds__(kThreads) void oal_bwd_readout_g(int T_len, int C, 
                                                                const float *__restrict__ st, float *__restrict__ gv,
                                                                float *__restrict__ gd) {
     __shared__ float xq[64 * 65];
-    __shared__ float ks[64 * 64];
-    __shared__ __align__(16) float vs[64 * 68];
+    __shared__ __align__(16) float ks[64 * 64];    // keys; before them the coefficient tables
+    __shared__ __align__(16) float vs[64 * 68];    // values; before them a block of S_c
+    __shared__ __align__(16) float uin[64 * 68];   // state part of u per query
     const int tpc = C / 64, c = blockIdx.x / tpc, qt = blockIdx.x % tpc;
     const int h = blockIdx.y, b = blockIdx.z, n_rep = n_q_heads / n_kv_heads, kv = h / n_rep;
     const int i = threadIdx.x & 63, w = wave_id();
     const int t0 = c * C + qt * 64, t = t0 + i;
     const bool valid = t < T_len;
     const OalHeadDev *hd = bwd_head(params, h);
-    const cfloat *wd = uni(hd->wdec);
     const int G = hd->G;
     const size_t qrow = ((size_t)b * n_q_heads + h) * T_len, krow = ((size_t)b * n_kv_heads + kv) * T_len;
     stage_rows(xq, 65, q, qrow, t0, T_len, 1.0f);
+    constexpr int NFP = 2176;                      // features padded to 34 blocks of 64
+    float *wdl = ks;                               // wdec_h[f], zero past 2145
+    unsigned short *fdl = reinterpret_cast<unsigned short *>(ks + NFP);   // dims of f: a | b << 8
+    for (int f = threadIdx.x; f < NFP; f += kThreads) {
+        wdl[f] = f < OAL_NFEAT ? hd->wdec[f] : 0.0f;
+        int fa = OAL_D, fb = OAL_D;
+        if (f >= 1 && f <= OAL_D) {
+            fa = f - 1;
+        } else if (f > OAL_D && f < OAL_NFEAT) {
+            int idx = f - 1 - OAL_D, r = 0;
+            while (idx >= OAL_D - r) { idx -= OAL_D - r; ++r; }
+            fa = r;
+            fb = r + idx;
+        }
+        fdl[f] = (unsigned short)(fa | (fb << 8));
+    }
     __syncthreads();
     const float *xi = xq + i * 65;
+
+    {
+        const int lr = threadIdx.x & 15, kg = (threadIdx.x >> 4) & 3;   // MFMA lane roles
+        const float *xa = xq + (16 * w + lr) * 65;                     // A row: query 16 w + lr
+        oal_f32x4 D[5], E[5];                       // even and odd K-steps: independent chains
+#pragma unroll
+        for (int ct = 0; ct < 5; ++ct) D[ct] = E[ct] = oal_splat(0.0f);
+        if (c > 0) {                               // S_0 = 0
+            const float *S = st + ((size_t)((size_t)b * n_kv_heads + kv) * nch + c) * OAL_STATE_STRIDE;
+            const float *Sd = S + (size_t)OAL_NFEAT * OAL_D;
+            float *sblk = vs;
+            // block f0 .. f0 + 63 of S_c: thread's share (4 float4 of the 64 columns, one
+            // normaliser entry), loaded into registers one block ahead of its use
+            float4 pre[4];
+            float pre64 = 0.0f;
+            auto load_block = [&](int f0) {
+#pragma unroll
+                for (int m = 0; m < 4; ++m) {
+                    const int e = threadIdx.x + kThreads * m, kk = e >> 4, c4 = (e & 15) * 4, f = f0 + kk;
+                    pre[m] = f < OAL_NFEAT ? *reinterpret_cast<const float4 *>(S + (size_t)f * OAL_D + c4)
+                                           : make_float4(0, 0, 0, 0);
+                }
+                if (threadIdx.x < 64) pre64 = f0 + (int)threadIdx.x < OAL_NFEAT ? Sd[f0 + threadIdx.x] : 0.0f;
+            };
+            load_block(0);
+            for (int f0 = 0; f0 < NFP; f0 += 64) {
+                __syncthreads();                   // the previous block is consumed
+#pragma unroll
+                for (int m = 0; m < 4; ++m) {
+                    const int e = threadIdx.x + kThreads * m, kk = e >> 4, c4 = (e & 15) * 4;
+                    *reinterpret_cast<float4 *>(sblk + kk * 68 + c4) = pre[m];
+                }
+                if (threadIdx.x < 64) sblk[threadIdx.x * 68 + 64] = pre64;
+                __syncthreads();
+                if (f0 + 64 < NFP) load_block(f0 + 64);
+#pragma unroll 2
+                for (int kst = 0; kst < 16; kst += 2) {
+                    const int kk = 4 * kst + kg, f = f0 + kk;
+                    const unsigned short ab = fdl[f], ab2 = fdl[f + 4];
+                    const float a = wdl[f] * xa[ab & 0xff] * xa[ab >> 8];
+                    const float a2 = wdl[f + 4] * xa[ab2 & 0xff] * xa[ab2 >> 8];
+                    const float *brow = sblk + kk * 68, *brow2 = brow + 4 * 68;
+#pragma unroll
+                    for (int ct = 0; ct < 4; ++ct) {
+                        D[ct] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, brow[16 * ct + lr], D[ct], 0, 0, 0);
+                        E[ct] = __builtin_amdgcn_mfma_f32_16x16x4f32(a2, brow2[16 * ct + lr], E[ct], 0, 0, 0);
+                    }
+                    D[4] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, lr == 0 ? brow[64] : 0.0f, D[4], 0, 0, 0);
+                    E[4] = __builtin_amdgcn_mfma_f32_16x16x4f32(a2, lr == 0 ? brow2[64] : 0.0f, E[4], 0, 0, 0);
+                }
+            }
+        }
+#pragma unroll
+        for (int ct = 0; ct < 5; ++ct) D[ct] += E[ct];
+        // D[ct][j]: query 16 w + 4 (l / 16) + j, column 16 ct + l % 16
+#pragma unroll
+        for (int ct = 0; ct < 5; ++ct)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int col = 16 * ct + lr;
+                if (col <= 64) uin[(16 * w + 4 * kg + j) * 68 + col] = D[ct][j];
+            }
+    }
 
     float acc[65];
 #pragma unroll
     for (int e = 0; e < 65; ++e) acc[e] = 0.0f;
-    if (c > 0) {                                   // S_0 = 0
-        const float *Sg = st + ((size_t)((size_t)b * n_kv_heads + kv) * nch + c) * OAL_STATE_STRIDE;
-        const cfloat *S = uni(Sg), *Sd = uni(Sg + (size_t)OAL_NFEAT * OAL_D);
-        if (w == 0) row_axpy<65>(acc, wd[0], S, Sd, 0);
-        for (int r = w; r < OAL_D; r += 4) {
-            const float qr = xi[r];
-            row_axpy<65>(acc, wd[1 + r] * qr, S, Sd, 1 + r);
-            const int base = quad_base(r);
-#pragma unroll 4
-            for (int tt = r; tt < OAL_D; ++tt) row_axpy<65>(acc, wd[base + tt] * qr * xi[tt], S, Sd, base + tt);
-        }
-    }
     for (int kt = 0; kt <= qt; ++kt) {
         const int k0 = c * C + kt * 64;
         __syncthreads();
@@ -398,6 +471,8 @@ __global__ __launch_bounds__(kThreads) void oal_bwd_readout_g(int T_len, int C, 
         }
     }
     if (w == 0 && valid) {
+#pragma unroll
+        for (int e = 0; e < 65; ++e) acc[e] += uin[i * 68 + e];
         const float inv = 1.0f / acc[64];
         const float *dyr = dy + (qrow + t) * OAL_D;
         float *gr = gv + (qrow + t) * OAL_D;
