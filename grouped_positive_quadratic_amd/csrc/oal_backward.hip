@@ -201,8 +201,13 @@ __device__ inline void stage_g(float *dst, const float *gv, const float *gd, siz
 //   queries: a_n = wdec_h[f] mono_f(q_n),      b_n = g_n        (n over the chunk's queries of
 //                                                                every head h of the KV head);
 //            with dwp, also the state part of each head's coefficient gradient (see below)
-// Workgroup = (64 features, chunk, sequence x KV head); thread = (feature, quarter of the 64
-// value columns); the feature's dims are fixed per thread, rows are staged 64 at a time.
+// fp32 MFMA (16x16x4): M = features, N = value columns (five 16-column tiles, the fifth
+// holding column 64), K = rows. Workgroup = (64 features, chunk, sequence x KV head), wave w
+// the features 16 w .. 16 w + 15; rows are staged 64 at a time. A operand: lane l holds
+// mono_f(x_n) of feature 16 w + l % 16 and row n = 4 K-step + l / 16 (the feature's dims are
+// fixed per lane); B operand: b_n[16 tile + l % 16]. Accumulators: the head's tile D (lane l
+// holds features 16 w + 4 (l / 16) + j, column 16 tile + l % 16), folded into the total with
+// the head's coefficients after its rows.
 template <typename T, bool QSIDE>
 __global__ __launch_bounds__(kThreads) void oal_bwd_increments(int T_len, int C, int nch, int n_q_heads,
                                                                 int n_kv_heads, const T *__restrict__ x,
@@ -212,89 +217,129 @@ __global__ __launch_bounds__(kThreads) void oal_bwd_increments(int T_len, int C,
                                                                 float *__restrict__ st, float *__restrict__ dwp) {
     __shared__ float xs[64 * 65];
     __shared__ __align__(16) float bs[64 * 68];
-    const int tid = threadIdx.x, fl = tid >> 2, cq = tid & 3;
-    const int f = blockIdx.x * kFeatBlock + fl;
+    const int tid = threadIdx.x, lane = tid & 63, lr = lane & 15, kg = lane >> 4, w = wave_id();
     const int c = blockIdx.y, bkv = blockIdx.z;
     const int b = bkv / n_kv_heads, kv = bkv % n_kv_heads, n_rep = n_q_heads / n_kv_heads;
-    int ia = OAL_D, ib = OAL_D;                    // dims of feature f; dim 64 reads the 1
-    if (f >= 1 && f <= OAL_D) {
-        ia = f - 1;
-    } else if (f > OAL_D && f < OAL_NFEAT) {
-        int idx = f - 1 - OAL_D, r = 0;
+    const int fbase = blockIdx.x * kFeatBlock + 16 * w;      // this wave's 16 features
+    const int fa_lane = fbase + lr;                           // A operand feature of this lane
+    int ia = OAL_D, ib = OAL_D;                    // its dims; dim 64 reads the 1
+    if (fa_lane >= 1 && fa_lane <= OAL_D) {
+        ia = fa_lane - 1;
+    } else if (fa_lane > OAL_D && fa_lane < OAL_NFEAT) {
+        int idx = fa_lane - 1 - OAL_D, r = 0;
         while (idx >= OAL_D - r) { idx -= OAL_D - r; ++r; }
         ia = r;
         ib = r + idx;
     }
-    float acc[16], acc64 = 0.0f;
-#pragma unroll
-    for (int e = 0; e < 16; ++e) acc[e] = 0.0f;
     float *out = st + ((size_t)bkv * nch + c) * OAL_STATE_STRIDE;
+    // output positions of this lane: features fo + j (j = 0..3), column 16 ct + lr
+    const int fo = fbase + 4 * kg;
     // queries with dwp: the state S_c this kernel overwrites, for the coefficient gradient
     // dw_h[f] = sum_{i in chunk} mono_f(q_i) (S_c g_i)[f] = S_c[f] . (sum_i mono_f(q_i) g_i)
     const bool coef = QSIDE && dwp != nullptr;
-    float sv[16], s64 = 0.0f;
+    oal_f32x4 sv[5], tot[5];
 #pragma unroll
-    for (int e = 0; e < 16; ++e) sv[e] = 0.0f;
-    if (coef && f < OAL_NFEAT) {
-        const float4 *sp = reinterpret_cast<const float4 *>(out + (size_t)f * OAL_D + cq * 16);
+    for (int ct = 0; ct < 5; ++ct) sv[ct] = tot[ct] = oal_splat(0.0f);
+    if (coef) {
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const float4 x4 = sp[u];
-            sv[4 * u] = x4.x; sv[4 * u + 1] = x4.y; sv[4 * u + 2] = x4.z; sv[4 * u + 3] = x4.w;
+        for (int j = 0; j < 4; ++j) {
+            const int f = fo + j;
+            if (f < OAL_NFEAT) {
+#pragma unroll
+                for (int ct = 0; ct < 4; ++ct) sv[ct][j] = out[(size_t)f * OAL_D + 16 * ct + lr];
+                sv[4][j] = lr == 0 ? out[(size_t)OAL_NFEAT * OAL_D + f] : 0.0f;
+            }
         }
-        if (cq == 0) s64 = out[(size_t)OAL_NFEAT * OAL_D + f];
     }
     const int nsrc = QSIDE ? n_rep : 1;
     const int tend = min(c * C + C, T_len);
+    // the (row tile, head) steps in order; each step's x and b rows are loaded into registers
+    // one step ahead (thread's share: 16 elements of each, plus one b[64])
+    const int ntile = (tend - c * C + 63) / 64, nstep = nsrc * ntile;
+    float px[16], pb[16], pb64 = 0.0f;
+    auto load_step = [&](int stp) {
+        const int hs = stp / ntile, t0 = c * C + (stp % ntile) * 64;
+        const int h = kv * n_rep + hs;
+        const size_t row0 = QSIDE ? ((size_t)b * n_q_heads + h) * T_len : ((size_t)b * n_kv_heads + kv) * T_len;
+#pragma unroll
+        for (int m = 0; m < 16; ++m) {
+            const int e = tid + kThreads * m, n = e >> 6, col = e & 63;
+            const bool ok = t0 + n < T_len;
+            const size_t off = (row0 + t0 + n) * OAL_D + col;
+            px[m] = ok ? oal_ld(x + off) : 0.0f;
+            if constexpr (QSIDE) pb[m] = ok ? gv[off] : 0.0f;
+            else pb[m] = ok ? oal_ld(v + off) : 0.0f;
+        }
+        if (tid < 64) {
+            const bool ok = t0 + tid < T_len;
+            if constexpr (QSIDE) pb64 = ok ? gd[row0 + t0 + tid] : 0.0f;
+            else pb64 = ok ? 1.0f : 0.0f;
+        }
+    };
+    if (nstep > 0) load_step(0);
+    int stp = 0;
     for (int hs = 0; hs < nsrc; ++hs) {
         const int h = kv * n_rep + hs;
-        const float w = QSIDE ? (f < OAL_NFEAT ? bwd_head(params, h)->wdec[f] : 0.0f) : 1.0f;
-        const size_t row0 = QSIDE ? ((size_t)b * n_q_heads + h) * T_len : ((size_t)b * n_kv_heads + kv) * T_len;
-        float ah[16], ah64 = 0.0f;                 // this head's sum of mono_f(x_n) b_n
+        oal_f32x4 D[5];
 #pragma unroll
-        for (int e = 0; e < 16; ++e) ah[e] = 0.0f;
-        for (int t0 = c * C; t0 < tend; t0 += 64) {
+        for (int ct = 0; ct < 5; ++ct) D[ct] = oal_splat(0.0f);
+        for (int t0 = c * C; t0 < tend; t0 += 64, ++stp) {
             __syncthreads();                       // the previous tile is consumed
-            stage_rows(xs, 65, x, row0, t0, T_len, 1.0f);
-            if constexpr (QSIDE) {
-                stage_g(bs, gv, gd, row0, t0, T_len);
-            } else {
-                stage_rows(bs, 68, v, row0, t0, T_len, 0.0f);
-                if (tid < 64) bs[tid * 68 + 64] = t0 + tid < T_len ? 1.0f : 0.0f;
+#pragma unroll
+            for (int m = 0; m < 16; ++m) {
+                const int e = tid + kThreads * m, n = e >> 6, col = e & 63;
+                xs[n * 65 + col] = px[m];
+                bs[n * 68 + col] = pb[m];
+            }
+            if (tid < 64) {
+                xs[tid * 65 + 64] = 1.0f;
+                bs[tid * 68 + 64] = pb64;
             }
             __syncthreads();
-            for (int n = 0; n < 64; ++n) {
+            if (stp + 1 < nstep) load_step(stp + 1);
+#pragma unroll 4
+            for (int kst = 0; kst < 16; ++kst) {
+                const int n = 4 * kst + kg;
                 const float a = xs[n * 65 + ia] * xs[n * 65 + ib];
-                const float4 *br = reinterpret_cast<const float4 *>(bs + n * 68 + cq * 16);
+                const float *br = bs + n * 68;
 #pragma unroll
-                for (int u = 0; u < 4; ++u) {
-                    const float4 bb = br[u];
-                    ah[4 * u] += a * bb.x;
-                    ah[4 * u + 1] += a * bb.y;
-                    ah[4 * u + 2] += a * bb.z;
-                    ah[4 * u + 3] += a * bb.w;
-                }
-                ah64 += a * bs[n * 68 + 64];
+                for (int ct = 0; ct < 4; ++ct)
+                    D[ct] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, br[16 * ct + lr], D[ct], 0, 0, 0);
+                D[4] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, lr == 0 ? br[64] : 0.0f, D[4], 0, 0, 0);
             }
         }
+        // fold: total += wdec_h[f] D (keys: weight 1); coefficient-gradient partial per feature
+        float wj[4];
 #pragma unroll
-        for (int e = 0; e < 16; ++e) acc[e] += w * ah[e];
-        acc64 += w * ah64;
+        for (int j = 0; j < 4; ++j)
+            wj[j] = QSIDE ? (fo + j < OAL_NFEAT ? bwd_head(params, h)->wdec[fo + j] : 0.0f) : 1.0f;
+#pragma unroll
+        for (int ct = 0; ct < 5; ++ct)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) tot[ct][j] += wj[j] * D[ct][j];
         if (coef) {
-            float pdw = cq == 0 ? s64 * ah64 : 0.0f;
 #pragma unroll
-            for (int e = 0; e < 16; ++e) pdw += sv[e] * ah[e];
-            pdw += __shfl_xor(pdw, 1);             // the four column quarters of feature f
-            pdw += __shfl_xor(pdw, 2);
-            if (cq == 0 && f < OAL_NFEAT)
-                dwp[(((size_t)b * n_q_heads + h) * nch + c) * OAL_NFEAT + f] = pdw;
+            for (int j = 0; j < 4; ++j) {
+                float pdw = 0.0f;
+#pragma unroll
+                for (int ct = 0; ct < 5; ++ct) pdw += sv[ct][j] * D[ct][j];
+                pdw += __shfl_xor(pdw, 1);         // the 16 columns of the tile row
+                pdw += __shfl_xor(pdw, 2);
+                pdw += __shfl_xor(pdw, 4);
+                pdw += __shfl_xor(pdw, 8);
+                if (lr == 0 && fo + j < OAL_NFEAT)
+                    dwp[(((size_t)b * n_q_heads + h) * nch + c) * OAL_NFEAT + fo + j] = pdw;
+            }
         }
     }
-    if (f < OAL_NFEAT) {
-        float4 *o = reinterpret_cast<float4 *>(out + (size_t)f * OAL_D + cq * 16);
 #pragma unroll
-        for (int u = 0; u < 4; ++u) o[u] = make_float4(acc[4 * u], acc[4 * u + 1], acc[4 * u + 2], acc[4 * u + 3]);
-        if (cq == 0) out[(size_t)OAL_NFEAT * OAL_D + f] = acc64;
+    for (int j = 0; j < 4; ++j) {
+        const int f = fo + j;
+        if (f < OAL_NFEAT) {
+#pragma unroll
+            for (int ct = 0; ct < 4; ++ct) out[(size_t)f * OAL_D + 16 * ct + lr] = tot[ct][j];
+            if (lr == 0) out[(size_t)OAL_NFEAT * OAL_D + f] = tot[4][j];
+        }
     }
 }
 
