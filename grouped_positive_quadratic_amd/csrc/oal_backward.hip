@@ -175,23 +175,87 @@ __device__ inline void pair_grad(const OalHeadDev *hd, int G, float e, const flo
     if (G == 64) grad_block<1>(hd, 64, e, x, y, acc);
 }
 
+// 16-byte loads of a row segment as fp32: 8 bf16 or 4 fp32 elements.
+template <typename T> struct RowVec;
+template <> struct RowVec<__bf16> {
+    static constexpr int N = 8;
+    __device__ static inline void load(const __bf16 *p, float *out) {
+        const oal_bf16x8 x = *reinterpret_cast<const oal_bf16x8 *>(p);
+#pragma unroll
+        for (int u = 0; u < 8; ++u) out[u] = (float)x[u];
+    }
+};
+template <> struct RowVec<float> {
+    static constexpr int N = 4;
+    __device__ static inline void load(const float *p, float *out) {
+        const float4 x = *reinterpret_cast<const float4 *>(p);
+        out[0] = x.x; out[1] = x.y; out[2] = x.z; out[3] = x.w;
+    }
+};
+
+// Element slot s (0..15) of this thread in a 64 x 64 tile loaded with RowVec<T>: row n, column col.
+template <typename T>
+__device__ inline void tile_slot(int s, int &n, int &col) {
+    constexpr int N = RowVec<T>::N, PER = 64 / N;       // vectors per row
+    const int e = threadIdx.x + kThreads * (s / N);
+    n = e / PER;
+    col = (e % PER) * N + s % N;
+}
+
+// This thread's 16 elements of rows t0 .. t0 + 63 (zero past T) of a [*, T, 64] tensor.
+template <typename T>
+__device__ inline void load_tile(float (&out)[16], const T *src, size_t row0, int t0, int T_len) {
+    constexpr int N = RowVec<T>::N;
+#pragma unroll
+    for (int m = 0; m < 16 / N; ++m) {
+        int n, col;
+        tile_slot<T>(m * N, n, col);
+        if (t0 + n < T_len) {
+            RowVec<T>::load(src + (row0 + t0 + n) * OAL_D + col, out + m * N);
+        } else {
+#pragma unroll
+            for (int u = 0; u < N; ++u) out[m * N + u] = 0.0f;
+        }
+    }
+}
+
+template <typename T>
+__device__ inline void store_tile(float *dst, int stride, const float (&in)[16]) {
+#pragma unroll
+    for (int s = 0; s < 16; ++s) {
+        int n, col;
+        tile_slot<T>(s, n, col);
+        dst[n * stride + col] = in[s];
+    }
+}
+
 // Stage 64 rows (tokens t0 .. t0 + 63, zero past T) of a [*, T, 64] tensor into LDS with the
 // given row stride, as fp32; column 64 (if the stride has room) gets `one`.
+// One 16-byte vector at a time, so that only a vector's worth of registers is live (the
+// callers hold large accumulator arrays).
 template <typename T>
 __device__ inline void stage_rows(float *dst, int stride, const T *src, size_t row0, int t0, int T_len, float one) {
-    for (int e = threadIdx.x; e < 64 * 64; e += kThreads) {
-        const int n = e >> 6, col = e & 63;
-        dst[n * stride + col] = t0 + n < T_len ? oal_ld(src + (row0 + t0 + n) * OAL_D + col) : 0.0f;
+    constexpr int N = RowVec<T>::N;
+#pragma unroll 1
+    for (int m = 0; m < 16 / N; ++m) {
+        int n, col;
+        tile_slot<T>(m * N, n, col);
+        float tmp[N];
+        if (t0 + n < T_len) {
+            RowVec<T>::load(src + (row0 + t0 + n) * OAL_D + col, tmp);
+        } else {
+#pragma unroll
+            for (int u = 0; u < N; ++u) tmp[u] = 0.0f;
+        }
+#pragma unroll
+        for (int u = 0; u < N; ++u) dst[n * stride + col + u] = tmp[u];
     }
     if (stride > 64 && threadIdx.x < 64) dst[threadIdx.x * stride + 64] = one;
 }
 
 // Stage 64 rows of g (64 values from gv, the 65th from gd; zero past T) with row stride 68.
 __device__ inline void stage_g(float *dst, const float *gv, const float *gd, size_t row0, int t0, int T_len) {
-    for (int e = threadIdx.x; e < 64 * 64; e += kThreads) {
-        const int n = e >> 6, col = e & 63;
-        dst[n * 68 + col] = t0 + n < T_len ? gv[(row0 + t0 + n) * OAL_D + col] : 0.0f;
-    }
+    stage_rows(dst, 68, gv, row0, t0, T_len, 0.0f);
     if (threadIdx.x < 64) dst[threadIdx.x * 68 + 64] = t0 + (int)threadIdx.x < T_len ? gd[row0 + t0 + threadIdx.x] : 0.0f;
 }
 
@@ -215,8 +279,11 @@ __global__ __launch_bounds__(kThreads) void oal_bwd_increments(int T_len, int C,
                                                                 const float *__restrict__ gd,
                                                                 const unsigned char *__restrict__ params,
                                                                 float *__restrict__ st, float *__restrict__ dwp) {
-    __shared__ float xs[64 * 65];
-    __shared__ __align__(16) float bs[64 * 68];
+    // row stride 80 (16 mod 32 banks): the four row groups of a wave's MFMA operand reads fall
+    // on two bank halves, the two-pass minimum for 64 lanes (65 or 68 gave up to 4-way conflicts)
+    constexpr int XS = 80;
+    __shared__ __align__(16) float xs[64 * XS];
+    __shared__ __align__(16) float bs[64 * XS];
     const int tid = threadIdx.x, lane = tid & 63, lr = lane & 15, kg = lane >> 4, w = wave_id();
     const int c = blockIdx.y, bkv = blockIdx.z;
     const int b = bkv / n_kv_heads, kv = bkv % n_kv_heads, n_rep = n_q_heads / n_kv_heads;
@@ -261,15 +328,9 @@ __global__ __launch_bounds__(kThreads) void oal_bwd_increments(int T_len, int C,
         const int hs = stp / ntile, t0 = c * C + (stp % ntile) * 64;
         const int h = kv * n_rep + hs;
         const size_t row0 = QSIDE ? ((size_t)b * n_q_heads + h) * T_len : ((size_t)b * n_kv_heads + kv) * T_len;
-#pragma unroll
-        for (int m = 0; m < 16; ++m) {
-            const int e = tid + kThreads * m, n = e >> 6, col = e & 63;
-            const bool ok = t0 + n < T_len;
-            const size_t off = (row0 + t0 + n) * OAL_D + col;
-            px[m] = ok ? oal_ld(x + off) : 0.0f;
-            if constexpr (QSIDE) pb[m] = ok ? gv[off] : 0.0f;
-            else pb[m] = ok ? oal_ld(v + off) : 0.0f;
-        }
+        load_tile(px, x, row0, t0, T_len);
+        if constexpr (QSIDE) load_tile(pb, gv, row0, t0, T_len);
+        else load_tile(pb, v, row0, t0, T_len);
         if (tid < 64) {
             const bool ok = t0 + tid < T_len;
             if constexpr (QSIDE) pb64 = ok ? gd[row0 + t0 + tid] : 0.0f;
@@ -285,23 +346,20 @@ __global__ __launch_bounds__(kThreads) void oal_bwd_increments(int T_len, int C,
         for (int ct = 0; ct < 5; ++ct) D[ct] = oal_splat(0.0f);
         for (int t0 = c * C; t0 < tend; t0 += 64, ++stp) {
             __syncthreads();                       // the previous tile is consumed
-#pragma unroll
-            for (int m = 0; m < 16; ++m) {
-                const int e = tid + kThreads * m, n = e >> 6, col = e & 63;
-                xs[n * 65 + col] = px[m];
-                bs[n * 68 + col] = pb[m];
-            }
+            store_tile<T>(xs, XS, px);
+            if constexpr (QSIDE) store_tile<float>(bs, XS, pb);
+            else store_tile<T>(bs, XS, pb);
             if (tid < 64) {
-                xs[tid * 65 + 64] = 1.0f;
-                bs[tid * 68 + 64] = pb64;
+                xs[tid * XS + 64] = 1.0f;
+                bs[tid * XS + 64] = pb64;
             }
             __syncthreads();
             if (stp + 1 < nstep) load_step(stp + 1);
 #pragma unroll 4
             for (int kst = 0; kst < 16; ++kst) {
                 const int n = 4 * kst + kg;
-                const float a = xs[n * 65 + ia] * xs[n * 65 + ib];
-                const float *br = bs + n * 68;
+                const float a = xs[n * XS + ia] * xs[n * XS + ib];
+                const float *br = bs + n * XS;
 #pragma unroll
                 for (int ct = 0; ct < 4; ++ct)
                     D[ct] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, br[16 * ct + lr], D[ct], 0, 0, 0);
@@ -368,7 +426,8 @@ __device__ inline bool sees(int kt, int qt, int jj, int i) { return kt < qt || j
 //    State part on fp32 MFMA (v_mfma_f32_16x16x4_f32): U = phi(Q) S_c, wave w computing the
 //    queries 16 w .. 16 w + 15 against 80 columns (five 16 x 16 tiles; the fifth holds the
 //    column 64 of S_c, the normaliser) with K over the features in blocks of 64, each block
-//    of S_c staged once in LDS. A operand: lane l holds phi_f(q) of query l % 16 and feature
+//    of S_c staged once in LDS (row stride 80: the four K rows of an operand read fall on two
+//    bank halves). A operand: lane l holds phi_f(q) of query l % 16 and feature
 //    f = 4 K-step + l / 16, built from the query tile, the head's coefficients and the dims of
 //    f (LDS tables); B operand: S_c[f][col], col = 16 tile + l % 16. The result goes to an LDS
 //    tile. Pairs inside the chunk: lane = query, the four waves split the keys.
@@ -382,7 +441,7 @@ __global__ __launch_bounds__(kThreads) void oal_bwd_readout_g(int T_len, int C, 
                                                                float *__restrict__ gd) {
     __shared__ float xq[64 * 65];
     __shared__ __align__(16) float ks[64 * 64];    // keys; before them the coefficient tables
-    __shared__ __align__(16) float vs[64 * 68];    // values; before them a block of S_c
+    __shared__ __align__(16) float vs[64 * 80];    // values; before them a block of S_c (stride 80)
     __shared__ __align__(16) float uin[64 * 68];   // state part of u per query
     const int tpc = C / 64, c = blockIdx.x / tpc, qt = blockIdx.x % tpc;
     const int h = blockIdx.y, b = blockIdx.z, n_rep = n_q_heads / n_kv_heads, kv = h / n_rep;
@@ -441,9 +500,9 @@ __global__ __launch_bounds__(kThreads) void oal_bwd_readout_g(int T_len, int C, 
 #pragma unroll
                 for (int m = 0; m < 4; ++m) {
                     const int e = threadIdx.x + kThreads * m, kk = e >> 4, c4 = (e & 15) * 4;
-                    *reinterpret_cast<float4 *>(sblk + kk * 68 + c4) = pre[m];
+                    *reinterpret_cast<float4 *>(sblk + kk * 80 + c4) = pre[m];
                 }
-                if (threadIdx.x < 64) sblk[threadIdx.x * 68 + 64] = pre64;
+                if (threadIdx.x < 64) sblk[threadIdx.x * 80 + 64] = pre64;
                 __syncthreads();
                 if (f0 + 64 < NFP) load_block(f0 + 64);
 #pragma unroll 2
@@ -452,7 +511,7 @@ __global__ __launch_bounds__(kThreads) void oal_bwd_readout_g(int T_len, int C, 
                     const unsigned short ab = fdl[f], ab2 = fdl[f + 4];
                     const float a = wdl[f] * xa[ab & 0xff] * xa[ab >> 8];
                     const float a2 = wdl[f + 4] * xa[ab2 & 0xff] * xa[ab2 >> 8];
-                    const float *brow = sblk + kk * 68, *brow2 = brow + 4 * 68;
+                    const float *brow = sblk + kk * 80, *brow2 = brow + 4 * 80;
 #pragma unroll
                     for (int ct = 0; ct < 4; ++ct) {
                         D[ct] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, brow[16 * ct + lr], D[ct], 0, 0, 0);
