@@ -126,3 +126,44 @@ def test_concurrent_streams_match_sequential():
     for i in range(2):
         assert torch.equal(ys[i], seq_out[i][0]) and torch.equal(yds[i], seq_out[i][1])
         assert torch.equal(sessions[i].state, seq_out[i][2])
+
+
+def test_backward_graph_replays_match_eager():
+    """The backward (with the coefficient gradients) enqueues kernels only: captured once, every
+    replay gives the eager call's dq, dk, dv, dL, deps bit for bit."""
+    B, Hq, Hkv, T, C = 1, 7, 1, 200, 64
+    inp = small(802, B, Hq, Hkv, T, "bf16")
+    q, k, v = (to_dev(x, "bf16") for x in (inp.q, inp.k, inp.v))
+    dims = gpq.make_dims(B, Hq, Hkv, "bf16")
+    params = torch.empty(gpq.oal_params_bytes(dims), dtype=torch.uint8, device="cuda")
+    gpq.oal_state_init(dims, gpq.HeadParamsC.from_params(inp.params), params, None)
+    dy = torch.from_numpy(np.random.default_rng(802).normal(0.0, 1.0, (B, Hq, T, 64)).astype(np.float32)).cuda()
+    ws = torch.empty(gpq.oal_prefill_backward_workspace_bytes(dims, T, C), dtype=torch.uint8, device="cuda")
+
+    def outs():
+        return [torch.empty((B, Hq, T, 64), device="cuda"), torch.empty((B, Hkv, T, 64), device="cuda"),
+                torch.empty((B, Hkv, T, 64), device="cuda"), torch.empty((Hq, 65, 65), device="cuda"),
+                torch.empty((Hq,), device="cuda")]
+
+    ref = outs()
+    gpq.oal_prefill_backward(dims, T, C, q, k, v, dy, params, ws, *ref)
+    torch.cuda.synchronize()
+    got = outs()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        gpq.oal_prefill_backward(dims, T, C, q, k, v, dy, params, ws, *got)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        gpq.oal_prefill_backward(dims, T, C, q, k, v, dy, params, ws, *got)
+    for rep in range(3):
+        for x in got:
+            x.fill_(float("nan"))
+        ws.fill_(7)                                # the workspace needs no initialisation
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for name, a, b in zip(("dq", "dk", "dv", "dL", "deps"), got, ref):
+            assert torch.equal(a, b), f"replay {rep}: {name} differs"
