@@ -18,11 +18,13 @@
 //   z_m = [m = 0] L00 + sum_r Lz[m][r] q_r k_r,   kappa = eps + sum_{m <= G} z_m^2,
 //   dkappa/dq_r = 2 k_r sum_m z_m Lz[m][r]        (and the same with q and k exchanged).
 //
-// Every kernel computes in fp32 (inputs of either dtype are widened on load). State rows are
-// read with wave-uniform addresses through the constant address space, so they arrive in
-// scalar registers and feed the FMAs directly; the per-lane operand (a query or key row) is
-// in LDS or in registers. The work is fp32 VALU: with packed fp32 off, the bound is the
-// non-packed FMA rate (256 CUs x 4 SIMDs x 16 lanes x 2 flops x 2.4 GHz = 78.6 TFLOP/s).
+// Every kernel computes in fp32 (inputs of either dtype are widened on load). The state
+// contractions run three ways: on fp32 MFMA (v_mfma_f32_16x16x4_f32; the readout gradient and
+// the chunk increments), on the VALU with blocks of state rows staged in LDS and read by
+// several heads (dq), or on the VALU with the state row read at a wave-uniform address through
+// the constant address space, so that it arrives in scalar registers and feeds the FMAs
+// directly (dk, dv). With packed fp32 off, the VALU bound is the non-packed FMA rate (256 CUs
+// x 4 SIMDs x 16 lanes x 2 flops x 2.4 GHz = 78.6 TFLOP/s); fp32 MFMA reaches 157.3.
 //
 // Launch order (all on the caller's stream):
 //   1. oal_bwd_increments<keys>:    per chunk psi(K_c)^T [V_c; 1]           -> workspace states
@@ -36,7 +38,7 @@
 //   8. oal_bwd_dk_inter, _dv_inter: dk, dv partials of the state part
 //   9. oal_bwd_kv_reduce:           dk, dv (the partials added in a fixed order)
 // With coefficient gradients, also oal_bwd_dw_intra (before 6), the per-head partials of 6,
-// and oal_bwd_coef (after 6): dL, deps.
+// and oal_bwd_dw_sum, oal_bwd_coef (after 6): dL, deps.
 #include <hip/hip_runtime.h>
 
 #include "oal_device.h"

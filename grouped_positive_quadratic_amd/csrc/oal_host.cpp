@@ -409,8 +409,11 @@ oal_status oal_contribution(const oal_dims *d, int32_t T, const void *q, const v
     return OAL_OK;
 }
 
+// grid limits of the backward's launches: chunks (dimension y of the increments and the
+// coefficient kernels), query heads and 8 workgroups per KV head (dimension y elsewhere)
 static bool backward_shape_ok(const oal_dims *d, int32_t T, int32_t chunk) {
-    return (T + chunk - 1) / chunk <= 65535 && d->n_q_heads <= 65535;
+    return (T + chunk - 1) / chunk <= 65535 && d->n_q_heads + 3 * d->n_kv_heads <= 65535 &&
+           d->n_kv_heads * 8 <= 65535;
 }
 
 size_t oal_prefill_backward_workspace_bytes(const oal_dims *d, int32_t T, int32_t chunk) {

@@ -240,11 +240,11 @@ oal_status oal_contribution(const oal_dims *dims, int32_t T, const void *q, cons
  *   params_dev -- the blob oal_state_init uploaded.
  *   workspace  -- oal_prefill_backward_workspace_bytes(dims, T, chunk) bytes of device scratch
  *                 (per-chunk states, one block of OAL_STATE_STRIDE floats per sequence, KV
- *                 head and chunk; the per-query readout gradients; partial key gradients;
- *                 partial coefficient gradients); contents on entry do not matter.
+ *                 head and chunk; the per-query readout gradients; partial dq, key and
+ *                 coefficient gradients); contents on entry do not matter.
  * All arithmetic is fp32 whatever dims->dtype is (bf16 inputs are widened on load). Every
- * pointer must be 16-byte aligned (OAL_E_ALIGN). More than 65535 chunks per sequence or
- * more than 65535 query heads give OAL_E_UNSUPPORTED. */
+ * pointer but dL and deps must be 16-byte aligned (OAL_E_ALIGN). More than 65535 chunks per sequence,
+ * n_q_heads + 3 n_kv_heads > 65535 or n_kv_heads > 8191 give OAL_E_UNSUPPORTED (grid limits). */
 size_t oal_prefill_backward_workspace_bytes(const oal_dims *dims, int32_t T, int32_t chunk);
 oal_status oal_prefill_backward(const oal_dims *dims, int32_t T, int32_t chunk, const void *q,
                                 const void *k, const void *v, const float *dy,

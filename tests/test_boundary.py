@@ -131,6 +131,7 @@ def test_validation_errors_enqueue_nothing():
     assert _code(gpq.oal_prefill_backward, d, 8, 64, A, A, A, A, A, A, A, A, A, A, A + 2, 0) == 4  # deps
     assert _code(gpq.oal_prefill_backward, d, 64 * 65536, 64, *b9, 0) == 5    # > 65535 chunks
     assert _code(gpq.oal_prefill_backward, gpq.make_dims(1, 3, 2, "bf16"), 8, 64, *b9, 0) == 2
+    assert _code(gpq.oal_prefill_backward, gpq.make_dims(1, 8192, 8192, "bf16"), 8, 64, *b9, 0) == 5  # grid
 
 
 def test_param_validation():
