@@ -1007,40 +1007,41 @@ __global__ __launch_bounds__(kThreads) void oal_bwd_kv_reduce(size_t rows, int n
 //     sum of dw over the features whose dims lie in groups g and g' (oal_bwd_coef), then
 //     dL = 2 (dLoss/dM) L and deps = dLoss/dM[0][0].
 //
-// Pairs inside chunk c for head h: workgroup = (chunk, head, sequence); thread = features
-// f = tid + 256 u. Per (query tile, key tile) pair: the tile of dkappa (masked to j <= i)
-// in LDS, then per feature dw += sum_i mono_f(q_i) sum_j dkappa_ij psi_f(k_j).
+// Pairs inside chunk c for head h: workgroup = (chunk, head, sequence). Per (query tile, key
+// tile) pair: the tile of dkappa (masked to j <= i) in LDS, then on fp32 MFMA (16x16x4)
+// Y = dkappa psi(K) (M = 64 queries in four 16-row tiles, N = features, K = 64 keys) and
+// dw[f] += sum_i mono_f(q_i) Y[i][f]. Wave w takes the feature tiles w, w + 4, ...; lane l
+// holds the A operand dkappa[16 it + l % 16][4 s + l / 16] in registers for the whole pair and
+// builds the B operand psi_f(k_j) (f = 16 ft + l % 16, j = 4 s + l / 16) from the key tile.
 template <typename T>
 __global__ __launch_bounds__(kThreads) void oal_bwd_dw_intra(int T_len, int C, int nch, int n_q_heads,
                                                               int n_kv_heads, const T *__restrict__ q,
                                                               const T *__restrict__ k, const T *__restrict__ v,
                                                               const float *__restrict__ gv, const float *__restrict__ gd,
                                                               float *__restrict__ dwp) {
-    constexpr int NU = (OAL_NFEAT + kThreads - 1) / kThreads;
+    constexpr int NFP = 2176, NFT = NFP / 16;      // features padded to 136 tiles of 16
     __shared__ __align__(16) float ta[64 * 68];   // g tile, then the query tile
-    __shared__ float tb[64 * 65];                  // v tile, then the key tile
+    __shared__ __align__(16) float tb[64 * 68];   // v tile, then the key tile
     __shared__ __align__(16) float dk[64 * 68];   // dkappa tile
+    __shared__ float dwl[NFP];                     // dw of this (chunk, head)
+    __shared__ unsigned short fdl[NFP];            // dims of feature f: a | b << 8 (64 reads the 1)
     const int tpc = C / 64, c = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
     const int n_rep = n_q_heads / n_kv_heads, kv = h / n_rep, tid = threadIdx.x;
+    const int lane = tid & 63, lr = lane & 15, kg = lane >> 4, w = wave_id();
     const size_t qrow = ((size_t)b * n_q_heads + h) * T_len, krow = ((size_t)b * n_kv_heads + kv) * T_len;
-    int fa[NU], fb[NU];                            // dims of the thread's features (64 reads the 1)
-#pragma unroll
-    for (int u = 0; u < NU; ++u) {
-        const int f = tid + kThreads * u;
-        fa[u] = OAL_D;
-        fb[u] = OAL_D;
+    for (int f = tid; f < NFP; f += kThreads) {
+        int fa = OAL_D, fb = OAL_D;
         if (f >= 1 && f <= OAL_D) {
-            fa[u] = f - 1;
+            fa = f - 1;
         } else if (f > OAL_D && f < OAL_NFEAT) {
             int idx = f - 1 - OAL_D, r = 0;
             while (idx >= OAL_D - r) { idx -= OAL_D - r; ++r; }
-            fa[u] = r;
-            fb[u] = r + idx;
+            fa = r;
+            fb = r + idx;
         }
+        fdl[f] = (unsigned short)(fa | (fb << 8));
+        dwl[f] = 0.0f;
     }
-    float acc[NU];
-#pragma unroll
-    for (int u = 0; u < NU; ++u) acc[u] = 0.0f;
     for (int qt = 0; qt < tpc; ++qt) {
         const int q0 = c * C + qt * 64;
         if (q0 >= T_len) break;
@@ -1048,13 +1049,13 @@ __global__ __launch_bounds__(kThreads) void oal_bwd_dw_intra(int T_len, int C, i
             const int k0 = c * C + kt * 64;
             __syncthreads();
             stage_g(ta, gv, gd, qrow, q0, T_len);
-            stage_rows(tb, 65, v, krow, k0, T_len, 1.0f);
+            stage_rows(tb, 68, v, krow, k0, T_len, 1.0f);
             __syncthreads();
             for (int e = tid; e < 64 * 64; e += kThreads) {
                 const int i = e >> 6, j = e & 63;
                 float x = 0.0f;
                 if (kt < qt || j <= i) {
-                    const float *gi = ta + i * 68, *vj = tb + j * 65;
+                    const float *gi = ta + i * 68, *vj = tb + j * 68;
                     float x1 = 0.0f;
                     for (int cc = 0; cc < 64; cc += 2) {
                         x += gi[cc] * vj[cc];
@@ -1065,48 +1066,46 @@ __global__ __launch_bounds__(kThreads) void oal_bwd_dw_intra(int T_len, int C, i
                 dk[i * 68 + j] = x;
             }
             __syncthreads();
-            stage_rows(ta, 65, q, qrow, q0, T_len, 1.0f);
-            stage_rows(tb, 65, k, krow, k0, T_len, 1.0f);
+            stage_rows(ta, 68, q, qrow, q0, T_len, 1.0f);
+            stage_rows(tb, 68, k, krow, k0, T_len, 1.0f);
             __syncthreads();
-            // two features per pass over the dkappa rows (each row read once per pair)
-#pragma unroll 1
-            for (int u = 0; u < NU; u += 2) {
-                if (tid + kThreads * u >= OAL_NFEAT) break;
-                const int a0 = fa[u], b0 = fb[u];
-                const int a1 = u + 1 < NU ? fa[u + 1] : OAL_D, b1 = u + 1 < NU ? fb[u + 1] : OAL_D;
-                float p0[64], p1[64];
+            float A[4][16];                        // dkappa[16 it + lr][4 s + kg]
 #pragma unroll
-                for (int j = 0; j < 64; ++j) {
-                    p0[j] = tb[j * 65 + a0] * tb[j * 65 + b0];
-                    p1[j] = tb[j * 65 + a1] * tb[j * 65 + b1];
+            for (int it = 0; it < 4; ++it)
+#pragma unroll
+                for (int st = 0; st < 16; ++st) A[it][st] = dk[(16 * it + lr) * 68 + 4 * st + kg];
+            for (int ft = w; ft < NFT; ft += 4) {
+                const int fB = 16 * ft + lr;                         // B operand feature of this lane
+                const unsigned short abB = fdl[fB];
+                oal_f32x4 D[4];
+#pragma unroll
+                for (int it = 0; it < 4; ++it) D[it] = oal_splat(0.0f);
+#pragma unroll
+                for (int st = 0; st < 16; ++st) {
+                    const float *kr = tb + (4 * st + kg) * 68;
+                    const float bpsi = kr[abB & 0xff] * kr[abB >> 8];
+#pragma unroll
+                    for (int it = 0; it < 4; ++it)
+                        D[it] = __builtin_amdgcn_mfma_f32_16x16x4f32(A[it][st], bpsi, D[it], 0, 0, 0);
                 }
-                float s0 = 0.0f, s1 = 0.0f;
-#pragma unroll 2
-                for (int i = 0; i < 64; ++i) {
-                    const float4 *dr = reinterpret_cast<const float4 *>(dk + i * 68);
-                    float y0 = 0.0f, y1 = 0.0f, z0 = 0.0f, z1 = 0.0f;
+                // D[it][jj]: query 16 it + 4 kg + jj, feature 16 ft + lr
+                float sum = 0.0f;
 #pragma unroll
-                    for (int jj = 0; jj < 16; ++jj) {
-                        const float4 d4 = dr[jj];
-                        y0 += d4.x * p0[4 * jj] + d4.z * p0[4 * jj + 2];
-                        y1 += d4.y * p0[4 * jj + 1] + d4.w * p0[4 * jj + 3];
-                        z0 += d4.x * p1[4 * jj] + d4.z * p1[4 * jj + 2];
-                        z1 += d4.y * p1[4 * jj + 1] + d4.w * p1[4 * jj + 3];
+                for (int it = 0; it < 4; ++it)
+#pragma unroll
+                    for (int jj = 0; jj < 4; ++jj) {
+                        const float *qi = ta + (16 * it + 4 * kg + jj) * 68;
+                        sum += qi[abB & 0xff] * qi[abB >> 8] * D[it][jj];
                     }
-                    const float *qi = ta + i * 65;
-                    s0 += qi[a0] * qi[b0] * (y0 + y1);
-                    s1 += qi[a1] * qi[b1] * (z0 + z1);
-                }
-                acc[u] += s0;
-                if (u + 1 < NU) acc[u + 1] += s1;
+                sum += __shfl_xor(sum, 16);                          // the four query groups
+                sum += __shfl_xor(sum, 32);
+                if (kg == 0) dwl[fB] += sum;                         // feature tile of this wave alone
             }
         }
     }
-#pragma unroll
-    for (int u = 0; u < NU; ++u) {
-        const int f = tid + kThreads * u;
-        if (f < OAL_NFEAT) dwp[(((size_t)b * n_q_heads + h) * nch + c) * OAL_NFEAT + f] = acc[u];
-    }
+    __syncthreads();
+    for (int f = tid; f < OAL_NFEAT; f += kThreads)
+        dwp[(((size_t)b * n_q_heads + h) * nch + c) * OAL_NFEAT + f] = dwl[f];
 }
 
 // dw_h[f]: the partials summed over sequences and chunks (state part, then the pairs inside
