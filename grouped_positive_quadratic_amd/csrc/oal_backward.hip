@@ -652,19 +652,35 @@ __global__ __launch_bounds__(kThreads) void oal_bwd_dq_inter(int T_len, int C, i
     if (c > 0) {                                    // S_0 = 0
         const float *S = st + ((size_t)((size_t)b * n_kv_heads + kv) * nch + c) * OAL_STATE_STRIDE;
         const float *Sd = S + (size_t)OAL_NFEAT * OAL_D;
-        for (int r = p; r < OAL_D; r += kDqSplits) {
+        // row block of r in registers one row ahead: thread's share of (65 - r) rows x 16 float4
+        // (at most 5 float4) and one normaliser entry
+        float4 pre[5];
+        float pre64 = 0.0f;
+        auto load_block = [&](int r) {
             const int base = quad_base(r), nslot = OAL_D + 1 - r;
-            __syncthreads();                        // the previous block is consumed
-            for (int e = threadIdx.x; e < nslot * 16; e += kThreads) {
-                const int k = e >> 4, c4 = (e & 15) * 4;
+#pragma unroll
+            for (int m = 0; m < 5; ++m) {
+                const int e = threadIdx.x + kThreads * m, k = e >> 4, c4 = (e & 15) * 4;
                 const int f = k == 0 ? 1 + r : base + r + k - 1;
-                *reinterpret_cast<float4 *>(sb + k * 68 + c4) = *reinterpret_cast<const float4 *>(S + (size_t)f * OAL_D + c4);
+                pre[m] = k < nslot ? *reinterpret_cast<const float4 *>(S + (size_t)f * OAL_D + c4) : make_float4(0, 0, 0, 0);
             }
             if (threadIdx.x < nslot) {
                 const int k = threadIdx.x;
-                sb[k * 68 + 64] = Sd[k == 0 ? 1 + r : base + r + k - 1];
+                pre64 = Sd[k == 0 ? 1 + r : base + r + k - 1];
             }
+        };
+        load_block(p);
+        for (int r = p; r < OAL_D; r += kDqSplits) {
+            const int base = quad_base(r), nslot = OAL_D + 1 - r;
+            __syncthreads();                        // the previous block is consumed
+#pragma unroll
+            for (int m = 0; m < 5; ++m) {
+                const int e = threadIdx.x + kThreads * m, k = e >> 4, c4 = (e & 15) * 4;
+                if (k < nslot) *reinterpret_cast<float4 *>(sb + k * 68 + c4) = pre[m];
+            }
+            if (threadIdx.x < nslot) sb[threadIdx.x * 68 + 64] = pre64;
             __syncthreads();
+            if (r + kDqSplits < OAL_D) load_block(r + kDqSplits);
             if (active) {
                 float qr = 0.0f;                    // qv[r] by selection: a dynamic index would
 #pragma unroll                                      // move the arrays to scratch memory
