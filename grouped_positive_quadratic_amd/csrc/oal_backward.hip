@@ -664,7 +664,7 @@ __global__ __launch_bounds__(kThreads) void oal_bwd_dq_inter(int T_len, int C, i
                 const int f = k == 0 ? 1 + r : base + r + k - 1;
                 pre[m] = k < nslot ? *reinterpret_cast<const float4 *>(S + (size_t)f * OAL_D + c4) : make_float4(0, 0, 0, 0);
             }
-            if (threadIdx.x < nslot) {
+            if ((int)threadIdx.x < nslot) {
                 const int k = threadIdx.x;
                 pre64 = Sd[k == 0 ? 1 + r : base + r + k - 1];
             }
@@ -678,7 +678,7 @@ __global__ __launch_bounds__(kThreads) void oal_bwd_dq_inter(int T_len, int C, i
                 const int e = threadIdx.x + kThreads * m, k = e >> 4, c4 = (e & 15) * 4;
                 if (k < nslot) *reinterpret_cast<float4 *>(sb + k * 68 + c4) = pre[m];
             }
-            if (threadIdx.x < nslot) sb[threadIdx.x * 68 + 64] = pre64;
+            if ((int)threadIdx.x < nslot) sb[threadIdx.x * 68 + 64] = pre64;
             __syncthreads();
             if (r + kDqSplits < OAL_D) load_block(r + kDqSplits);
             if (active) {
