@@ -30,7 +30,7 @@
 //   1. oal_bwd_increments<keys>:    per chunk psi(K_c)^T [V_c; 1]           -> workspace states
 //   2. oal_bwd_scan (forward):      exclusive prefix over chunks: S_c
 //   3. oal_bwd_readout_g:           u_i (inter + intra), y, den -> g_i     -> workspace g
-//   4. oal_bwd_dq_inter, oal_bwd_sum_parts, oal_bwd_dq_intra: dq (state part in four row
+//   4. oal_bwd_dq_inter, oal_bwd_sum_parts, oal_bwd_dq_intra_mfma: dq (state part in four row
 //      splits, their sum, then the pairs inside the chunk)
 //   5. oal_bwd_dkv_intra:           dk, dv partials of the pairs inside the chunk
 //   6. oal_bwd_increments<queries>: per chunk sum_h phi_h(Q_c)^T G_c       -> workspace states
@@ -121,23 +121,6 @@ __device__ inline float pair_kappa(const OalHeadDev *hd, int G, const float *x, 
     return kap;
 }
 
-template <int NB>
-__device__ inline void grad_block(const OalHeadDev *hd, int m0, float e, const float *x, const float *y,
-                                  float (&acc)[64]) {
-    float z[NB];
-    z_block<NB>(hd, m0, x, y, z);
-    const cfloat *Lz = uni(hd->Lz) + m0 * OAL_D;
-#pragma unroll
-    for (int mm = 0; mm < NB; ++mm) z[mm] *= 2.0f * e;
-#pragma unroll
-    for (int r = 0; r < OAL_D; ++r) {
-        float s = 0.0f;
-#pragma unroll
-        for (int mm = 0; mm < NB; ++mm) s += z[mm] * Lz[mm * OAL_D + r];
-        acc[r] += s * y[r];
-    }
-}
-
 // Both at once for one pair: returns kappa and adds e * dkappa/dx to acc (one z per block).
 template <int NB>
 __device__ inline float kappa_grad_block(const OalHeadDev *hd, int m0, float e, const float *x, const float *y,
@@ -169,13 +152,6 @@ __device__ inline float pair_kappa_grad(const OalHeadDev *hd, int G, float e, co
     return kap;
 }
 
-// acc[r] += e * y[r] * 2 sum_m z_m Lz[m][r]: the pair's dkappa/dx scaled by e (dkappa), with
-// x the lane's operand and y the other side's row (wave-uniform).
-__device__ inline void pair_grad(const OalHeadDev *hd, int G, float e, const float *x, const float *y,
-                                 float (&acc)[64]) {
-    for (int m0 = 0; m0 <= min(G, 63); m0 += kMBlock) grad_block<kMBlock>(hd, m0, e, x, y, acc);
-    if (G == 64) grad_block<1>(hd, 64, e, x, y, acc);
-}
 
 // 16-byte loads of a row segment as fp32: 8 bf16 or 4 fp32 elements.
 template <typename T> struct RowVec;
@@ -720,77 +696,116 @@ __global__ __launch_bounds__(kThreads) void oal_bwd_sum_parts(size_t n4, int npa
     reinterpret_cast<float4 *>(out)[e] = s;
 }
 
-// 4b. dq_i += sum_{j <= i in the chunk} dkappa_ij dkappa_ij/dq_i, dkappa_ij = g_i . [v_j; 1].
-//     Same workgroups as 4a (launched after it); the four waves take the keys j = w (mod 4).
+// 4b. dq_i += sum_{j <= i in the chunk} dkappa_ij dkappa_ij/dq_i, dkappa_ij = g_i . [v_j; 1], on
+//     fp32 MFMA (16x16x4). dkappa/dq_ir = 2 k_jr sum_m z_m Lz[m][r] with
+//     z_m = (Q diag(Lz[m]) K^T)_ij (+ L00 for m = 0), so per (query tile, key tile) pair and
+//     z-term m: Z_m = (Q o Lz[m]) K^T, E_m = dkappa o Z_m (the dkappa tile is masked to
+//     j <= i), dq += 2 Lz[m] o (E_m K) -- two 64 x 64 x 64 products. Wave w owns the queries
+//     16 w .. 16 w + 15 of every product; E_m passes through LDS (the wave's own rows) to become
+//     the A operand of the second. Rows of Lz past G are zero, so m runs to G.
 template <typename T>
-__global__ __launch_bounds__(kThreads) void oal_bwd_dq_intra(int T_len, int C, int n_q_heads, int n_kv_heads,
-                                                              const T *__restrict__ q, const T *__restrict__ k,
-                                                              const T *__restrict__ v, const unsigned char *__restrict__ params,
-                                                              const float *__restrict__ gv, const float *__restrict__ gd,
-                                                              float *__restrict__ dq) {
-    __shared__ float xq[64 * 65];
-    __shared__ float ks[64 * 64];
-    __shared__ __align__(16) float vs[64 * 68];
+__global__ __launch_bounds__(kThreads) void oal_bwd_dq_intra_mfma(int T_len, int C, int n_q_heads, int n_kv_heads,
+                                                                   const T *__restrict__ q, const T *__restrict__ k,
+                                                                   const T *__restrict__ v,
+                                                                   const unsigned char *__restrict__ params,
+                                                                   const float *__restrict__ gv,
+                                                                   const float *__restrict__ gd, float *__restrict__ dq) {
+    __shared__ __align__(16) float ks[64 * 68];
+    __shared__ __align__(16) float dks[64 * 68];   // dkappa tile
+    __shared__ __align__(16) float gs[64 * 68];    // g tile, then E_m
+    __shared__ __align__(16) float vs[64 * 68];    // v tile, then the query tile
+    float *qs = vs;
     const int tpc = C / 64, c = blockIdx.x / tpc, qt = blockIdx.x % tpc;
     const int h = blockIdx.y, b = blockIdx.z, n_rep = n_q_heads / n_kv_heads, kv = h / n_rep;
-    const int i = threadIdx.x & 63, w = wave_id();
-    const int t0 = c * C + qt * 64, t = t0 + i;
-    const bool valid = t < T_len;
+    const int tid = threadIdx.x, lane = tid & 63, lr = lane & 15, kg = lane >> 4, w = wave_id();
+    const int t0 = c * C + qt * 64;
     const OalHeadDev *hd = bwd_head(params, h);
     const int G = hd->G;
+    const float L00 = hd->L00;
+    const float *Lz = hd->Lz;
     const size_t qrow = ((size_t)b * n_q_heads + h) * T_len, krow = ((size_t)b * n_kv_heads + kv) * T_len;
-    stage_rows(xq, 65, q, qrow, t0, T_len, 1.0f);
-    float g[65];
+    if (t0 >= T_len) return;                       // a tile past the sequence (uniform)
+    oal_f32x4 acc[4];                              // dq: query 16 w + 4 kg + j, dim 16 rt + lr
 #pragma unroll
-    for (int e = 0; e < 64; e += 4) {
-        const float4 g4 = valid ? *reinterpret_cast<const float4 *>(gv + (qrow + t) * OAL_D + e) : make_float4(0, 0, 0, 0);
-        g[e] = g4.x; g[e + 1] = g4.y; g[e + 2] = g4.z; g[e + 3] = g4.w;
-    }
-    g[64] = valid ? gd[qrow + t] : 0.0f;
-    const float *xi = xq + i * 65;
-    float d[64];
-#pragma unroll
-    for (int e = 0; e < 64; ++e) d[e] = 0.0f;
+    for (int rt = 0; rt < 4; ++rt) acc[rt] = oal_splat(0.0f);
     for (int kt = 0; kt <= qt; ++kt) {
         const int k0 = c * C + kt * 64;
-        __syncthreads();
-        stage_rows(ks, 64, k, krow, k0, T_len, 0.0f);
+        __syncthreads();                           // previous pair consumed
+        stage_g(gs, gv, gd, qrow, t0, T_len);
         stage_rows(vs, 68, v, krow, k0, T_len, 1.0f);
+        stage_rows(ks, 68, k, krow, k0, T_len, 0.0f);
         __syncthreads();
-        if (valid) {
-            for (int jj = w; jj < 64; jj += 4) {
-                if (!sees(kt, qt, jj, i)) continue;
-                const float4 *vr = reinterpret_cast<const float4 *>(vs + jj * 68);
-                float e0 = g[64], e1 = 0.0f;
-#pragma unroll
-                for (int u = 0; u < 16; ++u) {
-                    const float4 vv = vr[u];
-                    e0 += g[4 * u] * vv.x + g[4 * u + 2] * vv.z;
-                    e1 += g[4 * u + 1] * vv.y + g[4 * u + 3] * vv.w;
+        for (int e = tid; e < 64 * 64; e += kThreads) {
+            const int i = e >> 6, j = e & 63;
+            float x = 0.0f;
+            if (kt < qt || j <= i) {
+                const float *gi = gs + i * 68, *vj = vs + j * 68;
+                float x1 = 0.0f;
+                for (int cc = 0; cc < 64; cc += 2) {
+                    x += gi[cc] * vj[cc];
+                    x1 += gi[cc + 1] * vj[cc + 1];
                 }
-                pair_grad(hd, G, e0 + e1, xi, ks + jj * 64, d);
+                x += x1 + gi[64];
             }
+            dks[i * 68 + j] = x;
         }
-    }
-    float *red = vs;
-    for (int s = 0; s < 4; ++s) {
+        __syncthreads();                           // dkappa ready; gs and vs are free
+        stage_rows(qs, 68, q, qrow, t0, T_len, 0.0f);
         __syncthreads();
-        if (w == s) {
+        float *es = gs;
+        for (int m = 0; m <= G; ++m) {
+            const float *lzm = Lz + m * OAL_D;
+            // Z_m for the wave's 16 queries x 64 keys
+            oal_f32x4 Z[4];
 #pragma unroll
-            for (int e = 0; e < 64; ++e) red[i * 65 + e] = (s == 0 ? 0.0f : red[i * 65 + e]) + d[e];
+            for (int jt = 0; jt < 4; ++jt) Z[jt] = oal_splat(m == 0 ? L00 : 0.0f);
+#pragma unroll 4
+            for (int st = 0; st < 16; ++st) {
+                const int r = 4 * st + kg;
+                const float a = qs[(16 * w + lr) * 68 + r] * lzm[r];
+#pragma unroll
+                for (int jt = 0; jt < 4; ++jt)
+                    Z[jt] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, ks[(16 * jt + lr) * 68 + r], Z[jt], 0, 0, 0);
+            }
+            // E_m = dkappa o Z_m into the wave's rows of es (row = query, column = key)
+#pragma unroll
+            for (int jt = 0; jt < 4; ++jt)
+#pragma unroll
+                for (int jj = 0; jj < 4; ++jj) {
+                    const int i = 16 * w + 4 * kg + jj, j = 16 * jt + lr;
+                    es[i * 68 + j] = dks[i * 68 + j] * Z[jt][jj];
+                }
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");   // the wave reads its own rows
+            __builtin_amdgcn_s_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+            // F = E_m K for the wave's 16 queries x 64 dims, then dq += 2 Lz[m][r] F
+            oal_f32x4 F[4];
+#pragma unroll
+            for (int rt = 0; rt < 4; ++rt) F[rt] = oal_splat(0.0f);
+#pragma unroll 4
+            for (int st = 0; st < 16; ++st) {
+                const int j = 4 * st + kg;
+                const float a = es[(16 * w + lr) * 68 + j];
+#pragma unroll
+                for (int rt = 0; rt < 4; ++rt)
+                    F[rt] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, ks[j * 68 + 16 * rt + lr], F[rt], 0, 0, 0);
+            }
+#pragma unroll
+            for (int rt = 0; rt < 4; ++rt) {
+                const float l2 = 2.0f * lzm[16 * rt + lr];
+#pragma unroll
+                for (int jj = 0; jj < 4; ++jj) acc[rt][jj] += l2 * F[rt][jj];
+            }
+            __builtin_amdgcn_s_barrier();           // es rows rewritten by the next m
         }
     }
-    __syncthreads();
-    if (valid) {
-        float *o = dq + (qrow + t) * OAL_D + w * 16;
-        const float *src = red + i * 65 + w * 16;
 #pragma unroll
-        for (int e = 0; e < 16; e += 4) {
-            float4 x = *reinterpret_cast<float4 *>(o + e);
-            x.x += src[e]; x.y += src[e + 1]; x.z += src[e + 2]; x.w += src[e + 3];
-            *reinterpret_cast<float4 *>(o + e) = x;
+    for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+            const int t = t0 + 16 * w + 4 * kg + jj;
+            if (t < T_len) dq[(qrow + t) * OAL_D + 16 * rt + lr] += acc[rt][jj];
         }
-    }
 }
 
 // 7. dk and dv. Each 64-key tile is covered by:
@@ -1238,7 +1253,7 @@ hipError_t launch_backward(const oal_dims &d, int T_len, int C, const void *q_, 
         hipLaunchKernelGGL(oal_bwd_sum_parts, dim3((unsigned)((n4 + kThreads - 1) / kThreads)), blk, 0, stream, n4,
                            kDqSplits, dqp, dq);
     }
-    hipLaunchKernelGGL(oal_bwd_dq_intra<T>, g_q, blk, 0, stream, T_len, C, Hq, Hkv, q, k, v, params, gv, gd, dq);
+    hipLaunchKernelGGL(oal_bwd_dq_intra_mfma<T>, g_q, blk, 0, stream, T_len, C, Hq, Hkv, q, k, v, params, gv, gd, dq);
     hipLaunchKernelGGL(oal_bwd_dkv_intra<T>, g_kh, blk, 0, stream, T_len, C, Hq, Hkv, q, k, v, params, gv, gd, part);
     if (coef)
         hipLaunchKernelGGL(oal_bwd_dw_intra<T>, dim3(nch, Hq, B), blk, 0, stream, T_len, C, nch, Hq, Hkv, q, k, v,
