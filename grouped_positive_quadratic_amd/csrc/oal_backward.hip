@@ -32,7 +32,7 @@
 //   3. oal_bwd_readout_g:           u_i (inter + intra), y, den -> g_i     -> workspace g
 //   4. oal_bwd_dq_inter, oal_bwd_sum_parts, oal_bwd_dq_intra_mfma: dq (state part in four row
 //      splits, their sum, then the pairs inside the chunk)
-//   5. oal_bwd_dkv_intra:           dk, dv partials of the pairs inside the chunk
+//   5. oal_bwd_dkv_intra_mfma:      dk, dv partials of the pairs inside the chunk
 //   6. oal_bwd_increments<queries>: per chunk sum_h phi_h(Q_c)^T G_c       -> workspace states
 //   7. oal_bwd_scan (reverse):      exclusive suffix over chunks: R_c
 //   8. oal_bwd_dk_inter, _dv_inter: dk, dv partials of the state part
@@ -121,36 +121,6 @@ __device__ inline float pair_kappa(const OalHeadDev *hd, int G, const float *x, 
     return kap;
 }
 
-// Both at once for one pair: returns kappa and adds e * dkappa/dx to acc (one z per block).
-template <int NB>
-__device__ inline float kappa_grad_block(const OalHeadDev *hd, int m0, float e, const float *x, const float *y,
-                                         float (&acc)[64]) {
-    float z[NB];
-    z_block<NB>(hd, m0, x, y, z);
-    const cfloat *Lz = uni(hd->Lz) + m0 * OAL_D;
-    float kap = 0.0f;
-#pragma unroll
-    for (int mm = 0; mm < NB; ++mm) {
-        kap += z[mm] * z[mm];
-        z[mm] *= 2.0f * e;
-    }
-#pragma unroll
-    for (int r = 0; r < OAL_D; ++r) {
-        float s = 0.0f;
-#pragma unroll
-        for (int mm = 0; mm < NB; ++mm) s += z[mm] * Lz[mm * OAL_D + r];
-        acc[r] += s * y[r];
-    }
-    return kap;
-}
-
-__device__ inline float pair_kappa_grad(const OalHeadDev *hd, int G, float e, const float *x, const float *y,
-                                        float (&acc)[64]) {
-    float kap = hd->eps;
-    for (int m0 = 0; m0 <= min(G, 63); m0 += kMBlock) kap += kappa_grad_block<kMBlock>(hd, m0, e, x, y, acc);
-    if (G == 64) kap += kappa_grad_block<1>(hd, 64, e, x, y, acc);
-    return kap;
-}
 
 
 // 16-byte loads of a row segment as fp32: 8 bf16 or 4 fp32 elements.
@@ -813,7 +783,7 @@ __global__ __launch_bounds__(kThreads) void oal_bwd_dq_intra_mfma(int T_len, int
 //      splits (worker 4 p + w) take the feature-row pairs {worker, 63 - worker} (65 features
 //      each) of the state part: dv_j += psi_f(k_j) R_c[f][0:64], dk_j += (R_c[f] . [v_j; 1])
 //      dpsi_f/dk_j;
-//    - one workgroup of oal_bwd_dkv_intra per query head h of the KV head: the pairs inside the
+//    - one workgroup of oal_bwd_dkv_intra_mfma per query head h of the KV head: the pairs inside the
 //      chunk, i >= j, with the waves on the queries i = w (mod 4): dv_j += kappa_ij g_i[0:64],
 //      dk_j += dkappa_ij dkappa_ij/dk_j.
 //    Each writes a partial row of 128 floats (dk, then dv) per key into part[slot]: slots
@@ -937,82 +907,146 @@ __global__ __launch_bounds__(kThreads) void oal_bwd_dv_inter(int T_len, int C, i
     }
 }
 
+
+// dk and dv pairs inside the chunk for one query head, on fp32 MFMA (16x16x4). Workgroup =
+// (64-key tile, query head, sequence); wave w owns the keys 16 w .. 16 w + 15 of every product.
+// Per query tile (qt >= kt) and z-term m: Z_m = (K o Lz[m]) Q^T (keys x queries, + L00 for
+// m = 0), kappa += Z_m^2, E_m = dkappa^T o Z_m, dk += 2 Lz[m] o (E_m Q); after the z-terms,
+// kappa = eps + sum_m Z_m^2 on the pairs that see each other, and dv += kappa G. E_m and kappa
+// pass through LDS (the wave's own rows) to become A operands. Writes part[8 + head slot].
 template <typename T>
-__global__ __launch_bounds__(kThreads) void oal_bwd_dkv_intra(int T_len, int C, int n_q_heads, int n_kv_heads,
-                                                               const T *__restrict__ q, const T *__restrict__ k,
-                                                               const T *__restrict__ v,
-                                                               const unsigned char *__restrict__ params,
-                                                               const float *__restrict__ gv, const float *__restrict__ gd,
-                                                               float *__restrict__ part) {
-    __shared__ float xk[64 * 65];
-    __shared__ float xv[64 * 65];
-    __shared__ float qs[64 * 64];
-    __shared__ __align__(16) float gs[64 * 68];
+__global__ __launch_bounds__(kThreads) void oal_bwd_dkv_intra_mfma(int T_len, int C, int n_q_heads, int n_kv_heads,
+                                                                    const T *__restrict__ q, const T *__restrict__ k,
+                                                                    const T *__restrict__ v,
+                                                                    const unsigned char *__restrict__ params,
+                                                                    const float *__restrict__ gv,
+                                                                    const float *__restrict__ gd, float *__restrict__ part) {
+    __shared__ __align__(16) float ks[64 * 68];    // key tile (row = key)
+    __shared__ __align__(16) float qs[64 * 68];    // query tile (row = query)
+    __shared__ __align__(16) float gs[64 * 68];    // g tile (row = query, column 64 = g64)
+    __shared__ __align__(16) float es[64 * 68];    // v tile, then E_m, then kappa (row = key, col = query)
     const int tpc = C / 64, c = blockIdx.x / tpc, kt = blockIdx.x % tpc;
     const int n_rep = n_q_heads / n_kv_heads;
     const int hs = blockIdx.y % n_rep, kv = blockIdx.y / n_rep, b = blockIdx.z, h = kv * n_rep + hs;
-    const int j = threadIdx.x & 63, w = wave_id();
-    const int t0 = c * C + kt * 64, t = t0 + j;
-    const bool valid = t < T_len;
+    const int tid = threadIdx.x, lane = tid & 63, lr = lane & 15, kg = lane >> 4, w = wave_id();
+    const int t0 = c * C + kt * 64;
     const size_t krow = ((size_t)b * n_kv_heads + kv) * T_len, rows = (size_t)gridDim.z * n_kv_heads * T_len;
     const size_t qrow = ((size_t)b * n_q_heads + h) * T_len;
     const OalHeadDev *hd = bwd_head(params, h);
     const int G = hd->G;
-    stage_rows(xk, 65, k, krow, t0, T_len, 1.0f);
-    stage_rows(xv, 65, v, krow, t0, T_len, 1.0f);
-    const float *xj = xk + j * 65, *vjl = xv + j * 65;
-    float d[64], a[64];
+    const float L00 = hd->L00, eps = hd->eps;
+    const float *Lz = hd->Lz;
+    if (t0 >= T_len) return;                       // a tile past the sequence (uniform)
+    oal_f32x4 dkacc[4], dvacc[4];                  // key 16 w + 4 kg + jj, dim / column 16 rt + lr
 #pragma unroll
-    for (int e = 0; e < 64; ++e) d[e] = a[e] = 0.0f;
+    for (int rt = 0; rt < 4; ++rt) dkacc[rt] = dvacc[rt] = oal_splat(0.0f);
     for (int qt = kt; qt < tpc; ++qt) {
         const int q0 = c * C + qt * 64;
         if (q0 >= T_len) break;
-        __syncthreads();
-        stage_rows(qs, 64, q, qrow, q0, T_len, 0.0f);
+        __syncthreads();                           // previous tile consumed
+        stage_rows(ks, 68, k, krow, t0, T_len, 0.0f);
+        stage_rows(qs, 68, q, qrow, q0, T_len, 0.0f);
         stage_g(gs, gv, gd, qrow, q0, T_len);
+        stage_rows(es, 68, v, krow, t0, T_len, 1.0f);
         __syncthreads();
-        if (valid) {
-            for (int ii = w; ii < 64; ii += 4) {
-                if (!sees(kt, qt, j, ii)) continue;   // key j of tile kt, query ii of tile qt
-                const float *gr = gs + ii * 68;
-                float e0 = gr[64], e1 = 0.0f;
+        // dkappa[i][j] = g_i . [v_j; 1] on the pairs j <= i, in the accumulator layout:
+        // dkr[it][jj] for key j = 16 w + 4 kg + jj, query i = 16 it + lr
+        float dkr[4][4];
 #pragma unroll
-                for (int u = 0; u < 64; u += 2) {
-                    e0 += gr[u] * vjl[u];
-                    e1 += gr[u + 1] * vjl[u + 1];
-                }
-                const float kap = pair_kappa_grad(hd, G, e0 + e1, xj, qs + ii * 64, d);
-                const float4 *g4 = reinterpret_cast<const float4 *>(gr);
+        for (int it = 0; it < 4; ++it)
 #pragma unroll
-                for (int u = 0; u < 16; ++u) {
-                    const float4 gg = g4[u];
-                    a[4 * u] += kap * gg.x;
-                    a[4 * u + 1] += kap * gg.y;
-                    a[4 * u + 2] += kap * gg.z;
-                    a[4 * u + 3] += kap * gg.w;
+            for (int jj = 0; jj < 4; ++jj) {
+                const int j = 16 * w + 4 * kg + jj, i = 16 * it + lr;
+                float x = 0.0f;
+                if (kt < qt || j <= i) {
+                    const float *gi = gs + i * 68, *vj = es + j * 68;
+                    float x1 = 0.0f;
+                    for (int cc = 0; cc < 64; cc += 2) {
+                        x += gi[cc] * vj[cc];
+                        x1 += gi[cc + 1] * vj[cc + 1];
+                    }
+                    x += x1 + gi[64];
                 }
+                dkr[it][jj] = x;
             }
+        __syncthreads();                           // the v tile is consumed
+        oal_f32x4 kap[4];                          // sum_m Z_m^2: key 16 w + 4 kg + jj, query 16 it + lr
+#pragma unroll
+        for (int it = 0; it < 4; ++it) kap[it] = oal_splat(0.0f);
+        for (int m = 0; m <= G; ++m) {
+            const float *lzm = Lz + m * OAL_D;
+            oal_f32x4 Z[4];
+#pragma unroll
+            for (int it = 0; it < 4; ++it) Z[it] = oal_splat(m == 0 ? L00 : 0.0f);
+#pragma unroll 4
+            for (int st = 0; st < 16; ++st) {
+                const int r = 4 * st + kg;
+                const float a = ks[(16 * w + lr) * 68 + r] * lzm[r];
+#pragma unroll
+                for (int it = 0; it < 4; ++it)
+                    Z[it] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, qs[(16 * it + lr) * 68 + r], Z[it], 0, 0, 0);
+            }
+#pragma unroll
+            for (int it = 0; it < 4; ++it)
+#pragma unroll
+                for (int jj = 0; jj < 4; ++jj) {
+                    const int j = 16 * w + 4 * kg + jj, i = 16 * it + lr;
+                    kap[it][jj] += Z[it][jj] * Z[it][jj];
+                    es[j * 68 + i] = dkr[it][jj] * Z[it][jj];
+                }
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");   // the wave reads its own rows
+            __builtin_amdgcn_s_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+            oal_f32x4 F[4];
+#pragma unroll
+            for (int rt = 0; rt < 4; ++rt) F[rt] = oal_splat(0.0f);
+#pragma unroll 4
+            for (int st = 0; st < 16; ++st) {
+                const int i = 4 * st + kg;
+                const float a = es[(16 * w + lr) * 68 + i];
+#pragma unroll
+                for (int rt = 0; rt < 4; ++rt)
+                    F[rt] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, qs[i * 68 + 16 * rt + lr], F[rt], 0, 0, 0);
+            }
+#pragma unroll
+            for (int rt = 0; rt < 4; ++rt) {
+                const float l2 = 2.0f * lzm[16 * rt + lr];
+#pragma unroll
+                for (int jj = 0; jj < 4; ++jj) dkacc[rt][jj] += l2 * F[rt][jj];
+            }
+            __builtin_amdgcn_s_barrier();           // es rows rewritten next
+        }
+        // kappa on the visible pairs, then dv += kappa G
+#pragma unroll
+        for (int it = 0; it < 4; ++it)
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) {
+                const int j = 16 * w + 4 * kg + jj, i = 16 * it + lr;
+                es[j * 68 + i] = (kt < qt || j <= i) ? eps + kap[it][jj] : 0.0f;
+            }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+        __builtin_amdgcn_s_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+#pragma unroll 4
+        for (int st = 0; st < 16; ++st) {
+            const int i = 4 * st + kg;
+            const float a = es[(16 * w + lr) * 68 + i];
+#pragma unroll
+            for (int rt = 0; rt < 4; ++rt)
+                dvacc[rt] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, gs[i * 68 + 16 * rt + lr], dvacc[rt], 0, 0, 0);
         }
     }
-    float *dkr = xv, *dvr = gs;                     // reuse: the v and g tiles are consumed
-    for (int s = 0; s < 4; ++s) {
-        __syncthreads();
-        if (w == s) {
 #pragma unroll
-            for (int e = 0; e < 64; ++e) {
-                dkr[j * 65 + e] = (s == 0 ? 0.0f : dkr[j * 65 + e]) + d[e];
-                dvr[j * 65 + e] = (s == 0 ? 0.0f : dvr[j * 65 + e]) + a[e];
+    for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+            const int t = t0 + 16 * w + 4 * kg + jj;
+            if (t < T_len) {
+                float *o = part_row(part, kInterSplits + hs, rows, krow + t);
+                o[16 * rt + lr] = dkacc[rt][jj];
+                o[64 + 16 * rt + lr] = dvacc[rt][jj];
             }
         }
-    }
-    __syncthreads();
-    if (valid) {
-        float *o = part_row(part, kInterSplits + hs, rows, krow + t) + w * 32;
-        const float *src = (w < 2 ? dkr : dvr) + j * 65 + (w & 1) * 32;
-#pragma unroll
-        for (int e = 0; e < 32; e += 4)
-            *reinterpret_cast<float4 *>(o + e) = make_float4(src[e], src[e + 1], src[e + 2], src[e + 3]);
-    }
 }
 
 // Sum the nslots partial rows in slot order: dk, dv [rows][64] from part [slot][rows][128].
@@ -1254,7 +1288,8 @@ hipError_t launch_backward(const oal_dims &d, int T_len, int C, const void *q_, 
                            kDqSplits, dqp, dq);
     }
     hipLaunchKernelGGL(oal_bwd_dq_intra_mfma<T>, g_q, blk, 0, stream, T_len, C, Hq, Hkv, q, k, v, params, gv, gd, dq);
-    hipLaunchKernelGGL(oal_bwd_dkv_intra<T>, g_kh, blk, 0, stream, T_len, C, Hq, Hkv, q, k, v, params, gv, gd, part);
+    hipLaunchKernelGGL(oal_bwd_dkv_intra_mfma<T>, g_kh, blk, 0, stream, T_len, C, Hq, Hkv, q, k, v, params, gv, gd,
+                       part);
     if (coef)
         hipLaunchKernelGGL(oal_bwd_dw_intra<T>, dim3(nch, Hq, B), blk, 0, stream, T_len, C, nch, Hq, Hkv, q, k, v,
                            gv, gd, dwp + (size_t)B * Hq * nch * OAL_NFEAT);
