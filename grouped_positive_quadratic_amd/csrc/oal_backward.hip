@@ -16,7 +16,8 @@
 // R_c sums phi_h(q_i) g_i^T over the chunks after c and the query heads h of the KV head.
 // Inside a chunk kappa is taken from its z-terms, as in the forward's intra-chunk part:
 //   z_m = [m = 0] L00 + sum_r Lz[m][r] q_r k_r,   kappa = eps + sum_{m <= G} z_m^2,
-//   dkappa/dq_r = 2 k_r sum_m z_m Lz[m][r]        (and the same with q and k exchanged).
+//   dkappa/dq_r = 2 k_r sum_m z_m Lz[m][r]        (and the same with q and k exchanged);
+// for a (query tile, key tile) pair each z-term is the product (Q o Lz[m]) K^T on MFMA.
 //
 // Every kernel computes in fp32 (inputs of either dtype are widened on load). The state
 // contractions run three ways: on fp32 MFMA (v_mfma_f32_16x16x4_f32; the readout gradient and
@@ -48,7 +49,6 @@ namespace {
 
 constexpr int kThreads = 256;                 // four waves
 constexpr int kFeatBlock = 64;                // features per increment workgroup
-constexpr int kMBlock = 8;                    // z-terms kept in registers at a time
 
 typedef const float __attribute__((address_space(4))) cfloat;   // wave-uniform reads
 
@@ -86,40 +86,7 @@ __device__ inline void row_axpy(float (&acc)[NC], float a, const cfloat *S, cons
     if constexpr (NC == 65) acc[64] += a * Sd[f];
 }
 
-// z-terms m0 .. m0 + NB - 1 of the pair (x, y): z_m = [m = 0] L00 + sum_r Lz[m][r] x_r y_r.
-// x is lane-distinct (stride-65 LDS row), y wave-uniform (LDS row, broadcast). Rows of Lz
-// past the head's G are zero, so a block may run past G; blocks never pass row 64.
-template <int NB>
-__device__ inline void z_block(const OalHeadDev *hd, int m0, const float *x, const float *y, float (&z)[NB]) {
-    const cfloat *Lz = uni(hd->Lz) + m0 * OAL_D;
-#pragma unroll
-    for (int mm = 0; mm < NB; ++mm) z[mm] = 0.0f;
-    if (m0 == 0) z[0] = hd->L00;
-#pragma unroll 8
-    for (int r = 0; r < OAL_D; ++r) {
-        const float p = x[r] * y[r];
-#pragma unroll
-        for (int mm = 0; mm < NB; ++mm) z[mm] += Lz[mm * OAL_D + r] * p;
-    }
-}
 
-// kappa of the pair (x, y) (same operand placement as z_block): blocks of kMBlock z-terms
-// cover m = 0 .. 63; row 64 exists only when G = 64.
-__device__ inline float pair_kappa(const OalHeadDev *hd, int G, const float *x, const float *y) {
-    float kap = hd->eps;
-    for (int m0 = 0; m0 <= min(G, 63); m0 += kMBlock) {
-        float z[kMBlock];
-        z_block<kMBlock>(hd, m0, x, y, z);
-#pragma unroll
-        for (int mm = 0; mm < kMBlock; ++mm) kap += z[mm] * z[mm];
-    }
-    if (G == 64) {
-        float z[1];
-        z_block<1>(hd, 64, x, y, z);
-        kap += z[0] * z[0];
-    }
-    return kap;
-}
 
 
 
@@ -388,7 +355,7 @@ __global__ __launch_bounds__(kThreads) void oal_bwd_readout_g(int T_len, int C, 
                                                                const float *__restrict__ st, float *__restrict__ gv,
                                                                float *__restrict__ gd) {
     __shared__ float xq[64 * 65];
-    __shared__ __align__(16) float ks[64 * 64];    // keys; before them the coefficient tables
+    __shared__ __align__(16) float ks[64 * 68];    // keys; before them the coefficient tables
     __shared__ __align__(16) float vs[64 * 80];    // values; before them a block of S_c (stride 80)
     __shared__ __align__(16) float uin[64 * 68];   // state part of u per query
     const int tpc = C / 64, c = blockIdx.x / tpc, qt = blockIdx.x % tpc;
@@ -417,12 +384,12 @@ __global__ __launch_bounds__(kThreads) void oal_bwd_readout_g(int T_len, int C, 
         fdl[f] = (unsigned short)(fa | (fb << 8));
     }
     __syncthreads();
-    const float *xi = xq + i * 65;
 
+    const int lr = threadIdx.x & 15, kg = (threadIdx.x >> 4) & 3;       // MFMA lane roles
+    const float *xa = xq + (16 * w + lr) * 65;                         // A row: query 16 w + lr
+    oal_f32x4 D[5];                                 // u: query 16 w + 4 kg + j, column 16 ct + lr
     {
-        const int lr = threadIdx.x & 15, kg = (threadIdx.x >> 4) & 3;   // MFMA lane roles
-        const float *xa = xq + (16 * w + lr) * 65;                     // A row: query 16 w + lr
-        oal_f32x4 D[5], E[5];                       // even and odd K-steps: independent chains
+        oal_f32x4 E[5];                             // even and odd K-steps: independent chains
 #pragma unroll
         for (int ct = 0; ct < 5; ++ct) D[ct] = E[ct] = oal_splat(0.0f);
         if (c > 0) {                               // S_0 = 0
@@ -472,59 +439,77 @@ __global__ __launch_bounds__(kThreads) void oal_bwd_readout_g(int T_len, int C, 
         }
 #pragma unroll
         for (int ct = 0; ct < 5; ++ct) D[ct] += E[ct];
-        // D[ct][j]: query 16 w + 4 (l / 16) + j, column 16 ct + l % 16
-#pragma unroll
-        for (int ct = 0; ct < 5; ++ct)
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int col = 16 * ct + lr;
-                if (col <= 64) uin[(16 * w + 4 * kg + j) * 68 + col] = D[ct][j];
-            }
     }
 
-    float acc[65];
+    // pairs inside the chunk (fp32 MFMA): per key tile and z-term m, Z_m = (Q o Lz[m]) K^T
+    // (+ L00 for m = 0); kappa = eps + sum_m Z_m^2 on the pairs that see each other; then
+    // D += kappa [V; 1]. kappa passes through uin (the wave's own rows) to be an A operand.
+    {
+        const float *Lz = hd->Lz;
+        const float L00 = hd->L00, eps = hd->eps;
+        for (int kt = 0; kt <= qt; ++kt) {
+            const int k0 = c * C + kt * 64;
+            __syncthreads();
+            stage_rows(ks, 68, k, krow, k0, T_len, 0.0f);
+            stage_rows(vs, 68, v, krow, k0, T_len, 1.0f);
+            __syncthreads();
+            oal_f32x4 kap[4];                       // query 16 w + 4 kg + jj, key 16 jt + lr
 #pragma unroll
-    for (int e = 0; e < 65; ++e) acc[e] = 0.0f;
-    for (int kt = 0; kt <= qt; ++kt) {
-        const int k0 = c * C + kt * 64;
-        __syncthreads();
-        stage_rows(ks, 64, k, krow, k0, T_len, 0.0f);
-        stage_rows(vs, 68, v, krow, k0, T_len, 1.0f);
-        __syncthreads();
-        if (valid) {
-            for (int jj = w; jj < 64; jj += 4) {
-                if (!sees(kt, qt, jj, i)) continue;
-                const float kap = pair_kappa(hd, G, xi, ks + jj * 64);
-                const float4 *vr = reinterpret_cast<const float4 *>(vs + jj * 68);
+            for (int jt = 0; jt < 4; ++jt) kap[jt] = oal_splat(0.0f);
+            for (int m = 0; m <= G; ++m) {
+                const float *lzm = Lz + m * OAL_D;
+                oal_f32x4 Z[4];
 #pragma unroll
-                for (int u = 0; u < 16; ++u) {
-                    const float4 vv = vr[u];
-                    acc[4 * u] += kap * vv.x;
-                    acc[4 * u + 1] += kap * vv.y;
-                    acc[4 * u + 2] += kap * vv.z;
-                    acc[4 * u + 3] += kap * vv.w;
+                for (int jt = 0; jt < 4; ++jt) Z[jt] = oal_splat(m == 0 ? L00 : 0.0f);
+#pragma unroll 4
+                for (int st = 0; st < 16; ++st) {
+                    const int r = 4 * st + kg;
+                    const float a = xa[r] * lzm[r];
+#pragma unroll
+                    for (int jt = 0; jt < 4; ++jt)
+                        Z[jt] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, ks[(16 * jt + lr) * 68 + r], Z[jt], 0, 0, 0);
                 }
-                acc[64] += kap;
+#pragma unroll
+                for (int jt = 0; jt < 4; ++jt)
+#pragma unroll
+                    for (int jj = 0; jj < 4; ++jj) kap[jt][jj] += Z[jt][jj] * Z[jt][jj];
+            }
+#pragma unroll
+            for (int jt = 0; jt < 4; ++jt)
+#pragma unroll
+                for (int jj = 0; jj < 4; ++jj) {
+                    const int il = 16 * w + 4 * kg + jj, jl = 16 * jt + lr;
+                    uin[il * 68 + jl] = sees(kt, qt, jl, il) ? eps + kap[jt][jj] : 0.0f;
+                }
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");   // the wave reads its own rows
+            __builtin_amdgcn_s_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+#pragma unroll 4
+            for (int st = 0; st < 16; ++st) {
+                const int j = 4 * st + kg;
+                const float a = uin[(16 * w + lr) * 68 + j];
+                const float *vr = vs + j * 68;
+#pragma unroll
+                for (int ct = 0; ct < 4; ++ct)
+                    D[ct] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, vr[16 * ct + lr], D[ct], 0, 0, 0);
+                D[4] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, lr == 0 ? vr[64] : 0.0f, D[4], 0, 0, 0);
             }
         }
     }
-    // wave 0 collects the other waves' partial sums
-    float *red = vs;
-    for (int s = 1; s < 4; ++s) {
-        __syncthreads();
-        if (w == s) {
+    // u into uin (row = query, columns 0..64), then the epilogue of wave 0
+    __syncthreads();
 #pragma unroll
-            for (int e = 0; e < 65; ++e) red[i * 65 + e] = acc[e];
-        }
-        __syncthreads();
-        if (w == 0) {
+    for (int ct = 0; ct < 5; ++ct)
 #pragma unroll
-            for (int e = 0; e < 65; ++e) acc[e] += red[i * 65 + e];
+        for (int j = 0; j < 4; ++j) {
+            const int col = 16 * ct + lr;
+            if (col <= 64) uin[(16 * w + 4 * kg + j) * 68 + col] = D[ct][j];
         }
-    }
+    __syncthreads();
+    float acc[65];
     if (w == 0 && valid) {
 #pragma unroll
-        for (int e = 0; e < 65; ++e) acc[e] += uin[i * 68 + e];
+        for (int e = 0; e < 65; ++e) acc[e] = uin[i * 68 + e];
         const float inv = 1.0f / acc[64];
         const float *dyr = dy + (qrow + t) * OAL_D;
         float *gr = gv + (qrow + t) * OAL_D;
@@ -783,9 +768,8 @@ __global__ __launch_bounds__(kThreads) void oal_bwd_dq_intra_mfma(int T_len, int
 //      splits (worker 4 p + w) take the feature-row pairs {worker, 63 - worker} (65 features
 //      each) of the state part: dv_j += psi_f(k_j) R_c[f][0:64], dk_j += (R_c[f] . [v_j; 1])
 //      dpsi_f/dk_j;
-//    - one workgroup of oal_bwd_dkv_intra_mfma per query head h of the KV head: the pairs inside the
-//      chunk, i >= j, with the waves on the queries i = w (mod 4): dv_j += kappa_ij g_i[0:64],
-//      dk_j += dkappa_ij dkappa_ij/dk_j.
+//    - one workgroup of oal_bwd_dkv_intra_mfma per query head h of the KV head: the pairs inside
+//      the chunk, i >= j: dv_j += kappa_ij g_i[0:64], dk_j += dkappa_ij dkappa_ij/dk_j.
 //    Each writes a partial row of 128 floats (dk, then dv) per key into part[slot]: slots
 //    0 .. kInterSplits-1 the state parts (dk_inter the first half, dv_inter the second),
 //    then one slot per query head. oal_bwd_kv_reduce adds the slots in order.
