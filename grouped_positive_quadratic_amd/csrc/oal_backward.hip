@@ -31,8 +31,8 @@
 //   1. oal_bwd_increments<keys>:    per chunk psi(K_c)^T [V_c; 1]           -> workspace states
 //   2. oal_bwd_scan (forward):      exclusive prefix over chunks: S_c
 //   3. oal_bwd_readout_g:           u_i (inter + intra), y, den -> g_i     -> workspace g
-//   4. oal_bwd_dq_inter, oal_bwd_sum_parts, oal_bwd_dq_intra_mfma: dq (state part in four row
-//      splits, their sum, then the pairs inside the chunk)
+//   4. oal_bwd_dq_inter_mfma, oal_bwd_dq_intra_mfma: dq (state part, then the pairs inside
+//      the chunk)
 //   5. oal_bwd_dkv_intra_mfma:      dk, dv partials of the pairs inside the chunk
 //   6. oal_bwd_increments<queries>: per chunk sum_h phi_h(Q_c)^T G_c       -> workspace states
 //   7. oal_bwd_scan (reverse):      exclusive suffix over chunks: R_c
@@ -525,130 +525,110 @@ __global__ __launch_bounds__(kThreads) void oal_bwd_readout_g(int T_len, int C, 
     }
 }
 
-// 4a. dq_i = Jphi_h(q_i)^T (S_c g_i) (the state part). Workgroup = (64-query tile, four query
-//     heads of one KV head -- one per wave --, row split p, sequence); lane = query. Split p
-//     takes the feature rows r = p (mod kDqSplits): per row, the block of state rows it needs
-//     (the linear feature 1 + r and the quadratic (r, t), t >= r) is staged once in LDS and
-//     read by the four heads. Per quadratic feature: x = S_c[f] . g, then dq_t += wdec x q_r and
-//     dq_r += wdec x q_t (t = r gives the 2 of the square); dq_t and q_t are registers (t
-//     unrolled), q_r and dq_r picked out of those by selection. Each split writes its partial
-//     dq; oal_bwd_sum_parts adds them in order.
-constexpr int kDqSplits = 4;
-constexpr int kDqHeads = 4;
 
-__device__ inline float lds_dot(const float *row, const float (&g)[65]) {
-    const float4 *r4 = reinterpret_cast<const float4 *>(row);
-    float x0 = row[64] * g[64], x1 = 0.0f, x2 = 0.0f, x3 = 0.0f;
-#pragma unroll
-    for (int u = 0; u < 16; ++u) {
-        const float4 s4 = r4[u];
-        x0 += s4.x * g[4 * u];
-        x1 += s4.y * g[4 * u + 1];
-        x2 += s4.z * g[4 * u + 2];
-        x3 += s4.w * g[4 * u + 3];
-    }
-    return (x0 + x1) + (x2 + x3);
+// 4a. dq_i = Jphi_h(q_i)^T (S_c g_i) (the state part) on fp32 MFMA. With c_st = wdec of the
+//     feature (min(s,t), max(s,t)), doubled for s = t (the square), dq_i[s] = wdec_{1+s}
+//     (S_c[1+s] . g_i) + sum_t c_st q_i[t] (S_c[(s,t)] . g_i): per t, X_t = G T_t^T with
+//     T_t[s] = S_c[pair(s, t)] (K = the 65 columns), then dq += c_st q_i[t] X_t; the linear
+//     features are one more step (T[s] = S_c[1 + s], q factor 1). Workgroup = (64-query tile,
+//     head, sequence); wave w owns the queries 16 w .. 16 w + 15 and all 64 dims. The A
+//     operand (g) stays in registers for every step; T_t is prefetched into registers one step
+//     ahead and staged in LDS.
+// State row of T_t[s] (the feature (min(s,t), max(s,t))); t = 64: the linear feature 1 + s.
+__device__ inline int dq_row_of(int s, int t) {
+    return t == OAL_D ? 1 + s : (s <= t ? quad_base(s) + t : quad_base(t) + s);
 }
 
 template <typename T>
-__global__ __launch_bounds__(kThreads) void oal_bwd_dq_inter(int T_len, int C, int nch, int n_q_heads,
-                                                              int n_kv_heads, const T *__restrict__ q,
-                                                              const unsigned char *__restrict__ params,
-                                                              const float *__restrict__ st, const float *__restrict__ gv,
-                                                              const float *__restrict__ gd, float *__restrict__ dqp) {
-    __shared__ __align__(16) float sb[65 * 68];     // slot 0: feature 1 + r; slot 1 + k: (r, r + k)
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void oal_bwd_dq_inter_mfma(int T_len, int C, int nch, int n_q_heads,
+                                                                   int n_kv_heads, const T *__restrict__ q,
+                                                                   const unsigned char *__restrict__ params,
+                                                                   const float *__restrict__ st,
+                                                                   const float *__restrict__ gv,
+                                                                   const float *__restrict__ gd, float *__restrict__ dq) {
+    __shared__ __align__(16) float xq[64 * 68];   // query tile
+    __shared__ __align__(16) float tb[64 * 68];   // T_t: row s, 65 columns, zero to 68
+    __shared__ float wdl[2176];                    // wdec of the head
     const int tpc = C / 64, c = blockIdx.x / tpc, qt = blockIdx.x % tpc;
-    const int n_rep = n_q_heads / n_kv_heads, ngrp = (n_rep + kDqHeads - 1) / kDqHeads;
-    const int p = blockIdx.y % kDqSplits, grp = (blockIdx.y / kDqSplits) % ngrp;
-    const int kv = blockIdx.y / (kDqSplits * ngrp), b = blockIdx.z;
-    const int i = threadIdx.x & 63, w = wave_id(), hs = grp * kDqHeads + w;
-    const bool active = hs < n_rep;                 // wave-uniform
-    const int h = kv * n_rep + (active ? hs : 0);
-    const int t0 = c * C + qt * 64, t = t0 + i;
-    const bool valid = active && t < T_len;
+    const int h = blockIdx.y, b = blockIdx.z, n_rep = n_q_heads / n_kv_heads, kv = h / n_rep;
+    const int tid = threadIdx.x, lane = tid & 63, lr = lane & 15, kg = lane >> 4, w = wave_id();
+    const int t0 = c * C + qt * 64;
+    if (t0 >= T_len) return;                       // a tile past the sequence (uniform)
+    const OalHeadDev *hd = bwd_head(params, h);
     const size_t qrow = ((size_t)b * n_q_heads + h) * T_len;
-    const cfloat *wd = uni(bwd_head(params, h)->wdec);
-    float qv[64], g[65], d[64];
+    stage_rows(xq, 68, q, qrow, t0, T_len, 0.0f);
+    for (int f = tid; f < 2176; f += kThreads) wdl[f] = f < OAL_NFEAT ? hd->wdec[f] : 0.0f;
+    float ga[17];                                  // g of query 16 w + lr, column 4 s + kg
+    {
+        const int ta = t0 + 16 * w + lr;
+        const bool ok = ta < T_len;
 #pragma unroll
-    for (int e = 0; e < 64; ++e) {
-        qv[e] = valid ? oal_ld(q + (qrow + t) * OAL_D + e) : 0.0f;
-        d[e] = 0.0f;
+        for (int ks = 0; ks < 17; ++ks) {
+            const int col = 4 * ks + kg;
+            ga[ks] = !ok ? 0.0f : col < 64 ? gv[(qrow + ta) * OAL_D + col] : col == 64 ? gd[qrow + ta] : 0.0f;
+        }
     }
+    oal_f32x4 acc[4];                              // dq: query 16 w + 4 kg + jj, dim 16 st + lr
 #pragma unroll
-    for (int e = 0; e < 64; e += 4) {
-        const float4 g4 = valid ? *reinterpret_cast<const float4 *>(gv + (qrow + t) * OAL_D + e) : make_float4(0, 0, 0, 0);
-        g[e] = g4.x; g[e + 1] = g4.y; g[e + 2] = g4.z; g[e + 3] = g4.w;
-    }
-    g[64] = valid ? gd[qrow + t] : 0.0f;
-    if (c > 0) {                                    // S_0 = 0
+    for (int sti = 0; sti < 4; ++sti) acc[sti] = oal_splat(0.0f);
+    if (c > 0) {                                   // S_0 = 0
         const float *S = st + ((size_t)((size_t)b * n_kv_heads + kv) * nch + c) * OAL_STATE_STRIDE;
         const float *Sd = S + (size_t)OAL_NFEAT * OAL_D;
-        // row block of r in registers one row ahead: thread's share of (65 - r) rows x 16 float4
-        // (at most 5 float4) and one normaliser entry
-        float4 pre[5];
-        float pre64 = 0.0f;
-        auto load_block = [&](int r) {
-            const int base = quad_base(r), nslot = OAL_D + 1 - r;
-#pragma unroll
-            for (int m = 0; m < 5; ++m) {
-                const int e = threadIdx.x + kThreads * m, k = e >> 4, c4 = (e & 15) * 4;
-                const int f = k == 0 ? 1 + r : base + r + k - 1;
-                pre[m] = k < nslot ? *reinterpret_cast<const float4 *>(S + (size_t)f * OAL_D + c4) : make_float4(0, 0, 0, 0);
-            }
-            if ((int)threadIdx.x < nslot) {
-                const int k = threadIdx.x;
-                pre64 = Sd[k == 0 ? 1 + r : base + r + k - 1];
-            }
+        // T of the next step, this thread's share: rows s = (tid + 256 m) / 16, 4 columns each
+        const int s0 = tid >> 4, c4 = (tid & 15) * 4;
+        auto ld4 = [&](int srow, int t) {
+            return *reinterpret_cast<const float4 *>(S + (size_t)dq_row_of(srow, t) * OAL_D + c4);
         };
-        load_block(p);
-        for (int r = p; r < OAL_D; r += kDqSplits) {
-            const int base = quad_base(r), nslot = OAL_D + 1 - r;
-            __syncthreads();                        // the previous block is consumed
-#pragma unroll
-            for (int m = 0; m < 5; ++m) {
-                const int e = threadIdx.x + kThreads * m, k = e >> 4, c4 = (e & 15) * 4;
-                if (k < nslot) *reinterpret_cast<float4 *>(sb + k * 68 + c4) = pre[m];
+        float4 p0 = ld4(s0, 0), p1 = ld4(s0 + 16, 0), p2 = ld4(s0 + 32, 0), p3 = ld4(s0 + 48, 0);
+        float p64 = Sd[dq_row_of(tid & 63, 0)];
+        for (int t = 0; t <= OAL_D; ++t) {
+            __syncthreads();                       // the previous T is consumed
+            *reinterpret_cast<float4 *>(tb + s0 * 68 + c4) = p0;
+            *reinterpret_cast<float4 *>(tb + (s0 + 16) * 68 + c4) = p1;
+            *reinterpret_cast<float4 *>(tb + (s0 + 32) * 68 + c4) = p2;
+            *reinterpret_cast<float4 *>(tb + (s0 + 48) * 68 + c4) = p3;
+            if (tid < 64) {
+                tb[tid * 68 + 64] = p64;
+                tb[tid * 68 + 65] = tb[tid * 68 + 66] = tb[tid * 68 + 67] = 0.0f;
             }
-            if ((int)threadIdx.x < nslot) sb[threadIdx.x * 68 + 64] = pre64;
             __syncthreads();
-            if (r + kDqSplits < OAL_D) load_block(r + kDqSplits);
-            if (active) {
-                float qr = 0.0f;                    // qv[r] by selection: a dynamic index would
-#pragma unroll                                      // move the arrays to scratch memory
-                for (int e = 0; e < 64; ++e) qr = e == r ? qv[e] : qr;
-                float dr = wd[1 + r] * lds_dot(sb, g);
+            {                                      // the last step reloads its own T (harmless)
+                const int tn = t < OAL_D ? t + 1 : OAL_D;
+                p0 = ld4(s0, tn);
+                p1 = ld4(s0 + 16, tn);
+                p2 = ld4(s0 + 32, tn);
+                p3 = ld4(s0 + 48, tn);
+                p64 = Sd[dq_row_of(tid & 63, tn)];
+            }
+            oal_f32x4 X[4];
 #pragma unroll
-                for (int tt = 0; tt < OAL_D; ++tt) {
-                    if (tt >= r) {
-                        const float wx = wd[base + tt] * lds_dot(sb + (tt - r + 1) * 68, g);
-                        d[tt] += wx * qr;
-                        dr += wx * qv[tt];
-                    }
+            for (int sti = 0; sti < 4; ++sti) X[sti] = oal_splat(0.0f);
+#pragma unroll
+            for (int ks = 0; ks < 17; ++ks) {
+                const int col = 4 * ks + kg;
+#pragma unroll
+                for (int sti = 0; sti < 4; ++sti)
+                    X[sti] = __builtin_amdgcn_mfma_f32_16x16x4f32(ga[ks], tb[(16 * sti + lr) * 68 + col], X[sti], 0, 0, 0);
+            }
+#pragma unroll
+            for (int sti = 0; sti < 4; ++sti) {
+                const int sd = 16 * sti + lr;
+                const float cst = t == OAL_D ? wdl[1 + sd] : (sd == t ? 2.0f : 1.0f) * wdl[dq_row_of(sd, t)];
+#pragma unroll
+                for (int jj = 0; jj < 4; ++jj) {
+                    const float qf = t == OAL_D ? 1.0f : xq[(16 * w + 4 * kg + jj) * 68 + t];
+                    acc[sti][jj] += cst * qf * X[sti][jj];
                 }
-#pragma unroll
-                for (int e = 0; e < 64; ++e) d[e] += e == r ? dr : 0.0f;
             }
         }
     }
-    if (valid) {
-        float *o = dqp + ((size_t)p * gridDim.z * n_q_heads * T_len + qrow + t) * OAL_D;
 #pragma unroll
-        for (int e = 0; e < 64; e += 4) *reinterpret_cast<float4 *>(o + e) = make_float4(d[e], d[e + 1], d[e + 2], d[e + 3]);
-    }
-}
-
-// out[n] = sum_{s < nparts} parts[s][n] in order (n counted in float4s).
-__global__ __launch_bounds__(kThreads) void oal_bwd_sum_parts(size_t n4, int nparts, const float *__restrict__ parts,
-                                                              float *__restrict__ out) {
-    const size_t e = (size_t)blockIdx.x * kThreads + threadIdx.x;
-    if (e >= n4) return;
-    const float4 *p4 = reinterpret_cast<const float4 *>(parts);
-    float4 s = p4[e];
-    for (int k = 1; k < nparts; ++k) {
-        const float4 x = p4[(size_t)k * n4 + e];
-        s.x += x.x; s.y += x.y; s.z += x.z; s.w += x.w;
-    }
-    reinterpret_cast<float4 *>(out)[e] = s;
+    for (int sti = 0; sti < 4; ++sti)
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+            const int tq = t0 + 16 * w + 4 * kg + jj;
+            if (tq < T_len) dq[(qrow + tq) * OAL_D + 16 * sti + lr] = acc[sti][jj];
+        }
 }
 
 // 4b. dq_i += sum_{j <= i in the chunk} dkappa_ij dkappa_ij/dq_i, dkappa_ij = g_i . [v_j; 1], on
@@ -1250,8 +1230,6 @@ hipError_t launch_backward(const oal_dims &d, int T_len, int C, const void *q_, 
     float *dwp = reinterpret_cast<float *>(reinterpret_cast<unsigned char *>(part) +
                                            align256((size_t)(kInterSplits + Hq / Hkv) * kvrows * 128 * 4));
     const bool coef = dL != nullptr;
-    float *dqp = reinterpret_cast<float *>(reinterpret_cast<unsigned char *>(dwp) +
-                                           align256(((size_t)2 * B * nch + 1) * Hq * OAL_NFEAT * 4));
     const dim3 blk(kThreads);
     const dim3 g_inc((OAL_NFEAT + kFeatBlock - 1) / kFeatBlock, nch, B * Hkv);
     const dim3 g_scan((OAL_NFEAT * OAL_V1 + kThreads - 1) / kThreads, B * Hkv);
@@ -1263,14 +1241,8 @@ hipError_t launch_backward(const oal_dims &d, int T_len, int C, const void *q_, 
     hipLaunchKernelGGL(oal_bwd_scan, g_scan, blk, 0, stream, nch, 0, st);
     hipLaunchKernelGGL(oal_bwd_readout_g<T>, g_q, blk, 0, stream, T_len, C, nch, Hq, Hkv, q, k, v, dy, params, st,
                        gv, gd);
-    {
-        const int ngrp = (Hq / Hkv + kDqHeads - 1) / kDqHeads;
-        const size_t n4 = (size_t)B * Hq * T_len * 16;
-        hipLaunchKernelGGL(oal_bwd_dq_inter<T>, dim3(nch * tpc, Hkv * ngrp * kDqSplits, B), blk, 0, stream, T_len, C,
-                           nch, Hq, Hkv, q, params, st, gv, gd, dqp);
-        hipLaunchKernelGGL(oal_bwd_sum_parts, dim3((unsigned)((n4 + kThreads - 1) / kThreads)), blk, 0, stream, n4,
-                           kDqSplits, dqp, dq);
-    }
+    hipLaunchKernelGGL(oal_bwd_dq_inter_mfma<T>, g_q, blk, 0, stream, T_len, C, nch, Hq, Hkv, q, params, st, gv, gd,
+                       dq);
     hipLaunchKernelGGL(oal_bwd_dq_intra_mfma<T>, g_q, blk, 0, stream, T_len, C, Hq, Hkv, q, k, v, params, gv, gd, dq);
     hipLaunchKernelGGL(oal_bwd_dkv_intra_mfma<T>, g_kh, blk, 0, stream, T_len, C, Hq, Hkv, q, k, v, params, gv, gd,
                        part);
@@ -1299,8 +1271,7 @@ size_t oal_backward_ws_bytes_impl(const oal_dims &d, int T_len, int C) {
     return align256((size_t)d.batch * d.n_kv_heads * nch * OAL_STATE_STRIDE * 4) +
            align256((size_t)d.batch * d.n_q_heads * T_len * 64 * 4) + align256((size_t)d.batch * d.n_q_heads * T_len * 4) +
            align256((size_t)(kInterSplits + d.n_q_heads / d.n_kv_heads) * d.batch * d.n_kv_heads * T_len * 128 * 4) +
-           align256(((size_t)2 * d.batch * nch + 1) * d.n_q_heads * OAL_NFEAT * 4) +
-           align256((size_t)kDqSplits * d.batch * d.n_q_heads * T_len * 64 * 4);
+           align256(((size_t)2 * d.batch * nch + 1) * d.n_q_heads * OAL_NFEAT * 4);
 }
 
 hipError_t oal_launch_backward(const oal_dims &d, int T_len, int C, const void *q, const void *k, const void *v,
