@@ -36,7 +36,7 @@
 //   5. oal_bwd_dkv_intra_mfma:      dk, dv partials of the pairs inside the chunk
 //   6. oal_bwd_increments<queries>: per chunk sum_h phi_h(Q_c)^T G_c       -> workspace states
 //   7. oal_bwd_scan (reverse):      exclusive suffix over chunks: R_c
-//   8. oal_bwd_dk_inter, _dv_inter: dk, dv partials of the state part
+//   8. oal_bwd_dq_inter_mfma<keys>, oal_bwd_dv_inter: dk, dv partials of the state part
 //   9. oal_bwd_kv_reduce:           dk, dv (the partials added in a fixed order)
 // With coefficient gradients, also oal_bwd_dw_intra (before 6), the per-head partials of 6,
 // and oal_bwd_dw_sum, oal_bwd_coef (after 6): dL, deps.
@@ -63,19 +63,6 @@ __device__ inline int wave_id() { return __builtin_amdgcn_readfirstlane(threadId
 // first feature of the quadratic row r, minus r: feature (r, t) is quad_base(r) + t
 __device__ inline int quad_base(int r) { return 1 + OAL_D + r * OAL_D - (r * (r - 1)) / 2 - r; }
 
-// x = S[f][0:64] . g[0:64] + S[f][64] g[64] (S rows wave-uniform)
-__device__ inline float row_dot(const cfloat *S, const cfloat *Sd, int f, const float (&g)[65]) {
-    const cfloat *row = S + (size_t)f * OAL_D;
-    float x0 = Sd[f] * g[64], x1 = 0.0f, x2 = 0.0f, x3 = 0.0f;
-#pragma unroll
-    for (int c = 0; c < 64; c += 4) {
-        x0 += row[c] * g[c];
-        x1 += row[c + 1] * g[c + 1];
-        x2 += row[c + 2] * g[c + 2];
-        x3 += row[c + 3] * g[c + 3];
-    }
-    return (x0 + x1) + (x2 + x3);
-}
 
 // acc[0:NC] += a S[f][0:NC] (NC = 64 or 65, column 64 from the separate vector)
 template <int NC>
@@ -539,25 +526,29 @@ __device__ inline int dq_row_of(int s, int t) {
     return t == OAL_D ? 1 + s : (s <= t ? quad_base(s) + t : quad_base(t) + s);
 }
 
-template <typename T>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void oal_bwd_dq_inter_mfma(int T_len, int C, int nch, int n_q_heads,
-                                                                   int n_kv_heads, const T *__restrict__ q,
-                                                                   const unsigned char *__restrict__ params,
-                                                                   const float *__restrict__ st,
-                                                                   const float *__restrict__ gv,
-                                                                   const float *__restrict__ gd, float *__restrict__ dq) {
+//     KEYS: the same for dk_j = Jpsi(k_j)^T (R_c [v_j; 1]) -- psi has no coefficients (c_st = 1,
+//     2 for s = t, 1 for the linear features), the A operand is [v_j; 1], the rows come from R_c
+//     (zero for the last chunk); workgroup = (64-key tile, KV head, sequence), the result goes
+//     to the dk half of partial slot 0.
+template <typename T, bool KEYS>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void oal_bwd_dq_inter_mfma(
+    int T_len, int C, int nch, int n_q_heads, int n_kv_heads, const T *__restrict__ q, const T *__restrict__ v,
+    const unsigned char *__restrict__ params, const float *__restrict__ st, const float *__restrict__ gv,
+    const float *__restrict__ gd, float *__restrict__ dq) {
     __shared__ __align__(16) float xq[64 * 68];   // query tile
     __shared__ __align__(16) float tb[64 * 68];   // T_t: row s, 65 columns, zero to 68
     __shared__ float wdl[2176];                    // wdec of the head
     const int tpc = C / 64, c = blockIdx.x / tpc, qt = blockIdx.x % tpc;
-    const int h = blockIdx.y, b = blockIdx.z, n_rep = n_q_heads / n_kv_heads, kv = h / n_rep;
+    const int h = blockIdx.y, b = blockIdx.z, n_rep = n_q_heads / n_kv_heads, kv = KEYS ? h : h / n_rep;
     const int tid = threadIdx.x, lane = tid & 63, lr = lane & 15, kg = lane >> 4, w = wave_id();
     const int t0 = c * C + qt * 64;
     if (t0 >= T_len) return;                       // a tile past the sequence (uniform)
-    const OalHeadDev *hd = bwd_head(params, h);
-    const size_t qrow = ((size_t)b * n_q_heads + h) * T_len;
+    const size_t qrow = KEYS ? ((size_t)b * n_kv_heads + kv) * T_len : ((size_t)b * n_q_heads + h) * T_len;
     stage_rows(xq, 68, q, qrow, t0, T_len, 0.0f);
-    for (int f = tid; f < 2176; f += kThreads) wdl[f] = f < OAL_NFEAT ? hd->wdec[f] : 0.0f;
+    if constexpr (!KEYS) {
+        const OalHeadDev *hd = bwd_head(params, h);
+        for (int f = tid; f < 2176; f += kThreads) wdl[f] = f < OAL_NFEAT ? hd->wdec[f] : 0.0f;
+    }
     float ga[17];                                  // g of query 16 w + lr, column 4 s + kg
     {
         const int ta = t0 + 16 * w + lr;
@@ -565,13 +556,16 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
 #pragma unroll
         for (int ks = 0; ks < 17; ++ks) {
             const int col = 4 * ks + kg;
-            ga[ks] = !ok ? 0.0f : col < 64 ? gv[(qrow + ta) * OAL_D + col] : col == 64 ? gd[qrow + ta] : 0.0f;
+            if constexpr (KEYS)
+                ga[ks] = !ok ? 0.0f : col < 64 ? oal_ld(v + (qrow + ta) * OAL_D + col) : col == 64 ? 1.0f : 0.0f;
+            else
+                ga[ks] = !ok ? 0.0f : col < 64 ? gv[(qrow + ta) * OAL_D + col] : col == 64 ? gd[qrow + ta] : 0.0f;
         }
     }
     oal_f32x4 acc[4];                              // dq: query 16 w + 4 kg + jj, dim 16 st + lr
 #pragma unroll
     for (int sti = 0; sti < 4; ++sti) acc[sti] = oal_splat(0.0f);
-    if (c > 0) {                                   // S_0 = 0
+    if (KEYS ? c < nch - 1 : c > 0) {              // S_0 = 0, R of the last chunk = 0
         const float *S = st + ((size_t)((size_t)b * n_kv_heads + kv) * nch + c) * OAL_STATE_STRIDE;
         const float *Sd = S + (size_t)OAL_NFEAT * OAL_D;
         // T of the next step, this thread's share: rows s = (tid + 256 m) / 16, 4 columns each
@@ -613,7 +607,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
 #pragma unroll
             for (int sti = 0; sti < 4; ++sti) {
                 const int sd = 16 * sti + lr;
-                const float cst = t == OAL_D ? wdl[1 + sd] : (sd == t ? 2.0f : 1.0f) * wdl[dq_row_of(sd, t)];
+                const float cst = KEYS ? (sd == t ? 2.0f : 1.0f)
+                                       : t == OAL_D ? wdl[1 + sd] : (sd == t ? 2.0f : 1.0f) * wdl[dq_row_of(sd, t)];
 #pragma unroll
                 for (int jj = 0; jj < 4; ++jj) {
                     const float qf = t == OAL_D ? 1.0f : xq[(16 * w + 4 * kg + jj) * 68 + t];
@@ -627,7 +622,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
 #pragma unroll
         for (int jj = 0; jj < 4; ++jj) {
             const int tq = t0 + 16 * w + 4 * kg + jj;
-            if (tq < T_len) dq[(qrow + tq) * OAL_D + 16 * sti + lr] = acc[sti][jj];
+            if (tq < T_len) {
+                if constexpr (KEYS)   // part slot 0, dk half: part[0][row][0:64], rows = B Hkv T
+                    dq[(qrow + tq) * 128 + 16 * sti + lr] = acc[sti][jj];
+                else
+                    dq[(qrow + tq) * OAL_D + 16 * sti + lr] = acc[sti][jj];
+            }
         }
 }
 
@@ -744,84 +744,22 @@ __global__ __launch_bounds__(kThreads) void oal_bwd_dq_intra_mfma(int T_len, int
 }
 
 // 7. dk and dv. Each 64-key tile is covered by:
-//    - kInterSplits workgroups of oal_bwd_dk_inter and of oal_bwd_dv_inter: the 32 waves of the
-//      splits (worker 4 p + w) take the feature-row pairs {worker, 63 - worker} (65 features
-//      each) of the state part: dv_j += psi_f(k_j) R_c[f][0:64], dk_j += (R_c[f] . [v_j; 1])
-//      dpsi_f/dk_j;
+//    - oal_bwd_dq_inter_mfma<KEYS>: the state part of dk, dk_j += Jpsi(k_j)^T (R_c [v_j; 1]);
+//    - kInterSplits workgroups of oal_bwd_dv_inter: the 32 waves of the splits (worker
+//      4 p + w) take the feature-row pairs {worker, 63 - worker} (65 features each) of the
+//      state part of dv, dv_j += psi_f(k_j) R_c[f][0:64];
 //    - one workgroup of oal_bwd_dkv_intra_mfma per query head h of the KV head: the pairs inside
 //      the chunk, i >= j: dv_j += kappa_ij g_i[0:64], dk_j += dkappa_ij dkappa_ij/dk_j.
-//    Each writes a partial row of 128 floats (dk, then dv) per key into part[slot]: slots
-//    0 .. kInterSplits-1 the state parts (dk_inter the first half, dv_inter the second),
-//    then one slot per query head. oal_bwd_kv_reduce adds the slots in order.
+//    Each writes partial rows of 128 floats (dk, then dv) per key into part[slot]: slot 0 the
+//    state parts (dk whole, dv of split 0), slots 1 .. kInterSplits-1 the other dv splits
+//    (their dk half unused), then one slot per query head. oal_bwd_kv_reduce adds the slots
+//    in order.
 constexpr int kInterSplits = 8;
 
 __device__ inline float *part_row(float *part, int slot, size_t rows, size_t row) {
     return part + ((size_t)slot * rows + row) * 128;
 }
 
-template <typename T>
-__global__ __launch_bounds__(kThreads) void oal_bwd_dk_inter(int T_len, int C, int nch, int n_kv_heads,
-                                                              const T *__restrict__ k, const T *__restrict__ v,
-                                                              const float *__restrict__ st, float *__restrict__ part) {
-    __shared__ float xk[64 * 65];
-    __shared__ float dkl[64 * 65];
-    const int tpc = C / 64, c = blockIdx.x / tpc, kt = blockIdx.x % tpc;
-    const int p = blockIdx.y % kInterSplits, kv = blockIdx.y / kInterSplits, b = blockIdx.z;
-    const int j = threadIdx.x & 63, w = wave_id(), worker = p * 4 + w;
-    const int t0 = c * C + kt * 64, t = t0 + j;
-    const bool valid = t < T_len;
-    const size_t krow = ((size_t)b * n_kv_heads + kv) * T_len, rows = (size_t)gridDim.z * n_kv_heads * T_len;
-    stage_rows(xk, 65, k, krow, t0, T_len, 1.0f);
-    for (int e = threadIdx.x; e < 64 * 65; e += kThreads) dkl[e] = 0.0f;
-    float vj[65];
-#pragma unroll
-    for (int e = 0; e < 64; ++e) vj[e] = valid ? oal_ld(v + (krow + t) * OAL_D + e) : 0.0f;
-    vj[64] = 1.0f;
-    __syncthreads();
-    const float *xj = xk + j * 65;
-    float d[64];
-#pragma unroll
-    for (int e = 0; e < 64; ++e) d[e] = 0.0f;
-    if (c < nch - 1) {                             // R of the last chunk is 0
-        const float *Rg = st + ((size_t)((size_t)b * n_kv_heads + kv) * nch + c) * OAL_STATE_STRIDE;
-        const cfloat *R = uni(Rg), *Rd = uni(Rg + (size_t)OAL_NFEAT * OAL_D);
-        for (int half = 0; half < 2; ++half) {
-            const int r = half ? 63 - worker : worker;
-            const float kr = xj[r];
-            const int base = quad_base(r);
-            float dr = row_dot(R, Rd, 1 + r, vj);  // linear feature: d psi / d k_r = 1
-            // blocks of 8 columns t, the columns t < r of r's block masked (as in dq)
-#pragma unroll
-            for (int tb = 0; tb < 8; ++tb) {
-                if (tb >= (r >> 3)) {
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) {
-                        const int tt = tb * 8 + e;
-                        const float y = (tt >= r ? 1.0f : 0.0f) * row_dot(R, Rd, base + tt, vj);
-                        d[tt] += y * kr;
-                        dr += y * xj[tt];
-                    }
-                }
-            }
-            dkl[j * 65 + r] += dr;                 // row r belongs to this wave alone
-        }
-    }
-    for (int s = 0; s < 4; ++s) {
-        __syncthreads();
-        if (w == s) {
-#pragma unroll
-            for (int e = 0; e < 64; ++e) dkl[j * 65 + e] += d[e];
-        }
-    }
-    __syncthreads();
-    if (valid) {
-        float *o = part_row(part, p, rows, krow + t) + w * 16;
-        const float *src = dkl + j * 65 + w * 16;
-#pragma unroll
-        for (int e = 0; e < 16; e += 4)
-            *reinterpret_cast<float4 *>(o + e) = make_float4(src[e], src[e + 1], src[e + 2], src[e + 3]);
-    }
-}
 
 template <typename T>
 __global__ __launch_bounds__(kThreads) void oal_bwd_dv_inter(int T_len, int C, int nch, int n_kv_heads,
@@ -1020,7 +958,8 @@ __global__ __launch_bounds__(kThreads) void oal_bwd_kv_reduce(size_t rows, int n
     if (e >= rows * 32) return;
     const size_t row = e / 32, col = (e % 32) * 4;
     float4 s = *reinterpret_cast<const float4 *>(part + row * 128 + col);
-    for (int p = 1; p < nslots; ++p) {
+    // dk: slot 0 holds the whole state part (slots 1 .. kInterSplits - 1 are dv's only)
+    for (int p = col < 64 ? kInterSplits : 1; p < nslots; ++p) {
         const float4 x = *reinterpret_cast<const float4 *>(part + ((size_t)p * rows + row) * 128 + col);
         s.x += x.x; s.y += x.y; s.z += x.z; s.w += x.w;
     }
@@ -1241,8 +1180,8 @@ hipError_t launch_backward(const oal_dims &d, int T_len, int C, const void *q_, 
     hipLaunchKernelGGL(oal_bwd_scan, g_scan, blk, 0, stream, nch, 0, st);
     hipLaunchKernelGGL(oal_bwd_readout_g<T>, g_q, blk, 0, stream, T_len, C, nch, Hq, Hkv, q, k, v, dy, params, st,
                        gv, gd);
-    hipLaunchKernelGGL(oal_bwd_dq_inter_mfma<T>, g_q, blk, 0, stream, T_len, C, nch, Hq, Hkv, q, params, st, gv, gd,
-                       dq);
+    hipLaunchKernelGGL((oal_bwd_dq_inter_mfma<T, false>), g_q, blk, 0, stream, T_len, C, nch, Hq, Hkv, q,
+                       (const T *)nullptr, params, st, gv, gd, dq);
     hipLaunchKernelGGL(oal_bwd_dq_intra_mfma<T>, g_q, blk, 0, stream, T_len, C, Hq, Hkv, q, k, v, params, gv, gd, dq);
     hipLaunchKernelGGL(oal_bwd_dkv_intra_mfma<T>, g_kh, blk, 0, stream, T_len, C, Hq, Hkv, q, k, v, params, gv, gd,
                        part);
@@ -1258,7 +1197,8 @@ hipError_t launch_backward(const oal_dims &d, int T_len, int C, const void *q_, 
         hipLaunchKernelGGL(oal_bwd_coef, dim3(Hq), blk, 0, stream, params, dwt, dL, deps);
     }
     hipLaunchKernelGGL(oal_bwd_scan, g_scan, blk, 0, stream, nch, 1, st);
-    hipLaunchKernelGGL(oal_bwd_dk_inter<T>, g_ki, blk, 0, stream, T_len, C, nch, Hkv, k, v, st, part);
+    hipLaunchKernelGGL((oal_bwd_dq_inter_mfma<T, true>), dim3(nch * tpc, Hkv, B), blk, 0, stream, T_len, C, nch, Hq,
+                       Hkv, k, v, params, st, gv, gd, part);
     hipLaunchKernelGGL(oal_bwd_dv_inter<T>, g_ki, blk, 0, stream, T_len, C, nch, Hkv, k, st, part);
     hipLaunchKernelGGL(oal_bwd_kv_reduce, g_red, blk, 0, stream, kvrows, nslots, part, dk, dv);
     return hipGetLastError();
