@@ -20,12 +20,12 @@
 // for a (query tile, key tile) pair each z-term is the product (Q o Lz[m]) K^T on MFMA.
 //
 // Every kernel computes in fp32 (inputs of either dtype are widened on load). The state
-// contractions run three ways: on fp32 MFMA (v_mfma_f32_16x16x4_f32; the readout gradient and
-// the chunk increments), on the VALU with blocks of state rows staged in LDS and read by
-// several heads (dq), or on the VALU with the state row read at a wave-uniform address through
-// the constant address space, so that it arrives in scalar registers and feeds the FMAs
-// directly (dk, dv). With packed fp32 off, the VALU bound is the non-packed FMA rate (256 CUs
-// x 4 SIMDs x 16 lanes x 2 flops x 2.4 GHz = 78.6 TFLOP/s); fp32 MFMA reaches 157.3.
+// contractions and the products over the pairs inside a chunk run on fp32 MFMA
+// (v_mfma_f32_16x16x4_f32), except dv's state part, which runs on the VALU with the state row
+// read at a wave-uniform address through the constant address space, so that it arrives in
+// scalar registers and feeds the FMAs directly. With packed fp32 off, the VALU bound is the
+// non-packed FMA rate (256 CUs x 4 SIMDs x 16 lanes x 2 flops x 2.4 GHz = 78.6 TFLOP/s); fp32
+// MFMA reaches 157.3.
 //
 // Launch order (all on the caller's stream):
 //   1. oal_bwd_increments<keys>:    per chunk psi(K_c)^T [V_c; 1]           -> workspace states
