@@ -49,6 +49,7 @@ namespace {
 
 constexpr int kThreads = 256;                 // four waves
 constexpr int kFeatBlock = 64;                // features per increment workgroup
+constexpr int kDkSplits = 4;                  // dk state part: its t steps over 4 workgroups
 
 typedef const float __attribute__((address_space(4))) cfloat;   // wave-uniform reads
 
@@ -528,8 +529,8 @@ __device__ inline int dq_row_of(int s, int t) {
 
 //     KEYS: the same for dk_j = Jpsi(k_j)^T (R_c [v_j; 1]) -- psi has no coefficients (c_st = 1,
 //     2 for s = t, 1 for the linear features), the A operand is [v_j; 1], the rows come from R_c
-//     (zero for the last chunk); workgroup = (64-key tile, KV head, sequence), the result goes
-//     to the dk half of partial slot 0.
+//     (zero for the last chunk); workgroup = (64-key tile, KV head x 4 splits of the t steps,
+//     sequence), each split's result going to the dk half of its partial slot.
 template <typename T, bool KEYS>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void oal_bwd_dq_inter_mfma(
     int T_len, int C, int nch, int n_q_heads, int n_kv_heads, const T *__restrict__ q, const T *__restrict__ v,
@@ -539,7 +540,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     __shared__ __align__(16) float tb[64 * 68];   // T_t: row s, 65 columns, zero to 68
     __shared__ float wdl[2176];                    // wdec of the head
     const int tpc = C / 64, c = blockIdx.x / tpc, qt = blockIdx.x % tpc;
-    const int h = blockIdx.y, b = blockIdx.z, n_rep = n_q_heads / n_kv_heads, kv = KEYS ? h : h / n_rep;
+    // keys: blockIdx.y = KV head x kDkSplits, split p taking the steps t = 16 p .. 16 p + 15 (p = 0
+    // also the linear step)
+    const int h = KEYS ? blockIdx.y / kDkSplits : blockIdx.y, b = blockIdx.z, n_rep = n_q_heads / n_kv_heads;
+    const int kv = KEYS ? h : h / n_rep, psplit = KEYS ? blockIdx.y % kDkSplits : 0;
+    const int tbeg = KEYS ? 16 * psplit : 0;
     const int tid = threadIdx.x, lane = tid & 63, lr = lane & 15, kg = lane >> 4, w = wave_id();
     const int t0 = c * C + qt * 64;
     if (t0 >= T_len) return;                       // a tile past the sequence (uniform)
@@ -573,9 +578,15 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
         auto ld4 = [&](int srow, int t) {
             return *reinterpret_cast<const float4 *>(S + (size_t)dq_row_of(srow, t) * OAL_D + c4);
         };
-        float4 p0 = ld4(s0, 0), p1 = ld4(s0 + 16, 0), p2 = ld4(s0 + 32, 0), p3 = ld4(s0 + 48, 0);
-        float p64 = Sd[dq_row_of(tid & 63, 0)];
-        for (int t = 0; t <= OAL_D; ++t) {
+        // queries: n = t (64 = the linear step); keys: t = 16 p + n, and n = 16 (split 0 only) the
+        // linear step
+        auto step_t = [&](int n) { return KEYS ? (n < 16 ? tbeg + n : OAL_D) : n; };
+        const int nsteps = KEYS ? (psplit == 0 ? 17 : 16) : OAL_D + 1;
+        float4 p0 = ld4(s0, step_t(0)), p1 = ld4(s0 + 16, step_t(0)), p2 = ld4(s0 + 32, step_t(0)),
+               p3 = ld4(s0 + 48, step_t(0));
+        float p64 = Sd[dq_row_of(tid & 63, step_t(0))];
+        for (int n = 0; n < nsteps; ++n) {
+            const int t = step_t(n);
             __syncthreads();                       // the previous T is consumed
             *reinterpret_cast<float4 *>(tb + s0 * 68 + c4) = p0;
             *reinterpret_cast<float4 *>(tb + (s0 + 16) * 68 + c4) = p1;
@@ -587,7 +598,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
             }
             __syncthreads();
             {                                      // the last step reloads its own T (harmless)
-                const int tn = t < OAL_D ? t + 1 : OAL_D;
+                const int tn = step_t(n + 1 < nsteps ? n + 1 : n);
                 p0 = ld4(s0, tn);
                 p1 = ld4(s0 + 16, tn);
                 p2 = ld4(s0 + 32, tn);
@@ -623,8 +634,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
         for (int jj = 0; jj < 4; ++jj) {
             const int tq = t0 + 16 * w + 4 * kg + jj;
             if (tq < T_len) {
-                if constexpr (KEYS)   // part slot 0, dk half: part[0][row][0:64], rows = B Hkv T
-                    dq[(qrow + tq) * 128 + 16 * sti + lr] = acc[sti][jj];
+                if constexpr (KEYS)   // part slot psplit, dk half; rows = B Hkv T
+                    dq[((size_t)psplit * gridDim.z * n_kv_heads * T_len + qrow + tq) * 128 + 16 * sti + lr] = acc[sti][jj];
                 else
                     dq[(qrow + tq) * OAL_D + 16 * sti + lr] = acc[sti][jj];
             }
@@ -750,9 +761,9 @@ __global__ __launch_bounds__(kThreads) void oal_bwd_dq_intra_mfma(int T_len, int
 //      state part of dv, dv_j += psi_f(k_j) R_c[f][0:64];
 //    - one workgroup of oal_bwd_dkv_intra_mfma per query head h of the KV head: the pairs inside
 //      the chunk, i >= j: dv_j += kappa_ij g_i[0:64], dk_j += dkappa_ij dkappa_ij/dk_j.
-//    Each writes partial rows of 128 floats (dk, then dv) per key into part[slot]: slot 0 the
-//    state parts (dk whole, dv of split 0), slots 1 .. kInterSplits-1 the other dv splits
-//    (their dk half unused), then one slot per query head. oal_bwd_kv_reduce adds the slots
+//    Each writes partial rows of 128 floats (dk, then dv) per key into part[slot]: slots
+//    0 .. kInterSplits-1 the state parts (dv's 8 splits; dk's 4 splits in slots 0 .. 3, the dk
+//    half of slots 4 .. 7 unused), then one slot per query head. oal_bwd_kv_reduce adds the slots
 //    in order.
 constexpr int kInterSplits = 8;
 
@@ -958,8 +969,9 @@ __global__ __launch_bounds__(kThreads) void oal_bwd_kv_reduce(size_t rows, int n
     if (e >= rows * 32) return;
     const size_t row = e / 32, col = (e % 32) * 4;
     float4 s = *reinterpret_cast<const float4 *>(part + row * 128 + col);
-    // dk: slot 0 holds the whole state part (slots 1 .. kInterSplits - 1 are dv's only)
-    for (int p = col < 64 ? kInterSplits : 1; p < nslots; ++p) {
+    // dk: slots 0 .. kDkSplits - 1 hold its state part (slots up to kInterSplits - 1 are dv's only)
+    for (int p = 1; p < nslots; ++p) {
+        if (col < 64 && p >= kDkSplits && p < kInterSplits) continue;
         const float4 x = *reinterpret_cast<const float4 *>(part + ((size_t)p * rows + row) * 128 + col);
         s.x += x.x; s.y += x.y; s.z += x.z; s.w += x.w;
     }
@@ -1197,7 +1209,7 @@ hipError_t launch_backward(const oal_dims &d, int T_len, int C, const void *q_, 
         hipLaunchKernelGGL(oal_bwd_coef, dim3(Hq), blk, 0, stream, params, dwt, dL, deps);
     }
     hipLaunchKernelGGL(oal_bwd_scan, g_scan, blk, 0, stream, nch, 1, st);
-    hipLaunchKernelGGL((oal_bwd_dq_inter_mfma<T, true>), dim3(nch * tpc, Hkv, B), blk, 0, stream, T_len, C, nch, Hq,
+    hipLaunchKernelGGL((oal_bwd_dq_inter_mfma<T, true>), dim3(nch * tpc, Hkv * kDkSplits, B), blk, 0, stream, T_len, C, nch, Hq,
                        Hkv, k, v, params, st, gv, gd, part);
     hipLaunchKernelGGL(oal_bwd_dv_inter<T>, g_ki, blk, 0, stream, T_len, C, nch, Hkv, k, st, part);
     hipLaunchKernelGGL(oal_bwd_kv_reduce, g_red, blk, 0, stream, kvrows, nslots, part, dk, dv);
