@@ -65,17 +65,17 @@ def _load():
     lib.oal_decode_workspace_bytes.argtypes, lib.oal_decode_workspace_bytes.restype = [dp], S
     lib.oal_params_pack.argtypes, lib.oal_params_pack.restype = [dp, hp, P, S], ctypes.c_int
     lib.oal_state_init.argtypes, lib.oal_state_init.restype = [dp, hp, P, P, P], ctypes.c_int
-    lib.oal_prefill.argtypes = [dp, I, I, P, P, P, P, P, P, P, P]
+    lib.oal_prefill.argtypes = [dp, I, I, P, P, P, P, P, P, S, P, P]
     lib.oal_prefill.restype = ctypes.c_int
-    lib.oal_prefill_timed.argtypes = [dp, I, I, P, P, P, P, P, P, P, P, ctypes.POINTER(P)]
+    lib.oal_prefill_timed.argtypes = [dp, I, I, P, P, P, P, P, P, S, P, P, ctypes.POINTER(P)]
     lib.oal_prefill_timed.restype = ctypes.c_int
-    lib.oal_prefill_varlen.argtypes = [dp, I, P, I, P, P, P, P, P, P, P, P]
+    lib.oal_prefill_varlen.argtypes = [dp, I, P, I, P, P, P, P, P, P, S, P, P]
     lib.oal_prefill_varlen.restype = ctypes.c_int
-    lib.oal_prefill_packed.argtypes = [dp, I, P, ctypes.c_int64, I, P, P, P, P, P, P, P, P]
+    lib.oal_prefill_packed.argtypes = [dp, I, P, ctypes.c_int64, I, P, P, P, P, P, P, S, P, P]
     lib.oal_prefill_packed.restype = ctypes.c_int
-    lib.oal_decode_step.argtypes = [dp, P, P, P, P, P, P, P, P]
+    lib.oal_decode_step.argtypes = [dp, P, P, P, P, P, P, S, P, P]
     lib.oal_decode_step.restype = ctypes.c_int
-    lib.oal_decode_step_indexed.argtypes = [dp, P, I, P, P, P, P, P, P, P, P]
+    lib.oal_decode_step_indexed.argtypes = [dp, P, I, P, P, P, P, P, P, S, P, P]
     lib.oal_decode_step_indexed.restype = ctypes.c_int
     lib.oal_status_string.argtypes, lib.oal_status_string.restype = [ctypes.c_int], ctypes.c_char_p
     lib.oal_timing_event_create.argtypes, lib.oal_timing_event_create.restype = [ctypes.POINTER(P)], ctypes.c_int
@@ -85,10 +85,10 @@ def _load():
     lib.oal_timing_elapsed_ms.restype = ctypes.c_int
     lib.oal_contribution_workspace_bytes.argtypes = [dp, I]
     lib.oal_contribution_workspace_bytes.restype = S
-    lib.oal_contribution.argtypes, lib.oal_contribution.restype = [dp, I, P, P, P, P, P, P], ctypes.c_int
+    lib.oal_contribution.argtypes, lib.oal_contribution.restype = [dp, I, P, P, P, S, P, P, P], ctypes.c_int
     lib.oal_prefill_backward_workspace_bytes.argtypes = [dp, I, I]
     lib.oal_prefill_backward_workspace_bytes.restype = S
-    lib.oal_prefill_backward.argtypes = [dp, I, I, P, P, P, P, P, P, P, P, P, P, P, P]
+    lib.oal_prefill_backward.argtypes = [dp, I, I, P, P, P, P, P, P, S, P, P, P, P, P, P]
     lib.oal_prefill_backward.restype = ctypes.c_int
     return lib
 
@@ -133,6 +133,21 @@ def _ptr(t) -> int | None:
     if not t.is_contiguous():
         raise ValueError("device buffers must be contiguous")
     return t.data_ptr()
+
+
+# a raw integer pointer carries no size: the caller vouches for it (tests of argument checks)
+_UNSIZED = (1 << 63) - 1
+
+
+def _nbytes(t, given=None) -> int:
+    """Size in bytes of a device buffer: `given` if the caller states it, else the tensor's."""
+    if given is not None:
+        return int(given)
+    if t is None:
+        return 0
+    if isinstance(t, int):
+        return _UNSIZED
+    return int(t.numel() * t.element_size())
 
 
 def _stream(stream):
@@ -184,38 +199,42 @@ def oal_state_init(dims: oal_dims, params: HeadParamsC, params_dev, state_dev=No
 
 
 def oal_prefill(dims: oal_dims, T: int, chunk: int, q, k, v, params_dev, state_dev, workspace, y,
-                stream=None):
+                stream=None, workspace_bytes=None):
     """y=None (and then q may be None) only advances the state."""
     _check("oal_prefill", _lib.oal_prefill(ctypes.byref(dims), int(T), int(chunk), _ptr(q), _ptr(k),
                                            _ptr(v), _ptr(params_dev), _ptr(state_dev),
-                                           _ptr(workspace), _ptr(y), _stream(stream)))
+                                           _ptr(workspace), _nbytes(workspace, workspace_bytes), _ptr(y),
+                                           _stream(stream)))
 
 
 def oal_prefill_varlen(dims: oal_dims, T: int, lengths, chunk: int, q, k, v, params_dev, state_dev,
-                       workspace, y, stream=None):
+                       workspace, y, stream=None, workspace_bytes=None):
     """Ragged batch padded to T: lengths is a device int32 tensor [batch]."""
     _check("oal_prefill_varlen", _lib.oal_prefill_varlen(
         ctypes.byref(dims), int(T), _ptr(lengths), int(chunk), _ptr(q), _ptr(k), _ptr(v),
-        _ptr(params_dev), _ptr(state_dev), _ptr(workspace), _ptr(y), _stream(stream)))
+        _ptr(params_dev), _ptr(state_dev), _ptr(workspace), _nbytes(workspace, workspace_bytes), _ptr(y),
+        _stream(stream)))
 
 
 def oal_prefill_packed(dims: oal_dims, T: int, cu_seqlens, total_tokens: int, chunk: int, q, k, v,
-                       params_dev, state_dev, workspace, y, stream=None):
+                       params_dev, state_dev, workspace, y, stream=None, workspace_bytes=None):
     """Packed ragged batch: q, y [n_q_heads, total, 64], k, v [n_kv_heads, total, 64];
     cu_seqlens is a device int32 tensor [batch + 1]."""
     _check("oal_prefill_packed", _lib.oal_prefill_packed(
         ctypes.byref(dims), int(T), _ptr(cu_seqlens), int(total_tokens), int(chunk), _ptr(q), _ptr(k),
-        _ptr(v), _ptr(params_dev), _ptr(state_dev), _ptr(workspace), _ptr(y), _stream(stream)))
+        _ptr(v), _ptr(params_dev), _ptr(state_dev), _ptr(workspace), _nbytes(workspace, workspace_bytes),
+        _ptr(y), _stream(stream)))
 
 
 def oal_prefill_timed(dims: oal_dims, T: int, chunk: int, q, k, v, params_dev, state_dev, workspace,
-                      y, marks, stream=None):
+                      y, marks, stream=None, workspace_bytes=None):
     """oal_prefill plus three caller-owned events (torch.cuda.Event, already created) recorded
     before the scan, between scan and readout, and after the readout."""
     handles = (ctypes.c_void_p * 3)(*[int(m.cuda_event) for m in marks])
     _check("oal_prefill_timed", _lib.oal_prefill_timed(
         ctypes.byref(dims), int(T), int(chunk), _ptr(q), _ptr(k), _ptr(v), _ptr(params_dev),
-        _ptr(state_dev), _ptr(workspace), _ptr(y), _stream(stream), handles))
+        _ptr(state_dev), _ptr(workspace), _nbytes(workspace, workspace_bytes), _ptr(y), _stream(stream),
+        handles))
 
 
 class TimingEvent:
@@ -243,21 +262,25 @@ class TimingEvent:
             self.cuda_event = None
 
 
-def oal_decode_step(dims: oal_dims, q, k, v, params_dev, state_dev, workspace, y, stream=None):
+def oal_decode_step(dims: oal_dims, q, k, v, params_dev, state_dev, workspace, y, stream=None,
+                    workspace_bytes=None):
     _check("oal_decode_step", _lib.oal_decode_step(ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v),
                                                    _ptr(params_dev), _ptr(state_dev),
-                                                   _ptr(workspace), _ptr(y), _stream(stream)))
+                                                   _ptr(workspace), _nbytes(workspace, workspace_bytes),
+                                                   _ptr(y), _stream(stream)))
 
 
 def oal_contribution_workspace_bytes(dims: oal_dims, T: int) -> int:
     return int(_lib.oal_contribution_workspace_bytes(ctypes.byref(dims), int(T)))
 
 
-def oal_contribution(dims: oal_dims, T: int, q, k, workspace, chi, chi_mean=None, stream=None):
+def oal_contribution(dims: oal_dims, T: int, q, k, workspace, chi, chi_mean=None, stream=None,
+                     workspace_bytes=None):
     """Causal contribution scores chi [batch, n_q_heads, 64] and (unless chi_mean is None)
     their prompt mean [n_q_heads, 64], both fp32 device tensors written by the library."""
     _check("oal_contribution", _lib.oal_contribution(ctypes.byref(dims), int(T), _ptr(q), _ptr(k),
-                                                     _ptr(workspace), _ptr(chi), _ptr(chi_mean),
+                                                     _ptr(workspace), _nbytes(workspace, workspace_bytes),
+                                                     _ptr(chi), _ptr(chi_mean),
                                                      _stream(stream)))
 
 
@@ -266,23 +289,24 @@ def oal_prefill_backward_workspace_bytes(dims: oal_dims, T: int, chunk: int) -> 
 
 
 def oal_prefill_backward(dims: oal_dims, T: int, chunk: int, q, k, v, dy, params_dev, workspace,
-                         dq, dk, dv, dL=None, deps=None, stream=None):
+                         dq, dk, dv, dL=None, deps=None, stream=None, workspace_bytes=None):
     """Gradients dq [batch, n_q_heads, T, 64], dk, dv [batch, n_kv_heads, T, 64] (fp32 device
     tensors written by the library) of sum(dy * y) for the prefill of T tokens from an empty
     prefix; with dL [n_q_heads, 65, 65] and deps [n_q_heads] (fp32 device tensors, or both
     None) also the coefficient gradients."""
     _check("oal_prefill_backward", _lib.oal_prefill_backward(
         ctypes.byref(dims), int(T), int(chunk), _ptr(q), _ptr(k), _ptr(v), _ptr(dy),
-        _ptr(params_dev), _ptr(workspace), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dL), _ptr(deps),
+        _ptr(params_dev), _ptr(workspace), _nbytes(workspace, workspace_bytes), _ptr(dq), _ptr(dk),
+        _ptr(dv), _ptr(dL), _ptr(deps),
         _stream(stream)))
 
 
 def oal_decode_step_indexed(dims: oal_dims, slots, pool_size: int, q, k, v, params_dev, state_pool,
-                            workspace, y, stream=None):
+                            workspace, y, stream=None, workspace_bytes=None):
     """Decode step on pool blocks: slots is a device int32 tensor [batch]."""
     _check("oal_decode_step_indexed", _lib.oal_decode_step_indexed(
         ctypes.byref(dims), _ptr(slots), int(pool_size), _ptr(q), _ptr(k), _ptr(v), _ptr(params_dev),
-        _ptr(state_pool), _ptr(workspace), _ptr(y), _stream(stream)))
+        _ptr(state_pool), _ptr(workspace), _nbytes(workspace, workspace_bytes), _ptr(y), _stream(stream)))
 
 
 # ---- buffer helper (torch allocations sized by the library) ------------------------------

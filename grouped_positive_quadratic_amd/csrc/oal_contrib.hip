@@ -32,6 +32,7 @@
 #include <stdint.h>
 
 #include "oal.h"
+#include "oal_device.h"
 #include "oal_internal.h"
 
 namespace {
@@ -180,8 +181,10 @@ __global__ __launch_bounds__(kThreads, 4) void oal_chi_kernel(
     }
     // 3. arrival: the last range of a (prompt, head) to arrive folds its ranges in order and
     //    writes chi. The agent-scope stores and loads are coherent across the XCDs' L2 caches;
-    //    the workgroup-scope fences order them around the counter (they wait for the stores)
-    //    without writing back L2. Each counter has a 128-byte line of its own.
+    //    the storing wave waits for its stores to complete before the barrier that precedes
+    //    the counter RMW, so they are performed before it (no L2 write-back). Each counter has
+    //    a 128-byte line of its own.
+    oal_wait_own_stores();
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
     __syncthreads();
     const int bh = b * n_q_heads + h;
@@ -228,7 +231,9 @@ __global__ __launch_bounds__(kThreads, 4) void oal_chi_kernel(
     if (tid == 0)
         __hip_atomic_store(counters + (size_t)bh * kCounterStride, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if (!chi_mean) return;
-    // 4. arrival per head: the last prompt writes the mean over prompts, in prompt order
+    // 4. arrival per head: the last prompt writes the mean over prompts, in prompt order (its
+    //    chi stores completed before the counter RMW, as above)
+    oal_wait_own_stores();
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
     __syncthreads();
     unsigned int *hc = counters + ((size_t)batch * n_q_heads + h) * kCounterStride;

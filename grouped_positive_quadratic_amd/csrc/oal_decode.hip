@@ -179,14 +179,17 @@ __global__ __launch_bounds__(kThreads) void oal_decode_kernel(
     }
     __syncthreads();
     // 4. cross-workgroup combine. Partials are written and read with agent-scope atomics, which
-    //    are coherent across the XCDs' L2 caches; the workgroup-scope fences order them around
-    //    the arrival counter (they wait for the stores to complete) without flushing L2.
+    //    are coherent across the XCDs' L2 caches. Every wave waits for its partial stores to
+    //    complete before the barrier, so all of them are performed before thread 0's arrival
+    //    RMW; the last workgroup to arrive issues its loads only after its own RMW returned,
+    //    so it reads every split's partial (no L2 write-back is needed for that).
     float *mypart = partial + ((size_t)bkv * kSplits + split) * MAXH * OAL_V1;
     for (int idx = tid; idx < n_rep * OAL_V1; idx += kThreads) {
         int h = idx / OAL_V1, c = idx % OAL_V1;
         __hip_atomic_store(mypart + idx, s_red[0][h][c] + s_red[1][h][c] + s_red[2][h][c] + s_red[3][h][c],
                            __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
+    oal_wait_own_stores();
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
     __syncthreads();
     if (tid == 0) {

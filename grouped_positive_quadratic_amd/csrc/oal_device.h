@@ -89,3 +89,14 @@ __device__ inline oal_f32x4 oal_splat(float x) {
     r[0] = x; r[1] = x; r[2] = x; r[3] = x;
     return r;
 }
+
+// Cross-workgroup publish (the decode and contribution combines): a workgroup stores its
+// partial sums with agent-scope atomic stores, which are coherent across the XCDs' L2
+// caches, then one thread counts the workgroup in with an agent-scope RMW on an arrival
+// counter. The stores of every wave must be performed before that RMW: each wave waits for
+// its own outstanding stores (gfx9 counts stores in vmcnt; this is s_waitcnt vmcnt(0) with
+// the other counters left at their maxima, expcnt 7 and lgkmcnt 15) before the barrier that
+// precedes the RMW. A release fence at agent scope would do the same and also write back the
+// whole L2 (full of the state rows the decode just wrote), which costs far more.
+__device__ inline void oal_wait_own_stores() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+

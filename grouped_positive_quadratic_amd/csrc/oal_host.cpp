@@ -287,8 +287,8 @@ oal_status oal_state_init(const oal_dims *d, const oal_head_params *hp, void *pa
 
 static oal_status prefill_impl(const oal_dims *d, int32_t T, const int32_t *lens, const int32_t *cu,
                                int64_t total, int32_t chunk, const void *q, const void *k, const void *v,
-                               const void *params_dev, float *state_dev, void *workspace, float *y,
-                               hipStream_t stream, hipEvent_t *marks) {
+                               const void *params_dev, float *state_dev, void *workspace, size_t ws_bytes,
+                               float *y, hipStream_t stream, hipEvent_t *marks) {
     oal_status st = check_dims(d);
     if (st != OAL_OK) return st;
     if (T < 0) return OAL_E_SHAPE;
@@ -301,6 +301,7 @@ static oal_status prefill_impl(const oal_dims *d, int32_t T, const int32_t *lens
         (reinterpret_cast<uintptr_t>(lens) & 3u) || (reinterpret_cast<uintptr_t>(cu) & 3u))
         return OAL_E_ALIGN;
     if ((T + chunk - 1) / chunk > 65535) return OAL_E_UNSUPPORTED;
+    if (ws_bytes < oal_prefill_ws_bytes_impl(*d, T, chunk)) return OAL_E_ARG;
     hipError_t e = oal_launch_prefill(*d, T, lens, cu, (long long)total, chunk, q, k, v, params_dev, state_dev,
                                       workspace, y, stream, marks);
     if (e != hipSuccess) {
@@ -312,44 +313,45 @@ static oal_status prefill_impl(const oal_dims *d, int32_t T, const int32_t *lens
 
 oal_status oal_prefill(const oal_dims *d, int32_t T, int32_t chunk, const void *q, const void *k,
                        const void *v, const void *params_dev, float *state_dev, void *workspace,
-                       float *y, hipStream_t stream) {
-    return prefill_impl(d, T, nullptr, nullptr, 0, chunk, q, k, v, params_dev, state_dev, workspace, y, stream,
-                        nullptr);
+                       size_t workspace_bytes, float *y, hipStream_t stream) {
+    return prefill_impl(d, T, nullptr, nullptr, 0, chunk, q, k, v, params_dev, state_dev, workspace,
+                        workspace_bytes, y, stream, nullptr);
 }
 
 oal_status oal_prefill_timed(const oal_dims *d, int32_t T, int32_t chunk, const void *q,
                              const void *k, const void *v, const void *params_dev,
-                             float *state_dev, void *workspace, float *y, hipStream_t stream,
-                             hipEvent_t marks[3]) {
+                             float *state_dev, void *workspace, size_t workspace_bytes, float *y,
+                             hipStream_t stream, hipEvent_t marks[3]) {
     if (!marks || !marks[0] || !marks[1] || !marks[2]) return OAL_E_ARG;
-    return prefill_impl(d, T, nullptr, nullptr, 0, chunk, q, k, v, params_dev, state_dev, workspace, y, stream,
-                        marks);
+    return prefill_impl(d, T, nullptr, nullptr, 0, chunk, q, k, v, params_dev, state_dev, workspace,
+                        workspace_bytes, y, stream, marks);
 }
 
 oal_status oal_prefill_varlen(const oal_dims *d, int32_t T, const int32_t *lengths, int32_t chunk,
                               const void *q, const void *k, const void *v, const void *params_dev,
-                              float *state_dev, void *workspace, float *y, hipStream_t stream) {
+                              float *state_dev, void *workspace, size_t workspace_bytes, float *y,
+                              hipStream_t stream) {
     if (!lengths && check_dims(d) == OAL_OK && T > 0 && d->batch > 0) return OAL_E_ARG;
-    return prefill_impl(d, T, lengths, nullptr, 0, chunk, q, k, v, params_dev, state_dev, workspace, y, stream,
-                        nullptr);
+    return prefill_impl(d, T, lengths, nullptr, 0, chunk, q, k, v, params_dev, state_dev, workspace,
+                        workspace_bytes, y, stream, nullptr);
 }
 
 oal_status oal_prefill_packed(const oal_dims *d, int32_t T, const int32_t *cu_seqlens, int64_t total_tokens,
                               int32_t chunk, const void *q, const void *k, const void *v,
-                              const void *params_dev, float *state_dev, void *workspace, float *y,
-                              hipStream_t stream) {
+                              const void *params_dev, float *state_dev, void *workspace,
+                              size_t workspace_bytes, float *y, hipStream_t stream) {
     if (total_tokens < 0) return OAL_E_SHAPE;
     if (check_dims(d) == OAL_OK && T > 0 && d->batch > 0) {
         if (!cu_seqlens) return OAL_E_ARG;
         if (total_tokens == 0) return OAL_OK;     // every sequence is empty
     }
     return prefill_impl(d, T, nullptr, cu_seqlens, total_tokens, chunk, q, k, v, params_dev, state_dev,
-                        workspace, y, stream, nullptr);
+                        workspace, workspace_bytes, y, stream, nullptr);
 }
 
 oal_status oal_decode_step(const oal_dims *d, const void *q, const void *k, const void *v,
-                           const void *params_dev, float *state_dev, void *workspace, float *y,
-                           hipStream_t stream) {
+                           const void *params_dev, float *state_dev, void *workspace, size_t workspace_bytes,
+                           float *y, hipStream_t stream) {
     oal_status st = check_dims(d);
     if (st != OAL_OK) return st;
     if (d->n_q_heads / d->n_kv_heads > 16) return OAL_E_UNSUPPORTED;
@@ -358,6 +360,7 @@ oal_status oal_decode_step(const oal_dims *d, const void *q, const void *k, cons
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(params_dev) ||
         !aligned16(state_dev) || !aligned16(workspace) || !aligned16(y))
         return OAL_E_ALIGN;
+    if (workspace_bytes < oal_decode_ws_bytes_impl(*d)) return OAL_E_ARG;
     hipError_t e = oal_launch_decode(*d, q, k, v, params_dev, state_dev, nullptr, 0, workspace, y, stream);
     if (e != hipSuccess) {
         (void)hipGetLastError();
@@ -368,7 +371,8 @@ oal_status oal_decode_step(const oal_dims *d, const void *q, const void *k, cons
 
 oal_status oal_decode_step_indexed(const oal_dims *d, const int32_t *slots, int32_t pool_size,
                                    const void *q, const void *k, const void *v, const void *params_dev,
-                                   float *state_pool, void *workspace, float *y, hipStream_t stream) {
+                                   float *state_pool, void *workspace, size_t workspace_bytes, float *y,
+                                   hipStream_t stream) {
     oal_status st = check_dims(d);
     if (st != OAL_OK) return st;
     if (d->n_q_heads / d->n_kv_heads > 16) return OAL_E_UNSUPPORTED;
@@ -378,6 +382,7 @@ oal_status oal_decode_step_indexed(const oal_dims *d, const int32_t *slots, int3
     if ((reinterpret_cast<uintptr_t>(slots) & 3u) || !aligned16(q) || !aligned16(k) || !aligned16(v) ||
         !aligned16(params_dev) || !aligned16(state_pool) || !aligned16(workspace) || !aligned16(y))
         return OAL_E_ALIGN;
+    if (workspace_bytes < oal_decode_ws_bytes_impl(*d)) return OAL_E_ARG;
     hipError_t e = oal_launch_decode(*d, q, k, v, params_dev, state_pool, slots, pool_size, workspace, y, stream);
     if (e != hipSuccess) {
         (void)hipGetLastError();
@@ -392,7 +397,8 @@ size_t oal_contribution_workspace_bytes(const oal_dims *d, int32_t T) {
 }
 
 oal_status oal_contribution(const oal_dims *d, int32_t T, const void *q, const void *k,
-                            void *workspace, float *chi, float *chi_mean, hipStream_t stream) {
+                            void *workspace, size_t workspace_bytes, float *chi, float *chi_mean,
+                            hipStream_t stream) {
     oal_status st = check_dims(d);
     if (st != OAL_OK) return st;
     if (T < 1 || d->batch < 1) return OAL_E_SHAPE;
@@ -401,6 +407,7 @@ oal_status oal_contribution(const oal_dims *d, int32_t T, const void *q, const v
     if (!aligned16(q) || !aligned16(k) || !aligned16(workspace) || !aligned16(chi) ||
         (chi_mean && !aligned16(chi_mean)))
         return OAL_E_ALIGN;
+    if (workspace_bytes < oal_contribution_ws_bytes_impl(*d, T)) return OAL_E_ARG;
     hipError_t e = oal_launch_contribution(*d, T, q, k, workspace, chi, chi_mean, stream);
     if (e != hipSuccess) {
         (void)hipGetLastError();
@@ -424,7 +431,8 @@ size_t oal_prefill_backward_workspace_bytes(const oal_dims *d, int32_t T, int32_
 
 oal_status oal_prefill_backward(const oal_dims *d, int32_t T, int32_t chunk, const void *q, const void *k,
                                 const void *v, const float *dy, const void *params_dev, void *workspace,
-                                float *dq, float *dk, float *dv, float *dL, float *deps, hipStream_t stream) {
+                                size_t workspace_bytes, float *dq, float *dk, float *dv, float *dL, float *deps,
+                                hipStream_t stream) {
     oal_status st = check_dims(d);
     if (st != OAL_OK) return st;
     if (T < 0) return OAL_E_SHAPE;
@@ -437,6 +445,7 @@ oal_status oal_prefill_backward(const oal_dims *d, int32_t T, int32_t chunk, con
         !aligned16(workspace) || !aligned16(dq) || !aligned16(dk) || !aligned16(dv) ||
         (reinterpret_cast<uintptr_t>(dL) & 3u) || (reinterpret_cast<uintptr_t>(deps) & 3u))
         return OAL_E_ALIGN;
+    if (workspace_bytes < oal_backward_ws_bytes_impl(*d, T, chunk)) return OAL_E_ARG;
     hipError_t e = oal_launch_backward(*d, T, chunk, q, k, v, dy, params_dev, workspace, dq, dk, dv, dL, deps,
                                        stream);
     if (e != hipSuccess) {

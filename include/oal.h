@@ -39,6 +39,11 @@
  * Streams: every call enqueues work on `stream` and returns; the caller synchronises.
  * oal_state_init additionally waits for its host-to-device copy before returning.
  *
+ * Workspaces: every call that takes a `workspace` also takes `workspace_bytes`, the size of
+ * the buffer the caller passes. It must be at least the matching *_workspace_bytes() value
+ * for the call's dims (and T, chunk); a smaller buffer gives OAL_E_ARG and nothing is
+ * enqueued, so an undersized workspace is an error code, never a write past its end.
+ *
  * Errors: arguments are validated on the host before anything is enqueued; on any error
  * nothing is enqueued and a status code is returned. HIP launch failures map to OAL_E_HIP.
  * NaN/Inf in q, k, v propagate to y. eps = 0 together with a singular L can make a
@@ -136,7 +141,7 @@ oal_status oal_state_init(const oal_dims *dims, const oal_head_params *hp, void 
  * into the input state and tokens 0..i of this call). T = 0 is a no-op. */
 oal_status oal_prefill(const oal_dims *dims, int32_t T, int32_t chunk, const void *q,
                        const void *k, const void *v, const void *params_dev, float *state_dev,
-                       void *workspace, float *y, hipStream_t stream);
+                       void *workspace, size_t workspace_bytes, float *y, hipStream_t stream);
 
 /* oal_prefill for measurement: identical work, and additionally records the caller-owned
  * events marks[0] on `stream` before the first kernel, marks[1] after the chunk-state scan
@@ -145,8 +150,8 @@ oal_status oal_prefill(const oal_dims *dims, int32_t T, int32_t chunk, const voi
  * from oal_timing_event_create keep the recording cheap. */
 oal_status oal_prefill_timed(const oal_dims *dims, int32_t T, int32_t chunk, const void *q,
                              const void *k, const void *v, const void *params_dev,
-                             float *state_dev, void *workspace, float *y, hipStream_t stream,
-                             hipEvent_t marks[3]);
+                             float *state_dev, void *workspace, size_t workspace_bytes, float *y,
+                             hipStream_t stream, hipEvent_t marks[3]);
 
 /* oal_prefill for a ragged batch (sequences of different lengths, padded to T): sequence b
  * takes the first lengths[b] tokens of its rows of q, k, v ([batch, heads, T, 64], as in
@@ -157,7 +162,8 @@ oal_status oal_prefill_timed(const oal_dims *dims, int32_t T, int32_t chunk, con
  * A batch whose lengths are all T gives the results of oal_prefill. */
 oal_status oal_prefill_varlen(const oal_dims *dims, int32_t T, const int32_t *lengths, int32_t chunk,
                               const void *q, const void *k, const void *v, const void *params_dev,
-                              float *state_dev, void *workspace, float *y, hipStream_t stream);
+                              float *state_dev, void *workspace, size_t workspace_bytes, float *y,
+                              hipStream_t stream);
 
 /* oal_prefill for a packed ragged batch: the sequences are concatenated along the token axis,
  * sequence b being tokens cu_seqlens[b] .. cu_seqlens[b+1] - 1 of every head.
@@ -175,7 +181,7 @@ oal_status oal_prefill_varlen(const oal_dims *dims, int32_t T, const int32_t *le
 oal_status oal_prefill_packed(const oal_dims *dims, int32_t T, const int32_t *cu_seqlens,
                               int64_t total_tokens, int32_t chunk, const void *q, const void *k,
                               const void *v, const void *params_dev, float *state_dev,
-                              void *workspace, float *y, hipStream_t stream);
+                              void *workspace, size_t workspace_bytes, float *y, hipStream_t stream);
 
 /* One decode step: appends one token per sequence to the prefix states and reads out the
  * attention of each query head over all tokens so far (the new one included).
@@ -188,8 +194,8 @@ oal_status oal_prefill_packed(const oal_dims *dims, int32_t T, const int32_t *cu
  *                another. Calls that share a workspace must be ordered (same stream or
  *                synchronised). */
 oal_status oal_decode_step(const oal_dims *dims, const void *q, const void *k, const void *v,
-                           const void *params_dev, float *state_dev, void *workspace, float *y,
-                           hipStream_t stream);
+                           const void *params_dev, float *state_dev, void *workspace,
+                           size_t workspace_bytes, float *y, hipStream_t stream);
 
 /* Causal contribution scores of the q/k dims (reproduction notes, section "核心公式", first
  * display; the per-prompt causal statistics that feed the tail grouping in the method's
@@ -218,7 +224,8 @@ oal_status oal_decode_step(const oal_dims *dims, const void *q, const void *k, c
 #define OAL_CHI_MAX_T (1 << 22)
 size_t oal_contribution_workspace_bytes(const oal_dims *dims, int32_t T);
 oal_status oal_contribution(const oal_dims *dims, int32_t T, const void *q, const void *k,
-                            void *workspace, float *chi, float *chi_mean, hipStream_t stream);
+                            void *workspace, size_t workspace_bytes, float *chi, float *chi_mean,
+                            hipStream_t stream);
 
 /* Backward of oal_prefill from an empty prefix (reproduction notes of arXiv 2610.13674,
  * section "核心公式": kappa, the H-state recurrence and the readout; the gradients follow by
@@ -248,7 +255,8 @@ oal_status oal_contribution(const oal_dims *dims, int32_t T, const void *q, cons
 size_t oal_prefill_backward_workspace_bytes(const oal_dims *dims, int32_t T, int32_t chunk);
 oal_status oal_prefill_backward(const oal_dims *dims, int32_t T, int32_t chunk, const void *q,
                                 const void *k, const void *v, const float *dy,
-                                const void *params_dev, void *workspace, float *dq, float *dk,
+                                const void *params_dev, void *workspace, size_t workspace_bytes,
+                                float *dq, float *dk,
                                 float *dv, float *dL, float *deps, hipStream_t stream);
 
 /* Decode step for sequences whose states live in a pool (serving: a batch of active
@@ -271,7 +279,7 @@ oal_status oal_prefill_backward(const oal_dims *dims, int32_t T, int32_t chunk, 
 oal_status oal_decode_step_indexed(const oal_dims *dims, const int32_t *slots, int32_t pool_size,
                                    const void *q, const void *k, const void *v,
                                    const void *params_dev, float *state_pool, void *workspace,
-                                   float *y, hipStream_t stream);
+                                   size_t workspace_bytes, float *y, hipStream_t stream);
 
 /* Timing events for oal_prefill_timed and for bracketing a timed region. A default HIP event
  * performs a system-scope release when it is recorded, which writes back the L2: between two

@@ -67,9 +67,9 @@ def test_sizes():
     assert gpq.oal_prefill_backward_workspace_bytes(bad, 64, 64) == 0
 
 
-def _code(fn, *args):
+def _code(fn, *args, **kw):
     try:
-        fn(*args)
+        fn(*args, **kw)
     except gpq.OALError as e:
         return e.code
     return 0
@@ -132,6 +132,40 @@ def test_validation_errors_enqueue_nothing():
     assert _code(gpq.oal_prefill_backward, d, 64 * 65536, 64, *b9, 0) == 5    # > 65535 chunks
     assert _code(gpq.oal_prefill_backward, gpq.make_dims(1, 3, 2, "bf16"), 8, 64, *b9, 0) == 2
     assert _code(gpq.oal_prefill_backward, gpq.make_dims(1, 8192, 8192, "bf16"), 8, 64, *b9, 0) == 5  # grid
+
+
+def test_undersized_workspace_is_an_error():
+    """Every call that takes a workspace compares the size it is given with the matching
+    *_workspace_bytes value and returns OAL_E_ARG (nothing enqueued) when it is smaller, so
+    a workspace sized for another shape or build cannot be written past its end. Only the
+    undersized case is run here: the pointers are fake."""
+    A = 4096
+    for dt in ("bf16", "f32"):
+        d = gpq.make_dims(2, 14, 2, dt)
+        for T, C in ((300, 64), (4096, 128), (77, 256)):
+            need = gpq.oal_prefill_workspace_bytes(d, T, C)
+            assert need > 0
+            for small_ws in (0, 16, need - 1):
+                kw = dict(workspace_bytes=small_ws)
+                assert _code(gpq.oal_prefill, d, T, C, *([A] * 7), 0, **kw) == 1
+                assert _code(gpq.oal_prefill, d, T, C, None, A, A, A, A, A, None, 0, **kw) == 1
+                assert _code(gpq.oal_prefill_varlen, d, T, A, C, *([A] * 7), 0, **kw) == 1
+                assert _code(gpq.oal_prefill_packed, d, T, A, 2 * T, C, *([A] * 7), 0, **kw) == 1
+            need_b = gpq.oal_prefill_backward_workspace_bytes(d, T, C)
+            assert _code(gpq.oal_prefill_backward, d, T, C, *([A] * 9), None, None, 0,
+                         workspace_bytes=need_b - 1) == 1
+        need_d = gpq.oal_decode_workspace_bytes(d)
+        assert _code(gpq.oal_decode_step, d, *([A] * 7), 0, workspace_bytes=need_d - 1) == 1
+        assert _code(gpq.oal_decode_step_indexed, d, A, 8, *([A] * 7), 0, workspace_bytes=need_d - 1) == 1
+        need_c = gpq.oal_contribution_workspace_bytes(d, 4096)
+        assert _code(gpq.oal_contribution, d, 4096, A, A, A, A, A, 0, workspace_bytes=need_c - 1) == 1
+        assert _code(gpq.oal_contribution, d, 4096, A, A, A, A, None, 0, workspace_bytes=0) == 1
+    # a workspace sized for a smaller shape is too small for a larger one
+    d1, d8 = gpq.make_dims(1, 14, 2, "bf16"), gpq.make_dims(8, 14, 2, "bf16")
+    assert _code(gpq.oal_decode_step, d8, *([A] * 7), 0,
+                 workspace_bytes=gpq.oal_decode_workspace_bytes(d1)) == 1
+    assert _code(gpq.oal_prefill, d8, 4096, 128, *([A] * 7), 0,
+                 workspace_bytes=gpq.oal_prefill_workspace_bytes(d1, 4096, 128)) == 1
 
 
 def test_param_validation():

@@ -17,8 +17,9 @@ torch = pytest.importorskip("torch")
 from gpu_util import to_dev  # noqa: E402
 import grouped_positive_quadratic_amd as gpq  # noqa: E402
 
-# fp32 arithmetic throughout (the inputs are exact in fp32 for both dtypes)
-BWD_TOL = 2e-4
+# fp32 arithmetic throughout (the inputs are exact in fp32 for both dtypes): the bound of
+# the fp32 forward tests. Measured errors are below 2e-6.
+BWD_TOL = 1e-5
 # dL and deps sum dkappa_ij sbar sbar^T over every causal pair, and each query's dkappa row is
 # orthogonal to its kappa row (sum_j kappa_ij dkappa_ij = g_i . u_i = 0): the result is a small
 # difference of large terms, so the same fp32 roundings give a larger error relative to it.

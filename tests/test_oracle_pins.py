@@ -554,3 +554,48 @@ def test_backward_pins_catch_planted_mistakes(name, tmp_path):
         assert failed, f"planted mistake {name} passed the backward pins"
     finally:
         oracle._lib = saved
+
+
+# --------------------------------------------------------------------------------------
+# 6. The parity metric itself. Every GPU parity test and smoke() decide pass or fail with
+# oracle.row_error = max over rows of ||y_i - y*_i||_inf / ||y*_i||_inf (row-normwise
+# relative error over the last axis). Hand-computed values pin it; each case names the
+# plausible mistake it catches.
+
+def test_row_error_hand_computed():
+    re_ = oracle.row_error
+    # one row: |2.5 - 2| / max(|1|, |2|, |-4|) = 0.5 / 4
+    assert re_([[1.0, 2.5, -4.0]], [[1.0, 2.0, -4.0]]) == 0.125
+    # a zero reference entry: its absolute error counts against the row norm, 0.3 / 3
+    # (an elementwise ratio would divide by zero)
+    assert abs(re_([[0.3, 3.0]], [[0.0, 3.0]]) - 0.1) < 1e-15
+    # the error sits in a small-magnitude column: normwise 1e-6 / 10 = 1e-7, whereas an
+    # elementwise relative error would report 1.0
+    assert abs(re_([[2e-6, 10.0]], [[1e-6, 10.0]]) - 1e-7) < 1e-20
+    # per-row normalisation: row 0 has 0.5 / 100, row 1 has 0.001 / 0.01 = 0.1; a global
+    # normaliser would give 0.5 / 100 = 0.005
+    assert abs(re_([[100.5, 0.0], [0.011, 0.0]], [[100.0, 0.0], [0.01, 0.0]]) - 0.1) < 1e-12
+    # max over rows, not mean: rows at 0.25 and 0 give 0.25 (the mean would be 0.125)
+    assert re_([[1.25, 0.0], [3.0, -3.0]], [[1.0, 0.0], [3.0, -3.0]]) == 0.25
+    # the last axis is the row: [B, H, T, d] arrays, worst row (b=1, h=0, t=2) = 0.5 / 2
+    y_ref = np.ones((2, 3, 4, 5))
+    y_ref[1, 0, 2] = [2.0, -2.0, 1.0, 0.5, 0.0]
+    y_ref[1, 0, 0, 1] = 10.0    # the error's column has norm 10, its row norm 2
+    y = y_ref.copy()
+    y[1, 0, 2, 1] += 0.5
+    y[0, 2, 3, 4] += 0.1        # a second, smaller row error (0.1 / 1)
+    assert re_(y, y_ref) == 0.25
+    # read along the wrong axis the same data give max(0.5 / 10, 0.1 / 1) = 0.1
+    assert abs(re_(np.swapaxes(y, -1, -2), np.swapaxes(y_ref, -1, -2)) - 0.1) < 1e-12
+    # an exact match is 0, an empty array is 0
+    assert re_(y_ref, y_ref) == 0.0 and re_(np.zeros((0, 64)), np.zeros((0, 64))) == 0.0
+
+
+def test_row_error_nan_and_inf_fail():
+    """A NaN or Inf output anywhere makes the metric NaN or Inf, so `err <= tol` is False."""
+    y_ref = np.ones((3, 4))
+    for bad in (np.nan, np.inf, -np.inf):
+        y = y_ref.copy()
+        y[1, 2] = bad
+        e = oracle.row_error(y, y_ref)
+        assert not (e <= 3e-2), (bad, e)
