@@ -26,7 +26,8 @@ EXPORTED = ("oal_params_bytes", "oal_state_bytes", "oal_prefill_workspace_bytes"
             "oal_timing_event_destroy", "oal_timing_event_record", "oal_timing_elapsed_ms",
             "oal_contribution_workspace_bytes", "oal_contribution", "oal_decode_step_indexed",
             "oal_prefill_varlen", "oal_prefill_packed", "oal_prefill_backward_workspace_bytes",
-            "oal_prefill_backward")
+            "oal_prefill_backward", "oal_decode_step_noalloc")
+DECODE_NOALLOC_MAX_BLOCKS = 256   # OAL_DECODE_NOALLOC_MAX_BLOCKS
 
 
 class OALError(RuntimeError):
@@ -77,6 +78,8 @@ def _load():
     lib.oal_decode_step.restype = ctypes.c_int
     lib.oal_decode_step_indexed.argtypes = [dp, P, I, P, P, P, P, P, P, S, P, P]
     lib.oal_decode_step_indexed.restype = ctypes.c_int
+    lib.oal_decode_step_noalloc.argtypes = [dp, P, P, P, P, P, P, P]
+    lib.oal_decode_step_noalloc.restype = ctypes.c_int
     lib.oal_status_string.argtypes, lib.oal_status_string.restype = [ctypes.c_int], ctypes.c_char_p
     lib.oal_timing_event_create.argtypes, lib.oal_timing_event_create.restype = [ctypes.POINTER(P)], ctypes.c_int
     lib.oal_timing_event_destroy.argtypes, lib.oal_timing_event_destroy.restype = [P], ctypes.c_int
@@ -268,6 +271,13 @@ def oal_decode_step(dims: oal_dims, q, k, v, params_dev, state_dev, workspace, y
                                                    _ptr(params_dev), _ptr(state_dev),
                                                    _ptr(workspace), _nbytes(workspace, workspace_bytes),
                                                    _ptr(y), _stream(stream)))
+
+
+def oal_decode_step_noalloc(dims: oal_dims, q, k, v, params_dev, state_dev, y, stream=None):
+    """oal_decode_step with the library's static per-GPU workspace (no caller buffer)."""
+    _check("oal_decode_step_noalloc", _lib.oal_decode_step_noalloc(
+        ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v), _ptr(params_dev), _ptr(state_dev), _ptr(y),
+        _stream(stream)))
 
 
 def oal_contribution_workspace_bytes(dims: oal_dims, T: int) -> int:

@@ -22,6 +22,8 @@
 // fresh state rows.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
+
 #include "oal.h"
 #include "oal_device.h"
 #include "oal_internal.h"
@@ -241,6 +243,64 @@ size_t oal_decode_ws_bytes_impl(const oal_dims &d) {
     size_t bkv = (size_t)d.batch * d.n_kv_heads;
     size_t cbytes = (bkv * sizeof(unsigned int) + 255) / 256 * 256;
     return cbytes + bkv * kSplits * 16 * OAL_V1 * sizeof(float);
+}
+
+hipError_t oal_launch_decode(const oal_dims &d, const void *q, const void *k, const void *v,
+                             const void *params, float *state, const int *slots, int pool_size, void *ws,
+                             float *y, hipStream_t stream);
+
+// ---- allocation-free variant --------------------------------------------------------------
+// The workspace of up to OAL_DECODE_NOALLOC_MAX_BLOCKS (sequence, KV head) blocks as a static
+// device array of the library: each GPU the library runs on holds its own copy until the
+// process ends. Host code never passes the array's name to a kernel (on the host it is only a
+// stand-in symbol): its device address is looked up once per device with that device current
+// and kept, and that address is what the kernels receive.
+namespace {
+constexpr size_t kNoAllocBytes =
+    ((size_t)OAL_DECODE_NOALLOC_MAX_BLOCKS * sizeof(unsigned int) + 255) / 256 * 256 +
+    (size_t)OAL_DECODE_NOALLOC_MAX_BLOCKS * kSplits * 16 * OAL_V1 * sizeof(float);
+constexpr int kNoAllocDevices = 64;
+std::atomic<void *> g_scratch_addr[kNoAllocDevices];
+
+// arrival counters of the combine back to zero (a kernel, not a memset: a caller may capture
+// the call into a graph)
+__global__ __launch_bounds__(256) void oal_zero_counters(unsigned int *__restrict__ c, int n) {
+    const int i = blockIdx.x * 256 + threadIdx.x;
+    if (i < n) c[i] = 0u;
+}
+}  // namespace
+
+static __device__ __align__(256) unsigned char scratch[kNoAllocBytes];
+
+hipError_t oal_decode_scratch_addr(void **out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kNoAllocDevices) return hipErrorInvalidDevice;
+    void *p = g_scratch_addr[dev].load(std::memory_order_acquire);
+    if (!p) {
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        if (!p) return hipErrorInvalidSymbol;
+        g_scratch_addr[dev].store(p, std::memory_order_release);
+    }
+    *out = p;
+    return hipSuccess;
+}
+
+hipError_t oal_launch_decode_noalloc(const oal_dims &d, const void *q, const void *k, const void *v,
+                                     const void *params, float *state, float *y, hipStream_t stream) {
+    static_assert(kNoAllocBytes % 256 == 0, "scratch size");
+    void *ws = nullptr;
+    hipError_t e = oal_decode_scratch_addr(&ws);
+    if (e != hipSuccess) return e;
+    if (oal_decode_ws_bytes_impl(d) > kNoAllocBytes) return hipErrorInvalidValue;   // checked by the caller too
+    const int bkv = d.batch * d.n_kv_heads;
+    // the array keeps the previous call's contents: its counters start at zero here
+    hipLaunchKernelGGL(oal_zero_counters, dim3((bkv + 255) / 256), dim3(256), 0, stream,
+                       reinterpret_cast<unsigned int *>(ws), bkv);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    return oal_launch_decode(d, q, k, v, params, state, nullptr, 0, ws, y, stream);
 }
 
 hipError_t oal_launch_decode(const oal_dims &d, const void *q, const void *k, const void *v,

@@ -23,6 +23,8 @@ hipError_t oal_launch_prefill(const oal_dims &d, int T_len, const int *lens, con
                               const void *v, const void *params, float *state, void *ws, float *y,
                               hipStream_t stream, hipEvent_t *marks);
 size_t oal_decode_ws_bytes_impl(const oal_dims &d);
+hipError_t oal_launch_decode_noalloc(const oal_dims &d, const void *q, const void *k, const void *v,
+                                     const void *params, float *state, float *y, hipStream_t stream);
 hipError_t oal_launch_contribution(const oal_dims &d, int T_len, const void *q, const void *k, void *ws,
                                    float *chi, float *chi_mean, hipStream_t stream);
 size_t oal_contribution_ws_bytes_impl(const oal_dims &d, int T_len);
@@ -384,6 +386,25 @@ oal_status oal_decode_step_indexed(const oal_dims *d, const int32_t *slots, int3
         return OAL_E_ALIGN;
     if (workspace_bytes < oal_decode_ws_bytes_impl(*d)) return OAL_E_ARG;
     hipError_t e = oal_launch_decode(*d, q, k, v, params_dev, state_pool, slots, pool_size, workspace, y, stream);
+    if (e != hipSuccess) {
+        (void)hipGetLastError();
+        return OAL_E_HIP;
+    }
+    return OAL_OK;
+}
+
+oal_status oal_decode_step_noalloc(const oal_dims *d, const void *q, const void *k, const void *v,
+                                   const void *params_dev, float *state_dev, float *y, hipStream_t stream) {
+    oal_status st = check_dims(d);
+    if (st != OAL_OK) return st;
+    if (d->n_q_heads / d->n_kv_heads > 16) return OAL_E_UNSUPPORTED;
+    if ((long long)d->batch * d->n_kv_heads > OAL_DECODE_NOALLOC_MAX_BLOCKS) return OAL_E_UNSUPPORTED;
+    if (d->batch == 0) return OAL_OK;
+    if (!q || !k || !v || !params_dev || !state_dev || !y) return OAL_E_ARG;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(params_dev) || !aligned16(state_dev) ||
+        !aligned16(y))
+        return OAL_E_ALIGN;
+    hipError_t e = oal_launch_decode_noalloc(*d, q, k, v, params_dev, state_dev, y, stream);
     if (e != hipSuccess) {
         (void)hipGetLastError();
         return OAL_E_HIP;

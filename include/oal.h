@@ -197,6 +197,20 @@ oal_status oal_decode_step(const oal_dims *dims, const void *q, const void *k, c
                            const void *params_dev, float *state_dev, void *workspace,
                            size_t workspace_bytes, float *y, hipStream_t stream);
 
+/* oal_decode_step without a caller workspace, for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc). Same
+ * kernel, arguments (minus the workspace) and results as oal_decode_step, bit for bit. Its
+ * workspace is a static device array inside the library, one per GPU, sized for
+ * OAL_DECODE_NOALLOC_MAX_BLOCKS (sequence, KV head) blocks (about 12.8 MB) and held until the
+ * process ends; the call allocates nothing and zeroes the array's counters itself (with a
+ * kernel) before the step. batch * n_kv_heads above the maximum gives OAL_E_UNSUPPORTED.
+ * All calls on one GPU share that GPU's array: calls that overlap in time on one GPU (other
+ * streams, other threads) race and must not be issued; order them on one stream. */
+#define OAL_DECODE_NOALLOC_MAX_BLOCKS 256
+oal_status oal_decode_step_noalloc(const oal_dims *dims, const void *q, const void *k, const void *v,
+                                   const void *params_dev, float *state_dev, float *y,
+                                   hipStream_t stream);
+
 /* Causal contribution scores of the q/k dims (reproduction notes, section "核心公式", first
  * display; the per-prompt causal statistics that feed the tail grouping in the method's
  * flowchart). For every prompt p (a sequence of the batch), query head h (KV head

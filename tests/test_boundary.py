@@ -108,6 +108,13 @@ def test_validation_errors_enqueue_nothing():
     assert _code(gpq.oal_decode_step_indexed, d, A, 4, A, A, A, A, A + 8, A, A, 0) == 4
     assert _code(gpq.oal_decode_step_indexed, gpq.make_dims(1, 17, 1, "bf16"), A, 4, *ix, 0) == 5
     assert _code(gpq.oal_decode_step_indexed, gpq.make_dims(0, 2, 1, "bf16"), None, 4, *([None] * 7), 0) == 0
+    na = (A, A, A, A, A, A)   # q, k, v, params, state, y
+    big = gpq.make_dims(gpq.DECODE_NOALLOC_MAX_BLOCKS // 2 + 1, 2, 2, "bf16")
+    assert _code(gpq.oal_decode_step_noalloc, big, *na, 0) == 5               # above the static capacity
+    assert _code(gpq.oal_decode_step_noalloc, gpq.make_dims(128, 2, 2, "bf16"), None, *na[1:], 0) == 1
+    assert _code(gpq.oal_decode_step_noalloc, d, A, A, A, A, A, A + 4, 0) == 4
+    assert _code(gpq.oal_decode_step_noalloc, gpq.make_dims(1, 17, 1, "bf16"), *na, 0) == 5
+    assert _code(gpq.oal_decode_step_noalloc, gpq.make_dims(0, 2, 1, "bf16"), *([None] * 6), 0) == 0
     c4 = (A, A, A, A, A)   # q, k, workspace, chi, chi_mean
     assert _code(gpq.oal_contribution, d, 0, *c4, 0) == 2                  # T < 1
     assert _code(gpq.oal_contribution, d, (1 << 22) + 1, *c4, 0) == 5      # above the max T
