@@ -100,3 +100,9 @@ __device__ inline oal_f32x4 oal_splat(float x) {
 // whole L2 (full of the state rows the decode just wrote), which costs far more.
 __device__ inline void oal_wait_own_stores() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
+// An empty asm statement that clobbers memory: loads issued before it cannot be moved after
+// it. Without it the optimizer turns a prefetch ring (load in step k, use in step k + d) back
+// into load-and-use in step k + d (the loads' sources are read-only and unaliased, so moving
+// a load to its use is legal), and every step then waits for its own loads.
+__device__ inline void oal_pin_loads() { asm volatile("" ::: "memory"); }
+

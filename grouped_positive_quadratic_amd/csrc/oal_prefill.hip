@@ -137,7 +137,7 @@ __device__ inline void row_products(const OalFrag<T> &a, const OalFrag<T> &b, fl
 }
 
 constexpr int kFrags = 4 * 64 + 4;                   // fragments per K-step
-constexpr int kDeltaStep = kFrags * 8;                // fp32 per (chunk, K-step)
+constexpr int kDeltaStep = kFrags * 8;                // values per (chunk, K-step)
 
 // Slot tables of one fragment's lane: its 8 state rows and snapshot scales (rows j = 4 h + i
 // are slots (g, 4 h + i)), and the two K^T rows of the A-operand rows (lr / 4, 4 h + lr % 4).
@@ -172,14 +172,18 @@ __device__ inline void slot_tables(int s, const OalKvDev *kvd, int g, int lr, in
     }
 }
 
-// the 8 accumulator values of each fragment of this lane, contiguous (fragment layout)
-__device__ inline void store_frags(float *dp, const oal_f32x4 (&acc)[2][5], int lane, int g, int lr) {
+// the 8 accumulator values of each fragment of this lane, contiguous (fragment layout), in
+// the element type D (the increments of a bf16 call are stored in bf16, everything else fp32)
+template <typename D>
+__device__ inline void store_frags(D *dp, const oal_f32x4 (&acc)[2][5], int lane, int g, int lr) {
 #pragma unroll
     for (int n = 0; n < 5; ++n) {
         if (n == 4 && lr != 0) continue;
-        float4 *q4 = reinterpret_cast<float4 *>(dp + (n < 4 ? n * 64 + lane : 256 + g) * 8);
-        q4[0] = make_float4(acc[0][n][0], acc[0][n][1], acc[0][n][2], acc[0][n][3]);
-        q4[1] = make_float4(acc[1][n][0], acc[1][n][1], acc[1][n][2], acc[1][n][3]);
+        const float x[8] = {acc[0][n][0], acc[0][n][1], acc[0][n][2], acc[0][n][3],
+                            acc[1][n][0], acc[1][n][1], acc[1][n][2], acc[1][n][3]};
+        OalFrag<D> fr;
+        fr.set(x);
+        fr.store(dp + (n < 4 ? n * 64 + lane : 256 + g) * 8);
     }
 }
 
@@ -212,7 +216,7 @@ template <typename T, int C>
 __device__ __forceinline__ void scan_delta_block(
     int bx, int c, int bkv, int T_len, OalSeqLayout sl, int nchunks, int n_q_heads, int n_kv_heads,
     const T *__restrict__ k, const T *__restrict__ v, const unsigned char *__restrict__ params,
-    const float *__restrict__ state, float *__restrict__ delta, float *__restrict__ tinit) {
+    const float *__restrict__ state, T *__restrict__ delta, float *__restrict__ tinit) {
     constexpr int EPU = 16 / (int)sizeof(T);
     constexpr int LD = C + EPU;                         // padded row, 16-byte aligned
     constexpr int UPT = OAL_D / EPU;                    // 16-byte units per token row
@@ -329,7 +333,7 @@ template <typename T, int C>
 __global__ __launch_bounds__(64 * kScanWaves) void oal_scan_delta(
     int T_len, OalSeqLayout sl, int nchunks, int n_q_heads, int n_kv_heads, const T *__restrict__ k,
     const T *__restrict__ v, const unsigned char *__restrict__ params, const float *__restrict__ state,
-    float *__restrict__ delta, float *__restrict__ tinit) {
+    T *__restrict__ delta, float *__restrict__ tinit) {
     scan_delta_block<T, C>(blockIdx.x, blockIdx.y, blockIdx.z, T_len, sl, nchunks, n_q_heads, n_kv_heads, k,
                            v, params, state, delta, tinit);
 }
@@ -339,7 +343,7 @@ __global__ __launch_bounds__(64 * kScanWaves) void oal_scan_delta(
 template <typename T>
 __global__ __launch_bounds__(256) void oal_scan_prefix(int nchunks, int n_q_heads, int n_kv_heads, int n_bkv,
                                                        const unsigned char *__restrict__ params,
-                                                       const float *__restrict__ delta,
+                                                       const T *__restrict__ delta,
                                                        const float *__restrict__ tinit,
                                                        float *__restrict__ state, unsigned char *__restrict__ snap) {
     constexpr int KB = snap_kstep_bytes<T>();
@@ -376,49 +380,53 @@ __global__ __launch_bounds__(256) void oal_scan_prefix(int nchunks, int n_q_head
         S[0] = a0.x; S[1] = a0.y; S[2] = a0.z; S[3] = a0.w;
         S[4] = a1.x; S[5] = a1.y; S[6] = a1.z; S[7] = a1.w;
     }
-    const float *dp = delta + ((size_t)bkv * nchunks * OAL_SNAP_KSTEPS + s) * kDeltaStep + f * 8;
+    const T *dp = delta + ((size_t)bkv * nchunks * OAL_SNAP_KSTEPS + s) * kDeltaStep + f * 8;
     // snap == nullptr: only the final state is wanted (no readout follows)
     unsigned char *sp = snap ? snap + ((size_t)bkv * nchunks * OAL_SNAP_KSTEPS + s) * KB + (size_t)f * OalFrag<T>::kBytes
                              : nullptr;
     constexpr size_t DSTRIDE = (size_t)OAL_SNAP_KSTEPS * kDeltaStep, SSTRIDE = (size_t)OAL_SNAP_KSTEPS * KB;
-    // chunks in batches of PB; the next batch's increments are requested before the current
-    // batch is summed (two buffers, the loop unrolled by two batches)
-    constexpr int PB = 4;
-    auto load_batch = [&](int c0, float4 (&d)[PB][2]) {
+    // chunks in batches of PB: the next batch's increments (independent of the running sum)
+    // are requested before the current batch is summed. Full batches run in a loop without
+    // branches around their loads or stores (loads past the last chunk are clamped reloads),
+    // so the compiler can count the loads in flight; the remaining chunks follow one by one.
+    constexpr int PB = sizeof(T) == 2 ? 16 : 8;
+    auto load_batch = [&](int c0, OalFrag<T> (&d)[PB]) {
 #pragma unroll
-        for (int u = 0; u < PB; ++u) {
-            if (c0 + u < nchunks) {
-                const float4 *q4 = reinterpret_cast<const float4 *>(dp + (size_t)(c0 + u) * DSTRIDE);
-                d[u][0] = q4[0];
-                d[u][1] = q4[1];
-            }
-        }
+        for (int u = 0; u < PB; ++u) d[u].load(dp + (size_t)min(c0 + u, nchunks - 1) * DSTRIDE);
     };
-    auto run_batch = [&](int c0, const float4 (&d)[PB][2]) {
+    auto step = [&](int c, const OalFrag<T> &d) {
+        if (sp) {
+            float x[8];
 #pragma unroll
-        for (int u = 0; u < PB; ++u) {
-            if (c0 + u < nchunks) {
-                if (sp) {
-                    float x[8];
-#pragma unroll
-                    for (int j = 0; j < 8; ++j) x[j] = S[j] * fsc[j];
-                    OalFrag<T> fr;
-                    fr.set(x);
-                    fr.store(sp + (size_t)(c0 + u) * SSTRIDE);
-                }
-                S[0] += d[u][0].x; S[1] += d[u][0].y; S[2] += d[u][0].z; S[3] += d[u][0].w;
-                S[4] += d[u][1].x; S[5] += d[u][1].y; S[6] += d[u][1].z; S[7] += d[u][1].w;
-            }
+            for (int j = 0; j < 8; ++j) x[j] = S[j] * fsc[j];
+            OalFrag<T> fr;
+            fr.set(x);
+            fr.store(sp + (size_t)c * SSTRIDE);
         }
+#pragma unroll
+        for (int j = 0; j < 8; ++j) S[j] += (float)d.v[j];
     };
-    float4 da[PB][2], db[PB][2];
-    load_batch(0, da);
-    for (int c0 = 0; c0 < nchunks; c0 += 2 * PB) {
-        if (c0 + PB < nchunks) load_batch(c0 + PB, db);
-        run_batch(c0, da);
-        if (c0 + PB >= nchunks) break;
-        if (c0 + 2 * PB < nchunks) load_batch(c0 + 2 * PB, da);
-        run_batch(c0 + PB, db);
+    const int nfull = nchunks / PB * PB;
+    OalFrag<T> da[PB], db[PB];
+    if (nfull > 0) {
+        load_batch(0, da);
+        oal_pin_loads();
+        for (int c0 = 0; c0 < nfull; c0 += 2 * PB) {
+            load_batch(c0 + PB, db);
+            oal_pin_loads();
+#pragma unroll
+            for (int u = 0; u < PB; ++u) step(c0 + u, da[u]);
+            if (c0 + PB >= nfull) break;
+            load_batch(c0 + 2 * PB, da);
+            oal_pin_loads();
+#pragma unroll
+            for (int u = 0; u < PB; ++u) step(c0 + PB + u, db[u]);
+        }
+    }
+    for (int c = nfull; c < nchunks; ++c) {
+        OalFrag<T> d1;
+        d1.load(dp + (size_t)c * DSTRIDE);
+        step(c, d1);
     }
 #pragma unroll
     for (int j = 0; j < 8; ++j)     // tail pairs duplicate main rows: only owners write
@@ -733,7 +741,7 @@ template <typename T, int C>
 __global__ __launch_bounds__(64 * kIntraWaves) __attribute__((amdgpu_waves_per_eu(4))) void oal_intra_delta(
     int T_len, OalSeqLayout sl, int n_q_heads, int n_kv_heads, int nchunks, int n_bkv, int n_delta,
     const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ v,
-    const unsigned char *__restrict__ params, const float *__restrict__ state, float *__restrict__ delta,
+    const unsigned char *__restrict__ params, const float *__restrict__ state, T *__restrict__ delta,
     float *__restrict__ tinit, float *__restrict__ uintra) {
     static_assert(kScanWaves == kIntraWaves, "one workgroup shape for both parts");
     const int n_intra = (int)gridDim.x - n_delta;
@@ -1020,10 +1028,13 @@ __global__ __launch_bounds__(256, 2) void oal_readout(
         OalFrag<T> bq[DEP][5];
 #pragma unroll
         for (int d = 0; d + 1 < DEP; ++d) load_next(bq[d]);      // ntot > NMAIN >= DEP - 1
+        oal_pin_loads();
         for (int it = 0; it < NMAIN; it += DEP) {
 #pragma unroll
             for (int u = 0; u < DEP; ++u) {
-                if (it + u + DEP - 1 < ntot) load_next(bq[(u + DEP - 1) % DEP]);
+                // always inside the list here: ntot >= NMAIN + 1 (at least 3 tail K-steps)
+                load_next(bq[(u + DEP - 1) % DEP]);
+                oal_pin_loads();
                 main_step(bq[u]);
             }
         }
@@ -1033,6 +1044,7 @@ __global__ __launch_bounds__(256, 2) void oal_readout(
             for (int u = 0; u < DEP; ++u) {
                 if (x + u < ntot - NMAIN) {
                     if (NMAIN + x + u + DEP - 1 < ntot) load_next(bq[(u + DEP - 1) % DEP]);
+                    oal_pin_loads();
                     tail_step(bq[u], 2 * (x + u) + par);
                 }
             }
@@ -1103,7 +1115,7 @@ PrefillPlan make_plan(const oal_dims &d, int T_len, int C) {
     p.Tpad = p.nchunks * C;
     auto r256 = [](size_t x) { return (x + 255) / 256 * 256; };
     p.snap_bytes = r256(bkv * p.nchunks * OAL_SNAP_KSTEPS * (size_t)snap_kstep_bytes<T>());
-    p.delta_bytes = r256(bkv * p.nchunks * OAL_SNAP_KSTEPS * (size_t)kDeltaStep * sizeof(float));
+    p.delta_bytes = r256(bkv * p.nchunks * OAL_SNAP_KSTEPS * (size_t)kDeltaStep * sizeof(T));
     p.tinit_bytes = r256(bkv * OAL_TAIL_STEPS * (size_t)kDeltaStep * sizeof(float));
     p.uintra_bytes = r256((size_t)d.batch * d.n_q_heads * (p.Tpad / 16) * (size_t)kFragFloats * sizeof(float));
     return p;
@@ -1160,7 +1172,7 @@ hipError_t launch_all(const oal_dims &d, int T_len, OalSeqLayout sl, const void 
                       hipEvent_t *marks) {
     PrefillPlan p = make_plan<T>(d, T_len, C);
     unsigned char *snap = reinterpret_cast<unsigned char *>(ws);
-    float *delta = reinterpret_cast<float *>(snap + p.snap_bytes);
+    T *delta = reinterpret_cast<T *>(snap + p.snap_bytes);
     float *tinit = reinterpret_cast<float *>(snap + p.snap_bytes + p.delta_bytes);
     float *uintra = reinterpret_cast<float *>(snap + p.snap_bytes + p.delta_bytes + p.tinit_bytes);
     const int bkv = d.batch * d.n_kv_heads;

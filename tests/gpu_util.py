@@ -56,16 +56,18 @@ def state_ok(S, k, v, dtype):
     """Final prefix states against the oracle's.
 
     fp32 inputs: blockwise relative error <= 1e-5. bf16 inputs: the scan feeds each feature
-    psi(k) = k_r k_t (exact in fp32) to the MFMA rounded once to bf16 (<= 2^-9 relative), so
-    each element obeys |S - S*| <= 2^-8 * sum_j |psi_f(k_j)| |[v_j;1]_c| (2x margin), where the
-    right-hand side is the oracle's state of |k|, |v|.
+    psi(k) = k_r k_t (exact in fp32) to the MFMA rounded once to bf16 (<= 2^-9 relative), and
+    each chunk's increment sum_{j in chunk} psi(k_j) [v_j;1] (fp32 on the MFMA) is stored once
+    in bf16 (<= 2^-9 of its absolute sum) before the fp32 sum over chunks, so each element obeys
+    |S - S*| <= 2^-8 * sum_j |psi_f(k_j)| |[v_j;1]_c| up to fp32 terms; the bound 2^-7 keeps a
+    2x margin. The right-hand side is the oracle's state of |k|, |v|.
     """
     import oracle
     S_ref = oracle.state(k, v)
     if dtype == "f32":
         return state_error(S, S_ref) <= 1e-5
     S_abs = oracle.state(np.abs(k), np.abs(v))
-    return bool(np.all(np.abs(S - S_ref) <= 2.0 ** -8 * S_abs + 1e-6 * S_abs.max()))
+    return bool(np.all(np.abs(S - S_ref) <= 2.0 ** -7 * S_abs + 1e-6 * S_abs.max()))
 
 
 def state_error(S, S_ref):
