@@ -13,11 +13,18 @@ per sequence each).
 Contribution scores: oal_contribution (the per-dim causal statistic chi and its prompt
 mean) over a calibration batch of 8 prompts x 4096 tokens, timed over 50 back-to-back calls.
 
-Prints one JSON line. `value` is prefill tokens/s; `roofline` is the readout kernel
-(the dominant one) against the bf16 MFMA peak; `decode` holds decode tokens/s and the
-decode kernel against HBM peak; `contribution` the chi kernel against HBM peak; `backward` the
-prefill backward (dq, dk, dv) of the headline workload against the fp32 vector peak;
-`cpu_baseline` is the fp64 CPU oracle on the full prefill batch, timed on this host.
+Decode against HBM: 512 sequences (571 MB of prefix state, more than the 256 MB last-level
+cache), each step reading and writing every state once.
+
+Prints one JSON line. `value` is prefill tokens/s; `roofline` is the whole prefill step (its
+three kernels together) against the bf16 MFMA peak, with the readout kernel (the dominant
+one) as `roofline.readout`; `achievable_peaks` holds the rates of a matrix-core loop and a
+streaming copy measured on this device; `decode` holds decode tokens/s and the decode kernel
+against HBM peak (`decode.hbm_512seq` for the state that does not fit in the cache);
+`contribution` the chi kernel against HBM peak; `backward` the prefill backward (dq, dk, dv)
+of the headline workload against the fp32 MFMA peak; `cpu_baseline` is the fp64 CPU oracle on
+the full prefill batch, timed on this host, with the other workloads under
+`cpu_baseline.other_workloads`.
 """
 from __future__ import annotations
 
@@ -34,7 +41,7 @@ D, V1, NFEAT = 64, 65, 2145
 FLOP_PER_TOKEN_HEAD = 2 * NFEAT * V1          # 278,850: one feature-space contraction
 PEAK_BF16_TFLOPS = 2500.0                     # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0                         # MI355X HBM3E
-PEAK_FP32_TFLOPS = 157.3                      # MI355X fp32 vector (packed FMA; 78.6 without)
+PEAK_FP32_TFLOPS = 157.3                      # MI355X fp32 MFMA dense (fp64: 78.6)
 PHASE_EVERY = 4                               # timed steps with per-kernel events
 
 
@@ -48,6 +55,10 @@ def parse():
     ap.add_argument("--seq", type=int, default=4096)
     ap.add_argument("--decode-seqs", type=int, default=64)
     ap.add_argument("--decode-steps", type=int, default=256)
+    ap.add_argument("--hbm-decode-seqs", type=int, default=512,
+                    help="sequences of the decode run whose state exceeds the caches (0: skip)")
+    ap.add_argument("--no-peaks", action="store_true",
+                    help="skip the matrix-core loop and streaming-copy measurements")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-contribution", action="store_true",
@@ -173,6 +184,8 @@ def main():
         except (OSError, ValueError):
             tj = {}
     traffic = measured_traffic(tj, f"readout_B{B}_T{T}_C{C}")
+    step_flops = readout_flops + scan_flops
+    step_tflops = step_flops / (ms_step * 1e-3) / 1e12
     out = {
         "metric": METRIC,
         "value": tokens / (ms_step * 1e-3),
@@ -188,19 +201,60 @@ def main():
         "data": "synthetic",
         "config": {"workload": f"prefill B={B} T={T} Hq={Hq} Hkv={Hkv} d=64 (Qwen2.5-0.5B-shaped layer)",
                    "global_batch": B, "seq_len": T, "chunk": C, "parallelism": "none (1 GPU)"},
-        "roofline": {"bound": "mfma", "kernel": "oal_readout", "achieved": achieved,
-                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
-                     "traffic": traffic, "avg_ms": read_ms,
-                     "algorithmic_flops_per_launch": readout_flops},
+        "roofline": {"bound": "mfma", "kernel": "whole prefill step (intra/increments, chunk prefix, readout)",
+                     "achieved": step_tflops, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": step_tflops / PEAK_BF16_TFLOPS,
+                     "traffic": measured_traffic(tj, f"prefill_step_B{B}_T{T}_C{C}"), "avg_ms": ms_step,
+                     "algorithmic_flops_per_launch": step_flops,
+                     "readout": {"kernel": "oal_readout", "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
+                                 "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
+                                 "traffic": traffic, "avg_ms": read_ms,
+                                 "algorithmic_flops_per_launch": readout_flops}},
         "phases_ms": {"intra_and_scan": scan_ms, "readout": read_ms,
                       "sampled_steps": len(marks), "note": "events around the kernels in every "
                       f"{PHASE_EVERY}th timed step"},
-        "prefill_algorithmic_tflops": (readout_flops + scan_flops) / (ms_step * 1e-3) / 1e12,
         "graph_replay": {"ms_per_step": ms_graph, "value": tokens / (ms_graph * 1e-3),
                          "note": "the timed steps captured into one HIP graph, replayed once"},
     }
     del q, k, v, y, ws, state, params
     torch.cuda.empty_cache()
+
+    # ---------------- achievable peaks on this device ----------------
+    if not args.no_peaks:
+        props = torch.cuda.get_device_properties(dev)
+        nblk = props.multi_processor_count * 8          # 2 wavefronts per SIMD
+        mout = torch.empty(nblk * 256, dtype=torch.float32, device=dev)
+        gpq.oal_calib_mfma_bf16(nblk, 2048, mout)       # warm-up: code object load, clock ramp
+        torch.cuda.synchronize()
+        e0, e1 = gpq.TimingEvent(), gpq.TimingEvent()
+        e0.record(stream)
+        mflops = sum(gpq.oal_calib_mfma_bf16(nblk, 2048, mout) for _ in range(3))
+        e1.record(stream)
+        mms = e0.elapsed_time(e1)
+        mfma_tflops = mflops / (mms * 1e-3) / 1e12
+        del mout
+        nbytes = 1 << 30                                # 1 GiB each way: 8x the last-level cache
+        csrc = torch.ones(nbytes // 4, dtype=torch.float32, device=dev)
+        cdst = torch.empty_like(csrc)
+        gpq.oal_calib_copy(csrc, cdst, nbytes)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(5):
+            gpq.oal_calib_copy(csrc, cdst, nbytes)
+        e1.record(stream)
+        cms = e0.elapsed_time(e1) / 5
+        copy_gbs = 2 * nbytes / (cms * 1e-3) / 1e9
+        del csrc, cdst
+        torch.cuda.empty_cache()
+        out["achievable_peaks"] = {
+            "mfma_bf16": {"tflops": mfma_tflops, "frac_of_nominal": mfma_tflops / PEAK_BF16_TFLOPS,
+                          "kernel": "oal_calib_mfma_bf16: 8 independent 16x16x32 bf16 MFMA chains per "
+                                    f"wavefront, {nblk} workgroups x 4 wavefronts, 3 x 2048 rounds"},
+            "hbm_copy": {"gbs": copy_gbs, "frac_of_nominal": copy_gbs / PEAK_HBM_GBS,
+                         "kernel": "oal_calib_copy: 1 GiB device-to-device, one 16-byte load and "
+                                   "store per thread; bytes read + written"},
+            "prefill_step_frac_of_achievable": step_tflops / mfma_tflops,
+            "readout_frac_of_achievable": achieved / mfma_tflops}
 
     cache = {}
 
@@ -386,6 +440,42 @@ def main():
                                           "frac": alg / (gms * 1e-3) / 1e9 / PEAK_HBM_GBS,
                                           "note": "the timed step loop captured into one HIP graph, replayed once"}}
 
+        # ---- the same step on 512 sequences: 571 MB of state, more than the last-level cache ----
+        if args.hbm_decode_seqs > 0:
+            n2 = args.hbm_decode_seqs
+            d2 = gpq.make_dims(n2, 14, 2, "bf16")
+            p2, s2, _, w2 = gpq.alloc_buffers(d2, 0, 128)
+            gpq.oal_state_init(d2, dhp, p2, s2)
+            # sequence b starts from the prefix state of sequence b % nseq (same structure and
+            # size; the step's traffic does not depend on the values)
+            blk = gpq.STATE_STRIDE * 2
+            s2.view(n2, blk).copy_(dstate.view(nseq, blk).repeat((n2 + nseq - 1) // nseq, 1)[:n2])
+            ns2 = 16
+            t2 = cfg5_steps(n_seq=n2, steps=ns2)
+            q2, k2, v2 = (torch.from_numpy(a).to(torch.bfloat16).to(dev).permute(2, 0, 1, 3).contiguous()
+                          for a in (t2.q, t2.k, t2.v))
+            y2 = torch.empty((ns2, n2, 14, D), dtype=torch.float32, device=dev)
+            gpq.oal_decode_step(d2, q2[0], k2[0], v2[0], p2, s2, w2, y2[0])     # untimed
+            torch.cuda.synchronize()
+            ev[0].record(stream)
+            for i in range(1, ns2):
+                gpq.oal_decode_step(d2, q2[i], k2[i], v2[i], p2, s2, w2, y2[i])
+            ev[1].record(stream)
+            torch.cuda.synchronize()
+            hms = ev[0].elapsed_time(ev[1]) / (ns2 - 1)
+            alg2 = 2 * n2 * 2 * NFEAT * V1 * 4 + n2 * (14 * D * 2 + 2 * 2 * D * 2 + 14 * D * 4)
+            hach = alg2 / (hms * 1e-3) / 1e9
+            out["decode"]["hbm_512seq"] = {
+                "workload": f"decode {n2} seqs, 4096-token prefix states ({2 * n2 * NFEAT * V1 * 4 / 1e6:.0f} MB "
+                            "of state), 14q/2kv, eager launches",
+                "value": n2 / (hms * 1e-3), "unit": "tokens/s", "ms_per_step": hms, "steps": ns2 - 1,
+                "roofline": {"bound": "hbm", "kernel": "oal_decode_kernel", "achieved": hach,
+                             "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": hach / PEAK_HBM_GBS,
+                             "traffic": measured_traffic(tj, f"decode_{n2}seq"),
+                             "algorithmic_bytes_per_launch": alg2}}
+            del p2, s2, w2, q2, k2, v2, y2
+            torch.cuda.empty_cache()
+
     # ---------------- CPU oracle baseline ----------------
     if not args.no_cpu_baseline:
         import oracle
@@ -399,6 +489,46 @@ def main():
                                "kind": "oracle",
                                "sample": "full prefill batch (B=1, T=4096, 14 q heads), dense O(T^2) fp64, 1 pass",
                                "wall_s": wall}
+        other = {}
+        from oal_synth import cfg3, cfg4
+        c3 = cfg3()
+        t0 = time.perf_counter()
+        oracle.dense(c3.q, c3.k, c3.v, c3.params)
+        w3 = time.perf_counter() - t0
+        other["B8_T4096"] = {"value": c3.q.shape[0] * 4096 / w3, "unit": "tokens/s", "wall_s": w3,
+                             "sample": "all 8 sequences x 4096 positions, dense O(T^2) fp64, 1 pass"}
+        del c3
+        c4 = cfg4()
+        n4 = 4096
+        t0 = time.perf_counter()
+        oracle.dense(c4.q[:, :, :n4], c4.k[:, :, :n4], c4.v[:, :, :n4], c4.params)
+        w4 = time.perf_counter() - t0
+        T4 = c4.q.shape[2]
+        scale = (T4 / n4) ** 2                       # the dense definition's cost grows as T^2
+        other["B1_T32768"] = {"value": T4 / (w4 * scale), "unit": "tokens/s", "wall_s_sample": w4,
+                              "extrapolated": True,
+                              "sample": f"first {n4} positions (their outputs are exact: causal), timed, then "
+                                        f"x{scale:.0f} for the full {T4} (dense cost ~ T^2): extrapolated"}
+        del c4
+        # decode: each new token's output by the dense definition over its prefix
+        ns, nt = 8, 32
+        p5 = cfg5_prefix(n_seq=ns)
+        s5 = cfg5_steps(n_seq=ns, steps=args.decode_steps)
+        T0 = p5.k.shape[2]
+        t0 = time.perf_counter()
+        for b in range(ns):
+            kk = np.concatenate([p5.k[b:b + 1], s5.k[b:b + 1, :, :nt]], axis=2)
+            vv = np.concatenate([p5.v[b:b + 1], s5.v[b:b + 1, :, :nt]], axis=2)
+            qq = np.zeros((1, 14, T0 + nt, D))
+            qq[:, :, T0:] = s5.q[b:b + 1, :, :nt]
+            rows = [(0, h, T0 + t) for t in range(nt) for h in range(14)]
+            oracle.dense_rows(qq, kk, vv, p5.params, rows)
+        w5 = time.perf_counter() - t0
+        other["decode_64seq"] = {"value": ns * nt / w5, "unit": "tokens/s", "wall_s": w5,
+                                 "sample": f"{ns} of the 64 sequences x the first {nt} decode steps after "
+                                           f"the {T0}-token prefix; each new token's 14 head outputs by the "
+                                           "dense definition over its prefix (O(T) per token)"}
+        out["cpu_baseline"]["other_workloads"] = other
     print(json.dumps(out), flush=True)
 
 

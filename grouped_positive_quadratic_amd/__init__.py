@@ -26,7 +26,7 @@ EXPORTED = ("oal_params_bytes", "oal_state_bytes", "oal_prefill_workspace_bytes"
             "oal_timing_event_destroy", "oal_timing_event_record", "oal_timing_elapsed_ms",
             "oal_contribution_workspace_bytes", "oal_contribution", "oal_decode_step_indexed",
             "oal_prefill_varlen", "oal_prefill_packed", "oal_prefill_backward_workspace_bytes",
-            "oal_prefill_backward", "oal_decode_step_noalloc")
+            "oal_prefill_backward", "oal_decode_step_noalloc", "oal_calib_mfma_bf16", "oal_calib_copy")
 DECODE_NOALLOC_MAX_BLOCKS = 256   # OAL_DECODE_NOALLOC_MAX_BLOCKS
 
 
@@ -81,6 +81,9 @@ def _load():
     lib.oal_decode_step_noalloc.argtypes = [dp, P, P, P, P, P, P, P]
     lib.oal_decode_step_noalloc.restype = ctypes.c_int
     lib.oal_status_string.argtypes, lib.oal_status_string.restype = [ctypes.c_int], ctypes.c_char_p
+    lib.oal_calib_mfma_bf16.argtypes = [I, I, P, ctypes.POINTER(ctypes.c_double), P]
+    lib.oal_calib_mfma_bf16.restype = ctypes.c_int
+    lib.oal_calib_copy.argtypes, lib.oal_calib_copy.restype = [P, P, S, P], ctypes.c_int
     lib.oal_timing_event_create.argtypes, lib.oal_timing_event_create.restype = [ctypes.POINTER(P)], ctypes.c_int
     lib.oal_timing_event_destroy.argtypes, lib.oal_timing_event_destroy.restype = [P], ctypes.c_int
     lib.oal_timing_event_record.argtypes, lib.oal_timing_event_record.restype = [P, P], ctypes.c_int
@@ -238,6 +241,19 @@ def oal_prefill_timed(dims: oal_dims, T: int, chunk: int, q, k, v, params_dev, s
         ctypes.byref(dims), int(T), int(chunk), _ptr(q), _ptr(k), _ptr(v), _ptr(params_dev),
         _ptr(state_dev), _ptr(workspace), _nbytes(workspace, workspace_bytes), _ptr(y), _stream(stream),
         handles))
+
+
+def oal_calib_mfma_bf16(blocks: int, iters: int, out, stream=None) -> float:
+    """Matrix-core loop (measurement aid); returns the dense flop count it enqueued."""
+    flops = ctypes.c_double()
+    _check("oal_calib_mfma_bf16", _lib.oal_calib_mfma_bf16(blocks, iters, _ptr(out), ctypes.byref(flops),
+                                                           _stream(stream)))
+    return float(flops.value)
+
+
+def oal_calib_copy(src, dst, nbytes: int, stream=None):
+    """Streaming device copy of nbytes (measurement aid)."""
+    _check("oal_calib_copy", _lib.oal_calib_copy(_ptr(src), _ptr(dst), nbytes, _stream(stream)))
 
 
 class TimingEvent:

@@ -11,7 +11,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "liboal.so")
-SOURCES = ["oal_host.cpp", "oal_decode.hip", "oal_prefill.hip", "oal_contrib.hip", "oal_backward.hip"]
+SOURCES = ["oal_host.cpp", "oal_decode.hip", "oal_prefill.hip", "oal_contrib.hip", "oal_backward.hip",
+           "oal_calib.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["-O3", "--offload-arch=gfx950", "-fPIC", "-std=c++17",
          "-I", os.path.join(ROOT, "include"), "-I", CSRC,

@@ -23,7 +23,8 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 
 def test_exports_every_declared_symbol():
-    hdr = open(os.path.join(ROOT, "include", "oal.h")).read()
+    import glob
+    hdr = "".join(open(f).read() for f in sorted(glob.glob(os.path.join(ROOT, "include", "*.h"))))
     declared = set(re.findall(r"^\w[\w\s\*]*?\b(oal_\w+)\s*\(", hdr, flags=re.M))
     assert declared == set(gpq.EXPORTED), declared ^ set(gpq.EXPORTED)
     lib = ctypes.CDLL(gpq.LIB_PATH)
@@ -375,3 +376,14 @@ def test_build_entry_does_not_need_the_library():
     r = subprocess.run([sys.executable, "-c", code], cwd=os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
                        capture_output=True, text=True, timeout=120)
     assert r.returncode == 0, r.stderr
+
+
+def test_calibration_calls_validate_arguments():
+    A = 4096   # fake, aligned, never dereferenced: validation fails first
+    assert _code(gpq.oal_calib_mfma_bf16, 0, 10, A, stream=0) == 1
+    assert _code(gpq.oal_calib_mfma_bf16, 4, 0, A, stream=0) == 1
+    assert _code(gpq.oal_calib_mfma_bf16, 4, 10, None, stream=0) == 1
+    assert _code(gpq.oal_calib_copy, A, A + 4096, 100, stream=0) == 1       # not a multiple of 16
+    assert _code(gpq.oal_calib_copy, A + 8, A + 4096, 64, stream=0) == 4    # misaligned
+    assert _code(gpq.oal_calib_copy, None, A, 64, stream=0) == 1
+    assert _code(gpq.oal_calib_copy, A, A + 4096, 0, stream=0) == 0         # nothing to move
