@@ -371,7 +371,7 @@ def main():
             "workload": f"prefill backward (dq, dk, dv, dL, deps) from an empty prefix, B={Bb} T={Tb} "
                         f"{Hqb}q/{Hkvb}kv, bf16 inputs, fp32 arithmetic, chunk {Cb}",
             "value": Bb * Tb / (bms * 1e-3), "unit": "tokens/s", "ms_per_call": bms, "calls": reps,
-            "roofline": {"bound": "alu", "kernel": "the call's fp32 launches together",
+            "roofline": {"bound": "mfma", "kernel": "the call's fp32 MFMA launches together",
                          "achieved": bach, "peak": PEAK_FP32_TFLOPS, "unit": "TFLOP/s",
                          "frac": bach / PEAK_FP32_TFLOPS, "traffic": None,
                          "algorithmic_flops_per_call": bflops}}
