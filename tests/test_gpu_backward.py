@@ -128,10 +128,12 @@ def test_backward_chunk_sizes_agree(chunk):
     check(small(51, 1, 7, 1, 260, "bf16"), chunk, 51)
 
 
-def test_backward_many_groups():
-    """64 groups (one per dim): the z-terms run in several register blocks."""
+@pytest.mark.parametrize("chunk", [64, 128])
+def test_backward_many_groups(chunk):
+    """64 groups (one per dim): the z-terms run in several register blocks. T = 300 spans
+    several chunks of both sizes and a ragged tail."""
     rng = np.random.default_rng(52)
-    inp = small(52, 1, 2, 1, 150, dtype="bf16", g_hi=2)
+    inp = small(52, 1, 2, 1, 300, dtype="bf16", g_hi=2)
     G = 64
     L = np.zeros((2, G + 1, G + 1), np.float32)
     for h in range(2):
@@ -140,7 +142,7 @@ def test_backward_many_groups():
     inp.params = HeadParams(np.full(2, G, np.int32),
                             np.stack([rng.permutation(64), np.arange(64)]).astype(np.uint8), L,
                             np.full(2, 1e-3, np.float32))
-    check(inp, 64, 52, name="g64")
+    check(inp, chunk, 52, name="g64")
 
 
 def test_backward_l_zero_closed_form():
