@@ -8,7 +8,8 @@
 //
 // The state row f of a KV head holds 65 floats: 64 in a 256-byte row of the v part and one
 // in the separate column-64 vector (the state layout keeps the v part line-aligned).
-// Workgroup (split, bkv) owns 192 rows; wave w walks 48 of them in batches of 16 with lane c
+// Workgroup (split, bkv) owns 192 rows (384 for large batches); wave w walks a quarter of them
+// in batches of 16 with lane c
 // on column c (one aligned 256-byte row read and write per row) and the batch's 16
 // column-64 entries (64 contiguous bytes) on lanes 0..15. With 260-byte rows (column 64
 // inline) the rows straddled cache lines and the kernel wrote 17% more bytes than the state
@@ -30,29 +31,43 @@
 
 namespace {
 
-constexpr int kRows = 192;                  // state rows per workgroup (12 splits: 6 workgroups per CU at 128 KV heads)
+// State rows per workgroup: 192 (12 splits) up to kBigBatchBkv (sequence, KV head) blocks,
+// 384 (6 splits) from there on. Measured on MI355X, 14q/2kv bf16 steps: 64 sequences 30.6 us
+// with 192 rows, 31.5 us with 384; 512 sequences 276 us with 192 rows, 254 us with 384 (each
+// workgroup's set-up is paid over more rows once the grid runs in several rounds).
 constexpr int kThreads = 256;
-constexpr int kRowsPerWave = kRows / 4;
-constexpr int kSplits = (OAL_NFEAT + kRows - 1) / kRows;
+constexpr int kRowsSmall = 192, kRowsBig = 384;
+constexpr int kBigBatchBkv = 512;
+constexpr int splits_of(int rows) { return (OAL_NFEAT + rows - 1) / rows; }
+constexpr int kSplits = splits_of(kRowsSmall);   // the most splits: sizes the partial sums
 constexpr int kBatch = 16;                  // rows per load batch of a wave
-static_assert(kRows % 4 == 0 && kRows <= 2 * kThreads, "rows per workgroup");
 static_assert(8 * OAL_D % kThreads == 0, "query staging");
 
+// Dims of state row f: (-1, -1) the constant, (r, -1) linear feature r, else the quadratic
+// pair (r, t), r <= t, whose rows start at 65 + start(r), start(r) = 64 r - r (r - 1) / 2.
+// r is the root of start(r) = i rounded down (fp32 square root, then a +-1 correction; exact
+// for every i < 2080).
+__device__ inline int quad_start(int r) { return OAL_D * r - (r * (r - 1)) / 2; }
 __device__ inline void row_dims(int f, int &r, int &t) {
     if (f == 0) { r = -1; t = -1; return; }
     if (f <= OAL_D) { r = f - 1; t = -1; return; }
-    int i = f - 1 - OAL_D, rr = 0;
-    while (i >= OAL_D - rr) { i -= OAL_D - rr; ++rr; }
+    const int i = f - 1 - OAL_D;
+    int rr = (int)floorf((129.0f - sqrtf(16641.0f - 8.0f * (float)i)) * 0.5f);
+    if (quad_start(rr + 1) <= i) ++rr;
+    if (quad_start(rr) > i) --rr;
     r = rr;
-    t = rr + i;
+    t = rr + (i - quad_start(rr));
 }
 
-template <typename T, int MAXH>
+template <typename T, int MAXH, int kRows>
 __global__ __launch_bounds__(kThreads) void oal_decode_kernel(
     int n_q_heads, int n_kv_heads, const T *__restrict__ q, const T *__restrict__ k,
     const T *__restrict__ v, const unsigned char *__restrict__ params, float *__restrict__ state,
     const int *__restrict__ slots, int pool_size, float *__restrict__ partial,
     unsigned int *__restrict__ counters, float *__restrict__ y) {
+    static_assert(kRows % 4 == 0 && kRows <= 2 * kThreads, "rows per workgroup");
+    constexpr int kRowsPerWave = kRows / 4;
+    constexpr int NSPL = splits_of(kRows);
     const int split = blockIdx.x;
     const int bkv = blockIdx.y;
     const int b = bkv / n_kv_heads, kv = bkv % n_kv_heads;
@@ -185,7 +200,7 @@ __global__ __launch_bounds__(kThreads) void oal_decode_kernel(
     //    complete before the barrier, so all of them are performed before thread 0's arrival
     //    RMW; the last workgroup to arrive issues its loads only after its own RMW returned,
     //    so it reads every split's partial (no L2 write-back is needed for that).
-    float *mypart = partial + ((size_t)bkv * kSplits + split) * MAXH * OAL_V1;
+    float *mypart = partial + ((size_t)bkv * NSPL + split) * MAXH * OAL_V1;
     for (int idx = tid; idx < n_rep * OAL_V1; idx += kThreads) {
         int h = idx / OAL_V1, c = idx % OAL_V1;
         __hip_atomic_store(mypart + idx, s_red[0][h][c] + s_red[1][h][c] + s_red[2][h][c] + s_red[3][h][c],
@@ -196,25 +211,25 @@ __global__ __launch_bounds__(kThreads) void oal_decode_kernel(
     __syncthreads();
     if (tid == 0) {
         unsigned int old = __hip_atomic_fetch_add(counters + bkv, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        s_last = (old == (unsigned int)(kSplits - 1));
+        s_last = (old == (unsigned int)(NSPL - 1));
     }
     __syncthreads();
     if (!s_last) return;
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-    const float *allpart = partial + (size_t)bkv * kSplits * MAXH * OAL_V1;
+    const float *allpart = partial + (size_t)bkv * NSPL * MAXH * OAL_V1;
     // all splits are requested at once, then summed in split order (deterministic)
     for (int idx = tid; idx < n_rep * OAL_D; idx += kThreads) {
         int h = idx / OAL_D, c = idx % OAL_D;
-        float pn[kSplits], pd[kSplits];
+        float pn[NSPL], pd[NSPL];
 #pragma unroll
-        for (int sp = 0; sp < kSplits; ++sp) {
+        for (int sp = 0; sp < NSPL; ++sp) {
             const float *pp = allpart + (size_t)sp * MAXH * OAL_V1 + h * OAL_V1;
             pn[sp] = __hip_atomic_load(pp + c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             pd[sp] = __hip_atomic_load(pp + OAL_D, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
         float num = 0.0f, den = 0.0f;
 #pragma unroll
-        for (int sp = 0; sp < kSplits; ++sp) { num += pn[sp]; den += pd[sp]; }
+        for (int sp = 0; sp < NSPL; ++sp) { num += pn[sp]; den += pd[sp]; }
         y[((size_t)b * n_q_heads + h0 + h) * OAL_D + c] = num / den;
     }
     if (tid == 0) __hip_atomic_store(counters + bkv, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -228,12 +243,19 @@ hipError_t launch(const oal_dims &d, const void *q, const void *k, const void *v
     unsigned int *counters = reinterpret_cast<unsigned int *>(ws);
     size_t cbytes = ((size_t)bkv * sizeof(unsigned int) + 255) / 256 * 256;
     float *partial = reinterpret_cast<float *>(reinterpret_cast<char *>(ws) + cbytes);
-    dim3 grid(kSplits, bkv);
-    hipLaunchKernelGGL((oal_decode_kernel<T, MAXH>), grid, dim3(kThreads), 0, stream, d.n_q_heads,
-                       d.n_kv_heads, reinterpret_cast<const T *>(q), reinterpret_cast<const T *>(k),
-                       reinterpret_cast<const T *>(v),
-                       reinterpret_cast<const unsigned char *>(params), state, slots, pool_size, partial,
-                       counters, y);
+    if (bkv >= kBigBatchBkv) {
+        hipLaunchKernelGGL((oal_decode_kernel<T, MAXH, kRowsBig>), dim3(splits_of(kRowsBig), bkv), dim3(kThreads),
+                           0, stream, d.n_q_heads, d.n_kv_heads, reinterpret_cast<const T *>(q),
+                           reinterpret_cast<const T *>(k), reinterpret_cast<const T *>(v),
+                           reinterpret_cast<const unsigned char *>(params), state, slots, pool_size, partial,
+                           counters, y);
+    } else {
+        hipLaunchKernelGGL((oal_decode_kernel<T, MAXH, kRowsSmall>), dim3(splits_of(kRowsSmall), bkv),
+                           dim3(kThreads), 0, stream, d.n_q_heads, d.n_kv_heads, reinterpret_cast<const T *>(q),
+                           reinterpret_cast<const T *>(k), reinterpret_cast<const T *>(v),
+                           reinterpret_cast<const unsigned char *>(params), state, slots, pool_size, partial,
+                           counters, y);
+    }
     return hipGetLastError();
 }
 
