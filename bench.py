@@ -293,11 +293,20 @@ def main():
         c4 = cfg4()
         r4, ms4 = prefill_rate(c4, 128, 3)
         del c4
+        from oal_synth import per_dim_params
+        cg = qwen_like(1, 4096, 64, name="cfg2_g64")
+        cg.params = per_dim_params(640, 14)
+        rg, msg = prefill_rate(cg, 128, 5)
+        del cg
         out["prefill_other_workloads"] = {
             "B8_T4096": {"workload": "prefill B=8 T=4096 14q/2kv bf16, one call per step", **batch8},
             "B1_T32768": {"workload": "prefill B=1 T=32768 14q/2kv bf16, chunk 128", "tokens_per_s": r4,
                           "ms_per_call": ms4,
                           "vs_T4096_tokens_per_s": r4 / out["value"]},
+            "B1_T4096_G64": {"workload": "prefill B=1 T=4096 14q/2kv bf16, chunk 128, per-dimension "
+                                         "variant (G = 64 on every head: general coefficient blob)",
+                             "tokens_per_s": rg, "ms_per_call": msg,
+                             "vs_G_small_tokens_per_s": rg / out["value"]},
         }
 
     # ---------------- contribution scores (chi) on a calibration batch ----------------

@@ -26,7 +26,8 @@ EXPORTED = ("oal_params_bytes", "oal_state_bytes", "oal_prefill_workspace_bytes"
             "oal_timing_event_destroy", "oal_timing_event_record", "oal_timing_elapsed_ms",
             "oal_contribution_workspace_bytes", "oal_contribution", "oal_decode_step_indexed",
             "oal_prefill_varlen", "oal_prefill_packed", "oal_prefill_backward_workspace_bytes",
-            "oal_prefill_backward", "oal_decode_step_noalloc", "oal_calib_mfma_bf16", "oal_calib_copy")
+            "oal_prefill_backward", "oal_decode_step_noalloc", "oal_calib_mfma_bf16", "oal_calib_copy",
+            "oal_workspace_clear")
 DECODE_NOALLOC_MAX_BLOCKS = 256   # OAL_DECODE_NOALLOC_MAX_BLOCKS
 
 
@@ -84,6 +85,7 @@ def _load():
     lib.oal_calib_mfma_bf16.argtypes = [I, I, P, ctypes.POINTER(ctypes.c_double), P]
     lib.oal_calib_mfma_bf16.restype = ctypes.c_int
     lib.oal_calib_copy.argtypes, lib.oal_calib_copy.restype = [P, P, S, P], ctypes.c_int
+    lib.oal_workspace_clear.argtypes, lib.oal_workspace_clear.restype = [P, S, P], ctypes.c_int
     lib.oal_timing_event_create.argtypes, lib.oal_timing_event_create.restype = [ctypes.POINTER(P)], ctypes.c_int
     lib.oal_timing_event_destroy.argtypes, lib.oal_timing_event_destroy.restype = [P], ctypes.c_int
     lib.oal_timing_event_record.argtypes, lib.oal_timing_event_record.restype = [P, P], ctypes.c_int
@@ -241,6 +243,13 @@ def oal_prefill_timed(dims: oal_dims, T: int, chunk: int, q, k, v, params_dev, s
         ctypes.byref(dims), int(T), int(chunk), _ptr(q), _ptr(k), _ptr(v), _ptr(params_dev),
         _ptr(state_dev), _ptr(workspace), _nbytes(workspace, workspace_bytes), _ptr(y), _stream(stream),
         handles))
+
+
+def oal_workspace_clear(workspace, workspace_bytes=None, stream=None):
+    n = _nbytes(workspace, workspace_bytes)
+    if n == _UNSIZED:
+        raise ValueError("oal_workspace_clear: give workspace_bytes for a raw pointer")
+    _check("oal_workspace_clear", _lib.oal_workspace_clear(_ptr(workspace), n, _stream(stream)))
 
 
 def oal_calib_mfma_bf16(blocks: int, iters: int, out, stream=None) -> float:

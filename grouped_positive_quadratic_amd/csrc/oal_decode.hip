@@ -337,3 +337,22 @@ hipError_t oal_launch_decode(const oal_dims &d, const void *q, const void *k, co
     if (n_rep <= 8) return launch<float, 8>(d, q, k, v, params, state, slots, pool_size, ws, y, stream);
     return launch<float, 16>(d, q, k, v, params, state, slots, pool_size, ws, y, stream);
 }
+
+// ---- workspace clear ------------------------------------------------------------------------
+namespace {
+__global__ __launch_bounds__(256) void oal_fill_zero(unsigned int *__restrict__ p, size_t n) {
+    const size_t stride = (size_t)gridDim.x * 256;
+    for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n; i += stride) p[i] = 0u;
+}
+}  // namespace
+
+// zero n 4-byte words with a fill kernel (capturable: no memset node)
+hipError_t oal_launch_zero_words(void *p, size_t n, hipStream_t stream) {
+    if (n == 0) return hipSuccess;
+    size_t grid = (n + 255) / 256;
+    if (grid > 65536) grid = 65536;
+    hipLaunchKernelGGL(oal_fill_zero, dim3((unsigned)grid), dim3(256), 0, stream,
+                       reinterpret_cast<unsigned int *>(p), n);
+    return hipGetLastError();
+}
+

@@ -33,10 +33,14 @@ hipError_t oal_launch_backward(const oal_dims &d, int T_len, int C, const void *
                                const float *dy, const void *params, void *ws, float *dq, float *dk, float *dv,
                                float *dL, float *deps, hipStream_t stream);
 size_t oal_backward_ws_bytes_impl(const oal_dims &d, int T_len, int C);
+hipError_t oal_launch_zero_words(void *p, size_t n, hipStream_t stream);
 
 namespace {
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// prefill chunk lengths: 16, 32, 64, 128, 256 tokens
+bool prefill_chunk_ok(int32_t c) { return c == 16 || c == 32 || c == 64 || c == 128 || c == 256; }
 
 oal_status check_dims(const oal_dims *d) {
     if (!d) return OAL_E_ARG;
@@ -182,7 +186,7 @@ size_t oal_state_bytes(const oal_dims *d) {
 
 size_t oal_prefill_workspace_bytes(const oal_dims *d, int32_t T, int32_t chunk) {
     if (check_dims(d) != OAL_OK || T < 0) return 0;
-    if (chunk != 64 && chunk != 128 && chunk != 256) return 0;
+    if (!prefill_chunk_ok(chunk)) return 0;
     if (T == 0 || d->batch == 0) return 0;
     return oal_prefill_ws_bytes_impl(*d, T, chunk);
 }
@@ -294,7 +298,7 @@ static oal_status prefill_impl(const oal_dims *d, int32_t T, const int32_t *lens
     oal_status st = check_dims(d);
     if (st != OAL_OK) return st;
     if (T < 0) return OAL_E_SHAPE;
-    if (chunk != 64 && chunk != 128 && chunk != 256) return OAL_E_UNSUPPORTED;
+    if (!prefill_chunk_ok(chunk)) return OAL_E_UNSUPPORTED;
     if (T == 0 || d->batch == 0) return OAL_OK;
     // y == NULL: advance the state only (q is then not read and may be NULL)
     if ((y && !q) || !k || !v || !params_dev || !state_dev || !workspace) return OAL_E_ARG;
@@ -406,6 +410,17 @@ oal_status oal_decode_step_noalloc(const oal_dims *d, const void *q, const void 
         return OAL_E_ALIGN;
     hipError_t e = oal_launch_decode_noalloc(*d, q, k, v, params_dev, state_dev, y, stream);
     if (e != hipSuccess) {
+        (void)hipGetLastError();
+        return OAL_E_HIP;
+    }
+    return OAL_OK;
+}
+
+oal_status oal_workspace_clear(void *workspace, size_t workspace_bytes, hipStream_t stream) {
+    if (workspace_bytes == 0) return OAL_OK;
+    if (!workspace || workspace_bytes % 4) return OAL_E_ARG;
+    if (reinterpret_cast<uintptr_t>(workspace) & 3u) return OAL_E_ALIGN;
+    if (oal_launch_zero_words(workspace, workspace_bytes / 4, stream) != hipSuccess) {
         (void)hipGetLastError();
         return OAL_E_HIP;
     }

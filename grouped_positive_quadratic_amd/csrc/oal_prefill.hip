@@ -218,9 +218,11 @@ __device__ __forceinline__ void scan_delta_block(
     const T *__restrict__ k, const T *__restrict__ v, const unsigned char *__restrict__ params,
     const float *__restrict__ state, T *__restrict__ delta, float *__restrict__ tinit) {
     constexpr int EPU = 16 / (int)sizeof(T);
-    constexpr int LD = C + EPU;                         // padded row, 16-byte aligned
+    constexpr int CP = C < 32 ? 32 : C;                 // staged tokens: chunks below one K-step
+                                                        // are padded with zero tokens
+    constexpr int LD = CP + EPU;                        // padded row, 16-byte aligned
     constexpr int UPT = OAL_D / EPU;                    // 16-byte units per token row
-    constexpr int NU = 2 * C * UPT;                     // K and V units of one chunk
+    constexpr int NU = 2 * CP * UPT;                    // K and V units of one chunk
     constexpr int PER = NU / (64 * kScanWaves);
     static_assert(NU % (64 * kScanWaves) == 0, "chunk staging must tile the workgroup");
     extern __shared__ __align__(16) unsigned char smem[];
@@ -244,22 +246,22 @@ __device__ __forceinline__ void scan_delta_block(
 #pragma unroll
         for (int j = 0; j < PER; ++j) {
             const int u = tid + 64 * kScanWaves * j;
-            const int arr = u / (C * UPT), rem = u % (C * UPT), a = rem / C, tok = rem % C;
+            const int arr = u / (CP * UPT), rem = u % (CP * UPT), a = rem / CP, tok = rem % CP;
             const int pos = c * C + tok;
             const T *src = (arr ? v : k) + (krow0 + pos) * OAL_D + a * EPU;
-            r[j] = pos < Tb ? *reinterpret_cast<const oal_u32x4 *>(src) : zero16();
+            r[j] = (tok < C && pos < Tb) ? *reinterpret_cast<const oal_u32x4 *>(src) : zero16();
         }
 #pragma unroll
         for (int j = 0; j < PER; ++j) {
             const int u = tid + 64 * kScanWaves * j;
-            const int arr = u / (C * UPT), rem = u % (C * UPT), a = rem / C, tok = rem % C;
+            const int arr = u / (CP * UPT), rem = u % (CP * UPT), a = rem / CP, tok = rem % CP;
             const T *el = reinterpret_cast<const T *>(&r[j]);
             T *dst = (arr ? s_vT : s_kT) + (a * EPU) * LD + tok;
 #pragma unroll
             for (int e = 0; e < EPU; ++e) dst[e * LD] = el[e];
         }
-        for (int tok = tid; tok < C; tok += 64 * kScanWaves) {
-            s_kT[kRowOnes * LD + tok] = (c * C + tok < Tb) ? (T)1.0f : (T)0.0f;
+        for (int tok = tid; tok < CP; tok += 64 * kScanWaves) {
+            s_kT[kRowOnes * LD + tok] = (tok < C && c * C + tok < Tb) ? (T)1.0f : (T)0.0f;
             s_kT[kRowZero * LD + tok] = (T)0.0f;
         }
     }
@@ -287,7 +289,7 @@ __device__ __forceinline__ void scan_delta_block(
 #pragma unroll
         for (int n = 0; n < 5; ++n) acc[h][n] = oal_splat(0.0f);
 #pragma unroll
-    for (int sb = 0; sb < C / 32; ++sb) {
+    for (int sb = 0; sb < CP / 32; ++sb) {
         const int t0 = 32 * sb + 8 * g;
         OalFrag<T> a[2], bf[4];
 #pragma unroll
@@ -478,7 +480,10 @@ constexpr int kFragFloats = 5 * 4 * 64;   // one 16 x 80 accumulator tile, fragm
 template <typename T, int C> struct IntraLayout {
     static constexpr int EPU = 16 / (int)sizeof(T);
     static constexpr int QS = OAL_D + EPU;      // key row in LDS (16-byte aligned)
-    static constexpr int LDV = C + EPU;         // V^T row
+    // V^T row: at least 32 keys, since kappa [V;1] takes key tiles in pairs (a chunk of one
+    // 16-key tile reads a second, zero, tile)
+    static constexpr int CP = C < 32 ? 32 : C;
+    static constexpr int LDV = CP + EPU;
     static constexpr int O_K = 0;                                             // T [C][QS]
     static constexpr int O_VT = O_K + C * QS * (int)sizeof(T);                // T [64][LDV]
     static constexpr int O_LZ = O_VT + OAL_D * LDV * (int)sizeof(T);          // f32 [n_rep][8][64]
@@ -515,7 +520,7 @@ __device__ __forceinline__ void intra_block(int Lb, int T_len, OalSeqLayout sl, 
     // diagonal are skipped, and every workgroup then has NQT + 1 key tiles of work.
     // XCD-aware placement: the NQT / 2 workgroups of one (chunk, sequence x KV head) get
     // block ids congruent mod 8, i.e. the same XCD, so its K and V are fetched into one L2.
-    constexpr int NPAIR = NQT / 2;
+    constexpr int NPAIR = NQT > 1 ? NQT / 2 : 1;   // a chunk of one query tile: that tile alone
     const int xcd = Lb % kXcds, i8 = Lb / kXcds;
     const int unit = xcd + kXcds * (i8 / NPAIR), pi = i8 % NPAIR;
     if (unit >= nchunks * n_bkv) return;
@@ -585,6 +590,9 @@ __device__ __forceinline__ void intra_block(int Lb, int T_len, OalSeqLayout sl, 
             const int u = tid + NTH * j;
             if (u < nlz) reinterpret_cast<float4 *>(s_lz)[u] = rl[j];
         }
+        if (Lay::CP > C)   // the zero key tile beside a one-tile chunk
+            for (int u = tid; u < OAL_D * (Lay::CP - C); u += NTH)
+                s_vT[(u / (Lay::CP - C)) * LDV + C + u % (Lay::CP - C)] = (T)0.0f;
     }
     __syncthreads();
 
@@ -695,11 +703,11 @@ __device__ __forceinline__ void intra_block(int Lb, int T_len, OalSeqLayout sl, 
 #pragma unroll
             for (int ii = 0; ii < 4; ++ii) up[(n * 4 + ii) * 64] = acc[n][ii];
     };
-    static_assert(NQT % 2 == 0 && NQT <= 16, "tile pairs");
+    static_assert((NQT == 1 || NQT % 2 == 0) && NQT <= 16, "tile pairs");
     for (int i = wave; i < n_rep; i += kIntraWaves) {
         if (i != wave) hsc = head_scalars(i);
 #pragma unroll
-        for (int tt = 0; tt < 2; ++tt) {
+        for (int tt = 0; tt < (NQT > 1 ? 2 : 1); ++tt) {
             const int qt = tt == 0 ? pi : NQT - 1 - pi;
             if (c * C + qt * 16 >= Tb) break;
             if (i != wave || tt == 1) load_q(i, qt, qf);
@@ -1097,7 +1105,7 @@ __global__ __launch_bounds__(256, 2) void oal_readout(
 }
 
 template <typename T, int C>
-size_t scan_lds() { return (size_t)(66 + 64) * (C + 16 / sizeof(T)) * sizeof(T); }
+size_t scan_lds() { return (size_t)(66 + 64) * ((C < 32 ? 32 : C) + 16 / sizeof(T)) * sizeof(T); }
 
 template <typename T, int C, int R>
 size_t readout_lds() { return (size_t)ReadoutLayout<T, C, R>::BYTES; }
@@ -1186,7 +1194,7 @@ hipError_t launch_all(const oal_dims &d, int T_len, OalSeqLayout sl, const void 
         static std::atomic<int> lds_set[kMaxDevices];
         if ((e = ensure_lds_limit(kern, lds, lds_set)) != hipSuccess) return e;
         const int nunits = p.nchunks * bkv;
-        const int n_intra = kXcds * (C / 32) * ((nunits + kXcds - 1) / kXcds);   // tile pairs
+        const int n_intra = kXcds * (C > 16 ? C / 32 : 1) * ((nunits + kXcds - 1) / kXcds);   // tile pairs
         const int n_delta = kDeltaBlocks * p.nchunks * bkv;
         hipLaunchKernelGGL(kern, dim3(n_intra + n_delta), dim3(64 * kIntraWaves), lds, stream, T_len, sl,
                            d.n_q_heads, d.n_kv_heads, p.nchunks, bkv, n_delta, reinterpret_cast<const T *>(q),
@@ -1241,10 +1249,14 @@ hipError_t oal_launch_prefill(const oal_dims &d, int T_len, const int *lens, con
                               void *ws, float *y, hipStream_t stream, hipEvent_t *marks) {
     const OalSeqLayout sl{lens, cu, total};
     if (d.dtype == OAL_BF16) {
+        if (C == 16) return launch_all<__bf16, 16>(d, T_len, sl, q, k, v, params, state, ws, y, stream, marks);
+        if (C == 32) return launch_all<__bf16, 32>(d, T_len, sl, q, k, v, params, state, ws, y, stream, marks);
         if (C == 64) return launch_all<__bf16, 64>(d, T_len, sl, q, k, v, params, state, ws, y, stream, marks);
         if (C == 128) return launch_all<__bf16, 128>(d, T_len, sl, q, k, v, params, state, ws, y, stream, marks);
         return launch_all<__bf16, 256>(d, T_len, sl, q, k, v, params, state, ws, y, stream, marks);
     }
+    if (C == 16) return launch_all<float, 16>(d, T_len, sl, q, k, v, params, state, ws, y, stream, marks);
+    if (C == 32) return launch_all<float, 32>(d, T_len, sl, q, k, v, params, state, ws, y, stream, marks);
     if (C == 64) return launch_all<float, 64>(d, T_len, sl, q, k, v, params, state, ws, y, stream, marks);
     if (C == 128) return launch_all<float, 128>(d, T_len, sl, q, k, v, params, state, ws, y, stream, marks);
     return launch_all<float, 256>(d, T_len, sl, q, k, v, params, state, ws, y, stream, marks);

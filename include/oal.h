@@ -123,12 +123,19 @@ oal_status oal_params_pack(const oal_dims *dims, const oal_head_params *hp, void
 
 /* Validate the parameters, upload the parameter blob to `params_dev`
  * (oal_params_bytes(dims) bytes, device) and zero `state_dev` (oal_state_bytes(dims) bytes,
- * device; may be NULL to leave it untouched). A zero state is an empty prefix. */
+ * device; may be NULL to leave it untouched). A zero state is an empty prefix.
+ * Passage: reproduction notes, section "核心公式" -- the kernel's parameters (the group map
+ * of the dims, the lower-triangular factor L with M = L L^T, eps) and the prefix states
+ * H0, H1, H2, which are all zero before the first token. */
 oal_status oal_state_init(const oal_dims *dims, const oal_head_params *hp, void *params_dev,
                           float *state_dev, hipStream_t stream);
 
 /* Chunked causal prefill of T new tokens per sequence, continuing from `state_dev`.
- *   chunk      -- chunk length C in {64, 128, 256}: the tokens of a chunk see the state
+ * Passage: reproduction notes, section "核心公式" -- for every new token, the readout display
+ * u~ = phi_h(q) . H over the prefix states and y = u~[0:64] / u~[64], with H advanced by the
+ * H-state recurrence over the tokens. The chunking is this library's evaluation order: it
+ * gives the same causal kernel sums up to rounding.
+ *   chunk      -- chunk length C in {16, 32, 64, 128, 256}: the tokens of a chunk see the state
  *                 before the chunk plus an exact intra-chunk kernel sum.
  *   q, k, v    -- [batch, heads, T, 64] of dims->dtype (device).
  *   state_dev  -- in: prefix states of the tokens before these T; out: states after them.
@@ -185,6 +192,8 @@ oal_status oal_prefill_packed(const oal_dims *dims, int32_t T, const int32_t *cu
 
 /* One decode step: appends one token per sequence to the prefix states and reads out the
  * attention of each query head over all tokens so far (the new one included).
+ * Passage: reproduction notes, section "核心公式" -- one step of the H-state recurrence,
+ * H <- H + psi(k) [v;1]^T, then the readout display for the new token.
  *   q [batch, n_q_heads, 64], k, v [batch, n_kv_heads, 64] of dims->dtype (device);
  *   state_dev updated in place; y [batch, n_q_heads, 64] fp32.
  *   workspace -- oal_decode_workspace_bytes(dims) bytes of device scratch that must be
@@ -196,6 +205,16 @@ oal_status oal_prefill_packed(const oal_dims *dims, int32_t T, const int32_t *cu
 oal_status oal_decode_step(const oal_dims *dims, const void *q, const void *k, const void *v,
                            const void *params_dev, float *state_dev, void *workspace,
                            size_t workspace_bytes, float *y, hipStream_t stream);
+
+/* Zero a workspace of oal_decode_step, oal_decode_step_indexed or oal_contribution (its
+ * arrival counters and partial sums) with a fill kernel on `stream`: no memset node, so the
+ * call may be captured into a graph. A workspace needs it before its first use, before it
+ * serves calls of another shape, and after a call that did not run to completion (a device
+ * error or an abandoned stream): those calls return their counters to zero only as they
+ * finish. workspace 4-byte aligned (OAL_E_ALIGN), workspace_bytes a multiple of 4
+ * (OAL_E_ARG); 0 bytes is a no-op. Not a step of the method: the callers are those that keep
+ * workspaces across calls. */
+oal_status oal_workspace_clear(void *workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* oal_decode_step without a caller workspace, for callers that cannot allocate device memory
  * (code under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc). Same

@@ -130,6 +130,20 @@ def random_params(rng: np.random.Generator, n_q_heads: int, d: int = D_H, g_min:
     return HeadParams(Gs, gamma, Ls, np.full(n_q_heads, eps, dtype=np.float32))
 
 
+def per_dim_params(seed: int, n_heads: int, eps: float = 1e-3) -> HeadParams:
+    """The per-dimension variant: G = 64 on every head, dimension r of head h in group
+    perm_h[r] (a random permutation); L_h lower triangular 65 x 65 with N(0, 0.3^2) entries
+    and diagonal |.| + 0.1."""
+    rng = np.random.default_rng(seed)
+    G = 64
+    L = np.zeros((n_heads, G + 1, G + 1), np.float32)
+    for h in range(n_heads):
+        L[h] = np.tril(rng.normal(0.0, 0.3, (G + 1, G + 1)))
+        np.fill_diagonal(L[h], np.abs(np.diag(L[h])) + 0.1)
+    gamma = np.stack([rng.permutation(64) for _ in range(n_heads)]).astype(np.uint8)
+    return HeadParams(np.full(n_heads, G, np.int32), gamma, L, np.full(n_heads, eps, np.float32))
+
+
 # ---------------------------------------------------------------------------------------
 # configs
 

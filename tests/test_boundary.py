@@ -38,6 +38,11 @@ def test_sizes():
     assert gpq.oal_params_bytes(d) > 14 * 2176 * 4
     assert gpq.oal_prefill_workspace_bytes(d, 4096, 128) > 0
     assert gpq.oal_prefill_workspace_bytes(d, 4096, 100) == 0
+    assert gpq.oal_prefill_workspace_bytes(d, 4096, 48) == 0
+    for c in (16, 32, 64, 128, 256):    # every listed chunk length has a workspace
+        assert gpq.oal_prefill_workspace_bytes(d, 4096, c) > 0
+    # fewer, longer chunks need fewer snapshots
+    assert gpq.oal_prefill_workspace_bytes(d, 4096, 16) > gpq.oal_prefill_workspace_bytes(d, 4096, 32)
     assert gpq.oal_prefill_workspace_bytes(d, 0, 128) == 0
     assert gpq.oal_decode_workspace_bytes(d) > 0
     bad = gpq.make_dims(1, 14, 3, "bf16")
@@ -129,6 +134,7 @@ def test_validation_errors_enqueue_nothing():
     assert _code(gpq.oal_contribution, gpq.make_dims(1, 2, 1, "bf16", d_h=32), 8, *c4, 0) == 5
     b9 = (A, A, A, A, A, A, A, A, A, None, None)   # q, k, v, dy, params, workspace, dq, dk, dv, dL, deps
     assert _code(gpq.oal_prefill_backward, d, 8, 100, *b9, 0) == 5            # chunk
+    assert _code(gpq.oal_prefill_backward, d, 8, 32, *b9, 0) == 5             # backward: 64..256
     assert _code(gpq.oal_prefill_backward, d, -1, 64, *b9, 0) == 2            # T < 0
     assert _code(gpq.oal_prefill_backward, d, 0, 64, *([None] * 11), 0) == 0   # T = 0: no-op
     assert _code(gpq.oal_prefill_backward, gpq.make_dims(0, 2, 1, "bf16"), 8, 64, *([None] * 11), 0) == 0
@@ -387,3 +393,13 @@ def test_calibration_calls_validate_arguments():
     assert _code(gpq.oal_calib_copy, A + 8, A + 4096, 64, stream=0) == 4    # misaligned
     assert _code(gpq.oal_calib_copy, None, A, 64, stream=0) == 1
     assert _code(gpq.oal_calib_copy, A, A + 4096, 0, stream=0) == 0         # nothing to move
+
+
+def test_workspace_clear_validates_arguments():
+    A = 4096   # fake, aligned, never dereferenced: validation fails first
+    assert _code(gpq.oal_workspace_clear, A, 10, stream=0) == 1          # not a multiple of 4
+    assert _code(gpq.oal_workspace_clear, A + 2, 64, stream=0) == 4      # misaligned
+    assert _code(gpq.oal_workspace_clear, None, 64, stream=0) == 1
+    assert _code(gpq.oal_workspace_clear, A, 0, stream=0) == 0           # nothing to clear
+    with pytest.raises(ValueError):
+        gpq.oal_workspace_clear(A, stream=0)                             # raw pointer needs a size

@@ -15,7 +15,7 @@ import numpy as np
 import pytest
 
 import oracle
-from oal_synth import HeadParams, qwen_like, small
+from oal_synth import per_dim_params, qwen_like, small
 
 pytestmark = pytest.mark.gpu
 
@@ -30,16 +30,7 @@ def _need_gpu():
 
 
 def g64_params(seed, n_heads):
-    """G = 64 on every head: dimension r of head h is group perm_h[r] (a random permutation);
-    L_h lower triangular 65 x 65 with N(0, 0.3^2) entries and diagonal |.| + 0.1."""
-    rng = np.random.default_rng(seed)
-    G = 64
-    L = np.zeros((n_heads, G + 1, G + 1), np.float32)
-    for h in range(n_heads):
-        L[h] = np.tril(rng.normal(0.0, 0.3, (G + 1, G + 1)))
-        np.fill_diagonal(L[h], np.abs(np.diag(L[h])) + 0.1)
-    gamma = np.stack([rng.permutation(64) for _ in range(n_heads)]).astype(np.uint8)
-    return HeadParams(np.full(n_heads, G, np.int32), gamma, L, np.full(n_heads, 1e-3, np.float32))
+    return per_dim_params(seed, n_heads)
 
 
 def _positions(T, chunk, rng, n_random=6):

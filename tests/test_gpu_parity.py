@@ -45,7 +45,7 @@ def test_decode_from_zero_cfg1():
     assert serr <= 1e-5
 
 
-@pytest.mark.parametrize("chunk", [64, 128, 256])
+@pytest.mark.parametrize("chunk", [16, 32, 64, 128, 256])
 def test_prefill_cfg1(chunk):
     inp = cfg1()
     sess = session_for(inp, chunk)
@@ -70,6 +70,9 @@ SMALL = [  # seed, B, Hq, Hkv, T, chunk
     (19, 1, 12, 1, 130, 64),    # 12 per KV head: readout head groups of 4
     (20, 2, 5, 1, 90, 128),     # 5 per KV head: head groups of 1
     (21, 1, 6, 6, 70, 64),      # one query head per KV head (no GQA)
+    (23, 1, 14, 2, 101, 16),    # chunks of one query tile (ragged tail)
+    (24, 2, 7, 1, 77, 32),      # chunks of two query tiles
+    (25, 1, 14, 2, 40, 16),     # T = 2.5 chunks
 ]
 
 
@@ -115,6 +118,22 @@ def test_prefill_then_decode(dtype):
     _report(f"prefill+decode {dtype}", err)
     assert err <= TOL[dtype]
     assert state_ok(sess.state_np(), inp.k, inp.v, dtype)
+
+
+def test_workspace_clear_recovers_a_poisoned_decode_workspace():
+    """A decode workspace whose arrival counters hold garbage (as after a call that did not
+    finish) gives wrong results; oal_workspace_clear makes it serve exactly like a fresh one."""
+    inp = small(22, 2, 14, 2, 40, dtype="bf16")
+    a, b = session_for(inp, 64), session_for(inp, 64)
+    for sess in (a, b):
+        sess.prefill(inp.q[:, :, :32], inp.k[:, :, :32], inp.v[:, :, :32], 64)
+    b.dws.fill_(0xA5)                       # poisoned counters and partial sums
+    gpq.oal_workspace_clear(b.dws)
+    for i in range(32, 40):
+        ya = a.decode(inp.q[:, :, i], inp.k[:, :, i], inp.v[:, :, i])
+        yb = b.decode(inp.q[:, :, i], inp.k[:, :, i], inp.v[:, :, i])
+        assert torch.equal(ya, yb), i
+    assert np.array_equal(a.state_np(), b.state_np())
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
