@@ -96,7 +96,7 @@ def _load():
     lib.oal_contribution.argtypes, lib.oal_contribution.restype = [dp, I, P, P, P, S, P, P, P], ctypes.c_int
     lib.oal_prefill_backward_workspace_bytes.argtypes = [dp, I, I]
     lib.oal_prefill_backward_workspace_bytes.restype = S
-    lib.oal_prefill_backward.argtypes = [dp, I, I, P, P, P, P, P, P, S, P, P, P, P, P, P]
+    lib.oal_prefill_backward.argtypes = [dp, I, I, P, P, P, P, P, P, P, S, P, P, P, P, P, P, P]
     lib.oal_prefill_backward.restype = ctypes.c_int
     return lib
 
@@ -324,15 +324,17 @@ def oal_prefill_backward_workspace_bytes(dims: oal_dims, T: int, chunk: int) -> 
 
 
 def oal_prefill_backward(dims: oal_dims, T: int, chunk: int, q, k, v, dy, params_dev, workspace,
-                         dq, dk, dv, dL=None, deps=None, stream=None, workspace_bytes=None):
+                         dq, dk, dv, dL=None, deps=None, stream=None, workspace_bytes=None,
+                         state_in=None, dstate_in=None):
     """Gradients dq [batch, n_q_heads, T, 64], dk, dv [batch, n_kv_heads, T, 64] (fp32 device
-    tensors written by the library) of sum(dy * y) for the prefill of T tokens from an empty
-    prefix; with dL [n_q_heads, 65, 65] and deps [n_q_heads] (fp32 device tensors, or both
-    None) also the coefficient gradients."""
+    tensors written by the library) of sum(dy * y) for the prefill of T tokens continuing from
+    state_in (None: an empty prefix); with dL [n_q_heads, 65, 65] and deps [n_q_heads] (fp32
+    device tensors, or both None) also the coefficient gradients, and with dstate_in (a state
+    buffer) the gradient of the incoming state."""
     _check("oal_prefill_backward", _lib.oal_prefill_backward(
         ctypes.byref(dims), int(T), int(chunk), _ptr(q), _ptr(k), _ptr(v), _ptr(dy),
-        _ptr(params_dev), _ptr(workspace), _nbytes(workspace, workspace_bytes), _ptr(dq), _ptr(dk),
-        _ptr(dv), _ptr(dL), _ptr(deps),
+        _ptr(params_dev), _ptr(state_in), _ptr(workspace), _nbytes(workspace, workspace_bytes), _ptr(dq),
+        _ptr(dk), _ptr(dv), _ptr(dstate_in), _ptr(dL), _ptr(deps),
         _stream(stream)))
 
 

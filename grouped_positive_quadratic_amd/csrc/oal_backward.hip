@@ -1,6 +1,6 @@
 // oal_backward.hip -- gfx950 kernels of the prefill backward: dq, dk, dv (and the gradients of
-// the kernel coefficients L, eps) of sum(dy * y) for the causal attention y of a prefill from
-// an empty prefix.
+// the kernel coefficients L, eps, and of the incoming prefix state) of sum(dy * y) for the
+// causal attention y of a prefill that continues from a given (or an empty) prefix state.
 //
 // The forward (reproduction notes of arXiv 2610.13674, section "核心公式": the kernel kappa,
 // the H-state recurrence and the readout u~ = phi(q) . H, y = u~[0:64] / u~[64]) is
@@ -12,8 +12,9 @@
 //   dq_i = Jphi_h(q_i)^T (S_c g_i)         + sum_{j <= i, same chunk} dkappa_ij dkappa_ij/dq_i
 //   dv_j = (R_c^T psi(k_j))[0:64]          + sum_h sum_{i >= j, same chunk} kappa_ij g_i[0:64]
 //   dk_j = Jpsi(k_j)^T (R_c [v_j; 1])      + sum_h sum_{i >= j, same chunk} dkappa_ij dkappa_ij/dk_j
-// where S_c sums psi(k_j) [v_j; 1]^T over the chunks before c (the forward's prefix state) and
-// R_c sums phi_h(q_i) g_i^T over the chunks after c and the query heads h of the KV head.
+// where S_c is the incoming state S_0 plus psi(k_j) [v_j; 1]^T summed over the chunks before c
+// (the forward's prefix state) and R_c sums phi_h(q_i) g_i^T over the chunks after c and the
+// query heads h of the KV head; the gradient of S_0 is that sum over every chunk.
 // Inside a chunk kappa is taken from its z-terms, as in the forward's intra-chunk part:
 //   z_m = [m = 0] L00 + sum_r Lz[m][r] q_r k_r,   kappa = eps + sum_{m <= G} z_m^2,
 //   dkappa/dq_r = 2 k_r sum_m z_m Lz[m][r]        (and the same with q and k exchanged);
@@ -305,12 +306,16 @@ __global__ __launch_bounds__(kThreads) void oal_bwd_increments(int T_len, int C,
 }
 
 // 2 / 6. Exclusive prefix (reverse = 0) or suffix (reverse = 1) sum over the chunks of each
-// (sequence x KV head), in place; one thread per state element.
-__global__ __launch_bounds__(kThreads) void oal_bwd_scan(int nch, int reverse, float *__restrict__ st) {
+// (sequence x KV head), in place; one thread per state element. The running sum starts from
+// init (the incoming state of the forward, NULL: zero) and its final value, the sum over all
+// chunks, is written to total when given (the reverse scan's total is the gradient of the
+// incoming state: every chunk's state contains it).
+__global__ __launch_bounds__(kThreads) void oal_bwd_scan(int nch, int reverse, float *__restrict__ st,
+                                                         const float *__restrict__ init, float *__restrict__ total) {
     const int e = blockIdx.x * kThreads + threadIdx.x;
     if (e >= OAL_NFEAT * OAL_V1) return;
     float *p = st + (size_t)blockIdx.y * nch * OAL_STATE_STRIDE + e;
-    float run = 0.0f;
+    float run = init ? init[(size_t)blockIdx.y * OAL_STATE_STRIDE + e] : 0.0f;
 #pragma unroll 4
     for (int i = 0; i < nch; ++i) {
         const size_t o = (size_t)(reverse ? nch - 1 - i : i) * OAL_STATE_STRIDE;
@@ -318,6 +323,7 @@ __global__ __launch_bounds__(kThreads) void oal_bwd_scan(int nch, int reverse, f
         p[o] = run;
         run += t;
     }
+    if (total) total[(size_t)blockIdx.y * OAL_STATE_STRIDE + e] = run;
 }
 
 // Keys of the chunk that query lane i of tile qt sees, tile kt: all of an earlier tile, up to
@@ -335,7 +341,7 @@ __device__ inline bool sees(int kt, int qt, int jj, int i) { return kt < qt || j
 //    f (LDS tables); B operand: S_c[f][col], col = 16 tile + l % 16. The result goes to an LDS
 //    tile. Pairs inside the chunk: lane = query, the four waves split the keys.
 template <typename T>
-__global__ __launch_bounds__(kThreads) void oal_bwd_readout_g(int T_len, int C, int nch, int n_q_heads,
+__global__ __launch_bounds__(kThreads) void oal_bwd_readout_g(int s0, int T_len, int C, int nch, int n_q_heads,
                                                                int n_kv_heads, const T *__restrict__ q,
                                                                const T *__restrict__ k, const T *__restrict__ v,
                                                                const float *__restrict__ dy,
@@ -380,7 +386,7 @@ __global__ __launch_bounds__(kThreads) void oal_bwd_readout_g(int T_len, int C, 
         oal_f32x4 E[5];                             // even and odd K-steps: independent chains
 #pragma unroll
         for (int ct = 0; ct < 5; ++ct) D[ct] = E[ct] = oal_splat(0.0f);
-        if (c > 0) {                               // S_0 = 0
+        if (c > 0 || s0) {                         // S_0 = 0 without an incoming state
             const float *S = st + ((size_t)((size_t)b * n_kv_heads + kv) * nch + c) * OAL_STATE_STRIDE;
             const float *Sd = S + (size_t)OAL_NFEAT * OAL_D;
             float *sblk = vs;
@@ -533,7 +539,7 @@ __device__ inline int dq_row_of(int s, int t) {
 //     sequence), each split's result going to the dk half of its partial slot.
 template <typename T, bool KEYS>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void oal_bwd_dq_inter_mfma(
-    int T_len, int C, int nch, int n_q_heads, int n_kv_heads, const T *__restrict__ q, const T *__restrict__ v,
+    int s0, int T_len, int C, int nch, int n_q_heads, int n_kv_heads, const T *__restrict__ q, const T *__restrict__ v,
     const unsigned char *__restrict__ params, const float *__restrict__ st, const float *__restrict__ gv,
     const float *__restrict__ gd, float *__restrict__ dq) {
     __shared__ __align__(16) float xq[64 * 68];   // query tile
@@ -570,7 +576,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     oal_f32x4 acc[4];                              // dq: query 16 w + 4 kg + jj, dim 16 st + lr
 #pragma unroll
     for (int sti = 0; sti < 4; ++sti) acc[sti] = oal_splat(0.0f);
-    if (KEYS ? c < nch - 1 : c > 0) {              // S_0 = 0, R of the last chunk = 0
+    if (KEYS ? c < nch - 1 : (c > 0 || s0)) {      // R of the last chunk = 0; S_0 = 0 without
+                                                   // an incoming state
         const float *S = st + ((size_t)((size_t)b * n_kv_heads + kv) * nch + c) * OAL_STATE_STRIDE;
         const float *Sd = S + (size_t)OAL_NFEAT * OAL_D;
         // T of the next step, this thread's share: rows s = (tid + 256 m) / 16, 4 columns each
@@ -1167,8 +1174,8 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 template <typename T>
 hipError_t launch_backward(const oal_dims &d, int T_len, int C, const void *q_, const void *k_, const void *v_,
-                           const float *dy, const unsigned char *params, void *ws, float *dq, float *dk, float *dv,
-                           float *dL, float *deps, hipStream_t stream) {
+                           const float *dy, const unsigned char *params, const float *state_in, void *ws, float *dq,
+                           float *dk, float *dv, float *dstate_in, float *dL, float *deps, hipStream_t stream) {
     const T *q = static_cast<const T *>(q_), *k = static_cast<const T *>(k_), *v = static_cast<const T *>(v_);
     const int B = d.batch, Hq = d.n_q_heads, Hkv = d.n_kv_heads;
     const int nch = (T_len + C - 1) / C, tpc = C / 64;
@@ -1189,10 +1196,11 @@ hipError_t launch_backward(const oal_dims &d, int T_len, int C, const void *q_, 
     const int nslots = kInterSplits + Hq / Hkv;
     hipLaunchKernelGGL((oal_bwd_increments<T, false>), g_inc, blk, 0, stream, T_len, C, nch, Hq, Hkv, k, v,
                        (const float *)nullptr, (const float *)nullptr, params, st, (float *)nullptr);
-    hipLaunchKernelGGL(oal_bwd_scan, g_scan, blk, 0, stream, nch, 0, st);
-    hipLaunchKernelGGL(oal_bwd_readout_g<T>, g_q, blk, 0, stream, T_len, C, nch, Hq, Hkv, q, k, v, dy, params, st,
+    hipLaunchKernelGGL(oal_bwd_scan, g_scan, blk, 0, stream, nch, 0, st, state_in, (float *)nullptr);
+    const int s0 = state_in != nullptr;
+    hipLaunchKernelGGL(oal_bwd_readout_g<T>, g_q, blk, 0, stream, s0, T_len, C, nch, Hq, Hkv, q, k, v, dy, params, st,
                        gv, gd);
-    hipLaunchKernelGGL((oal_bwd_dq_inter_mfma<T, false>), g_q, blk, 0, stream, T_len, C, nch, Hq, Hkv, q,
+    hipLaunchKernelGGL((oal_bwd_dq_inter_mfma<T, false>), g_q, blk, 0, stream, s0, T_len, C, nch, Hq, Hkv, q,
                        (const T *)nullptr, params, st, gv, gd, dq);
     hipLaunchKernelGGL(oal_bwd_dq_intra_mfma<T>, g_q, blk, 0, stream, T_len, C, Hq, Hkv, q, k, v, params, gv, gd, dq);
     hipLaunchKernelGGL(oal_bwd_dkv_intra_mfma<T>, g_kh, blk, 0, stream, T_len, C, Hq, Hkv, q, k, v, params, gv, gd,
@@ -1208,8 +1216,8 @@ hipError_t launch_backward(const oal_dims &d, int T_len, int C, const void *q_, 
                            Hq, dwp, dwt);
         hipLaunchKernelGGL(oal_bwd_coef, dim3(Hq), blk, 0, stream, params, dwt, dL, deps);
     }
-    hipLaunchKernelGGL(oal_bwd_scan, g_scan, blk, 0, stream, nch, 1, st);
-    hipLaunchKernelGGL((oal_bwd_dq_inter_mfma<T, true>), dim3(nch * tpc, Hkv * kDkSplits, B), blk, 0, stream, T_len, C, nch, Hq,
+    hipLaunchKernelGGL(oal_bwd_scan, g_scan, blk, 0, stream, nch, 1, st, (const float *)nullptr, dstate_in);
+    hipLaunchKernelGGL((oal_bwd_dq_inter_mfma<T, true>), dim3(nch * tpc, Hkv * kDkSplits, B), blk, 0, stream, s0, T_len, C, nch, Hq,
                        Hkv, k, v, params, st, gv, gd, part);
     hipLaunchKernelGGL(oal_bwd_dv_inter<T>, g_ki, blk, 0, stream, T_len, C, nch, Hkv, k, st, part);
     hipLaunchKernelGGL(oal_bwd_kv_reduce, g_red, blk, 0, stream, kvrows, nslots, part, dk, dv);
@@ -1227,10 +1235,11 @@ size_t oal_backward_ws_bytes_impl(const oal_dims &d, int T_len, int C) {
 }
 
 hipError_t oal_launch_backward(const oal_dims &d, int T_len, int C, const void *q, const void *k, const void *v,
-                               const float *dy, const void *params, void *ws, float *dq, float *dk, float *dv,
-                               float *dL, float *deps, hipStream_t stream) {
+                               const float *dy, const void *params, const float *state_in, void *ws, float *dq,
+                               float *dk, float *dv, float *dstate_in, float *dL, float *deps, hipStream_t stream) {
     const unsigned char *p = static_cast<const unsigned char *>(params);
     if (d.dtype == OAL_BF16)
-        return launch_backward<__bf16>(d, T_len, C, q, k, v, dy, p, ws, dq, dk, dv, dL, deps, stream);
-    return launch_backward<float>(d, T_len, C, q, k, v, dy, p, ws, dq, dk, dv, dL, deps, stream);
+        return launch_backward<__bf16>(d, T_len, C, q, k, v, dy, p, state_in, ws, dq, dk, dv, dstate_in, dL, deps,
+                                       stream);
+    return launch_backward<float>(d, T_len, C, q, k, v, dy, p, state_in, ws, dq, dk, dv, dstate_in, dL, deps, stream);
 }

@@ -30,8 +30,8 @@ hipError_t oal_launch_contribution(const oal_dims &d, int T_len, const void *q, 
 size_t oal_contribution_ws_bytes_impl(const oal_dims &d, int T_len);
 size_t oal_prefill_ws_bytes_impl(const oal_dims &d, int T_len, int C);
 hipError_t oal_launch_backward(const oal_dims &d, int T_len, int C, const void *q, const void *k, const void *v,
-                               const float *dy, const void *params, void *ws, float *dq, float *dk, float *dv,
-                               float *dL, float *deps, hipStream_t stream);
+                               const float *dy, const void *params, const float *state_in, void *ws, float *dq,
+                               float *dk, float *dv, float *dstate_in, float *dL, float *deps, hipStream_t stream);
 size_t oal_backward_ws_bytes_impl(const oal_dims &d, int T_len, int C);
 hipError_t oal_launch_zero_words(void *p, size_t n, hipStream_t stream);
 
@@ -466,9 +466,9 @@ size_t oal_prefill_backward_workspace_bytes(const oal_dims *d, int32_t T, int32_
 }
 
 oal_status oal_prefill_backward(const oal_dims *d, int32_t T, int32_t chunk, const void *q, const void *k,
-                                const void *v, const float *dy, const void *params_dev, void *workspace,
-                                size_t workspace_bytes, float *dq, float *dk, float *dv, float *dL, float *deps,
-                                hipStream_t stream) {
+                                const void *v, const float *dy, const void *params_dev, const float *state_in,
+                                void *workspace, size_t workspace_bytes, float *dq, float *dk, float *dv,
+                                float *dstate_in, float *dL, float *deps, hipStream_t stream) {
     oal_status st = check_dims(d);
     if (st != OAL_OK) return st;
     if (T < 0) return OAL_E_SHAPE;
@@ -479,11 +479,12 @@ oal_status oal_prefill_backward(const oal_dims *d, int32_t T, int32_t chunk, con
         return OAL_E_ARG;
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(dy) || !aligned16(params_dev) ||
         !aligned16(workspace) || !aligned16(dq) || !aligned16(dk) || !aligned16(dv) ||
+        (state_in && !aligned16(state_in)) || (dstate_in && !aligned16(dstate_in)) ||
         (reinterpret_cast<uintptr_t>(dL) & 3u) || (reinterpret_cast<uintptr_t>(deps) & 3u))
         return OAL_E_ALIGN;
     if (workspace_bytes < oal_backward_ws_bytes_impl(*d, T, chunk)) return OAL_E_ARG;
-    hipError_t e = oal_launch_backward(*d, T, chunk, q, k, v, dy, params_dev, workspace, dq, dk, dv, dL, deps,
-                                       stream);
+    hipError_t e = oal_launch_backward(*d, T, chunk, q, k, v, dy, params_dev, state_in, workspace, dq, dk, dv,
+                                       dstate_in, dL, deps, stream);
     if (e != hipSuccess) {
         (void)hipGetLastError();
         return OAL_E_HIP;

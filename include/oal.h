@@ -260,11 +260,16 @@ oal_status oal_contribution(const oal_dims *dims, int32_t T, const void *q, cons
                             void *workspace, size_t workspace_bytes, float *chi, float *chi_mean,
                             hipStream_t stream);
 
-/* Backward of oal_prefill from an empty prefix (reproduction notes of arXiv 2610.13674,
- * section "核心公式": kappa, the H-state recurrence and the readout; the gradients follow by
- * the chain rule through the chunked form). For y = oal_prefill(q, k, v) of T tokens per
- * sequence starting from a zero state, and the loss sum(dy * y), it writes
- *   dq [batch, n_q_heads, T, 64], dk and dv [batch, n_kv_heads, T, 64], all fp32 (device).
+/* Backward of oal_prefill (reproduction notes of arXiv 2610.13674, section "核心公式": kappa,
+ * the H-state recurrence and the readout; the gradients follow by the chain rule through the
+ * chunked form). For y = oal_prefill(q, k, v) of T tokens per sequence continuing from the
+ * prefix states state_in (NULL: a zero state, an empty prefix), and the loss sum(dy * y), it
+ * writes
+ *   dq [batch, n_q_heads, T, 64], dk and dv [batch, n_kv_heads, T, 64], all fp32 (device);
+ *   dstate_in, unless NULL: dLoss/dstate_in, in the state layout (the gradient of each stored
+ *        element of H; the 31 padding floats of a block are not written). Chained with the
+ *        backward of the call that produced state_in (whose outputs' loss then also depends
+ *        on its states through later calls), it trains over a sequence prefilled in pieces.
  * and, unless dL and deps are NULL, the gradients of the kernel coefficients of every query
  * head (summed over the batch):
  *   dL   [n_q_heads][65][65] fp32 (device, 4-byte aligned): entry [h][a][b] is dLoss/dL[a][b]
@@ -278,19 +283,22 @@ oal_status oal_contribution(const oal_dims *dims, int32_t T, const void *q, cons
  *   q, k, v    -- as for oal_prefill ([batch, heads, T, 64] of dims->dtype, device).
  *   dy         -- [batch, n_q_heads, T, 64] fp32 (device).
  *   params_dev -- the blob oal_state_init uploaded.
+ *   state_in   -- [batch, n_kv_heads] state blocks (oal_state_bytes(dims) bytes, device) that
+ *                 the forward call started from, or NULL for an empty prefix.
  *   workspace  -- oal_prefill_backward_workspace_bytes(dims, T, chunk) bytes of device scratch
  *                 (per-chunk states, one block of OAL_STATE_STRIDE floats per sequence, KV
  *                 head and chunk; the per-query readout gradients; partial dq, key and
  *                 coefficient gradients); contents on entry do not matter.
  * All arithmetic is fp32 whatever dims->dtype is (bf16 inputs are widened on load). Every
- * pointer but dL and deps must be 16-byte aligned (OAL_E_ALIGN). More than 65535 chunks per sequence,
+ * pointer but dL and deps must be 16-byte aligned (OAL_E_ALIGN; state_in and dstate_in when
+ * given). T = 0 writes nothing. More than 65535 chunks per sequence,
  * n_q_heads + 3 n_kv_heads > 65535 or n_kv_heads > 8191 give OAL_E_UNSUPPORTED (grid limits). */
 size_t oal_prefill_backward_workspace_bytes(const oal_dims *dims, int32_t T, int32_t chunk);
 oal_status oal_prefill_backward(const oal_dims *dims, int32_t T, int32_t chunk, const void *q,
                                 const void *k, const void *v, const float *dy,
-                                const void *params_dev, void *workspace, size_t workspace_bytes,
-                                float *dq, float *dk,
-                                float *dv, float *dL, float *deps, hipStream_t stream);
+                                const void *params_dev, const float *state_in, void *workspace,
+                                size_t workspace_bytes, float *dq, float *dk, float *dv,
+                                float *dstate_in, float *dL, float *deps, hipStream_t stream);
 
 /* Decode step for sequences whose states live in a pool (serving: a batch of active
  * sequences over a larger set of state blocks). Sequence b of the batch uses pool block

@@ -219,3 +219,74 @@ def test_backward_empty_and_validation():
     gpq.oal_prefill_backward(dims, 0, 64, x, x, x, x, ws, ws, x, x, x)
     with pytest.raises(gpq.OALError, match="OAL_E_UNSUPPORTED"):
         gpq.oal_prefill_backward(dims, 10, 32, x, x, x, x, ws, ws, x, x, x)
+
+
+def _to_state_buffer(S):
+    """[B, Hkv, 2145, 65] states (the oracle's layout) -> the library's state buffer (fp32):
+    per block the [2145, 64] v part, then column 64, then zero padding."""
+    B, Hkv = S.shape[:2]
+    blk = np.zeros((B, Hkv, gpq.STATE_STRIDE), np.float32)
+    blk[..., : 2145 * 64] = S[..., :64].reshape(B, Hkv, -1)
+    blk[..., 2145 * 64: 2145 * 65] = S[..., 64]
+    return torch.from_numpy(blk.reshape(-1)).cuda()
+
+
+def _psi_pairs():
+    """(a, b) of the quadratic state rows 65.. (a <= b, row-major upper triangle)."""
+    return np.array([(a, b) for a in range(64) for b in range(a, 64)], np.int64)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("chunk", [64, 128])
+def test_backward_from_a_prefix_state(dtype, chunk):
+    """Backward of a prefill that continues from the state of a prefix (the state built by the
+    oracle from the prefix tokens). Reference: the oracle's dense backward over prefix + new
+    tokens with dy = 0 on the prefix rows. dq, dk, dv of the new tokens and dL, deps match it;
+    the incoming-state gradient dS0 must give, by the chain rule through
+    S0 = sum_j psi(k_j) [v_j; 1]^T, the oracle's dv_j = (psi(k_j)^T dS0)[0:64] and
+    dk_j = Jpsi(k_j)^T (dS0 [v_j; 1]) of every prefix token j."""
+    T0, T1 = 150, 200
+    full = small(61, 2, 4, 2, T0 + T1, dtype=dtype)
+    B, Hq, Hkv = 2, 4, 2
+    qp, kp, vp = (x[:, :, :T0] for x in (full.q, full.k, full.v))
+    qn, kn, vn = (np.ascontiguousarray(x[:, :, T0:]) for x in (full.q, full.k, full.v))
+    S0 = oracle.state(kp, vp)                                   # [B, Hkv, 2145, 65], fp64
+    dims = gpq.make_dims(B, Hq, Hkv, dtype)
+    params = torch.empty(max(gpq.oal_params_bytes(dims), 16), dtype=torch.uint8, device="cuda")
+    gpq.oal_state_init(dims, gpq.HeadParamsC.from_params(full.params), params, None)
+    state_in = _to_state_buffer(S0)
+    q, k, v = (to_dev(x, dtype) for x in (qn, kn, vn))
+    dy = np.random.default_rng(62).normal(0.0, 1.0, (B, Hq, T1, 64)).astype(np.float32)
+    ws = torch.empty(gpq.oal_prefill_backward_workspace_bytes(dims, T1, chunk), dtype=torch.uint8, device="cuda")
+    dq = torch.full((B, Hq, T1, 64), np.nan, dtype=torch.float32, device="cuda")
+    dk = torch.full((B, Hkv, T1, 64), np.nan, dtype=torch.float32, device="cuda")
+    dv = torch.full_like(dk, np.nan)
+    dL = torch.full((Hq, 65, 65), np.nan, dtype=torch.float32, device="cuda")
+    deps = torch.full((Hq,), np.nan, dtype=torch.float32, device="cuda")
+    dS0 = torch.zeros_like(state_in)
+    gpq.oal_prefill_backward(dims, T1, chunk, q, k, v, torch.from_numpy(dy).cuda(), params, ws, dq, dk, dv,
+                             dL, deps, state_in=state_in, dstate_in=dS0)
+    torch.cuda.synchronize()
+    dy_full = np.concatenate([np.zeros((B, Hq, T0, 64), np.float32), dy], axis=2)
+    rq, rk, rv, rL, reps = oracle.backward(full.q, full.k, full.v, full.params, dy_full)
+    e = (slice_err(dq.cpu().numpy(), rq[:, :, T0:]), slice_err(dk.cpu().numpy(), rk[:, :, T0:]),
+         slice_err(dv.cpu().numpy(), rv[:, :, T0:]))
+    ec = coef_err(dL.cpu().numpy(), deps.cpu().numpy(), rL, reps)
+    # chain rule for the prefix tokens
+    G = gpq.state_view(dS0, B, Hkv).cpu().numpy().astype(np.float64)   # [B, Hkv, 2145, 65]
+    pr = _psi_pairs()
+    kp64, vp64 = np.asarray(kp, np.float64), np.asarray(vp, np.float64)
+    psi = np.concatenate([np.ones(kp64.shape[:3] + (1,)), kp64, kp64[..., pr[:, 0]] * kp64[..., pr[:, 1]]], -1)
+    pv = np.einsum("bhjf,bhfc->bhjc", psi, G[..., :64])              # predicted dv of prefix tokens
+    w = np.einsum("bhfc,bhjc->bhjf", G[..., :64], vp64) + G[..., 64][:, :, None, :]
+    pk = w[..., 1:65].copy()                                          # linear rows: d k_r / d k_r = 1
+    wq = w[..., 65:]                                                  # pair rows: d (k_a k_b)
+    for f, (a, b) in enumerate(pr):
+        pk[..., a] += wq[..., f] * kp64[..., b]
+        pk[..., b] += wq[..., f] * kp64[..., a]
+    es = (slice_err(pv, rv[:, :, :T0]), slice_err(pk, rk[:, :, :T0]))
+    print(f"[parity] backward from a {T0}-token prefix state, {T1} tokens C={chunk} {dtype}: "
+          f"dq={e[0]:.2e} dk={e[1]:.2e} dv={e[2]:.2e} dL,deps={ec:.2e} dS0->dv={es[0]:.2e} dS0->dk={es[1]:.2e}",
+          flush=True)
+    assert max(e) <= BWD_TOL and ec <= COEF_TOL
+    assert max(es) <= BWD_TOL
