@@ -477,6 +477,55 @@ constexpr int kIntraLzr = 8;          // Lz rows m < 8 staged in LDS ...
 constexpr int kIntraLzHeads = 16;     // ... for the first 16 query heads of a KV head
 constexpr int kFragFloats = 5 * 4 * 64;   // one 16 x 80 accumulator tile, fragment order
 
+// The intra-chunk tile of one (head, 16-query tile), unnormalised, in accumulator-fragment
+// order, written by the intra part and added by the readout. Stored in the input dtype: for
+// bf16 inputs as bf16 pairs (values ii = 0,1 and 2,3 of a lane's column tile in one 32-bit
+// word: ten 4-byte stores per lane), one rounding of at most 2^-9 of each value; for fp32
+// inputs as fp32.
+template <typename T> struct IntraTile;
+template <> struct IntraTile<float> {
+    static constexpr size_t kElems = kFragFloats;
+    __device__ static void store(float *up, int lane, const oal_f32x4 (&acc)[5]) {
+#pragma unroll
+        for (int n = 0; n < 5; ++n)
+#pragma unroll
+            for (int ii = 0; ii < 4; ++ii) up[(n * 4 + ii) * 64 + lane] = acc[n][ii];
+    }
+    __device__ static void load(const float *up, int lane, float (&x)[5][4]) {
+#pragma unroll
+        for (int n = 0; n < 5; ++n)
+#pragma unroll
+            for (int ii = 0; ii < 4; ++ii) x[n][ii] = up[(n * 4 + ii) * 64 + lane];
+    }
+};
+template <> struct IntraTile<__bf16> {
+    static constexpr size_t kElems = kFragFloats;
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    __device__ static void store(__bf16 *up, int lane, const oal_f32x4 (&acc)[5]) {
+        bf16x2 *w = reinterpret_cast<bf16x2 *>(up);
+#pragma unroll
+        for (int n = 0; n < 5; ++n)
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                bf16x2 pr;
+                pr[0] = (__bf16)acc[n][2 * h];
+                pr[1] = (__bf16)acc[n][2 * h + 1];
+                w[(n * 2 + h) * 64 + lane] = pr;
+            }
+    }
+    __device__ static void load(const __bf16 *up, int lane, float (&x)[5][4]) {
+        const bf16x2 *w = reinterpret_cast<const bf16x2 *>(up);
+#pragma unroll
+        for (int n = 0; n < 5; ++n)
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const bf16x2 pr = w[(n * 2 + h) * 64 + lane];
+                x[n][2 * h] = (float)pr[0];
+                x[n][2 * h + 1] = (float)pr[1];
+            }
+    }
+};
+
 template <typename T, int C> struct IntraLayout {
     static constexpr int EPU = 16 / (int)sizeof(T);
     static constexpr int QS = OAL_D + EPU;      // key row in LDS (16-byte aligned)
@@ -505,7 +554,7 @@ __device__ __forceinline__ void intra_block(int Lb, int T_len, OalSeqLayout sl, 
                                             int n_kv_heads, int nchunks, int n_bkv,
                                             const T *__restrict__ q, const T *__restrict__ k,
                                             const T *__restrict__ v, const unsigned char *__restrict__ params,
-                                            float *__restrict__ uintra) {
+                                            T *__restrict__ uintra) {
     using Lay = IntraLayout<T, C>;
     constexpr int EPU = Lay::EPU, QS = Lay::QS, LDV = Lay::LDV;
     constexpr int NQT = C / 16;
@@ -697,11 +746,8 @@ __device__ __forceinline__ void intra_block(int Lb, int T_len, OalSeqLayout sl, 
             }
             acc[4] = oal_mma(a, lr == 0 ? ones : zeros, acc[4]);
         }
-        float *up = uintra + (((size_t)b * n_q_heads + h0 + i) * ntiles + c * NQT + qt) * kFragFloats + lane;
-#pragma unroll
-        for (int n = 0; n < 5; ++n)
-#pragma unroll
-            for (int ii = 0; ii < 4; ++ii) up[(n * 4 + ii) * 64] = acc[n][ii];
+        IntraTile<T>::store(uintra + (((size_t)b * n_q_heads + h0 + i) * ntiles + c * NQT + qt) * kFragFloats,
+                            lane, acc);
     };
     static_assert((NQT == 1 || NQT % 2 == 0) && NQT <= 16, "tile pairs");
     for (int i = wave; i < n_rep; i += kIntraWaves) {
@@ -750,7 +796,7 @@ __global__ __launch_bounds__(64 * kIntraWaves) __attribute__((amdgpu_waves_per_e
     int T_len, OalSeqLayout sl, int n_q_heads, int n_kv_heads, int nchunks, int n_bkv, int n_delta,
     const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ v,
     const unsigned char *__restrict__ params, const float *__restrict__ state, T *__restrict__ delta,
-    float *__restrict__ tinit, float *__restrict__ uintra) {
+    float *__restrict__ tinit, T *__restrict__ uintra) {
     static_assert(kScanWaves == kIntraWaves, "one workgroup shape for both parts");
     const int n_intra = (int)gridDim.x - n_delta;
     const int id = blockIdx.x;
@@ -801,7 +847,7 @@ template <typename T, int C, int R>
 __global__ __launch_bounds__(256, 2) void oal_readout(
     int T_len, OalSeqLayout sl, int n_q_heads, int n_kv_heads, int nchunks, int n_hgroups, int nunits, int warm,
     const T *__restrict__ q, const unsigned char *__restrict__ params,
-    const unsigned char *__restrict__ snap, const float *__restrict__ uintra, float *__restrict__ y) {
+    const unsigned char *__restrict__ snap, const T *__restrict__ uintra, float *__restrict__ y) {
     using Lay = ReadoutLayout<T, C, R>;
     constexpr int EPU = Lay::EPU, QS = Lay::QS, PS = Lay::PS, RW = Lay::RW, NT = Lay::NT;
     constexpr int NQT = C / 16;
@@ -1083,11 +1129,12 @@ __global__ __launch_bounds__(256, 2) void oal_readout(
     for (int li = 0; li < RW; ++li) {
         if (li >= nh || (li & 1) != par) continue;
         const int i = hb + li;
-        const float *up = uintra + (((size_t)b * n_q_heads + h0 + i) * ntiles + c * NQT + qt) * kFragFloats + lane;
+        float xu[5][4];
+        IntraTile<T>::load(uintra + (((size_t)b * n_q_heads + h0 + i) * ntiles + c * NQT + qt) * kFragFloats, lane, xu);
 #pragma unroll
         for (int n = 0; n < 5; ++n)
 #pragma unroll
-            for (int ii = 0; ii < 4; ++ii) acc[li][n][ii] += s_x[((i * 5 + n) * 4 + ii) * 64 + lane] + up[(n * 4 + ii) * 64];
+            for (int ii = 0; ii < 4; ++ii) acc[li][n][ii] += s_x[((i * 5 + n) * 4 + ii) * 64 + lane] + xu[n][ii];
         float *yh = y + sl.row0(b, h0 + i, n_q_heads, T_len) * OAL_D;
 #pragma unroll
         for (int ii = 0; ii < 4; ++ii) {
@@ -1125,7 +1172,7 @@ PrefillPlan make_plan(const oal_dims &d, int T_len, int C) {
     p.snap_bytes = r256(bkv * p.nchunks * OAL_SNAP_KSTEPS * (size_t)snap_kstep_bytes<T>());
     p.delta_bytes = r256(bkv * p.nchunks * OAL_SNAP_KSTEPS * (size_t)kDeltaStep * sizeof(T));
     p.tinit_bytes = r256(bkv * OAL_TAIL_STEPS * (size_t)kDeltaStep * sizeof(float));
-    p.uintra_bytes = r256((size_t)d.batch * d.n_q_heads * (p.Tpad / 16) * (size_t)kFragFloats * sizeof(float));
+    p.uintra_bytes = r256((size_t)d.batch * d.n_q_heads * (p.Tpad / 16) * (size_t)kFragFloats * sizeof(T));
     return p;
 }
 
@@ -1153,7 +1200,7 @@ hipError_t ensure_lds_limit(K kern, size_t lds, std::atomic<int> (&set_bytes)[kM
 
 template <typename T, int C, int R>
 hipError_t launch_readout(const oal_dims &d, int T_len, OalSeqLayout sl, const PrefillPlan &p, const void *q,
-                          const void *params, const unsigned char *snap, const float *uintra, float *y,
+                          const void *params, const unsigned char *snap, const T *uintra, float *y,
                           hipStream_t stream) {
     int n_rep = d.n_q_heads / d.n_kv_heads;
     int n_hg = n_rep / R;
@@ -1182,7 +1229,7 @@ hipError_t launch_all(const oal_dims &d, int T_len, OalSeqLayout sl, const void 
     unsigned char *snap = reinterpret_cast<unsigned char *>(ws);
     T *delta = reinterpret_cast<T *>(snap + p.snap_bytes);
     float *tinit = reinterpret_cast<float *>(snap + p.snap_bytes + p.delta_bytes);
-    float *uintra = reinterpret_cast<float *>(snap + p.snap_bytes + p.delta_bytes + p.tinit_bytes);
+    T *uintra = reinterpret_cast<T *>(snap + p.snap_bytes + p.delta_bytes + p.tinit_bytes);
     const int bkv = d.batch * d.n_kv_heads;
     const unsigned char *pb = reinterpret_cast<const unsigned char *>(params);
     hipError_t e;
