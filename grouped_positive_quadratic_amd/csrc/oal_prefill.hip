@@ -1021,13 +1021,27 @@ __global__ __launch_bounds__(256, 2) void oal_readout(
             gen_mul(li, rq, phi);
             a.set(phi);
         };
-        auto main_step = [&](const OalFrag<T> (&bc)[5]) {
-            const int rq = 2 * j + par;
-            const int r = 4 * rq + g;
-            if (j == 0) load_pt();
-            float prv[NH];
+        // bf16: p_r of the next main K-step (and p_t of its t block) are read from LDS at the
+        // end of the step before, so the step finds them in registers (readout 33.8 -> 33.2 us
+        // at B = 1 x 4096); fp32 reads them at the start of the step (the early copies would
+        // not fit its registers)
+        constexpr bool kAhead = sizeof(T) == 2;
+        float prv[NH];
+        auto load_prv = [&]() {
+            const int r = 4 * (2 * j + par) + g;
 #pragma unroll
             for (int li = 0; li < NH; ++li) prv[li] = s_p[((hb + li) * 16 + lr) * PS + r];
+        };
+        if (kAhead) {
+            load_pt();
+            load_prv();
+        }
+        auto main_step = [&](const OalFrag<T> (&bc)[5]) {
+            const int rq = 2 * j + par;
+            if (!kAhead) {
+                if (j == 0) load_pt();
+                load_prv();
+            }
             // the next head's operand is formed while this head's MFMAs run (two buffers;
             // bf16: the scheduler is told to alternate one MFMA with three VALU ops)
             OalFrag<T> a[2];
@@ -1048,7 +1062,12 @@ __global__ __launch_bounds__(256, 2) void oal_readout(
                     }
                 }
             }
-            if (++j > tb) { ++tb; j = 0; }
+            if (++j > tb) {
+                ++tb;
+                j = 0;
+                if (kAhead && tb < 8) load_pt();
+            }
+            if (kAhead && tb < 8) load_prv();
         };
         // tail K-step x: slot jj = 32 x + 8 g + e carries entry (ra[jj], rb[jj]); head li adds
         // tail[jj] q_ra q_rb with q_64 = 1 (zero past the KV head's entries)
