@@ -20,28 +20,33 @@
 //   dkappa/dq_r = 2 k_r sum_m z_m Lz[m][r]        (and the same with q and k exchanged);
 // for a (query tile, key tile) pair each z-term is the product (Q o Lz[m]) K^T on MFMA.
 //
-// Every kernel computes in fp32 (inputs of either dtype are widened on load). The state
-// contractions and the products over the pairs inside a chunk run on fp32 MFMA
-// (v_mfma_f32_16x16x4_f32), except dv's state part, which runs on the VALU with the state row
-// read at a wave-uniform address through the constant address space, so that it arrives in
-// scalar registers and feeds the FMAs directly. With packed fp32 off, the VALU bound is the
-// non-packed FMA rate (256 CUs x 4 SIMDs x 16 lanes x 2 flops x 2.4 GHz = 78.6 TFLOP/s); fp32
-// MFMA reaches 157.3.
+// Every kernel computes to fp32 accuracy (inputs of either dtype are widened on load). The
+// state contractions of the readout (u) and of dq and dk run on bf16 MFMA
+// (v_mfma_f32_16x16x32_bf16) with every fp32 operand split in three bf16 parts and six
+// products per fp32 product (split3 below); the increments and the products over the pairs
+// inside a chunk run on fp32 MFMA (v_mfma_f32_16x16x4_f32); dv's state part runs on the VALU
+// with the state row read at a wave-uniform address through the constant address space, so
+// that it arrives in scalar registers and feeds the FMAs directly. With packed fp32 off, the
+// VALU bound is the non-packed FMA rate (256 CUs x 4 SIMDs x 16 lanes x 2 flops x 2.4 GHz =
+// 78.6 TFLOP/s); fp32 MFMA reaches 157.3, bf16 MFMA 2500 (about 417 for the six-term fp32
+// products).
 //
 // Launch order (all on the caller's stream):
 //   1. oal_bwd_increments<keys>:    per chunk psi(K_c)^T [V_c; 1]           -> workspace states
 //   2. oal_bwd_scan (forward):      exclusive prefix over chunks: S_c
 //   3. oal_bwd_readout_g:           u_i (inter + intra), y, den -> g_i     -> workspace g
-//   4. oal_bwd_dq_inter_mfma, oal_bwd_dq_intra_mfma: dq (state part, then the pairs inside
-//      the chunk)
+//   4. oal_bwd_dstate_x6, oal_bwd_dq_intra_mfma: dq (state part, then the pairs inside the
+//      chunk)
 //   5. oal_bwd_dkv_intra_mfma:      dk, dv partials of the pairs inside the chunk
 //   6. oal_bwd_increments<queries>: per chunk sum_h phi_h(Q_c)^T G_c       -> workspace states
 //   7. oal_bwd_scan (reverse):      exclusive suffix over chunks: R_c
-//   8. oal_bwd_dq_inter_mfma<keys>, oal_bwd_dv_inter: dk, dv partials of the state part
+//   8. oal_bwd_dstate_x6<keys>, oal_bwd_dv_inter: dk, dv partials of the state part
 //   9. oal_bwd_kv_reduce:           dk, dv (the partials added in a fixed order)
 // With coefficient gradients, also oal_bwd_dw_intra (before 6), the per-head partials of 6,
 // and oal_bwd_dw_sum, oal_bwd_coef (after 6): dL, deps.
 #include <hip/hip_runtime.h>
+
+#include <type_traits>
 
 #include "oal_device.h"
 #include "oal_internal.h"
@@ -326,20 +331,47 @@ __global__ __launch_bounds__(kThreads) void oal_bwd_scan(int nch, int reverse, f
     if (total) total[(size_t)blockIdx.y * OAL_STATE_STRIDE + e] = run;
 }
 
+constexpr int kXcds = 8;                       // MI355X: workgroups go round-robin to 8 XCDs
+
+// Workgroup coordinates renumbered so that each XCD takes a contiguous range of the work
+// items, blockIdx.y varying fastest: the workgroups that read the same state (the query heads
+// of a KV head, the splits of a key tile) run on one XCD at about the same time and share its
+// L2. Falls back to the plain numbering when the grid does not divide by the XCD count.
+__device__ inline void xcd_order(int &x, int &y, int &z) {
+    const int gx = gridDim.x, gy = gridDim.y, n = gx * gy * gridDim.z;
+    const int id = blockIdx.x + gx * (blockIdx.y + gy * blockIdx.z);
+    int item = n % kXcds == 0 ? (id % kXcds) * (n / kXcds) + id / kXcds : id;
+    y = item % gy;
+    item /= gy;
+    x = item % gx;
+    z = item / gx;
+}
+
+// fp32 x = x0 + x1 + x2 (+ a remainder below 2^-24 |x|) in bf16 parts, each difference exact in
+// fp32: x0 = bf16(x), x1 = bf16(x - x0), x2 = bf16(x - x0 - x1). A product x y is taken as the
+// six terms x_i y_j with i + j <= 2 (Henry, Tang and Heinecke, "Leveraging the bfloat16
+// artificial intelligence datatype for higher-precision computations", 2019: the "bf16x6"
+// product); the dropped terms are below about 2^-22 |x y|, and each 16x16x32 bf16 MFMA is exact
+// in its products and accumulates in fp32.
+__device__ inline void split3(float x, __bf16 &x0, __bf16 &x1, __bf16 &x2) {
+    x0 = (__bf16)x;
+    const float r = x - (float)x0;
+    x1 = (__bf16)r;
+    x2 = (__bf16)(r - (float)x1);
+}
+
+typedef __bf16 oal_bf16x4 __attribute__((ext_vector_type(4)));
+
 // Keys of the chunk that query lane i of tile qt sees, tile kt: all of an earlier tile, up to
 // and including its own position in its own tile.
 __device__ inline bool sees(int kt, int qt, int jj, int i) { return kt < qt || jj <= i; }
 
 // 3. u_i = phi_h(q_i) . S_c + sum_{j <= i in the chunk} kappa_ij [v_j; 1]; y = u[0:64] / u[64];
 //    g_i = (dy_i / den, -(dy_i . y_i) / den). Workgroup = (64-query tile, head, sequence).
-//    State part on fp32 MFMA (v_mfma_f32_16x16x4_f32): U = phi(Q) S_c, wave w computing the
-//    queries 16 w .. 16 w + 15 against 80 columns (five 16 x 16 tiles; the fifth holds the
-//    column 64 of S_c, the normaliser) with K over the features in blocks of 64, each block
-//    of S_c staged once in LDS (row stride 80: the four K rows of an operand read fall on two
-//    bank halves). A operand: lane l holds phi_f(q) of query l % 16 and feature
-//    f = 4 K-step + l / 16, built from the query tile, the head's coefficients and the dims of
-//    f (LDS tables); B operand: S_c[f][col], col = 16 tile + l % 16. The result goes to an LDS
-//    tile. Pairs inside the chunk: lane = query, the four waves split the keys.
+//    State part U = phi(Q) S_c on split-bf16 MFMA (below), wave w computing the queries
+//    16 w .. 16 w + 15 against the 64 value columns, K over the features in blocks of 64, each
+//    block of S_c split and staged once in LDS; the normaliser column on the VALU. Pairs
+//    inside the chunk on fp32 MFMA: lane = query, the four waves split the keys.
 template <typename T>
 __global__ __launch_bounds__(kThreads) void oal_bwd_readout_g(int s0, int T_len, int C, int nch, int n_q_heads,
                                                                int n_kv_heads, const T *__restrict__ q,
@@ -350,10 +382,13 @@ __global__ __launch_bounds__(kThreads) void oal_bwd_readout_g(int s0, int T_len,
                                                                float *__restrict__ gd) {
     __shared__ float xq[64 * 65];
     __shared__ __align__(16) float ks[64 * 68];    // keys; before them the coefficient tables
-    __shared__ __align__(16) float vs[64 * 80];    // values; before them a block of S_c (stride 80)
-    __shared__ __align__(16) float uin[64 * 68];   // state part of u per query
-    const int tpc = C / 64, c = blockIdx.x / tpc, qt = blockIdx.x % tpc;
-    const int h = blockIdx.y, b = blockIdx.z, n_rep = n_q_heads / n_kv_heads, kv = h / n_rep;
+    // values (vs) and kappa / u (uin); before them the split block of S_c across both
+    __shared__ __align__(16) float vu[64 * 80 + 64 * 68];
+    float *const vs = vu, *const uin = vu + 64 * 80;
+    int bx, by, bz;
+    xcd_order(bx, by, bz);
+    const int tpc = C / 64, c = bx / tpc, qt = bx % tpc;
+    const int h = by, b = bz, n_rep = n_q_heads / n_kv_heads, kv = h / n_rep;
     const int i = threadIdx.x & 63, w = wave_id();
     const int t0 = c * C + qt * 64, t = t0 + i;
     const bool valid = t < T_len;
@@ -382,57 +417,107 @@ __global__ __launch_bounds__(kThreads) void oal_bwd_readout_g(int s0, int T_len,
     const int lr = threadIdx.x & 15, kg = (threadIdx.x >> 4) & 3;       // MFMA lane roles
     const float *xa = xq + (16 * w + lr) * 65;                         // A row: query 16 w + lr
     oal_f32x4 D[5];                                 // u: query 16 w + 4 kg + j, column 16 ct + lr
-    {
-        oal_f32x4 E[5];                             // even and odd K-steps: independent chains
 #pragma unroll
-        for (int ct = 0; ct < 5; ++ct) D[ct] = E[ct] = oal_splat(0.0f);
-        if (c > 0 || s0) {                         // S_0 = 0 without an incoming state
-            const float *S = st + ((size_t)((size_t)b * n_kv_heads + kv) * nch + c) * OAL_STATE_STRIDE;
-            const float *Sd = S + (size_t)OAL_NFEAT * OAL_D;
-            float *sblk = vs;
-            // block f0 .. f0 + 63 of S_c: thread's share (4 float4 of the 64 columns, one
-            // normaliser entry), loaded into registers one block ahead of its use
-            float4 pre[4];
-            float pre64 = 0.0f;
-            auto load_block = [&](int f0) {
+    for (int ct = 0; ct < 5; ++ct) D[ct] = oal_splat(0.0f);
+    if (c > 0 || s0) {                             // S_0 = 0 without an incoming state
+        // U = phi(Q) S_c on bf16 MFMA (16x16x32) with both operands split in three parts (the six
+        // products of split3): K = the features in blocks of 64 (two K-steps), N = the 64 value
+        // columns in four tiles; the normaliser column 64 on the VALU. A operand: lane (lr, kg)
+        // holds phi_f(q) of query 16 w + lr for the features 32 ks + 8 kg + e of the block,
+        // formed and split in registers. B operand: the block of S_c staged in LDS transposed,
+        // plane row = value column, 64 features (stride PS), so that a lane's 8 features are one
+        // 16-byte read.
+        constexpr int PS = 72;
+        __bf16 *pb = reinterpret_cast<__bf16 *>(vs);              // 3 planes x 64 columns x PS
+        float *sdb = vs + 3 * 64 * PS / 2;                         // column 64 of the block
+        const float *S = st + ((size_t)((size_t)b * n_kv_heads + kv) * nch + c) * OAL_STATE_STRIDE;
+        const float *Sd = S + (size_t)OAL_NFEAT * OAL_D;
+        // staging share: features sf + u (u < 4), columns sc + j (j < 4)
+        const int sf = 4 * (threadIdx.x & 15), sc = 4 * (threadIdx.x >> 4);
+        float4 pre[4];
+        float pre64 = 0.0f;
+        auto load_block = [&](int f0) {
 #pragma unroll
-                for (int m = 0; m < 4; ++m) {
-                    const int e = threadIdx.x + kThreads * m, kk = e >> 4, c4 = (e & 15) * 4, f = f0 + kk;
-                    pre[m] = f < OAL_NFEAT ? *reinterpret_cast<const float4 *>(S + (size_t)f * OAL_D + c4)
-                                           : make_float4(0, 0, 0, 0);
+            for (int u = 0; u < 4; ++u) {
+                const int f = f0 + sf + u;
+                pre[u] = f < OAL_NFEAT ? *reinterpret_cast<const float4 *>(S + (size_t)f * OAL_D + sc)
+                                       : make_float4(0, 0, 0, 0);
+            }
+            if (threadIdx.x < 64) pre64 = f0 + (int)threadIdx.x < OAL_NFEAT ? Sd[f0 + threadIdx.x] : 0.0f;
+        };
+        float dpart = 0.0f;                        // normaliser of query 16 w + lr, the lane's features
+        load_block(0);
+        for (int f0 = 0; f0 < NFP; f0 += 64) {
+            __syncthreads();                       // the previous block is consumed
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                oal_bf16x4 p0, p1, p2;
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    const float x = j == 0 ? pre[u].x : j == 1 ? pre[u].y : j == 2 ? pre[u].z : pre[u].w;
+                    __bf16 x0, x1, x2;
+                    split3(x, x0, x1, x2);
+                    p0[u] = x0;
+                    p1[u] = x1;
+                    p2[u] = x2;
                 }
-                if (threadIdx.x < 64) pre64 = f0 + (int)threadIdx.x < OAL_NFEAT ? Sd[f0 + threadIdx.x] : 0.0f;
-            };
-            load_block(0);
-            for (int f0 = 0; f0 < NFP; f0 += 64) {
-                __syncthreads();                   // the previous block is consumed
+                const int o = (sc + j) * PS + sf;
+                *reinterpret_cast<oal_bf16x4 *>(pb + o) = p0;
+                *reinterpret_cast<oal_bf16x4 *>(pb + 64 * PS + o) = p1;
+                *reinterpret_cast<oal_bf16x4 *>(pb + 2 * 64 * PS + o) = p2;
+            }
+            if (threadIdx.x < 64) sdb[threadIdx.x] = pre64;
+            __syncthreads();
+            if (f0 + 64 < NFP) load_block(f0 + 64);
+            oal_pin_loads();
 #pragma unroll
-                for (int m = 0; m < 4; ++m) {
-                    const int e = threadIdx.x + kThreads * m, kk = e >> 4, c4 = (e & 15) * 4;
-                    *reinterpret_cast<float4 *>(sblk + kk * 80 + c4) = pre[m];
-                }
-                if (threadIdx.x < 64) sblk[threadIdx.x * 80 + 64] = pre64;
-                __syncthreads();
-                if (f0 + 64 < NFP) load_block(f0 + 64);
-#pragma unroll 2
-                for (int kst = 0; kst < 16; kst += 2) {
-                    const int kk = 4 * kst + kg, f = f0 + kk;
-                    const unsigned short ab = fdl[f], ab2 = fdl[f + 4];
-                    const float a = wdl[f] * xa[ab & 0xff] * xa[ab >> 8];
-                    const float a2 = wdl[f + 4] * xa[ab2 & 0xff] * xa[ab2 >> 8];
-                    const float *brow = sblk + kk * 80, *brow2 = brow + 4 * 80;
+            for (int ks = 0; ks < 2; ++ks) {
+                const int fl = 32 * ks + 8 * kg;   // the lane's first feature in the block
+                oal_bf16x8 a0, a1, a2;
 #pragma unroll
-                    for (int ct = 0; ct < 4; ++ct) {
-                        D[ct] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, brow[16 * ct + lr], D[ct], 0, 0, 0);
-                        E[ct] = __builtin_amdgcn_mfma_f32_16x16x4f32(a2, brow2[16 * ct + lr], E[ct], 0, 0, 0);
-                    }
-                    D[4] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, lr == 0 ? brow[64] : 0.0f, D[4], 0, 0, 0);
-                    E[4] = __builtin_amdgcn_mfma_f32_16x16x4f32(a2, lr == 0 ? brow2[64] : 0.0f, E[4], 0, 0, 0);
+                for (int e = 0; e < 8; ++e) {
+                    const int f = f0 + fl + e;
+                    const unsigned short ab = fdl[f];
+                    const float ph = wdl[f] * xa[ab & 0xff] * xa[ab >> 8];
+                    dpart += ph * sdb[fl + e];
+                    __bf16 x0, x1, x2;
+                    split3(ph, x0, x1, x2);
+                    a0[e] = x0;
+                    a1[e] = x1;
+                    a2[e] = x2;
                 }
+                oal_bf16x8 b0[4], b1[4], b2[4];
+#pragma unroll
+                for (int ct = 0; ct < 4; ++ct) {
+                    const int o = (16 * ct + lr) * PS + fl;
+                    b0[ct] = *reinterpret_cast<const oal_bf16x8 *>(pb + o);
+                    b1[ct] = *reinterpret_cast<const oal_bf16x8 *>(pb + 64 * PS + o);
+                    b2[ct] = *reinterpret_cast<const oal_bf16x8 *>(pb + 2 * 64 * PS + o);
+                }
+                // small terms first
+#pragma unroll
+                for (int ct = 0; ct < 4; ++ct) D[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, b1[ct], D[ct], 0, 0, 0);
+#pragma unroll
+                for (int ct = 0; ct < 4; ++ct) D[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a2, b0[ct], D[ct], 0, 0, 0);
+#pragma unroll
+                for (int ct = 0; ct < 4; ++ct) D[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, b2[ct], D[ct], 0, 0, 0);
+#pragma unroll
+                for (int ct = 0; ct < 4; ++ct) D[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, b0[ct], D[ct], 0, 0, 0);
+#pragma unroll
+                for (int ct = 0; ct < 4; ++ct) D[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, b1[ct], D[ct], 0, 0, 0);
+#pragma unroll
+                for (int ct = 0; ct < 4; ++ct) D[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, b0[ct], D[ct], 0, 0, 0);
             }
         }
+        // the normaliser of query 16 w + lr summed over the four lanes kg, then moved to the
+        // accumulator layout of column 64: lane (0, kg) holds query 16 w + 4 kg + jj
+        dpart += __shfl_xor(dpart, 16);
+        dpart += __shfl_xor(dpart, 32);
 #pragma unroll
-        for (int ct = 0; ct < 5; ++ct) D[ct] += E[ct];
+        for (int jj = 0; jj < 4; ++jj) {
+            const float dj = __shfl(dpart, 4 * kg + jj);
+            D[4][jj] = lr == 0 ? dj : 0.0f;
+        }
     }
 
     // pairs inside the chunk (fp32 MFMA): per key tile and z-term m, Z_m = (Q o Lz[m]) K^T
@@ -520,131 +605,269 @@ __global__ __launch_bounds__(kThreads) void oal_bwd_readout_g(int s0, int T_len,
 }
 
 
-// 4a. dq_i = Jphi_h(q_i)^T (S_c g_i) (the state part) on fp32 MFMA. With c_st = wdec of the
-//     feature (min(s,t), max(s,t)), doubled for s = t (the square), dq_i[s] = wdec_{1+s}
-//     (S_c[1+s] . g_i) + sum_t c_st q_i[t] (S_c[(s,t)] . g_i): per t, X_t = G T_t^T with
-//     T_t[s] = S_c[pair(s, t)] (K = the 65 columns), then dq += c_st q_i[t] X_t; the linear
-//     features are one more step (T[s] = S_c[1 + s], q factor 1). Workgroup = (64-query tile,
-//     head, sequence); wave w owns the queries 16 w .. 16 w + 15 and all 64 dims. The A
-//     operand (g) stays in registers for every step; T_t is prefetched into registers one step
-//     ahead and staged in LDS.
-// State row of T_t[s] (the feature (min(s,t), max(s,t))); t = 64: the linear feature 1 + s.
-__device__ inline int dq_row_of(int s, int t) {
-    return t == OAL_D ? 1 + s : (s <= t ? quad_base(s) + t : quad_base(t) + s);
+// 4a. The state parts dq_i = Jphi_h(q_i)^T (S_c g_i) and (keys) dk_j = Jpsi(k_j)^T (R_c [v_j; 1])
+//     in one pass over the features, on bf16 MFMA with every fp32 operand split in three
+//     bf16 parts.
+//
+//     Products as six bf16 terms (split3). When the A operand is exact in bf16 (the keys'
+//     [v; 1] for bf16 inputs) only its first part is non-zero and three terms remain.
+//
+//     Work: W = G S^T over the 2145 features (K = the 64 value columns on MFMA, column 64 as a
+//     rank-1 update on the VALU), each feature visited once: feature (r, t), r <= t, adds
+//     c_f q[t] W_f to dq[r] and c_f q[r] W_f to dq[t] (c_f = wdec_h[f] for queries, 1 for keys;
+//     for r = t the two adds give the factor 2 of the square), a linear feature 1 + s adds
+//     c_f W_f to dq[s]. Features are taken in tiles of 16 along a row r of the triangle
+//     (t = 16 m .. 16 m + 15, lanes with t < r masked), two rows per stage: r = a and
+//     r = 63 - a, five tiles for every a in 0..31; stage 0 holds the 64 linear features.
+//     A stage's 80 state rows are staged in LDS once per workgroup as three bf16 planes and
+//     read by every wave as B operands. Wave w owns the queries (keys) 16 w .. 16 w + 15 and
+//     all 64 dims: lane l holds dq of query 16 w + 4 (l / 16) + jj, dim 16 m + l % 16; the
+//     dq[r] sums of a row are reduced over the 16 lanes of a row group at the end of the stage.
+//     Keys: the 33 stages are split over kDkSplits workgroups, each writing its own slot.
+
+// Sum over the 16 lanes of a DPP row, left in every lane of the row: row rotations by 8, 4,
+// 2 and 1 lanes (VALU data movement, no LDS round trip).
+__device__ inline float row16_sum(float x) {
+    x += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x128, 0xf, 0xf, false));
+    x += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x124, 0xf, 0xf, false));
+    x += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x122, 0xf, 0xf, false));
+    x += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x121, 0xf, 0xf, false));
+    return x;
 }
 
-//     KEYS: the same for dk_j = Jpsi(k_j)^T (R_c [v_j; 1]) -- psi has no coefficients (c_st = 1,
-//     2 for s = t, 1 for the linear features), the A operand is [v_j; 1], the rows come from R_c
-//     (zero for the last chunk); workgroup = (64-key tile, KV head x 4 splits of the t steps,
-//     sequence), each split's result going to the dk half of its partial slot.
 template <typename T, bool KEYS>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void oal_bwd_dq_inter_mfma(
-    int s0, int T_len, int C, int nch, int n_q_heads, int n_kv_heads, const T *__restrict__ q, const T *__restrict__ v,
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void oal_bwd_dstate_x6(
+    int s0, int T_len, int C, int nch, int n_q_heads, int n_kv_heads, const T *__restrict__ x, const T *__restrict__ v,
     const unsigned char *__restrict__ params, const float *__restrict__ st, const float *__restrict__ gv,
-    const float *__restrict__ gd, float *__restrict__ dq) {
-    __shared__ __align__(16) float xq[64 * 68];   // query tile
-    __shared__ __align__(16) float tb[64 * 68];   // T_t: row s, 65 columns, zero to 68
-    __shared__ float wdl[2176];                    // wdec of the head
-    const int tpc = C / 64, c = blockIdx.x / tpc, qt = blockIdx.x % tpc;
-    // keys: blockIdx.y = KV head x kDkSplits, split p taking the steps t = 16 p .. 16 p + 15 (p = 0
-    // also the linear step)
-    const int h = KEYS ? blockIdx.y / kDkSplits : blockIdx.y, b = blockIdx.z, n_rep = n_q_heads / n_kv_heads;
-    const int kv = KEYS ? h : h / n_rep, psplit = KEYS ? blockIdx.y % kDkSplits : 0;
-    const int tbeg = KEYS ? 16 * psplit : 0;
+    const float *__restrict__ gd, float *__restrict__ out) {
+    constexpr int NR = 80, PS = 72, NSTAGE = 33;   // rows per stage, plane row stride (bf16), stages
+    constexpr bool kAExact = KEYS && sizeof(T) == 2;
+    __shared__ __align__(16) __bf16 pl[3][NR * PS];
+    __shared__ float sdl[NR];                      // column 64 of the staged rows
+    __shared__ __align__(16) float xq[64 * 68];    // query (key) tile
+    __shared__ float wdl[KEYS ? 1 : 2176];         // wdec of the head
+    int bx, by, bz;
+    xcd_order(bx, by, bz);
+    const int tpc = C / 64, c = bx / tpc, qt = bx % tpc;
+    const int h = KEYS ? by / kDkSplits : by, b = bz, n_rep = n_q_heads / n_kv_heads;
+    const int kv = KEYS ? h : h / n_rep, psplit = KEYS ? by % kDkSplits : 0;
+    const int sbeg = KEYS ? NSTAGE * psplit / kDkSplits : 0;
+    const int send = KEYS ? NSTAGE * (psplit + 1) / kDkSplits : NSTAGE;
     const int tid = threadIdx.x, lane = tid & 63, lr = lane & 15, kg = lane >> 4, w = wave_id();
     const int t0 = c * C + qt * 64;
     if (t0 >= T_len) return;                       // a tile past the sequence (uniform)
-    const size_t qrow = KEYS ? ((size_t)b * n_kv_heads + kv) * T_len : ((size_t)b * n_q_heads + h) * T_len;
-    stage_rows(xq, 68, q, qrow, t0, T_len, 0.0f);
+    const size_t row0 = KEYS ? ((size_t)b * n_kv_heads + kv) * T_len : ((size_t)b * n_q_heads + h) * T_len;
+    stage_rows(xq, 68, x, row0, t0, T_len, 0.0f);
     if constexpr (!KEYS) {
         const OalHeadDev *hd = bwd_head(params, h);
         for (int f = tid; f < 2176; f += kThreads) wdl[f] = f < OAL_NFEAT ? hd->wdec[f] : 0.0f;
     }
-    float ga[17];                                  // g of query 16 w + lr, column 4 s + kg
-    {
-        const int ta = t0 + 16 * w + lr;
-        const bool ok = ta < T_len;
+    oal_f32x4 acc[4];                              // query 16 w + 4 kg + jj, dim 16 m + lr
 #pragma unroll
-        for (int ks = 0; ks < 17; ++ks) {
-            const int col = 4 * ks + kg;
-            if constexpr (KEYS)
-                ga[ks] = !ok ? 0.0f : col < 64 ? oal_ld(v + (qrow + ta) * OAL_D + col) : col == 64 ? 1.0f : 0.0f;
-            else
-                ga[ks] = !ok ? 0.0f : col < 64 ? gv[(qrow + ta) * OAL_D + col] : col == 64 ? gd[qrow + ta] : 0.0f;
-        }
-    }
-    oal_f32x4 acc[4];                              // dq: query 16 w + 4 kg + jj, dim 16 st + lr
-#pragma unroll
-    for (int sti = 0; sti < 4; ++sti) acc[sti] = oal_splat(0.0f);
+    for (int m = 0; m < 4; ++m) acc[m] = oal_splat(0.0f);
     if (KEYS ? c < nch - 1 : (c > 0 || s0)) {      // R of the last chunk = 0; S_0 = 0 without
                                                    // an incoming state
         const float *S = st + ((size_t)((size_t)b * n_kv_heads + kv) * nch + c) * OAL_STATE_STRIDE;
         const float *Sd = S + (size_t)OAL_NFEAT * OAL_D;
-        // T of the next step, this thread's share: rows s = (tid + 256 m) / 16, 4 columns each
-        const int s0 = tid >> 4, c4 = (tid & 15) * 4;
-        auto ld4 = [&](int srow, int t) {
-            return *reinterpret_cast<const float4 *>(S + (size_t)dq_row_of(srow, t) * OAL_D + c4);
+        // A operand: g (keys: [v; 1]) of row 16 w + lr, columns 32 ks + 8 kg + e, three parts
+        oal_bf16x8 ga[2][3];
+        float g64[4];
+        {
+            const int ta = t0 + 16 * w + lr;
+            const bool ok = ta < T_len;
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) {
+                float e8[8];
+                const size_t o = (row0 + ta) * OAL_D + 32 * ks + 8 * kg;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) e8[e] = 0.0f;
+                if (ok) {
+                    if constexpr (KEYS) {
+                        RowVec<T>::load(v + o, e8);
+                        if constexpr (RowVec<T>::N == 4) RowVec<T>::load(v + o + 4, e8 + 4);
+                    } else {
+                        RowVec<float>::load(gv + o, e8);
+                        RowVec<float>::load(gv + o + 4, e8 + 4);
+                    }
+                }
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    __bf16 x0, x1, x2;
+                    split3(e8[e], x0, x1, x2);
+                    ga[ks][0][e] = x0;
+                    ga[ks][1][e] = x1;
+                    ga[ks][2][e] = x2;
+                }
+            }
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) {
+                const int tq = t0 + 16 * w + 4 * kg + jj;
+                g64[jj] = tq < T_len ? (KEYS ? 1.0f : gd[row0 + tq]) : 0.0f;
+            }
+        }
+        __syncthreads();                           // xq staged
+        float qreg[4][4];                          // x[query 16 w + 4 kg + jj][16 m + lr]
+#pragma unroll
+        for (int m = 0; m < 4; ++m)
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) qreg[m][jj] = xq[(16 * w + 4 * kg + jj) * 68 + 16 * m + lr];
+        // first feature of tile i of stage s
+        auto tile_f0 = [](int s, int i) -> int {
+            if (s == 0) return 1 + 16 * (i & 3);
+            const int a = s - 1;
+            if (a < 16) return i < 4 ? quad_base(a) + 16 * i : quad_base(63 - a) + 48;
+            return i < 3 ? quad_base(a) + 16 * (i + 1) : quad_base(63 - a) + 16 * (i - 1);
         };
-        // queries: n = t (64 = the linear step); keys: t = 16 p + n, and n = 16 (split 0 only) the
-        // linear step
-        auto step_t = [&](int n) { return KEYS ? (n < 16 ? tbeg + n : OAL_D) : n; };
-        const int nsteps = KEYS ? (psplit == 0 ? 17 : 16) : OAL_D + 1;
-        float4 p0 = ld4(s0, step_t(0)), p1 = ld4(s0 + 16, step_t(0)), p2 = ld4(s0 + 32, step_t(0)),
-               p3 = ld4(s0 + 48, step_t(0));
-        float p64 = Sd[dq_row_of(tid & 63, step_t(0))];
-        for (int n = 0; n < nsteps; ++n) {
-            const int t = step_t(n);
-            __syncthreads();                       // the previous T is consumed
-            *reinterpret_cast<float4 *>(tb + s0 * 68 + c4) = p0;
-            *reinterpret_cast<float4 *>(tb + (s0 + 16) * 68 + c4) = p1;
-            *reinterpret_cast<float4 *>(tb + (s0 + 32) * 68 + c4) = p2;
-            *reinterpret_cast<float4 *>(tb + (s0 + 48) * 68 + c4) = p3;
-            if (tid < 64) {
-                tb[tid * 68 + 64] = p64;
-                tb[tid * 68 + 65] = tb[tid * 68 + 66] = tb[tid * 68 + 67] = 0.0f;
+        // this thread's staging share: float4 e = tid + 256 u of the 80 x 64 rows (row e / 16,
+        // columns 4 (e % 16)), and column 64 of row tid
+        float4 pre[5];
+        float pre64 = 0.0f;
+        auto load_stage = [&](int s) {
+#pragma unroll
+            for (int u = 0; u < 5; ++u) {
+                const int e = tid + kThreads * u, row = e >> 4;
+                pre[u] = *reinterpret_cast<const float4 *>(S + (size_t)(tile_f0(s, row >> 4) + (row & 15)) * OAL_D +
+                                                           (e & 15) * 4);
             }
-            __syncthreads();
-            {                                      // the last step reloads its own T (harmless)
-                const int tn = step_t(n + 1 < nsteps ? n + 1 : n);
-                p0 = ld4(s0, tn);
-                p1 = ld4(s0 + 16, tn);
-                p2 = ld4(s0 + 32, tn);
-                p3 = ld4(s0 + 48, tn);
-                p64 = Sd[dq_row_of(tid & 63, tn)];
+            if (tid < NR) pre64 = Sd[tile_f0(s, tid >> 4) + (tid & 15)];
+        };
+        auto store_stage = [&]() {
+#pragma unroll
+            for (int u = 0; u < 5; ++u) {
+                const int e = tid + kThreads * u, row = e >> 4, col = (e & 15) * 4;
+                const float xs[4] = {pre[u].x, pre[u].y, pre[u].z, pre[u].w};
+                oal_bf16x4 p0, p1, p2;
+#pragma unroll
+                for (int k4 = 0; k4 < 4; ++k4) {
+                    __bf16 x0, x1, x2;
+                    split3(xs[k4], x0, x1, x2);
+                    p0[k4] = x0;
+                    p1[k4] = x1;
+                    p2[k4] = x2;
+                }
+                *reinterpret_cast<oal_bf16x4 *>(&pl[0][row * PS + col]) = p0;
+                *reinterpret_cast<oal_bf16x4 *>(&pl[1][row * PS + col]) = p1;
+                *reinterpret_cast<oal_bf16x4 *>(&pl[2][row * PS + col]) = p2;
             }
-            oal_f32x4 X[4];
+            if (tid < NR) sdl[tid] = pre64;
+        };
+        // W of the stage's NT tiles: row 16 w + 4 kg + jj, feature (tile) lane lr
+        auto products = [&](auto nt_c, oal_f32x4 (&W)[5]) {
+            constexpr int NT = decltype(nt_c)::value;
 #pragma unroll
-            for (int sti = 0; sti < 4; ++sti) X[sti] = oal_splat(0.0f);
+            for (int i = 0; i < NT; ++i) W[i] = oal_splat(0.0f);
 #pragma unroll
-            for (int ks = 0; ks < 17; ++ks) {
-                const int col = 4 * ks + kg;
+            for (int ks = 0; ks < 2; ++ks) {
+                oal_bf16x8 bp[NT][3];
 #pragma unroll
-                for (int sti = 0; sti < 4; ++sti)
-                    X[sti] = __builtin_amdgcn_mfma_f32_16x16x4f32(ga[ks], tb[(16 * sti + lr) * 68 + col], X[sti], 0, 0, 0);
+                for (int i = 0; i < NT; ++i)
+#pragma unroll
+                    for (int p = 0; p < 3; ++p)
+                        bp[i][p] = *reinterpret_cast<const oal_bf16x8 *>(&pl[p][(16 * i + lr) * PS + 32 * ks + 8 * kg]);
+                // small terms first
+                if constexpr (!kAExact) {
+#pragma unroll
+                    for (int i = 0; i < NT; ++i) W[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ga[ks][1], bp[i][1], W[i], 0, 0, 0);
+#pragma unroll
+                    for (int i = 0; i < NT; ++i) W[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ga[ks][2], bp[i][0], W[i], 0, 0, 0);
+                }
+#pragma unroll
+                for (int i = 0; i < NT; ++i) W[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ga[ks][0], bp[i][2], W[i], 0, 0, 0);
+                if constexpr (!kAExact) {
+#pragma unroll
+                    for (int i = 0; i < NT; ++i) W[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ga[ks][1], bp[i][0], W[i], 0, 0, 0);
+                }
+#pragma unroll
+                for (int i = 0; i < NT; ++i) W[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ga[ks][0], bp[i][1], W[i], 0, 0, 0);
+#pragma unroll
+                for (int i = 0; i < NT; ++i) W[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ga[ks][0], bp[i][0], W[i], 0, 0, 0);
             }
 #pragma unroll
-            for (int sti = 0; sti < 4; ++sti) {
-                const int sd = 16 * sti + lr;
-                const float cst = KEYS ? (sd == t ? 2.0f : 1.0f)
-                                       : t == OAL_D ? wdl[1 + sd] : (sd == t ? 2.0f : 1.0f) * wdl[dq_row_of(sd, t)];
+            for (int i = 0; i < NT; ++i) {         // column 64: rank-1 update
+                const float sdv = sdl[16 * i + lr];
+#pragma unroll
+                for (int jj = 0; jj < 4; ++jj) W[i][jj] += g64[jj] * sdv;
+            }
+        };
+        // a row stage: KIND 1 (a < 16): tiles (a, 0..3), (63 - a, 3); KIND 2: (a, 1..3), (63 - a, 2..3)
+        auto row_stage = [&](auto kind_c, int a) {
+            constexpr int KIND = decltype(kind_c)::value;
+            oal_f32x4 W[5];
+            products(std::integral_constant<int, 5>{}, W);
+            const int rb = 63 - a;
+            float xa[4], xb[4], ra[4], rs[4];
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) {
+                xa[jj] = xq[(16 * w + 4 * kg + jj) * 68 + a];
+                xb[jj] = xq[(16 * w + 4 * kg + jj) * 68 + rb];
+                ra[jj] = rs[jj] = 0.0f;
+            }
+#pragma unroll
+            for (int i = 0; i < 5; ++i) {
+                const bool second = KIND == 1 ? i == 4 : i >= 3;
+                const int m = KIND == 1 ? (i < 4 ? i : 3) : (i < 3 ? i + 1 : i - 1);
+                const int r = second ? rb : a, t = 16 * m + lr;
+                // lanes with t < r read the coefficient of another feature (in range) and drop it
+                const float wraw = KEYS ? 1.0f : wdl[quad_base(r) + t];
+                const float cf = t >= r ? wraw : 0.0f;
 #pragma unroll
                 for (int jj = 0; jj < 4; ++jj) {
-                    const float qf = t == OAL_D ? 1.0f : xq[(16 * w + 4 * kg + jj) * 68 + t];
-                    acc[sti][jj] += cst * qf * X[sti][jj];
+                    const float wv = W[i][jj] * cf;
+                    if (second) {
+                        rs[jj] += wv * qreg[m][jj];
+                        acc[m][jj] += wv * xb[jj];
+                    } else {
+                        ra[jj] += wv * qreg[m][jj];
+                        acc[m][jj] += wv * xa[jj];
+                    }
                 }
+            }
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) {       // the row sums over the 16 lanes of the group
+                ra[jj] = row16_sum(ra[jj]);
+                rs[jj] = row16_sum(rs[jj]);
+            }
+            constexpr int MA = KIND == 1 ? 0 : 1, MB = KIND == 1 ? 3 : 2;
+            const int la = a - 16 * MA, lb = rb - 16 * MB;
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) {
+                if (lr == la) acc[MA][jj] += ra[jj];
+                if (lr == lb) acc[MB][jj] += rs[jj];
+            }
+        };
+        load_stage(sbeg);
+        for (int s = sbeg; s < send; ++s) {
+            __syncthreads();                       // the previous stage is consumed
+            store_stage();
+            __syncthreads();
+            if (s + 1 < send) load_stage(s + 1);
+            oal_pin_loads();
+            if (s == 0) {                          // linear features 1 + s
+                oal_f32x4 W[5];
+                products(std::integral_constant<int, 4>{}, W);
+#pragma unroll
+                for (int m = 0; m < 4; ++m) {
+                    const float cf = KEYS ? 1.0f : wdl[1 + 16 * m + lr];
+#pragma unroll
+                    for (int jj = 0; jj < 4; ++jj) acc[m][jj] += cf * W[m][jj];
+                }
+            } else if (s <= 16) {
+                row_stage(std::integral_constant<int, 1>{}, s - 1);
+            } else {
+                row_stage(std::integral_constant<int, 2>{}, s - 1);
             }
         }
     }
 #pragma unroll
-    for (int sti = 0; sti < 4; ++sti)
+    for (int m = 0; m < 4; ++m)
 #pragma unroll
         for (int jj = 0; jj < 4; ++jj) {
             const int tq = t0 + 16 * w + 4 * kg + jj;
             if (tq < T_len) {
                 if constexpr (KEYS)   // part slot psplit, dk half; rows = B Hkv T
-                    dq[((size_t)psplit * gridDim.z * n_kv_heads * T_len + qrow + tq) * 128 + 16 * sti + lr] = acc[sti][jj];
+                    out[((size_t)psplit * gridDim.z * n_kv_heads * T_len + row0 + tq) * 128 + 16 * m + lr] = acc[m][jj];
                 else
-                    dq[(qrow + tq) * OAL_D + 16 * sti + lr] = acc[sti][jj];
+                    out[(row0 + tq) * OAL_D + 16 * m + lr] = acc[m][jj];
             }
         }
 }
@@ -762,7 +985,7 @@ __global__ __launch_bounds__(kThreads) void oal_bwd_dq_intra_mfma(int T_len, int
 }
 
 // 7. dk and dv. Each 64-key tile is covered by:
-//    - oal_bwd_dq_inter_mfma<KEYS>: the state part of dk, dk_j += Jpsi(k_j)^T (R_c [v_j; 1]);
+//    - oal_bwd_dstate_x6<KEYS>: the state part of dk, dk_j += Jpsi(k_j)^T (R_c [v_j; 1]);
 //    - kInterSplits workgroups of oal_bwd_dv_inter: the 32 waves of the splits (worker
 //      4 p + w) take the feature-row pairs {worker, 63 - worker} (65 features each) of the
 //      state part of dv, dv_j += psi_f(k_j) R_c[f][0:64];
@@ -1200,7 +1423,7 @@ hipError_t launch_backward(const oal_dims &d, int T_len, int C, const void *q_, 
     const int s0 = state_in != nullptr;
     hipLaunchKernelGGL(oal_bwd_readout_g<T>, g_q, blk, 0, stream, s0, T_len, C, nch, Hq, Hkv, q, k, v, dy, params, st,
                        gv, gd);
-    hipLaunchKernelGGL((oal_bwd_dq_inter_mfma<T, false>), g_q, blk, 0, stream, s0, T_len, C, nch, Hq, Hkv, q,
+    hipLaunchKernelGGL((oal_bwd_dstate_x6<T, false>), g_q, blk, 0, stream, s0, T_len, C, nch, Hq, Hkv, q,
                        (const T *)nullptr, params, st, gv, gd, dq);
     hipLaunchKernelGGL(oal_bwd_dq_intra_mfma<T>, g_q, blk, 0, stream, T_len, C, Hq, Hkv, q, k, v, params, gv, gd, dq);
     hipLaunchKernelGGL(oal_bwd_dkv_intra_mfma<T>, g_kh, blk, 0, stream, T_len, C, Hq, Hkv, q, k, v, params, gv, gd,
@@ -1217,8 +1440,8 @@ hipError_t launch_backward(const oal_dims &d, int T_len, int C, const void *q_, 
         hipLaunchKernelGGL(oal_bwd_coef, dim3(Hq), blk, 0, stream, params, dwt, dL, deps);
     }
     hipLaunchKernelGGL(oal_bwd_scan, g_scan, blk, 0, stream, nch, 1, st, (const float *)nullptr, dstate_in);
-    hipLaunchKernelGGL((oal_bwd_dq_inter_mfma<T, true>), dim3(nch * tpc, Hkv * kDkSplits, B), blk, 0, stream, s0, T_len, C, nch, Hq,
-                       Hkv, k, v, params, st, gv, gd, part);
+    hipLaunchKernelGGL((oal_bwd_dstate_x6<T, true>), dim3(nch * tpc, Hkv * kDkSplits, B), blk, 0, stream, s0, T_len, C,
+                       nch, Hq, Hkv, k, v, params, st, gv, gd, part);
     hipLaunchKernelGGL(oal_bwd_dv_inter<T>, g_ki, blk, 0, stream, T_len, C, nch, Hkv, k, st, part);
     hipLaunchKernelGGL(oal_bwd_kv_reduce, g_red, blk, 0, stream, kvrows, nslots, part, dk, dv);
     return hipGetLastError();
