@@ -54,7 +54,8 @@
 namespace {
 
 constexpr int kThreads = 256;                 // four waves
-constexpr int kFeatBlock = 64;                // features per increment workgroup
+constexpr int kFeatBlock = 128;               // features per increment workgroup
+constexpr int kIncThreads = 512;              // its eight waves, 16 features each
 constexpr int kDkSplits = 4;                  // dk state part: its t steps over 4 workgroups
 
 typedef const float __attribute__((address_space(4))) cfloat;   // wave-uniform reads
@@ -169,30 +170,75 @@ __device__ inline void stage_g(float *dst, const float *gv, const float *gd, siz
 }
 
 // ---------------------------------------------------------------------------------------------
+// fp32 x = x0 + x1 + x2 (+ a remainder below 2^-24 |x|) in bf16 parts, each difference exact in
+// fp32: x0 = bf16(x), x1 = bf16(x - x0), x2 = bf16(x - x0 - x1). A product x y is taken as the
+// six terms x_i y_j with i + j <= 2 (Henry, Tang and Heinecke, "Leveraging the bfloat16
+// artificial intelligence datatype for higher-precision computations", 2019: the "bf16x6"
+// product); the dropped terms are below about 2^-22 |x y|, and each 16x16x32 bf16 MFMA is exact
+// in its products and accumulates in fp32.
+__device__ inline void split3(float x, __bf16 &x0, __bf16 &x1, __bf16 &x2) {
+    x0 = (__bf16)x;
+    const float r = x - (float)x0;
+    x1 = (__bf16)r;
+    x2 = (__bf16)(r - (float)x1);
+}
+
+typedef __bf16 oal_bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 oal_bf16x2 __attribute__((ext_vector_type(2)));
+
+// Sum over the 16 lanes of a DPP row, left in every lane of the row: row rotations by 8, 4,
+// 2 and 1 lanes (VALU data movement, no LDS round trip).
+__device__ inline float row16_sum(float x) {
+    x += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x128, 0xf, 0xf, false));
+    x += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x124, 0xf, 0xf, false));
+    x += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x122, 0xf, 0xf, false));
+    x += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x121, 0xf, 0xf, false));
+    return x;
+}
+
+// Four consecutive elements as fp32 (8-byte aligned for bf16, 16-byte for fp32).
+__device__ inline void oal_ld4(const float *p, float (&o)[4]) {
+    const float4 t = *reinterpret_cast<const float4 *>(p);
+    o[0] = t.x; o[1] = t.y; o[2] = t.z; o[3] = t.w;
+}
+__device__ inline void oal_ld4(const __bf16 *p, float (&o)[4]) {
+    const oal_bf16x4 t = *reinterpret_cast<const oal_bf16x4 *>(p);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) o[e] = (float)t[e];
+}
+
 // 1 / 5. Per-chunk increments of one (sequence, KV head): out_c[f][col] = sum_n a_n(f) b_n[col]
 //   keys:    a_n = psi_f(k_n),                 b_n = [v_n; 1]   (n over the chunk's keys)
 //   queries: a_n = wdec_h[f] mono_f(q_n),      b_n = g_n        (n over the chunk's queries of
 //                                                                every head h of the KV head);
 //            with dwp, also the state part of each head's coefficient gradient (see below)
-// fp32 MFMA (16x16x4): M = features, N = value columns (five 16-column tiles, the fifth
-// holding column 64), K = rows. Workgroup = (64 features, chunk, sequence x KV head), wave w
-// the features 16 w .. 16 w + 15; rows are staged 64 at a time. A operand: lane l holds
-// mono_f(x_n) of feature 16 w + l % 16 and row n = 4 K-step + l / 16 (the feature's dims are
-// fixed per lane); B operand: b_n[16 tile + l % 16]. Accumulators: the head's tile D (lane l
+// bf16 MFMA (16x16x32) on split operands: M = features, N = the 64 value columns (four
+// 16-column tiles), K = rows, 32 per K-step; column 64 (the 1 of the keys, g's 65th value of
+// the queries) on the VALU. Operand parts: mono_f(x) = x_r x_t is exact in two bf16 parts for
+// bf16 inputs (16 significant bits), three otherwise; v is exact in one part for bf16 inputs,
+// g takes three; the products are the terms of order <= 2 of split3 (keys with bf16 inputs:
+// two exact terms). Workgroup = (128 features, chunk, sequence x KV head), eight waves, wave w
+// the features 16 w .. 16 w + 15; rows are staged 64 at a time, transposed: x as fp32
+// [dim][row] (dim 64 holds the 1), b in bf16 parts [column][row] (the queries' g parts come
+// ready from oal_bwd_readout_g), so that a lane's 8 rows are contiguous. A
+// operand: lane l holds mono_f(x_n) of feature 16 w + l % 16, rows n = 32 ks + 8 (l / 16) + e;
+// B operand: b_n[16 tile + l % 16] of the same rows. Accumulators: the head's tile D (lane l
 // holds features 16 w + 4 (l / 16) + j, column 16 tile + l % 16), folded into the total with
 // the head's coefficients after its rows.
 template <typename T, bool QSIDE>
-__global__ __launch_bounds__(kThreads) void oal_bwd_increments(int T_len, int C, int nch, int n_q_heads,
+__global__ __launch_bounds__(kIncThreads) void oal_bwd_increments(int T_len, int C, int nch, int n_q_heads,
                                                                 int n_kv_heads, const T *__restrict__ x,
                                                                 const T *__restrict__ v, const float *__restrict__ gv,
                                                                 const float *__restrict__ gd,
+                                                                const __bf16 *__restrict__ gpl,
                                                                 const unsigned char *__restrict__ params,
                                                                 float *__restrict__ st, float *__restrict__ dwp) {
-    // row stride 80 (16 mod 32 banks): the four row groups of a wave's MFMA operand reads fall
-    // on two bank halves, the two-pass minimum for 64 lanes (65 or 68 gave up to 4-way conflicts)
-    constexpr int XS = 80;
-    __shared__ __align__(16) float xs[64 * XS];
-    __shared__ __align__(16) float bs[64 * XS];
+    constexpr int NA = sizeof(T) == 2 ? 2 : 3;                 // parts of mono_f(x)
+    constexpr int NB = (!QSIDE && sizeof(T) == 2) ? 1 : 3;     // parts of b
+    constexpr int XT = 68, PS = 72;                            // row strides (fp32 / bf16)
+    __shared__ __align__(16) float xt[65 * XT];
+    __shared__ __align__(16) __bf16 bpl[NB * 64 * PS];
+    __shared__ __align__(16) float b64s[64];
     const int tid = threadIdx.x, lane = tid & 63, lr = lane & 15, kg = lane >> 4, w = wave_id();
     const int c = blockIdx.y, bkv = blockIdx.z;
     const int b = bkv / n_kv_heads, kv = bkv % n_kv_heads, n_rep = n_q_heads / n_kv_heads;
@@ -208,14 +254,16 @@ __global__ __launch_bounds__(kThreads) void oal_bwd_increments(int T_len, int C,
         ib = r + idx;
     }
     float *out = st + ((size_t)bkv * nch + c) * OAL_STATE_STRIDE;
-    // output positions of this lane: features fo + j (j = 0..3), column 16 ct + lr
+    // output positions of this lane: features fo + j (j = 0..3), column 16 ct + lr; column 64
+    // of feature fa_lane
     const int fo = fbase + 4 * kg;
     // queries with dwp: the state S_c this kernel overwrites, for the coefficient gradient
     // dw_h[f] = sum_{i in chunk} mono_f(q_i) (S_c g_i)[f] = S_c[f] . (sum_i mono_f(q_i) g_i)
     const bool coef = QSIDE && dwp != nullptr;
-    oal_f32x4 sv[5], tot[5];
+    oal_f32x4 sv[4], tot[4];
+    float sv64[4] = {0.0f, 0.0f, 0.0f, 0.0f}, tot64 = 0.0f;
 #pragma unroll
-    for (int ct = 0; ct < 5; ++ct) sv[ct] = tot[ct] = oal_splat(0.0f);
+    for (int ct = 0; ct < 4; ++ct) sv[ct] = tot[ct] = oal_splat(0.0f);
     if (coef) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
@@ -223,23 +271,40 @@ __global__ __launch_bounds__(kThreads) void oal_bwd_increments(int T_len, int C,
             if (f < OAL_NFEAT) {
 #pragma unroll
                 for (int ct = 0; ct < 4; ++ct) sv[ct][j] = out[(size_t)f * OAL_D + 16 * ct + lr];
-                sv[4][j] = lr == 0 ? out[(size_t)OAL_NFEAT * OAL_D + f] : 0.0f;
+                sv64[j] = out[(size_t)OAL_NFEAT * OAL_D + f];
             }
         }
     }
     const int nsrc = QSIDE ? n_rep : 1;
     const int tend = min(c * C + C, T_len);
     // the (row tile, head) steps in order; each step's x and b rows are loaded into registers
-    // one step ahead (thread's share: 16 elements of each, plus one b[64])
+    // one step ahead: thread's share rows r0 + u (u < 4), dims / columns dc + j (j < 4), and
+    // b[64] of row tid
     const int ntile = (tend - c * C + 63) / 64, nstep = nsrc * ntile;
-    float px[16], pb[16], pb64 = 0.0f;
+    const int r0 = 2 * (tid & 31), dc = 4 * (tid >> 5);
+    float px[2][4], pb[2][4], pb64 = 0.0f;
+    uint4 pg0, pg1, pg2;                           // queries: g's parts as written by the readout
     auto load_step = [&](int stp) {
         const int hs = stp / ntile, t0 = c * C + (stp % ntile) * 64;
         const int h = kv * n_rep + hs;
         const size_t row0 = QSIDE ? ((size_t)b * n_q_heads + h) * T_len : ((size_t)b * n_kv_heads + kv) * T_len;
-        load_tile(px, x, row0, t0, T_len);
-        if constexpr (QSIDE) load_tile(pb, gv, row0, t0, T_len);
-        else load_tile(pb, v, row0, t0, T_len);
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const int t = t0 + r0 + u;
+            const size_t o = (row0 + t) * OAL_D + dc;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) px[u][j] = pb[u][j] = 0.0f;
+            if (t < T_len) {
+                oal_ld4(x + o, px[u]);
+                if constexpr (!QSIDE) oal_ld4(v + o, pb[u]);
+            }
+        }
+        if constexpr (QSIDE) {                     // 16-byte piece tid of each part
+            const __bf16 *gp = gpl + ((size_t)((size_t)b * n_q_heads + h) * ((T_len + 63) / 64) + t0 / 64) * 3 * 4096;
+            pg0 = *reinterpret_cast<const uint4 *>(gp + 8 * tid);
+            pg1 = *reinterpret_cast<const uint4 *>(gp + 4096 + 8 * tid);
+            pg2 = *reinterpret_cast<const uint4 *>(gp + 2 * 4096 + 8 * tid);
+        }
         if (tid < 64) {
             const bool ok = t0 + tid < T_len;
             if constexpr (QSIDE) pb64 = ok ? gd[row0 + t0 + tid] : 0.0f;
@@ -250,52 +315,112 @@ __global__ __launch_bounds__(kThreads) void oal_bwd_increments(int T_len, int C,
     int stp = 0;
     for (int hs = 0; hs < nsrc; ++hs) {
         const int h = kv * n_rep + hs;
-        oal_f32x4 D[5];
+        oal_f32x4 D[4];
 #pragma unroll
-        for (int ct = 0; ct < 5; ++ct) D[ct] = oal_splat(0.0f);
+        for (int ct = 0; ct < 4; ++ct) D[ct] = oal_splat(0.0f);
+        float dsum = 0.0f;                         // column 64: feature fa_lane, the lane's rows
         for (int t0 = c * C; t0 < tend; t0 += 64, ++stp) {
             __syncthreads();                       // the previous tile is consumed
-            store_tile<T>(xs, XS, px);
-            if constexpr (QSIDE) store_tile<float>(bs, XS, pb);
-            else store_tile<T>(bs, XS, pb);
+            if constexpr (QSIDE) {                 // piece tid: column tid / 8, queries 8 (tid % 8) .. + 7
+                const int o = (tid >> 3) * PS + 8 * (tid & 7);
+                *reinterpret_cast<uint4 *>(bpl + o) = pg0;
+                *reinterpret_cast<uint4 *>(bpl + 64 * PS + o) = pg1;
+                *reinterpret_cast<uint4 *>(bpl + 2 * 64 * PS + o) = pg2;
+            }
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                *reinterpret_cast<float2 *>(xt + (dc + j) * XT + r0) = make_float2(px[0][j], px[1][j]);
+                if constexpr (QSIDE) continue;
+                oal_bf16x2 p0, p1, p2;
+#pragma unroll
+                for (int u = 0; u < 2; ++u) {
+                    __bf16 x0, x1, x2;
+                    split3(pb[u][j], x0, x1, x2);
+                    p0[u] = x0;
+                    p1[u] = x1;
+                    p2[u] = x2;
+                }
+                const int o = (dc + j) * PS + r0;
+                *reinterpret_cast<oal_bf16x2 *>(bpl + o) = p0;
+                if constexpr (NB > 1) {
+                    *reinterpret_cast<oal_bf16x2 *>(bpl + 64 * PS + o) = p1;
+                    *reinterpret_cast<oal_bf16x2 *>(bpl + 2 * 64 * PS + o) = p2;
+                }
+            }
             if (tid < 64) {
-                xs[tid * XS + 64] = 1.0f;
-                bs[tid * XS + 64] = pb64;
+                xt[OAL_D * XT + tid] = 1.0f;
+                b64s[tid] = pb64;
             }
             __syncthreads();
             if (stp + 1 < nstep) load_step(stp + 1);
-#pragma unroll 4
-            for (int kst = 0; kst < 16; ++kst) {
-                const int n = 4 * kst + kg;
-                const float a = xs[n * XS + ia] * xs[n * XS + ib];
-                const float *br = bs + n * XS;
+            oal_pin_loads();
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) {
+                const int rr = 32 * ks + 8 * kg;   // the lane's first row
+                float m[8];
+                {
+                    const float4 xa0 = *reinterpret_cast<const float4 *>(xt + ia * XT + rr);
+                    const float4 xa1 = *reinterpret_cast<const float4 *>(xt + ia * XT + rr + 4);
+                    const float4 xb0 = *reinterpret_cast<const float4 *>(xt + ib * XT + rr);
+                    const float4 xb1 = *reinterpret_cast<const float4 *>(xt + ib * XT + rr + 4);
+                    const float4 g0 = *reinterpret_cast<const float4 *>(b64s + rr);
+                    const float4 g1 = *reinterpret_cast<const float4 *>(b64s + rr + 4);
+                    m[0] = xa0.x * xb0.x; m[1] = xa0.y * xb0.y; m[2] = xa0.z * xb0.z; m[3] = xa0.w * xb0.w;
+                    m[4] = xa1.x * xb1.x; m[5] = xa1.y * xb1.y; m[6] = xa1.z * xb1.z; m[7] = xa1.w * xb1.w;
+                    dsum += m[0] * g0.x + m[1] * g0.y + m[2] * g0.z + m[3] * g0.w + m[4] * g1.x + m[5] * g1.y +
+                            m[6] * g1.z + m[7] * g1.w;
+                }
+                oal_bf16x8 a[3];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    __bf16 x0, x1, x2;
+                    split3(m[e], x0, x1, x2);
+                    a[0][e] = x0;
+                    a[1][e] = x1;
+                    a[2][e] = x2;
+                }
+                oal_bf16x8 bb[4][NB];
 #pragma unroll
                 for (int ct = 0; ct < 4; ++ct)
-                    D[ct] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, br[16 * ct + lr], D[ct], 0, 0, 0);
-                D[4] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, lr == 0 ? br[64] : 0.0f, D[4], 0, 0, 0);
+#pragma unroll
+                    for (int p = 0; p < NB; ++p)
+                        bb[ct][p] = *reinterpret_cast<const oal_bf16x8 *>(bpl + p * 64 * PS + (16 * ct + lr) * PS + rr);
+                // the terms a_i b_j with i + j <= 2, small ones first
+#pragma unroll
+                for (int ord = 2; ord >= 0; --ord)
+#pragma unroll
+                    for (int i = 0; i < NA; ++i) {
+                        const int jb = ord - i;
+                        if (jb < 0 || jb >= NB) continue;
+#pragma unroll
+                        for (int ct = 0; ct < 4; ++ct)
+                            D[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], bb[ct][jb], D[ct], 0, 0, 0);
+                    }
             }
         }
+        // column 64 of feature fa_lane: the four row groups
+        dsum += __shfl_xor(dsum, 16);
+        dsum += __shfl_xor(dsum, 32);
         // fold: total += wdec_h[f] D (keys: weight 1); coefficient-gradient partial per feature
         float wj[4];
 #pragma unroll
         for (int j = 0; j < 4; ++j)
             wj[j] = QSIDE ? (fo + j < OAL_NFEAT ? bwd_head(params, h)->wdec[fo + j] : 0.0f) : 1.0f;
 #pragma unroll
-        for (int ct = 0; ct < 5; ++ct)
+        for (int ct = 0; ct < 4; ++ct)
 #pragma unroll
             for (int j = 0; j < 4; ++j) tot[ct][j] += wj[j] * D[ct][j];
+        tot64 += (QSIDE ? (fa_lane < OAL_NFEAT ? bwd_head(params, h)->wdec[fa_lane] : 0.0f) : 1.0f) * dsum;
         if (coef) {
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 float pdw = 0.0f;
 #pragma unroll
-                for (int ct = 0; ct < 5; ++ct) pdw += sv[ct][j] * D[ct][j];
-                pdw += __shfl_xor(pdw, 1);         // the 16 columns of the tile row
-                pdw += __shfl_xor(pdw, 2);
-                pdw += __shfl_xor(pdw, 4);
-                pdw += __shfl_xor(pdw, 8);
+                for (int ct = 0; ct < 4; ++ct) pdw += sv[ct][j] * D[ct][j];
+                pdw = row16_sum(pdw);              // the 64 columns of the feature
+                const float d64 = __shfl(dsum, 4 * kg + j);   // column 64 of feature fo + j
                 if (lr == 0 && fo + j < OAL_NFEAT)
-                    dwp[(((size_t)b * n_q_heads + h) * nch + c) * OAL_NFEAT + fo + j] = pdw;
+                    dwp[(((size_t)b * n_q_heads + h) * nch + c) * OAL_NFEAT + fo + j] = pdw + sv64[j] * d64;
             }
         }
     }
@@ -305,9 +430,9 @@ __global__ __launch_bounds__(kThreads) void oal_bwd_increments(int T_len, int C,
         if (f < OAL_NFEAT) {
 #pragma unroll
             for (int ct = 0; ct < 4; ++ct) out[(size_t)f * OAL_D + 16 * ct + lr] = tot[ct][j];
-            if (lr == 0) out[(size_t)OAL_NFEAT * OAL_D + f] = tot[4][j];
         }
     }
+    if (kg == 0 && fa_lane < OAL_NFEAT) out[(size_t)OAL_NFEAT * OAL_D + fa_lane] = tot64;
 }
 
 // 2 / 6. Exclusive prefix (reverse = 0) or suffix (reverse = 1) sum over the chunks of each
@@ -347,20 +472,6 @@ __device__ inline void xcd_order(int &x, int &y, int &z) {
     z = item / gx;
 }
 
-// fp32 x = x0 + x1 + x2 (+ a remainder below 2^-24 |x|) in bf16 parts, each difference exact in
-// fp32: x0 = bf16(x), x1 = bf16(x - x0), x2 = bf16(x - x0 - x1). A product x y is taken as the
-// six terms x_i y_j with i + j <= 2 (Henry, Tang and Heinecke, "Leveraging the bfloat16
-// artificial intelligence datatype for higher-precision computations", 2019: the "bf16x6"
-// product); the dropped terms are below about 2^-22 |x y|, and each 16x16x32 bf16 MFMA is exact
-// in its products and accumulates in fp32.
-__device__ inline void split3(float x, __bf16 &x0, __bf16 &x1, __bf16 &x2) {
-    x0 = (__bf16)x;
-    const float r = x - (float)x0;
-    x1 = (__bf16)r;
-    x2 = (__bf16)(r - (float)x1);
-}
-
-typedef __bf16 oal_bf16x4 __attribute__((ext_vector_type(4)));
 
 // Keys of the chunk that query lane i of tile qt sees, tile kt: all of an earlier tile, up to
 // and including its own position in its own tile.
@@ -379,7 +490,7 @@ __global__ __launch_bounds__(kThreads) void oal_bwd_readout_g(int s0, int T_len,
                                                                const float *__restrict__ dy,
                                                                const unsigned char *__restrict__ params,
                                                                const float *__restrict__ st, float *__restrict__ gv,
-                                                               float *__restrict__ gd) {
+                                                               float *__restrict__ gd, __bf16 *__restrict__ gpl) {
     __shared__ float xq[64 * 65];
     __shared__ __align__(16) float ks[64 * 68];    // keys; before them the coefficient tables
     // values (vs) and kappa / u (uin); before them the split block of S_c across both
@@ -586,21 +697,55 @@ __global__ __launch_bounds__(kThreads) void oal_bwd_readout_g(int s0, int T_len,
         }
     __syncthreads();
     float acc[65];
-    if (w == 0 && valid) {
+    float *gt = xq;                                // g transposed: [column][query], stride 65
+    if (w == 0) {
+        if (valid) {
 #pragma unroll
-        for (int e = 0; e < 65; ++e) acc[e] = uin[i * 68 + e];
-        const float inv = 1.0f / acc[64];
-        const float *dyr = dy + (qrow + t) * OAL_D;
-        float *gr = gv + (qrow + t) * OAL_D;
-        float dot = 0.0f;
+            for (int e = 0; e < 65; ++e) acc[e] = uin[i * 68 + e];
+            const float inv = 1.0f / acc[64];
+            const float *dyr = dy + (qrow + t) * OAL_D;
+            float *gr = gv + (qrow + t) * OAL_D;
+            float dot = 0.0f;
 #pragma unroll
-        for (int e = 0; e < 64; e += 4) {
-            const float4 d4 = *reinterpret_cast<const float4 *>(dyr + e);
-            dot += d4.x * (acc[e] * inv) + d4.y * (acc[e + 1] * inv) + d4.z * (acc[e + 2] * inv) +
-                   d4.w * (acc[e + 3] * inv);
-            *reinterpret_cast<float4 *>(gr + e) = make_float4(d4.x * inv, d4.y * inv, d4.z * inv, d4.w * inv);
+            for (int e = 0; e < 64; e += 4) {
+                const float4 d4 = *reinterpret_cast<const float4 *>(dyr + e);
+                dot += d4.x * (acc[e] * inv) + d4.y * (acc[e + 1] * inv) + d4.z * (acc[e + 2] * inv) +
+                       d4.w * (acc[e + 3] * inv);
+                const float4 g4 = make_float4(d4.x * inv, d4.y * inv, d4.z * inv, d4.w * inv);
+                *reinterpret_cast<float4 *>(gr + e) = g4;
+                gt[e * 65 + i] = g4.x;
+                gt[(e + 1) * 65 + i] = g4.y;
+                gt[(e + 2) * 65 + i] = g4.z;
+                gt[(e + 3) * 65 + i] = g4.w;
+            }
+            gd[qrow + t] = -dot * inv;
+        } else {
+#pragma unroll 8
+            for (int e = 0; e < 64; ++e) gt[e * 65 + i] = 0.0f;
         }
-        gd[qrow + t] = -dot * inv;
+    }
+    __syncthreads();
+    // g[0:64] of the tile also in three bf16 parts, transposed, for the query increments:
+    // gpl[tile][part][column][query], tile = (sequence x head, t0 / 64); thread's share: column
+    // tid / 4, queries 16 (tid % 4) .. + 15 (a tile past the sequence has no slot)
+    if (t0 < T_len) {
+        const int col = threadIdx.x >> 2, q0 = 16 * (threadIdx.x & 3);
+        __bf16 *gp = gpl + ((size_t)((size_t)b * n_q_heads + h) * ((T_len + 63) / 64) + t0 / 64) * 3 * 4096 + col * 64 + q0;
+#pragma unroll
+        for (int hv = 0; hv < 2; ++hv) {
+            oal_bf16x8 p0, p1, p2;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                __bf16 x0, x1, x2;
+                split3(gt[col * 65 + q0 + 8 * hv + e], x0, x1, x2);
+                p0[e] = x0;
+                p1[e] = x1;
+                p2[e] = x2;
+            }
+            *reinterpret_cast<oal_bf16x8 *>(gp + 8 * hv) = p0;
+            *reinterpret_cast<oal_bf16x8 *>(gp + 4096 + 8 * hv) = p1;
+            *reinterpret_cast<oal_bf16x8 *>(gp + 2 * 4096 + 8 * hv) = p2;
+        }
     }
 }
 
@@ -625,15 +770,6 @@ __global__ __launch_bounds__(kThreads) void oal_bwd_readout_g(int s0, int T_len,
 //     dq[r] sums of a row are reduced over the 16 lanes of a row group at the end of the stage.
 //     Keys: the 33 stages are split over kDkSplits workgroups, each writing its own slot.
 
-// Sum over the 16 lanes of a DPP row, left in every lane of the row: row rotations by 8, 4,
-// 2 and 1 lanes (VALU data movement, no LDS round trip).
-__device__ inline float row16_sum(float x) {
-    x += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x128, 0xf, 0xf, false));
-    x += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x124, 0xf, 0xf, false));
-    x += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x122, 0xf, 0xf, false));
-    x += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x121, 0xf, 0xf, false));
-    return x;
-}
 
 template <typename T, bool KEYS>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void oal_bwd_dstate_x6(
@@ -1410,6 +1546,9 @@ hipError_t launch_backward(const oal_dims &d, int T_len, int C, const void *q_, 
     const size_t kvrows = (size_t)B * Hkv * T_len;
     float *dwp = reinterpret_cast<float *>(reinterpret_cast<unsigned char *>(part) +
                                            align256((size_t)(kInterSplits + Hq / Hkv) * kvrows * 128 * 4));
+    // g in three bf16 parts per 64-query tile (oal_bwd_readout_g -> query increments)
+    __bf16 *gpl = reinterpret_cast<__bf16 *>(reinterpret_cast<unsigned char *>(dwp) +
+                                             align256(((size_t)2 * B * nch + 1) * Hq * OAL_NFEAT * 4));
     const bool coef = dL != nullptr;
     const dim3 blk(kThreads);
     const dim3 g_inc((OAL_NFEAT + kFeatBlock - 1) / kFeatBlock, nch, B * Hkv);
@@ -1417,12 +1556,13 @@ hipError_t launch_backward(const oal_dims &d, int T_len, int C, const void *q_, 
     const dim3 g_q(nch * tpc, Hq, B), g_ki(nch * tpc, Hkv * kInterSplits, B), g_kh(nch * tpc, Hq, B);
     const dim3 g_red((unsigned)((kvrows * 32 + kThreads - 1) / kThreads));
     const int nslots = kInterSplits + Hq / Hkv;
-    hipLaunchKernelGGL((oal_bwd_increments<T, false>), g_inc, blk, 0, stream, T_len, C, nch, Hq, Hkv, k, v,
-                       (const float *)nullptr, (const float *)nullptr, params, st, (float *)nullptr);
+    hipLaunchKernelGGL((oal_bwd_increments<T, false>), g_inc, dim3(kIncThreads), 0, stream, T_len, C, nch, Hq, Hkv, k, v,
+                       (const float *)nullptr, (const float *)nullptr, (const __bf16 *)nullptr, params, st,
+                       (float *)nullptr);
     hipLaunchKernelGGL(oal_bwd_scan, g_scan, blk, 0, stream, nch, 0, st, state_in, (float *)nullptr);
     const int s0 = state_in != nullptr;
     hipLaunchKernelGGL(oal_bwd_readout_g<T>, g_q, blk, 0, stream, s0, T_len, C, nch, Hq, Hkv, q, k, v, dy, params, st,
-                       gv, gd);
+                       gv, gd, gpl);
     hipLaunchKernelGGL((oal_bwd_dstate_x6<T, false>), g_q, blk, 0, stream, s0, T_len, C, nch, Hq, Hkv, q,
                        (const T *)nullptr, params, st, gv, gd, dq);
     hipLaunchKernelGGL(oal_bwd_dq_intra_mfma<T>, g_q, blk, 0, stream, T_len, C, Hq, Hkv, q, k, v, params, gv, gd, dq);
@@ -1431,8 +1571,8 @@ hipError_t launch_backward(const oal_dims &d, int T_len, int C, const void *q_, 
     if (coef)
         hipLaunchKernelGGL(oal_bwd_dw_intra<T>, dim3(nch, Hq, B), blk, 0, stream, T_len, C, nch, Hq, Hkv, q, k, v,
                            gv, gd, dwp + (size_t)B * Hq * nch * OAL_NFEAT);
-    hipLaunchKernelGGL((oal_bwd_increments<T, true>), g_inc, blk, 0, stream, T_len, C, nch, Hq, Hkv, q,
-                       (const T *)nullptr, gv, gd, params, st, coef ? dwp : (float *)nullptr);
+    hipLaunchKernelGGL((oal_bwd_increments<T, true>), g_inc, dim3(kIncThreads), 0, stream, T_len, C, nch, Hq, Hkv, q,
+                       (const T *)nullptr, gv, gd, gpl, params, st, coef ? dwp : (float *)nullptr);
     if (coef) {
         float *dwt = dwp + 2 * (size_t)B * Hq * nch * OAL_NFEAT;
         hipLaunchKernelGGL(oal_bwd_dw_sum, dim3((OAL_NFEAT + kThreads - 1) / kThreads, Hq), blk, 0, stream, B, nch,
@@ -1454,7 +1594,8 @@ size_t oal_backward_ws_bytes_impl(const oal_dims &d, int T_len, int C) {
     return align256((size_t)d.batch * d.n_kv_heads * nch * OAL_STATE_STRIDE * 4) +
            align256((size_t)d.batch * d.n_q_heads * T_len * 64 * 4) + align256((size_t)d.batch * d.n_q_heads * T_len * 4) +
            align256((size_t)(kInterSplits + d.n_q_heads / d.n_kv_heads) * d.batch * d.n_kv_heads * T_len * 128 * 4) +
-           align256(((size_t)2 * d.batch * nch + 1) * d.n_q_heads * OAL_NFEAT * 4);
+           align256(((size_t)2 * d.batch * nch + 1) * d.n_q_heads * OAL_NFEAT * 4) +
+           align256((size_t)d.batch * d.n_q_heads * ((T_len + 63) / 64) * 3 * 4096 * 2);
 }
 
 hipError_t oal_launch_backward(const oal_dims &d, int T_len, int C, const void *q, const void *k, const void *v,

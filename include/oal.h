@@ -287,9 +287,12 @@ oal_status oal_contribution(const oal_dims *dims, int32_t T, const void *q, cons
  *                 the forward call started from, or NULL for an empty prefix.
  *   workspace  -- oal_prefill_backward_workspace_bytes(dims, T, chunk) bytes of device scratch
  *                 (per-chunk states, one block of OAL_STATE_STRIDE floats per sequence, KV
- *                 head and chunk; the per-query readout gradients; partial dq, key and
- *                 coefficient gradients); contents on entry do not matter.
- * All arithmetic is fp32 whatever dims->dtype is (bf16 inputs are widened on load). Every
+ *                 head and chunk; the per-query readout gradients, also in three bf16 parts
+ *                 per 64-query tile; partial dq, key and coefficient gradients); contents on
+ *                 entry do not matter.
+ * All arithmetic is to fp32 accuracy whatever dims->dtype is (bf16 inputs are widened on load;
+ * the state contractions run on bf16 MFMA with each fp32 operand split in three bf16 parts and
+ * the six products of order <= 2, the rest on fp32 MFMA or the VALU). Every
  * pointer but dL and deps must be 16-byte aligned (OAL_E_ALIGN; state_in and dstate_in when
  * given). T = 0 writes nothing. More than 65535 chunks per sequence,
  * n_q_heads + 3 n_kv_heads > 65535 or n_kv_heads > 8191 give OAL_E_UNSUPPORTED (grid limits). */

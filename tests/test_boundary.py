@@ -59,14 +59,17 @@ def test_sizes():
     assert gpq.oal_contribution_workspace_bytes(gpq.make_dims(0, 14, 2, "bf16"), 64) == 0
     assert gpq.oal_contribution_workspace_bytes(bad, 64) == 0
     # backward: per-chunk states per (sequence, KV head), g (64 + 1 floats per query), then
-    # 8 + n_rep partial (dk, dv) rows of 128 floats per key, two per-chunk coefficient partials and their sum per head
+    # 8 + n_rep partial (dk, dv) rows of 128 floats per key, two per-chunk coefficient partials
+    # and their sum per head, and g[0:64] in three bf16 parts per 64-query tile
     al = lambda x: -(-x // 256) * 256
     assert gpq.oal_prefill_backward_workspace_bytes(d, 4096, 64) == (
         al(3 * 2 * 64 * 139456 * 4) + al(3 * 14 * 4096 * 64 * 4) + al(3 * 14 * 4096 * 4) +
-        al((8 + 7) * 3 * 2 * 4096 * 128 * 4) + al((2 * 3 * 64 + 1) * 14 * 2145 * 4))
+        al((8 + 7) * 3 * 2 * 4096 * 128 * 4) + al((2 * 3 * 64 + 1) * 14 * 2145 * 4) +
+        al(3 * 14 * 64 * 3 * 4096 * 2))
     assert gpq.oal_prefill_backward_workspace_bytes(d, 130, 128) == (
         al(3 * 2 * 2 * 139456 * 4) + al(3 * 14 * 130 * 64 * 4) + al(3 * 14 * 130 * 4) +
-        al((8 + 7) * 3 * 2 * 130 * 128 * 4) + al((2 * 3 * 2 + 1) * 14 * 2145 * 4))
+        al((8 + 7) * 3 * 2 * 130 * 128 * 4) + al((2 * 3 * 2 + 1) * 14 * 2145 * 4) +
+        al(3 * 14 * 3 * 3 * 4096 * 2))
     assert gpq.oal_prefill_backward_workspace_bytes(d, 4096, 100) == 0
     assert gpq.oal_prefill_backward_workspace_bytes(d, -1, 64) == 0
     assert gpq.oal_prefill_backward_workspace_bytes(d, 64 * 65536, 64) == 0
