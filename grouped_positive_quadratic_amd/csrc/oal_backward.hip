@@ -1354,11 +1354,15 @@ __global__ __launch_bounds__(kThreads) void oal_bwd_kv_reduce(size_t rows, int n
 //     dL = 2 (dLoss/dM) L and deps = dLoss/dM[0][0].
 //
 // Pairs inside chunk c for head h: workgroup = (chunk, head, sequence). Per (query tile, key
-// tile) pair: the tile of dkappa (masked to j <= i) in LDS, then on fp32 MFMA (16x16x4)
-// Y = dkappa psi(K) (M = 64 queries in four 16-row tiles, N = features, K = 64 keys) and
-// dw[f] += sum_i mono_f(q_i) Y[i][f]. Wave w takes the feature tiles w, w + 4, ...; lane l
-// holds the A operand dkappa[16 it + l % 16][4 s + l / 16] in registers for the whole pair and
-// builds the B operand psi_f(k_j) (f = 16 ft + l % 16, j = 4 s + l / 16) from the key tile.
+// tile) pair: the tile of dkappa (masked to j <= i) in LDS, then on split-bf16 MFMA (16x16x32,
+// the terms of order <= 2 of split3; psi_f(k) = k_r k_t is exact in two bf16 parts for bf16
+// inputs) Y = dkappa psi(K) (M = 64 queries in four 16-row tiles, N = features, K = 64 keys in
+// two K-steps) and dw[f] += sum_i mono_f(q_i) Y[i][f]. Wave w takes the feature tiles w, w + 4,
+// ...; lane l holds the A operand dkappa[16 it + l % 16][32 ks + 8 (l / 16) + e] in three bf16
+// parts in registers for the whole pair and builds the B operand psi_f(k_j)
+// (f = 16 ft + l % 16, the same keys j) from the key tile. The query and key tiles are staged
+// transposed ([dim][token], dim 64 holding the 1) so that a lane's 8 keys, and the 4 queries
+// of its accumulator rows, are 16-byte reads.
 template <typename T>
 __global__ __launch_bounds__(kThreads) void oal_bwd_dw_intra(int T_len, int C, int nch, int n_q_heads,
                                                               int n_kv_heads, const T *__restrict__ q,
@@ -1366,8 +1370,9 @@ __global__ __launch_bounds__(kThreads) void oal_bwd_dw_intra(int T_len, int C, i
                                                               const float *__restrict__ gv, const float *__restrict__ gd,
                                                               float *__restrict__ dwp) {
     constexpr int NFP = 2176, NFT = NFP / 16;      // features padded to 136 tiles of 16
-    __shared__ __align__(16) float ta[64 * 68];   // g tile, then the query tile
-    __shared__ __align__(16) float tb[64 * 68];   // v tile, then the key tile
+    constexpr int NBP = sizeof(T) == 2 ? 2 : 3;    // parts of psi_f(k)
+    __shared__ __align__(16) float ta[65 * 68];   // g tile [query][col], then the query tile [dim][query]
+    __shared__ __align__(16) float tb[65 * 68];   // v tile [key][col], then the key tile [dim][key]
     __shared__ __align__(16) float dk[64 * 68];   // dkappa tile
     __shared__ float dwl[NFP];                     // dw of this (chunk, head)
     __shared__ unsigned short fdl[NFP];            // dims of feature f: a | b << 8 (64 reads the 1)
@@ -1388,6 +1393,22 @@ __global__ __launch_bounds__(kThreads) void oal_bwd_dw_intra(int T_len, int C, i
         fdl[f] = (unsigned short)(fa | (fb << 8));
         dwl[f] = 0.0f;
     }
+    // transposed staging of 64 tokens (zero past T): thread's share tokens r0 .. r0 + 3, dims
+    // dc .. dc + 3; row 64 = 1
+    const int r0 = 4 * (tid & 15), dc = 4 * (tid >> 4);
+    auto stage_t = [&](float *dst, const T *src, size_t row0, int t0) {
+        float x[4][4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) x[u][j] = 0.0f;
+            if (t0 + r0 + u < T_len) oal_ld4(src + (row0 + t0 + r0 + u) * OAL_D + dc, x[u]);
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            *reinterpret_cast<float4 *>(dst + (dc + j) * 68 + r0) = make_float4(x[0][j], x[1][j], x[2][j], x[3][j]);
+        if (tid < 64) dst[OAL_D * 68 + tid] = 1.0f;
+    };
     for (int qt = 0; qt < tpc; ++qt) {
         const int q0 = c * C + qt * 64;
         if (q0 >= T_len) break;
@@ -1412,37 +1433,71 @@ __global__ __launch_bounds__(kThreads) void oal_bwd_dw_intra(int T_len, int C, i
                 dk[i * 68 + j] = x;
             }
             __syncthreads();
-            stage_rows(ta, 68, q, qrow, q0, T_len, 1.0f);
-            stage_rows(tb, 68, k, krow, k0, T_len, 1.0f);
+            stage_t(ta, q, qrow, q0);
+            stage_t(tb, k, krow, k0);
             __syncthreads();
-            float A[4][16];                        // dkappa[16 it + lr][4 s + kg]
+            oal_bf16x8 A[4][2][3];                 // dkappa[16 it + lr][32 ks + 8 kg + e], three parts
 #pragma unroll
             for (int it = 0; it < 4; ++it)
 #pragma unroll
-                for (int st = 0; st < 16; ++st) A[it][st] = dk[(16 * it + lr) * 68 + 4 * st + kg];
+                for (int ks = 0; ks < 2; ++ks) {
+                    const float *src = dk + (16 * it + lr) * 68 + 32 * ks + 8 * kg;
+                    const float4 x0 = *reinterpret_cast<const float4 *>(src);
+                    const float4 x1 = *reinterpret_cast<const float4 *>(src + 4);
+                    const float xs[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        __bf16 p0, p1, p2;
+                        split3(xs[e], p0, p1, p2);
+                        A[it][ks][0][e] = p0;
+                        A[it][ks][1][e] = p1;
+                        A[it][ks][2][e] = p2;
+                    }
+                }
             for (int ft = w; ft < NFT; ft += 4) {
                 const int fB = 16 * ft + lr;                         // B operand feature of this lane
                 const unsigned short abB = fdl[fB];
+                const int fa = abB & 0xff, fb = abB >> 8;
                 oal_f32x4 D[4];
 #pragma unroll
                 for (int it = 0; it < 4; ++it) D[it] = oal_splat(0.0f);
 #pragma unroll
-                for (int st = 0; st < 16; ++st) {
-                    const float *kr = tb + (4 * st + kg) * 68;
-                    const float bpsi = kr[abB & 0xff] * kr[abB >> 8];
+                for (int ks = 0; ks < 2; ++ks) {
+                    const float *ka = tb + fa * 68 + 32 * ks + 8 * kg, *kb = tb + fb * 68 + 32 * ks + 8 * kg;
+                    const float4 a0 = *reinterpret_cast<const float4 *>(ka), a1 = *reinterpret_cast<const float4 *>(ka + 4);
+                    const float4 b0 = *reinterpret_cast<const float4 *>(kb), b1 = *reinterpret_cast<const float4 *>(kb + 4);
+                    const float ps[8] = {a0.x * b0.x, a0.y * b0.y, a0.z * b0.z, a0.w * b0.w,
+                                         a1.x * b1.x, a1.y * b1.y, a1.z * b1.z, a1.w * b1.w};
+                    oal_bf16x8 B[3];
 #pragma unroll
-                    for (int it = 0; it < 4; ++it)
-                        D[it] = __builtin_amdgcn_mfma_f32_16x16x4f32(A[it][st], bpsi, D[it], 0, 0, 0);
+                    for (int e = 0; e < 8; ++e) {
+                        __bf16 p0, p1, p2;
+                        split3(ps[e], p0, p1, p2);
+                        B[0][e] = p0;
+                        B[1][e] = p1;
+                        B[2][e] = p2;
+                    }
+                    // the terms A_i B_j with i + j <= 2, small ones first
+#pragma unroll
+                    for (int ord = 2; ord >= 0; --ord)
+#pragma unroll
+                        for (int jb = 0; jb < NBP; ++jb) {
+                            const int ia = ord - jb;
+                            if (ia < 0) continue;
+#pragma unroll
+                            for (int it = 0; it < 4; ++it)
+                                D[it] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[it][ks][ia], B[jb], D[it], 0, 0, 0);
+                        }
                 }
                 // D[it][jj]: query 16 it + 4 kg + jj, feature 16 ft + lr
                 float sum = 0.0f;
 #pragma unroll
-                for (int it = 0; it < 4; ++it)
-#pragma unroll
-                    for (int jj = 0; jj < 4; ++jj) {
-                        const float *qi = ta + (16 * it + 4 * kg + jj) * 68;
-                        sum += qi[abB & 0xff] * qi[abB >> 8] * D[it][jj];
-                    }
+                for (int it = 0; it < 4; ++it) {
+                    const float4 qa = *reinterpret_cast<const float4 *>(ta + fa * 68 + 16 * it + 4 * kg);
+                    const float4 qb = *reinterpret_cast<const float4 *>(ta + fb * 68 + 16 * it + 4 * kg);
+                    sum += qa.x * qb.x * D[it][0] + qa.y * qb.y * D[it][1] + qa.z * qb.z * D[it][2] +
+                           qa.w * qb.w * D[it][3];
+                }
                 sum += __shfl_xor(sum, 16);                          // the four query groups
                 sum += __shfl_xor(sum, 32);
                 if (kg == 0) dwl[fB] += sum;                         // feature tile of this wave alone
