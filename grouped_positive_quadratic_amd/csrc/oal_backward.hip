@@ -196,6 +196,50 @@ __device__ inline float row16_sum(float x) {
     return x;
 }
 
+
+// Eight consecutive fp32 values (16-byte aligned, LDS) in N bf16 parts (split3; N = 1 when the
+// values are exact in bf16).
+template <int N>
+__device__ inline void split_frag(const float *p, oal_bf16x8 (&out)[3]) {
+    const float4 a = *reinterpret_cast<const float4 *>(p), b = *reinterpret_cast<const float4 *>(p + 4);
+    const float x[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        __bf16 x0, x1, x2;
+        split3(x[e], x0, x1, x2);
+        out[0][e] = x0;
+        if constexpr (N > 1) out[1][e] = x1;
+        if constexpr (N > 2) out[2][e] = x2;
+    }
+}
+
+// P[r][c] = sum_{k < 64} X[r][k] Y[c][k] for the wave's 16 rows of X (this lane's row lr) and
+// the 64 rows of Y (LDS tiles, row stride 68), on bf16 MFMA with NX and NY parts per operand
+// (the terms of order <= 2). P[ct][jj]: row 4 kg + jj, column 16 ct + lr.
+template <int NX, int NY>
+__device__ inline void mfma_xyt(const float *X, const float *Y, int lr, int kg, oal_f32x4 (&P)[4]) {
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct) P[ct] = oal_splat(0.0f);
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+        oal_bf16x8 a[3];
+        split_frag<NX>(X + lr * 68 + 32 * ks + 8 * kg, a);
+#pragma unroll
+        for (int ct = 0; ct < 4; ++ct) {
+            oal_bf16x8 bq[3];
+            split_frag<NY>(Y + (16 * ct + lr) * 68 + 32 * ks + 8 * kg, bq);
+#pragma unroll
+            for (int ord = 2; ord >= 0; --ord)
+#pragma unroll
+                for (int i = 0; i < NX; ++i) {
+                    const int j = ord - i;
+                    if (j < 0 || j >= NY) continue;
+                    P[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], bq[j], P[ct], 0, 0, 0);
+                }
+        }
+    }
+}
+
 // Four consecutive elements as fp32 (8-byte aligned for bf16, 16-byte for fp32).
 __device__ inline void oal_ld4(const float *p, float (&o)[4]) {
     const float4 t = *reinterpret_cast<const float4 *>(p);
@@ -1047,19 +1091,16 @@ __global__ __launch_bounds__(kThreads) void oal_bwd_dq_intra_mfma(int T_len, int
         stage_rows(vs, 68, v, krow, k0, T_len, 1.0f);
         stage_rows(ks, 68, k, krow, k0, T_len, 0.0f);
         __syncthreads();
-        for (int e = tid; e < 64 * 64; e += kThreads) {
-            const int i = e >> 6, j = e & 63;
-            float x = 0.0f;
-            if (kt < qt || j <= i) {
-                const float *gi = gs + i * 68, *vj = vs + j * 68;
-                float x1 = 0.0f;
-                for (int cc = 0; cc < 64; cc += 2) {
-                    x += gi[cc] * vj[cc];
-                    x1 += gi[cc + 1] * vj[cc + 1];
+        {                                          // dkappa = G V^T + g64 on the wave's 16 queries
+            oal_f32x4 P[4];
+            mfma_xyt<3, sizeof(T) == 2 ? 1 : 3>(gs + 16 * w * 68, vs, lr, kg, P);
+#pragma unroll
+            for (int jt = 0; jt < 4; ++jt)
+#pragma unroll
+                for (int jj = 0; jj < 4; ++jj) {
+                    const int i = 16 * w + 4 * kg + jj, j = 16 * jt + lr;
+                    dks[i * 68 + j] = (kt < qt || j <= i) ? P[jt][jj] + gs[i * 68 + 64] : 0.0f;
                 }
-                x += x1 + gi[64];
-            }
-            dks[i * 68 + j] = x;
         }
         __syncthreads();                           // dkappa ready; gs and vs are free
         stage_rows(qs, 68, q, qrow, t0, T_len, 0.0f);
@@ -1229,25 +1270,21 @@ __global__ __launch_bounds__(kThreads) void oal_bwd_dkv_intra_mfma(int T_len, in
         stage_rows(es, 68, v, krow, t0, T_len, 1.0f);
         __syncthreads();
         // dkappa[i][j] = g_i . [v_j; 1] on the pairs j <= i, in the accumulator layout:
-        // dkr[it][jj] for key j = 16 w + 4 kg + jj, query i = 16 it + lr
+        // dkr[it][jj] for key j = 16 w + 4 kg + jj, query i = 16 it + lr (V G^T on MFMA)
         float dkr[4][4];
+        {
+            oal_f32x4 P[4];
+            mfma_xyt<sizeof(T) == 2 ? 1 : 3, 3>(es + 16 * w * 68, gs, lr, kg, P);
 #pragma unroll
-        for (int it = 0; it < 4; ++it)
+            for (int it = 0; it < 4; ++it) {
+                const float g64 = gs[(16 * it + lr) * 68 + 64];
 #pragma unroll
-            for (int jj = 0; jj < 4; ++jj) {
-                const int j = 16 * w + 4 * kg + jj, i = 16 * it + lr;
-                float x = 0.0f;
-                if (kt < qt || j <= i) {
-                    const float *gi = gs + i * 68, *vj = es + j * 68;
-                    float x1 = 0.0f;
-                    for (int cc = 0; cc < 64; cc += 2) {
-                        x += gi[cc] * vj[cc];
-                        x1 += gi[cc + 1] * vj[cc + 1];
-                    }
-                    x += x1 + gi[64];
+                for (int jj = 0; jj < 4; ++jj) {
+                    const int j = 16 * w + 4 * kg + jj, i = 16 * it + lr;
+                    dkr[it][jj] = (kt < qt || j <= i) ? P[it][jj] + g64 : 0.0f;
                 }
-                dkr[it][jj] = x;
             }
+        }
         __syncthreads();                           // the v tile is consumed
         oal_f32x4 kap[4];                          // sum_m Z_m^2: key 16 w + 4 kg + jj, query 16 it + lr
 #pragma unroll
@@ -1418,19 +1455,16 @@ __global__ __launch_bounds__(kThreads) void oal_bwd_dw_intra(int T_len, int C, i
             stage_g(ta, gv, gd, qrow, q0, T_len);
             stage_rows(tb, 68, v, krow, k0, T_len, 1.0f);
             __syncthreads();
-            for (int e = tid; e < 64 * 64; e += kThreads) {
-                const int i = e >> 6, j = e & 63;
-                float x = 0.0f;
-                if (kt < qt || j <= i) {
-                    const float *gi = ta + i * 68, *vj = tb + j * 68;
-                    float x1 = 0.0f;
-                    for (int cc = 0; cc < 64; cc += 2) {
-                        x += gi[cc] * vj[cc];
-                        x1 += gi[cc + 1] * vj[cc + 1];
+            {                                      // dkappa = G V^T + g64 on the wave's 16 queries
+                oal_f32x4 P[4];
+                mfma_xyt<3, sizeof(T) == 2 ? 1 : 3>(ta + 16 * w * 68, tb, lr, kg, P);
+#pragma unroll
+                for (int jt = 0; jt < 4; ++jt)
+#pragma unroll
+                    for (int jj = 0; jj < 4; ++jj) {
+                        const int i = 16 * w + 4 * kg + jj, j = 16 * jt + lr;
+                        dk[i * 68 + j] = (kt < qt || j <= i) ? P[jt][jj] + ta[i * 68 + 64] : 0.0f;
                     }
-                    x += x1 + gi[64];
-                }
-                dk[i * 68 + j] = x;
             }
             __syncthreads();
             stage_t(ta, q, qrow, q0);
