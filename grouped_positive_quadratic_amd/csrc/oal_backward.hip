@@ -46,6 +46,7 @@
 // and oal_bwd_dw_sum, oal_bwd_coef (after 6): dL, deps.
 #include <hip/hip_runtime.h>
 
+#include <cstddef>
 #include <type_traits>
 
 #include "oal_device.h"
@@ -239,6 +240,52 @@ __device__ inline void mfma_xyt(const float *X, const float *Y, int lr, int kg, 
         }
     }
 }
+
+// A z-term tile Z = (X o s) Y^T + z0 for the wave's 16 rows of X (this lane's row lr) and the
+// 64 rows of Y (LDS tiles, row stride 68), s = a row of Lz (64 floats, 16-byte aligned), on
+// bf16 MFMA: X o s in three parts, Y in NY parts (the terms of order <= 2). Z[ct][jj]: row
+// 4 kg + jj, column 16 ct + lr.
+template <int NY>
+__device__ inline void mfma_zterm(const float *X, const float *sc, const float *Y, float z0, int lr, int kg,
+                                  oal_f32x4 (&Z)[4]) {
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct) Z[ct] = oal_splat(0.0f);
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+        const int k0 = 32 * ks + 8 * kg;
+        const float4 x0 = *reinterpret_cast<const float4 *>(X + lr * 68 + k0);
+        const float4 x1 = *reinterpret_cast<const float4 *>(X + lr * 68 + k0 + 4);
+        const float4 s0 = *reinterpret_cast<const float4 *>(sc + k0);
+        const float4 s1 = *reinterpret_cast<const float4 *>(sc + k0 + 4);
+        const float xs[8] = {x0.x * s0.x, x0.y * s0.y, x0.z * s0.z, x0.w * s0.w,
+                             x1.x * s1.x, x1.y * s1.y, x1.z * s1.z, x1.w * s1.w};
+        oal_bf16x8 a[3];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            __bf16 p0, p1, p2;
+            split3(xs[e], p0, p1, p2);
+            a[0][e] = p0;
+            a[1][e] = p1;
+            a[2][e] = p2;
+        }
+#pragma unroll
+        for (int ct = 0; ct < 4; ++ct) {
+            oal_bf16x8 bq[3];
+            split_frag<NY>(Y + (16 * ct + lr) * 68 + k0, bq);
+#pragma unroll
+            for (int ord = 2; ord >= 0; --ord)
+#pragma unroll
+                for (int j = 0; j < NY; ++j) {
+                    const int i = ord - j;
+                    if (i < 0) continue;
+                    Z[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], bq[j], Z[ct], 0, 0, 0);
+                }
+        }
+    }
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct) Z[ct] += oal_splat(z0);
+}
+static_assert(offsetof(OalHeadDev, Lz) % 16 == 0, "Lz rows are read as float4");
 
 // Four consecutive elements as fp32 (8-byte aligned for bf16, 16-byte for fp32).
 __device__ inline void oal_ld4(const float *p, float (&o)[4]) {
@@ -535,7 +582,7 @@ __global__ __launch_bounds__(kThreads) void oal_bwd_readout_g(int s0, int T_len,
                                                                const unsigned char *__restrict__ params,
                                                                const float *__restrict__ st, float *__restrict__ gv,
                                                                float *__restrict__ gd, __bf16 *__restrict__ gpl) {
-    __shared__ float xq[64 * 65];
+    __shared__ __align__(16) float xq[64 * 68];
     __shared__ __align__(16) float ks[64 * 68];    // keys; before them the coefficient tables
     // values (vs) and kappa / u (uin); before them the split block of S_c across both
     __shared__ __align__(16) float vu[64 * 80 + 64 * 68];
@@ -550,7 +597,7 @@ __global__ __launch_bounds__(kThreads) void oal_bwd_readout_g(int s0, int T_len,
     const OalHeadDev *hd = bwd_head(params, h);
     const int G = hd->G;
     const size_t qrow = ((size_t)b * n_q_heads + h) * T_len, krow = ((size_t)b * n_kv_heads + kv) * T_len;
-    stage_rows(xq, 65, q, qrow, t0, T_len, 1.0f);
+    stage_rows(xq, 68, q, qrow, t0, T_len, 1.0f);
     constexpr int NFP = 2176;                      // features padded to 34 blocks of 64
     float *wdl = ks;                               // wdec_h[f], zero past 2145
     unsigned short *fdl = reinterpret_cast<unsigned short *>(ks + NFP);   // dims of f: a | b << 8
@@ -570,18 +617,19 @@ __global__ __launch_bounds__(kThreads) void oal_bwd_readout_g(int s0, int T_len,
     __syncthreads();
 
     const int lr = threadIdx.x & 15, kg = (threadIdx.x >> 4) & 3;       // MFMA lane roles
-    const float *xa = xq + (16 * w + lr) * 65;                         // A row: query 16 w + lr
+    const float *xa = xq + (16 * w + lr) * 68;                         // A row: query 16 w + lr
     oal_f32x4 D[5];                                 // u: query 16 w + 4 kg + j, column 16 ct + lr
 #pragma unroll
     for (int ct = 0; ct < 5; ++ct) D[ct] = oal_splat(0.0f);
     if (c > 0 || s0) {                             // S_0 = 0 without an incoming state
-        // U = phi(Q) S_c on bf16 MFMA (16x16x32) with both operands split in three parts (the six
-        // products of split3): K = the features in blocks of 64 (two K-steps), N = the 64 value
-        // columns in four tiles; the normaliser column 64 on the VALU. A operand: lane (lr, kg)
-        // holds phi_f(q) of query 16 w + lr for the features 32 ks + 8 kg + e of the block,
-        // formed and split in registers. B operand: the block of S_c staged in LDS transposed,
-        // plane row = value column, 64 features (stride PS), so that a lane's 8 features are one
-        // 16-byte read.
+        // U = phi(Q) S_c = mono(Q) (wdec_h o S_c) on bf16 MFMA (16x16x32) with split operands
+        // (the terms of order <= 2 of split3; mono_f(q) = q_r q_t is exact in two bf16 parts for
+        // bf16 inputs): K = the features in blocks of 64 (two K-steps), N = the 64 value columns
+        // in four tiles; the normaliser column 64 on the VALU. A operand: lane (lr, kg) holds
+        // mono_f(q) of query 16 w + lr for the features 32 ks + 8 kg + e of the block, formed
+        // and split in registers. B operand: the block of wdec_h[f] S_c[f] staged in LDS
+        // transposed, plane row = value column, 64 features (stride PS), so that a lane's 8
+        // features are one 16-byte read.
         constexpr int PS = 72;
         __bf16 *pb = reinterpret_cast<__bf16 *>(vs);              // 3 planes x 64 columns x PS
         float *sdb = vs + 3 * 64 * PS / 2;                         // column 64 of the block
@@ -600,16 +648,20 @@ __global__ __launch_bounds__(kThreads) void oal_bwd_readout_g(int s0, int T_len,
             }
             if (threadIdx.x < 64) pre64 = f0 + (int)threadIdx.x < OAL_NFEAT ? Sd[f0 + threadIdx.x] : 0.0f;
         };
+        constexpr int NQP = sizeof(T) == 2 ? 2 : 3;    // parts of mono_f(q)
         float dpart = 0.0f;                        // normaliser of query 16 w + lr, the lane's features
         load_block(0);
         for (int f0 = 0; f0 < NFP; f0 += 64) {
             __syncthreads();                       // the previous block is consumed
+            float wf[4];                           // wdec_h of the thread's four features
+#pragma unroll
+            for (int u = 0; u < 4; ++u) wf[u] = wdl[f0 + sf + u];
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 oal_bf16x4 p0, p1, p2;
 #pragma unroll
                 for (int u = 0; u < 4; ++u) {
-                    const float x = j == 0 ? pre[u].x : j == 1 ? pre[u].y : j == 2 ? pre[u].z : pre[u].w;
+                    const float x = wf[u] * (j == 0 ? pre[u].x : j == 1 ? pre[u].y : j == 2 ? pre[u].z : pre[u].w);
                     __bf16 x0, x1, x2;
                     split3(x, x0, x1, x2);
                     p0[u] = x0;
@@ -621,7 +673,7 @@ __global__ __launch_bounds__(kThreads) void oal_bwd_readout_g(int s0, int T_len,
                 *reinterpret_cast<oal_bf16x4 *>(pb + 64 * PS + o) = p1;
                 *reinterpret_cast<oal_bf16x4 *>(pb + 2 * 64 * PS + o) = p2;
             }
-            if (threadIdx.x < 64) sdb[threadIdx.x] = pre64;
+            if (threadIdx.x < 64) sdb[threadIdx.x] = wdl[f0 + threadIdx.x] * pre64;
             __syncthreads();
             if (f0 + 64 < NFP) load_block(f0 + 64);
             oal_pin_loads();
@@ -633,7 +685,7 @@ __global__ __launch_bounds__(kThreads) void oal_bwd_readout_g(int s0, int T_len,
                 for (int e = 0; e < 8; ++e) {
                     const int f = f0 + fl + e;
                     const unsigned short ab = fdl[f];
-                    const float ph = wdl[f] * xa[ab & 0xff] * xa[ab >> 8];
+                    const float ph = xa[ab & 0xff] * xa[ab >> 8];
                     dpart += ph * sdb[fl + e];
                     __bf16 x0, x1, x2;
                     split3(ph, x0, x1, x2);
@@ -649,11 +701,13 @@ __global__ __launch_bounds__(kThreads) void oal_bwd_readout_g(int s0, int T_len,
                     b1[ct] = *reinterpret_cast<const oal_bf16x8 *>(pb + 64 * PS + o);
                     b2[ct] = *reinterpret_cast<const oal_bf16x8 *>(pb + 2 * 64 * PS + o);
                 }
-                // small terms first
+                // small terms first (a2 = 0 for bf16 inputs)
 #pragma unroll
                 for (int ct = 0; ct < 4; ++ct) D[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, b1[ct], D[ct], 0, 0, 0);
+                if constexpr (NQP > 2) {
 #pragma unroll
-                for (int ct = 0; ct < 4; ++ct) D[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a2, b0[ct], D[ct], 0, 0, 0);
+                    for (int ct = 0; ct < 4; ++ct) D[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a2, b0[ct], D[ct], 0, 0, 0);
+                }
 #pragma unroll
                 for (int ct = 0; ct < 4; ++ct) D[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, b2[ct], D[ct], 0, 0, 0);
 #pragma unroll
@@ -691,18 +745,8 @@ __global__ __launch_bounds__(kThreads) void oal_bwd_readout_g(int s0, int T_len,
 #pragma unroll
             for (int jt = 0; jt < 4; ++jt) kap[jt] = oal_splat(0.0f);
             for (int m = 0; m <= G; ++m) {
-                const float *lzm = Lz + m * OAL_D;
                 oal_f32x4 Z[4];
-#pragma unroll
-                for (int jt = 0; jt < 4; ++jt) Z[jt] = oal_splat(m == 0 ? L00 : 0.0f);
-#pragma unroll 4
-                for (int st = 0; st < 16; ++st) {
-                    const int r = 4 * st + kg;
-                    const float a = xa[r] * lzm[r];
-#pragma unroll
-                    for (int jt = 0; jt < 4; ++jt)
-                        Z[jt] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, ks[(16 * jt + lr) * 68 + r], Z[jt], 0, 0, 0);
-                }
+                mfma_zterm<sizeof(T) == 2 ? 1 : 3>(xq + 16 * w * 68, Lz + m * OAL_D, ks, m == 0 ? L00 : 0.0f, lr, kg, Z);
 #pragma unroll
                 for (int jt = 0; jt < 4; ++jt)
 #pragma unroll
@@ -1110,16 +1154,7 @@ __global__ __launch_bounds__(kThreads) void oal_bwd_dq_intra_mfma(int T_len, int
             const float *lzm = Lz + m * OAL_D;
             // Z_m for the wave's 16 queries x 64 keys
             oal_f32x4 Z[4];
-#pragma unroll
-            for (int jt = 0; jt < 4; ++jt) Z[jt] = oal_splat(m == 0 ? L00 : 0.0f);
-#pragma unroll 4
-            for (int st = 0; st < 16; ++st) {
-                const int r = 4 * st + kg;
-                const float a = qs[(16 * w + lr) * 68 + r] * lzm[r];
-#pragma unroll
-                for (int jt = 0; jt < 4; ++jt)
-                    Z[jt] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, ks[(16 * jt + lr) * 68 + r], Z[jt], 0, 0, 0);
-            }
+            mfma_zterm<sizeof(T) == 2 ? 1 : 3>(qs + 16 * w * 68, lzm, ks, m == 0 ? L00 : 0.0f, lr, kg, Z);
             // E_m = dkappa o Z_m into the wave's rows of es (row = query, column = key)
 #pragma unroll
             for (int jt = 0; jt < 4; ++jt)
@@ -1292,16 +1327,7 @@ __global__ __launch_bounds__(kThreads) void oal_bwd_dkv_intra_mfma(int T_len, in
         for (int m = 0; m <= G; ++m) {
             const float *lzm = Lz + m * OAL_D;
             oal_f32x4 Z[4];
-#pragma unroll
-            for (int it = 0; it < 4; ++it) Z[it] = oal_splat(m == 0 ? L00 : 0.0f);
-#pragma unroll 4
-            for (int st = 0; st < 16; ++st) {
-                const int r = 4 * st + kg;
-                const float a = ks[(16 * w + lr) * 68 + r] * lzm[r];
-#pragma unroll
-                for (int it = 0; it < 4; ++it)
-                    Z[it] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, qs[(16 * it + lr) * 68 + r], Z[it], 0, 0, 0);
-            }
+            mfma_zterm<sizeof(T) == 2 ? 1 : 3>(ks + 16 * w * 68, lzm, qs, m == 0 ? L00 : 0.0f, lr, kg, Z);
 #pragma unroll
             for (int it = 0; it < 4; ++it)
 #pragma unroll
