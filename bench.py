@@ -22,7 +22,8 @@ one) as `roofline.readout`; `achievable_peaks` holds the rates of a matrix-core 
 streaming copy measured on this device; `decode` holds decode tokens/s and the decode kernel
 against HBM peak (`decode.hbm_512seq` for the state that does not fit in the cache);
 `contribution` the chi kernel against HBM peak; `backward` the prefill backward (dq, dk, dv)
-of the headline workload against the fp32 MFMA peak; `cpu_baseline` is the fp64 CPU oracle on
+of the headline workload against the fp32 MFMA peak (its fp32-accurate products run as six
+bf16 MFMA products, whose ceiling is also given); `cpu_baseline` is the fp64 CPU oracle on
 the full prefill batch, timed on this host, with the other workloads under
 `cpu_baseline.other_workloads`.
 """
@@ -378,12 +379,17 @@ def main():
         bach = bflops / (bms * 1e-3) / 1e12
         out["backward"] = {
             "workload": f"prefill backward (dq, dk, dv, dL, deps) from an empty prefix, B={Bb} T={Tb} "
-                        f"{Hqb}q/{Hkvb}kv, bf16 inputs, fp32 arithmetic, chunk {Cb}",
+                        f"{Hqb}q/{Hkvb}kv, bf16 inputs, fp32-accurate arithmetic, chunk {Cb}",
             "value": Bb * Tb / (bms * 1e-3), "unit": "tokens/s", "ms_per_call": bms, "calls": reps,
-            "roofline": {"bound": "mfma", "kernel": "the call's fp32 MFMA launches together",
+            "roofline": {"bound": "mfma",
+                         "kernel": "the call's launches together (state contractions and intra-chunk "
+                                   "products on bf16 MFMA with three-part split fp32 operands)",
                          "achieved": bach, "peak": PEAK_FP32_TFLOPS, "unit": "TFLOP/s",
                          "frac": bach / PEAK_FP32_TFLOPS, "traffic": None,
-                         "algorithmic_flops_per_call": bflops}}
+                         "algorithmic_flops_per_call": bflops,
+                         # six bf16 products per fp32-accurate product: the split ceiling
+                         "split_bf16_peak": PEAK_BF16_TFLOPS / 6,
+                         "frac_of_split_peak": bach / (PEAK_BF16_TFLOPS / 6)}}
         del bq, bk, bv, bdy, bws, bdq, bdk, bdv, bdL, bde, bparams
         torch.cuda.empty_cache()
 
