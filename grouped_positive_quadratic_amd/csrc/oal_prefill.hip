@@ -1023,9 +1023,9 @@ __global__ __launch_bounds__(256, 2) void oal_readout(
         };
         // bf16: p_r of the next main K-step (and p_t of its t block) are read from LDS at the
         // end of the step before, so the step finds them in registers (readout 33.8 -> 33.2 us
-        // at B = 1 x 4096); fp32 reads them at the start of the step (the early copies would
-        // not fit its registers)
-        constexpr bool kAhead = sizeof(T) == 2;
+        // at B = 1 x 4096); fp32 and the general blob read them at the start of the step (the
+        // early copies do not fit fp32's registers, and cost the general blob 53 -> 68 us)
+        constexpr bool kAhead = sizeof(T) == 2 && !GEN;
         float prv[NH];
         auto load_prv = [&]() {
             const int r = 4 * (2 * j + par) + g;
