@@ -171,6 +171,28 @@ __device__ inline void stage_g(float *dst, const float *gv, const float *gd, siz
 }
 
 // ---------------------------------------------------------------------------------------------
+// Stage 64 rows (tokens t0 .. t0 + 63, zero past T) of a [*, T, 64] tensor into LDS transposed,
+// dst[dim * 68 + token] (dims 0 .. 63), as fp32. Thread's share: tokens 4 (tid % 16) .. + 3,
+// dims 4 (tid / 16) .. + 3 (16-byte writes).
+template <typename T>
+__device__ inline void stage_cols(float *dst, const T *src, size_t row0, int t0, int T_len) {
+    const int r0 = 4 * (threadIdx.x & 15), dc = 4 * (threadIdx.x >> 4);
+    float x[4][4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) x[u][j] = 0.0f;
+        if (t0 + r0 + u < T_len) {
+            const T *p = src + (row0 + t0 + r0 + u) * OAL_D + dc;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) x[u][j] = oal_ld(p + j);
+        }
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+        *reinterpret_cast<float4 *>(dst + (dc + j) * 68 + r0) = make_float4(x[0][j], x[1][j], x[2][j], x[3][j]);
+}
+
 // fp32 x = x0 + x1 + x2 (+ a remainder below 2^-24 |x|) in bf16 parts, each difference exact in
 // fp32: x0 = bf16(x), x1 = bf16(x - x0), x2 = bf16(x - x0 - x1). A product x y is taken as the
 // six terms x_i y_j with i + j <= 2 (Henry, Tang and Heinecke, "Leveraging the bfloat16
@@ -729,9 +751,10 @@ __global__ __launch_bounds__(kThreads) void oal_bwd_readout_g(int s0, int T_len,
         }
     }
 
-    // pairs inside the chunk (fp32 MFMA): per key tile and z-term m, Z_m = (Q o Lz[m]) K^T
+    // pairs inside the chunk (split-bf16 MFMA): per key tile and z-term m, Z_m = (Q o Lz[m]) K^T
     // (+ L00 for m = 0); kappa = eps + sum_m Z_m^2 on the pairs that see each other; then
-    // D += kappa [V; 1]. kappa passes through uin (the wave's own rows) to be an A operand.
+    // D += kappa V (V staged transposed) and the normaliser column += the row sums of kappa.
+    // kappa passes through uin (the wave's own rows) to be an A operand.
     {
         const float *Lz = hd->Lz;
         const float L00 = hd->L00, eps = hd->eps;
@@ -739,7 +762,7 @@ __global__ __launch_bounds__(kThreads) void oal_bwd_readout_g(int s0, int T_len,
             const int k0 = c * C + kt * 64;
             __syncthreads();
             stage_rows(ks, 68, k, krow, k0, T_len, 0.0f);
-            stage_rows(vs, 68, v, krow, k0, T_len, 1.0f);
+            stage_cols(vs, v, krow, k0, T_len);    // [column][key]
             __syncthreads();
             oal_f32x4 kap[4];                       // query 16 w + 4 kg + jj, key 16 jt + lr
 #pragma unroll
@@ -752,26 +775,28 @@ __global__ __launch_bounds__(kThreads) void oal_bwd_readout_g(int s0, int T_len,
 #pragma unroll
                     for (int jj = 0; jj < 4; ++jj) kap[jt][jj] += Z[jt][jj] * Z[jt][jj];
             }
+            float ksum[4] = {0.0f, 0.0f, 0.0f, 0.0f};   // row sums of kappa: query 16 w + 4 kg + jj
 #pragma unroll
             for (int jt = 0; jt < 4; ++jt)
 #pragma unroll
                 for (int jj = 0; jj < 4; ++jj) {
                     const int il = 16 * w + 4 * kg + jj, jl = 16 * jt + lr;
-                    uin[il * 68 + jl] = sees(kt, qt, jl, il) ? eps + kap[jt][jj] : 0.0f;
+                    const float x = sees(kt, qt, jl, il) ? eps + kap[jt][jj] : 0.0f;
+                    uin[il * 68 + jl] = x;
+                    ksum[jj] += x;
                 }
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) {
+                const float sj = row16_sum(ksum[jj]);
+                if (lr == 0) D[4][jj] += sj;
+            }
             __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");   // the wave reads its own rows
             __builtin_amdgcn_s_barrier();
             __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-#pragma unroll 4
-            for (int st = 0; st < 16; ++st) {
-                const int j = 4 * st + kg;
-                const float a = uin[(16 * w + lr) * 68 + j];
-                const float *vr = vs + j * 68;
+            oal_f32x4 P[4];
+            mfma_xyt<3, sizeof(T) == 2 ? 1 : 3>(uin + 16 * w * 68, vs, lr, kg, P);
 #pragma unroll
-                for (int ct = 0; ct < 4; ++ct)
-                    D[ct] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, vr[16 * ct + lr], D[ct], 0, 0, 0);
-                D[4] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, lr == 0 ? vr[64] : 0.0f, D[4], 0, 0, 0);
-            }
+            for (int ct = 0; ct < 4; ++ct) D[ct] += P[ct];
         }
     }
     // u into uin (row = query, columns 0..64), then the epilogue of wave 0
@@ -1097,7 +1122,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
 }
 
 // 4b. dq_i += sum_{j <= i in the chunk} dkappa_ij dkappa_ij/dq_i, dkappa_ij = g_i . [v_j; 1], on
-//     fp32 MFMA (16x16x4). dkappa/dq_ir = 2 k_jr sum_m z_m Lz[m][r] with
+//     split-bf16 MFMA (mfma_xyt, mfma_zterm). dkappa/dq_ir = 2 k_jr sum_m z_m Lz[m][r] with
 //     z_m = (Q diag(Lz[m]) K^T)_ij (+ L00 for m = 0), so per (query tile, key tile) pair and
 //     z-term m: Z_m = (Q o Lz[m]) K^T, E_m = dkappa o Z_m (the dkappa tile is masked to
 //     j <= i), dq += 2 Lz[m] o (E_m K) -- two 64 x 64 x 64 products. Wave w owns the queries
@@ -1110,8 +1135,8 @@ __global__ __launch_bounds__(kThreads) void oal_bwd_dq_intra_mfma(int T_len, int
                                                                    const unsigned char *__restrict__ params,
                                                                    const float *__restrict__ gv,
                                                                    const float *__restrict__ gd, float *__restrict__ dq) {
-    __shared__ __align__(16) float ks[64 * 68];
-    __shared__ __align__(16) float dks[64 * 68];   // dkappa tile
+    __shared__ __align__(16) float ks[64 * 68];    // key tile [key][dim]
+    __shared__ __align__(16) float kts[64 * 68];   // key tile transposed [dim][key]
     __shared__ __align__(16) float gs[64 * 68];    // g tile, then E_m
     __shared__ __align__(16) float vs[64 * 68];    // v tile, then the query tile
     float *qs = vs;
@@ -1124,6 +1149,7 @@ __global__ __launch_bounds__(kThreads) void oal_bwd_dq_intra_mfma(int T_len, int
     const float L00 = hd->L00;
     const float *Lz = hd->Lz;
     const size_t qrow = ((size_t)b * n_q_heads + h) * T_len, krow = ((size_t)b * n_kv_heads + kv) * T_len;
+    constexpr int NK = sizeof(T) == 2 ? 1 : 3;     // parts of k (exact in bf16 for bf16 inputs)
     if (t0 >= T_len) return;                       // a tile past the sequence (uniform)
     oal_f32x4 acc[4];                              // dq: query 16 w + 4 kg + j, dim 16 rt + lr
 #pragma unroll
@@ -1134,19 +1160,23 @@ __global__ __launch_bounds__(kThreads) void oal_bwd_dq_intra_mfma(int T_len, int
         stage_g(gs, gv, gd, qrow, t0, T_len);
         stage_rows(vs, 68, v, krow, k0, T_len, 1.0f);
         stage_rows(ks, 68, k, krow, k0, T_len, 0.0f);
+        stage_cols(kts, k, krow, k0, T_len);
         __syncthreads();
-        {                                          // dkappa = G V^T + g64 on the wave's 16 queries
+        // dkappa = G V^T + g64 on the wave's 16 queries, masked, kept in registers in the
+        // accumulator layout of Z_m (query 16 w + 4 kg + jj, key 16 jt + lr)
+        oal_f32x4 dk[4];
+        {
             oal_f32x4 P[4];
-            mfma_xyt<3, sizeof(T) == 2 ? 1 : 3>(gs + 16 * w * 68, vs, lr, kg, P);
+            mfma_xyt<3, NK>(gs + 16 * w * 68, vs, lr, kg, P);
 #pragma unroll
             for (int jt = 0; jt < 4; ++jt)
 #pragma unroll
                 for (int jj = 0; jj < 4; ++jj) {
                     const int i = 16 * w + 4 * kg + jj, j = 16 * jt + lr;
-                    dks[i * 68 + j] = (kt < qt || j <= i) ? P[jt][jj] + gs[i * 68 + 64] : 0.0f;
+                    dk[jt][jj] = (kt < qt || j <= i) ? P[jt][jj] + gs[i * 68 + 64] : 0.0f;
                 }
         }
-        __syncthreads();                           // dkappa ready; gs and vs are free
+        __syncthreads();                           // gs and vs are free
         stage_rows(qs, 68, q, qrow, t0, T_len, 0.0f);
         __syncthreads();
         float *es = gs;
@@ -1154,30 +1184,19 @@ __global__ __launch_bounds__(kThreads) void oal_bwd_dq_intra_mfma(int T_len, int
             const float *lzm = Lz + m * OAL_D;
             // Z_m for the wave's 16 queries x 64 keys
             oal_f32x4 Z[4];
-            mfma_zterm<sizeof(T) == 2 ? 1 : 3>(qs + 16 * w * 68, lzm, ks, m == 0 ? L00 : 0.0f, lr, kg, Z);
+            mfma_zterm<NK>(qs + 16 * w * 68, lzm, ks, m == 0 ? L00 : 0.0f, lr, kg, Z);
             // E_m = dkappa o Z_m into the wave's rows of es (row = query, column = key)
 #pragma unroll
             for (int jt = 0; jt < 4; ++jt)
 #pragma unroll
-                for (int jj = 0; jj < 4; ++jj) {
-                    const int i = 16 * w + 4 * kg + jj, j = 16 * jt + lr;
-                    es[i * 68 + j] = dks[i * 68 + j] * Z[jt][jj];
-                }
+                for (int jj = 0; jj < 4; ++jj) es[(16 * w + 4 * kg + jj) * 68 + 16 * jt + lr] = dk[jt][jj] * Z[jt][jj];
             __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");   // the wave reads its own rows
             __builtin_amdgcn_s_barrier();
             __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-            // F = E_m K for the wave's 16 queries x 64 dims, then dq += 2 Lz[m][r] F
+            // F = E_m K for the wave's 16 queries x 64 dims (split bf16: E in three parts, K
+            // transposed), then dq += 2 Lz[m][r] F
             oal_f32x4 F[4];
-#pragma unroll
-            for (int rt = 0; rt < 4; ++rt) F[rt] = oal_splat(0.0f);
-#pragma unroll 4
-            for (int st = 0; st < 16; ++st) {
-                const int j = 4 * st + kg;
-                const float a = es[(16 * w + lr) * 68 + j];
-#pragma unroll
-                for (int rt = 0; rt < 4; ++rt)
-                    F[rt] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, ks[j * 68 + 16 * rt + lr], F[rt], 0, 0, 0);
-            }
+            mfma_xyt<3, NK>(es + 16 * w * 68, kts, lr, kg, F);
 #pragma unroll
             for (int rt = 0; rt < 4; ++rt) {
                 const float l2 = 2.0f * lzm[16 * rt + lr];
