@@ -21,15 +21,13 @@
 // for a (query tile, key tile) pair each z-term is the product (Q o Lz[m]) K^T on MFMA.
 //
 // Every kernel computes to fp32 accuracy (inputs of either dtype are widened on load). The
-// state contractions of the readout (u) and of dq and dk run on bf16 MFMA
-// (v_mfma_f32_16x16x32_bf16) with every fp32 operand split in three bf16 parts and six
-// products per fp32 product (split3 below); the increments and the products over the pairs
-// inside a chunk run on fp32 MFMA (v_mfma_f32_16x16x4_f32); dv's state part runs on the VALU
-// with the state row read at a wave-uniform address through the constant address space, so
-// that it arrives in scalar registers and feeds the FMAs directly. With packed fp32 off, the
-// VALU bound is the non-packed FMA rate (256 CUs x 4 SIMDs x 16 lanes x 2 flops x 2.4 GHz =
-// 78.6 TFLOP/s); fp32 MFMA reaches 157.3, bf16 MFMA 2500 (about 417 for the six-term fp32
-// products).
+// state contractions (the readout's u, the increments, the state parts of dq, dk and dv) and
+// most products over the pairs inside a chunk run on bf16 MFMA (v_mfma_f32_16x16x32_bf16) with
+// every fp32 operand split in three bf16 parts and up to six products per fp32 product (split3
+// below); the rest of the intra-chunk products of dk, dv run on fp32 MFMA
+// (v_mfma_f32_16x16x4_f32). With packed fp32 off, the VALU bound is the non-packed FMA rate
+// (256 CUs x 4 SIMDs x 16 lanes x 2 flops x 2.4 GHz = 78.6 TFLOP/s); fp32 MFMA reaches 157.3,
+// bf16 MFMA 2500 (about 417 for the six-term fp32 products).
 //
 // Launch order (all on the caller's stream):
 //   1. oal_bwd_increments<keys>:    per chunk psi(K_c)^T [V_c; 1]           -> workspace states
@@ -40,7 +38,7 @@
 //   5. oal_bwd_dkv_intra_mfma:      dk, dv partials of the pairs inside the chunk
 //   6. oal_bwd_increments<queries>: per chunk sum_h phi_h(Q_c)^T G_c       -> workspace states
 //   7. oal_bwd_scan (reverse):      exclusive suffix over chunks: R_c
-//   8. oal_bwd_dstate_x6<keys>, oal_bwd_dv_inter: dk, dv partials of the state part
+//   8. oal_bwd_dstate_x6<keys>, oal_bwd_dv_x6: dk, dv partials of the state part
 //   9. oal_bwd_kv_reduce:           dk, dv (the partials added in a fixed order)
 // With coefficient gradients, also oal_bwd_dw_intra (before 6), the per-head partials of 6,
 // and oal_bwd_dw_sum, oal_bwd_coef (after 6): dL, deps.
@@ -59,13 +57,9 @@ constexpr int kFeatBlock = 128;               // features per increment workgrou
 constexpr int kIncThreads = 512;              // its eight waves, 16 features each
 constexpr int kDkSplits = 4;                  // dk state part: its t steps over 4 workgroups
 
-typedef const float __attribute__((address_space(4))) cfloat;   // wave-uniform reads
-
 __device__ inline const OalHeadDev *bwd_head(const unsigned char *params, int h) {
     return reinterpret_cast<const OalHeadDev *>(params + sizeof(OalParamsHeader) + (size_t)h * OAL_HEAD_BYTES);
 }
-
-__device__ inline const cfloat *uni(const float *p) { return (const cfloat *)p; }
 
 __device__ inline int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
 
@@ -73,14 +67,6 @@ __device__ inline int wave_id() { return __builtin_amdgcn_readfirstlane(threadId
 __device__ inline int quad_base(int r) { return 1 + OAL_D + r * OAL_D - (r * (r - 1)) / 2 - r; }
 
 
-// acc[0:NC] += a S[f][0:NC] (NC = 64 or 65, column 64 from the separate vector)
-template <int NC>
-__device__ inline void row_axpy(float (&acc)[NC], float a, const cfloat *S, const cfloat *Sd, int f) {
-    const cfloat *row = S + (size_t)f * OAL_D;
-#pragma unroll
-    for (int c = 0; c < 64; ++c) acc[c] += a * row[c];
-    if constexpr (NC == 65) acc[64] += a * Sd[f];
-}
 
 
 
@@ -1217,9 +1203,8 @@ __global__ __launch_bounds__(kThreads) void oal_bwd_dq_intra_mfma(int T_len, int
 
 // 7. dk and dv. Each 64-key tile is covered by:
 //    - oal_bwd_dstate_x6<KEYS>: the state part of dk, dk_j += Jpsi(k_j)^T (R_c [v_j; 1]);
-//    - kInterSplits workgroups of oal_bwd_dv_inter: the 32 waves of the splits (worker
-//      4 p + w) take the feature-row pairs {worker, 63 - worker} (65 features each) of the
-//      state part of dv, dv_j += psi_f(k_j) R_c[f][0:64];
+//    - kInterSplits workgroups of oal_bwd_dv_x6: split p takes its share of the 34 feature
+//      blocks of the state part of dv, dv_j += psi_f(k_j) R_c[f][0:64];
 //    - one workgroup of oal_bwd_dkv_intra_mfma per query head h of the KV head: the pairs inside
 //      the chunk, i >= j: dv_j += kappa_ij g_i[0:64], dk_j += dkappa_ij dkappa_ij/dk_j.
 //    Each writes partial rows of 128 floats (dk, then dv) per key into part[slot]: slots
@@ -1233,54 +1218,122 @@ __device__ inline float *part_row(float *part, int slot, size_t rows, size_t row
 }
 
 
+// dv's state part dv_j += (R_c^T psi(k_j))[0:64] on split-bf16 MFMA: M = the 64 keys of the tile
+// (wave w: keys 16 w .. 16 w + 15), N = the 64 value columns, K = the features in blocks of 64.
+// A operand: psi_f(k) of the lane's key for the features 32 ks + 8 kg + e of the block (exact in
+// two bf16 parts for bf16 inputs, three otherwise); B operand: the block of R_c split in three
+// parts and staged transposed in LDS ([column][feature]), as in the readout gradient. The 34
+// feature blocks are split over kInterSplits workgroups per key tile; split p writes the dv half
+// of partial slot p.
 template <typename T>
-__global__ __launch_bounds__(kThreads) void oal_bwd_dv_inter(int T_len, int C, int nch, int n_kv_heads,
-                                                              const T *__restrict__ k, const float *__restrict__ st,
-                                                              float *__restrict__ part) {
-    __shared__ float xk[64 * 65];
-    __shared__ float red[64 * 65];
+__global__ __launch_bounds__(kThreads) void oal_bwd_dv_x6(int T_len, int C, int nch, int n_kv_heads,
+                                                           const T *__restrict__ k, const float *__restrict__ st,
+                                                           float *__restrict__ part) {
+    constexpr int PS = 72, NFB = 34;               // plane row stride (bf16), feature blocks of 64
+    constexpr int NA = sizeof(T) == 2 ? 2 : 3;     // parts of psi_f(k)
+    __shared__ __align__(16) float xk[64 * 68];    // key tile, column 64 = 1
+    __shared__ __align__(16) __bf16 pb[3 * 64 * PS];
+    __shared__ unsigned short fdl[NFB * 64];       // dims of feature f: a | b << 8 (64 reads the 1)
     const int tpc = C / 64, c = blockIdx.x / tpc, kt = blockIdx.x % tpc;
     const int p = blockIdx.y % kInterSplits, kv = blockIdx.y / kInterSplits, b = blockIdx.z;
-    const int j = threadIdx.x & 63, w = wave_id(), worker = p * 4 + w;
-    const int t0 = c * C + kt * 64, t = t0 + j;
-    const bool valid = t < T_len;
+    const int tid = threadIdx.x, lane = tid & 63, lr = lane & 15, kg = lane >> 4, w = wave_id();
+    const int t0 = c * C + kt * 64;
+    if (t0 >= T_len) return;                       // a tile past the sequence (uniform)
     const size_t krow = ((size_t)b * n_kv_heads + kv) * T_len, rows = (size_t)gridDim.z * n_kv_heads * T_len;
-    stage_rows(xk, 65, k, krow, t0, T_len, 1.0f);
-    __syncthreads();
-    const float *xj = xk + j * 65;
-    float a[64];
+    const int fb0 = NFB * p / kInterSplits, fb1 = NFB * (p + 1) / kInterSplits;
+    oal_f32x4 D[4];                                // key 16 w + 4 kg + jj, column 16 ct + lr
 #pragma unroll
-    for (int e = 0; e < 64; ++e) a[e] = 0.0f;
-    if (c < nch - 1) {
-        const float *Rg = st + ((size_t)((size_t)b * n_kv_heads + kv) * nch + c) * OAL_STATE_STRIDE;
-        const cfloat *R = uni(Rg), *Rd = uni(Rg + (size_t)OAL_NFEAT * OAL_D);
-        if (worker == 0) row_axpy<64>(a, 1.0f, R, Rd, 0);      // constant feature
-        for (int half = 0; half < 2; ++half) {
-            const int r = half ? 63 - worker : worker;
-            const float kr = xj[r];
-            const int base = quad_base(r);
-            row_axpy<64>(a, kr, R, Rd, 1 + r);
-#pragma unroll 4
-            for (int tt = r; tt < OAL_D; ++tt) row_axpy<64>(a, kr * xj[tt], R, Rd, base + tt);
+    for (int ct = 0; ct < 4; ++ct) D[ct] = oal_splat(0.0f);
+    if (c < nch - 1) {                             // R of the last chunk = 0
+        stage_rows(xk, 68, k, krow, t0, T_len, 1.0f);
+        for (int f = 64 * fb0 + tid; f < 64 * fb1; f += kThreads) {
+            int fa = OAL_D, fb = OAL_D;
+            if (f >= 1 && f <= OAL_D) {
+                fa = f - 1;
+            } else if (f > OAL_D && f < OAL_NFEAT) {
+                int idx = f - 1 - OAL_D, r = 0;
+                while (idx >= OAL_D - r) { idx -= OAL_D - r; ++r; }
+                fa = r;
+                fb = r + idx;
+            }
+            fdl[f] = (unsigned short)(fa | (fb << 8));
+        }
+        const float *R = st + ((size_t)((size_t)b * n_kv_heads + kv) * nch + c) * OAL_STATE_STRIDE;
+        const float *xa = xk + (16 * w + lr) * 68;
+        // staging share: features sf + u (u < 4), columns sc + j (j < 4)
+        const int sf = 4 * (tid & 15), sc = 4 * (tid >> 4);
+        float4 pre[4];
+        auto load_block = [&](int f0) {
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int f = f0 + sf + u;
+                pre[u] = f < OAL_NFEAT ? *reinterpret_cast<const float4 *>(R + (size_t)f * OAL_D + sc)
+                                       : make_float4(0, 0, 0, 0);
+            }
+        };
+        load_block(64 * fb0);
+        for (int fbk = fb0; fbk < fb1; ++fbk) {
+            const int f0 = 64 * fbk;
+            __syncthreads();                       // the previous block is consumed (and xk, fdl staged)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                oal_bf16x4 p0, p1, p2;
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    const float x = j == 0 ? pre[u].x : j == 1 ? pre[u].y : j == 2 ? pre[u].z : pre[u].w;
+                    __bf16 x0, x1, x2;
+                    split3(x, x0, x1, x2);
+                    p0[u] = x0;
+                    p1[u] = x1;
+                    p2[u] = x2;
+                }
+                const int o = (sc + j) * PS + sf;
+                *reinterpret_cast<oal_bf16x4 *>(pb + o) = p0;
+                *reinterpret_cast<oal_bf16x4 *>(pb + 64 * PS + o) = p1;
+                *reinterpret_cast<oal_bf16x4 *>(pb + 2 * 64 * PS + o) = p2;
+            }
+            __syncthreads();
+            if (fbk + 1 < fb1) load_block(f0 + 64);
+            oal_pin_loads();
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) {
+                const int fl = 32 * ks + 8 * kg;   // the lane's first feature in the block
+                oal_bf16x8 a[3];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const unsigned short ab = fdl[f0 + fl + e];
+                    __bf16 x0, x1, x2;
+                    split3(xa[ab & 0xff] * xa[ab >> 8], x0, x1, x2);
+                    a[0][e] = x0;
+                    a[1][e] = x1;
+                    a[2][e] = x2;
+                }
+#pragma unroll
+                for (int ct = 0; ct < 4; ++ct) {
+                    const int o = (16 * ct + lr) * PS + fl;
+                    oal_bf16x8 bq[3];
+#pragma unroll
+                    for (int q3 = 0; q3 < 3; ++q3) bq[q3] = *reinterpret_cast<const oal_bf16x8 *>(pb + q3 * 64 * PS + o);
+#pragma unroll
+                    for (int ord = 2; ord >= 0; --ord)
+#pragma unroll
+                        for (int i = 0; i < NA; ++i) {
+                            const int jb = ord - i;
+                            if (jb < 0 || jb > 2) continue;
+                            D[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], bq[jb], D[ct], 0, 0, 0);
+                        }
+                }
+            }
         }
     }
-    for (int s = 0; s < 4; ++s) {
-        __syncthreads();
-        if (w == s) {
 #pragma unroll
-            for (int e = 0; e < 64; ++e) red[j * 65 + e] = (s == 0 ? 0.0f : red[j * 65 + e]) + a[e];
+    for (int ct = 0; ct < 4; ++ct)
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+            const int t = t0 + 16 * w + 4 * kg + jj;
+            if (t < T_len) part_row(part, p, rows, krow + t)[64 + 16 * ct + lr] = D[ct][jj];
         }
-    }
-    __syncthreads();
-    if (valid) {
-        float *o = part_row(part, p, rows, krow + t) + 64 + w * 16;
-        const float *src = red + j * 65 + w * 16;
-#pragma unroll
-        for (int e = 0; e < 16; e += 4)
-            *reinterpret_cast<float4 *>(o + e) = make_float4(src[e], src[e + 1], src[e + 2], src[e + 3]);
-    }
 }
-
 
 // dk and dv pairs inside the chunk for one query head, on fp32 MFMA (16x16x4). Workgroup =
 // (64-key tile, query head, sequence); wave w owns the keys 16 w .. 16 w + 15 of every product.
@@ -1716,7 +1769,7 @@ hipError_t launch_backward(const oal_dims &d, int T_len, int C, const void *q_, 
     hipLaunchKernelGGL(oal_bwd_scan, g_scan, blk, 0, stream, nch, 1, st, (const float *)nullptr, dstate_in);
     hipLaunchKernelGGL((oal_bwd_dstate_x6<T, true>), dim3(nch * tpc, Hkv * kDkSplits, B), blk, 0, stream, s0, T_len, C,
                        nch, Hq, Hkv, k, v, params, st, gv, gd, part);
-    hipLaunchKernelGGL(oal_bwd_dv_inter<T>, g_ki, blk, 0, stream, T_len, C, nch, Hkv, k, st, part);
+    hipLaunchKernelGGL(oal_bwd_dv_x6<T>, g_ki, blk, 0, stream, T_len, C, nch, Hkv, k, st, part);
     hipLaunchKernelGGL(oal_bwd_kv_reduce, g_red, blk, 0, stream, kvrows, nslots, part, dk, dv);
     return hipGetLastError();
 }
