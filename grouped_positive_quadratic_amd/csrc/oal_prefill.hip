@@ -872,7 +872,10 @@ __global__ __launch_bounds__(256, 2) void oal_readout(
     const int h0 = kv * n_rep + hg * R;
     const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
     const int g = lane >> 4, lr = lane & 15;
-    const int hs = wave >> 1, par = wave & 1;
+    // head subsets of unequal size (R odd: 4 + 3 heads): workgroups i8 and i8 + 32 of an XCD
+    // share a CU (measured placement), and swapping the subsets' roles in one of them puts a
+    // long and a short wave on each SIMD (readout 32.2 -> 31.6 us at B = 1 x 4096)
+    const int hs = (wave >> 1) ^ (R - (R + 1) / 2 > 0 ? (i8 >> 5) & 1 : 0), par = wave & 1;
     const int hb = hs * RW;                       // first local head of this wave's subset
     const int nh = hs == 0 ? RW : R - RW;         // heads of the subset (0 when R == 1)
     const int pos0 = c * C + qt * 16;
@@ -1073,6 +1076,26 @@ __global__ __launch_bounds__(256, 2) void oal_readout(
         // tail[jj] q_ra q_rb with q_64 = 1 (zero past the KV head's entries)
         auto tail_step = [&](const OalFrag<T> (&bc)[5], int x) {
             const int j0 = 32 * x + 8 * g;
+            if (x < 2) {
+                // entries 0..63 are the linear features, pair (j, 64): the lane's 8 entries are
+                // the 8 consecutive dims j0.. of the query row, one 16- or 32-byte read
+#pragma unroll
+                for (int li = 0; li < NH; ++li) {
+                    OalFrag<T> qv;
+                    qv.load(s_q + ((hb + li) * 16 + lr) * QS + j0);
+                    const float4 *cp = reinterpret_cast<const float4 *>(s_tail + (hb + li) * OAL_TAIL_PAIRS + j0);
+                    const float4 c0 = cp[0], c1 = cp[1];
+                    const float cf[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
+                    float phi[8];
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) phi[e] = cf[e] * (float)qv.v[e];
+                    OalFrag<T> a;
+                    a.set(phi);
+#pragma unroll
+                    for (int n = 0; n < 5; ++n) acc[li][n] = oal_mma(a, bc[n], acc[li][n]);
+                }
+                return;
+            }
             const uint2 pra = *reinterpret_cast<const uint2 *>(s_pair + j0);
             const uint2 prb = *reinterpret_cast<const uint2 *>(s_pair + OAL_TAIL_PAIRS + j0);
             int ia[8], ib[8];
