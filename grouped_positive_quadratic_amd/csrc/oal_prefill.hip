@@ -473,8 +473,7 @@ __device__ inline void oal_z_step(const float (&lzv)[16], float cm, const float 
     }
 }
 
-constexpr int kIntraLzr = 8;          // Lz rows m < 8 staged in LDS ...
-constexpr int kIntraLzHeads = 16;     // ... for the first 16 query heads of a KV head
+constexpr int kIntraLzr = 8;          // Lz rows per LDS block of a wave (the rows m < 8, then refills)
 constexpr int kFragFloats = 5 * 4 * 64;   // one 16 x 80 accumulator tile, fragment order
 
 // The intra-chunk tile of one (head, 16-query tile), unnormalised, in accumulator-fragment
@@ -535,8 +534,8 @@ template <typename T, int C> struct IntraLayout {
     static constexpr int LDV = CP + EPU;
     static constexpr int O_K = 0;                                             // T [C][QS]
     static constexpr int O_VT = O_K + C * QS * (int)sizeof(T);                // T [64][LDV]
-    static constexpr int O_LZ = O_VT + OAL_D * LDV * (int)sizeof(T);          // f32 [n_rep][8][64]
-    static size_t bytes(int n_rep) { return (size_t)O_LZ + (size_t)n_rep * kIntraLzr * OAL_D * 4; }
+    static constexpr int O_LZ = O_VT + OAL_D * LDV * (int)sizeof(T);          // f32 [8 waves][8][64]
+    static constexpr size_t BYTES = (size_t)O_LZ + (size_t)8 * kIntraLzr * OAL_D * 4;
     static_assert(O_VT % 16 == 0 && O_LZ % 16 == 0, "alignment");
 };
 
@@ -604,10 +603,10 @@ __device__ __forceinline__ void intra_block(int Lb, int T_len, OalSeqLayout sl, 
     {
         constexpr int NKU = C * UPQ;                      // 16-byte units of K (and of V)
         constexpr int NKJ = (NKU + NTH - 1) / NTH;
-        constexpr int NLJ = (kIntraLzHeads * kIntraLzr * OAL_D / 4 + NTH - 1) / NTH;
+        constexpr int NLJ = (kIntraWaves * kIntraLzr * OAL_D / 4 + NTH - 1) / NTH;
         const T *kb = k + sl.row0(b, kv, n_kv_heads, T_len) * OAL_D;
         const T *vb = v + sl.row0(b, kv, n_kv_heads, T_len) * OAL_D;
-        const int nlz = min(n_rep, kIntraLzHeads) * kIntraLzr * OAL_D / 4;
+        const int nlz = min(n_rep, kIntraWaves) * kIntraLzr * OAL_D / 4;   // wave w: head w's rows 0..7
         oal_u32x4 rk[NKJ], rv[NKJ];
         float4 rl[NLJ];
 #pragma unroll
@@ -654,6 +653,9 @@ __device__ __forceinline__ void intra_block(int Lb, int T_len, OalSeqLayout sl, 
         zeros.set(zz);
     }
     const int ntiles = nchunks * NQT;
+    // head whose Lz rows lz_blk * 8 .. + 7 the wave's LDS block holds (rows 0..7 of head
+    // `wave` after the staging)
+    int lz_head = wave < n_rep ? wave : -1, lz_blk = 0;
     // one head and query tile: NK = qt + 1 key tiles (compile time)
     auto tile = [&](auto nk_c, int i, int qt) {
         constexpr int NK = decltype(nk_c)::value;
@@ -670,17 +672,47 @@ __device__ __forceinline__ void intra_block(int Lb, int T_len, OalSeqLayout sl, 
         oal_f32x4 kap[NK + (NK & 1)];          // even count: key tiles go to the MFMA in pairs
 #pragma unroll
         for (int kt = 0; kt < NK + (NK & 1); ++kt) kap[kt] = oal_splat(eps);
+        // Lz rows come from the wave's LDS block of 8 rows: rows 0..7 of head `wave` are staged
+        // before the first tile; another head, or G >= 8 (up to 65 terms, the block refilled
+        // every 8 terms with the next rows, loaded into registers one block ahead: lane l holds
+        // row l / 8, dims 8 (l % 8) ..), reloads rows 0..7 first. Rows past 64 are clamped reads.
+        float4 *lz_dst = reinterpret_cast<float4 *>(s_lz + (wave * kIntraLzr + (lane >> 3)) * OAL_D + 8 * (lane & 7));
+        const float *lz_src = hd->Lz + (lane >> 3) * OAL_D + 8 * (lane & 7);
+        if (lz_head != i || lz_blk != 0) {
+            const float4 a0 = reinterpret_cast<const float4 *>(lz_src)[0];
+            const float4 a1 = reinterpret_cast<const float4 *>(lz_src)[1];
+            oal_pin_loads();             // the wave's reads of the previous rows come first
+            lz_dst[0] = a0;
+            lz_dst[1] = a1;
+            lz_head = i;
+            lz_blk = 0;
+        }
+        float4 lz0 = make_float4(0.f, 0.f, 0.f, 0.f), lz1 = lz0;
+        if (G >= kIntraLzr) {
+            const float4 *nx = reinterpret_cast<const float4 *>(lz_src + kIntraLzr * OAL_D);
+            lz0 = nx[0];
+            lz1 = nx[1];
+        }
+        const float *lz_row = s_lz + wave * kIntraLzr * OAL_D + 8 * g;
         for (int m = 0; m <= G; ++m) {
-            float lzv[16];
-            if (G < kIntraLzr && i < kIntraLzHeads) {
-                const float *p = s_lz + (i * kIntraLzr + m) * OAL_D + 8 * g;
-#pragma unroll
-                for (int e = 0; e < 8; ++e) { lzv[e] = p[e]; lzv[8 + e] = p[32 + e]; }
-            } else {
-                const float *p = hd->Lz + m * OAL_D + 8 * g;
-#pragma unroll
-                for (int e = 0; e < 8; ++e) { lzv[e] = p[e]; lzv[8 + e] = p[32 + e]; }
+            if (m > 0 && (m & (kIntraLzr - 1)) == 0) {
+                oal_pin_loads();          // the wave's reads of the previous block come first
+                lz_dst[0] = lz0;
+                lz_dst[1] = lz1;
+                lz_blk = m / kIntraLzr;
+                // next block: rows m + 8 .. m + 15 (rows past 64, never used, clamped to 64)
+                const int row = min(m + kIntraLzr + (lane >> 3), OAL_D) - (lane >> 3);
+                const float4 *nx = reinterpret_cast<const float4 *>(lz_src + row * OAL_D);
+                if (m + kIntraLzr <= G) {
+                    lz0 = nx[0];
+                    lz1 = nx[1];
+                }
+                oal_pin_loads();
             }
+            float lzv[16];
+            const float *p = lz_row + (m & (kIntraLzr - 1)) * OAL_D;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) { lzv[e] = p[e]; lzv[8 + e] = p[32 + e]; }
             // z_m^T (16 keys x 16 queries) = K_kt . (Lz[m] o q)^T + c_m for every key tile
             OalFrag<T> bq[2];
 #pragma unroll
@@ -791,8 +823,12 @@ __device__ __forceinline__ void intra_block(int Lb, int T_len, OalSeqLayout sl, 
 // CUs overlaps them. Blocks [0, n_intra) are intra-chunk blocks (the longer ones, dispatched
 // first; n_intra is a multiple of 8, so their XCD placement is the one described above); the
 // rest are increment blocks (K-step block fastest, then chunk, then sequence x KV head).
+// Four waves per SIMD (128 VGPRs) let an increment workgroup run beside an intra-chunk one;
+// with 256-token chunks the intra part needs more registers than that (at 128 it spills:
+// 417 us against 219 us at B = 8 x 4096), so that size gets two waves per SIMD.
+template <int C> constexpr int intra_waves_per_eu() { return C >= 256 ? 2 : 4; }
 template <typename T, int C>
-__global__ __launch_bounds__(64 * kIntraWaves) __attribute__((amdgpu_waves_per_eu(4))) void oal_intra_delta(
+__global__ __launch_bounds__(64 * kIntraWaves) __attribute__((amdgpu_waves_per_eu(intra_waves_per_eu<C>()))) void oal_intra_delta(
     int T_len, OalSeqLayout sl, int n_q_heads, int n_kv_heads, int nchunks, int n_bkv, int n_delta,
     const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ v,
     const unsigned char *__restrict__ params, const float *__restrict__ state, T *__restrict__ delta,
@@ -1278,7 +1314,7 @@ hipError_t launch_all(const oal_dims &d, int T_len, OalSeqLayout sl, const void 
     if (marks && (e = hipEventRecord(marks[0], stream)) != hipSuccess) return e;
     if (y) {   // intra-chunk sums and chunk increments in one launch
         using IL = IntraLayout<T, C>;
-        const size_t lds = std::max(IL::bytes(std::min(d.n_q_heads / d.n_kv_heads, kIntraLzHeads)), scan_lds<T, C>());
+        const size_t lds = std::max(IL::BYTES, scan_lds<T, C>());
         auto kern = oal_intra_delta<T, C>;
         static std::atomic<int> lds_set[kMaxDevices];
         if ((e = ensure_lds_limit(kern, lds, lds_set)) != hipSuccess) return e;
