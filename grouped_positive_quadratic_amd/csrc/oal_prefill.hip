@@ -724,13 +724,14 @@ __device__ __forceinline__ void intra_block(int Lb, int T_len, OalSeqLayout sl, 
             }
             const oal_f32x4 cinit = oal_splat(m == 0 ? L00 : 0.0f);
             // key tiles are re-read from LDS for every z term (an opaque offset keeps the
-            // compiler from holding all of them in registers)
+            // compiler from holding all of them in registers). Software-pipelined: the next
+            // tile's fragments are requested before this tile's MFMAs, and a tile's squares
+            // are taken after the next tile's MFMAs are issued, so neither the LDS latency nor
+            // the MFMA latency stands between two tiles.
             int koff = (lr * QS + 8 * g) * (int)sizeof(T);
             asm volatile("" : "+v"(koff));
-#pragma unroll
-            for (int kt = 0; kt < NK; ++kt) {
+            auto load_k = [&](int kt, OalFrag<T> (&ak)[2]) {
                 const T *kr = reinterpret_cast<const T *>(reinterpret_cast<const unsigned char *>(s_k) + koff) + 16 * kt * QS;
-                OalFrag<T> ak[2];
                 if (EPU == 8) {
                     ak[0].load(kr);
                     ak[1].load(kr + 32);
@@ -738,13 +739,41 @@ __device__ __forceinline__ void intra_block(int Lb, int T_len, OalSeqLayout sl, 
                     ak[0].load4x2(kr, kr + 4);
                     ak[1].load4x2(kr + 32, kr + 36);
                 }
-                // the two halves of the 64 dims as independent MFMAs, added after
-                const oal_f32x4 za = oal_mma(ak[0], bq[0], cinit);
-                const oal_f32x4 zb = oal_mma(ak[1], bq[1], oal_splat(0.0f));
+            };
+            if constexpr (sizeof(T) != 2) {
+                // fp32 fragments are twice the registers: one tile at a time
 #pragma unroll
-                for (int ii = 0; ii < 4; ++ii) {
-                    const float zz = za[ii] + zb[ii];
-                    kap[kt][ii] += zz * zz;
+                for (int kt = 0; kt < NK; ++kt) {
+                    OalFrag<T> ak[2];
+                    load_k(kt, ak);
+                    const oal_f32x4 za = oal_mma(ak[0], bq[0], cinit);
+                    const oal_f32x4 zb = oal_mma(ak[1], bq[1], oal_splat(0.0f));
+#pragma unroll
+                    for (int ii = 0; ii < 4; ++ii) {
+                        const float zz = za[ii] + zb[ii];
+                        kap[kt][ii] += zz * zz;
+                    }
+                }
+                continue;
+            }
+            OalFrag<T> ak[2][2];
+            oal_f32x4 za[2], zb[2];
+            load_k(0, ak[0]);
+#pragma unroll
+            for (int kt = 0; kt <= NK; ++kt) {
+                if (kt + 1 < NK) load_k(kt + 1, ak[(kt + 1) & 1]);
+                if (kt < NK) {
+                    // the two halves of the 64 dims as independent MFMAs, added after
+                    za[kt & 1] = oal_mma(ak[kt & 1][0], bq[0], cinit);
+                    zb[kt & 1] = oal_mma(ak[kt & 1][1], bq[1], oal_splat(0.0f));
+                }
+                if (kt > 0) {
+                    const int p = (kt - 1) & 1;
+#pragma unroll
+                    for (int ii = 0; ii < 4; ++ii) {
+                        const float zz = za[p][ii] + zb[p][ii];
+                        kap[kt - 1][ii] += zz * zz;
+                    }
                 }
             }
         }
