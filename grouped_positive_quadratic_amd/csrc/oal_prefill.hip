@@ -274,7 +274,22 @@ __device__ __forceinline__ void scan_delta_block(
     int frow[8], ra[2], rb[2];
     float fsc[8];
     bool fown[8];
-    slot_tables(s, kvd, g, lr, frow, fsc, fown, ra, rb);
+    if (s < OAL_KSTEPS) {
+        // main K-step: only the A-operand rows are needed, (r, t) = (4 rq + lr / 4, 8 tb + 4 h +
+        // lr % 4), a product of K^T rows r and t when r <= t, else the zero row
+        int tb = 0;
+#pragma unroll
+        for (int k = 1; k < 8; ++k) tb += (k * (k + 1) <= s) ? 1 : 0;
+        const int rq = s - tb * (tb + 1);
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int r = 4 * rq + (lr >> 2), t = 8 * tb + 4 * h + (lr & 3);
+            ra[h] = r <= t ? r : kRowZero;
+            rb[h] = r <= t ? t : kRowZero;
+        }
+    } else {
+        slot_tables(s, kvd, g, lr, frow, fsc, fown, ra, rb);
+    }
     OalFrag<T> ones, zeros;
     {
         float o[8], zz[8];
