@@ -894,6 +894,10 @@ __global__ __launch_bounds__(64 * kIntraWaves) __attribute__((amdgpu_waves_per_e
 
 // ------------------------------------------------------------------------------------
 // 4. readout
+// the general blob's slot coefficients of a wave's heads, one main K-step ahead (ON) or none
+template <bool ON, int N> struct WRing { float4 n[N][2], c[N][2]; };
+template <int N> struct WRing<false, N> {};
+
 template <typename T, int C, int R> struct ReadoutLayout {
     static constexpr int EPU = 16 / (int)sizeof(T);
     static constexpr int NT = 256;              // threads: 2 head subsets x 2 parities
@@ -1087,15 +1091,42 @@ __global__ __launch_bounds__(256, 2) void oal_readout(
                 pt[li][4] = x1.x; pt[li][5] = x1.y; pt[li][6] = x1.z; pt[li][7] = x1.w;
             }
         };
+        // general blob: the full coefficient of each slot, from the blob; for bf16 inputs
+        // requested one main K-step ahead (wn: the next step's, wc: this step's; G = 64 readout
+        // 56 -> .. us), for fp32 inputs (whose registers are taken by the fp32 operands) at use
+        constexpr bool kWAhead = GEN && sizeof(T) == 2;
+        WRing<kWAhead, NH> wr;
+        auto load_w = [&](int tb_, int j_) {
+            if constexpr (kWAhead) {
+#pragma unroll
+                for (int li = 0; li < NH; ++li) {
+                    const float4 *wp = reinterpret_cast<const float4 *>(
+                        head_ptr(params, h0 + hb + li)->wslot + oal_kstep(tb_, 2 * j_ + par) * 32 + 8 * g);
+                    wr.n[li][0] = wp[0];
+                    wr.n[li][1] = wp[1];
+                }
+            } else {
+                (void)tb_;
+                (void)j_;
+            }
+        };
         auto gen_mul = [&](int li, int rq, float (&phi)[8]) {
-            if (GEN) {   // general blob: the full coefficient of each slot, from the blob
-                const float4 *wp = reinterpret_cast<const float4 *>(
-                    head_ptr(params, h0 + hb + li)->wslot + oal_kstep(tb, rq) * 32 + 8 * g);
-                const float4 w0v = wp[0], w1v = wp[1];
+            if (GEN) {
+                float4 w0v, w1v;
+                if constexpr (kWAhead) {
+                    w0v = wr.c[li][0];
+                    w1v = wr.c[li][1];
+                } else {
+                    const float4 *wp = reinterpret_cast<const float4 *>(
+                        head_ptr(params, h0 + hb + li)->wslot + oal_kstep(tb, rq) * 32 + 8 * g);
+                    w0v = wp[0];
+                    w1v = wp[1];
+                }
                 phi[0] *= w0v.x; phi[1] *= w0v.y; phi[2] *= w0v.z; phi[3] *= w0v.w;
                 phi[4] *= w1v.x; phi[5] *= w1v.y; phi[6] *= w1v.z; phi[7] *= w1v.w;
             }
         };
+        load_w(0, 0);
         // main K-step: A = p_r p_t (times the slot coefficient in a general blob)
         auto make_a = [&](int li, int rq, float pr, OalFrag<T> &a) {
             float phi[8];
@@ -1124,6 +1155,13 @@ __global__ __launch_bounds__(256, 2) void oal_readout(
             if (!kAhead) {
                 if (j == 0) load_pt();
                 load_prv();
+            }
+            if constexpr (kWAhead) {
+#pragma unroll
+                for (int li = 0; li < NH; ++li) { wr.c[li][0] = wr.n[li][0]; wr.c[li][1] = wr.n[li][1]; }
+                const int j2 = j + 1 > tb ? 0 : j + 1, tb2 = j + 1 > tb ? tb + 1 : tb;
+                if (tb2 < 8) load_w(tb2, j2);
+                oal_pin_loads();
             }
             // the next head's operand is formed while this head's MFMAs run (two buffers;
             // bf16: the scheduler is told to alternate one MFMA with three VALU ops)
@@ -1156,7 +1194,7 @@ __global__ __launch_bounds__(256, 2) void oal_readout(
         // tail[jj] q_ra q_rb with q_64 = 1 (zero past the KV head's entries)
         auto tail_step = [&](const OalFrag<T> (&bc)[5], int x) {
             const int j0 = 32 * x + 8 * g;
-            if (x < 2) {
+            if (sizeof(T) == 2 && x < 2) {   // (fp32: the gather below, fewer registers)
                 // entries 0..63 are the linear features, pair (j, 64): the lane's 8 entries are
                 // the 8 consecutive dims j0.. of the query row, one 16- or 32-byte read
 #pragma unroll
