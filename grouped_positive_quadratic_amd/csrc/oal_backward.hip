@@ -253,8 +253,20 @@ __device__ inline void mfma_xyt(const float *X, const float *Y, int lr, int kg, 
 // 64 rows of Y (LDS tiles, row stride 68), s = a row of Lz (64 floats, 16-byte aligned), on
 // bf16 MFMA: X o s in three parts, Y in NY parts (the terms of order <= 2). Z[ct][jj]: row
 // 4 kg + jj, column 16 ct + lr.
+// The lane's 16 scale values of a z term: Lz[m][32 ks + 8 kg + e], ks = 0, 1, e = 0..7
+// (fetched a term ahead by the callers, so that no term waits for its Lz row).
+struct ZScale {
+    float4 v[4];
+};
+__device__ inline void zscale_load(const float *sc, int kg, ZScale &z) {
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+        z.v[2 * ks] = *reinterpret_cast<const float4 *>(sc + 32 * ks + 8 * kg);
+        z.v[2 * ks + 1] = *reinterpret_cast<const float4 *>(sc + 32 * ks + 8 * kg + 4);
+    }
+}
 template <int NY>
-__device__ inline void mfma_zterm(const float *X, const float *sc, const float *Y, float z0, int lr, int kg,
+__device__ inline void mfma_zterm(const float *X, const ZScale &zs, const float *Y, float z0, int lr, int kg,
                                   oal_f32x4 (&Z)[4]) {
 #pragma unroll
     for (int ct = 0; ct < 4; ++ct) Z[ct] = oal_splat(0.0f);
@@ -263,8 +275,8 @@ __device__ inline void mfma_zterm(const float *X, const float *sc, const float *
         const int k0 = 32 * ks + 8 * kg;
         const float4 x0 = *reinterpret_cast<const float4 *>(X + lr * 68 + k0);
         const float4 x1 = *reinterpret_cast<const float4 *>(X + lr * 68 + k0 + 4);
-        const float4 s0 = *reinterpret_cast<const float4 *>(sc + k0);
-        const float4 s1 = *reinterpret_cast<const float4 *>(sc + k0 + 4);
+        const float4 s0 = zs.v[2 * ks];
+        const float4 s1 = zs.v[2 * ks + 1];
         const float xs[8] = {x0.x * s0.x, x0.y * s0.y, x0.z * s0.z, x0.w * s0.w,
                              x1.x * s1.x, x1.y * s1.y, x1.z * s1.z, x1.w * s1.w};
         oal_bf16x8 a[3];
@@ -753,9 +765,13 @@ __global__ __launch_bounds__(kThreads) void oal_bwd_readout_g(int s0, int T_len,
             oal_f32x4 kap[4];                       // query 16 w + 4 kg + jj, key 16 jt + lr
 #pragma unroll
             for (int jt = 0; jt < 4; ++jt) kap[jt] = oal_splat(0.0f);
+            ZScale zn, zc;
+            zscale_load(Lz, kg, zn);
             for (int m = 0; m <= G; ++m) {
+                zc = zn;
+                if (m < G) zscale_load(Lz + (m + 1) * OAL_D, kg, zn);
                 oal_f32x4 Z[4];
-                mfma_zterm<sizeof(T) == 2 ? 1 : 3>(xq + 16 * w * 68, Lz + m * OAL_D, ks, m == 0 ? L00 : 0.0f, lr, kg, Z);
+                mfma_zterm<sizeof(T) == 2 ? 1 : 3>(xq + 16 * w * 68, zc, ks, m == 0 ? L00 : 0.0f, lr, kg, Z);
 #pragma unroll
                 for (int jt = 0; jt < 4; ++jt)
 #pragma unroll
@@ -1166,11 +1182,15 @@ __global__ __launch_bounds__(kThreads) void oal_bwd_dq_intra_mfma(int T_len, int
         stage_rows(qs, 68, q, qrow, t0, T_len, 0.0f);
         __syncthreads();
         float *es = gs;
+        ZScale zn, zc;
+        zscale_load(Lz, kg, zn);
         for (int m = 0; m <= G; ++m) {
             const float *lzm = Lz + m * OAL_D;
+            zc = zn;
+            if (m < G) zscale_load(lzm + OAL_D, kg, zn);
             // Z_m for the wave's 16 queries x 64 keys
             oal_f32x4 Z[4];
-            mfma_zterm<NK>(qs + 16 * w * 68, lzm, ks, m == 0 ? L00 : 0.0f, lr, kg, Z);
+            mfma_zterm<NK>(qs + 16 * w * 68, zc, ks, m == 0 ? L00 : 0.0f, lr, kg, Z);
             // E_m = dkappa o Z_m into the wave's rows of es (row = query, column = key)
 #pragma unroll
             for (int jt = 0; jt < 4; ++jt)
@@ -1396,10 +1416,14 @@ __global__ __launch_bounds__(kThreads) void oal_bwd_dkv_intra_mfma(int T_len, in
         oal_f32x4 kap[4];                          // sum_m Z_m^2: key 16 w + 4 kg + jj, query 16 it + lr
 #pragma unroll
         for (int it = 0; it < 4; ++it) kap[it] = oal_splat(0.0f);
+        ZScale zn, zc;
+        zscale_load(Lz, kg, zn);
         for (int m = 0; m <= G; ++m) {
             const float *lzm = Lz + m * OAL_D;
+            zc = zn;
+            if (m < G) zscale_load(lzm + OAL_D, kg, zn);
             oal_f32x4 Z[4];
-            mfma_zterm<sizeof(T) == 2 ? 1 : 3>(ks + 16 * w * 68, lzm, qs, m == 0 ? L00 : 0.0f, lr, kg, Z);
+            mfma_zterm<sizeof(T) == 2 ? 1 : 3>(ks + 16 * w * 68, zc, qs, m == 0 ? L00 : 0.0f, lr, kg, Z);
 #pragma unroll
             for (int it = 0; it < 4; ++it)
 #pragma unroll
