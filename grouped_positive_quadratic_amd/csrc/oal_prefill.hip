@@ -772,21 +772,20 @@ __device__ __forceinline__ void intra_block(int Lb, int T_len, OalSeqLayout sl, 
                 continue;
             }
             OalFrag<T> ak[2][2];
-            oal_f32x4 za[2], zb[2];
+            oal_f32x4 za[2];
             load_k(0, ak[0]);
 #pragma unroll
             for (int kt = 0; kt <= NK; ++kt) {
                 if (kt + 1 < NK) load_k(kt + 1, ak[(kt + 1) & 1]);
                 if (kt < NK) {
-                    // the two halves of the 64 dims as independent MFMAs, added after
-                    za[kt & 1] = oal_mma(ak[kt & 1][0], bq[0], cinit);
-                    zb[kt & 1] = oal_mma(ak[kt & 1][1], bq[1], oal_splat(0.0f));
+                    // the two halves of the 64 dims accumulate into one result
+                    za[kt & 1] = oal_mma(ak[kt & 1][1], bq[1], oal_mma(ak[kt & 1][0], bq[0], cinit));
                 }
                 if (kt > 0) {
                     const int p = (kt - 1) & 1;
 #pragma unroll
                     for (int ii = 0; ii < 4; ++ii) {
-                        const float zz = za[p][ii] + zb[p][ii];
+                        const float zz = za[p][ii];
                         kap[kt - 1][ii] += zz * zz;
                     }
                 }
