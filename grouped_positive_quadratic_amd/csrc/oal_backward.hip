@@ -268,8 +268,9 @@ __device__ inline void zscale_load(const float *sc, int kg, ZScale &z) {
 template <int NY>
 __device__ inline void mfma_zterm(const float *X, const ZScale &zs, const float *Y, float z0, int lr, int kg,
                                   oal_f32x4 (&Z)[4]) {
+    // the constant term seeds the accumulators
 #pragma unroll
-    for (int ct = 0; ct < 4; ++ct) Z[ct] = oal_splat(0.0f);
+    for (int ct = 0; ct < 4; ++ct) Z[ct] = oal_splat(z0);
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
         const int k0 = 32 * ks + 8 * kg;
@@ -302,8 +303,6 @@ __device__ inline void mfma_zterm(const float *X, const ZScale &zs, const float 
                 }
         }
     }
-#pragma unroll
-    for (int ct = 0; ct < 4; ++ct) Z[ct] += oal_splat(z0);
 }
 static_assert(offsetof(OalHeadDev, Lz) % 16 == 0, "Lz rows are read as float4");
 
